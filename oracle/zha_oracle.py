@@ -1,0 +1,247 @@
+"""CPU oracle for tree-indexed sparse decode attention (Zyphra Hierarchical Attention).
+
+TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the benchmark's
+CPU-baseline leg may import this module. The product path (the HIP library and
+its Python binding) never calls it, and it shares no code with that path.
+
+Source: "Zyphra présente Zyphra Hierarchical Attention (ZHA), une voie vers une
+attention vraiment sous-quadratique" (Le Fil IA, from MarkTechPost), paragraph 1,
+which states the whole mechanism:
+
+* the full KV cache is kept; the tree only decides which keys each query reads;
+* keys are cut into contiguous blocks, each summarised by one summary key
+  obtained from 16 learned reference queries, then grouped level by level
+  (blocks of 4 with 6 levels give top nodes of 4,096 tokens);
+* at inference a query scores the top nodes, keeps the smallest set covering a
+  fraction p of the estimated attention mass, then expands only those branches
+  down to raw KV entries;
+* the first token is always kept as an anchor.
+
+Paragraph 2 of the same page fixes p = 0.95 and the two geometries (blocks of
+4 with 6 levels; blocks of 256 with 1 level).
+
+Readings where the page is silent (each is listed in the design doc):
+
+* pooling (not stated beyond "from 16 reference queries"): each reference query
+  attends over a node's b children with a softmax at scale tau = 1/sqrt(d); the
+  16 attention outputs are averaged. The summary is a convex combination of the
+  children. Upper levels pool the stored level below with the same rule and
+  the same reference queries.
+* estimated mass: softmax over the current frontier of sigma * q . X, sigma =
+  1/sqrt(d) (renormalised at every level); the same top-p rule is applied at
+  every level to the children of the nodes kept one level up.
+* order: score descending, ties by ascending node index; "covering" means the
+  cumulative mass reaches p (>=); p >= 1 keeps every node.
+* anchor: tokens 0 .. anchor-1 are added after the selection (anchor = 1 is the
+  page's rule); they take no part in the mass.
+* final attention: exact softmax attention at scale sigma over the gathered keys.
+
+Precision: inputs are upcast exactly to float64 and every sum is float64. The
+method stores two float32 quantities that decide integers downstream, and the
+oracle rounds at exactly those points: the summary pyramid (stored float32) and
+the node scores (float32, so the selection decision is taken on float32 scores
+as the GPU path takes it). Masses are exp(s - max s) of those float32 scores,
+evaluated in float64; cumulative masses are float64.
+
+Pins (tests marked "not gpu"): dense attention through torch's SDPA at p = 1
+and for a one-level tree with one node; closed forms of the pooling rule
+(R = 0 gives the mean, identical children, one-hot softmax, two-way split,
+permutation invariance, convexity); subtree coverage of b^L tokens; token 0
+always kept; a brute-force minimal-set search over every subset of small
+frontiers; score-scale and cut-condition closed forms. The pooling rule and the
+per-level renormalisation are readings the pages do not fix: the oracle is
+pinned to those readings, not to the pages ("parity unpinned by the pages" for
+those two choices; everything else about them is pinned by the tests above).
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+N_REF = 16           # reference queries per KV head (page 3, paragraph 1)
+NEAR_TIE_REL = 1e-5  # relative score gap / mass gap under which a decision is fragile
+
+
+def sigma(d: int) -> float:
+    """Scale of scaled dot-product attention, 1/sqrt(d), used both for node
+    scores and for the final attention (reading of page 3, paragraph 1)."""
+    return 1.0 / np.sqrt(float(d))
+
+
+# ---------------------------------------------------------------------------
+# Build: the summary-key pyramid (page 3, paragraph 1: contiguous blocks, one
+# summary key per block from 16 reference queries, grouped level by level).
+# ---------------------------------------------------------------------------
+
+def pool(children: np.ndarray, R: np.ndarray, tau: float) -> np.ndarray:
+    """One summary key per node from its children.
+
+    children: [n, b, d] float64, R: [16, d] float64 -> [n, d] float64.
+    For each reference query r and child c: z[r, c] = tau * R[r] . x[c];
+    a[r, :] = softmax over the b children; w[c] = mean over r of a[r, c];
+    summary = sum_c w[c] * x[c].
+    """
+    n, b, d = children.shape
+    z = tau * (children.reshape(n * b, d) @ R.T).reshape(n, b, R.shape[0])   # [n, b, 16]
+    z = z - z.max(axis=1, keepdims=True)
+    a = np.exp(z)
+    a = a / a.sum(axis=1, keepdims=True)        # softmax over children, per reference query
+    w = a.mean(axis=2)                          # [n, b]: average over reference queries
+    return np.einsum("nb,nbd->nd", w, children)
+
+
+def build_tree_unit(K_u: np.ndarray, R_g: np.ndarray, b: int, L: int) -> list:
+    """Pyramid of one (sequence, KV head): levels[l] is the float32 [N / b^l, d]
+    array of level-l summary keys for l = 1..L (levels[0] is the raw keys).
+
+    The node count at every level must be a whole number (N % b^L == 0)."""
+    N, d = K_u.shape
+    if b < 2 or L < 1 or N % (b ** L) != 0:
+        raise ValueError("need b >= 2, L >= 1 and N divisible by b^L")
+    tau = sigma(d)
+    R64 = np.asarray(R_g, np.float64)
+    levels = [np.asarray(K_u, np.float32)]
+    X = np.asarray(K_u, np.float64)
+    for _ in range(L):
+        n = X.shape[0] // b
+        Xn = pool(X.reshape(n, b, d), R64, tau).astype(np.float32)   # stored float32
+        levels.append(Xn)
+        X = Xn.astype(np.float64)
+    return levels
+
+
+def build_tree(K: np.ndarray, R: np.ndarray, b: int, L: int) -> list:
+    """Pyramid for K [B, Hkv, N, d] and R [Hkv, 16, d]: levels[l] is
+    [B, Hkv, N / b^l, d] float32 for l = 1..L; levels[0] is None."""
+    B, H, N, d = K.shape
+    out = [None] + [np.empty((B, H, N // b ** l, d), np.float32) for l in range(1, L + 1)]
+    for bi in range(B):
+        for g in range(H):
+            lv = build_tree_unit(K[bi, g], R[g], b, L)
+            for l in range(1, L + 1):
+                out[l][bi, g] = lv[l]
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Search: score, top-p, expand (page 3, paragraph 1).
+# ---------------------------------------------------------------------------
+
+def node_scores(X_rows: np.ndarray, q: np.ndarray) -> np.ndarray:
+    """sigma * q . X for each row, evaluated in float64, stored float32."""
+    d = X_rows.shape[1]
+    return (sigma(d) * (np.asarray(X_rows, np.float64) @ np.asarray(q, np.float64))).astype(np.float32)
+
+
+@dataclass
+class LevelDecision:
+    level: int
+    frontier: np.ndarray          # node ids, ascending
+    scores: np.ndarray            # float32, aligned with frontier
+    kept: np.ndarray              # node ids, ascending
+    fragile: list = field(default_factory=list)   # [(kind, gap)]
+
+
+def select_top_p(F: np.ndarray, s: np.ndarray, p: float):
+    """Smallest set of frontier nodes whose estimated mass reaches p.
+
+    Mass of node c = exp(s_c - max s) / sum over the frontier (softmax over the
+    frontier). Nodes are taken in order of descending score, ties by ascending
+    node id, until the cumulative mass is >= p. p >= 1 keeps every node.
+    Returns (kept ids ascending, fragility list). A decision is fragile when the
+    last kept and first dropped scores are within NEAR_TIE_REL (relative, floor
+    1), or when a cumulative mass at the cut is within NEAR_TIE_REL of p.
+    """
+    F = np.asarray(F, np.int64)
+    s = np.asarray(s, np.float32)
+    if p >= 1.0:
+        return F.copy(), []
+    s64 = s.astype(np.float64)
+    order = np.lexsort((F, -s64))                 # score descending, then id ascending
+    e = np.exp(s64 - s64.max())
+    C = np.cumsum(e[order]) / e.sum()
+    hit = np.nonzero(C >= p)[0]
+    k = int(hit[0]) + 1 if hit.size else F.size
+    fragile = []
+    if k < F.size:
+        a, c = s64[order[k - 1]], s64[order[k]]
+        gap = a - c
+        if gap <= NEAR_TIE_REL * max(1.0, abs(a), abs(c)):
+            fragile.append(("score", float(gap)))
+        if C[k - 1] - p <= NEAR_TIE_REL:
+            fragile.append(("mass_hi", float(C[k - 1] - p)))
+    if k >= 2 and p - C[k - 2] <= NEAR_TIE_REL:
+        fragile.append(("mass_lo", float(p - C[k - 2])))
+    return np.sort(F[order[:k]]), fragile
+
+
+def expand(kept: np.ndarray, b: int) -> np.ndarray:
+    """Children of the kept nodes, ascending: {c * b + i : c in kept, i < b}."""
+    kept = np.asarray(kept, np.int64)
+    return (kept[:, None] * b + np.arange(b, dtype=np.int64)[None, :]).reshape(-1)
+
+
+@dataclass
+class HeadResult:
+    O: np.ndarray                 # [d] float64
+    S: np.ndarray                 # selected token ids, ascending, unique
+    levels: list                  # LevelDecision for l = L .. 1
+
+    @property
+    def fragile(self) -> list:
+        return [(lv.level, kind, gap) for lv in self.levels for kind, gap in lv.fragile]
+
+
+def search(q: np.ndarray, levels: list, b: int, L: int, p: float, anchor: int):
+    """Tree descent for one query head over one (sequence, KV head) pyramid.
+    Returns (S, [LevelDecision for l = L .. 1])."""
+    N = levels[0].shape[0]
+    p = float(np.float32(p))          # p is a float32 argument on the C boundary
+    F = np.arange(levels[L].shape[0], dtype=np.int64)
+    decisions = []
+    kept = F
+    for l in range(L, 0, -1):
+        s = node_scores(levels[l][F], q)
+        kept, fragile = select_top_p(F, s, p)
+        decisions.append(LevelDecision(l, F, s, kept, fragile))
+        if l > 1:
+            F = expand(kept, b)
+    S = np.union1d(np.arange(min(anchor, N), dtype=np.int64), expand(kept, b))
+    return S, decisions
+
+
+def attention_over(q: np.ndarray, K_u: np.ndarray, V_u: np.ndarray, S: np.ndarray) -> np.ndarray:
+    """Exact softmax attention of q over the keys/values with ids in S
+    (scale sigma), float64."""
+    d = K_u.shape[1]
+    lam = sigma(d) * (np.asarray(K_u[S], np.float64) @ np.asarray(q, np.float64))
+    w = np.exp(lam - lam.max())
+    w = w / w.sum()
+    return w @ np.asarray(V_u[S], np.float64)
+
+
+def attend_head(q, levels, K_u, V_u, b, L, p, anchor=1) -> HeadResult:
+    S, decisions = search(q, levels, b, L, p, anchor)
+    return HeadResult(attention_over(q, K_u, V_u, S), S, decisions)
+
+
+def attend(Q, K, V, tree, b, L, p, anchor=1):
+    """Every query head: Q [B, T, Hq, d]; K, V [B, Hkv, N, d]; tree from
+    build_tree. Returns a nested list res[b][t][h] of HeadResult."""
+    B, T, Hq, _ = Q.shape
+    Hkv = K.shape[1]
+    G = Hq // Hkv
+    out = []
+    for bi in range(B):
+        rows = []
+        for t in range(T):
+            row = []
+            for h in range(Hq):
+                g = h // G
+                levels = [K[bi, g]] + [tree[l][bi, g] for l in range(1, L + 1)]
+                row.append(attend_head(Q[bi, t, h], levels, K[bi, g], V[bi, g], b, L, p, anchor))
+            rows.append(row)
+        out.append(rows)
+    return out
