@@ -1,0 +1,146 @@
+/*
+ * zha.h -- C ABI of the MI355X (gfx950) tree-indexed sparse decode attention library.
+ *
+ * Method: Zyphra Hierarchical Attention's tree-indexed sparse attention, as stated in
+ * "Zyphra présente Zyphra Hierarchical Attention (ZHA), une voie vers une attention
+ * vraiment sous-quadratique" (Le Fil IA, from MarkTechPost), paragraph 1: the full KV
+ * cache is kept; keys are cut into contiguous blocks of b, each summarised by one
+ * summary key obtained from 16 reference queries; summaries are grouped level by level
+ * (b = 4 with 6 levels gives top nodes of 4,096 tokens); a decoding query scores the top
+ * nodes, keeps the smallest set covering a fraction p of the estimated attention mass,
+ * expands only those branches down to raw keys, always keeps the first token, and
+ * attention runs over the gathered keys. Paragraph 2 of the same page fixes p = 0.95 and
+ * the deep (b = 4, L = 6) and wide (b = 256, L = 1) geometries.
+ *
+ * Conventions shared by every entry point:
+ *   - Every pointer argument named as "device" is HIP device memory owned by the caller.
+ *     The library allocates nothing and keeps no state beyond a thread-local error string.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream). Entry points
+ *     only enqueue work on it and never synchronise; device faults surface at the
+ *     caller's next synchronisation.
+ *   - Every argument check happens on the host before anything is enqueued; a negative
+ *     zha_status is returned and zha_last_error() describes the problem.
+ *   - Shapes are row-major. A KV cache is [B][Hkv][N_cap][d]: N_cap is its allocated
+ *     length, and tokens [0, N) are in use.
+ *   - Supported: d in {64, 128}; dtype ZHA_F32 or ZHA_BF16 (K, V, Q and the reference
+ *     queries share one dtype); b >= 2; 1 <= L <= ZHA_MAX_LEVELS; N % b^L == 0;
+ *     Hq % Hkv == 0 and Hq / Hkv <= 16; N / b <= 2^21.
+ */
+#ifndef ZHA_H_
+#define ZHA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ZHA_OK = 0,
+  ZHA_ERR_INVALID_ARG = -1, /* null pointer, p not in (0, 1], anchor out of range, b < 2, L < 1 */
+  ZHA_ERR_SHAPE = -2,       /* N % b^L != 0, Hq % Hkv != 0, N > N_cap, buffer too small */
+  ZHA_ERR_DTYPE = -3,       /* unknown dtype */
+  ZHA_ERR_CAPACITY = -4,    /* selected-list capacity smaller than N */
+  ZHA_ERR_UNSUPPORTED = -5, /* d not in {64, 128}, Hq / Hkv > 16, L > ZHA_MAX_LEVELS, N / b > 2^21 */
+  ZHA_ERR_HIP = -6          /* a HIP call or kernel launch failed */
+} zha_status;
+
+typedef enum { ZHA_F32 = 0, ZHA_BF16 = 1 } zha_dtype;
+
+#define ZHA_MAX_LEVELS 12
+#define ZHA_N_REF 16 /* reference queries per KV head (page 3, paragraph 1) */
+
+/*
+ * Summary-key pyramid: a plain view of caller-owned device memory; nothing to free.
+ * Level l (1..L) holds float32 summary keys [B][Hkv][N_cap / b^l][d] starting at
+ * pyramid + level_off[l] (float elements). Node j of level l covers tokens
+ * [j * b^l, (j + 1) * b^l). Levels are written by zha_build_tree / zha_tree_append.
+ */
+typedef struct {
+  int32_t B, Hkv, N, N_cap, d, b, L;
+  int32_t dtype;                              /* zha_dtype of the keys it was built from */
+  int64_t level_off[ZHA_MAX_LEVELS + 1];      /* float offset of level l; [0] unused (= 0) */
+  float* pyramid;                             /* device */
+} zha_tree;
+
+/* Bytes of pyramid storage for a cache of capacity N_cap (0 if the geometry is invalid). */
+size_t zha_tree_bytes(int B, int Hkv, int N_cap, int d, int b, int L);
+
+/*
+ * Build the pyramid over tokens [0, N) (page 3, paragraph 1: contiguous blocks of b, one
+ * summary key per block from 16 reference queries, grouped level by level).
+ *   K            device, dtype, [B][Hkv][N_cap][d]
+ *   ref_queries  device, dtype, [Hkv][16][d]: one set per KV head, shared by all levels
+ *   pyramid      device, at least zha_tree_bytes(B, Hkv, N_cap, d, b, L) bytes
+ *   out          host; receives the view (N set to N)
+ * Pooling: for each node, reference query r attends over the node's b children at scale
+ * 1/sqrt(d); the 16 attention outputs are averaged into the node's summary key (a convex
+ * combination of the children). Upper levels pool the stored level below the same way.
+ * Summaries are float32 at every level.
+ */
+int zha_build_tree(const void* K, const void* ref_queries, int dtype, int B, int Hkv, int N,
+                   int N_cap, int d, int b, int L, void* pyramid, size_t pyramid_bytes,
+                   zha_tree* out, void* stream);
+
+/*
+ * Extend a tree by whole top nodes: pools tokens [t->N, t->N + n_new) at every level and
+ * then sets t->N += n_new. n_new % b^L == 0 and t->N + n_new <= t->N_cap. K and
+ * ref_queries as for zha_build_tree (same cache, same reference queries).
+ */
+int zha_tree_append(zha_tree* t, const void* K, const void* ref_queries, int n_new, void* stream);
+
+/* Workspace bytes zha_attend needs for this tree and query shape (0 if invalid). */
+size_t zha_attend_workspace_bytes(const zha_tree* t, int T, int Hq);
+
+/*
+ * Tree-indexed sparse decode attention (page 3, paragraph 1).
+ *   t          tree built over the same K (its dtype, B, Hkv, N, N_cap, d)
+ *   Q          device, dtype, [B][T][Hq][d]: T decode queries per sequence; query head h
+ *              reads KV head h / (Hq / Hkv)
+ *   K, V       device, dtype, [B][Hkv][N_cap][d]
+ *   p          fraction of estimated attention mass to cover, in (0, 1]; p = 1 keeps all
+ *   anchor     number of leading tokens always kept (the page's rule is 1; 0 disables),
+ *              0 <= anchor <= N; added after the selection, outside the mass
+ *   O          device, float32, [B][T][Hq][d]
+ *   sel_idx    device, int32, [B][T][Hq][cap] or NULL: ascending selected token ids;
+ *              entries past sel_count are left untouched
+ *   cap        row length of sel_idx; must be >= N when sel_idx is not NULL
+ *   sel_count  device, int32, [B][T][Hq]: number of selected tokens per query head
+ *   workspace  device, at least zha_attend_workspace_bytes(t, T, Hq) bytes; its contents
+ *              need no initialisation and are overwritten
+ * Per query head: the top level's nodes form the first frontier; at each level the node
+ * scores are sigma * q . X (sigma = 1/sqrt(d)), the estimated mass is their softmax over
+ * the frontier, and the kept set is the shortest prefix of the frontier in order of
+ * descending score (ties: lower node id first) whose mass reaches p; the next frontier
+ * is the children of the kept nodes. The selected tokens are the b tokens of every kept
+ * level-1 node plus tokens [0, anchor). O is exact softmax attention at scale sigma over
+ * them, accumulated in float32. Calls that share a workspace must not overlap.
+ */
+int zha_attend(const zha_tree* t, const void* Q, int T, int Hq, const void* K, const void* V,
+               float p, int anchor, float* O, int32_t* sel_idx, int64_t cap,
+               int32_t* sel_count, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Diagnostics of the last zha_attend that used `workspace` (valid once it completed).
+ * The G = Hq / Hkv heads of one KV head (and up to 16 / G queries of one sequence) form a
+ * "unit" that shares one union list per level: unit u = ((b * Hkv + g) * nTB + tb), with
+ * Tb = min(T, 16 / G) queries per unit, nTB = ceil(T / Tb); member m = (t % Tb) * G + h % G.
+ * For level l in 1..L this reports byte offsets into the workspace of:
+ *   nodes  uint32 [U][stride]: ascending ids of the level-l nodes kept by any member
+ *   masks  uint32 [U][stride]: bit m set when member m kept that node
+ *   count  uint32 [U]:         number of valid entries per unit
+ * and the number of units U and members per unit bound Tb * G through *units / *stride.
+ */
+int zha_attend_level_view(const zha_tree* t, int T, int Hq, int level, int64_t* off_nodes,
+                          int64_t* off_masks, int64_t* off_count, int64_t* stride,
+                          int64_t* units);
+
+/* Thread-local description of the last failing call on this thread ("" if none). */
+const char* zha_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ZHA_H_ */

@@ -1,0 +1,69 @@
+"""Run the HIP path on a seeded workload and compare it with the oracle (tests only)."""
+
+from __future__ import annotations
+
+import os
+import sys
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import oracle as O  # noqa: E402
+from oracle import compare as C  # noqa: E402
+import tree_indexed_sparse_amd as Z  # noqa: E402
+import workloads as W  # noqa: E402
+
+
+def run_gpu(spec, p, anchor=1, inputs=None, want_lists=True, tree=None, device="cuda"):
+    inp = inputs if inputs is not None else W.gen_all(spec, device=device)
+    if tree is None:
+        tree = Z.build_tree(inp["K"], inp["R"], spec["b"], spec["L"])
+    O_, sel, cnt = Z.attend(inp["Q"], inp["K"], inp["V"], tree, p, anchor, want_lists=want_lists)
+    ws = Z.attend.last_workspace
+    torch.cuda.synchronize()
+    T, Hq = spec["T"], spec["Hq"]
+    lists = {l: Z.level_view(tree, T, Hq, l, ws) for l in range(1, spec["L"] + 1)}
+    return dict(tree=tree, O=O_.cpu().numpy(), sel=None if sel is None else sel.cpu().numpy(),
+                cnt=cnt.cpu().numpy(), lists=lists, inputs=inp)
+
+
+def oracle_unit(spec, b, g, Q=None, R=None):
+    Q = W.gen_Q(spec) if Q is None else Q
+    R = W.gen_R(spec) if R is None else R
+    K_u, V_u = W.gen_KV_unit(spec, b, g, Q)
+    levels = O.build_tree_unit(K_u, R[g], spec["b"], spec["L"])
+    return K_u, V_u, levels
+
+
+def check_units(spec, res, p, anchor=1, units=None, check_pyramid=True, oracle_levels=None):
+    """Guided comparison of every query head of the given (sequence, KV head) units.
+    Returns (list of HeadReport, max pyramid relative error)."""
+    B, T, Hq, Hkv = spec["B"], spec["T"], spec["Hq"], spec["Hkv"]
+    G = Hq // Hkv
+    Q = W.gen_Q(spec)
+    R = W.gen_R(spec)
+    units = [(b, g) for b in range(B) for g in range(Hkv)] if units is None else units
+    reports, pyr_err = [], 0.0
+    for (b, g) in units:
+        if oracle_levels is not None:
+            K_u, V_u = W.gen_KV_unit(spec, b, g, Q)
+            levels = oracle_levels[(b, g)]
+        else:
+            K_u, V_u, levels = oracle_unit(spec, b, g, Q, R)
+        if check_pyramid:
+            for l in range(1, spec["L"] + 1):
+                n = spec["N"] // spec["b"] ** l
+                gl = Z.pyramid_level(res["tree"], l)[b, g, :n].cpu().numpy()
+                pyr_err = max(pyr_err, C.pyramid_rel_err(gl, levels[l]))
+        for t in range(T):
+            for h in range(g * G, (g + 1) * G):
+                u, m = C.unit_member(b, t, h, T, Hq, Hkv)
+                sel_row = None if res["sel"] is None else res["sel"][b, t, h]
+                reports.append(C.check_head(Q[b, t, h], levels, K_u, V_u, spec["b"], spec["L"], p,
+                                            anchor, res["lists"], u, m, sel_row,
+                                            res["cnt"][b, t, h], res["O"][b, t, h], qh=(b, t, h)))
+    return reports, pyr_err

@@ -1,0 +1,135 @@
+"""The C-ABI library without a GPU: it loads, exports every declared entry point, and
+rejects bad arguments on the host before enqueueing anything."""
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from tree_indexed_sparse_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "zha.h")
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(L.LIB_PATH):
+        pytest.skip("libzha.so not built")
+    return L.load()
+
+
+def test_every_declared_function_is_exported(lib):
+    text = open(HEADER).read()
+    declared = set(re.findall(r"\b(zha_[a-z_]+)\s*\(", text))
+    assert declared == set(L.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name)
+
+
+def test_tree_bytes_closed_form(lib):
+    # levels of B*Hkv*(N/b^l)*d float32, each rounded up to 256 bytes
+    def want(B, H, N, d, b, Ll):
+        tot = 0
+        for l in range(1, Ll + 1):
+            tot += 4 * B * H * (N // b ** l) * d
+            tot = (tot + 255) // 256 * 256
+        return tot
+    assert lib.zha_tree_bytes(4, 4, 262144, 128, 4, 6) == want(4, 4, 262144, 128, 4, 6)
+    assert lib.zha_tree_bytes(1, 1, 4096, 64, 4, 3) == want(1, 1, 4096, 64, 4, 3)
+    assert lib.zha_tree_bytes(4, 4, 262144, 128, 256, 1) == 4 * 16 * 1024 * 128
+    assert lib.zha_tree_bytes(1, 1, 4096, 96, 4, 3) == 0      # d unsupported
+    assert lib.zha_tree_bytes(1, 1, 4000, 64, 4, 3) == 0      # not a multiple of b^L
+    assert lib.zha_tree_bytes(1, 1, 4096, 64, 1, 3) == 0      # b < 2
+
+
+def _build(lib, **kw):
+    a = dict(K=FAKE, R=FAKE, dtype=1, B=1, Hkv=1, N=4096, N_cap=4096, d=64, b=4, L=3,
+             pyr=FAKE, nbytes=1 << 30)
+    a.update(kw)
+    t = L.ZhaTree()
+    return lib.zha_build_tree(a["K"], a["R"], a["dtype"], a["B"], a["Hkv"], a["N"], a["N_cap"],
+                              a["d"], a["b"], a["L"], a["pyr"], a["nbytes"], ctypes.byref(t), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(K=None), -1), (dict(R=None), -1), (dict(pyr=None), -1),
+    (dict(dtype=7), -3), (dict(d=96), -5), (dict(b=1), -1), (dict(L=0), -1), (dict(L=13), -5),
+    (dict(N=4000), -2), (dict(N_cap=4000, N=0), -2), (dict(N=8192), -2), (dict(nbytes=1024), -2),
+    (dict(B=0), -2), (dict(N_cap=4 * 2 ** 22, N=64, b=4, L=3), -5),
+])
+def test_build_rejects_bad_arguments(lib, kw, code):
+    assert _build(lib, **kw) == code
+    assert len(lib.zha_last_error()) > 0
+
+
+def _tree(**kw):
+    t = L.ZhaTree()
+    a = dict(B=1, Hkv=2, N=4096, N_cap=4096, d=64, b=4, L=3, dtype=1)
+    a.update(kw)
+    for k, v in a.items():
+        setattr(t, k, v)
+    t.pyramid = 0x2000
+    return t
+
+
+def _attend(lib, t=None, **kw):
+    t = _tree() if t is None else t
+    a = dict(Q=FAKE, T=1, Hq=8, K=FAKE, V=FAKE, p=0.95, anchor=1, O=FAKE, sel=FAKE, cap=4096,
+             cnt=FAKE, ws=FAKE, wsb=1 << 40)
+    a.update(kw)
+    return lib.zha_attend(ctypes.byref(t), a["Q"], a["T"], a["Hq"], a["K"], a["V"], a["p"],
+                          a["anchor"], a["O"], a["sel"], a["cap"], a["cnt"], a["ws"], a["wsb"],
+                          None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Q=None), -1), (dict(K=None), -1), (dict(V=None), -1), (dict(O=None), -1),
+    (dict(cnt=None), -1), (dict(ws=None), -1),
+    (dict(p=0.0), -1), (dict(p=-0.5), -1), (dict(p=1.5), -1), (dict(p=math.nan), -1),
+    (dict(anchor=-1), -1), (dict(anchor=4097), -1),
+    (dict(cap=4095), -4), (dict(Hq=7), -2), (dict(Hq=64), -5), (dict(T=0), -2),
+    (dict(wsb=1024), -2),
+])
+def test_attend_rejects_bad_arguments(lib, kw, code):
+    assert _attend(lib, **kw) == code
+    assert len(lib.zha_last_error()) > 0
+
+
+def test_attend_rejects_bad_trees(lib):
+    assert _attend(lib, t=_tree(d=80)) == -5
+    assert _attend(lib, t=_tree(N=4000)) == -2
+    assert _attend(lib, t=_tree(dtype=3)) == -3
+    assert _attend(lib, t=_tree(N=0)) == -2
+    t = _tree()
+    t.pyramid = None
+    assert _attend(lib, t=t) == -1
+    assert lib.zha_attend(None, FAKE, 1, 8, FAKE, FAKE, 0.9, 1, FAKE, FAKE, 4096, FAKE, FAKE,
+                          1 << 40, None) == -1
+
+
+def test_workspace_size_grows_with_queries_and_is_zero_when_invalid(lib):
+    t = _tree()
+    a = lib.zha_attend_workspace_bytes(ctypes.byref(t), 1, 8)
+    b = lib.zha_attend_workspace_bytes(ctypes.byref(t), 4, 8)
+    assert 0 < a < b
+    assert lib.zha_attend_workspace_bytes(ctypes.byref(t), 1, 7) == 0
+    assert lib.zha_attend_workspace_bytes(ctypes.byref(_tree(N=0)), 1, 8) == 0
+
+
+def test_level_view_offsets_are_inside_the_workspace(lib):
+    t = _tree()
+    need = lib.zha_attend_workspace_bytes(ctypes.byref(t), 3, 8)
+    vals = [ctypes.c_int64() for _ in range(5)]
+    for level in (1, 2, 3):
+        assert lib.zha_attend_level_view(ctypes.byref(t), 3, 8, level,
+                                         *[ctypes.byref(v) for v in vals]) == 0
+        o_n, o_m, o_c, stride, units = (v.value for v in vals)
+        assert stride == 4096 // 4 ** level
+        assert units == 1 * 2 * 1           # Tb = min(3, 16 / 4) = 3 queries per unit
+        assert max(o_n, o_m) + 4 * units * stride <= need and o_c + 4 * units <= need
+    assert lib.zha_attend_level_view(ctypes.byref(t), 3, 8, 4,
+                                     *[ctypes.byref(v) for v in vals]) == -1

@@ -1,0 +1,198 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bars: selected sets exact at every non-fragile decision (near-ties follow the rule in
+oracle/compare.py), token lists exact, O within max-abs 1e-4 (fp32 inputs) or 2e-2 (bf16
+inputs, unit-scale V), pyramid within 1e-5 relative to each level's largest magnitude.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import gpu_harness as H
+import workloads as W
+from oracle import compare as C
+
+pytestmark = pytest.mark.gpu
+
+O_TOL = {"f32": 1e-4, "bf16": 2e-2}
+PYR_TOL = 1e-5
+
+
+def _report(name, summ, pyr):
+    print(f"[{name}] pyramid {pyr:.2e} {summ}", flush=True)
+
+
+def _assert_ok(spec, summ, pyr):
+    assert summ["mismatches"] == 0, summ["first_mismatch"]
+    assert summ["max_o_err"] <= O_TOL[spec["dtype"]], summ["max_o_err"]
+    assert pyr <= PYR_TOL, pyr
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import tree_indexed_sparse_amd as Z
+    Z.load()
+
+
+@pytest.mark.parametrize("p", [0.95, 0.5, 0.8])
+def test_tiny_fp32(p):
+    spec = W.spec("tiny")
+    res = H.run_gpu(spec, p)
+    reps, pyr = H.check_units(spec, res, p)
+    summ = C.summarize(reps)
+    _report(f"tiny p={p}", summ, pyr)
+    _assert_ok(spec, summ, pyr)
+
+
+def test_tiny_search_on_oracle_pyramid():
+    """Feed the oracle's own pyramid, so scores differ only by dot-product rounding."""
+    import tree_indexed_sparse_amd as Z
+
+    spec = W.spec("tiny")
+    inp = W.gen_all(spec, device="cuda")
+    tree = Z.build_tree(inp["K"], inp["R"], spec["b"], spec["L"])
+    _, _, levels = H.oracle_unit(spec, 0, 0)
+    for l in range(1, spec["L"] + 1):
+        Z.pyramid_level(tree, l)[0, 0].copy_(torch.from_numpy(levels[l]))
+    res = H.run_gpu(spec, 0.95, inputs=inp, tree=tree)
+    reps, pyr = H.check_units(spec, res, 0.95, oracle_levels={(0, 0): levels})
+    summ = C.summarize(reps)
+    _report("tiny on oracle pyramid", summ, pyr)
+    _assert_ok(spec, summ, pyr)
+
+
+def test_32k_deep_all_heads():
+    spec = W.spec("32k_deep")
+    res = H.run_gpu(spec, 0.95)
+    reps, pyr = H.check_units(spec, res, 0.95)
+    summ = C.summarize(reps)
+    _report("32k deep", summ, pyr)
+    _assert_ok(spec, summ, pyr)
+    kr = np.array([r.keys for r in reps]) / spec["N"]
+    print(f"[32k deep] keys read mean {100 * kr.mean():.1f}%", flush=True)
+
+
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 128)])
+def test_p_one_keeps_every_token(dtype, d):
+    spec = W.spec("32k_deep", dtype=dtype, d=d, N=4096, B=2, Hq=8, Hkv=2, L=3,
+                  r_std=1.0 / np.sqrt(d))
+    res = H.run_gpu(spec, 1.0)
+    assert np.all(res["cnt"] == spec["N"])
+    assert np.array_equal(res["sel"][0, 0, 0], np.arange(spec["N"]))
+    reps, pyr = H.check_units(spec, res, 1.0)
+    summ = C.summarize(reps)
+    _report(f"p=1 {dtype}", summ, pyr)
+    _assert_ok(spec, summ, pyr)
+
+
+@pytest.mark.parametrize("dtype,d,N", [("f32", 64, 4096), ("bf16", 128, 1024)])
+def test_one_level_block_n_is_dense(dtype, d, N):
+    spec = W.spec("tiny", dtype=dtype, d=d, N=N, b=N, L=1, T=4, needles="none")
+    res = H.run_gpu(spec, 0.5)
+    assert np.all(res["cnt"] == N)
+    reps, pyr = H.check_units(spec, res, 0.5)
+    summ = C.summarize(reps)
+    _report(f"block=N {dtype}", summ, pyr)
+    _assert_ok(spec, summ, pyr)
+
+
+@pytest.mark.parametrize("p", [0.8, 0.95, 0.99])
+def test_wide_tree(p):
+    spec = W.spec("256k_wide", N=16384, B=2)
+    res = H.run_gpu(spec, p)
+    reps, pyr = H.check_units(spec, res, p)
+    summ = C.summarize(reps)
+    _report(f"wide N=16384 p={p}", summ, pyr)
+    _assert_ok(spec, summ, pyr)
+
+
+@pytest.mark.parametrize("case", [
+    dict(name="anchor0", anchor=0),
+    dict(name="anchor3", anchor=3),
+    dict(name="anchor=b+1", anchor=5),
+    dict(name="one top node", N=64, L=3),
+    dict(name="T3 G4", T=3, Hq=8, Hkv=2),
+    dict(name="T5 G2 two blocks", T=5, Hq=4, Hkv=2),
+    dict(name="G16", Hq=16, Hkv=1),
+    dict(name="b2 L5", b=2, L=5, N=2048),
+    dict(name="b8 L2", b=8, L=2, N=4096),
+    dict(name="sharp pooling", r_std=1.0),
+])
+def test_edge_cases(case):
+    case = dict(case)
+    name = case.pop("name")
+    anchor = case.pop("anchor", 1)
+    spec = W.spec("tiny", **case)
+    res = H.run_gpu(spec, 0.9, anchor=anchor)
+    reps, pyr = H.check_units(spec, res, 0.9, anchor=anchor)
+    summ = C.summarize(reps)
+    _report(name, summ, pyr)
+    _assert_ok(spec, summ, pyr)
+
+
+def test_bf16_d64_and_multi_sequence():
+    spec = W.spec("32k_deep", d=64, N=8192, B=3, Hq=8, Hkv=2, L=4, r_std=0.125)
+    res = H.run_gpu(spec, 0.95)
+    reps, pyr = H.check_units(spec, res, 0.95)
+    summ = C.summarize(reps)
+    _report("bf16 d64", summ, pyr)
+    _assert_ok(spec, summ, pyr)
+
+
+def test_exact_ties_broken_by_lowest_index():
+    """Identical keys everywhere: every score at every level ties. The cut must keep the
+    lowest node ids; the boundary bucket holds 4096 entries, past the sort capacity."""
+    import tree_indexed_sparse_amd as Z
+
+    spec = W.spec("tiny", N=16384, b=4, L=1, T=2, needles="none")
+    inp = W.gen_all(spec, device="cuda")
+    inp["K"][:] = inp["K"][0, 0, 0]
+    res = H.run_gpu(spec, 0.95, inputs=inp)
+    import oracle as O
+    K_u = inp["K"][0, 0].cpu().numpy()
+    V_u = inp["V"][0, 0].cpu().numpy()
+    levels = O.build_tree_unit(K_u, inp["R"][0].cpu().numpy(), 4, 1)
+    for t in range(2):
+        r = O.attend_head(inp["Q"][0, t, 0].cpu().numpy(), levels, K_u, V_u, 4, 1, 0.95, 1)
+        n = int(res["cnt"][0, t, 0])
+        assert np.array_equal(res["sel"][0, t, 0, :n], r.S)
+        assert np.max(np.abs(res["O"][0, t, 0] - r.O)) < 1e-4
+    Z.attend.last_workspace = None
+
+
+def test_deterministic_repeat():
+    spec = W.spec("32k_deep", N=8192, B=2)
+    inp = W.gen_all(spec, device="cuda")
+    a = H.run_gpu(spec, 0.95, inputs=inp)
+    b = H.run_gpu(spec, 0.95, inputs=inp, tree=a["tree"])
+    assert np.array_equal(a["cnt"], b["cnt"])
+    assert np.array_equal(a["sel"], b["sel"])
+    assert np.array_equal(a["O"], b["O"])
+
+
+def test_append_equals_one_shot_build():
+    import tree_indexed_sparse_amd as Z
+
+    spec = W.spec("32k_deep", N=16384, B=2)
+    inp = W.gen_all(spec, device="cuda")
+    full = Z.build_tree(inp["K"], inp["R"], 4, 6)
+    part = Z.build_tree(inp["K"], inp["R"], 4, 6, N=4096)
+    for _ in range(3):
+        Z.tree_append(part, inp["K"], inp["R"], 4096)
+    torch.cuda.synchronize()
+    assert part.N == full.N == 16384
+    for l in range(1, 7):
+        assert torch.equal(Z.pyramid_level(part, l), Z.pyramid_level(full, l))
+
+
+def test_256k_deep_sampled_units():
+    """The benchmark workload at full size; two (sequence, KV head) units checked."""
+    spec = W.spec("256k_deep")
+    res = H.run_gpu(spec, 0.95)
+    reps, pyr = H.check_units(spec, res, 0.95, units=[(0, 0), (3, 3)])
+    summ = C.summarize(reps)
+    _report("256k deep sampled", summ, pyr)
+    _assert_ok(spec, summ, pyr)

@@ -1,0 +1,150 @@
+"""Tree-indexed sparse decode attention (Zyphra Hierarchical Attention) on MI355X.
+
+Python face of the C ABI in include/zha.h. torch supplies device memory and the current
+HIP stream; the pyramid build, the tree search and the sparse decode all run in the
+library's hand-written gfx950 kernels (libzha.so). Names follow the C entry points:
+
+    tree = build_tree(K, R, b, L)             # zha_build_tree
+    tree_append(tree, K, R, n_new)            # zha_tree_append
+    O, sel_idx, sel_count = attend(Q, K, V, tree, p, anchor=1)   # zha_attend
+"""
+
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+
+import torch
+
+from ._lib import ZHA_BF16, ZHA_F32, ZHA_N_REF, ZhaError, ZhaTree, check, load  # noqa: F401
+
+__all__ = ["Tree", "build_tree", "tree_append", "attend", "workspace_bytes", "level_view",
+           "tree_bytes", "pyramid_level", "ZhaError", "load"]
+
+_DTYPES = {torch.float32: ZHA_F32, torch.bfloat16: ZHA_BF16}
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype not in _DTYPES:
+        raise ZhaError(-3, f"unsupported dtype {t.dtype}")
+    return _DTYPES[t.dtype]
+
+
+def _dev(t: torch.Tensor, name: str) -> int:
+    if not t.is_cuda:
+        raise ZhaError(-1, f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ZhaError(-2, f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def tree_bytes(B: int, Hkv: int, N_cap: int, d: int, b: int, L: int) -> int:
+    return int(load().zha_tree_bytes(B, Hkv, N_cap, d, b, L))
+
+
+@dataclass
+class Tree:
+    """A built pyramid: the C view plus the tensor that owns its storage."""
+    c: ZhaTree
+    storage: torch.Tensor
+
+    @property
+    def N(self) -> int:
+        return int(self.c.N)
+
+    @property
+    def b(self) -> int:
+        return int(self.c.b)
+
+    @property
+    def L(self) -> int:
+        return int(self.c.L)
+
+
+def pyramid_level(tree: Tree, level: int) -> torch.Tensor:
+    """Float32 view [B, Hkv, N_cap / b^level, d] of one pyramid level."""
+    c = tree.c
+    n = c.N_cap // c.b ** level
+    numel = c.B * c.Hkv * n * c.d
+    flat = tree.storage.view(torch.float32)
+    off = int(c.level_off[level])
+    return flat[off:off + numel].view(c.B, c.Hkv, n, c.d)
+
+
+def build_tree(K: torch.Tensor, R: torch.Tensor, b: int, L: int, N: int | None = None) -> Tree:
+    """zha_build_tree over tokens [0, N) of the cache K [B, Hkv, N_cap, d]."""
+    lib = load()
+    B, Hkv, N_cap, d = K.shape
+    N = N_cap if N is None else N
+    if R.dtype != K.dtype:
+        raise ZhaError(-3, "K and R must share a dtype")
+    nbytes = tree_bytes(B, Hkv, N_cap, d, b, L)
+    storage = torch.empty(max(nbytes, 4), dtype=torch.uint8, device=K.device)
+    c = ZhaTree()
+    check(lib.zha_build_tree(_dev(K, "K"), _dev(R, "R"), _dt(K), B, Hkv, N, N_cap, d, b, L,
+                             storage.data_ptr(), nbytes, ctypes.byref(c), _stream(K.device)))
+    return Tree(c, storage)
+
+
+def tree_append(tree: Tree, K: torch.Tensor, R: torch.Tensor, n_new: int) -> None:
+    """zha_tree_append: pool tokens [N, N + n_new) and extend the tree."""
+    check(load().zha_tree_append(ctypes.byref(tree.c), _dev(K, "K"), _dev(R, "R"), n_new,
+                                 _stream(K.device)))
+
+
+def workspace_bytes(tree: Tree, T: int, Hq: int) -> int:
+    return int(load().zha_attend_workspace_bytes(ctypes.byref(tree.c), T, Hq))
+
+
+def attend(Q, K, V, tree: Tree, p: float, anchor: int = 1, *, want_lists: bool = True,
+           out=None, sel_idx=None, sel_count=None, workspace=None):
+    """zha_attend. Returns (O [B,T,Hq,d] float32, sel_idx [B,T,Hq,N] int32 or None,
+    sel_count [B,T,Hq] int32). Buffers may be passed in to avoid allocation."""
+    lib = load()
+    B, T, Hq, d = Q.shape
+    dev = Q.device
+    if Q.dtype != K.dtype or V.dtype != K.dtype:
+        raise ZhaError(-3, "Q, K and V must share a dtype")
+    if out is None:
+        out = torch.empty((B, T, Hq, d), dtype=torch.float32, device=dev)
+    cap = tree.N
+    if want_lists and sel_idx is None:
+        sel_idx = torch.empty((B, T, Hq, cap), dtype=torch.int32, device=dev)
+    if sel_idx is not None:
+        cap = sel_idx.shape[-1]
+    if sel_count is None:
+        sel_count = torch.empty((B, T, Hq), dtype=torch.int32, device=dev)
+    need = workspace_bytes(tree, T, Hq)
+    if workspace is None:
+        workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=dev)
+    check(lib.zha_attend(ctypes.byref(tree.c), _dev(Q, "Q"), T, Hq, _dev(K, "K"), _dev(V, "V"),
+                         float(p), int(anchor), _dev(out, "O"),
+                         _dev(sel_idx, "sel_idx") if sel_idx is not None else None, cap,
+                         _dev(sel_count, "sel_count"), _dev(workspace, "workspace"),
+                         workspace.numel(), _stream(dev)))
+    attend.last_workspace = workspace
+    return out, sel_idx, sel_count
+
+
+def level_view(tree: Tree, T: int, Hq: int, level: int, workspace: torch.Tensor):
+    """Per-level union lists a finished zha_attend left in `workspace`:
+    (nodes [U, stride] int64, masks [U, stride] int64, count [U] int64) on the host."""
+    lib = load()
+    o_n, o_m, o_c, st, units = (ctypes.c_int64() for _ in range(5))
+    check(lib.zha_attend_level_view(ctypes.byref(tree.c), T, Hq, level, ctypes.byref(o_n),
+                                    ctypes.byref(o_m), ctypes.byref(o_c), ctypes.byref(st),
+                                    ctypes.byref(units)))
+    U, S = units.value, st.value
+    w = workspace.view(torch.uint8)
+
+    def u32(off, n):
+        return w[off:off + 4 * n].view(torch.int32).cpu().numpy().astype("int64") & 0xFFFFFFFF
+
+    nodes = u32(o_n.value, U * S).reshape(U, S)
+    masks = u32(o_m.value, U * S).reshape(U, S)
+    count = u32(o_c.value, U)
+    return nodes, masks, count

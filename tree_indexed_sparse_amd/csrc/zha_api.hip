@@ -1,0 +1,317 @@
+// Host entry points of the C ABI declared in include/zha.h: argument checks, workspace
+// layout and the launch sequence. Nothing here allocates device memory or synchronises.
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "zha_internal.h"
+
+using namespace zha;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(ZHA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
+
+int64_t ipow(int64_t b, int e) {
+  int64_t r = 1;
+  for (int i = 0; i < e; ++i) r *= b;
+  return r;
+}
+
+// Checks shared by the tree entry points. Returns ZHA_OK or an error code (message set).
+int check_geometry(int B, int Hkv, int N, int N_cap, int d, int b, int L) {
+  if (B < 1 || Hkv < 1) return fail(ZHA_ERR_SHAPE, "B and Hkv must be >= 1 (got %d, %d)", B, Hkv);
+  if (b < 2) return fail(ZHA_ERR_INVALID_ARG, "branching factor b must be >= 2 (got %d)", b);
+  if (L < 1) return fail(ZHA_ERR_INVALID_ARG, "levels L must be >= 1 (got %d)", L);
+  if (L > ZHA_MAX_LEVELS)
+    return fail(ZHA_ERR_UNSUPPORTED, "levels L must be <= %d (got %d)", ZHA_MAX_LEVELS, L);
+  if (d != 64 && d != 128) return fail(ZHA_ERR_UNSUPPORTED, "head dim must be 64 or 128 (got %d)", d);
+  const int64_t top = ipow(b, L);
+  if (top > (int64_t)1 << 31) return fail(ZHA_ERR_SHAPE, "b^L overflows");
+  if (N_cap < 1 || N_cap % top != 0)
+    return fail(ZHA_ERR_SHAPE, "cache capacity N_cap=%d must be a positive multiple of b^L=%lld",
+                N_cap, (long long)top);
+  if (N < 0 || N > N_cap) return fail(ZHA_ERR_SHAPE, "N=%d must lie in [0, N_cap=%d]", N, N_cap);
+  if (N % top != 0)
+    return fail(ZHA_ERR_SHAPE, "N=%d must be a multiple of b^L=%lld", N, (long long)top);
+  if (N_cap / b > (1 << kMaxLog2Nodes))
+    return fail(ZHA_ERR_UNSUPPORTED, "N_cap / b must be <= 2^%d", kMaxLog2Nodes);
+  return ZHA_OK;
+}
+
+// Workspace of zha_attend: every offset is in bytes and 256-byte aligned.
+struct WsLayout {
+  int U, QH, splits;
+  int64_t n[ZHA_MAX_LEVELS + 1];  // nodes per unit at each level (current N)
+  int64_t off_done, off_count, off_lvl, off_S, off_part;
+  int64_t off_nodes[ZHA_MAX_LEVELS + 1], off_masks[ZHA_MAX_LEVELS + 1],
+      off_keep[ZHA_MAX_LEVELS + 1];
+  int64_t S_stride;
+  int64_t total;
+};
+
+int make_geom(const zha_tree* t, int T, int Hq, Geom* g) {
+  if (T < 1 || Hq < 1) return fail(ZHA_ERR_SHAPE, "T and Hq must be >= 1 (got %d, %d)", T, Hq);
+  if (Hq % t->Hkv != 0)
+    return fail(ZHA_ERR_SHAPE, "Hq=%d must be a multiple of Hkv=%d", Hq, t->Hkv);
+  const int G = Hq / t->Hkv;
+  if (G > kMaxMembers)
+    return fail(ZHA_ERR_UNSUPPORTED, "Hq / Hkv = %d exceeds %d", G, kMaxMembers);
+  g->B = t->B;
+  g->T = T;
+  g->Hq = Hq;
+  g->Hkv = t->Hkv;
+  g->G = G;
+  g->Tb = T < kMaxMembers / G ? T : kMaxMembers / G;
+  g->nTB = (T + g->Tb - 1) / g->Tb;
+  g->U = t->B * t->Hkv * g->nTB;
+  g->D = t->d;
+  g->b = t->b;
+  g->L = t->L;
+  g->N = t->N;
+  g->Ncap = t->N_cap;
+  return ZHA_OK;
+}
+
+WsLayout layout_of(const Geom& g) {
+  WsLayout w{};
+  w.U = g.U;
+  w.QH = g.B * g.T * g.Hq;
+  w.splits = (2048 + g.U - 1) / g.U;
+  if (w.splits > 256) w.splits = 256;
+  if (w.splits < 1) w.splits = 1;
+  int64_t nl = g.N;
+  for (int l = 1; l <= g.L; ++l) {
+    nl /= g.b;
+    w.n[l] = nl;
+  }
+  int64_t off = 0;
+  w.off_done = off;
+  off = align256(off + 4 * (int64_t)(g.L + 1) * g.U);
+  w.off_count = off;
+  off = align256(off + 4 * (int64_t)(g.L + 1) * g.U);
+  w.off_lvl = off;
+  off = align256(off + 4 * (int64_t)w.QH * (g.L + 1));
+  for (int l = 1; l <= g.L; ++l) {
+    const int64_t bytes = 4 * (int64_t)g.U * w.n[l];
+    w.off_nodes[l] = off;
+    off = align256(off + bytes);
+    w.off_masks[l] = off;
+    off = align256(off + bytes);
+    w.off_keep[l] = off;
+    off = align256(off + bytes);
+  }
+  w.S_stride = w.n[1];
+  w.off_S = off;
+  off = align256(off + 4 * (int64_t)w.QH * w.S_stride);
+  w.off_part = off;
+  off = align256(off + 4 * (int64_t)g.U * w.splits * kMaxMembers * (g.D + 2));
+  w.total = off;
+  return w;
+}
+
+LevelBufs level_bufs(char* ws, const WsLayout& w, int l) {
+  LevelBufs lb;
+  lb.nodes = (uint32_t*)(ws + w.off_nodes[l]);
+  lb.masks = (uint32_t*)(ws + w.off_masks[l]);
+  lb.keep = (uint32_t*)(ws + w.off_keep[l]);
+  lb.count = (uint32_t*)(ws + w.off_count) + (int64_t)l * w.U;
+  lb.done = (uint32_t*)(ws + w.off_done) + (int64_t)(l - 1) * w.U;
+  lb.stride = w.n[l];
+  return lb;
+}
+
+int check_tree(const zha_tree* t) {
+  if (!t) return fail(ZHA_ERR_INVALID_ARG, "tree is NULL");
+  if (!t->pyramid) return fail(ZHA_ERR_INVALID_ARG, "tree has no pyramid");
+  if (t->dtype != ZHA_F32 && t->dtype != ZHA_BF16)
+    return fail(ZHA_ERR_DTYPE, "unknown dtype %d", t->dtype);
+  return check_geometry(t->B, t->Hkv, t->N, t->N_cap, t->d, t->b, t->L);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* zha_last_error(void) { return g_err.c_str(); }
+
+size_t zha_tree_bytes(int B, int Hkv, int N_cap, int d, int b, int L) {
+  const std::string saved = g_err;
+  const int st = check_geometry(B, Hkv, 0, N_cap, d, b, L);
+  g_err = saved;
+  if (st != ZHA_OK) return 0;
+  int64_t total = 0, nl = N_cap;
+  for (int l = 1; l <= L; ++l) {
+    nl /= b;
+    total = align256(total + 4 * (int64_t)B * Hkv * nl * d);
+  }
+  return (size_t)total;
+}
+
+int zha_tree_append(zha_tree* t, const void* K, const void* R, int n_new, void* stream) {
+  int st = check_tree(t);
+  if (st != ZHA_OK) return st;
+  if (!K || !R) return fail(ZHA_ERR_INVALID_ARG, "K and ref_queries must not be NULL");
+  const int64_t top = ipow(t->b, t->L);
+  if (n_new < 0 || n_new % top != 0)
+    return fail(ZHA_ERR_SHAPE, "n_new=%d must be a non-negative multiple of b^L=%lld", n_new,
+                (long long)top);
+  if ((int64_t)t->N + n_new > t->N_cap)
+    return fail(ZHA_ERR_SHAPE, "N + n_new = %lld exceeds N_cap=%d", (long long)t->N + n_new,
+                t->N_cap);
+  hipStream_t s = (hipStream_t)stream;
+  const int units = t->B * t->Hkv;
+  int64_t cap_prev = t->N_cap, b_l = 1;
+  for (int l = 1; l <= t->L; ++l) {
+    b_l *= t->b;
+    const int64_t cap_l = t->N_cap / b_l;
+    const void* child = (l == 1) ? K : (const void*)(t->pyramid + t->level_off[l - 1]);
+    const int dt_in = (l == 1) ? t->dtype : ZHA_F32;
+    hipError_t e = launch_pool_level(dt_in, child, cap_prev * t->d, R, t->dtype,
+                                     t->pyramid + t->level_off[l], cap_l * t->d, units, t->Hkv,
+                                     (int)(t->N / b_l), (int)((t->N + (int64_t)n_new) / b_l),
+                                     t->b, t->d, s);
+    if (e != hipSuccess) return hip_fail(e, "pooling launch");
+    cap_prev = cap_l;
+  }
+  t->N += n_new;
+  return ZHA_OK;
+}
+
+int zha_build_tree(const void* K, const void* R, int dtype, int B, int Hkv, int N, int N_cap,
+                   int d, int b, int L, void* pyramid, size_t pyramid_bytes, zha_tree* out,
+                   void* stream) {
+  if (!K || !R || !pyramid || !out)
+    return fail(ZHA_ERR_INVALID_ARG, "K, ref_queries, pyramid and out must not be NULL");
+  if (dtype != ZHA_F32 && dtype != ZHA_BF16) return fail(ZHA_ERR_DTYPE, "unknown dtype %d", dtype);
+  int st = check_geometry(B, Hkv, N, N_cap, d, b, L);
+  if (st != ZHA_OK) return st;
+  const size_t need = zha_tree_bytes(B, Hkv, N_cap, d, b, L);
+  if (pyramid_bytes < need)
+    return fail(ZHA_ERR_SHAPE, "pyramid buffer has %zu bytes, needs %zu", pyramid_bytes, need);
+  zha_tree t;
+  memset(&t, 0, sizeof(t));
+  t.B = B;
+  t.Hkv = Hkv;
+  t.N = 0;
+  t.N_cap = N_cap;
+  t.d = d;
+  t.b = b;
+  t.L = L;
+  t.dtype = dtype;
+  t.pyramid = (float*)pyramid;
+  int64_t off = 0, nl = N_cap;
+  for (int l = 1; l <= L; ++l) {
+    nl /= b;
+    t.level_off[l] = off / 4;
+    off = align256(off + 4 * (int64_t)B * Hkv * nl * d);
+  }
+  st = zha_tree_append(&t, K, R, N, stream);
+  if (st != ZHA_OK) return st;
+  *out = t;
+  return ZHA_OK;
+}
+
+size_t zha_attend_workspace_bytes(const zha_tree* t, int T, int Hq) {
+  const std::string saved = g_err;
+  Geom g;
+  int st = check_tree(t);
+  if (st == ZHA_OK) st = make_geom(t, T, Hq, &g);
+  g_err = saved;
+  if (st != ZHA_OK || t->N == 0) return 0;
+  return (size_t)layout_of(g).total;
+}
+
+int zha_attend_level_view(const zha_tree* t, int T, int Hq, int level, int64_t* off_nodes,
+                          int64_t* off_masks, int64_t* off_count, int64_t* stride,
+                          int64_t* units) {
+  int st = check_tree(t);
+  if (st != ZHA_OK) return st;
+  Geom g;
+  st = make_geom(t, T, Hq, &g);
+  if (st != ZHA_OK) return st;
+  if (level < 1 || level > t->L)
+    return fail(ZHA_ERR_INVALID_ARG, "level %d outside [1, %d]", level, t->L);
+  if (!off_nodes || !off_masks || !off_count || !stride || !units)
+    return fail(ZHA_ERR_INVALID_ARG, "output pointers must not be NULL");
+  const WsLayout w = layout_of(g);
+  *off_nodes = w.off_nodes[level];
+  *off_masks = w.off_masks[level];
+  *off_count = w.off_count + 4 * (int64_t)level * w.U;
+  *stride = w.n[level];
+  *units = w.U;
+  return ZHA_OK;
+}
+
+int zha_attend(const zha_tree* t, const void* Q, int T, int Hq, const void* K, const void* V,
+               float p, int anchor, float* O, int32_t* sel_idx, int64_t cap, int32_t* sel_count,
+               void* workspace, size_t ws_bytes, void* stream) {
+  int st = check_tree(t);
+  if (st != ZHA_OK) return st;
+  if (!Q || !K || !V || !O || !sel_count || !workspace)
+    return fail(ZHA_ERR_INVALID_ARG, "Q, K, V, O, sel_count and workspace must not be NULL");
+  if (t->N < 1) return fail(ZHA_ERR_SHAPE, "the tree covers no tokens");
+  if (!(p > 0.0f && p <= 1.0f)) return fail(ZHA_ERR_INVALID_ARG, "p=%g must lie in (0, 1]", (double)p);
+  if (anchor < 0 || anchor > t->N)
+    return fail(ZHA_ERR_INVALID_ARG, "anchor=%d must lie in [0, N=%d]", anchor, t->N);
+  if (sel_idx && cap < t->N)
+    return fail(ZHA_ERR_CAPACITY, "sel_idx row length cap=%lld is smaller than N=%d",
+                (long long)cap, t->N);
+  Geom g;
+  st = make_geom(t, T, Hq, &g);
+  if (st != ZHA_OK) return st;
+  const WsLayout w = layout_of(g);
+  if ((int64_t)ws_bytes < w.total)
+    return fail(ZHA_ERR_SHAPE, "workspace has %zu bytes, needs %lld", ws_bytes,
+                (long long)w.total);
+
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  LevelBufs lv[ZHA_MAX_LEVELS + 2];
+  for (int l = 1; l <= t->L; ++l) lv[l] = level_bufs(ws, w, l);
+  uint32_t* done_dec = (uint32_t*)(ws + w.off_done) + (int64_t)t->L * w.U;
+  float* S = (float*)(ws + w.off_S);
+  int32_t* lvl = (int32_t*)(ws + w.off_lvl);
+
+  hipError_t e = launch_attend_init((uint32_t*)(ws + w.off_done), (t->L + 1) * w.U, s);
+  if (e != hipSuccess) return hip_fail(e, "init launch");
+  int64_t cap_l = t->N_cap;
+  for (int l = 1; l <= t->L; ++l) cap_l /= t->b;  // capacity nodes at the top level
+  for (int l = t->L; l >= 1; --l) {
+    const LevelBufs* parent = (l < t->L) ? &lv[l + 1] : nullptr;
+    const int n_top = (l == t->L) ? (int)w.n[t->L] : 0;
+    const float* X = t->pyramid + t->level_off[l];
+    e = launch_score(g, l, X, cap_l * t->d, Q, t->dtype, parent, n_top, S, w.S_stride, lv[l], s);
+    if (e != hipSuccess) return hip_fail(e, "score launch");
+    e = launch_select(g, l, S, w.S_stride, parent, n_top, lv[l], p, anchor,
+                      l == 1 ? sel_idx : nullptr, cap, sel_count, lvl, s);
+    if (e != hipSuccess) return hip_fail(e, "select launch");
+    cap_l *= t->b;
+  }
+  e = launch_decode(g, t->dtype, K, V, Q, lv[1], anchor, w.splits,
+                    (float*)(ws + w.off_part), done_dec, O, s);
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  return ZHA_OK;
+}
+
+}  // extern "C"

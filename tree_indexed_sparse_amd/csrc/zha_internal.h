@@ -1,0 +1,92 @@
+// Internal definitions shared by the gfx950 kernels and the host entry points.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "zha.h"
+
+namespace zha {
+
+constexpr int kNRef = ZHA_N_REF;   // reference queries per KV head
+constexpr int kMaxMembers = 16;    // query heads (x queries) sharing one union list
+constexpr int kMaxLog2Nodes = 21;  // frontier bound that keeps 2^42-scaled masses in u64
+
+typedef uint16_t bf16_t;
+
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(bf16_t v) { return __uint_as_float(((uint32_t)v) << 16); }
+
+// Decode-call geometry. A unit is (sequence, KV head, block of Tb queries); its members
+// are the Tb * G (query, head) pairs that read that KV head.
+struct Geom {
+  int B, T, Hq, Hkv, G, Tb, nTB, U;
+  int D, b, L, N, Ncap;
+};
+
+__host__ __device__ __forceinline__ int members_of(const Geom& g, int u) {
+  const int tb = u % g.nTB;
+  const int rem = g.T - tb * g.Tb;
+  return (rem < g.Tb ? rem : g.Tb) * g.G;
+}
+
+// query head index qh = (bb * T + t) * Hq + h  <->  (unit, member)
+__host__ __device__ __forceinline__ void unit_member_of(const Geom& g, int qh, int* u, int* m) {
+  const int h = qh % g.Hq;
+  const int t = (qh / g.Hq) % g.T;
+  const int bb = qh / (g.Hq * g.T);
+  const int kv = h / g.G, j = h % g.G;
+  const int tb = t / g.Tb, tl = t % g.Tb;
+  *u = (bb * g.Hkv + kv) * g.nTB + tb;
+  *m = tl * g.G + j;
+}
+
+__host__ __device__ __forceinline__ int qh_of(const Geom& g, int u, int m) {
+  const int tb = u % g.nTB;
+  const int kv = (u / g.nTB) % g.Hkv;
+  const int bb = u / (g.nTB * g.Hkv);
+  const int t = tb * g.Tb + m / g.G;
+  const int h = kv * g.G + m % g.G;
+  return (bb * g.T + t) * g.Hq + h;
+}
+
+// (sequence, KV head) index of a unit: selects the K/V/pyramid slice.
+__host__ __device__ __forceinline__ int bg_of(const Geom& g, int u) { return u / g.nTB; }
+
+// Per-level union lists in the workspace.
+struct LevelBufs {
+  uint32_t* nodes;   // [U][stride] kept node ids (ascending), written by the selector
+  uint32_t* masks;   // [U][stride] member bitmask per kept node
+  uint32_t* count;   // [U]
+  uint32_t* keep;    // [U][stride] member bitmask per frontier entry (frontier index space)
+  uint32_t* done;    // [U] members finished at this level
+  int64_t stride;    // = nodes at this level
+};
+
+// ---------------------------------------------------------------------------------------
+// launchers (defined in the .hip files; all enqueue on `s`, return hipGetLastError())
+// ---------------------------------------------------------------------------------------
+
+// One pyramid level: children [B*Hkv][*][D] (in_unit_stride elements apart) -> out.
+hipError_t launch_pool_level(int dtype_in, const void* child, int64_t in_unit_stride,
+                             const void* R, int dtype_r, float* out, int64_t out_unit_stride,
+                             int units, int Hkv, int node_begin, int node_end, int b, int D,
+                             hipStream_t s);
+
+// zero `n` completion counters
+hipError_t launch_attend_init(uint32_t* done_all, int n, hipStream_t s);
+
+hipError_t launch_score(const Geom& geo, int level, const float* X, int64_t X_unit_stride,
+                        const void* Q, int dtype, const LevelBufs* parent, int n_top,
+                        float* S, int64_t S_stride, const LevelBufs& cur, hipStream_t s);
+
+hipError_t launch_select(const Geom& geo, int level, const float* S, int64_t S_stride,
+                         const LevelBufs* parent, int n_top, const LevelBufs& cur, float p,
+                         int anchor, int32_t* sel_idx, int64_t cap, int32_t* sel_count,
+                         int32_t* lvl_kept, hipStream_t s);
+
+hipError_t launch_decode(const Geom& geo, int dtype, const void* K, const void* V,
+                         const void* Q, const LevelBufs& l1, int anchor, int splits,
+                         float* partials, uint32_t* done_dec, float* O, hipStream_t s);
+
+}  // namespace zha
