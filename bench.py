@@ -1,0 +1,331 @@
+"""Benchmark: tree-indexed sparse decode attention on one MI355X.
+
+One step = one pass of the whole hot path over one batch: zha_build_tree (summary
+pyramid over the full cache) followed by zha_attend (top-level scoring, per-level top-p
+selection and expansion, sparse GQA decode and split-combine) for every query head.
+Default workload: single layer, 256K context (262,144 tokens), bf16, 32 query heads
+over 4 KV heads, head dim 128, deep tree b = 4, L = 6, decode batch 4, p = 0.95,
+clustered keys with 16 planted needles per sequence (seeded, synthetic).
+
+Prints one JSON line. `value` is query heads per second of whole steps; the same line
+reports the decode-only rate (tree prebuilt), per-kernel times from HIP events recorded
+on the library's launch stream, the dominant kernel's HBM roofline, keys-read
+statistics, and the CPU oracle timed on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode query-heads/s at 256K deep tree p=0.95; HBM GB/s % of peak; keys-read %"
+HBM_PEAK_GBS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="256k_deep")
+    ap.add_argument("--p", type=float, default=None)
+    ap.add_argument("--cpu-units", type=int, default=16,
+                    help="(sequence, KV head) units the CPU oracle baseline runs on")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def kernel_sources_sha() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "tree_indexed_sparse_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode())
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}). The (sequence, KV head) units shard with no "
+              f"communication; see DESIGN.md.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import tree_indexed_sparse_amd as Z
+    from tree_indexed_sparse_amd import _lib as LB
+    import workloads as W
+
+    lib = Z.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    spec = W.spec(args.workload)
+    p = args.p if args.p is not None else spec["p"][len(spec["p"]) // 2]
+    B, T, Hq, Hkv, d, N, b, L = (spec[k] for k in ("B", "T", "Hq", "Hkv", "d", "N", "b", "L"))
+    anchor = spec["anchor"]
+    QH = B * T * Hq
+    elem = 2 if spec["dtype"] == "bf16" else 4
+
+    t0 = time.time()
+    inp = W.gen_all(spec, device=dev)
+    torch.cuda.synchronize()
+    print(f"# inputs generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    K, V, Q, R = inp["K"], inp["V"], inp["Q"], inp["R"]
+
+    # preallocated outputs and workspace: the timed region allocates nothing
+    tree = Z.build_tree(K, R, b, L)
+    O = torch.empty((B, T, Hq, d), dtype=torch.float32, device=dev)
+    sel = torch.empty((B, T, Hq, N), dtype=torch.int32, device=dev)
+    cnt = torch.empty((B, T, Hq), dtype=torch.int32, device=dev)
+    ws = torch.empty(Z.workspace_bytes(tree, T, Hq), dtype=torch.uint8, device=dev)
+
+    # rebuild the pyramid in place each step (same storage, same view)
+    c_tree = tree.c
+
+    def build_into():
+        LB.check(lib.zha_build_tree(K.data_ptr(), R.data_ptr(), c_tree.dtype, B, Hkv, N, N, d, b,
+                                    L, tree.storage.data_ptr(), tree.storage.numel(),
+                                    ctypes.byref(c_tree), torch.cuda.current_stream().cuda_stream))
+
+    def full_step():
+        build_into()
+        Z.attend(Q, K, V, tree, p, anchor, out=O, sel_idx=sel, sel_count=cnt, workspace=ws)
+
+    def attend_only():
+        Z.attend(Q, K, V, tree, p, anchor, out=O, sel_idx=sel, sel_count=cnt, workspace=ws)
+
+    def timed(fn, steps):
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        w0 = time.perf_counter()
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps, (time.perf_counter() - w0) * 1e3 / steps
+
+    for _ in range(args.warmup):
+        full_step()
+    torch.cuda.synchronize()
+    ms_step, wall_step = timed(full_step, args.steps)
+    print(f"# step {ms_step:.3f} ms (wall {wall_step:.3f} ms)", file=sys.stderr, flush=True)
+    ms_attend, _ = timed(attend_only, args.steps)
+
+    # per-kernel durations: HIP events the library records around each of its launches
+    lib.zha_timing_enable(1)
+    ms_timed_pass, _ = timed(full_step, args.steps)
+    lib.zha_timing_enable(0)
+
+    def ktime(kind, level=-1):
+        tot, n = ctypes.c_double(), ctypes.c_int64()
+        LB.check(lib.zha_timing_read(kind, level, ctypes.byref(tot), ctypes.byref(n)))
+        return tot.value, n.value
+
+    kernels = {}
+    for name, kind, levels in (("pool", LB.ZHA_K_POOL, range(1, L + 1)),
+                               ("score", LB.ZHA_K_SCORE, range(1, L + 1)),
+                               ("select", LB.ZHA_K_SELECT, range(1, L + 1)),
+                               ("init", LB.ZHA_K_INIT, [0]), ("decode", LB.ZHA_K_DECODE, [0])):
+        for lv in levels:
+            tot, n = ktime(kind, lv)
+            if n:
+                kernels[f"{name}_l{lv}" if name in ("pool", "score", "select") else name] = dict(
+                    avg_ms=tot / n, launches=n)
+
+    # selection statistics and algorithmic bytes from this call's outputs
+    attend_only()
+    torch.cuda.synchronize()
+    counts = cnt.cpu().numpy().reshape(-1).astype(np.int64)
+    lists = {lv: Z.level_view(tree, T, Hq, lv, ws) for lv in range(1, L + 1)}
+    n1, _, c1 = lists[1]
+    U = c1.size
+    union_tokens = 0
+    for u in range(U):
+        # anchor tokens inside the unit's kept nodes are read once, not twice
+        first = n1[u, :min(int(c1[u]), -(-anchor // b))].astype(np.int64)
+        covered = int(sum(min(b, anchor - nd * b) for nd in first if nd * b < anchor))
+        union_tokens += int(c1[u]) * b + (anchor - covered)
+    kv_bytes = union_tokens * 2 * d * elem
+    decode_bytes = kv_bytes + int(c1.sum()) * 8 + QH * d * elem + QH * d * 4
+    frontier_rows = 0
+    score_bytes = {}
+    for lv in range(1, L + 1):
+        if lv == L:
+            rows = (N // b ** L) * U
+        else:
+            rows = int(lists[lv + 1][2].sum()) * b
+        frontier_rows += rows
+        score_bytes[lv] = rows * d * 4
+    build_bytes = {1: B * Hkv * N * d * elem + B * Hkv * (N // b) * d * 4}
+    for lv in range(2, L + 1):
+        build_bytes[lv] = B * Hkv * (N // b ** (lv - 1)) * d * 4 + B * Hkv * (N // b ** lv) * d * 4
+    list_bytes = 4 * int(counts.sum())
+    attend_alg = kv_bytes + frontier_rows * d * 4 + QH * (d * elem + d * 4 + 4) + list_bytes
+    step_alg = attend_alg + B * Hkv * N * d * elem + tree_bytes_written(B, Hkv, N, d, b, L)
+
+    alg_bytes = {"decode": decode_bytes}
+    for lv in range(1, L + 1):
+        alg_bytes[f"score_l{lv}"] = score_bytes[lv]
+        alg_bytes[f"pool_l{lv}"] = build_bytes[lv]
+    dom = max(kernels, key=lambda k: kernels[k]["avg_ms"] * kernels[k]["launches"])
+    dom_bytes = alg_bytes.get(dom)
+    roofline = None
+    if dom_bytes is not None:
+        ach = dom_bytes / (kernels[dom]["avg_ms"] * 1e-3) / 1e9
+        roofline = dict(kernel=dom, bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS,
+                        unit="GB/s", frac=round(ach / HBM_PEAK_GBS, 4),
+                        traffic=pmc_traffic(dom, args.workload), alg_bytes_per_launch=dom_bytes,
+                        avg_launch_ms=round(kernels[dom]["avg_ms"], 4))
+
+    kr = counts / N
+    keys = dict(mean=round(100 * kr.mean(), 3), min=round(100 * kr.min(), 3),
+                median=round(100 * float(np.median(kr)), 3), max=round(100 * kr.max(), 3),
+                union=round(100 * union_tokens / (U * N), 3))
+
+    copy_gbs = copy_probe(torch, dev)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(spec, p, anchor, args.cpu_units)
+
+    qhs = QH / (ms_step * 1e-3)
+    out = {
+        "metric": METRIC,
+        "value": round(qhs, 1),
+        "unit": "query-heads/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": spec["dtype"],
+        "data": "synthetic",
+        "config": {"workload": args.workload, "B": B, "T": T, "Hq": Hq, "Hkv": Hkv, "d": d,
+                   "N": N, "b": b, "L": L, "p": p, "anchor": anchor,
+                   "step": "zha_build_tree + zha_attend", "accumulate": "fp32",
+                   "parallelism": "single GPU"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "decode_only": {"ms": round(ms_attend, 4),
+                        "query_heads_per_s": round(QH / (ms_attend * 1e-3), 1),
+                        "alg_bytes": attend_alg,
+                        "alg_gbs": round(attend_alg / (ms_attend * 1e-3) / 1e9, 1),
+                        "hbm_frac": round(attend_alg / (ms_attend * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "step_alg_gbs": round(step_alg / (ms_step * 1e-3) / 1e9, 1),
+        "step_hbm_frac": round(step_alg / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "keys_read_pct": keys,
+        "time_split_ms": {
+            "build": round(sum(v["avg_ms"] for k, v in kernels.items() if k.startswith("pool")), 4),
+            "index": round(sum(v["avg_ms"] for k, v in kernels.items()
+                               if k.startswith(("score", "select", "init"))), 4),
+            "attend": round(kernels.get("decode", {}).get("avg_ms", 0.0), 4),
+            "timed_pass_ms_per_step": round(ms_timed_pass, 4)},
+        "kernels": {k: {"avg_ms": round(v["avg_ms"], 4), "launches": v["launches"]}
+                    for k, v in kernels.items()},
+        "copy_probe_gbs": copy_gbs,
+        "kernel_sources": kernel_sources_sha(),
+    }
+    print(json.dumps(out), flush=True)
+
+
+def tree_bytes_written(B, Hkv, N, d, b, L):
+    return sum(B * Hkv * (N // b ** lv) * d * 4 for lv in range(1, L + 1))
+
+
+def copy_probe(torch, dev):
+    """Device-to-device copy bandwidth (read + write bytes / time) of a 2 GiB buffer."""
+    n = 1 << 29
+    a = torch.empty(n, dtype=torch.float32, device=dev)
+    c = torch.empty_like(a)
+    a.fill_(1.0)
+    for _ in range(2):
+        c.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    reps = 5
+    for _ in range(reps):
+        c.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del a, c
+    return round(2 * n * 4 / (ms * 1e-3) / 1e9, 1)
+
+
+def pmc_traffic(kernel, workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary of this kernel,
+    if it was taken on the current kernel sources; otherwise None."""
+    path = os.path.join(PROFILES, f"{kernel}_{workload}_pmc.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("kernel_sources") != kernel_sources_sha():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(spec, p, anchor, n_units):
+    """The CPU oracle, as it stands, on a bounded sample: n_units (sequence, KV head) units
+    of the same workload, each running the whole path (pyramid build, descent and exact
+    attention for the unit's query heads). Rate = query heads / oracle seconds."""
+    import numpy as np
+    import threadpoolctl
+
+    import oracle as O
+    import workloads as W
+
+    G = spec["Hq"] // spec["Hkv"]
+    units = [(i % spec["B"], i % spec["Hkv"]) for i in range(n_units)]
+    Q = W.gen_Q(spec)
+    R = W.gen_R(spec)
+    data = {u: W.gen_KV_unit(spec, u[0], u[1], Q) for u in units}
+    info = threadpoolctl.threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in info] or [1])
+    t0 = time.perf_counter()
+    heads = 0
+    for (bb, g) in units:
+        K_u, V_u = data[(bb, g)]
+        levels = O.build_tree_unit(K_u, R[g], spec["b"], spec["L"])
+        for t in range(spec["T"]):
+            for h in range(g * G, (g + 1) * G):
+                O.attend_head(Q[bb, t, h], levels, K_u, V_u, spec["b"], spec["L"], p, anchor)
+                heads += 1
+    sec = time.perf_counter() - t0
+    return {"value": round(heads / sec, 3), "unit": "query-heads/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{n_units} (sequence, KV head) units = {heads} query heads of "
+                      f"{spec['name']}, full path per unit (pyramid build + descent + "
+                      f"attention), {sec:.1f}s",
+            "cpu": cpu_model()}
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip() + f" x{os.cpu_count()}"
+    except OSError:
+        pass
+    return None
+
+
+if __name__ == "__main__":
+    main()

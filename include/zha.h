@@ -136,6 +136,20 @@ int zha_attend_level_view(const zha_tree* t, int T, int Hq, int level, int64_t* 
                           int64_t* off_masks, int64_t* off_count, int64_t* stride,
                           int64_t* units);
 
+/*
+ * Per-launch timing (for benchmarks and profiling). While enabled, every kernel this
+ * library launches is bracketed by two HIP events recorded on the launch's stream;
+ * zha_timing_enable(1) starts a fresh record and zha_timing_enable(0) stops recording.
+ * zha_timing_read waits for the recorded events and returns, for one kernel kind and
+ * pyramid level (level = -1: every level), the summed duration in milliseconds and the
+ * number of launches. Kinds: ZHA_K_POOL (pooling, level 1 reads the keys), ZHA_K_INIT,
+ * ZHA_K_SCORE, ZHA_K_SELECT, ZHA_K_DECODE (decode and split-combine; level 0).
+ * Recording creates HIP events (host-side objects), so it is off by default.
+ */
+enum { ZHA_K_POOL = 0, ZHA_K_INIT = 1, ZHA_K_SCORE = 2, ZHA_K_SELECT = 3, ZHA_K_DECODE = 4 };
+int zha_timing_enable(int on);
+int zha_timing_read(int kind, int level, double* total_ms, int64_t* launches);
+
 /* Thread-local description of the last failing call on this thread ("" if none). */
 const char* zha_last_error(void);
 

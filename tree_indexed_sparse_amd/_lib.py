@@ -35,8 +35,12 @@ EXPORTS = (
     "zha_attend_workspace_bytes",
     "zha_attend",
     "zha_attend_level_view",
+    "zha_timing_enable",
+    "zha_timing_read",
     "zha_last_error",
 )
+
+ZHA_K_POOL, ZHA_K_INIT, ZHA_K_SCORE, ZHA_K_SELECT, ZHA_K_DECODE = 0, 1, 2, 3, 4
 
 
 class ZhaError(RuntimeError):
@@ -90,6 +94,10 @@ def load() -> ctypes.CDLL:
     lib.zha_attend_level_view.argtypes = [P(ZhaTree), i32, i32, i32, P(i64), P(i64), P(i64),
                                           P(i64), P(i64)]
     lib.zha_attend_level_view.restype = i32
+    lib.zha_timing_enable.argtypes = [i32]
+    lib.zha_timing_enable.restype = i32
+    lib.zha_timing_read.argtypes = [i32, i32, P(ctypes.c_double), P(i64)]
+    lib.zha_timing_read.restype = i32
     lib.zha_last_error.argtypes = []
     lib.zha_last_error.restype = ctypes.c_char_p
     _lib = lib

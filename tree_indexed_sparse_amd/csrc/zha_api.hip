@@ -6,7 +6,9 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
+#include <vector>
 
 #include "zha_internal.h"
 
@@ -28,6 +30,43 @@ int fail(int code, const char* fmt, ...) {
 
 int hip_fail(hipError_t e, const char* what) {
   return fail(ZHA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// ------------------------------------------------------------------ launch timing
+struct TimedLaunch {
+  int kind, level;
+  hipEvent_t start, stop;
+};
+std::mutex g_tmu;
+bool g_timing = false;
+std::vector<TimedLaunch> g_launches;
+std::vector<hipEvent_t> g_free_events;
+
+hipEvent_t take_event() {
+  if (!g_free_events.empty()) {
+    hipEvent_t e = g_free_events.back();
+    g_free_events.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Run `launch` (which enqueues one kernel on s); bracket it with events when timing is on.
+template <class F>
+hipError_t timed(int kind, int level, hipStream_t s, F&& launch) {
+  std::unique_lock<std::mutex> lk(g_tmu);
+  if (!g_timing) {
+    lk.unlock();
+    return launch();
+  }
+  TimedLaunch t{kind, level, take_event(), take_event()};
+  if (t.start) hipEventRecord(t.start, s);
+  const hipError_t e = launch();
+  if (t.stop) hipEventRecord(t.stop, s);
+  if (t.start && t.stop) g_launches.push_back(t);
+  return e;
 }
 
 int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
@@ -187,10 +226,12 @@ int zha_tree_append(zha_tree* t, const void* K, const void* R, int n_new, void* 
     const int64_t cap_l = t->N_cap / b_l;
     const void* child = (l == 1) ? K : (const void*)(t->pyramid + t->level_off[l - 1]);
     const int dt_in = (l == 1) ? t->dtype : ZHA_F32;
-    hipError_t e = launch_pool_level(dt_in, child, cap_prev * t->d, R, t->dtype,
-                                     t->pyramid + t->level_off[l], cap_l * t->d, units, t->Hkv,
-                                     (int)(t->N / b_l), (int)((t->N + (int64_t)n_new) / b_l),
-                                     t->b, t->d, s);
+    hipError_t e = timed(ZHA_K_POOL, l, s, [&] {
+      return launch_pool_level(dt_in, child, cap_prev * t->d, R, t->dtype,
+                               t->pyramid + t->level_off[l], cap_l * t->d, units, t->Hkv,
+                               (int)(t->N / b_l), (int)((t->N + (int64_t)n_new) / b_l), t->b,
+                               t->d, s);
+    });
     if (e != hipSuccess) return hip_fail(e, "pooling launch");
     cap_prev = cap_l;
   }
@@ -293,7 +334,9 @@ int zha_attend(const zha_tree* t, const void* Q, int T, int Hq, const void* K, c
   float* S = (float*)(ws + w.off_S);
   int32_t* lvl = (int32_t*)(ws + w.off_lvl);
 
-  hipError_t e = launch_attend_init((uint32_t*)(ws + w.off_done), (t->L + 1) * w.U, s);
+  hipError_t e = timed(ZHA_K_INIT, 0, s, [&] {
+    return launch_attend_init((uint32_t*)(ws + w.off_done), (t->L + 1) * w.U, s);
+  });
   if (e != hipSuccess) return hip_fail(e, "init launch");
   int64_t cap_l = t->N_cap;
   for (int l = 1; l <= t->L; ++l) cap_l /= t->b;  // capacity nodes at the top level
@@ -301,16 +344,56 @@ int zha_attend(const zha_tree* t, const void* Q, int T, int Hq, const void* K, c
     const LevelBufs* parent = (l < t->L) ? &lv[l + 1] : nullptr;
     const int n_top = (l == t->L) ? (int)w.n[t->L] : 0;
     const float* X = t->pyramid + t->level_off[l];
-    e = launch_score(g, l, X, cap_l * t->d, Q, t->dtype, parent, n_top, S, w.S_stride, lv[l], s);
+    e = timed(ZHA_K_SCORE, l, s, [&] {
+      return launch_score(g, l, X, cap_l * t->d, Q, t->dtype, parent, n_top, S, w.S_stride,
+                          lv[l], s);
+    });
     if (e != hipSuccess) return hip_fail(e, "score launch");
-    e = launch_select(g, l, S, w.S_stride, parent, n_top, lv[l], p, anchor,
-                      l == 1 ? sel_idx : nullptr, cap, sel_count, lvl, s);
+    e = timed(ZHA_K_SELECT, l, s, [&] {
+      return launch_select(g, l, S, w.S_stride, parent, n_top, lv[l], p, anchor,
+                           l == 1 ? sel_idx : nullptr, cap, sel_count, lvl, s);
+    });
     if (e != hipSuccess) return hip_fail(e, "select launch");
     cap_l *= t->b;
   }
-  e = launch_decode(g, t->dtype, K, V, Q, lv[1], anchor, w.splits,
-                    (float*)(ws + w.off_part), done_dec, O, s);
+  e = timed(ZHA_K_DECODE, 0, s, [&] {
+    return launch_decode(g, t->dtype, K, V, Q, lv[1], anchor, w.splits,
+                         (float*)(ws + w.off_part), done_dec, O, s);
+  });
   if (e != hipSuccess) return hip_fail(e, "decode launch");
+  return ZHA_OK;
+}
+
+int zha_timing_enable(int on) {
+  std::lock_guard<std::mutex> lk(g_tmu);
+  if (on) {
+    for (auto& t : g_launches) {
+      g_free_events.push_back(t.start);
+      g_free_events.push_back(t.stop);
+    }
+    g_launches.clear();
+  }
+  g_timing = on != 0;
+  return ZHA_OK;
+}
+
+int zha_timing_read(int kind, int level, double* total_ms, int64_t* launches) {
+  if (!total_ms || !launches) return fail(ZHA_ERR_INVALID_ARG, "output pointers must not be NULL");
+  std::lock_guard<std::mutex> lk(g_tmu);
+  double tot = 0.0;
+  int64_t n = 0;
+  for (auto& t : g_launches) {
+    if (t.kind != kind || (level >= 0 && t.level != level)) continue;
+    hipError_t e = hipEventSynchronize(t.stop);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, t.start, t.stop);
+    if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+    tot += ms;
+    ++n;
+  }
+  *total_ms = tot;
+  *launches = n;
   return ZHA_OK;
 }
 
