@@ -22,6 +22,69 @@ namespace {
 constexpr int kDecThreads = 256;
 constexpr int kDecWaves = kDecThreads / 64;
 
+// Merge the per-wave states (sm, sl: [wave][member], so: [wave][member][D], in LDS) into
+// this split's partial, then let the unit's last workgroup combine all splits in split
+// order and write O. Every thread of the workgroup calls this.
+template <int D>
+__device__ void finish_split(const Geom& geo, int u, int sp, int splits, int Mu, const float* sm,
+                             const float* sl, const float* so, float* __restrict__ part,
+                             uint32_t* __restrict__ done, float* __restrict__ O) {
+  const int64_t pstride = (int64_t)(D + 2);
+  float* pu = part + ((int64_t)u * splits + sp) * kMaxMembers * pstride;
+  for (int idx = threadIdx.x; idx < Mu * D; idx += kDecThreads) {
+    const int m = idx / D, k = idx % D;
+    float M = -INFINITY;
+    for (int w = 0; w < kDecWaves; ++w) M = fmaxf(M, sm[w * kMaxMembers + m]);
+    float acc = 0.f, lsum = 0.f;
+    if (M != -INFINITY) {
+      for (int w = 0; w < kDecWaves; ++w) {
+        const float mw = sm[w * kMaxMembers + m];
+        if (mw == -INFINITY) continue;
+        const float f = expf(mw - M);
+        acc = fmaf(f, so[(w * kMaxMembers + m) * D + k], acc);
+        lsum = fmaf(f, sl[w * kMaxMembers + m], lsum);
+      }
+    }
+    pu[m * pstride + k] = acc;
+    if (k == 0) {
+      pu[m * pstride + D] = M;
+      pu[m * pstride + D + 1] = lsum;
+    }
+  }
+
+  // last workgroup of the unit combines every split, in split order
+  __threadfence();
+  __syncthreads();
+  __shared__ uint32_t last;
+  if (threadIdx.x == 0) last = (atomicAdd(&done[u], 1u) == (uint32_t)splits - 1u) ? 1u : 0u;
+  __syncthreads();
+  if (!last) return;
+  __threadfence();
+  const float* pall = part + (int64_t)u * splits * kMaxMembers * pstride;
+  for (int idx = threadIdx.x; idx < Mu * D; idx += kDecThreads) {
+    const int m = idx / D, k = idx % D;
+    float M = -INFINITY;
+    for (int s2 = 0; s2 < splits; ++s2) {
+      const float ms = __hip_atomic_load(&pall[(s2 * kMaxMembers + m) * pstride + D],
+                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      M = fmaxf(M, ms);
+    }
+    float acc = 0.f, lsum = 0.f;
+    for (int s2 = 0; s2 < splits; ++s2) {
+      const float* ps = pall + (s2 * kMaxMembers + m) * pstride;
+      const float ms = __hip_atomic_load(&ps[D], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (ms == -INFINITY) continue;
+      const float f = expf(ms - M);
+      acc = fmaf(f, __hip_atomic_load(&ps[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), acc);
+      lsum = fmaf(f, __hip_atomic_load(&ps[D + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                  lsum);
+    }
+    O[(int64_t)qh_of(geo, u, m) * D + k] = acc / lsum;
+  }
+  if (threadIdx.x == 0) done[u] = 0u;
+}
+
+// float32 inputs: lanes across head dims, one token at a time per wave.
 template <typename T, int D>
 __global__ __launch_bounds__(kDecThreads) void decode_valu_kernel(
     Geom geo, const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ Q,
@@ -102,58 +165,215 @@ __global__ __launch_bounds__(kDecThreads) void decode_valu_kernel(
     for (int i = 0; i < DPL; ++i) so[wave][m][lane * DPL + i] = o[m][i];
   }
   __syncthreads();
-  const int64_t pstride = (int64_t)(D + 2);
-  float* pu = part + ((int64_t)u * splits + sp) * kMaxMembers * pstride;
-  for (int idx = threadIdx.x; idx < Mu * D; idx += kDecThreads) {
-    const int m = idx / D, k = idx % D;
-    float M = -INFINITY;
-    for (int w = 0; w < kDecWaves; ++w) M = fmaxf(M, sm[w][m]);
-    float acc = 0.f, lsum = 0.f;
-    if (M != -INFINITY) {
-      for (int w = 0; w < kDecWaves; ++w) {
-        if (sm[w][m] == -INFINITY) continue;
-        const float f = expf(sm[w][m] - M);
-        acc = fmaf(f, so[w][m][k], acc);
-        lsum = fmaf(f, sl[w][m], lsum);
+  finish_split<D>(geo, u, sp, splits, Mu, &sm[0][0], &sl[0][0], &so[0][0][0], part, done, O);
+}
+
+
+// ------------------------------------------------------------------------------------
+// bf16 inputs: matrix cores. Each wave walks 32-token tiles of the split's range.
+//   S^T[token][member] = K . Q^T  with v_mfma_f32_16x16x32_bf16: A = 16 key rows (each lane
+//     loads 16 contiguous bytes of its row straight from HBM), B = the members' queries,
+//     held in registers for the whole kernel. Two 16-token halves per tile.
+//   O^T[dim][member] += V^T . P^T: the probabilities stay in the lanes that produced them,
+//     which is exactly the B-operand layout once token slots are numbered to match; V is
+//     staged through a padded LDS tile and each lane reads one dword (two adjacent dims)
+//     per token, feeding an even-dim and an odd-dim MFMA. P is split into bf16 hi + lo
+//     parts (two MFMAs) so the product keeps about 16 mantissa bits; accumulation is fp32.
+// Lane l: member = l % 16, group = l / 16. Softmax state per member is shared by the 4
+// lanes of that member (one per group); the running sum is kept per lane and reduced at
+// the end.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kTile = 32;
+
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+template <int D>
+__global__ __launch_bounds__(kDecThreads) void decode_mfma_kernel(
+    Geom geo, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
+    const bf16_t* __restrict__ Q, LevelBufs l1, int anchor, int splits, float* __restrict__ part,
+    uint32_t* __restrict__ done, float* __restrict__ O, float sigma) {
+  constexpr int KC = D / 32;          // 32-dim chunks: QK k-steps and PV column blocks
+  constexpr int RW = D / 2 + 4;       // LDS row stride in dwords (padding spreads banks)
+  constexpr int CH = D / 8;           // 16-byte chunks per row
+  constexpr int RPI = 64 / CH;        // rows per wave-wide 16-byte load
+  constexpr int NI = kTile / RPI;     // such loads per tile
+  constexpr int VWORDS = kDecWaves * kTile * RW;
+  constexpr int MWORDS = kDecWaves * kMaxMembers * (D + 2);
+  __shared__ uint32_t smem[VWORDS > MWORDS ? VWORDS : MWORDS];
+
+  const int u = blockIdx.y, sp = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int mem = lane & 15, grp = lane >> 4;
+  const int Mu = members_of(geo, u);
+  const int b = geo.b;
+  const int ntok = (int)l1.count[u] * b;
+  int per = (ntok + splits - 1) / splits;
+  per = (per + kTile - 1) / kTile * kTile;
+  const int t0 = min(sp * per, ntok), t1 = min(t0 + per, ntok);
+  const int64_t row0 = (int64_t)bg_of(geo, u) * geo.Ncap;
+  const bf16_t* Ku = K + row0 * D;
+  const bf16_t* Vu = V + row0 * D;
+  const uint32_t* nodes = l1.nodes + u * l1.stride;
+  const uint32_t* masks = l1.masks + u * l1.stride;
+  uint32_t* sV = smem + wave * kTile * RW;
+
+  bf16x8_t qb[KC];
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc) {
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (mem < Mu)
+      v = *reinterpret_cast<const uint4*>(Q + (int64_t)qh_of(geo, u, mem) * D + 32 * kc + 8 * grp);
+    qb[kc] = as_bf16x8(v);
+  }
+  f32x4_t acc[KC][2];
+#pragma unroll
+  for (int c = 0; c < KC; ++c) acc[c][0] = acc[c][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_part = 0.f;
+
+  // token id and member mask of work index i: anchor tiles cover tokens [0, anchor) for
+  // every member; node tiles skip tokens below the anchor. Past `lim`: token 0, no member.
+  auto lookup = [&](int i, bool anc, int lim, int* tok) -> uint32_t {
+    if (i >= lim) {
+      *tok = 0;
+      return 0u;
+    }
+    if (anc) {
+      *tok = i;
+      return 0xffffu;
+    }
+    const int nd = i / b;
+    const int t = (int)nodes[nd] * b + (i - nd * b);
+    *tok = t;
+    return t < anchor ? 0u : masks[nd];
+  };
+
+  auto tile = [&](int base, bool anc, int lim) {
+    uint4 vv[NI];
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      int tok;
+      lookup(base + lane / CH + RPI * j, anc, lim, &tok);
+      vv[j] = *reinterpret_cast<const uint4*>(Vu + (int64_t)tok * D + 8 * (lane % CH));
+    }
+    f32x4_t sc[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      int tok;
+      lookup(base + 16 * h + mem, anc, lim, &tok);
+      const bf16_t* kr = Ku + (int64_t)tok * D + 8 * grp;
+      sc[h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc)
+        sc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            as_bf16x8(*reinterpret_cast<const uint4*>(kr + 32 * kc)), qb[kc], sc[h], 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < NI; ++j)
+      *reinterpret_cast<uint4*>(&sV[(lane / CH + RPI * j) * RW + 4 * (lane % CH)]) = vv[j];
+
+    // this lane's scores: tokens base + 16h + 4 grp + r, member `mem`
+    float p[8];
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        int tok;
+        const uint32_t mk = lookup(base + 16 * h + 4 * grp + r, anc, lim, &tok);
+        const bool ok = mem < Mu && ((mk >> mem) & 1u);
+        const float v = ok ? sigma * sc[h][r] : -INFINITY;
+        p[4 * h + r] = v;
+        mloc = fmaxf(mloc, v);
       }
     }
-    pu[m * pstride + k] = acc;
-    if (k == 0) {
-      pu[m * pstride + D] = M;
-      pu[m * pstride + D + 1] = lsum;
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+    const float m_new = fmaxf(m_run, mloc);
+    float alpha = 1.f, psum = 0.f;
+    if (m_new == -INFINITY) {
+#pragma unroll
+      for (int v = 0; v < 8; ++v) p[v] = 0.f;
+    } else {
+      alpha = expf(m_run - m_new);
+#pragma unroll
+      for (int v = 0; v < 8; ++v) {
+        p[v] = expf(p[v] - m_new);
+        psum += p[v];
+      }
     }
-  }
+    l_part = l_part * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      acc[c][0] *= alpha;
+      acc[c][1] *= alpha;
+    }
+    uint32_t hi[8], lo[8];
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+      hi[v] = bf16_rne(p[v]);
+      lo[v] = bf16_rne(p[v] - __uint_as_float(hi[v] << 16));
+    }
+    const bf16x8_t phi = as_bf16x8(make_uint4(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16),
+                                              hi[4] | (hi[5] << 16), hi[6] | (hi[7] << 16)));
+    const bf16x8_t plo = as_bf16x8(make_uint4(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16),
+                                              lo[4] | (lo[5] << 16), lo[6] | (lo[7] << 16)));
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      uint32_t dw[8];
+#pragma unroll
+      for (int v = 0; v < 8; ++v) {
+        const int rr = (v < 4) ? 4 * grp + v : 16 + 4 * grp + (v - 4);
+        dw[v] = sV[rr * RW + 16 * c + mem];
+      }
+      const bf16x8_t ae = as_bf16x8(make_uint4(
+          (dw[0] & 0xffffu) | (dw[1] << 16), (dw[2] & 0xffffu) | (dw[3] << 16),
+          (dw[4] & 0xffffu) | (dw[5] << 16), (dw[6] & 0xffffu) | (dw[7] << 16)));
+      const bf16x8_t ao = as_bf16x8(make_uint4(
+          (dw[0] >> 16) | (dw[1] & 0xffff0000u), (dw[2] >> 16) | (dw[3] & 0xffff0000u),
+          (dw[4] >> 16) | (dw[5] & 0xffff0000u), (dw[6] >> 16) | (dw[7] & 0xffff0000u)));
+      acc[c][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ae, phi, acc[c][0], 0, 0, 0);
+      acc[c][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ae, plo, acc[c][0], 0, 0, 0);
+      acc[c][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ao, phi, acc[c][1], 0, 0, 0);
+      acc[c][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ao, plo, acc[c][1], 0, 0, 0);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
 
-  // last workgroup of the unit combines every split, in split order
-  __threadfence();
-  __syncthreads();
-  __shared__ uint32_t last;
-  if (threadIdx.x == 0) last = (atomicAdd(&done[u], 1u) == (uint32_t)splits - 1u) ? 1u : 0u;
-  __syncthreads();
-  if (!last) return;
-  __threadfence();
-  const float* pall = part + (int64_t)u * splits * kMaxMembers * pstride;
-  for (int idx = threadIdx.x; idx < Mu * D; idx += kDecThreads) {
-    const int m = idx / D, k = idx % D;
-    float M = -INFINITY;
-    for (int s2 = 0; s2 < splits; ++s2) {
-      const float ms = __hip_atomic_load(&pall[(s2 * kMaxMembers + m) * pstride + D],
-                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      M = fmaxf(M, ms);
-    }
-    float acc = 0.f, lsum = 0.f;
-    for (int s2 = 0; s2 < splits; ++s2) {
-      const float* ps = pall + (s2 * kMaxMembers + m) * pstride;
-      const float ms = __hip_atomic_load(&ps[D], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (ms == -INFINITY) continue;
-      const float f = expf(ms - M);
-      acc = fmaf(f, __hip_atomic_load(&ps[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), acc);
-      lsum = fmaf(f, __hip_atomic_load(&ps[D + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
-                  lsum);
-    }
-    O[(int64_t)qh_of(geo, u, m) * D + k] = acc / lsum;
+  if (sp == 0 && wave == 0)
+    for (int base = 0; base < anchor; base += kTile) tile(base, true, anchor);
+  for (int base = t0 + wave * kTile; base < t1; base += kDecWaves * kTile) tile(base, false, t1);
+
+  // per-member totals over the 4 lanes of a member, then hand the states to LDS
+  l_part += __shfl_xor(l_part, 16, 64);
+  l_part += __shfl_xor(l_part, 32, 64);
+  __syncthreads();  // every wave is done with its V tile before the LDS is reused
+  float* sm = reinterpret_cast<float*>(smem);
+  float* sl = sm + kDecWaves * kMaxMembers;
+  float* so = sl + kDecWaves * kMaxMembers;
+  if (grp == 0) {
+    sm[wave * kMaxMembers + mem] = m_run;
+    sl[wave * kMaxMembers + mem] = l_part;
   }
-  if (threadIdx.x == 0) done[u] = 0u;
+#pragma unroll
+  for (int c = 0; c < KC; ++c)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int par = 0; par < 2; ++par)
+        so[(wave * kMaxMembers + mem) * D + 32 * c + 8 * grp + 2 * r + par] = acc[c][par][r];
+  __syncthreads();
+  finish_split<D>(geo, u, sp, splits, Mu, sm, sl, so, part, done, O);
 }
 
 template <typename T>
@@ -178,8 +398,19 @@ hipError_t launch_decode_t(const Geom& geo, const void* K, const void* V, const 
 hipError_t launch_decode(const Geom& geo, int dtype, const void* K, const void* V,
                          const void* Q, const LevelBufs& l1, int anchor, int splits,
                          float* partials, uint32_t* done_dec, float* O, hipStream_t s) {
-  if (dtype == ZHA_BF16)
-    return launch_decode_t<bf16_t>(geo, K, V, Q, l1, anchor, splits, partials, done_dec, O, s);
+  if (dtype == ZHA_BF16) {
+    dim3 grid(splits, geo.U);
+    const float sigma = 1.0f / sqrtf((float)geo.D);
+    if (geo.D == 64)
+      hipLaunchKernelGGL((decode_mfma_kernel<64>), grid, dim3(kDecThreads), 0, s, geo,
+                         (const bf16_t*)K, (const bf16_t*)V, (const bf16_t*)Q, l1, anchor, splits,
+                         partials, done_dec, O, sigma);
+    else
+      hipLaunchKernelGGL((decode_mfma_kernel<128>), grid, dim3(kDecThreads), 0, s, geo,
+                         (const bf16_t*)K, (const bf16_t*)V, (const bf16_t*)Q, l1, anchor, splits,
+                         partials, done_dec, O, sigma);
+    return hipGetLastError();
+  }
   return launch_decode_t<float>(geo, K, V, Q, l1, anchor, splits, partials, done_dec, O, s);
 }
 
