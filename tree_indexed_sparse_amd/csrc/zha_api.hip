@@ -137,7 +137,7 @@ WsLayout layout_of(const Geom& g) {
   w.U = g.U;
   w.QH = g.B * g.T * g.Hq;
   w.splits = (2048 + g.U - 1) / g.U;
-  if (w.splits > 256) w.splits = 256;
+  if (w.splits > kMaxSplits) w.splits = kMaxSplits;
   if (w.splits < 1) w.splits = 1;
   int64_t nl = g.N;
   for (int l = 1; l <= g.L; ++l) {

@@ -21,14 +21,17 @@ namespace {
 
 constexpr int kDecThreads = 256;
 constexpr int kDecWaves = kDecThreads / 64;
+constexpr int kNodeChunk = 2048;  // union-list entries staged in LDS at a time
 
 // Merge the per-wave states (sm, sl: [wave][member], so: [wave][member][D], in LDS) into
 // this split's partial, then let the unit's last workgroup combine all splits in split
-// order and write O. Every thread of the workgroup calls this.
+// order and write O. `scratch` is LDS for 2 * kMaxSplits * kMaxMembers floats that may
+// alias sm/sl/so. Every thread of the workgroup calls this.
 template <int D>
 __device__ void finish_split(const Geom& geo, int u, int sp, int splits, int Mu, const float* sm,
-                             const float* sl, const float* so, float* __restrict__ part,
-                             uint32_t* __restrict__ done, float* __restrict__ O) {
+                             const float* sl, const float* so, float* scratch,
+                             float* __restrict__ part, uint32_t* __restrict__ done,
+                             float* __restrict__ O) {
   const int64_t pstride = (int64_t)(D + 2);
   float* pu = part + ((int64_t)u * splits + sp) * kMaxMembers * pstride;
   for (int idx = threadIdx.x; idx < Mu * D; idx += kDecThreads) {
@@ -52,7 +55,7 @@ __device__ void finish_split(const Geom& geo, int u, int sp, int splits, int Mu,
     }
   }
 
-  // last workgroup of the unit combines every split, in split order
+  // the unit's last workgroup combines every split, in split order
   __threadfence();
   __syncthreads();
   __shared__ uint32_t last;
@@ -61,27 +64,51 @@ __device__ void finish_split(const Geom& geo, int u, int sp, int splits, int Mu,
   if (!last) return;
   __threadfence();
   const float* pall = part + (int64_t)u * splits * kMaxMembers * pstride;
+  float* cm = scratch;                              // [split][member] max, then weight
+  float* cl = scratch + kMaxSplits * kMaxMembers;   // [split][member] sum
+  for (int idx = threadIdx.x; idx < splits * Mu; idx += kDecThreads) {
+    const int s2 = idx / Mu, m = idx % Mu;
+    const float* ps = pall + (s2 * kMaxMembers + m) * pstride;
+    cm[s2 * kMaxMembers + m] = __hip_atomic_load(&ps[D], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    cl[s2 * kMaxMembers + m] =
+        __hip_atomic_load(&ps[D + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  if (threadIdx.x < Mu) {
+    const int m = threadIdx.x;
+    float M = -INFINITY;
+    for (int s2 = 0; s2 < splits; ++s2) M = fmaxf(M, cm[s2 * kMaxMembers + m]);
+    float L = 0.f;
+    for (int s2 = 0; s2 < splits; ++s2) {
+      const float ms = cm[s2 * kMaxMembers + m];
+      if (ms != -INFINITY) L = fmaf(expf(ms - M), cl[s2 * kMaxMembers + m], L);
+    }
+    for (int s2 = 0; s2 < splits; ++s2) {
+      const float ms = cm[s2 * kMaxMembers + m];
+      cm[s2 * kMaxMembers + m] = (ms == -INFINITY) ? 0.f : expf(ms - M) / L;
+    }
+  }
+  __syncthreads();
   for (int idx = threadIdx.x; idx < Mu * D; idx += kDecThreads) {
     const int m = idx / D, k = idx % D;
-    float M = -INFINITY;
+    float acc = 0.f;
+#pragma unroll 8
     for (int s2 = 0; s2 < splits; ++s2) {
-      const float ms = __hip_atomic_load(&pall[(s2 * kMaxMembers + m) * pstride + D],
-                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      M = fmaxf(M, ms);
+      const float o = __hip_atomic_load(&pall[(s2 * kMaxMembers + m) * pstride + k],
+                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      acc = fmaf(cm[s2 * kMaxMembers + m], o, acc);
     }
-    float acc = 0.f, lsum = 0.f;
-    for (int s2 = 0; s2 < splits; ++s2) {
-      const float* ps = pall + (s2 * kMaxMembers + m) * pstride;
-      const float ms = __hip_atomic_load(&ps[D], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (ms == -INFINITY) continue;
-      const float f = expf(ms - M);
-      acc = fmaf(f, __hip_atomic_load(&ps[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), acc);
-      lsum = fmaf(f, __hip_atomic_load(&ps[D + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
-                  lsum);
-    }
-    O[(int64_t)qh_of(geo, u, m) * D + k] = acc / lsum;
+    O[(int64_t)qh_of(geo, u, m) * D + k] = acc;
   }
   if (threadIdx.x == 0) done[u] = 0u;
+}
+
+__device__ __forceinline__ void split_range(int ntok, int splits, int sp, int align, int* t0,
+                                            int* t1) {
+  int per = (ntok + splits - 1) / splits;
+  per = (per + align - 1) / align * align;
+  *t0 = min(sp * per, ntok);
+  *t1 = min(*t0 + per, ntok);
 }
 
 // float32 inputs: lanes across head dims, one token at a time per wave.
@@ -95,9 +122,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_valu_kernel(
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int Mu = members_of(geo, u);
   const int b = geo.b;
-  const int ntok = (int)l1.count[u] * b;
-  const int per = (ntok + splits - 1) / splits;
-  const int t0 = min(sp * per, ntok), t1 = min(t0 + per, ntok);
+  int t0, t1;
+  split_range((int)l1.count[u] * b, splits, sp, 1, &t0, &t1);
   const int64_t row0 = (int64_t)bg_of(geo, u) * geo.Ncap;
   const T* Ku = K + row0 * D;
   const T* Vu = V + row0 * D;
@@ -154,7 +180,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_valu_kernel(
 
   // merge the waves' states through LDS, in wave order
   __shared__ float sm[kDecWaves][kMaxMembers], sl[kDecWaves][kMaxMembers];
-  __shared__ float so[kDecWaves][kMaxMembers][D];
+  __shared__ float so[kDecWaves * kMaxMembers * D > 2 * kMaxSplits * kMaxMembers
+                          ? kDecWaves * kMaxMembers * D
+                          : 2 * kMaxSplits * kMaxMembers];
 #pragma unroll
   for (int m = 0; m < kMaxMembers; ++m) {
     if (lane == 0) {
@@ -162,12 +190,11 @@ __global__ __launch_bounds__(kDecThreads) void decode_valu_kernel(
       sl[wave][m] = lrun[m];
     }
 #pragma unroll
-    for (int i = 0; i < DPL; ++i) so[wave][m][lane * DPL + i] = o[m][i];
+    for (int i = 0; i < DPL; ++i) so[(wave * kMaxMembers + m) * D + lane * DPL + i] = o[m][i];
   }
   __syncthreads();
-  finish_split<D>(geo, u, sp, splits, Mu, &sm[0][0], &sl[0][0], &so[0][0][0], part, done, O);
+  finish_split<D>(geo, u, sp, splits, Mu, &sm[0][0], &sl[0][0], so, so, part, done, O);
 }
-
 
 // ------------------------------------------------------------------------------------
 // bf16 inputs: matrix cores. Each wave walks 32-token tiles of the split's range.
@@ -181,7 +208,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_valu_kernel(
 //     parts (two MFMAs) so the product keeps about 16 mantissa bits; accumulation is fp32.
 // Lane l: member = l % 16, group = l / 16. Softmax state per member is shared by the 4
 // lanes of that member (one per group); the running sum is kept per lane and reduced at
-// the end.
+// the end. The workgroup's slice of the union node list is staged in LDS, and each wave
+// issues the loads of its next tile before computing the current one.
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
@@ -193,6 +221,14 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
 }
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+__device__ __forceinline__ uint4 ld16(const bf16_t* p) { return *reinterpret_cast<const uint4*>(p); }
+
+template <int D>
+struct TileRegs {
+  uint4 k[2][D / 32];
+  uint4 v[kTile / (64 / (D / 8))];
+};
 
 template <int D>
 __global__ __launch_bounds__(kDecThreads) void decode_mfma_kernel(
@@ -206,17 +242,18 @@ __global__ __launch_bounds__(kDecThreads) void decode_mfma_kernel(
   constexpr int NI = kTile / RPI;     // such loads per tile
   constexpr int VWORDS = kDecWaves * kTile * RW;
   constexpr int MWORDS = kDecWaves * kMaxMembers * (D + 2);
-  __shared__ uint32_t smem[VWORDS > MWORDS ? VWORDS : MWORDS];
+  constexpr int CWORDS = 2 * kMaxSplits * kMaxMembers;
+  constexpr int W1 = VWORDS > MWORDS ? VWORDS : MWORDS;
+  __shared__ uint32_t smem[W1 > CWORDS ? W1 : CWORDS];
+  __shared__ uint32_t s_nodes[kNodeChunk], s_masks[kNodeChunk];
 
   const int u = blockIdx.y, sp = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int mem = lane & 15, grp = lane >> 4;
   const int Mu = members_of(geo, u);
   const int b = geo.b;
-  const int ntok = (int)l1.count[u] * b;
-  int per = (ntok + splits - 1) / splits;
-  per = (per + kTile - 1) / kTile * kTile;
-  const int t0 = min(sp * per, ntok), t1 = min(t0 + per, ntok);
+  int t0, t1;
+  split_range((int)l1.count[u] * b, splits, sp, kTile, &t0, &t1);
   const int64_t row0 = (int64_t)bg_of(geo, u) * geo.Ncap;
   const bf16_t* Ku = K + row0 * D;
   const bf16_t* Vu = V + row0 * D;
@@ -228,8 +265,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_mfma_kernel(
 #pragma unroll
   for (int kc = 0; kc < KC; ++kc) {
     uint4 v = make_uint4(0u, 0u, 0u, 0u);
-    if (mem < Mu)
-      v = *reinterpret_cast<const uint4*>(Q + (int64_t)qh_of(geo, u, mem) * D + 32 * kc + 8 * grp);
+    if (mem < Mu) v = ld16(Q + (int64_t)qh_of(geo, u, mem) * D + 32 * kc + 8 * grp);
     qb[kc] = as_bf16x8(v);
   }
   f32x4_t acc[KC][2];
@@ -237,46 +273,51 @@ __global__ __launch_bounds__(kDecThreads) void decode_mfma_kernel(
   for (int c = 0; c < KC; ++c) acc[c][0] = acc[c][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_part = 0.f;
 
-  // token id and member mask of work index i: anchor tiles cover tokens [0, anchor) for
-  // every member; node tiles skip tokens below the anchor. Past `lim`: token 0, no member.
-  auto lookup = [&](int i, bool anc, int lim, int* tok) -> uint32_t {
-    if (i >= lim) {
-      *tok = 0;
-      return 0u;
-    }
-    if (anc) {
-      *tok = i;
-      return 0xffffu;
-    }
+  // Token id and member mask of work index i. Anchor tiles cover tokens [0, anchor) for
+  // every member; node tiles read the staged list (entry i / b - nbase) and skip tokens
+  // below the anchor. Past `lim`: token 0, no member (its loads stay in bounds).
+  auto token_at = [&](int i, bool anc, int lim, int nbase) -> int {
+    if (i >= lim) return 0;
+    if (anc) return i;
     const int nd = i / b;
-    const int t = (int)nodes[nd] * b + (i - nd * b);
-    *tok = t;
-    return t < anchor ? 0u : masks[nd];
+    return (int)s_nodes[nd - nbase] * b + (i - nd * b);
+  };
+  auto mask_at = [&](int i, bool anc, int lim, int nbase) -> uint32_t {
+    if (i >= lim) return 0u;
+    if (anc) return 0xffffu;
+    const int nd = i / b;
+    const int t = (int)s_nodes[nd - nbase] * b + (i - nd * b);
+    return t < anchor ? 0u : s_masks[nd - nbase];
   };
 
-  auto tile = [&](int base, bool anc, int lim) {
-    uint4 vv[NI];
+  auto issue = [&](TileRegs<D>& R, int base, bool anc, int lim, int nbase) {
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
-      int tok;
-      lookup(base + lane / CH + RPI * j, anc, lim, &tok);
-      vv[j] = *reinterpret_cast<const uint4*>(Vu + (int64_t)tok * D + 8 * (lane % CH));
+      const int tok = token_at(base + lane / CH + RPI * j, anc, lim, nbase);
+      R.v[j] = ld16(Vu + (int64_t)tok * D + 8 * (lane % CH));
     }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int tok = token_at(base + 16 * h + mem, anc, lim, nbase);
+      const bf16_t* kr = Ku + (int64_t)tok * D + 8 * grp;
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) R.k[h][kc] = ld16(kr + 32 * kc);
+    }
+  };
+
+  auto compute = [&](const TileRegs<D>& R, int base, bool anc, int lim, int nbase) {
     f32x4_t sc[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      int tok;
-      lookup(base + 16 * h + mem, anc, lim, &tok);
-      const bf16_t* kr = Ku + (int64_t)tok * D + 8 * grp;
       sc[h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc)
-        sc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            as_bf16x8(*reinterpret_cast<const uint4*>(kr + 32 * kc)), qb[kc], sc[h], 0, 0, 0);
+        sc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(R.k[h][kc]), qb[kc], sc[h],
+                                                        0, 0, 0);
     }
 #pragma unroll
     for (int j = 0; j < NI; ++j)
-      *reinterpret_cast<uint4*>(&sV[(lane / CH + RPI * j) * RW + 4 * (lane % CH)]) = vv[j];
+      *reinterpret_cast<uint4*>(&sV[(lane / CH + RPI * j) * RW + 4 * (lane % CH)]) = R.v[j];
 
     // this lane's scores: tokens base + 16h + 4 grp + r, member `mem`
     float p[8];
@@ -285,8 +326,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_mfma_kernel(
     for (int h = 0; h < 2; ++h) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        int tok;
-        const uint32_t mk = lookup(base + 16 * h + 4 * grp + r, anc, lim, &tok);
+        const uint32_t mk = mask_at(base + 16 * h + 4 * grp + r, anc, lim, nbase);
         const bool ok = mem < Mu && ((mk >> mem) & 1u);
         const float v = ok ? sigma * sc[h][r] : -INFINITY;
         p[4 * h + r] = v;
@@ -350,9 +390,42 @@ __global__ __launch_bounds__(kDecThreads) void decode_mfma_kernel(
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
 
-  if (sp == 0 && wave == 0)
-    for (int base = 0; base < anchor; base += kTile) tile(base, true, anchor);
-  for (int base = t0 + wave * kTile; base < t1; base += kDecWaves * kTile) tile(base, false, t1);
+  if (sp == 0 && wave == 0) {
+    for (int base = 0; base < anchor; base += kTile) {
+      TileRegs<D> R;
+      issue(R, base, true, anchor, 0);
+      compute(R, base, true, anchor, 0);
+    }
+  }
+
+  // node tiles, in chunks of the union list small enough to stage in LDS
+  const int span = ((kNodeChunk - 1) * b) / kTile * kTile;  // tokens per chunk
+  const int step = kDecWaves * kTile;
+  for (int c0 = t0; c0 < t1; c0 += span) {
+    const int c1 = min(c0 + span, t1);
+    const int nbase = c0 / b, nend = (c1 - 1) / b + 1;
+    __syncthreads();
+    for (int i = threadIdx.x; i < nend - nbase; i += kDecThreads) {
+      s_nodes[i] = nodes[nbase + i];
+      s_masks[i] = masks[nbase + i];
+    }
+    __syncthreads();
+    int base = c0 + wave * kTile;
+    if (base >= c1) continue;
+    TileRegs<D> A, Bq;
+    issue(A, base, false, c1, nbase);
+    while (true) {
+      const int n1 = base + step;
+      issue(Bq, n1, false, c1, nbase);  // past c1 this reads token 0, masked out
+      compute(A, base, false, c1, nbase);
+      if (n1 >= c1) break;
+      const int n2 = n1 + step;
+      issue(A, n2, false, c1, nbase);
+      compute(Bq, n1, false, c1, nbase);
+      if (n2 >= c1) break;
+      base = n2;
+    }
+  }
 
   // per-member totals over the 4 lanes of a member, then hand the states to LDS
   l_part += __shfl_xor(l_part, 16, 64);
@@ -373,13 +446,14 @@ __global__ __launch_bounds__(kDecThreads) void decode_mfma_kernel(
       for (int par = 0; par < 2; ++par)
         so[(wave * kMaxMembers + mem) * D + 32 * c + 8 * grp + 2 * r + par] = acc[c][par][r];
   __syncthreads();
-  finish_split<D>(geo, u, sp, splits, Mu, sm, sl, so, part, done, O);
+  finish_split<D>(geo, u, sp, splits, Mu, sm, sl, so, reinterpret_cast<float*>(smem), part, done,
+                  O);
 }
 
 template <typename T>
-hipError_t launch_decode_t(const Geom& geo, const void* K, const void* V, const void* Q,
-                           const LevelBufs& l1, int anchor, int splits, float* partials,
-                           uint32_t* done_dec, float* O, hipStream_t s) {
+hipError_t launch_valu(const Geom& geo, const void* K, const void* V, const void* Q,
+                       const LevelBufs& l1, int anchor, int splits, float* partials,
+                       uint32_t* done_dec, float* O, hipStream_t s) {
   dim3 grid(splits, geo.U);
   const float sigma = 1.0f / sqrtf((float)geo.D);
   if (geo.D == 64)
@@ -398,6 +472,7 @@ hipError_t launch_decode_t(const Geom& geo, const void* K, const void* V, const 
 hipError_t launch_decode(const Geom& geo, int dtype, const void* K, const void* V,
                          const void* Q, const LevelBufs& l1, int anchor, int splits,
                          float* partials, uint32_t* done_dec, float* O, hipStream_t s) {
+  if (splits < 1 || splits > kMaxSplits) return hipErrorInvalidValue;
   if (dtype == ZHA_BF16) {
     dim3 grid(splits, geo.U);
     const float sigma = 1.0f / sqrtf((float)geo.D);
@@ -411,7 +486,7 @@ hipError_t launch_decode(const Geom& geo, int dtype, const void* K, const void* 
                          partials, done_dec, O, sigma);
     return hipGetLastError();
   }
-  return launch_decode_t<float>(geo, K, V, Q, l1, anchor, splits, partials, done_dec, O, s);
+  return launch_valu<float>(geo, K, V, Q, l1, anchor, splits, partials, done_dec, O, s);
 }
 
 }  // namespace zha

@@ -11,6 +11,7 @@ namespace zha {
 constexpr int kNRef = ZHA_N_REF;   // reference queries per KV head
 constexpr int kMaxMembers = 16;    // query heads (x queries) sharing one union list
 constexpr int kMaxLog2Nodes = 21;  // frontier bound that keeps 2^42-scaled masses in u64
+constexpr int kMaxSplits = 128;    // decode splits per unit (partials merged in one workgroup)
 
 typedef uint16_t bf16_t;
 
