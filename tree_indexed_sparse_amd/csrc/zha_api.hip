@@ -220,20 +220,36 @@ int zha_tree_append(zha_tree* t, const void* K, const void* R, int n_new, void* 
                 t->N_cap);
   hipStream_t s = (hipStream_t)stream;
   const int units = t->B * t->Hkv;
-  int64_t cap_prev = t->N_cap, b_l = 1;
-  for (int l = 1; l <= t->L; ++l) {
-    b_l *= t->b;
-    const int64_t cap_l = t->N_cap / b_l;
+  // level l has N_cap / b^l nodes of capacity per (sequence, KV head)
+  auto cap_nodes = [&](int l) { return (int64_t)t->N_cap / ipow(t->b, l); };
+  for (int l = 1; l <= t->L;) {
     const void* child = (l == 1) ? K : (const void*)(t->pyramid + t->level_off[l - 1]);
     const int dt_in = (l == 1) ? t->dtype : ZHA_F32;
-    hipError_t e = timed(ZHA_K_POOL, l, s, [&] {
-      return launch_pool_level(dt_in, child, cap_prev * t->d, R, t->dtype,
-                               t->pyramid + t->level_off[l], cap_l * t->d, units, t->Hkv,
-                               (int)(t->N / b_l), (int)((t->N + (int64_t)n_new) / b_l), t->b,
-                               t->d, s);
-    });
+    const int64_t b_prev = ipow(t->b, l - 1);
+    const int row_begin = (int)(t->N / b_prev), row_end = (int)((t->N + (int64_t)n_new) / b_prev);
+    const int k = fused_levels(t->b, t->L - l + 1);
+    hipError_t e;
+    if (k >= 1) {
+      float* outs[ZHA_MAX_LEVELS];
+      int64_t strides[ZHA_MAX_LEVELS];
+      for (int j = 0; j < k; ++j) {
+        outs[j] = t->pyramid + t->level_off[l + j];
+        strides[j] = cap_nodes(l + j) * t->d;
+      }
+      e = timed(ZHA_K_POOL, l, s, [&] {
+        return launch_pool_fused(dt_in, child, cap_nodes(l - 1) * t->d, R, t->dtype, outs, strides,
+                                 k, units, t->Hkv, row_begin, row_end, t->b, t->d, s);
+      });
+      l += k;
+    } else {
+      e = timed(ZHA_K_POOL, l, s, [&] {
+        return launch_pool_level(dt_in, child, cap_nodes(l - 1) * t->d, R, t->dtype,
+                                 t->pyramid + t->level_off[l], cap_nodes(l) * t->d, units, t->Hkv,
+                                 row_begin / t->b, row_end / t->b, t->b, t->d, s);
+      });
+      l += 1;
+    }
     if (e != hipSuccess) return hip_fail(e, "pooling launch");
-    cap_prev = cap_l;
   }
   t->N += n_new;
   return ZHA_OK;

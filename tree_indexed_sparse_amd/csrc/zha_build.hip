@@ -166,6 +166,179 @@ __global__ __launch_bounds__(kPoolThreads) void pool_large_kernel(
   if (threadIdx.x < D) out[unit * out_unit_stride + (int64_t)node * D + threadIdx.x] = acc;
 }
 
+// ------------------------------------------------------------------------------------
+// Fused tile pooling for b <= 64: a workgroup stages TR = b^k child rows in LDS and pools
+// k consecutive levels from them (TR <= 64), so the child level is read once and every
+// pooled level is written once. The 16 x d reference-query contraction runs on the matrix
+// cores: v_mfma_f32_16x16x32_bf16 when the children are bf16 keys (products exact in
+// fp32), v_mfma_f32_16x16x4_f32 for float32 summaries. One 16-row block per wave:
+// A = 16 child rows (read from LDS), B = R^T (held in registers), C = z^T[row][ref].
+// The softmax over each node's children, the mean over reference queries and the
+// weighted sum of the children run on the vector units in fixed orders.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kTileRows = 64;
+constexpr int kMaxFuse = 6;  // 2^6 = 64 rows
+constexpr int kTilesPerWG = 4;
+
+struct PoolOut {
+  float* ptr[kMaxFuse];
+  int64_t unit_stride[kMaxFuse];
+};
+
+__device__ __forceinline__ uint4 lds16(const uint32_t* p) { return *reinterpret_cast<const uint4*>(p); }
+
+template <typename Tin, typename Tr, int D>
+__global__ __launch_bounds__(kPoolThreads) void pool_tile_kernel(
+    const Tin* __restrict__ child, int64_t in_unit_stride, const Tr* __restrict__ Rall,
+    PoolOut out, int nlev, int Hkv, int tile_begin, int tile_end, int b, float tau) {
+  constexpr bool kBF = sizeof(Tin) == 2;
+  constexpr int RWb = D / 2 + 4;  // bf16 row stride in dwords (padding spreads banks)
+  constexpr int RWf = D + 4;      // fp32 row stride in floats
+  constexpr int IN_WORDS = kBF ? kTileRows * RWb : kTileRows * RWf;
+  __shared__ uint32_t sIn[IN_WORDS];
+  __shared__ float sY[2][(kTileRows / 2) * RWf];
+  __shared__ float zs[kTileRows][kNRef + 1];
+  __shared__ float sw[kTileRows];
+
+  const int unit = blockIdx.y;
+  const int g = unit % Hkv;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int mem = lane & 15, grp = lane >> 4;
+  int TR = 1;
+  for (int j = 0; j < nlev; ++j) TR *= b;
+
+  // B operands: R^T. bf16 form for bf16 children, float32 form for float32 levels.
+  const Tr* R = Rall + (int64_t)g * kNRef * D;
+  bf16x8_t rb[D / 32];
+  float rf[D / 16][4];
+#pragma unroll
+  for (int kc = 0; kc < D / 32; ++kc) {
+    if constexpr (kBF)
+      rb[kc] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(R + mem * D + 32 * kc + 8 * grp));
+    else
+      rb[kc] = bf16x8_t{};
+  }
+#pragma unroll
+  for (int q = 0; q < D / 16; ++q)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) rf[q][e] = to_f32(R[mem * D + 16 * q + 4 * grp + e]);
+
+  // child rows of tile t go through registers: the next tile's loads are issued before
+  // the current tile is pooled
+  constexpr int VPR = kBF ? D / 8 : D / 4;   // 16-byte vectors per row
+  constexpr int PRE = kTileRows * VPR / kPoolThreads;
+  u32x4_t pre[PRE];
+  const u32x4_t* tiles = reinterpret_cast<const u32x4_t*>(child + unit * in_unit_stride);
+  const int tvec = TR * VPR;  // 16-byte vectors per tile
+  const int tfirst = tile_begin + blockIdx.x * kTilesPerWG;
+  if (tfirst < tile_end) {
+#pragma unroll
+    for (int q = 0; q < PRE; ++q) {
+      const int i = min((int)threadIdx.x + q * kPoolThreads, tvec - 1);
+      pre[q] = tiles[(int64_t)tfirst * tvec + i];
+    }
+  }
+  for (int ti = 0; ti < kTilesPerWG; ++ti) {
+    const int t = tfirst + ti;
+    if (t >= tile_end) break;
+    __syncthreads();  // the previous tile is fully consumed
+#pragma unroll
+    for (int q = 0; q < PRE; ++q) {
+      const int i = threadIdx.x + q * kPoolThreads;
+      if (i < TR * VPR) {
+        const int r = i / VPR, c = i % VPR;
+        *reinterpret_cast<u32x4_t*>(&sIn[r * (kBF ? RWb : RWf) + 4 * c]) = pre[q];
+      }
+    }
+    __syncthreads();
+    if (ti + 1 < kTilesPerWG && t + 1 < tile_end) {
+#pragma unroll
+      for (int q = 0; q < PRE; ++q) {
+        const int i = min((int)threadIdx.x + q * kPoolThreads, tvec - 1);
+        pre[q] = tiles[(int64_t)(t + 1) * tvec + i];
+      }
+    }
+
+    int rows = TR;
+    for (int j = 0; j < nlev; ++j) {
+      const bool bf_in = kBF && j == 0;
+      const float* inF = (j == 0) ? reinterpret_cast<const float*>(sIn) : sY[(j - 1) & 1];
+      // z^T for this level's rows, 16 rows per MFMA block, one block per wave
+      for (int blk = wave; blk * 16 < rows; blk += kPoolThreads / 64) {
+        const int row = 16 * blk + mem;
+        const bool rv = row < rows;
+        f32x4_t zc = {0.f, 0.f, 0.f, 0.f};
+        if (bf_in) {
+#pragma unroll
+          for (int kc = 0; kc < D / 32; ++kc) {
+            const uint4 a = rv ? lds16(&sIn[row * RWb + 16 * kc + 4 * grp]) : make_uint4(0u, 0u, 0u, 0u);
+            zc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), rb[kc], zc,
+                                                         0, 0, 0);
+          }
+        } else {
+#pragma unroll
+          for (int q = 0; q < D / 16; ++q) {
+            const float4 a = rv ? *reinterpret_cast<const float4*>(&inF[row * RWf + 16 * q + 4 * grp])
+                                : make_float4(0.f, 0.f, 0.f, 0.f);
+            zc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x, rf[q][0], zc, 0, 0, 0);
+            zc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y, rf[q][1], zc, 0, 0, 0);
+            zc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z, rf[q][2], zc, 0, 0, 0);
+            zc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.w, rf[q][3], zc, 0, 0, 0);
+          }
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int zr = 16 * blk + 4 * grp + r;
+          if (zr < rows) zs[zr][mem] = tau * zc[r];
+        }
+      }
+      __syncthreads();
+      const int nodes = rows / b;
+      // softmax over each node's children, per reference query
+      for (int i = threadIdx.x; i < nodes * kNRef; i += kPoolThreads) {
+        const int nd = i / kNRef, rf_ = i % kNRef;
+        float mx = -INFINITY;
+        for (int c = 0; c < b; ++c) mx = fmaxf(mx, zs[nd * b + c][rf_]);
+        float sum = 0.f;
+        for (int c = 0; c < b; ++c) sum += expf(zs[nd * b + c][rf_] - mx);
+        for (int c = 0; c < b; ++c) zs[nd * b + c][rf_] = expf(zs[nd * b + c][rf_] - mx) / sum;
+      }
+      __syncthreads();
+      for (int r = threadIdx.x; r < rows; r += kPoolThreads) {
+        float s = 0.f;
+#pragma unroll
+        for (int rf_ = 0; rf_ < kNRef; ++rf_) s += zs[r][rf_];
+        sw[r] = s * (1.f / kNRef);
+      }
+      __syncthreads();
+      float* dst = out.ptr[j] + unit * out.unit_stride[j] + (int64_t)t * nodes * D;
+      float* ynext = sY[j & 1];
+      for (int i = threadIdx.x; i < nodes * D; i += kPoolThreads) {
+        const int nd = i / D, k = i % D;
+        float acc = 0.f;
+        for (int c = 0; c < b; ++c) {
+          const int r = nd * b + c;
+          float x;
+          if (bf_in) {
+            const uint32_t w = sIn[r * RWb + (k >> 1)];
+            x = __uint_as_float((k & 1) ? (w & 0xffff0000u) : (w << 16));
+          } else {
+            x = inF[r * RWf + k];
+          }
+          acc = fmaf(sw[r], x, acc);
+        }
+        dst[(int64_t)nd * D + k] = acc;
+        if (j + 1 < nlev) ynext[nd * RWf + k] = acc;
+      }
+      __syncthreads();
+      rows = nodes;
+    }
+  }
+}
+
 template <typename Tin, typename Tr, int D>
 hipError_t launch_pool_t(const void* child, int64_t in_unit_stride, const void* R, float* out,
                          int64_t out_unit_stride, int units, int Hkv, int node_begin,
@@ -199,7 +372,63 @@ hipError_t launch_pool_d(int D, const void* child, int64_t in_unit_stride, const
                                      node_begin, node_end, b, s);
 }
 
+template <typename Tin, typename Tr, int D>
+hipError_t launch_tile_t(const void* child, int64_t in_unit_stride, const void* R,
+                         const PoolOut& out, int nlev, int units, int Hkv, int row_begin,
+                         int row_end, int b, hipStream_t s) {
+  int TR = 1;
+  for (int j = 0; j < nlev; ++j) TR *= b;
+  const int t0 = row_begin / TR, t1 = row_end / TR;
+  if (t1 <= t0) return hipSuccess;
+  dim3 grid((t1 - t0 + kTilesPerWG - 1) / kTilesPerWG, units);
+  hipLaunchKernelGGL((pool_tile_kernel<Tin, Tr, D>), grid, dim3(kPoolThreads), 0, s,
+                     (const Tin*)child, in_unit_stride, (const Tr*)R, out, nlev, Hkv, t0, t1, b,
+                     1.0f / sqrtf((float)D));
+  return hipGetLastError();
+}
+
+template <typename Tin, typename Tr>
+hipError_t launch_tile_d(int D, const void* child, int64_t in_unit_stride, const void* R,
+                         const PoolOut& out, int nlev, int units, int Hkv, int row_begin,
+                         int row_end, int b, hipStream_t s) {
+  if (D == 64)
+    return launch_tile_t<Tin, Tr, 64>(child, in_unit_stride, R, out, nlev, units, Hkv,
+                                      row_begin, row_end, b, s);
+  return launch_tile_t<Tin, Tr, 128>(child, in_unit_stride, R, out, nlev, units, Hkv, row_begin,
+                                     row_end, b, s);
+}
+
 }  // namespace
+
+int fused_levels(int b, int levels_left) {
+  int k = 0, tr = 1;
+  while (k < levels_left && k < kMaxFuse && tr * b <= kTileRows) {
+    tr *= b;
+    ++k;
+  }
+  return k;
+}
+
+hipError_t launch_pool_fused(int dtype_in, const void* child, int64_t in_unit_stride,
+                             const void* R, int dtype_r, float* const* outs,
+                             const int64_t* out_unit_strides, int nlev, int units, int Hkv,
+                             int row_begin, int row_end, int b, int D, hipStream_t s) {
+  if (nlev < 1 || nlev > kMaxFuse) return hipErrorInvalidValue;
+  PoolOut out{};
+  for (int j = 0; j < nlev; ++j) {
+    out.ptr[j] = outs[j];
+    out.unit_stride[j] = out_unit_strides[j];
+  }
+  if (dtype_r == ZHA_BF16) {
+    if (dtype_in == ZHA_BF16)
+      return launch_tile_d<bf16_t, bf16_t>(D, child, in_unit_stride, R, out, nlev, units, Hkv,
+                                           row_begin, row_end, b, s);
+    return launch_tile_d<float, bf16_t>(D, child, in_unit_stride, R, out, nlev, units, Hkv,
+                                        row_begin, row_end, b, s);
+  }
+  return launch_tile_d<float, float>(D, child, in_unit_stride, R, out, nlev, units, Hkv,
+                                     row_begin, row_end, b, s);
+}
 
 hipError_t launch_pool_level(int dtype_in, const void* child, int64_t in_unit_stride,
                              const void* R, int dtype_r, float* out, int64_t out_unit_stride,

@@ -74,6 +74,16 @@ hipError_t launch_pool_level(int dtype_in, const void* child, int64_t in_unit_st
                              int units, int Hkv, int node_begin, int node_end, int b, int D,
                              hipStream_t s);
 
+// Levels that one fused tile launch pools for branching factor b (0 if b > 64).
+int fused_levels(int b, int levels_left);
+
+// `nlev` consecutive levels pooled from one child level in one launch (b^nlev <= 64):
+// child rows [row_begin, row_end) -> outs[j] (level j + 1 above the child level).
+hipError_t launch_pool_fused(int dtype_in, const void* child, int64_t in_unit_stride,
+                             const void* R, int dtype_r, float* const* outs,
+                             const int64_t* out_unit_strides, int nlev, int units, int Hkv,
+                             int row_begin, int row_end, int b, int D, hipStream_t s);
+
 // zero `n` completion counters
 hipError_t launch_attend_init(uint32_t* done_all, int n, hipStream_t s);
 
