@@ -139,12 +139,12 @@ def main():
     for name, kind, levels in (("pool", LB.ZHA_K_POOL, range(1, L + 1)),
                                ("score", LB.ZHA_K_SCORE, range(1, L + 1)),
                                ("select", LB.ZHA_K_SELECT, range(1, L + 1)),
-                               ("init", LB.ZHA_K_INIT, [0]), ("decode", LB.ZHA_K_DECODE, [0])):
+                               ("compact", LB.ZHA_K_COMPACT, range(1, L + 1)),
+                               ("decode", LB.ZHA_K_DECODE, [0]), ("combine", LB.ZHA_K_COMBINE, [0])):
         for lv in levels:
             tot, n = ktime(kind, lv)
             if n:
-                kernels[f"{name}_l{lv}" if name in ("pool", "score", "select") else name] = dict(
-                    avg_ms=tot / n, launches=n)
+                kernels[f"{name}_l{lv}" if lv else name] = dict(avg_ms=tot / n, launches=n)
 
     # selection statistics and algorithmic bytes from this call's outputs
     attend_only()
@@ -233,8 +233,9 @@ def main():
         "time_split_ms": {
             "build": round(sum(v["avg_ms"] for k, v in kernels.items() if k.startswith("pool")), 4),
             "index": round(sum(v["avg_ms"] for k, v in kernels.items()
-                               if k.startswith(("score", "select", "init"))), 4),
-            "attend": round(kernels.get("decode", {}).get("avg_ms", 0.0), 4),
+                               if k.startswith(("score", "select", "compact"))), 4),
+            "attend": round(sum(v["avg_ms"] for k, v in kernels.items()
+                                if k in ("decode", "combine")), 4),
             "timed_pass_ms_per_step": round(ms_timed_pass, 4)},
         "kernels": {k: {"avg_ms": round(v["avg_ms"], 4), "launches": v["launches"]}
                     for k, v in kernels.items()},

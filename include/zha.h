@@ -14,7 +14,8 @@
  *
  * Conventions shared by every entry point:
  *   - Every pointer argument named as "device" is HIP device memory owned by the caller.
- *     The library allocates nothing and keeps no state beyond a thread-local error string.
+ *     The library allocates no device memory; its only state is a thread-local error
+ *     string and, while launch timing is enabled, the recorded HIP events.
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream). Entry points
  *     only enqueue work on it and never synchronise; device faults surface at the
  *     caller's next synchronisation.
@@ -142,11 +143,19 @@ int zha_attend_level_view(const zha_tree* t, int T, int Hq, int level, int64_t* 
  * zha_timing_enable(1) starts a fresh record and zha_timing_enable(0) stops recording.
  * zha_timing_read waits for the recorded events and returns, for one kernel kind and
  * pyramid level (level = -1: every level), the summed duration in milliseconds and the
- * number of launches. Kinds: ZHA_K_POOL (pooling, level 1 reads the keys), ZHA_K_INIT,
- * ZHA_K_SCORE, ZHA_K_SELECT, ZHA_K_DECODE (decode and split-combine; level 0).
- * Recording creates HIP events (host-side objects), so it is off by default.
+ * number of launches. Kinds: ZHA_K_POOL (pooling; the level is the first level a launch
+ * writes, level 1 reads the keys), ZHA_K_SCORE, ZHA_K_SELECT, ZHA_K_COMPACT (per level),
+ * ZHA_K_DECODE and ZHA_K_COMBINE (level 0). Recording creates HIP events (host-side
+ * objects), so it is off by default.
  */
-enum { ZHA_K_POOL = 0, ZHA_K_INIT = 1, ZHA_K_SCORE = 2, ZHA_K_SELECT = 3, ZHA_K_DECODE = 4 };
+enum {
+  ZHA_K_POOL = 0,
+  ZHA_K_SCORE = 2,
+  ZHA_K_SELECT = 3,
+  ZHA_K_DECODE = 4,
+  ZHA_K_COMPACT = 5,
+  ZHA_K_COMBINE = 6
+};
 int zha_timing_enable(int on);
 int zha_timing_read(int kind, int level, double* total_ms, int64_t* launches);
 

@@ -40,7 +40,7 @@ EXPORTS = (
     "zha_last_error",
 )
 
-ZHA_K_POOL, ZHA_K_INIT, ZHA_K_SCORE, ZHA_K_SELECT, ZHA_K_DECODE = 0, 1, 2, 3, 4
+ZHA_K_POOL, ZHA_K_SCORE, ZHA_K_SELECT, ZHA_K_DECODE, ZHA_K_COMPACT, ZHA_K_COMBINE = 0, 2, 3, 4, 5, 6
 
 
 class ZhaError(RuntimeError):

@@ -102,10 +102,9 @@ int check_geometry(int B, int Hkv, int N, int N_cap, int d, int b, int L) {
 struct WsLayout {
   int U, QH, splits;
   int64_t n[ZHA_MAX_LEVELS + 1];  // nodes per unit at each level (current N)
-  int64_t off_done, off_count, off_lvl, off_S, off_part;
-  int64_t off_nodes[ZHA_MAX_LEVELS + 1], off_masks[ZHA_MAX_LEVELS + 1],
-      off_keep[ZHA_MAX_LEVELS + 1];
-  int64_t S_stride;
+  int64_t off_count, off_lvl, off_S, off_bits, off_part;
+  int64_t off_nodes[ZHA_MAX_LEVELS + 1], off_masks[ZHA_MAX_LEVELS + 1];
+  int64_t S_stride, bit_words;
   int64_t total;
 };
 
@@ -145,8 +144,6 @@ WsLayout layout_of(const Geom& g) {
     w.n[l] = nl;
   }
   int64_t off = 0;
-  w.off_done = off;
-  off = align256(off + 4 * (int64_t)(g.L + 1) * g.U);
   w.off_count = off;
   off = align256(off + 4 * (int64_t)(g.L + 1) * g.U);
   w.off_lvl = off;
@@ -157,12 +154,13 @@ WsLayout layout_of(const Geom& g) {
     off = align256(off + bytes);
     w.off_masks[l] = off;
     off = align256(off + bytes);
-    w.off_keep[l] = off;
-    off = align256(off + bytes);
   }
-  w.S_stride = w.n[1];
+  w.S_stride = (w.n[1] + 3) / 4 * 4;  // score rows start 16-byte aligned
   w.off_S = off;
   off = align256(off + 4 * (int64_t)w.QH * w.S_stride);
+  w.bit_words = (w.n[1] + 31) / 32;
+  w.off_bits = off;
+  off = align256(off + 4 * (int64_t)w.QH * w.bit_words);
   w.off_part = off;
   off = align256(off + 4 * (int64_t)g.U * w.splits * kMaxMembers * (g.D + 2));
   w.total = off;
@@ -173,9 +171,7 @@ LevelBufs level_bufs(char* ws, const WsLayout& w, int l) {
   LevelBufs lb;
   lb.nodes = (uint32_t*)(ws + w.off_nodes[l]);
   lb.masks = (uint32_t*)(ws + w.off_masks[l]);
-  lb.keep = (uint32_t*)(ws + w.off_keep[l]);
   lb.count = (uint32_t*)(ws + w.off_count) + (int64_t)l * w.U;
-  lb.done = (uint32_t*)(ws + w.off_done) + (int64_t)(l - 1) * w.U;
   lb.stride = w.n[l];
   return lb;
 }
@@ -346,14 +342,11 @@ int zha_attend(const zha_tree* t, const void* Q, int T, int Hq, const void* K, c
   char* ws = (char*)workspace;
   LevelBufs lv[ZHA_MAX_LEVELS + 2];
   for (int l = 1; l <= t->L; ++l) lv[l] = level_bufs(ws, w, l);
-  uint32_t* done_dec = (uint32_t*)(ws + w.off_done) + (int64_t)t->L * w.U;
   float* S = (float*)(ws + w.off_S);
   int32_t* lvl = (int32_t*)(ws + w.off_lvl);
+  const KeepBits kb{(uint32_t*)(ws + w.off_bits), w.bit_words};
 
-  hipError_t e = timed(ZHA_K_INIT, 0, s, [&] {
-    return launch_attend_init((uint32_t*)(ws + w.off_done), (t->L + 1) * w.U, s);
-  });
-  if (e != hipSuccess) return hip_fail(e, "init launch");
+  hipError_t e = hipSuccess;
   int64_t cap_l = t->N_cap;
   for (int l = 1; l <= t->L; ++l) cap_l /= t->b;  // capacity nodes at the top level
   for (int l = t->L; l >= 1; --l) {
@@ -361,22 +354,25 @@ int zha_attend(const zha_tree* t, const void* Q, int T, int Hq, const void* K, c
     const int n_top = (l == t->L) ? (int)w.n[t->L] : 0;
     const float* X = t->pyramid + t->level_off[l];
     e = timed(ZHA_K_SCORE, l, s, [&] {
-      return launch_score(g, l, X, cap_l * t->d, Q, t->dtype, parent, n_top, S, w.S_stride,
-                          lv[l], s);
+      return launch_score(g, X, cap_l * t->d, Q, t->dtype, parent, n_top, S, w.S_stride, s);
     });
     if (e != hipSuccess) return hip_fail(e, "score launch");
     e = timed(ZHA_K_SELECT, l, s, [&] {
-      return launch_select(g, l, S, w.S_stride, parent, n_top, lv[l], p, anchor,
+      return launch_select(g, l, S, w.S_stride, parent, n_top, kb, p, anchor,
                            l == 1 ? sel_idx : nullptr, cap, sel_count, lvl, s);
     });
     if (e != hipSuccess) return hip_fail(e, "select launch");
+    e = timed(ZHA_K_COMPACT, l, s, [&] { return launch_compact(g, parent, n_top, kb, lv[l], s); });
+    if (e != hipSuccess) return hip_fail(e, "compact launch");
     cap_l *= t->b;
   }
+  float* part = (float*)(ws + w.off_part);
   e = timed(ZHA_K_DECODE, 0, s, [&] {
-    return launch_decode(g, t->dtype, K, V, Q, lv[1], anchor, w.splits,
-                         (float*)(ws + w.off_part), done_dec, O, s);
+    return launch_decode(g, t->dtype, K, V, Q, lv[1], anchor, w.splits, part, s);
   });
   if (e != hipSuccess) return hip_fail(e, "decode launch");
+  e = timed(ZHA_K_COMBINE, 0, s, [&] { return launch_combine(g, w.splits, part, O, s); });
+  if (e != hipSuccess) return hip_fail(e, "combine launch");
   return ZHA_OK;
 }
 

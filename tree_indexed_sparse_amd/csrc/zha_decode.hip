@@ -10,9 +10,9 @@
 // read once per unit and scored for every member; tokens outside a member's own set are
 // masked. Tokens below `anchor` are skipped inside nodes and attended once, for every
 // member, by split 0. The union token range is cut into `splits` equal pieces; each
-// workgroup writes one (max, sum, weighted-V) partial per member and the last workgroup
-// of a unit merges the partials in split order, so the result does not depend on which
-// workgroup finishes last.
+// workgroup writes one (max, sum, weighted-V) partial per member, and a separate combine
+// launch merges a unit's partials in split order, so the result does not depend on the
+// order in which workgroups run.
 
 #include "zha_internal.h"
 
@@ -24,14 +24,10 @@ constexpr int kDecWaves = kDecThreads / 64;
 constexpr int kNodeChunk = 2048;  // union-list entries staged in LDS at a time
 
 // Merge the per-wave states (sm, sl: [wave][member], so: [wave][member][D], in LDS) into
-// this split's partial, then let the unit's last workgroup combine all splits in split
-// order and write O. `scratch` is LDS for 2 * kMaxSplits * kMaxMembers floats that may
-// alias sm/sl/so. Every thread of the workgroup calls this.
+// this split's partial (max, sum, sum of p * v per member). Every thread calls this.
 template <int D>
-__device__ void finish_split(const Geom& geo, int u, int sp, int splits, int Mu, const float* sm,
-                             const float* sl, const float* so, float* scratch,
-                             float* __restrict__ part, uint32_t* __restrict__ done,
-                             float* __restrict__ O) {
+__device__ void write_partial(int u, int sp, int splits, int Mu, const float* sm, const float* sl,
+                              const float* so, float* __restrict__ part) {
   const int64_t pstride = (int64_t)(D + 2);
   float* pu = part + ((int64_t)u * splits + sp) * kMaxMembers * pstride;
   for (int idx = threadIdx.x; idx < Mu * D; idx += kDecThreads) {
@@ -54,53 +50,47 @@ __device__ void finish_split(const Geom& geo, int u, int sp, int splits, int Mu,
       pu[m * pstride + D + 1] = lsum;
     }
   }
+}
 
-  // the unit's last workgroup combines every split, in split order
-  __threadfence();
-  __syncthreads();
-  __shared__ uint32_t last;
-  if (threadIdx.x == 0) last = (atomicAdd(&done[u], 1u) == (uint32_t)splits - 1u) ? 1u : 0u;
-  __syncthreads();
-  if (!last) return;
-  __threadfence();
-  const float* pall = part + (int64_t)u * splits * kMaxMembers * pstride;
-  float* cm = scratch;                              // [split][member] max, then weight
-  float* cl = scratch + kMaxSplits * kMaxMembers;   // [split][member] sum
-  for (int idx = threadIdx.x; idx < splits * Mu; idx += kDecThreads) {
-    const int s2 = idx / Mu, m = idx % Mu;
-    const float* ps = pall + (s2 * kMaxMembers + m) * pstride;
-    cm[s2 * kMaxMembers + m] = __hip_atomic_load(&ps[D], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    cl[s2 * kMaxMembers + m] =
-        __hip_atomic_load(&ps[D + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// One workgroup per (unit, member): merge the member's partials of every split, in split
+// order, into its output row. Runs after the decode launch, which orders it.
+constexpr int kCombThreads = 128;
+
+template <int D>
+__global__ __launch_bounds__(kCombThreads) void combine_kernel(Geom geo, int splits,
+                                                               const float* __restrict__ part,
+                                                               float* __restrict__ O) {
+  __shared__ float sw[kMaxSplits], sl[kMaxSplits];
+  __shared__ float sM, sL;
+  const int u = blockIdx.x, m = blockIdx.y;
+  if (m >= members_of(geo, u)) return;
+  const int64_t pstride = (int64_t)(D + 2);
+  const int64_t sstride = kMaxMembers * pstride;  // between splits
+  const float* pm = part + ((int64_t)u * splits * kMaxMembers + m) * pstride;
+  for (int s2 = threadIdx.x; s2 < splits; s2 += kCombThreads) {
+    sw[s2] = pm[s2 * sstride + D];
+    sl[s2] = pm[s2 * sstride + D + 1];
   }
   __syncthreads();
-  if (threadIdx.x < Mu) {
-    const int m = threadIdx.x;
+  if (threadIdx.x == 0) {
     float M = -INFINITY;
-    for (int s2 = 0; s2 < splits; ++s2) M = fmaxf(M, cm[s2 * kMaxMembers + m]);
+    for (int s2 = 0; s2 < splits; ++s2) M = fmaxf(M, sw[s2]);
     float L = 0.f;
-    for (int s2 = 0; s2 < splits; ++s2) {
-      const float ms = cm[s2 * kMaxMembers + m];
-      if (ms != -INFINITY) L = fmaf(expf(ms - M), cl[s2 * kMaxMembers + m], L);
-    }
-    for (int s2 = 0; s2 < splits; ++s2) {
-      const float ms = cm[s2 * kMaxMembers + m];
-      cm[s2 * kMaxMembers + m] = (ms == -INFINITY) ? 0.f : expf(ms - M) / L;
-    }
+    for (int s2 = 0; s2 < splits; ++s2)
+      if (sw[s2] != -INFINITY) L = fmaf(expf(sw[s2] - M), sl[s2], L);
+    sM = M;
+    sL = L;
   }
   __syncthreads();
-  for (int idx = threadIdx.x; idx < Mu * D; idx += kDecThreads) {
-    const int m = idx / D, k = idx % D;
+  for (int s2 = threadIdx.x; s2 < splits; s2 += kCombThreads)
+    sw[s2] = (sw[s2] == -INFINITY) ? 0.f : expf(sw[s2] - sM) / sL;
+  __syncthreads();
+  for (int k = threadIdx.x; k < D; k += kCombThreads) {
     float acc = 0.f;
 #pragma unroll 8
-    for (int s2 = 0; s2 < splits; ++s2) {
-      const float o = __hip_atomic_load(&pall[(s2 * kMaxMembers + m) * pstride + k],
-                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      acc = fmaf(cm[s2 * kMaxMembers + m], o, acc);
-    }
+    for (int s2 = 0; s2 < splits; ++s2) acc = fmaf(sw[s2], pm[s2 * sstride + k], acc);
     O[(int64_t)qh_of(geo, u, m) * D + k] = acc;
   }
-  if (threadIdx.x == 0) done[u] = 0u;
 }
 
 __device__ __forceinline__ void split_range(int ntok, int splits, int sp, int align, int* t0,
@@ -115,8 +105,7 @@ __device__ __forceinline__ void split_range(int ntok, int splits, int sp, int al
 template <typename T, int D>
 __global__ __launch_bounds__(kDecThreads) void decode_valu_kernel(
     Geom geo, const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ Q,
-    LevelBufs l1, int anchor, int splits, float* __restrict__ part, uint32_t* __restrict__ done,
-    float* __restrict__ O, float sigma) {
+    LevelBufs l1, int anchor, int splits, float* __restrict__ part, float sigma) {
   constexpr int DPL = D / 64;  // dims per lane
   const int u = blockIdx.y, sp = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -180,9 +169,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_valu_kernel(
 
   // merge the waves' states through LDS, in wave order
   __shared__ float sm[kDecWaves][kMaxMembers], sl[kDecWaves][kMaxMembers];
-  __shared__ float so[kDecWaves * kMaxMembers * D > 2 * kMaxSplits * kMaxMembers
-                          ? kDecWaves * kMaxMembers * D
-                          : 2 * kMaxSplits * kMaxMembers];
+  __shared__ float so[kDecWaves * kMaxMembers * D];
 #pragma unroll
   for (int m = 0; m < kMaxMembers; ++m) {
     if (lane == 0) {
@@ -193,7 +180,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_valu_kernel(
     for (int i = 0; i < DPL; ++i) so[(wave * kMaxMembers + m) * D + lane * DPL + i] = o[m][i];
   }
   __syncthreads();
-  finish_split<D>(geo, u, sp, splits, Mu, &sm[0][0], &sl[0][0], so, so, part, done, O);
+  write_partial<D>(u, sp, splits, Mu, &sm[0][0], &sl[0][0], so, part);
 }
 
 // ------------------------------------------------------------------------------------
@@ -234,7 +221,7 @@ template <int D>
 __global__ __launch_bounds__(kDecThreads) void decode_mfma_kernel(
     Geom geo, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
     const bf16_t* __restrict__ Q, LevelBufs l1, int anchor, int splits, float* __restrict__ part,
-    uint32_t* __restrict__ done, float* __restrict__ O, float sigma) {
+    float sigma) {
   constexpr int KC = D / 32;          // 32-dim chunks: QK k-steps and PV column blocks
   constexpr int RW = D / 2 + 4;       // LDS row stride in dwords (padding spreads banks)
   constexpr int CH = D / 8;           // 16-byte chunks per row
@@ -242,9 +229,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_mfma_kernel(
   constexpr int NI = kTile / RPI;     // such loads per tile
   constexpr int VWORDS = kDecWaves * kTile * RW;
   constexpr int MWORDS = kDecWaves * kMaxMembers * (D + 2);
-  constexpr int CWORDS = 2 * kMaxSplits * kMaxMembers;
-  constexpr int W1 = VWORDS > MWORDS ? VWORDS : MWORDS;
-  __shared__ uint32_t smem[W1 > CWORDS ? W1 : CWORDS];
+  __shared__ uint32_t smem[VWORDS > MWORDS ? VWORDS : MWORDS];
   __shared__ uint32_t s_nodes[kNodeChunk], s_masks[kNodeChunk];
 
   const int u = blockIdx.y, sp = blockIdx.x;
@@ -446,47 +431,41 @@ __global__ __launch_bounds__(kDecThreads) void decode_mfma_kernel(
       for (int par = 0; par < 2; ++par)
         so[(wave * kMaxMembers + mem) * D + 32 * c + 8 * grp + 2 * r + par] = acc[c][par][r];
   __syncthreads();
-  finish_split<D>(geo, u, sp, splits, Mu, sm, sl, so, reinterpret_cast<float*>(smem), part, done,
-                  O);
-}
-
-template <typename T>
-hipError_t launch_valu(const Geom& geo, const void* K, const void* V, const void* Q,
-                       const LevelBufs& l1, int anchor, int splits, float* partials,
-                       uint32_t* done_dec, float* O, hipStream_t s) {
-  dim3 grid(splits, geo.U);
-  const float sigma = 1.0f / sqrtf((float)geo.D);
-  if (geo.D == 64)
-    hipLaunchKernelGGL((decode_valu_kernel<T, 64>), grid, dim3(kDecThreads), 0, s, geo,
-                       (const T*)K, (const T*)V, (const T*)Q, l1, anchor, splits, partials,
-                       done_dec, O, sigma);
-  else
-    hipLaunchKernelGGL((decode_valu_kernel<T, 128>), grid, dim3(kDecThreads), 0, s, geo,
-                       (const T*)K, (const T*)V, (const T*)Q, l1, anchor, splits, partials,
-                       done_dec, O, sigma);
-  return hipGetLastError();
+  write_partial<D>(u, sp, splits, Mu, sm, sl, so, part);
 }
 
 }  // namespace
 
 hipError_t launch_decode(const Geom& geo, int dtype, const void* K, const void* V,
                          const void* Q, const LevelBufs& l1, int anchor, int splits,
-                         float* partials, uint32_t* done_dec, float* O, hipStream_t s) {
+                         float* partials, hipStream_t s) {
   if (splits < 1 || splits > kMaxSplits) return hipErrorInvalidValue;
+  dim3 grid(splits, geo.U);
+  const float sigma = 1.0f / sqrtf((float)geo.D);
+#define ZHA_DEC(KERNEL, T)                                                                    \
+  hipLaunchKernelGGL(KERNEL, grid, dim3(kDecThreads), 0, s, geo, (const T*)K, (const T*)V,     \
+                     (const T*)Q, l1, anchor, splits, partials, sigma)
   if (dtype == ZHA_BF16) {
-    dim3 grid(splits, geo.U);
-    const float sigma = 1.0f / sqrtf((float)geo.D);
-    if (geo.D == 64)
-      hipLaunchKernelGGL((decode_mfma_kernel<64>), grid, dim3(kDecThreads), 0, s, geo,
-                         (const bf16_t*)K, (const bf16_t*)V, (const bf16_t*)Q, l1, anchor, splits,
-                         partials, done_dec, O, sigma);
-    else
-      hipLaunchKernelGGL((decode_mfma_kernel<128>), grid, dim3(kDecThreads), 0, s, geo,
-                         (const bf16_t*)K, (const bf16_t*)V, (const bf16_t*)Q, l1, anchor, splits,
-                         partials, done_dec, O, sigma);
-    return hipGetLastError();
+    if (geo.D == 64) ZHA_DEC((decode_mfma_kernel<64>), bf16_t);
+    else ZHA_DEC((decode_mfma_kernel<128>), bf16_t);
+  } else {
+    if (geo.D == 64) ZHA_DEC((decode_valu_kernel<float, 64>), float);
+    else ZHA_DEC((decode_valu_kernel<float, 128>), float);
   }
-  return launch_valu<float>(geo, K, V, Q, l1, anchor, splits, partials, done_dec, O, s);
+#undef ZHA_DEC
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const Geom& geo, int splits, const float* partials, float* O,
+                          hipStream_t s) {
+  dim3 grid(geo.U, geo.Tb * geo.G);
+  if (geo.D == 64)
+    hipLaunchKernelGGL((combine_kernel<64>), grid, dim3(kCombThreads), 0, s, geo, splits,
+                       partials, O);
+  else
+    hipLaunchKernelGGL((combine_kernel<128>), grid, dim3(kCombThreads), 0, s, geo, splits,
+                       partials, O);
+  return hipGetLastError();
 }
 
 }  // namespace zha

@@ -56,12 +56,17 @@ __host__ __device__ __forceinline__ int bg_of(const Geom& g, int u) { return u /
 
 // Per-level union lists in the workspace.
 struct LevelBufs {
-  uint32_t* nodes;   // [U][stride] kept node ids (ascending), written by the selector
+  uint32_t* nodes;   // [U][stride] kept node ids (ascending)
   uint32_t* masks;   // [U][stride] member bitmask per kept node
   uint32_t* count;   // [U]
-  uint32_t* keep;    // [U][stride] member bitmask per frontier entry (frontier index space)
-  uint32_t* done;    // [U] members finished at this level
   int64_t stride;    // = nodes at this level
+};
+
+// Per-query-head kept flags over the current frontier (bit k of row qh), rewritten at
+// every level by the selector and read by the compaction.
+struct KeepBits {
+  uint32_t* bits;    // [QH][words]
+  int64_t words;
 };
 
 // ---------------------------------------------------------------------------------------
@@ -84,20 +89,27 @@ hipError_t launch_pool_fused(int dtype_in, const void* child, int64_t in_unit_st
                              const int64_t* out_unit_strides, int nlev, int units, int Hkv,
                              int row_begin, int row_end, int b, int D, hipStream_t s);
 
-// zero `n` completion counters
-hipError_t launch_attend_init(uint32_t* done_all, int n, hipStream_t s);
+// Scores of a level's union frontier for every member: S[qh][k].
+hipError_t launch_score(const Geom& geo, const float* X, int64_t X_unit_stride, const void* Q,
+                        int dtype, const LevelBufs* parent, int n_top, float* S,
+                        int64_t S_stride, hipStream_t s);
 
-hipError_t launch_score(const Geom& geo, int level, const float* X, int64_t X_unit_stride,
-                        const void* Q, int dtype, const LevelBufs* parent, int n_top,
-                        float* S, int64_t S_stride, const LevelBufs& cur, hipStream_t s);
-
+// Per-member top-p: kept flags into `kb`; at level 1 also the token lists and counts.
 hipError_t launch_select(const Geom& geo, int level, const float* S, int64_t S_stride,
-                         const LevelBufs* parent, int n_top, const LevelBufs& cur, float p,
-                         int anchor, int32_t* sel_idx, int64_t cap, int32_t* sel_count,
-                         int32_t* lvl_kept, hipStream_t s);
+                         const LevelBufs* parent, int n_top, KeepBits kb, float p, int anchor,
+                         int32_t* sel_idx, int64_t cap, int32_t* sel_count, int32_t* lvl_kept,
+                         hipStream_t s);
+
+// Union of the members' kept flags -> ascending kept-node list with member masks.
+hipError_t launch_compact(const Geom& geo, const LevelBufs* parent, int n_top, KeepBits kb,
+                          const LevelBufs& cur, hipStream_t s);
 
 hipError_t launch_decode(const Geom& geo, int dtype, const void* K, const void* V,
                          const void* Q, const LevelBufs& l1, int anchor, int splits,
-                         float* partials, uint32_t* done_dec, float* O, hipStream_t s);
+                         float* partials, hipStream_t s);
+
+// Merge the decode partials of every split, in split order, into O.
+hipError_t launch_combine(const Geom& geo, int splits, const float* partials, float* O,
+                          hipStream_t s);
 
 }  // namespace zha

@@ -10,15 +10,21 @@
 //
 // GQA: the members of a unit (the query heads, and queries, that read one KV head) share
 // one union frontier per level, so each summary row is read once and scored for every
-// member. Each member then selects over its own sub-frontier.
+// member. Each member then selects over its own sub-frontier, and a per-unit compaction
+// turns the members' kept flags into the next level's union list.
+//
+// One level = three launches (score, select, compact). Kernel boundaries order them; no
+// kernel here uses a device-scope fence.
 
 #include "zha_internal.h"
 
 namespace zha {
 namespace {
 
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
 constexpr int kScoreThreads = 256;
-constexpr int kScoreEntries = 256;  // frontier entries per workgroup
+constexpr int kScoreEntries = 256;  // frontier entries per workgroup (64 per wave)
 
 constexpr int kSelThreads = 512;
 constexpr int kSelWaves = kSelThreads / 64;
@@ -27,6 +33,9 @@ constexpr int kCand = 2048;
 constexpr float kMassScale = 4398046511104.0f;  // 2^42: fixed-point scale of a node mass
 constexpr float kMaxSpread = 32.0f;             // exp(-32) * 2^42 < 1: lower masses are 0
 
+constexpr int kCompactThreads = 1024;
+constexpr int kCompactChunk = 16384;            // frontier entries per compaction step
+
 // node id of frontier entry k: the top level's frontier is every node; below, entry k
 // is child k % b of the (k / b)-th node the level above kept (pnodes: that unit's list)
 __device__ __forceinline__ uint32_t frontier_node(const uint32_t* pnodes, int k, int b) {
@@ -34,64 +43,84 @@ __device__ __forceinline__ uint32_t frontier_node(const uint32_t* pnodes, int k,
   return pnodes[k / b] * (uint32_t)b + (uint32_t)(k % b);
 }
 
+// ------------------------------------------------------------------------------ score
+// S^T[row][member] = X[row] . Q[member] on v_mfma_f32_16x16x4_f32, 16 frontier rows per
+// MFMA block: lane (member = l % 16, group = l / 16) feeds row `member`'s dims
+// 16q + 4 group + e as A and member `member`'s query at the same dims as B, so each
+// lane's 16-byte row loads are contiguous within the row. The C block leaves four
+// consecutive rows of one member per lane, stored as one 16-byte write.
 template <int D, typename Tq>
 __global__ __launch_bounds__(kScoreThreads) void score_kernel(
     Geom geo, const float* __restrict__ X, int64_t X_unit_stride, const Tq* __restrict__ Q,
     LevelBufs parent, int has_parent, int n_top, float* __restrict__ S, int64_t S_stride,
-    LevelBufs cur, float sigma) {
-  constexpr int LPR = D / 4;       // lanes per row (4 floats per lane)
-  constexpr int RPW = 64 / LPR;    // rows per wave per step
+    float sigma) {
+  constexpr int NQ = D / 16;
+  constexpr int kMaxParents = kScoreEntries / 2 + 2;
+  __shared__ uint32_t sPn[kMaxParents];
+
   const int u = blockIdx.y;
-  const int F = has_parent ? geo.b * (int)parent.count[u] : n_top;
+  const int b = geo.b;
+  const int F = has_parent ? b * (int)parent.count[u] : n_top;
   const int k_wg = blockIdx.x * kScoreEntries;
   if (k_wg >= F) return;
   const int Mu = members_of(geo, u);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int sub = lane / LPR, li = lane % LPR;
+  const int mem = lane & 15, grp = lane >> 4;
 
-  float q[kMaxMembers][4];
-#pragma unroll
-  for (int m = 0; m < kMaxMembers; ++m) {
-    if (m < Mu) {
-      const Tq* qp = Q + (int64_t)qh_of(geo, u, m) * D + li * 4;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) q[m][i] = to_f32(qp[i]);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) q[m][i] = 0.f;
-    }
+  const int p0 = k_wg / b;
+  if (has_parent) {
+    const int np = (min(k_wg + kScoreEntries, F) - 1) / b - p0 + 1;
+    for (int i = threadIdx.x; i < np; i += kScoreThreads)
+      sPn[i] = parent.nodes[u * parent.stride + p0 + i];
   }
+  float qf[NQ][4];
+  const Tq* qrow = Q + (int64_t)qh_of(geo, u, mem < Mu ? mem : 0) * D;
+#pragma unroll
+  for (int q = 0; q < NQ; ++q)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) qf[q][e] = mem < Mu ? to_f32(qrow[16 * q + 4 * grp + e]) : 0.f;
+  __syncthreads();
   const float* Xu = X + (int64_t)bg_of(geo, u) * X_unit_stride;
-  const uint32_t full = (Mu >= 32) ? 0xffffffffu : ((1u << Mu) - 1u);
-  const uint32_t* pnodes = has_parent ? parent.nodes + u * parent.stride : nullptr;
-  constexpr int kPerWave = kScoreEntries / (kScoreThreads / 64);
+  float* Srow = S + (int64_t)qh_of(geo, u, mem < Mu ? mem : 0) * S_stride;
+  const int k_wave = k_wg + wave * (kScoreEntries / 4);
 
-  for (int e = 0; e < kPerWave; e += RPW) {
-    const int k = k_wg + wave * kPerWave + e + sub;
-    const bool valid = k < F;
-    uint32_t mask = 0;
-    float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (valid) {
-      const uint32_t node = frontier_node(pnodes, k, geo.b);
-      mask = has_parent ? parent.masks[u * parent.stride + k / geo.b] : full;
-      x = *reinterpret_cast<const float4*>(Xu + (int64_t)node * D + li * 4);
-    }
-    float mine = 0.f;
 #pragma unroll
-    for (int m = 0; m < kMaxMembers; ++m) {
-      float v = q[m][0] * x.x;
-      v = fmaf(q[m][1], x.y, v);
-      v = fmaf(q[m][2], x.z, v);
-      v = fmaf(q[m][3], x.w, v);
+  for (int half = 0; half < 2; ++half) {
+    float4 a[2][NQ];
 #pragma unroll
-      for (int off = LPR / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-      if (m == li) mine = v;
+    for (int bb = 0; bb < 2; ++bb) {
+      const int k = k_wave + 16 * (2 * half + bb) + mem;
+      const bool ok = k < F;
+      const uint32_t node =
+          ok ? (has_parent ? sPn[k / b - p0] * (uint32_t)b + (uint32_t)(k % b) : (uint32_t)k) : 0u;
+      const float* xr = Xu + (int64_t)node * D + 4 * grp;
+#pragma unroll
+      for (int q = 0; q < NQ; ++q)
+        a[bb][q] = ok ? *reinterpret_cast<const float4*>(xr + 16 * q) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    if (valid) {
-      if (li == 0) cur.keep[u * cur.stride + k] = 0u;
-      if (li < Mu && ((mask >> li) & 1u)) {
-        // + 0.0f turns a -0 score into +0 so float and bit orders agree
-        S[(int64_t)qh_of(geo, u, li) * S_stride + k] = sigma * mine + 0.0f;
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb) {
+      f32x4_t c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[bb][q].x, qf[q][0], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[bb][q].y, qf[q][1], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[bb][q].z, qf[q][2], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[bb][q].w, qf[q][3], c, 0, 0, 0);
+      }
+      // rows kb..kb+3 of member `mem`; + 0.0f turns a -0 score into +0 so float and bit
+      // orders agree
+      const int kb = k_wave + 16 * (2 * half + bb) + 4 * grp;
+      if (mem < Mu && kb < F) {
+        const float4 o = make_float4(sigma * c[0] + 0.0f, sigma * c[1] + 0.0f,
+                                     sigma * c[2] + 0.0f, sigma * c[3] + 0.0f);
+        if (kb + 3 < F) {
+          *reinterpret_cast<float4*>(Srow + kb) = o;
+        } else {
+          Srow[kb] = o.x;
+          if (kb + 1 < F) Srow[kb + 1] = o.y;
+          if (kb + 2 < F) Srow[kb + 2] = o.z;
+        }
       }
     }
   }
@@ -159,41 +188,59 @@ __device__ __forceinline__ uint64_t wave_incl_scan_u64(uint64_t v, int lane) {
   return v;
 }
 
+constexpr int kVec = 4;                         // frontier entries per thread per tile
+constexpr int kTileE = kSelThreads * kVec;      // 2048 entries per tile
+constexpr int kCache = 16384;                   // frontier entries cached in LDS (64 KB)
+
 struct SelShared {
-  unsigned long long hm[kBuckets];
+  float cache[kCache];              // member scores (NaN: not a member) when F <= kCache
+  unsigned long long hm[kBuckets];  // fixed-point mass per bucket / per radix digit
   uint32_t hc[kBuckets];
   unsigned long long cand[kCand];
+  uint32_t tile_nodes[kTileE];
+  uint32_t tile_bits[kTileE / 32];
   float red_f[2][kSelWaves];
-  uint32_t red_u[kSelWaves];
-  uint32_t wave_cnt[kSelWaves];
-  uint32_t tile_nodes[kSelThreads];
+  uint32_t wave_sum[kSelWaves];
   unsigned long long scalar_u64[4];
   uint32_t scalar_u32[8];
-  float scalar_f[4];
 };
 
-// Block-wide exclusive rank of `flag` in thread order; returns rank, *total = count.
-__device__ __forceinline__ uint32_t block_rank(bool flag, uint32_t* wave_cnt, uint32_t* total) {
+// Block-wide exclusive prefix of per-thread counts in thread order; *total = their sum.
+template <int NT>
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wave_sum,
+                                                    uint32_t* total) {
+  constexpr int NW = NT / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const uint64_t bal = __ballot(flag);
-  const uint32_t in_wave = __popcll(bal & ((1ull << lane) - 1ull));
+  uint32_t incl = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t o = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += o;
+  }
   __syncthreads();
-  if (lane == 0) wave_cnt[wave] = __popcll(bal);
+  if (lane == 63) wave_sum[wave] = incl;
   __syncthreads();
   uint32_t before = 0, tot = 0;
 #pragma unroll
-  for (int w = 0; w < kSelWaves; ++w) {
-    const uint32_t c = wave_cnt[w];
-    before += (w < wave) ? c : 0;
+  for (int w = 0; w < NW; ++w) {
+    const uint32_t c = wave_sum[w];
+    before += (w < wave) ? c : 0u;
     tot += c;
   }
   *total = tot;
-  return before + in_wave;
+  return before + incl - v;
 }
+
+// Four consecutive frontier entries k0..k0+3 (k0 % 4 == 0) of one member: scores and
+// membership, from the LDS cache or from the member's score row in global memory.
+struct Quad {
+  float s[kVec];
+  bool in[kVec];
+};
 
 __global__ __launch_bounds__(kSelThreads) void select_kernel(
     Geom geo, int level, const float* __restrict__ S, int64_t S_stride, LevelBufs parent,
-    int has_parent, int n_top, LevelBufs cur, float p, int anchor, int32_t* __restrict__ sel_idx,
+    int has_parent, int n_top, KeepBits kb, float p, int anchor, int32_t* __restrict__ sel_idx,
     int64_t cap, int32_t* __restrict__ sel_count, int32_t* __restrict__ lvl_kept) {
   __shared__ SelShared sh;
   const int qh = blockIdx.x;
@@ -205,22 +252,60 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   const float* Sq = S + (int64_t)qh * S_stride;
   const uint32_t* pmask = has_parent ? parent.masks + u * parent.stride : nullptr;
   const uint32_t* pnodes = has_parent ? parent.nodes + u * parent.stride : nullptr;
-  auto member = [&](int k) -> bool { return !pmask || ((pmask[k / b] >> m) & 1u); };
-
+  uint32_t* kbits = kb.bits + (int64_t)qh * kb.words;
+  const bool cached = F <= kCache;
   if (tid == 0) {
+    sh.scalar_u32[0] = 0u;
     sh.scalar_u32[1] = 0u;
     sh.scalar_u64[0] = 0ull;
     sh.scalar_u64[1] = 0ull;
     sh.scalar_u64[2] = ~0ull;
   }
-  // pass 0: max, min over the member's frontier
-  float mx = -INFINITY, mn = INFINITY;
-  for (int k = tid; k < F; k += kSelThreads) {
-    if (member(k)) {
-      const float s = Sq[k];
-      mx = fmaxf(mx, s);
-      mn = fminf(mn, s);
+
+  auto load_global = [&](int k0) -> Quad {
+    Quad q;
+    const float4 v = (k0 + 3 < F) ? *reinterpret_cast<const float4*>(Sq + k0)
+                                  : make_float4(k0 < F ? Sq[k0] : 0.f, k0 + 1 < F ? Sq[k0 + 1] : 0.f,
+                                                k0 + 2 < F ? Sq[k0 + 2] : 0.f, 0.f);
+    q.s[0] = v.x;
+    q.s[1] = v.y;
+    q.s[2] = v.z;
+    q.s[3] = v.w;
+#pragma unroll
+    for (int i = 0; i < kVec; ++i) {
+      const int k = k0 + i;
+      q.in[i] = k < F && (!pmask || ((pmask[k / b] >> m) & 1u));
     }
+    return q;
+  };
+  auto get = [&](int k0) -> Quad {
+    if (!cached) return load_global(k0);
+    Quad q;
+    const float4 v = *reinterpret_cast<const float4*>(&sh.cache[k0]);
+    q.s[0] = v.x;
+    q.s[1] = v.y;
+    q.s[2] = v.z;
+    q.s[3] = v.w;
+#pragma unroll
+    for (int i = 0; i < kVec; ++i) q.in[i] = !isnan(q.s[i]);
+    return q;
+  };
+
+  // pass 0: max, min over the member's frontier; fill the LDS cache when it fits
+  float mx = -INFINITY, mn = INFINITY;
+  for (int k0 = kVec * tid; k0 < F; k0 += kTileE) {
+    const Quad q = load_global(k0);
+#pragma unroll
+    for (int i = 0; i < kVec; ++i) {
+      if (q.in[i]) {
+        mx = fmaxf(mx, q.s[i]);
+        mn = fminf(mn, q.s[i]);
+      }
+    }
+    if (cached)
+      *reinterpret_cast<float4*>(&sh.cache[k0]) =
+          make_float4(q.in[0] ? q.s[0] : NAN, q.in[1] ? q.s[1] : NAN, q.in[2] ? q.s[2] : NAN,
+                      q.in[3] ? q.s[3] : NAN);
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
@@ -250,15 +335,17 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
       sh.hm[i] = 0ull;
       sh.hc[i] = 0u;
     }
-    if (tid == 0) sh.scalar_u32[0] = 0u;
     __syncthreads();
     // pass 1: fixed-point mass histogram over score buckets (bucket 0 = highest scores)
-    for (int k = tid; k < F; k += kSelThreads) {
-      if (member(k)) {
-        const float s = Sq[k];
-        const int bk = bucket_of(s, mx, scale, spread);
-        atomicAdd(&sh.hm[bk], (unsigned long long)mass_fixed(s, mx));
-        atomicAdd(&sh.hc[bk], 1u);
+    for (int k0 = kVec * tid; k0 < F; k0 += kTileE) {
+      const Quad q = get(k0);
+#pragma unroll
+      for (int i = 0; i < kVec; ++i) {
+        if (q.in[i]) {
+          const int bk = bucket_of(q.s[i], mx, scale, spread);
+          atomicAdd(&sh.hm[bk], (unsigned long long)mass_fixed(q.s[i], mx));
+          atomicAdd(&sh.hc[bk], 1u);
+        }
       }
     }
     __syncthreads();
@@ -292,12 +379,13 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const uint32_t nb = sh.hc[bstar];
     if (nb <= (uint32_t)kCand) {
       // gather the boundary bucket, sort it by rank key, scan its masses
-      for (int k = tid; k < F; k += kSelThreads) {
-        if (member(k)) {
-          const float s = Sq[k];
-          if (bucket_of(s, mx, scale, spread) == bstar) {
+      for (int k0 = kVec * tid; k0 < F; k0 += kTileE) {
+        const Quad q = get(k0);
+#pragma unroll
+        for (int i = 0; i < kVec; ++i) {
+          if (q.in[i] && bucket_of(q.s[i], mx, scale, spread) == bstar) {
             const uint32_t slot = atomicAdd(&sh.scalar_u32[0], 1u);
-            sh.cand[slot] = rank_key(s, (uint32_t)k);
+            sh.cand[slot] = rank_key(q.s[i], (uint32_t)(k0 + i));
           }
         }
       }
@@ -311,11 +399,11 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
           for (int i = tid; i < P2; i += kSelThreads) {
             const int j = i ^ stride;
             if (j > i) {
-              const unsigned long long a = sh.cand[i], c = sh.cand[j];
+              const unsigned long long x = sh.cand[i], y = sh.cand[j];
               const bool desc = (i & size) == 0;  // descending blocks give a descending result
-              if (desc ? (a < c) : (a > c)) {
-                sh.cand[i] = c;
-                sh.cand[j] = a;
+              if (desc ? (x < y) : (x > y)) {
+                sh.cand[i] = y;
+                sh.cand[j] = x;
               }
             }
           }
@@ -353,13 +441,14 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
       for (int shift = 56; shift >= 0; shift -= 8) {
         for (int i = tid; i < 256; i += kSelThreads) sh.hm[i] = 0ull;
         __syncthreads();
-        for (int k = tid; k < F; k += kSelThreads) {
-          if (member(k)) {
-            const float s = Sq[k];
-            if (bucket_of(s, mx, scale, spread) != bstar) continue;
-            const uint64_t key = rank_key(s, (uint32_t)k);
+        for (int k0 = kVec * tid; k0 < F; k0 += kTileE) {
+          const Quad q = get(k0);
+#pragma unroll
+          for (int i = 0; i < kVec; ++i) {
+            if (!q.in[i] || bucket_of(q.s[i], mx, scale, spread) != bstar) continue;
+            const uint64_t key = rank_key(q.s[i], (uint32_t)(k0 + i));
             if ((key & pmask_bits) != prefix) continue;
-            atomicAdd(&sh.hm[(key >> shift) & 255u], (unsigned long long)mass_fixed(s, mx));
+            atomicAdd(&sh.hm[(key >> shift) & 255u], (unsigned long long)mass_fixed(q.s[i], mx));
           }
         }
         __syncthreads();
@@ -373,11 +462,11 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
             }
             run += sh.hm[dg];
           }
-          sh.scalar_u64[3] = ((uint64_t)dsel << 32) | 0u;
+          sh.scalar_u64[3] = (uint64_t)dsel;
           sh.scalar_u64[2] = run;
         }
         __syncthreads();
-        const uint64_t dsel = sh.scalar_u64[3] >> 32;
+        const uint64_t dsel = sh.scalar_u64[3];
         need -= sh.scalar_u64[2];
         prefix |= dsel << shift;
         pmask_bits |= 255ull << shift;
@@ -390,20 +479,20 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     s_cut = float_of_ord((uint32_t)(key >> 32));
     k_cut = 0xffffffffu - (uint32_t)key;
   }
-  auto kept_at = [&](int k) -> bool {
-    if (!member(k)) return false;
+  auto keep_of = [&](float s, bool in, int k) -> bool {
+    if (!in) return false;
     if (keep_all) return true;
-    const float s = Sq[k];
     return s > s_cut || (s == s_cut && (uint32_t)k <= k_cut);
   };
 
   // anchor overlap: kept level-1 tokens below `anchor` (they can only sit in the first
   // ceil(anchor / b) frontier entries, since node ids are distinct and ascending)
-  int dup = 0;
   if (level == 1 && tid == 0) {
+    int dup = 0;
     const int lim = min(F, (anchor + b - 1) / b);
     for (int k = 0; k < lim; ++k) {
-      if (kept_at(k)) {
+      const bool in = !pmask || ((pmask[k / b] >> m) & 1u);
+      if (keep_of(Sq[k], in, k)) {
         const int node = (int)frontier_node(pnodes, k, b);
         if (node * b < anchor) dup += min(b, anchor - node * b);
       }
@@ -411,22 +500,41 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     sh.scalar_u32[2] = (uint32_t)dup;
   }
   __syncthreads();
-  dup = (int)sh.scalar_u32[2];
+  const int dup = (level == 1) ? (int)sh.scalar_u32[2] : 0;
   int32_t* sel = sel_idx ? sel_idx + (int64_t)qh * cap : nullptr;
   if (level == 1 && sel)
     for (int i = tid; i < anchor; i += kSelThreads) sel[i] = i;
 
-  // emit: mark kept entries in the unit's keep masks; at level 1 write the token list
+  // emit: the member's kept flags as a bit row (one 32-bit word per 32 entries, plain
+  // stores); at level 1 also the token list
   uint32_t running = 0;
-  for (int k0 = 0; k0 < F; k0 += kSelThreads) {
-    const int k = k0 + tid;
-    const bool kept = k < F && kept_at(k);
-    if (kept) atomicOr(&cur.keep[u * cur.stride + k], 1u << m);
+  for (int t0 = 0; t0 < F; t0 += kTileE) {
+    const int k0 = t0 + kVec * tid;
+    uint32_t kept_bits = 0, cnt = 0;
+    if (k0 < F) {
+      const Quad q = get(k0);
+#pragma unroll
+      for (int i = 0; i < kVec; ++i) {
+        if (keep_of(q.s[i], q.in[i], k0 + i)) {
+          kept_bits |= 1u << i;
+          ++cnt;
+        }
+      }
+    }
+    if (tid < kTileE / 32) sh.tile_bits[tid] = 0u;
     uint32_t tile_total;
-    const uint32_t r = block_rank(kept, sh.wave_cnt, &tile_total);
+    const uint32_t r0 = block_excl_scan<kSelThreads>(cnt, sh.wave_sum, &tile_total);
+    if (kept_bits) atomicOr(&sh.tile_bits[tid / 8], kept_bits << (4 * (tid % 8)));
     if (level == 1 && sel) {
-      if (kept) sh.tile_nodes[r] = frontier_node(pnodes, k, b);
-      __syncthreads();
+      uint32_t r = r0;
+#pragma unroll
+      for (int i = 0; i < kVec; ++i)
+        if ((kept_bits >> i) & 1u) sh.tile_nodes[r++] = frontier_node(pnodes, k0 + i, b);
+    }
+    __syncthreads();
+    const int words = min(kTileE, F - t0 + 31) / 32;
+    if (tid < words) kbits[t0 / 32 + tid] = sh.tile_bits[tid];
+    if (level == 1 && sel) {
       const int ntok = (int)tile_total * b;
       for (int i = tid; i < ntok; i += kSelThreads) {
         const int rr = i / b, c = i % b;
@@ -434,93 +542,113 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
         if (tok >= anchor) sel[anchor + (int64_t)(running + rr) * b + c - dup] = tok;
       }
     }
+    __syncthreads();
     running += tile_total;
   }
   if (tid == 0) {
     lvl_kept[(int64_t)qh * (geo.L + 1) + level] = (int32_t)running;
     if (level == 1) sel_count[qh] = anchor + (int32_t)running * b - dup;
   }
-
-  // the last member of the unit to finish compacts the union keep masks into the
-  // ascending list of kept nodes for the next level (or for the decode at level 1)
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const uint32_t prev = atomicAdd(&cur.done[u], 1u);
-    sh.scalar_u32[3] = (prev == (uint32_t)members_of(geo, u) - 1u) ? 1u : 0u;
-  }
-  __syncthreads();
-  if (sh.scalar_u32[3] == 0u) return;
-  __threadfence();
-  uint32_t out = 0;
-  for (int k0 = 0; k0 < F; k0 += kSelThreads) {
-    const int k = k0 + tid;
-    uint32_t msk = 0;
-    if (k < F)
-      msk = __hip_atomic_load(&cur.keep[u * cur.stride + k], __ATOMIC_RELAXED,
-                              __HIP_MEMORY_SCOPE_AGENT);
-    uint32_t tile_total;
-    const uint32_t r = block_rank(msk != 0u, sh.wave_cnt, &tile_total);
-    if (msk) {
-      cur.nodes[u * cur.stride + out + r] = frontier_node(pnodes, k, b);
-      cur.masks[u * cur.stride + out + r] = msk;
-    }
-    out += tile_total;
-  }
-  if (tid == 0) {
-    cur.count[u] = out;
-    cur.done[u] = 0u;
-  }
 }
 
-__global__ void init_kernel(uint32_t* done_all, int n) {
-  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x)
-    done_all[i] = 0u;
+// --------------------------------------------------------------------------- compaction
+// One workgroup per unit: OR the members' kept-flag rows into a member mask per frontier
+// entry and write the entries with a non-empty mask, in ascending order, as the level's
+// union list.
+__global__ __launch_bounds__(kCompactThreads) void compact_kernel(
+    Geom geo, LevelBufs parent, int has_parent, int n_top, KeepBits kb, LevelBufs cur) {
+  constexpr int WPM = kCompactChunk / 32;  // words per member per chunk
+  constexpr int EPT = kCompactChunk / kCompactThreads;  // entries per thread (16)
+  __shared__ uint32_t sbits[kMaxMembers][WPM];
+  __shared__ uint32_t wave_sum[kCompactThreads / 64];
+  const int u = blockIdx.x;
+  const int b = geo.b;
+  const int F = has_parent ? b * (int)parent.count[u] : n_top;
+  const int Mu = members_of(geo, u);
+  const uint32_t* pnodes = has_parent ? parent.nodes + u * parent.stride : nullptr;
+  uint32_t out = 0;
+  for (int c0 = 0; c0 < F; c0 += kCompactChunk) {
+    const int words = (min(kCompactChunk, F - c0) + 31) / 32;
+    __syncthreads();
+    for (int i = threadIdx.x; i < Mu * words; i += kCompactThreads) {
+      const int mm = i / words, w = i % words;
+      sbits[mm][w] = kb.bits[(int64_t)qh_of(geo, u, mm) * kb.words + c0 / 32 + w];
+    }
+    __syncthreads();
+    // thread t: entries c0 + EPT t .. + EPT - 1 (half of one 32-bit word)
+    const int e0 = EPT * threadIdx.x;
+    uint32_t msk[EPT];
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) msk[i] = 0u;
+    if (c0 + e0 < F) {
+      for (int mm = 0; mm < Mu; ++mm) {
+        const uint32_t w = sbits[mm][e0 / 32] >> (e0 % 32);
+#pragma unroll
+        for (int i = 0; i < EPT; ++i) msk[i] |= ((w >> i) & 1u) << mm;
+      }
+#pragma unroll
+      for (int i = 0; i < EPT; ++i) {
+        if (c0 + e0 + i >= F) msk[i] = 0u;
+        cnt += msk[i] != 0u;
+      }
+    }
+    uint32_t total;
+    uint32_t r = out + block_excl_scan<kCompactThreads>(cnt, wave_sum, &total);
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+      if (msk[i]) {
+        cur.nodes[u * cur.stride + r] = frontier_node(pnodes, c0 + e0 + i, b);
+        cur.masks[u * cur.stride + r] = msk[i];
+        ++r;
+      }
+    }
+    out += total;
+  }
+  if (threadIdx.x == 0) cur.count[u] = out;
 }
 
 }  // namespace
 
-hipError_t launch_attend_init(uint32_t* done_all, int n, hipStream_t s) {
-  hipLaunchKernelGGL(init_kernel, dim3(1), dim3(256), 0, s, done_all, n);
-  return hipGetLastError();
-}
-
-hipError_t launch_score(const Geom& geo, int level, const float* X, int64_t X_unit_stride,
-                        const void* Q, int dtype, const LevelBufs* parent, int n_top, float* S,
-                        int64_t S_stride, const LevelBufs& cur, hipStream_t s) {
-  (void)level;
-  const int cap_entries = parent ? (int)cur.stride : n_top;
+hipError_t launch_score(const Geom& geo, const float* X, int64_t X_unit_stride, const void* Q,
+                        int dtype, const LevelBufs* parent, int n_top, float* S,
+                        int64_t S_stride, hipStream_t s) {
+  const int cap_entries = parent ? (int)(geo.b * parent->stride) : n_top;
   dim3 grid((cap_entries + kScoreEntries - 1) / kScoreEntries, geo.U);
   const float sigma = 1.0f / sqrtf((float)geo.D);
   LevelBufs par = parent ? *parent : LevelBufs{};
   const int hp = parent ? 1 : 0;
+#define ZHA_SCORE(DD, TQ)                                                                     \
+  hipLaunchKernelGGL((score_kernel<DD, TQ>), grid, dim3(kScoreThreads), 0, s, geo, X,          \
+                     X_unit_stride, (const TQ*)Q, par, hp, n_top, S, S_stride, sigma)
   if (geo.D == 64) {
-    if (dtype == ZHA_BF16)
-      hipLaunchKernelGGL((score_kernel<64, bf16_t>), grid, dim3(kScoreThreads), 0, s, geo, X,
-                         X_unit_stride, (const bf16_t*)Q, par, hp, n_top, S, S_stride, cur, sigma);
-    else
-      hipLaunchKernelGGL((score_kernel<64, float>), grid, dim3(kScoreThreads), 0, s, geo, X,
-                         X_unit_stride, (const float*)Q, par, hp, n_top, S, S_stride, cur, sigma);
+    if (dtype == ZHA_BF16) ZHA_SCORE(64, bf16_t);
+    else ZHA_SCORE(64, float);
   } else {
-    if (dtype == ZHA_BF16)
-      hipLaunchKernelGGL((score_kernel<128, bf16_t>), grid, dim3(kScoreThreads), 0, s, geo, X,
-                         X_unit_stride, (const bf16_t*)Q, par, hp, n_top, S, S_stride, cur, sigma);
-    else
-      hipLaunchKernelGGL((score_kernel<128, float>), grid, dim3(kScoreThreads), 0, s, geo, X,
-                         X_unit_stride, (const float*)Q, par, hp, n_top, S, S_stride, cur, sigma);
+    if (dtype == ZHA_BF16) ZHA_SCORE(128, bf16_t);
+    else ZHA_SCORE(128, float);
   }
+#undef ZHA_SCORE
   return hipGetLastError();
 }
 
 hipError_t launch_select(const Geom& geo, int level, const float* S, int64_t S_stride,
-                         const LevelBufs* parent, int n_top, const LevelBufs& cur, float p,
-                         int anchor, int32_t* sel_idx, int64_t cap, int32_t* sel_count,
-                         int32_t* lvl_kept, hipStream_t s) {
+                         const LevelBufs* parent, int n_top, KeepBits kb, float p, int anchor,
+                         int32_t* sel_idx, int64_t cap, int32_t* sel_count, int32_t* lvl_kept,
+                         hipStream_t s) {
   LevelBufs par = parent ? *parent : LevelBufs{};
   const int QH = geo.B * geo.T * geo.Hq;
   hipLaunchKernelGGL(select_kernel, dim3(QH), dim3(kSelThreads), 0, s, geo, level, S, S_stride,
-                     par, parent ? 1 : 0, n_top, cur, p, anchor, sel_idx, cap, sel_count,
+                     par, parent ? 1 : 0, n_top, kb, p, anchor, sel_idx, cap, sel_count,
                      lvl_kept);
+  return hipGetLastError();
+}
+
+hipError_t launch_compact(const Geom& geo, const LevelBufs* parent, int n_top, KeepBits kb,
+                          const LevelBufs& cur, hipStream_t s) {
+  LevelBufs par = parent ? *parent : LevelBufs{};
+  hipLaunchKernelGGL(compact_kernel, dim3(geo.U), dim3(kCompactThreads), 0, s, geo, par,
+                     parent ? 1 : 0, n_top, kb, cur);
   return hipGetLastError();
 }
 
