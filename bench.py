@@ -170,9 +170,19 @@ def main():
             rows = int(lists[lv + 1][2].sum()) * b
         frontier_rows += rows
         score_bytes[lv] = rows * d * 4
-    build_bytes = {1: B * Hkv * N * d * elem + B * Hkv * (N // b) * d * 4}
-    for lv in range(2, L + 1):
-        build_bytes[lv] = B * Hkv * (N // b ** (lv - 1)) * d * 4 + B * Hkv * (N // b ** lv) * d * 4
+    # a pooling launch that starts at level lv reads level lv - 1 once and writes every
+    # level it fuses (b^k <= 64 rows per tile, as the library groups them)
+    build_bytes = {}
+    lv = 1
+    while lv <= L:
+        k = 1
+        while k < L - lv + 1 and b ** (k + 1) <= 64:
+            k += 1
+        if b > 64:
+            k = 1
+        child = B * Hkv * (N // b ** (lv - 1)) * d * (elem if lv == 1 else 4)
+        build_bytes[lv] = child + sum(B * Hkv * (N // b ** j) * d * 4 for j in range(lv, lv + k))
+        lv += k
     list_bytes = 4 * int(counts.sum())
     attend_alg = kv_bytes + frontier_rows * d * 4 + QH * (d * elem + d * 4 + 4) + list_bytes
     step_alg = attend_alg + B * Hkv * N * d * elem + tree_bytes_written(B, Hkv, N, d, b, L)

@@ -339,6 +339,187 @@ __global__ __launch_bounds__(kPoolThreads) void pool_tile_kernel(
   }
 }
 
+// ------------------------------------------------------------------------------------
+// Deep trees (b = 4) over bf16 keys: wave-centric fused pooling of up to three levels.
+// Each wave owns 64 consecutive key rows (16 level-1 nodes, 4 level-2 nodes, 1 level-3
+// node) and pools them with no workgroup barrier:
+//  * z^T = K . R^T on v_mfma_f32_16x16x32_bf16 with the 16-row block loaded straight into
+//    A-operand registers; the C layout gives lane (ref = l % 16, group g = l / 16) the
+//    scores of rows 4g..4g+3, i.e. of all four children of node g, so the softmax over
+//    children is lane-local; the mean over references is a 16-lane reduction;
+//  * the rows go through a small per-wave LDS tile, and lane l sums the four children of
+//    node l / 16 over dims 8 (l % 16) .. +8 (its weights are already in its lane group);
+//  * levels 2 and 3 repeat this on the float32 rows kept in LDS (v_mfma_f32_16x16x4_f32).
+// The arithmetic for a node never depends on its position, so identical subtrees give
+// identical summaries.
+constexpr int kWaveRows = 64;
+constexpr int kWaveTilesPerWave = 2;
+
+template <int D>
+__global__ __launch_bounds__(kPoolThreads) void pool_wave_b4_kernel(
+    const bf16_t* __restrict__ child, int64_t in_unit_stride, const bf16_t* __restrict__ Rall,
+    PoolOut out, int nlev, int Hkv, int tile_begin, int tile_end, float tau) {
+  constexpr int KC = D / 32;
+  constexpr int NQ = D / 16;
+  constexpr int RWb = D / 2 + 4;  // bf16 raw-row stride in dwords
+  constexpr int RWf = D + 4;      // float row stride
+  constexpr int DL = D / 16;      // output dims per lane in the weighted sums
+  __shared__ uint32_t sRaw[4][16 * RWb];
+  __shared__ float sL1[4][16 * RWf];
+  __shared__ float sL2[4][4 * RWf];
+
+  const int unit = blockIdx.y;
+  const int g_kv = unit % Hkv;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int mem = lane & 15, grp = lane >> 4;
+
+  const bf16_t* R = Rall + (int64_t)g_kv * kNRef * D;
+  bf16x8_t rb[KC];
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc)
+    rb[kc] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(R + mem * D + 32 * kc + 8 * grp));
+  float rf[NQ][4];
+#pragma unroll
+  for (int q = 0; q < NQ; ++q)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) rf[q][e] = to_f32(R[mem * D + 16 * q + 4 * grp + e]);
+
+  uint32_t* raw = sRaw[wave];
+  float* l1 = sL1[wave];
+  float* l2 = sL2[wave];
+
+  // child weights of node `grp` from this lane's four scores z[r] (rows 4 grp + r):
+  // softmax over the children, then the mean over the 16 references of the lane group
+  auto weights = [&](const f32x4_t& zc, float w[4]) {
+    float z[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) z[r] = tau * zc[r];
+    const float mx = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+    float e[4], sum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      e[r] = expf(z[r] - mx);
+      sum += e[r];
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float a = e[r] / sum;
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) a += __shfl_xor(a, off, 64);
+      w[r] = a * (1.f / kNRef);
+    }
+  };
+
+  for (int it = 0; it < kWaveTilesPerWave; ++it) {
+    const int t = tile_begin + (blockIdx.x * (kPoolThreads / 64) + wave) * kWaveTilesPerWave + it;
+    if (t >= tile_end) break;
+    const bf16_t* src = child + unit * in_unit_stride + (int64_t)t * kWaveRows * D;
+    uint4 a[4][KC];
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk)
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc)
+        a[blk][kc] = *reinterpret_cast<const uint4*>(src + (int64_t)(16 * blk + mem) * D + 32 * kc + 8 * grp);
+
+    // level 1: four 16-row blocks -> 16 nodes
+    float* dst1 = out.ptr[0] + unit * out.unit_stride[0] + (int64_t)t * 16 * D;
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk) {
+      f32x4_t zc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc)
+        zc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[blk][kc]), rb[kc], zc,
+                                                     0, 0, 0);
+      float w[4];
+      weights(zc, w);
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc)
+        *reinterpret_cast<uint4*>(&raw[mem * RWb + 16 * kc + 4 * grp]) = a[blk][kc];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      // node grp of this block, dims DL * mem .. + DL
+      float acc[DL];
+#pragma unroll
+      for (int i = 0; i < DL; ++i) acc[i] = 0.f;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint32_t* rp = &raw[(4 * grp + c) * RWb + (DL / 2) * mem];
+#pragma unroll
+        for (int i = 0; i < DL / 2; ++i) {
+          const uint32_t v = rp[i];
+          acc[2 * i] = fmaf(w[c], __uint_as_float(v << 16), acc[2 * i]);
+          acc[2 * i + 1] = fmaf(w[c], __uint_as_float(v & 0xffff0000u), acc[2 * i + 1]);
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const int node = 4 * blk + grp;
+#pragma unroll
+      for (int i = 0; i < DL; i += 4) {
+        const float4 o = make_float4(acc[i], acc[i + 1], acc[i + 2], acc[i + 3]);
+        *reinterpret_cast<float4*>(dst1 + (int64_t)node * D + DL * mem + i) = o;
+        *reinterpret_cast<float4*>(&l1[node * RWf + DL * mem + i]) = o;
+      }
+    }
+    if (nlev < 2) continue;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    // levels 2 and 3 from the float32 rows in LDS (16 rows, then 4)
+    for (int j = 1; j < nlev; ++j) {
+      const float* in = (j == 1) ? l1 : l2;
+      const int rows = (j == 1) ? 16 : 4;
+      f32x4_t zc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        const float4 x = mem < rows ? *reinterpret_cast<const float4*>(&in[mem * RWf + 16 * q + 4 * grp])
+                                    : make_float4(0.f, 0.f, 0.f, 0.f);
+        zc = __builtin_amdgcn_mfma_f32_16x16x4f32(x.x, rf[q][0], zc, 0, 0, 0);
+        zc = __builtin_amdgcn_mfma_f32_16x16x4f32(x.y, rf[q][1], zc, 0, 0, 0);
+        zc = __builtin_amdgcn_mfma_f32_16x16x4f32(x.z, rf[q][2], zc, 0, 0, 0);
+        zc = __builtin_amdgcn_mfma_f32_16x16x4f32(x.w, rf[q][3], zc, 0, 0, 0);
+      }
+      float w[4];
+      weights(zc, w);
+      const int nodes = rows / 4;
+      if (grp < nodes) {
+        float acc[DL];
+#pragma unroll
+        for (int i = 0; i < DL; ++i) acc[i] = 0.f;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const float* rp = &in[(4 * grp + c) * RWf + DL * mem];
+#pragma unroll
+          for (int i = 0; i < DL; ++i) acc[i] = fmaf(w[c], rp[i], acc[i]);
+        }
+        float* dst = out.ptr[j] + unit * out.unit_stride[j] + ((int64_t)t * nodes + grp) * D;
+#pragma unroll
+        for (int i = 0; i < DL; i += 4) {
+          const float4 o = make_float4(acc[i], acc[i + 1], acc[i + 2], acc[i + 3]);
+          *reinterpret_cast<float4*>(dst + DL * mem + i) = o;
+          if (j == 1) *reinterpret_cast<float4*>(&l2[grp * RWf + DL * mem + i]) = o;
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+  }
+}
+
+template <int D>
+hipError_t launch_wave_b4(const void* child, int64_t in_unit_stride, const void* R,
+                          const PoolOut& out, int nlev, int units, int Hkv, int row_begin,
+                          int row_end, hipStream_t s) {
+  const int t0 = row_begin / kWaveRows, t1 = row_end / kWaveRows;
+  if (t1 <= t0) return hipSuccess;
+  const int per_wg = (kPoolThreads / 64) * kWaveTilesPerWave;
+  dim3 grid((t1 - t0 + per_wg - 1) / per_wg, units);
+  hipLaunchKernelGGL((pool_wave_b4_kernel<D>), grid, dim3(kPoolThreads), 0, s,
+                     (const bf16_t*)child, in_unit_stride, (const bf16_t*)R, out, nlev, Hkv, t0,
+                     t1, 1.0f / sqrtf((float)D));
+  return hipGetLastError();
+}
+
 template <typename Tin, typename Tr, int D>
 hipError_t launch_pool_t(const void* child, int64_t in_unit_stride, const void* R, float* out,
                          int64_t out_unit_stride, int units, int Hkv, int node_begin,
@@ -420,6 +601,15 @@ hipError_t launch_pool_fused(int dtype_in, const void* child, int64_t in_unit_st
     out.unit_stride[j] = out_unit_strides[j];
   }
   if (dtype_r == ZHA_BF16) {
+    // bf16 keys, b = 4, rows in whole 64-row wave tiles: the wave-centric kernel
+    if (dtype_in == ZHA_BF16 && b == 4 && nlev <= 3 && row_begin % kWaveRows == 0 &&
+        row_end % kWaveRows == 0) {
+      if (D == 64)
+        return launch_wave_b4<64>(child, in_unit_stride, R, out, nlev, units, Hkv, row_begin,
+                                  row_end, s);
+      return launch_wave_b4<128>(child, in_unit_stride, R, out, nlev, units, Hkv, row_begin,
+                                 row_end, s);
+    }
     if (dtype_in == ZHA_BF16)
       return launch_tile_d<bf16_t, bf16_t>(D, child, in_unit_stride, R, out, nlev, units, Hkv,
                                            row_begin, row_end, b, s);
