@@ -190,7 +190,8 @@ def main():
     alg_bytes = {"decode": decode_bytes}
     for lv in range(1, L + 1):
         alg_bytes[f"score_l{lv}"] = score_bytes[lv]
-        alg_bytes[f"pool_l{lv}"] = build_bytes[lv]
+    for lv, nbytes in build_bytes.items():
+        alg_bytes[f"pool_l{lv}"] = nbytes
     dom = max(kernels, key=lambda k: kernels[k]["avg_ms"] * kernels[k]["launches"])
     dom_bytes = alg_bytes.get(dom)
     roofline = None

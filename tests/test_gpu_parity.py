@@ -119,6 +119,8 @@ def test_wide_tree(p):
     dict(name="G16", Hq=16, Hkv=1),
     dict(name="b2 L5", b=2, L=5, N=2048),
     dict(name="b8 L2", b=8, L=2, N=4096),
+    dict(name="b3 L4", b=3, L=4, N=81 * 25),
+    dict(name="b5 L3", b=5, L=3, N=125 * 20, anchor=7),
     dict(name="sharp pooling", r_std=1.0),
 ])
 def test_edge_cases(case):

@@ -102,7 +102,7 @@ int check_geometry(int B, int Hkv, int N, int N_cap, int d, int b, int L) {
 struct WsLayout {
   int U, QH, splits;
   int64_t n[ZHA_MAX_LEVELS + 1];  // nodes per unit at each level (current N)
-  int64_t off_count, off_lvl, off_S, off_bits, off_part;
+  int64_t off_count, off_lvl, off_S, off_bits, off_part, off_chunks;
   int64_t off_nodes[ZHA_MAX_LEVELS + 1], off_masks[ZHA_MAX_LEVELS + 1];
   int64_t S_stride, bit_words;
   int64_t total;
@@ -128,6 +128,7 @@ int make_geom(const zha_tree* t, int T, int Hq, Geom* g) {
   g->L = t->L;
   g->N = t->N;
   g->Ncap = t->N_cap;
+  g->bdiv = make_fastdiv((uint32_t)t->b);
   return ZHA_OK;
 }
 
@@ -163,6 +164,8 @@ WsLayout layout_of(const Geom& g) {
   off = align256(off + 4 * (int64_t)w.QH * w.bit_words);
   w.off_part = off;
   off = align256(off + 4 * (int64_t)g.U * w.splits * kMaxMembers * (g.D + 2));
+  w.off_chunks = off;
+  off = align256(off + 4 * compact_counter_words(g.U, w.n[1]));
   w.total = off;
   return w;
 }
@@ -362,7 +365,9 @@ int zha_attend(const zha_tree* t, const void* Q, int T, int Hq, const void* K, c
                            l == 1 ? sel_idx : nullptr, cap, sel_count, lvl, s);
     });
     if (e != hipSuccess) return hip_fail(e, "select launch");
-    e = timed(ZHA_K_COMPACT, l, s, [&] { return launch_compact(g, parent, n_top, kb, lv[l], s); });
+    e = timed(ZHA_K_COMPACT, l, s, [&] {
+      return launch_compact(g, parent, n_top, kb, lv[l], (uint32_t*)(ws + w.off_chunks), s);
+    });
     if (e != hipSuccess) return hip_fail(e, "compact launch");
     cap_l *= t->b;
   }

@@ -161,7 +161,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_valu_kernel(
   if (sp == 0 && wave == 0)
     for (int tok = 0; tok < anchor; ++tok) consume(tok, full);
   for (int i = t0 + wave; i < t1; i += kDecWaves) {
-    const int nd = i / b, c = i % b;
+    const int nd = (int)geo.bdiv.div((uint32_t)i), c = i - nd * b;
     const int tok = (int)l1.nodes[u * l1.stride + nd] * b + c;
     if (tok < anchor) continue;
     consume(tok, l1.masks[u * l1.stride + nd]);
@@ -264,13 +264,13 @@ __global__ __launch_bounds__(kDecThreads) void decode_mfma_kernel(
   auto token_at = [&](int i, bool anc, int lim, int nbase) -> int {
     if (i >= lim) return 0;
     if (anc) return i;
-    const int nd = i / b;
+    const int nd = (int)geo.bdiv.div((uint32_t)i);
     return (int)s_nodes[nd - nbase] * b + (i - nd * b);
   };
   auto mask_at = [&](int i, bool anc, int lim, int nbase) -> uint32_t {
     if (i >= lim) return 0u;
     if (anc) return 0xffffu;
-    const int nd = i / b;
+    const int nd = (int)geo.bdiv.div((uint32_t)i);
     const int t = (int)s_nodes[nd - nbase] * b + (i - nd * b);
     return t < anchor ? 0u : s_masks[nd - nbase];
   };

@@ -18,11 +18,32 @@ typedef uint16_t bf16_t;
 __device__ __forceinline__ float to_f32(float v) { return v; }
 __device__ __forceinline__ float to_f32(bf16_t v) { return __uint_as_float(((uint32_t)v) << 16); }
 
+// Division by a runtime constant d >= 1 for numerators below 2^31 (round-up magic
+// number): q = (mulhi(n, m) + n) >> l with l = ceil(log2 d), m = 2^32 (2^l - d) / d + 1.
+// The GPU has no integer divider; this replaces ~30 instructions by three.
+struct FastDiv {
+  uint32_t d, m, l;
+  __host__ __device__ __forceinline__ uint32_t div(uint32_t n) const {
+    return (__umulhi(n, m) + n) >> l;
+  }
+};
+
+inline FastDiv make_fastdiv(uint32_t d) {
+  uint32_t l = 0;
+  while ((1ull << l) < d) ++l;
+  FastDiv f;
+  f.d = d;
+  f.l = l;
+  f.m = (uint32_t)((((1ull << 32) * ((1ull << l) - d)) / d) + 1);
+  return f;
+}
+
 // Decode-call geometry. A unit is (sequence, KV head, block of Tb queries); its members
 // are the Tb * G (query, head) pairs that read that KV head.
 struct Geom {
   int B, T, Hq, Hkv, G, Tb, nTB, U;
   int D, b, L, N, Ncap;
+  FastDiv bdiv;  // division by b
 };
 
 __host__ __device__ __forceinline__ int members_of(const Geom& g, int u) {
@@ -101,8 +122,10 @@ hipError_t launch_select(const Geom& geo, int level, const float* S, int64_t S_s
                          hipStream_t s);
 
 // Union of the members' kept flags -> ascending kept-node list with member masks.
+// chunk_cnt: scratch of compact_counter_words(U, frontier capacity) words.
 hipError_t launch_compact(const Geom& geo, const LevelBufs* parent, int n_top, KeepBits kb,
-                          const LevelBufs& cur, hipStream_t s);
+                          const LevelBufs& cur, uint32_t* chunk_cnt, hipStream_t s);
+int64_t compact_counter_words(int U, int64_t n);
 
 hipError_t launch_decode(const Geom& geo, int dtype, const void* K, const void* V,
                          const void* Q, const LevelBufs& l1, int anchor, int splits,

@@ -30,7 +30,6 @@ constexpr int kSelThreads = 512;
 constexpr int kSelWaves = kSelThreads / 64;
 constexpr int kBuckets = 2048;
 constexpr int kCand = 2048;
-constexpr float kMassScale = 4398046511104.0f;  // 2^42: fixed-point scale of a node mass
 constexpr float kMaxSpread = 32.0f;             // exp(-32) * 2^42 < 1: lower masses are 0
 
 constexpr int kCompactThreads = 1024;
@@ -38,9 +37,10 @@ constexpr int kCompactChunk = 16384;            // frontier entries per compacti
 
 // node id of frontier entry k: the top level's frontier is every node; below, entry k
 // is child k % b of the (k / b)-th node the level above kept (pnodes: that unit's list)
-__device__ __forceinline__ uint32_t frontier_node(const uint32_t* pnodes, int k, int b) {
+__device__ __forceinline__ uint32_t frontier_node(const uint32_t* pnodes, int k, const FastDiv& bd) {
   if (!pnodes) return (uint32_t)k;
-  return pnodes[k / b] * (uint32_t)b + (uint32_t)(k % b);
+  const uint32_t q = bd.div((uint32_t)k);
+  return pnodes[q] * bd.d + ((uint32_t)k - q * bd.d);
 }
 
 // ------------------------------------------------------------------------------ score
@@ -67,9 +67,9 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int mem = lane & 15, grp = lane >> 4;
 
-  const int p0 = k_wg / b;
+  const int p0 = (int)geo.bdiv.div((uint32_t)k_wg);
   if (has_parent) {
-    const int np = (min(k_wg + kScoreEntries, F) - 1) / b - p0 + 1;
+    const int np = (int)geo.bdiv.div((uint32_t)(min(k_wg + kScoreEntries, F) - 1)) - p0 + 1;
     for (int i = threadIdx.x; i < np; i += kScoreThreads)
       sPn[i] = parent.nodes[u * parent.stride + p0 + i];
   }
@@ -91,8 +91,10 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
     for (int bb = 0; bb < 2; ++bb) {
       const int k = k_wave + 16 * (2 * half + bb) + mem;
       const bool ok = k < F;
+      const uint32_t kq = geo.bdiv.div((uint32_t)k);
       const uint32_t node =
-          ok ? (has_parent ? sPn[k / b - p0] * (uint32_t)b + (uint32_t)(k % b) : (uint32_t)k) : 0u;
+          ok ? (has_parent ? sPn[kq - p0] * (uint32_t)b + ((uint32_t)k - kq * (uint32_t)b) : (uint32_t)k)
+             : 0u;
       const float* xr = Xu + (int64_t)node * D + 4 * grp;
 #pragma unroll
       for (int q = 0; q < NQ; ++q)
@@ -139,8 +141,15 @@ __device__ __forceinline__ float float_of_ord(uint32_t o) {
 __device__ __forceinline__ uint64_t rank_key(float s, uint32_t k) {
   return ((uint64_t)ord_of(s) << 32) | (uint64_t)(0xffffffffu - k);
 }
+// trunc(e * 2^42) for e = exp(s - max) in (0, 1], from the float's bits: e = f * 2^(E-150)
+// with the 24-bit significand f, so e * 2^42 = f * 2^(E - 108) (zero for subnormal e).
 __device__ __forceinline__ uint64_t mass_fixed(float s, float smax) {
-  return (uint64_t)(expf(s - smax) * kMassScale);
+  const uint32_t v = __float_as_uint(expf(s - smax));
+  const int E = (int)(v >> 23);
+  if (E == 0) return 0ull;
+  const uint64_t f = (uint64_t)((v & 0x7fffffu) | 0x800000u);
+  const int sh = E - 108;
+  return sh >= 0 ? (f << sh) : (sh > -64 ? (f >> -sh) : 0ull);
 }
 // bucket 0 holds the highest scores; t * scale stays within [0, kBuckets] because
 // t is clamped to the spread that defines the scale
@@ -191,6 +200,7 @@ __device__ __forceinline__ uint64_t wave_incl_scan_u64(uint64_t v, int lane) {
 constexpr int kVec = 4;                         // frontier entries per thread per tile
 constexpr int kTileE = kSelThreads * kVec;      // 2048 entries per tile
 constexpr int kCache = 16384;                   // frontier entries cached in LDS (64 KB)
+constexpr int kUnroll = 4;                      // tiles loaded per pass iteration
 
 struct SelShared {
   float cache[kCache];              // member scores (NaN: not a member) when F <= kCache
@@ -274,13 +284,21 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
 #pragma unroll
     for (int i = 0; i < kVec; ++i) {
       const int k = k0 + i;
-      q.in[i] = k < F && (!pmask || ((pmask[k / b] >> m) & 1u));
+      q.in[i] = k < F && (!pmask || ((pmask[geo.bdiv.div((uint32_t)k)] >> m) & 1u));
     }
     return q;
   };
   auto get = [&](int k0) -> Quad {
     if (!cached) return load_global(k0);
     Quad q;
+    if (k0 >= F) {
+#pragma unroll
+      for (int i = 0; i < kVec; ++i) {
+        q.s[i] = 0.f;
+        q.in[i] = false;
+      }
+      return q;
+    }
     const float4 v = *reinterpret_cast<const float4*>(&sh.cache[k0]);
     q.s[0] = v.x;
     q.s[1] = v.y;
@@ -291,21 +309,28 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     return q;
   };
 
-  // pass 0: max, min over the member's frontier; fill the LDS cache when it fits
+  // pass 0: max, min over the member's frontier; fill the LDS cache when it fits.
+  // Every pass loads kUnroll tiles before using them, to keep several loads in flight.
   float mx = -INFINITY, mn = INFINITY;
-  for (int k0 = kVec * tid; k0 < F; k0 += kTileE) {
-    const Quad q = load_global(k0);
+  for (int base = kVec * tid; base < F; base += kTileE * kUnroll) {
+    Quad q[kUnroll];
 #pragma unroll
-    for (int i = 0; i < kVec; ++i) {
-      if (q.in[i]) {
-        mx = fmaxf(mx, q.s[i]);
-        mn = fminf(mn, q.s[i]);
+    for (int j = 0; j < kUnroll; ++j) q[j] = load_global(base + j * kTileE);
+#pragma unroll
+    for (int j = 0; j < kUnroll; ++j) {
+      const int k0 = base + j * kTileE;
+#pragma unroll
+      for (int i = 0; i < kVec; ++i) {
+        if (q[j].in[i]) {
+          mx = fmaxf(mx, q[j].s[i]);
+          mn = fminf(mn, q[j].s[i]);
+        }
       }
+      if (cached && k0 < F)
+        *reinterpret_cast<float4*>(&sh.cache[k0]) =
+            make_float4(q[j].in[0] ? q[j].s[0] : NAN, q[j].in[1] ? q[j].s[1] : NAN,
+                        q[j].in[2] ? q[j].s[2] : NAN, q[j].in[3] ? q[j].s[3] : NAN);
     }
-    if (cached)
-      *reinterpret_cast<float4*>(&sh.cache[k0]) =
-          make_float4(q.in[0] ? q.s[0] : NAN, q.in[1] ? q.s[1] : NAN, q.in[2] ? q.s[2] : NAN,
-                      q.in[3] ? q.s[3] : NAN);
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
@@ -337,14 +362,19 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     }
     __syncthreads();
     // pass 1: fixed-point mass histogram over score buckets (bucket 0 = highest scores)
-    for (int k0 = kVec * tid; k0 < F; k0 += kTileE) {
-      const Quad q = get(k0);
+    for (int base = kVec * tid; base < F; base += kTileE * kUnroll) {
+      Quad q[kUnroll];
 #pragma unroll
-      for (int i = 0; i < kVec; ++i) {
-        if (q.in[i]) {
-          const int bk = bucket_of(q.s[i], mx, scale, spread);
-          atomicAdd(&sh.hm[bk], (unsigned long long)mass_fixed(q.s[i], mx));
-          atomicAdd(&sh.hc[bk], 1u);
+      for (int j = 0; j < kUnroll; ++j) q[j] = get(base + j * kTileE);
+#pragma unroll
+      for (int j = 0; j < kUnroll; ++j) {
+#pragma unroll
+        for (int i = 0; i < kVec; ++i) {
+          if (q[j].in[i]) {
+            const int bk = bucket_of(q[j].s[i], mx, scale, spread);
+            atomicAdd(&sh.hm[bk], (unsigned long long)mass_fixed(q[j].s[i], mx));
+            atomicAdd(&sh.hc[bk], 1u);
+          }
         }
       }
     }
@@ -379,13 +409,18 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const uint32_t nb = sh.hc[bstar];
     if (nb <= (uint32_t)kCand) {
       // gather the boundary bucket, sort it by rank key, scan its masses
-      for (int k0 = kVec * tid; k0 < F; k0 += kTileE) {
-        const Quad q = get(k0);
+      for (int base = kVec * tid; base < F; base += kTileE * kUnroll) {
+        Quad q[kUnroll];
 #pragma unroll
-        for (int i = 0; i < kVec; ++i) {
-          if (q.in[i] && bucket_of(q.s[i], mx, scale, spread) == bstar) {
-            const uint32_t slot = atomicAdd(&sh.scalar_u32[0], 1u);
-            sh.cand[slot] = rank_key(q.s[i], (uint32_t)(k0 + i));
+        for (int j = 0; j < kUnroll; ++j) q[j] = get(base + j * kTileE);
+#pragma unroll
+        for (int j = 0; j < kUnroll; ++j) {
+#pragma unroll
+          for (int i = 0; i < kVec; ++i) {
+            if (q[j].in[i] && bucket_of(q[j].s[i], mx, scale, spread) == bstar) {
+              const uint32_t slot = atomicAdd(&sh.scalar_u32[0], 1u);
+              sh.cand[slot] = rank_key(q[j].s[i], (uint32_t)(base + j * kTileE + i));
+            }
           }
         }
       }
@@ -491,9 +526,9 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     int dup = 0;
     const int lim = min(F, (anchor + b - 1) / b);
     for (int k = 0; k < lim; ++k) {
-      const bool in = !pmask || ((pmask[k / b] >> m) & 1u);
+      const bool in = !pmask || ((pmask[geo.bdiv.div((uint32_t)k)] >> m) & 1u);
       if (keep_of(Sq[k], in, k)) {
-        const int node = (int)frontier_node(pnodes, k, b);
+        const int node = (int)frontier_node(pnodes, k, geo.bdiv);
         if (node * b < anchor) dup += min(b, anchor - node * b);
       }
     }
@@ -508,17 +543,17 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   // emit: the member's kept flags as a bit row (one 32-bit word per 32 entries, plain
   // stores); at level 1 also the token list
   uint32_t running = 0;
+  Quad qn = get(kVec * tid);  // the next tile's entries are loaded one tile ahead
   for (int t0 = 0; t0 < F; t0 += kTileE) {
     const int k0 = t0 + kVec * tid;
+    const Quad q = qn;
+    qn = get(k0 + kTileE);
     uint32_t kept_bits = 0, cnt = 0;
-    if (k0 < F) {
-      const Quad q = get(k0);
 #pragma unroll
-      for (int i = 0; i < kVec; ++i) {
-        if (keep_of(q.s[i], q.in[i], k0 + i)) {
-          kept_bits |= 1u << i;
-          ++cnt;
-        }
+    for (int i = 0; i < kVec; ++i) {
+      if (keep_of(q.s[i], q.in[i], k0 + i)) {
+        kept_bits |= 1u << i;
+        ++cnt;
       }
     }
     if (tid < kTileE / 32) sh.tile_bits[tid] = 0u;
@@ -529,7 +564,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
       uint32_t r = r0;
 #pragma unroll
       for (int i = 0; i < kVec; ++i)
-        if ((kept_bits >> i) & 1u) sh.tile_nodes[r++] = frontier_node(pnodes, k0 + i, b);
+        if ((kept_bits >> i) & 1u) sh.tile_nodes[r++] = frontier_node(pnodes, k0 + i, geo.bdiv);
     }
     __syncthreads();
     const int words = min(kTileE, F - t0 + 31) / 32;
@@ -537,7 +572,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     if (level == 1 && sel) {
       const int ntok = (int)tile_total * b;
       for (int i = tid; i < ntok; i += kSelThreads) {
-        const int rr = i / b, c = i % b;
+        const int rr = (int)geo.bdiv.div((uint32_t)i), c = i - rr * b;
         const int tok = (int)sh.tile_nodes[rr] * b + c;
         if (tok >= anchor) sel[anchor + (int64_t)(running + rr) * b + c - dup] = tok;
       }
@@ -552,60 +587,103 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
 }
 
 // --------------------------------------------------------------------------- compaction
-// One workgroup per unit: OR the members' kept-flag rows into a member mask per frontier
-// entry and write the entries with a non-empty mask, in ascending order, as the level's
-// union list.
+// The members' kept-flag rows are ORed into a member mask per frontier entry; entries with
+// a non-empty mask, in ascending order, form the level's union list. The frontier is cut
+// into chunks of kCompactChunk entries: a frontier of one chunk is compacted by one
+// workgroup per unit; larger ones by a count launch (entries kept per chunk) and a write
+// launch (each chunk adds the counts of the chunks before it), one workgroup per
+// (unit, chunk) in both.
+
+// Member masks of this thread's EPT entries c0 + EPT t .. (zero past F); returns count.
+template <int EPT>
+__device__ __forceinline__ uint32_t chunk_masks(const Geom& geo, int u, int Mu, int F, int c0,
+                                                const KeepBits& kb, uint32_t (*sbits)[kCompactChunk / 32],
+                                                uint32_t (&msk)[EPT]) {
+  const int words = (min(kCompactChunk, F - c0) + 31) / 32;
+  for (int i = threadIdx.x; i < Mu * words; i += kCompactThreads) {
+    const int mm = i / words, w = i % words;
+    sbits[mm][w] = kb.bits[(int64_t)qh_of(geo, u, mm) * kb.words + c0 / 32 + w];
+  }
+  __syncthreads();
+  const int e0 = EPT * threadIdx.x;
+  uint32_t cnt = 0;
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) msk[i] = 0u;
+  if (c0 + e0 < F) {
+    for (int mm = 0; mm < Mu; ++mm) {
+      const uint32_t w = sbits[mm][e0 / 32] >> (e0 % 32);
+#pragma unroll
+      for (int i = 0; i < EPT; ++i) msk[i] |= ((w >> i) & 1u) << mm;
+    }
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+      if (c0 + e0 + i >= F) msk[i] = 0u;
+      cnt += msk[i] != 0u;
+    }
+  }
+  return cnt;
+}
+
+template <int EPT>
+__device__ __forceinline__ void chunk_write(const uint32_t* pnodes, const FastDiv& bd, int c0, uint32_t r,
+                                            const uint32_t (&msk)[EPT], const LevelBufs& cur, int u) {
+  const int e0 = EPT * threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) {
+    if (msk[i]) {
+      cur.nodes[u * cur.stride + r] = frontier_node(pnodes, c0 + e0 + i, bd);
+      cur.masks[u * cur.stride + r] = msk[i];
+      ++r;
+    }
+  }
+}
+
+constexpr int kEPT = kCompactChunk / kCompactThreads;  // entries per thread (16)
+
+// mode 0: one workgroup walks every chunk of the unit. mode 1: count chunk blockIdx.x into
+// chunk_cnt. mode 2: write chunk blockIdx.x after the counts of the chunks before it.
 __global__ __launch_bounds__(kCompactThreads) void compact_kernel(
-    Geom geo, LevelBufs parent, int has_parent, int n_top, KeepBits kb, LevelBufs cur) {
-  constexpr int WPM = kCompactChunk / 32;  // words per member per chunk
-  constexpr int EPT = kCompactChunk / kCompactThreads;  // entries per thread (16)
-  __shared__ uint32_t sbits[kMaxMembers][WPM];
+    Geom geo, LevelBufs parent, int has_parent, int n_top, KeepBits kb, LevelBufs cur,
+    int mode, uint32_t* __restrict__ chunk_cnt, int max_chunks) {
+  __shared__ uint32_t sbits[kMaxMembers][kCompactChunk / 32];
   __shared__ uint32_t wave_sum[kCompactThreads / 64];
-  const int u = blockIdx.x;
+  const int u = blockIdx.y;
   const int b = geo.b;
   const int F = has_parent ? b * (int)parent.count[u] : n_top;
   const int Mu = members_of(geo, u);
   const uint32_t* pnodes = has_parent ? parent.nodes + u * parent.stride : nullptr;
-  uint32_t out = 0;
-  for (int c0 = 0; c0 < F; c0 += kCompactChunk) {
-    const int words = (min(kCompactChunk, F - c0) + 31) / 32;
-    __syncthreads();
-    for (int i = threadIdx.x; i < Mu * words; i += kCompactThreads) {
-      const int mm = i / words, w = i % words;
-      sbits[mm][w] = kb.bits[(int64_t)qh_of(geo, u, mm) * kb.words + c0 / 32 + w];
+  uint32_t msk[kEPT];
+  if (mode == 0) {
+    uint32_t out = 0;
+    for (int c0 = 0; c0 < F; c0 += kCompactChunk) {
+      __syncthreads();
+      const uint32_t cnt = chunk_masks<kEPT>(geo, u, Mu, F, c0, kb, sbits, msk);
+      uint32_t total;
+      const uint32_t r = out + block_excl_scan<kCompactThreads>(cnt, wave_sum, &total);
+      chunk_write<kEPT>(pnodes, geo.bdiv, c0, r, msk, cur, u);
+      out += total;
     }
-    __syncthreads();
-    // thread t: entries c0 + EPT t .. + EPT - 1 (half of one 32-bit word)
-    const int e0 = EPT * threadIdx.x;
-    uint32_t msk[EPT];
-    uint32_t cnt = 0;
-#pragma unroll
-    for (int i = 0; i < EPT; ++i) msk[i] = 0u;
-    if (c0 + e0 < F) {
-      for (int mm = 0; mm < Mu; ++mm) {
-        const uint32_t w = sbits[mm][e0 / 32] >> (e0 % 32);
-#pragma unroll
-        for (int i = 0; i < EPT; ++i) msk[i] |= ((w >> i) & 1u) << mm;
-      }
-#pragma unroll
-      for (int i = 0; i < EPT; ++i) {
-        if (c0 + e0 + i >= F) msk[i] = 0u;
-        cnt += msk[i] != 0u;
-      }
-    }
-    uint32_t total;
-    uint32_t r = out + block_excl_scan<kCompactThreads>(cnt, wave_sum, &total);
-#pragma unroll
-    for (int i = 0; i < EPT; ++i) {
-      if (msk[i]) {
-        cur.nodes[u * cur.stride + r] = frontier_node(pnodes, c0 + e0 + i, b);
-        cur.masks[u * cur.stride + r] = msk[i];
-        ++r;
-      }
-    }
-    out += total;
+    if (threadIdx.x == 0) cur.count[u] = out;
+    return;
   }
-  if (threadIdx.x == 0) cur.count[u] = out;
+  const int chunk = blockIdx.x;
+  const int c0 = chunk * kCompactChunk;
+  const int nchunks = (F + kCompactChunk - 1) / kCompactChunk;
+  if (c0 >= F) {
+    if (mode == 1 && threadIdx.x == 0) chunk_cnt[u * max_chunks + chunk] = 0u;
+    return;
+  }
+  const uint32_t cnt = chunk_masks<kEPT>(geo, u, Mu, F, c0, kb, sbits, msk);
+  uint32_t total;
+  const uint32_t r = block_excl_scan<kCompactThreads>(cnt, wave_sum, &total);
+  if (mode == 1) {
+    if (threadIdx.x == 0) chunk_cnt[u * max_chunks + chunk] = total;
+    return;
+  }
+  uint32_t before = 0;
+  for (int c = 0; c < chunk; ++c) before += chunk_cnt[u * max_chunks + c];
+  chunk_write<kEPT>(pnodes, geo.bdiv, c0, before + r, msk, cur, u);
+  if (chunk == nchunks - 1 && threadIdx.x == 0) cur.count[u] = before + total;
 }
 
 }  // namespace
@@ -645,11 +723,28 @@ hipError_t launch_select(const Geom& geo, int level, const float* S, int64_t S_s
 }
 
 hipError_t launch_compact(const Geom& geo, const LevelBufs* parent, int n_top, KeepBits kb,
-                          const LevelBufs& cur, hipStream_t s) {
+                          const LevelBufs& cur, uint32_t* chunk_cnt, hipStream_t s) {
   LevelBufs par = parent ? *parent : LevelBufs{};
-  hipLaunchKernelGGL(compact_kernel, dim3(geo.U), dim3(kCompactThreads), 0, s, geo, par,
-                     parent ? 1 : 0, n_top, kb, cur);
+  const int hp = parent ? 1 : 0;
+  const int cap = parent ? (int)(geo.b * parent->stride) : n_top;  // frontier capacity
+  const int max_chunks = (cap + kCompactChunk - 1) / kCompactChunk;
+  if (max_chunks <= 1) {
+    hipLaunchKernelGGL(compact_kernel, dim3(1, geo.U), dim3(kCompactThreads), 0, s, geo, par, hp,
+                       n_top, kb, cur, 0, chunk_cnt, 1);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(compact_kernel, dim3(max_chunks, geo.U), dim3(kCompactThreads), 0, s, geo,
+                     par, hp, n_top, kb, cur, 1, chunk_cnt, max_chunks);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(compact_kernel, dim3(max_chunks, geo.U), dim3(kCompactThreads), 0, s, geo,
+                     par, hp, n_top, kb, cur, 2, chunk_cnt, max_chunks);
   return hipGetLastError();
+}
+
+// Chunk counters the compaction needs (uint32 entries) for a frontier of up to n entries.
+int64_t compact_counter_words(int U, int64_t n) {
+  return (int64_t)U * ((n + kCompactChunk - 1) / kCompactChunk);
 }
 
 }  // namespace zha
