@@ -144,12 +144,37 @@ def test_bf16_d64_and_multi_sequence():
     _assert_ok(spec, summ, pyr)
 
 
-def test_exact_ties_broken_by_lowest_index():
+@pytest.mark.parametrize("case", [
+    dict(name="64k deep p=0.95", N=65536, p=0.95),
+    dict(name="64k deep p=0.5", N=65536, p=0.5),
+    dict(name="64k deep p=1", N=65536, p=1.0),
+    dict(name="64k b=2, two chunked levels", N=65536, b=2, L=10, p=0.9),
+    dict(name="64k one level, chunked top", N=65536, L=1, p=0.95),
+    dict(name="96k ragged last chunk, anchor 7", N=98304, p=0.8, anchor=7),
+])
+def test_chunked_selection(case):
+    """Frontiers of 16384 entries or more take the chunked selection (histogram, cut and
+    emit launches over frontier chunks); every head of one sequence is checked."""
+    case = dict(case)
+    name = case.pop("name")
+    p = case.pop("p")
+    anchor = case.pop("anchor", 1)
+    spec = W.spec("32k_deep", B=1, **case)
+    res = H.run_gpu(spec, p, anchor=anchor)
+    reps, pyr = H.check_units(spec, res, p, anchor=anchor)
+    summ = C.summarize(reps)
+    _report(name, summ, pyr)
+    _assert_ok(spec, summ, pyr)
+
+
+@pytest.mark.parametrize("N", [16384, 65536])
+def test_exact_ties_broken_by_lowest_index(N):
     """Identical keys everywhere: every score at every level ties. The cut must keep the
-    lowest node ids; the boundary bucket holds 4096 entries, past the sort capacity."""
+    lowest node ids; the boundary bucket holds N / 4 entries, past the sort capacity
+    (at N = 65536 in the chunked selection)."""
     import tree_indexed_sparse_amd as Z
 
-    spec = W.spec("tiny", N=16384, b=4, L=1, T=2, needles="none")
+    spec = W.spec("tiny", N=N, b=4, L=1, T=2, needles="none")
     inp = W.gen_all(spec, device="cuda")
     inp["K"][:] = inp["K"][0, 0, 0]
     res = H.run_gpu(spec, 0.95, inputs=inp)

@@ -103,6 +103,7 @@ struct WsLayout {
   int U, QH, splits;
   int64_t n[ZHA_MAX_LEVELS + 1];  // nodes per unit at each level (current N)
   int64_t off_count, off_lvl, off_S, off_bits, off_part, off_chunks;
+  int64_t off_pmax, off_pmin, off_hm, off_hc, off_choff, off_cut, pstride, nch;
   int64_t off_nodes[ZHA_MAX_LEVELS + 1], off_masks[ZHA_MAX_LEVELS + 1];
   int64_t S_stride, bit_words;
   int64_t total;
@@ -166,6 +167,21 @@ WsLayout layout_of(const Geom& g) {
   off = align256(off + 4 * (int64_t)g.U * w.splits * kMaxMembers * (g.D + 2));
   w.off_chunks = off;
   off = align256(off + 4 * compact_counter_words(g.U, w.n[1]));
+  // chunked-selection scratch, sized for the largest frontier (level 1)
+  w.pstride = wide_partial_stride(w.n[1]);
+  w.nch = wide_chunks(w.n[1]);
+  w.off_pmax = off;
+  off = align256(off + 4 * (int64_t)w.QH * w.pstride);
+  w.off_pmin = off;
+  off = align256(off + 4 * (int64_t)w.QH * w.pstride);
+  w.off_hm = off;
+  off = align256(off + 8 * (int64_t)w.QH * w.nch * wide_buckets());
+  w.off_hc = off;
+  off = align256(off + 4 * (int64_t)w.QH * w.nch * wide_buckets());
+  w.off_choff = off;
+  off = align256(off + 4 * (int64_t)w.QH * w.nch);
+  w.off_cut = off;
+  off = align256(off + 16 * (int64_t)w.QH);
   w.total = off;
   return w;
 }
@@ -348,6 +364,15 @@ int zha_attend(const zha_tree* t, const void* Q, int T, int Hq, const void* K, c
   float* S = (float*)(ws + w.off_S);
   int32_t* lvl = (int32_t*)(ws + w.off_lvl);
   const KeepBits kb{(uint32_t*)(ws + w.off_bits), w.bit_words};
+  WideSel wsel;
+  wsel.pmax = (float*)(ws + w.off_pmax);
+  wsel.pmin = (float*)(ws + w.off_pmin);
+  wsel.pstride = w.pstride;
+  wsel.hm = (unsigned long long*)(ws + w.off_hm);
+  wsel.hc = (uint32_t*)(ws + w.off_hc);
+  wsel.choff = (uint32_t*)(ws + w.off_choff);
+  wsel.cut = (uint32_t*)(ws + w.off_cut);
+  wsel.nch = w.nch;
 
   hipError_t e = hipSuccess;
   int64_t cap_l = t->N_cap;
@@ -356,13 +381,16 @@ int zha_attend(const zha_tree* t, const void* Q, int T, int Hq, const void* K, c
     const LevelBufs* parent = (l < t->L) ? &lv[l + 1] : nullptr;
     const int n_top = (l == t->L) ? (int)w.n[t->L] : 0;
     const float* X = t->pyramid + t->level_off[l];
+    const int64_t frontier_cap = parent ? t->b * parent->stride : n_top;
+    const WideSel* wide = select_is_wide(frontier_cap) ? &wsel : nullptr;
     e = timed(ZHA_K_SCORE, l, s, [&] {
-      return launch_score(g, X, cap_l * t->d, Q, t->dtype, parent, n_top, S, w.S_stride, s);
+      return launch_score(g, X, cap_l * t->d, Q, t->dtype, parent, n_top, S, w.S_stride, wide,
+                          s);
     });
     if (e != hipSuccess) return hip_fail(e, "score launch");
     e = timed(ZHA_K_SELECT, l, s, [&] {
       return launch_select(g, l, S, w.S_stride, parent, n_top, kb, p, anchor,
-                           l == 1 ? sel_idx : nullptr, cap, sel_count, lvl, s);
+                           l == 1 ? sel_idx : nullptr, cap, sel_count, lvl, wide, s);
     });
     if (e != hipSuccess) return hip_fail(e, "select launch");
     e = timed(ZHA_K_COMPACT, l, s, [&] {

@@ -90,6 +90,19 @@ struct KeepBits {
   int64_t words;
 };
 
+// Scratch of the chunked selection that large frontiers take (one workgroup per
+// (frontier chunk, query head) instead of one per query head).
+struct WideSel {
+  float* pmax;                // [QH][pstride] member max score per score workgroup
+  float* pmin;                // [QH][pstride] member min score per score workgroup
+  int64_t pstride;
+  unsigned long long* hm;     // [QH][nch][buckets] fixed-point mass per chunk and bucket
+  uint32_t* hc;               // [QH][nch][buckets] entry count per chunk and bucket
+  uint32_t* choff;            // [QH][nch] kept entries before each chunk
+  uint32_t* cut;              // [QH][4] cut score bits, cut index, token base, kept total
+  int64_t nch;
+};
+
 // ---------------------------------------------------------------------------------------
 // launchers (defined in the .hip files; all enqueue on `s`, return hipGetLastError())
 // ---------------------------------------------------------------------------------------
@@ -111,15 +124,23 @@ hipError_t launch_pool_fused(int dtype_in, const void* child, int64_t in_unit_st
                              int row_begin, int row_end, int b, int D, hipStream_t s);
 
 // Scores of a level's union frontier for every member: S[qh][k].
+// wide != nullptr: also write the per-workgroup member max/min the chunked selection reads.
 hipError_t launch_score(const Geom& geo, const float* X, int64_t X_unit_stride, const void* Q,
                         int dtype, const LevelBufs* parent, int n_top, float* S,
-                        int64_t S_stride, hipStream_t s);
+                        int64_t S_stride, const WideSel* wide, hipStream_t s);
+
+// Whether a frontier of up to `cap_entries` entries takes the chunked selection, and the
+// sizes of its scratch for frontiers up to `cap_entries`.
+bool select_is_wide(int64_t cap_entries);
+int64_t wide_partial_stride(int64_t cap_entries);
+int64_t wide_chunks(int64_t cap_entries);
+int wide_buckets();
 
 // Per-member top-p: kept flags into `kb`; at level 1 also the token lists and counts.
 hipError_t launch_select(const Geom& geo, int level, const float* S, int64_t S_stride,
                          const LevelBufs* parent, int n_top, KeepBits kb, float p, int anchor,
                          int32_t* sel_idx, int64_t cap, int32_t* sel_count, int32_t* lvl_kept,
-                         hipStream_t s);
+                         const WideSel* wide, hipStream_t s);
 
 // Union of the members' kept flags -> ascending kept-node list with member masks.
 // chunk_cnt: scratch of compact_counter_words(U, frontier capacity) words.

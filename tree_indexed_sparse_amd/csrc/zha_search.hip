@@ -53,10 +53,12 @@ template <int D, typename Tq>
 __global__ __launch_bounds__(kScoreThreads) void score_kernel(
     Geom geo, const float* __restrict__ X, int64_t X_unit_stride, const Tq* __restrict__ Q,
     LevelBufs parent, int has_parent, int n_top, float* __restrict__ S, int64_t S_stride,
-    float sigma) {
+    float sigma, float* __restrict__ pmax, float* __restrict__ pmin, int64_t pstride) {
   constexpr int NQ = D / 16;
   constexpr int kMaxParents = kScoreEntries / 2 + 2;
   __shared__ uint32_t sPn[kMaxParents];
+  __shared__ uint32_t sPm[kMaxParents];
+  __shared__ float sRed[2][kScoreThreads / 64][16];
 
   const int u = blockIdx.y;
   const int b = geo.b;
@@ -70,8 +72,10 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
   const int p0 = (int)geo.bdiv.div((uint32_t)k_wg);
   if (has_parent) {
     const int np = (int)geo.bdiv.div((uint32_t)(min(k_wg + kScoreEntries, F) - 1)) - p0 + 1;
-    for (int i = threadIdx.x; i < np; i += kScoreThreads)
+    for (int i = threadIdx.x; i < np; i += kScoreThreads) {
       sPn[i] = parent.nodes[u * parent.stride + p0 + i];
+      if (pmax) sPm[i] = parent.masks[u * parent.stride + p0 + i];
+    }
   }
   float qf[NQ][4];
   const Tq* qrow = Q + (int64_t)qh_of(geo, u, mem < Mu ? mem : 0) * D;
@@ -83,6 +87,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
   const float* Xu = X + (int64_t)bg_of(geo, u) * X_unit_stride;
   float* Srow = S + (int64_t)qh_of(geo, u, mem < Mu ? mem : 0) * S_stride;
   const int k_wave = k_wg + wave * (kScoreEntries / 4);
+  float lmx = -INFINITY, lmn = INFINITY;  // over this lane's member rows
 
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
@@ -123,7 +128,43 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
           if (kb + 1 < F) Srow[kb + 1] = o.y;
           if (kb + 2 < F) Srow[kb + 2] = o.z;
         }
+        if (pmax) {
+          const float ov[4] = {o.x, o.y, o.z, o.w};
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int k = kb + r;
+            const bool in = k < F && (!has_parent ||
+                                      ((sPm[geo.bdiv.div((uint32_t)k) - p0] >> mem) & 1u));
+            if (in) {
+              lmx = fmaxf(lmx, ov[r]);
+              lmn = fminf(lmn, ov[r]);
+            }
+          }
+        }
       }
+    }
+  }
+  if (pmax) {
+    // lanes l, l^16, l^32, l^48 hold one member; then the four waves
+    lmx = fmaxf(lmx, __shfl_xor(lmx, 16, 64));
+    lmn = fminf(lmn, __shfl_xor(lmn, 16, 64));
+    lmx = fmaxf(lmx, __shfl_xor(lmx, 32, 64));
+    lmn = fminf(lmn, __shfl_xor(lmn, 32, 64));
+    if (grp == 0) {
+      sRed[0][wave][mem] = lmx;
+      sRed[1][wave][mem] = lmn;
+    }
+    __syncthreads();
+    if (threadIdx.x < Mu) {
+      float mx = sRed[0][0][threadIdx.x], mn = sRed[1][0][threadIdx.x];
+#pragma unroll
+      for (int w = 1; w < kScoreThreads / 64; ++w) {
+        mx = fmaxf(mx, sRed[0][w][threadIdx.x]);
+        mn = fminf(mn, sRed[1][w][threadIdx.x]);
+      }
+      const int64_t at = (int64_t)qh_of(geo, u, threadIdx.x) * pstride + blockIdx.x;
+      pmax[at] = mx;
+      pmin[at] = mn;
     }
   }
 }
@@ -153,10 +194,11 @@ __device__ __forceinline__ uint64_t mass_fixed(float s, float smax) {
 }
 // bucket 0 holds the highest scores; t * scale stays within [0, kBuckets] because
 // t is clamped to the spread that defines the scale
+template <int NB = kBuckets>
 __device__ __forceinline__ int bucket_of(float s, float smax, float scale, float spread) {
   const float t = fminf(smax - s, spread);
   const int b = (int)(t * scale);
-  return b < kBuckets - 1 ? b : kBuckets - 1;
+  return b < NB - 1 ? b : NB - 1;
 }
 
 // ceil(p * Z) exactly, for 0 < p < 1 (p = mant * 2^-sh, mant < 2^24, sh >= 24)
@@ -586,6 +628,470 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   }
 }
 
+// ------------------------------------------------------------------ chunked selection
+// A large frontier is cut into chunks of kWideChunk entries and each query head's top-p
+// runs in three launches, so that (chunks x query heads) workgroups share the work:
+//   hist: per (chunk, head), the head's max/min (from the score partials) fixes the bucket
+//         grid; the chunk's fixed-point masses and counts go to a per-chunk histogram;
+//   cut:  per head, the chunk histograms are summed, the bucket where the cumulative mass
+//         reaches p is found, its entries are gathered from the score row and sorted (or
+//         radix-selected) to the exact cut, and kept counts per chunk are prefixed;
+//   emit: per (chunk, head), kept-flag words and, at level 1, the token list at the
+//         chunk's offset.
+// The buckets, masses and cut are those of the single-workgroup selection, so both paths
+// keep the same set.
+
+constexpr int kWideThreads = 512;
+constexpr int kWideChunk = 8192;                    // entries per chunk: 4 tiles of kTileE
+constexpr int kWideTiles = kWideChunk / kTileE;
+constexpr int kWB = 1024;                           // buckets of the chunked histogram
+constexpr int kCutThreads = 1024;                   // one bucket per thread
+constexpr int kCutWaves = kCutThreads / 64;
+constexpr int kMaxWideChunks = (1 << kMaxLog2Nodes) / kWideChunk;
+constexpr int64_t kWideMin = 16384;                 // frontiers of this size or more
+static_assert(kWB == kCutThreads, "the cut kernel gives each thread one bucket");
+static_assert(kWideChunk % kTileE == 0 && kTileE % 32 == 0, "chunks hold whole tiles and words");
+
+// Four consecutive entries k0..k0+3 of member m's score row, below `end`.
+__device__ __forceinline__ Quad load_quad(const float* Sq, const uint32_t* pmask, int m,
+                                          const FastDiv& bd, int k0, int end) {
+  Quad q;
+  const float4 v = (k0 + 3 < end)
+                       ? *reinterpret_cast<const float4*>(Sq + k0)
+                       : make_float4(k0 < end ? Sq[k0] : 0.f, k0 + 1 < end ? Sq[k0 + 1] : 0.f,
+                                     k0 + 2 < end ? Sq[k0 + 2] : 0.f, 0.f);
+  q.s[0] = v.x;
+  q.s[1] = v.y;
+  q.s[2] = v.z;
+  q.s[3] = v.w;
+#pragma unroll
+  for (int i = 0; i < kVec; ++i) {
+    const int k = k0 + i;
+    q.in[i] = k < end && (!pmask || ((pmask[bd.div((uint32_t)k)] >> m) & 1u));
+  }
+  return q;
+}
+
+// The head's max and min member score over a frontier of F entries, from the score
+// kernel's per-workgroup partials (block-wide, every thread gets both).
+template <int NT>
+__device__ __forceinline__ void partial_minmax(const WideSel& w, int qh, int F, float* red,
+                                               float* omx, float* omn) {
+  constexpr int NW = NT / 64;
+  const int np = (F + kScoreEntries - 1) / kScoreEntries;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float mx = -INFINITY, mn = INFINITY;
+  for (int i = threadIdx.x; i < np; i += NT) {
+    mx = fmaxf(mx, w.pmax[(int64_t)qh * w.pstride + i]);
+    mn = fminf(mn, w.pmin[(int64_t)qh * w.pstride + i]);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+    mn = fminf(mn, __shfl_xor(mn, off, 64));
+  }
+  if (lane == 0) {
+    red[wave] = mx;
+    red[NW + wave] = mn;
+  }
+  __syncthreads();
+  mx = red[0];
+  mn = red[NW];
+#pragma unroll
+  for (int v = 1; v < NW; ++v) {
+    mx = fmaxf(mx, red[v]);
+    mn = fminf(mn, red[NW + v]);
+  }
+  *omx = mx;
+  *omn = mn;
+}
+
+__global__ __launch_bounds__(kWideThreads) void wide_hist_kernel(
+    Geom geo, const float* __restrict__ S, int64_t S_stride, LevelBufs parent, int has_parent,
+    int n_top, WideSel w) {
+  __shared__ unsigned long long hm[kWB];
+  __shared__ uint32_t hc[kWB];
+  __shared__ float red[2 * (kWideThreads / 64)];
+  const int qh = blockIdx.y, chunk = blockIdx.x;
+  int u, m;
+  unit_member_of(geo, qh, &u, &m);
+  const int F = has_parent ? geo.b * (int)parent.count[u] : n_top;
+  const int c0 = chunk * kWideChunk;
+  if (c0 >= F) return;
+  const int tid = threadIdx.x;
+  const float* Sq = S + (int64_t)qh * S_stride;
+  const uint32_t* pmask = has_parent ? parent.masks + u * parent.stride : nullptr;
+  const int end = min(F, c0 + kWideChunk);
+  Quad q[kWideTiles];
+#pragma unroll
+  for (int j = 0; j < kWideTiles; ++j)
+    q[j] = load_quad(Sq, pmask, m, geo.bdiv, c0 + j * kTileE + kVec * tid, end);
+  for (int i = tid; i < kWB; i += kWideThreads) {
+    hm[i] = 0ull;
+    hc[i] = 0u;
+  }
+  float mx, mn;
+  partial_minmax<kWideThreads>(w, qh, F, red, &mx, &mn);  // its barrier orders the zeroing
+  const float spread = fminf(mx - mn, kMaxSpread);
+  const float scale = spread > 0.f ? (float)kWB / spread : 0.f;
+#pragma unroll
+  for (int j = 0; j < kWideTiles; ++j) {
+#pragma unroll
+    for (int i = 0; i < kVec; ++i) {
+      if (q[j].in[i]) {
+        const int bk = bucket_of<kWB>(q[j].s[i], mx, scale, spread);
+        atomicAdd(&hm[bk], (unsigned long long)mass_fixed(q[j].s[i], mx));
+        atomicAdd(&hc[bk], 1u);
+      }
+    }
+  }
+  __syncthreads();
+  const int64_t base = ((int64_t)qh * w.nch + chunk) * kWB;
+  for (int i = tid; i < kWB; i += kWideThreads) {
+    w.hm[base + i] = hm[i];
+    w.hc[base + i] = hc[i];
+  }
+}
+
+struct CutShared {
+  unsigned long long cand[kCand];
+  unsigned long long radix[256];
+  unsigned long long wsum[kCutWaves];
+  uint32_t chunk_keep[kMaxWideChunks];
+  float red[2 * kCutWaves];
+  unsigned long long scalar_u64[4];
+  uint32_t scalar_u32[4];
+};
+
+// block-wide inclusive scan of one u64 per thread; *total = the sum over the block
+__device__ __forceinline__ uint64_t cut_block_scan(uint64_t v, unsigned long long* wsum,
+                                                   uint64_t* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint64_t incl = wave_incl_scan_u64(v, lane);
+  __syncthreads();
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  uint64_t before = 0, tot = 0;
+#pragma unroll
+  for (int v2 = 0; v2 < kCutWaves; ++v2) {
+    const uint64_t c = wsum[v2];
+    before += (v2 < wave) ? c : 0ull;
+    tot += c;
+  }
+  *total = tot;
+  return before + incl;
+}
+
+__global__ __launch_bounds__(kCutThreads) void wide_cut_kernel(
+    Geom geo, int level, const float* __restrict__ S, int64_t S_stride, LevelBufs parent,
+    int has_parent, int n_top, float p, int anchor, int32_t* __restrict__ sel_idx, int64_t cap,
+    int32_t* __restrict__ sel_count, int32_t* __restrict__ lvl_kept, WideSel w) {
+  __shared__ CutShared sh;
+  const int qh = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int u, m;
+  unit_member_of(geo, qh, &u, &m);
+  const int b = geo.b;
+  const int F = has_parent ? b * (int)parent.count[u] : n_top;
+  const int nch = (F + kWideChunk - 1) / kWideChunk;
+  const float* Sq = S + (int64_t)qh * S_stride;
+  const uint32_t* pmask = has_parent ? parent.masks + u * parent.stride : nullptr;
+  const uint32_t* pnodes = has_parent ? parent.nodes + u * parent.stride : nullptr;
+  for (int i = tid; i < nch; i += kCutThreads) sh.chunk_keep[i] = 0u;
+  if (tid == 0) {
+    sh.scalar_u32[0] = 0u;  // boundary bucket
+    sh.scalar_u32[1] = 0u;  // its entry count
+    sh.scalar_u32[2] = 0u;  // gathered candidates
+    sh.scalar_u32[3] = 0u;  // last kept candidate (sorted position)
+    sh.scalar_u64[0] = 0ull;
+    sh.scalar_u64[2] = ~0ull;
+  }
+  float mx, mn;
+  partial_minmax<kCutThreads>(w, qh, F, sh.red, &mx, &mn);
+  const float spread = fminf(mx - mn, kMaxSpread);
+  const float scale = spread > 0.f ? (float)kWB / spread : 0.f;
+  const bool keep_all = !(p < 1.0f);
+
+  // bucket totals over the chunks: thread `tid` owns bucket `tid`
+  uint64_t hsum = 0;
+  uint32_t csum = 0;
+  const int64_t hbase = (int64_t)qh * w.nch * kWB;
+  for (int c = 0; c < nch; ++c) {
+    hsum += w.hm[hbase + (int64_t)c * kWB + tid];
+    csum += w.hc[hbase + (int64_t)c * kWB + tid];
+  }
+  uint64_t Z;
+  const uint64_t incl = cut_block_scan(hsum, sh.wsum, &Z);
+  const uint64_t T = keep_all ? Z : ceil_mul_p(p, Z);
+  const uint64_t excl = incl - hsum;
+  if (!keep_all && excl < T && incl >= T) {
+    sh.scalar_u32[0] = (uint32_t)tid;
+    sh.scalar_u32[1] = csum;
+    sh.scalar_u64[0] = excl;
+  }
+  __syncthreads();
+  const int bstar = keep_all ? kWB : (int)sh.scalar_u32[0];
+  const uint64_t before = sh.scalar_u64[0];
+  const uint32_t nb = keep_all ? 0u : sh.scalar_u32[1];
+
+  // kept entries per chunk in the buckets above the boundary: one wave per chunk
+  for (int c = wave; c < nch; c += kCutWaves) {
+    uint32_t acc = 0;
+    for (int j = lane; j < bstar; j += 64) acc += w.hc[hbase + (int64_t)c * kWB + j];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
+    if (lane == 0) sh.chunk_keep[c] = acc;
+  }
+
+  uint64_t key = ~0ull;  // keep_all: every member entry ranks at or above the cut
+  if (!keep_all) {
+    if (nb <= (uint32_t)kCand) {
+      for (int base = kVec * tid; base < F; base += kVec * kCutThreads * kUnroll) {
+        Quad q[kUnroll];
+#pragma unroll
+        for (int j = 0; j < kUnroll; ++j)
+          q[j] = load_quad(Sq, pmask, m, geo.bdiv, base + j * kVec * kCutThreads, F);
+#pragma unroll
+        for (int j = 0; j < kUnroll; ++j) {
+#pragma unroll
+          for (int i = 0; i < kVec; ++i) {
+            if (q[j].in[i] && bucket_of<kWB>(q[j].s[i], mx, scale, spread) == bstar) {
+              const uint32_t slot = atomicAdd(&sh.scalar_u32[2], 1u);
+              if (slot < (uint32_t)kCand)
+                sh.cand[slot] = rank_key(q[j].s[i], (uint32_t)(base + j * kVec * kCutThreads + i));
+            }
+          }
+        }
+      }
+      __syncthreads();
+      int P2 = 1;
+      while (P2 < (int)nb) P2 <<= 1;
+      for (int i = nb + tid; i < P2; i += kCutThreads) sh.cand[i] = 0ull;
+      __syncthreads();
+      for (int size = 2; size <= P2; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+          for (int i = tid; i < P2; i += kCutThreads) {
+            const int j = i ^ stride;
+            if (j > i) {
+              const unsigned long long x = sh.cand[i], y = sh.cand[j];
+              const bool desc = (i & size) == 0;
+              if (desc ? (x < y) : (x > y)) {
+                sh.cand[i] = y;
+                sh.cand[j] = x;
+              }
+            }
+          }
+          __syncthreads();
+        }
+      }
+      // cumulative mass in rank order from `before`: two candidates per thread
+      constexpr int per = kCand / kCutThreads;
+      uint64_t mloc[per];
+      uint64_t loc = 0;
+#pragma unroll
+      for (int i = 0; i < per; ++i) {
+        const int idx = per * tid + i;
+        mloc[i] = idx < (int)nb ? mass_fixed(float_of_ord((uint32_t)(sh.cand[idx] >> 32)), mx) : 0ull;
+        loc += mloc[i];
+      }
+      uint64_t tot;
+      const uint64_t cin = cut_block_scan(loc, sh.wsum, &tot) + before;
+      uint64_t run = cin - loc;
+      if (run < T && cin >= T) {
+#pragma unroll
+        for (int i = 0; i < per; ++i) {
+          run += mloc[i];
+          if (run >= T) {
+            sh.scalar_u64[2] = sh.cand[per * tid + i];
+            sh.scalar_u32[3] = (uint32_t)(per * tid + i);
+            break;
+          }
+        }
+      }
+      __syncthreads();
+      key = sh.scalar_u64[2];
+      const int last = (int)sh.scalar_u32[3];
+      for (int i = tid; i <= last; i += kCutThreads) {
+        const uint32_t k = 0xffffffffu - (uint32_t)sh.cand[i];
+        atomicAdd(&sh.chunk_keep[k / kWideChunk], 1u);
+      }
+    } else {
+      // boundary bucket too large to sort: exact MSD radix select on the rank key,
+      // restricted to the boundary bucket, 8 bits per pass
+      uint64_t prefix = 0, pbits = 0, need = T - before;
+      for (int shift = 56; shift >= 0; shift -= 8) {
+        for (int i = tid; i < 256; i += kCutThreads) sh.radix[i] = 0ull;
+        __syncthreads();
+        for (int k0 = kVec * tid; k0 < F; k0 += kVec * kCutThreads) {
+          const Quad q = load_quad(Sq, pmask, m, geo.bdiv, k0, F);
+#pragma unroll
+          for (int i = 0; i < kVec; ++i) {
+            if (!q.in[i] || bucket_of<kWB>(q.s[i], mx, scale, spread) != bstar) continue;
+            const uint64_t kk = rank_key(q.s[i], (uint32_t)(k0 + i));
+            if ((kk & pbits) != prefix) continue;
+            atomicAdd(&sh.radix[(kk >> shift) & 255u], (unsigned long long)mass_fixed(q.s[i], mx));
+          }
+        }
+        __syncthreads();
+        if (tid == 0) {
+          uint64_t r = 0;
+          int dsel = 0;
+          for (int dg = 255; dg >= 0; --dg) {
+            if (r + sh.radix[dg] >= need) {
+              dsel = dg;
+              break;
+            }
+            r += sh.radix[dg];
+          }
+          sh.scalar_u64[3] = (uint64_t)dsel;
+          sh.scalar_u64[1] = r;
+        }
+        __syncthreads();
+        need -= sh.scalar_u64[1];
+        prefix |= sh.scalar_u64[3] << shift;
+        pbits |= 255ull << shift;
+        __syncthreads();
+      }
+      key = prefix;
+      for (int k0 = kVec * tid; k0 < F; k0 += kVec * kCutThreads) {
+        const Quad q = load_quad(Sq, pmask, m, geo.bdiv, k0, F);
+#pragma unroll
+        for (int i = 0; i < kVec; ++i) {
+          if (q.in[i] && bucket_of<kWB>(q.s[i], mx, scale, spread) == bstar &&
+              rank_key(q.s[i], (uint32_t)(k0 + i)) >= key)
+            atomicAdd(&sh.chunk_keep[(k0 + i) / kWideChunk], 1u);
+        }
+      }
+    }
+  }
+  const float s_cut = keep_all ? -INFINITY : float_of_ord((uint32_t)(key >> 32));
+  const uint32_t k_cut = keep_all ? 0xffffffffu : 0xffffffffu - (uint32_t)key;
+  __syncthreads();
+
+  // chunk offsets: exclusive prefix of the kept counts (wave 0, four chunks per lane)
+  if (wave == 0) {
+    constexpr int per = kMaxWideChunks / 64;
+    uint32_t c4[per];
+    uint32_t loc = 0;
+#pragma unroll
+    for (int i = 0; i < per; ++i) {
+      const int c = per * lane + i;
+      c4[i] = c < nch ? sh.chunk_keep[c] : 0u;
+      loc += c4[i];
+    }
+    uint32_t inc = loc;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const uint32_t o = __shfl_up(inc, d, 64);
+      if (lane >= d) inc += o;
+    }
+    uint32_t run = inc - loc;
+#pragma unroll
+    for (int i = 0; i < per; ++i) {
+      const int c = per * lane + i;
+      if (c < nch) w.choff[(int64_t)qh * w.nch + c] = run;
+      run += c4[i];
+    }
+    if (lane == 63) sh.scalar_u32[2] = inc;  // kept total
+  }
+  // anchor overlap at level 1: kept tokens below `anchor` (first ceil(anchor / b) entries)
+  if (level == 1 && tid == 64) {
+    int dup = 0;
+    const int lim = min(F, (anchor + b - 1) / b);
+    for (int k = 0; k < lim; ++k) {
+      const bool in = !pmask || ((pmask[geo.bdiv.div((uint32_t)k)] >> m) & 1u);
+      const float sk = Sq[k];
+      if (in && (sk > s_cut || (sk == s_cut && (uint32_t)k <= k_cut))) {
+        const int node = (int)frontier_node(pnodes, k, geo.bdiv);
+        if (node * b < anchor) dup += min(b, anchor - node * b);
+      }
+    }
+    sh.scalar_u32[3] = (uint32_t)dup;
+  }
+  __syncthreads();
+  const uint32_t kept = sh.scalar_u32[2];
+  const int dup = level == 1 ? (int)sh.scalar_u32[3] : 0;
+  if (tid == 0) {
+    uint32_t* rec = w.cut + 4 * (int64_t)qh;
+    rec[0] = __float_as_uint(s_cut);
+    rec[1] = k_cut;
+    rec[2] = (uint32_t)(anchor - dup);
+    rec[3] = kept;
+    lvl_kept[(int64_t)qh * (geo.L + 1) + level] = (int32_t)kept;
+    if (level == 1) sel_count[qh] = anchor + (int32_t)kept * b - dup;
+  }
+  if (level == 1 && sel_idx)
+    for (int i = tid; i < anchor; i += kCutThreads) sel_idx[(int64_t)qh * cap + i] = i;
+}
+
+__global__ __launch_bounds__(kWideThreads) void wide_emit_kernel(
+    Geom geo, int level, const float* __restrict__ S, int64_t S_stride, LevelBufs parent,
+    int has_parent, int n_top, KeepBits kb, int anchor, int32_t* __restrict__ sel_idx,
+    int64_t cap, WideSel w) {
+  __shared__ uint32_t tile_nodes[kTileE];
+  __shared__ uint32_t wave_sum[kWideThreads / 64];
+  const int qh = blockIdx.y, chunk = blockIdx.x;
+  int u, m;
+  unit_member_of(geo, qh, &u, &m);
+  const int b = geo.b;
+  const int F = has_parent ? b * (int)parent.count[u] : n_top;
+  const int c0 = chunk * kWideChunk;
+  if (c0 >= F) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const float* Sq = S + (int64_t)qh * S_stride;
+  const uint32_t* pmask = has_parent ? parent.masks + u * parent.stride : nullptr;
+  const uint32_t* pnodes = has_parent ? parent.nodes + u * parent.stride : nullptr;
+  const int end = min(F, c0 + kWideChunk);
+  Quad q[kWideTiles];
+#pragma unroll
+  for (int j = 0; j < kWideTiles; ++j)
+    q[j] = load_quad(Sq, pmask, m, geo.bdiv, c0 + j * kTileE + kVec * tid, end);
+  const uint32_t* rec = w.cut + 4 * (int64_t)qh;
+  const float s_cut = __uint_as_float(rec[0]);
+  const uint32_t k_cut = rec[1];
+  const int tok_base = (int)rec[2];
+  uint32_t running = w.choff[(int64_t)qh * w.nch + chunk];
+  uint32_t* kbits = kb.bits + (int64_t)qh * kb.words;
+  int32_t* sel = (level == 1 && sel_idx) ? sel_idx + (int64_t)qh * cap : nullptr;
+#pragma unroll
+  for (int j = 0; j < kWideTiles; ++j) {
+    const int t0 = c0 + j * kTileE;
+    if (t0 >= end) break;
+    const int k0 = t0 + kVec * tid;
+    uint32_t bits = 0, cnt = 0;
+#pragma unroll
+    for (int i = 0; i < kVec; ++i) {
+      const float sv = q[j].s[i];
+      if (q[j].in[i] && (sv > s_cut || (sv == s_cut && (uint32_t)(k0 + i) <= k_cut))) {
+        bits |= 1u << i;
+        ++cnt;
+      }
+    }
+    // eight lanes' nibbles make one 32-entry word
+    uint32_t word = bits << (4 * (lane & 7));
+    word |= __shfl_xor(word, 1, 64);
+    word |= __shfl_xor(word, 2, 64);
+    word |= __shfl_xor(word, 4, 64);
+    if ((lane & 7) == 0 && k0 < end) kbits[k0 / 32] = word;
+    if (sel) {
+      uint32_t tile_total;
+      uint32_t r = block_excl_scan<kWideThreads>(cnt, wave_sum, &tile_total);
+#pragma unroll
+      for (int i = 0; i < kVec; ++i)
+        if ((bits >> i) & 1u) tile_nodes[r++] = frontier_node(pnodes, k0 + i, geo.bdiv);
+      __syncthreads();
+      const int ntok = (int)tile_total * b;
+      for (int i = tid; i < ntok; i += kWideThreads) {
+        const int rr = (int)geo.bdiv.div((uint32_t)i), c = i - rr * b;
+        const int tok = (int)tile_nodes[rr] * b + c;
+        if (tok >= anchor) sel[tok_base + (int64_t)(running + rr) * b + c] = tok;
+      }
+      __syncthreads();
+      running += tile_total;
+    }
+  }
+}
+
 // --------------------------------------------------------------------------- compaction
 // The members' kept-flag rows are ORed into a member mask per frontier entry; entries with
 // a non-empty mask, in ascending order, form the level's union list. The frontier is cut
@@ -690,15 +1196,19 @@ __global__ __launch_bounds__(kCompactThreads) void compact_kernel(
 
 hipError_t launch_score(const Geom& geo, const float* X, int64_t X_unit_stride, const void* Q,
                         int dtype, const LevelBufs* parent, int n_top, float* S,
-                        int64_t S_stride, hipStream_t s) {
+                        int64_t S_stride, const WideSel* wide, hipStream_t s) {
   const int cap_entries = parent ? (int)(geo.b * parent->stride) : n_top;
   dim3 grid((cap_entries + kScoreEntries - 1) / kScoreEntries, geo.U);
   const float sigma = 1.0f / sqrtf((float)geo.D);
   LevelBufs par = parent ? *parent : LevelBufs{};
   const int hp = parent ? 1 : 0;
+  float* pmax = wide ? wide->pmax : nullptr;
+  float* pmin = wide ? wide->pmin : nullptr;
+  const int64_t pstride = wide ? wide->pstride : 0;
 #define ZHA_SCORE(DD, TQ)                                                                     \
   hipLaunchKernelGGL((score_kernel<DD, TQ>), grid, dim3(kScoreThreads), 0, s, geo, X,          \
-                     X_unit_stride, (const TQ*)Q, par, hp, n_top, S, S_stride, sigma)
+                     X_unit_stride, (const TQ*)Q, par, hp, n_top, S, S_stride, sigma, pmax,    \
+                     pmin, pstride)
   if (geo.D == 64) {
     if (dtype == ZHA_BF16) ZHA_SCORE(64, bf16_t);
     else ZHA_SCORE(64, float);
@@ -710,12 +1220,36 @@ hipError_t launch_score(const Geom& geo, const float* X, int64_t X_unit_stride, 
   return hipGetLastError();
 }
 
+bool select_is_wide(int64_t cap_entries) { return cap_entries >= kWideMin; }
+int64_t wide_partial_stride(int64_t cap_entries) {
+  return (cap_entries + kScoreEntries - 1) / kScoreEntries;
+}
+int64_t wide_chunks(int64_t cap_entries) { return (cap_entries + kWideChunk - 1) / kWideChunk; }
+int wide_buckets() { return kWB; }
+
 hipError_t launch_select(const Geom& geo, int level, const float* S, int64_t S_stride,
                          const LevelBufs* parent, int n_top, KeepBits kb, float p, int anchor,
                          int32_t* sel_idx, int64_t cap, int32_t* sel_count, int32_t* lvl_kept,
-                         hipStream_t s) {
+                         const WideSel* wide, hipStream_t s) {
   LevelBufs par = parent ? *parent : LevelBufs{};
   const int QH = geo.B * geo.T * geo.Hq;
+  if (wide) {
+    const int hp = parent ? 1 : 0;
+    const int64_t cap_entries = parent ? geo.b * parent->stride : n_top;
+    const dim3 grid((unsigned)wide_chunks(cap_entries), QH);
+    hipLaunchKernelGGL(wide_hist_kernel, grid, dim3(kWideThreads), 0, s, geo, S, S_stride, par,
+                       hp, n_top, *wide);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(wide_cut_kernel, dim3(QH), dim3(kCutThreads), 0, s, geo, level, S,
+                       S_stride, par, hp, n_top, p, anchor, sel_idx, cap, sel_count, lvl_kept,
+                       *wide);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(wide_emit_kernel, grid, dim3(kWideThreads), 0, s, geo, level, S, S_stride,
+                       par, hp, n_top, kb, anchor, sel_idx, cap, *wide);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(select_kernel, dim3(QH), dim3(kSelThreads), 0, s, geo, level, S, S_stride,
                      par, parent ? 1 : 0, n_top, kb, p, anchor, sel_idx, cap, sel_count,
                      lvl_kept);
