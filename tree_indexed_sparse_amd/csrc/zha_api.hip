@@ -103,7 +103,8 @@ struct WsLayout {
   int U, QH, splits;
   int64_t n[ZHA_MAX_LEVELS + 1];  // nodes per unit at each level (current N)
   int64_t off_count, off_lvl, off_S, off_bits, off_part, off_chunks;
-  int64_t off_pmax, off_pmin, off_hm, off_hc, off_choff, off_cut, pstride, nch;
+  int64_t off_pmax, off_pmin, off_hm, off_hc, off_cut, off_umask, off_ucnt, off_mcnt;
+  int64_t pstride, nch, ustride, nuc;
   int64_t off_nodes[ZHA_MAX_LEVELS + 1], off_masks[ZHA_MAX_LEVELS + 1];
   int64_t S_stride, bit_words;
   int64_t total;
@@ -178,10 +179,16 @@ WsLayout layout_of(const Geom& g) {
   off = align256(off + 8 * (int64_t)w.QH * w.nch * wide_buckets());
   w.off_hc = off;
   off = align256(off + 4 * (int64_t)w.QH * w.nch * wide_buckets());
-  w.off_choff = off;
-  off = align256(off + 4 * (int64_t)w.QH * w.nch);
   w.off_cut = off;
   off = align256(off + 16 * (int64_t)w.QH);
+  w.ustride = wide_union_stride(w.n[1]);
+  w.nuc = wide_union_chunks(w.n[1]);
+  w.off_umask = off;
+  off = align256(off + 4 * (int64_t)g.U * w.ustride);
+  w.off_ucnt = off;
+  off = align256(off + 4 * (int64_t)g.U * w.nuc);
+  w.off_mcnt = off;
+  off = align256(off + 4 * (int64_t)w.QH * w.nuc);
   w.total = off;
   return w;
 }
@@ -370,9 +377,13 @@ int zha_attend(const zha_tree* t, const void* Q, int T, int Hq, const void* K, c
   wsel.pstride = w.pstride;
   wsel.hm = (unsigned long long*)(ws + w.off_hm);
   wsel.hc = (uint32_t*)(ws + w.off_hc);
-  wsel.choff = (uint32_t*)(ws + w.off_choff);
-  wsel.cut = (uint32_t*)(ws + w.off_cut);
   wsel.nch = w.nch;
+  wsel.cut = (uint32_t*)(ws + w.off_cut);
+  wsel.umask = (uint32_t*)(ws + w.off_umask);
+  wsel.ustride = w.ustride;
+  wsel.ucnt = (uint32_t*)(ws + w.off_ucnt);
+  wsel.mcnt = (uint32_t*)(ws + w.off_mcnt);
+  wsel.nuc = w.nuc;
 
   hipError_t e = hipSuccess;
   int64_t cap_l = t->N_cap;
@@ -394,6 +405,9 @@ int zha_attend(const zha_tree* t, const void* Q, int T, int Hq, const void* K, c
     });
     if (e != hipSuccess) return hip_fail(e, "select launch");
     e = timed(ZHA_K_COMPACT, l, s, [&] {
+      if (wide)
+        return launch_union(g, l, S, w.S_stride, parent, n_top, lv[l], anchor,
+                            l == 1 ? sel_idx : nullptr, cap, *wide, s);
       return launch_compact(g, parent, n_top, kb, lv[l], (uint32_t*)(ws + w.off_chunks), s);
     });
     if (e != hipSuccess) return hip_fail(e, "compact launch");

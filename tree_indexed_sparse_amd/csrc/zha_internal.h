@@ -90,17 +90,21 @@ struct KeepBits {
   int64_t words;
 };
 
-// Scratch of the chunked selection that large frontiers take (one workgroup per
-// (frontier chunk, query head) instead of one per query head).
+// Scratch of the chunked selection and compaction that large frontiers take (workgroups
+// over frontier chunks instead of one per query head or unit).
 struct WideSel {
   float* pmax;                // [QH][pstride] member max score per score workgroup
   float* pmin;                // [QH][pstride] member min score per score workgroup
   int64_t pstride;
   unsigned long long* hm;     // [QH][nch][buckets] fixed-point mass per chunk and bucket
   uint32_t* hc;               // [QH][nch][buckets] entry count per chunk and bucket
-  uint32_t* choff;            // [QH][nch] kept entries before each chunk
-  uint32_t* cut;              // [QH][4] cut score bits, cut index, token base, kept total
   int64_t nch;
+  uint32_t* cut;              // [QH][4] cut score bits, cut index, token base, kept total
+  uint32_t* umask;            // [U][ustride] member mask per frontier entry (uncompacted)
+  int64_t ustride;
+  uint32_t* ucnt;             // [U][nuc] union entries per compaction chunk
+  uint32_t* mcnt;             // [QH][nuc] member's kept entries per compaction chunk
+  int64_t nuc;
 };
 
 // ---------------------------------------------------------------------------------------
@@ -133,7 +137,9 @@ hipError_t launch_score(const Geom& geo, const float* X, int64_t X_unit_stride, 
 // sizes of its scratch for frontiers up to `cap_entries`.
 bool select_is_wide(int64_t cap_entries);
 int64_t wide_partial_stride(int64_t cap_entries);
-int64_t wide_chunks(int64_t cap_entries);
+int64_t wide_chunks(int64_t cap_entries);      // histogram chunks
+int64_t wide_union_chunks(int64_t cap_entries);  // compaction chunks
+int64_t wide_union_stride(int64_t cap_entries);  // umask row length
 int wide_buckets();
 
 // Per-member top-p: kept flags into `kb`; at level 1 also the token lists and counts.
@@ -146,6 +152,12 @@ hipError_t launch_select(const Geom& geo, int level, const float* S, int64_t S_s
 // chunk_cnt: scratch of compact_counter_words(U, frontier capacity) words.
 hipError_t launch_compact(const Geom& geo, const LevelBufs* parent, int n_top, KeepBits kb,
                           const LevelBufs& cur, uint32_t* chunk_cnt, hipStream_t s);
+
+// Compaction after the chunked selection: the members' keep flags straight from their
+// scores and cuts, the union list, and at level 1 the token lists.
+hipError_t launch_union(const Geom& geo, int level, const float* S, int64_t S_stride,
+                        const LevelBufs* parent, int n_top, const LevelBufs& cur, int anchor,
+                        int32_t* sel_idx, int64_t cap, const WideSel& wide, hipStream_t s);
 int64_t compact_counter_words(int U, int64_t n);
 
 hipError_t launch_decode(const Geom& geo, int dtype, const void* K, const void* V,

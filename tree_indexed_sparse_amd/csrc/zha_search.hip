@@ -629,28 +629,35 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
 }
 
 // ------------------------------------------------------------------ chunked selection
-// A large frontier is cut into chunks of kWideChunk entries and each query head's top-p
-// runs in three launches, so that (chunks x query heads) workgroups share the work:
-//   hist: per (chunk, head), the head's max/min (from the score partials) fixes the bucket
-//         grid; the chunk's fixed-point masses and counts go to a per-chunk histogram;
-//   cut:  per head, the chunk histograms are summed, the bucket where the cumulative mass
-//         reaches p is found, its entries are gathered from the score row and sorted (or
-//         radix-selected) to the exact cut, and kept counts per chunk are prefixed;
-//   emit: per (chunk, head), kept-flag words and, at level 1, the token list at the
-//         chunk's offset.
-// The buckets, masses and cut are those of the single-workgroup selection, so both paths
+// A large frontier runs its top-p and compaction in four launches whose workgroups each
+// take one chunk of the frontier:
+//   hist:  per (chunk, head): the head's max/min (from the score kernel's partials) fix
+//          the bucket grid; the chunk's fixed-point masses and counts per bucket are
+//          written as that chunk's histogram;
+//   cut:   per head: the chunk histograms are summed, the bucket where the cumulative
+//          mass reaches p is found, its entries are gathered from the score row and
+//          sorted (or radix-selected) to the exact cut (score, index), and the kept
+//          total is counted;
+//   union: per (chunk, unit): every member's keep flags from its scores and cut, ORed
+//          into per-entry member masks; kept counts per chunk, for the union and for
+//          each member;
+//   write: per (chunk, unit): the union list (ascending node ids and masks) at the
+//          chunk's offset and, at level 1, each member's token list.
+// Buckets, masses and cut are those of the single-workgroup selection, so both paths
 // keep the same set.
 
 constexpr int kWideThreads = 512;
-constexpr int kWideChunk = 8192;                    // entries per chunk: 4 tiles of kTileE
+constexpr int kWideChunk = 8192;                    // histogram chunk: 4 tiles of kTileE
 constexpr int kWideTiles = kWideChunk / kTileE;
 constexpr int kWB = 1024;                           // buckets of the chunked histogram
 constexpr int kCutThreads = 1024;                   // one bucket per thread
 constexpr int kCutWaves = kCutThreads / 64;
-constexpr int kMaxWideChunks = (1 << kMaxLog2Nodes) / kWideChunk;
+constexpr int kUnionThreads = 256;
+constexpr int kUnionChunk = 2048;                   // union/write chunk: 8 entries per thread
 constexpr int64_t kWideMin = 16384;                 // frontiers of this size or more
 static_assert(kWB == kCutThreads, "the cut kernel gives each thread one bucket");
-static_assert(kWideChunk % kTileE == 0 && kTileE % 32 == 0, "chunks hold whole tiles and words");
+static_assert(kWideChunk % kTileE == 0, "histogram chunks hold whole tiles");
+static_assert(kUnionChunk == 8 * kUnionThreads, "union threads take two float4 per row");
 
 // Four consecutive entries k0..k0+3 of member m's score row, below `end`.
 __device__ __forceinline__ Quad load_quad(const float* Sq, const uint32_t* pmask, int m,
@@ -757,7 +764,6 @@ struct CutShared {
   unsigned long long cand[kCand];
   unsigned long long radix[256];
   unsigned long long wsum[kCutWaves];
-  uint32_t chunk_keep[kMaxWideChunks];
   float red[2 * kCutWaves];
   unsigned long long scalar_u64[4];
   uint32_t scalar_u32[4];
@@ -788,7 +794,7 @@ __global__ __launch_bounds__(kCutThreads) void wide_cut_kernel(
     int32_t* __restrict__ sel_count, int32_t* __restrict__ lvl_kept, WideSel w) {
   __shared__ CutShared sh;
   const int qh = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x;
   int u, m;
   unit_member_of(geo, qh, &u, &m);
   const int b = geo.b;
@@ -797,12 +803,37 @@ __global__ __launch_bounds__(kCutThreads) void wide_cut_kernel(
   const float* Sq = S + (int64_t)qh * S_stride;
   const uint32_t* pmask = has_parent ? parent.masks + u * parent.stride : nullptr;
   const uint32_t* pnodes = has_parent ? parent.nodes + u * parent.stride : nullptr;
-  for (int i = tid; i < nch; i += kCutThreads) sh.chunk_keep[i] = 0u;
+
+  // bucket totals over the chunks (thread `tid` owns bucket `tid`); loads issued first
+  uint64_t hsum = 0;
+  uint32_t csum = 0;
+  const int64_t hbase = (int64_t)qh * w.nch * kWB + tid;
+  {
+    int c = 0;
+    for (; c + 4 <= nch; c += 4) {
+      uint64_t h[4];
+      uint32_t n[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        h[j] = w.hm[hbase + (int64_t)(c + j) * kWB];
+        n[j] = w.hc[hbase + (int64_t)(c + j) * kWB];
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        hsum += h[j];
+        csum += n[j];
+      }
+    }
+    for (; c < nch; ++c) {
+      hsum += w.hm[hbase + (int64_t)c * kWB];
+      csum += w.hc[hbase + (int64_t)c * kWB];
+    }
+  }
   if (tid == 0) {
     sh.scalar_u32[0] = 0u;  // boundary bucket
     sh.scalar_u32[1] = 0u;  // its entry count
     sh.scalar_u32[2] = 0u;  // gathered candidates
-    sh.scalar_u32[3] = 0u;  // last kept candidate (sorted position)
+    sh.scalar_u32[3] = 0u;  // kept candidates of the boundary bucket
     sh.scalar_u64[0] = 0ull;
     sh.scalar_u64[2] = ~0ull;
   }
@@ -812,14 +843,6 @@ __global__ __launch_bounds__(kCutThreads) void wide_cut_kernel(
   const float scale = spread > 0.f ? (float)kWB / spread : 0.f;
   const bool keep_all = !(p < 1.0f);
 
-  // bucket totals over the chunks: thread `tid` owns bucket `tid`
-  uint64_t hsum = 0;
-  uint32_t csum = 0;
-  const int64_t hbase = (int64_t)qh * w.nch * kWB;
-  for (int c = 0; c < nch; ++c) {
-    hsum += w.hm[hbase + (int64_t)c * kWB + tid];
-    csum += w.hc[hbase + (int64_t)c * kWB + tid];
-  }
   uint64_t Z;
   const uint64_t incl = cut_block_scan(hsum, sh.wsum, &Z);
   const uint64_t T = keep_all ? Z : ceil_mul_p(p, Z);
@@ -833,15 +856,6 @@ __global__ __launch_bounds__(kCutThreads) void wide_cut_kernel(
   const int bstar = keep_all ? kWB : (int)sh.scalar_u32[0];
   const uint64_t before = sh.scalar_u64[0];
   const uint32_t nb = keep_all ? 0u : sh.scalar_u32[1];
-
-  // kept entries per chunk in the buckets above the boundary: one wave per chunk
-  for (int c = wave; c < nch; c += kCutWaves) {
-    uint32_t acc = 0;
-    for (int j = lane; j < bstar; j += 64) acc += w.hc[hbase + (int64_t)c * kWB + j];
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
-    if (lane == 0) sh.chunk_keep[c] = acc;
-  }
 
   uint64_t key = ~0ull;  // keep_all: every member entry ranks at or above the cut
   if (!keep_all) {
@@ -903,18 +917,13 @@ __global__ __launch_bounds__(kCutThreads) void wide_cut_kernel(
           run += mloc[i];
           if (run >= T) {
             sh.scalar_u64[2] = sh.cand[per * tid + i];
-            sh.scalar_u32[3] = (uint32_t)(per * tid + i);
+            sh.scalar_u32[3] = (uint32_t)(per * tid + i + 1);
             break;
           }
         }
       }
       __syncthreads();
       key = sh.scalar_u64[2];
-      const int last = (int)sh.scalar_u32[3];
-      for (int i = tid; i <= last; i += kCutThreads) {
-        const uint32_t k = 0xffffffffu - (uint32_t)sh.cand[i];
-        atomicAdd(&sh.chunk_keep[k / kWideChunk], 1u);
-      }
     } else {
       // boundary bucket too large to sort: exact MSD radix select on the rank key,
       // restricted to the boundary bucket, 8 bits per pass
@@ -953,65 +962,38 @@ __global__ __launch_bounds__(kCutThreads) void wide_cut_kernel(
         __syncthreads();
       }
       key = prefix;
+      uint32_t nk = 0;
       for (int k0 = kVec * tid; k0 < F; k0 += kVec * kCutThreads) {
         const Quad q = load_quad(Sq, pmask, m, geo.bdiv, k0, F);
 #pragma unroll
-        for (int i = 0; i < kVec; ++i) {
-          if (q.in[i] && bucket_of<kWB>(q.s[i], mx, scale, spread) == bstar &&
-              rank_key(q.s[i], (uint32_t)(k0 + i)) >= key)
-            atomicAdd(&sh.chunk_keep[(k0 + i) / kWideChunk], 1u);
-        }
+        for (int i = 0; i < kVec; ++i)
+          nk += (q.in[i] && bucket_of<kWB>(q.s[i], mx, scale, spread) == bstar &&
+                 rank_key(q.s[i], (uint32_t)(k0 + i)) >= key);
       }
+      if (nk) atomicAdd(&sh.scalar_u32[3], nk);
     }
   }
   const float s_cut = keep_all ? -INFINITY : float_of_ord((uint32_t)(key >> 32));
   const uint32_t k_cut = keep_all ? 0xffffffffu : 0xffffffffu - (uint32_t)key;
+  // kept total: the buckets above the boundary plus the boundary's kept entries
+  uint64_t kept64;
+  cut_block_scan(tid < bstar ? (uint64_t)csum : 0ull, sh.wsum, &kept64);
   __syncthreads();
-
-  // chunk offsets: exclusive prefix of the kept counts (wave 0, four chunks per lane)
-  if (wave == 0) {
-    constexpr int per = kMaxWideChunks / 64;
-    uint32_t c4[per];
-    uint32_t loc = 0;
-#pragma unroll
-    for (int i = 0; i < per; ++i) {
-      const int c = per * lane + i;
-      c4[i] = c < nch ? sh.chunk_keep[c] : 0u;
-      loc += c4[i];
-    }
-    uint32_t inc = loc;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const uint32_t o = __shfl_up(inc, d, 64);
-      if (lane >= d) inc += o;
-    }
-    uint32_t run = inc - loc;
-#pragma unroll
-    for (int i = 0; i < per; ++i) {
-      const int c = per * lane + i;
-      if (c < nch) w.choff[(int64_t)qh * w.nch + c] = run;
-      run += c4[i];
-    }
-    if (lane == 63) sh.scalar_u32[2] = inc;  // kept total
-  }
-  // anchor overlap at level 1: kept tokens below `anchor` (first ceil(anchor / b) entries)
-  if (level == 1 && tid == 64) {
+  const uint32_t kept = (uint32_t)kept64 + sh.scalar_u32[3];
+  if (tid == 0) {
+    // anchor overlap at level 1: kept tokens below `anchor` (first ceil(anchor / b) entries)
     int dup = 0;
-    const int lim = min(F, (anchor + b - 1) / b);
-    for (int k = 0; k < lim; ++k) {
-      const bool in = !pmask || ((pmask[geo.bdiv.div((uint32_t)k)] >> m) & 1u);
-      const float sk = Sq[k];
-      if (in && (sk > s_cut || (sk == s_cut && (uint32_t)k <= k_cut))) {
-        const int node = (int)frontier_node(pnodes, k, geo.bdiv);
-        if (node * b < anchor) dup += min(b, anchor - node * b);
+    if (level == 1) {
+      const int lim = min(F, (anchor + b - 1) / b);
+      for (int k = 0; k < lim; ++k) {
+        const bool in = !pmask || ((pmask[geo.bdiv.div((uint32_t)k)] >> m) & 1u);
+        const float sk = Sq[k];
+        if (in && (sk > s_cut || (sk == s_cut && (uint32_t)k <= k_cut))) {
+          const int node = (int)frontier_node(pnodes, k, geo.bdiv);
+          if (node * b < anchor) dup += min(b, anchor - node * b);
+        }
       }
     }
-    sh.scalar_u32[3] = (uint32_t)dup;
-  }
-  __syncthreads();
-  const uint32_t kept = sh.scalar_u32[2];
-  const int dup = level == 1 ? (int)sh.scalar_u32[3] : 0;
-  if (tid == 0) {
     uint32_t* rec = w.cut + 4 * (int64_t)qh;
     rec[0] = __float_as_uint(s_cut);
     rec[1] = k_cut;
@@ -1024,70 +1006,161 @@ __global__ __launch_bounds__(kCutThreads) void wide_cut_kernel(
     for (int i = tid; i < anchor; i += kCutThreads) sel_idx[(int64_t)qh * cap + i] = i;
 }
 
-__global__ __launch_bounds__(kWideThreads) void wide_emit_kernel(
-    Geom geo, int level, const float* __restrict__ S, int64_t S_stride, LevelBufs parent,
-    int has_parent, int n_top, KeepBits kb, int anchor, int32_t* __restrict__ sel_idx,
-    int64_t cap, WideSel w) {
-  __shared__ uint32_t tile_nodes[kTileE];
-  __shared__ uint32_t wave_sum[kWideThreads / 64];
-  const int qh = blockIdx.y, chunk = blockIdx.x;
-  int u, m;
-  unit_member_of(geo, qh, &u, &m);
+// union: per (chunk of kUnionChunk entries, unit). Thread t takes entries 4t..4t+3 and
+// 1024+4t..1024+4t+3 of the chunk, so each member's row is read as two coalesced float4.
+__global__ __launch_bounds__(kUnionThreads) void wide_union_kernel(
+    Geom geo, const float* __restrict__ S, int64_t S_stride, LevelBufs parent, int has_parent,
+    int n_top, WideSel w) {
+  __shared__ float s_cut[kMaxMembers];
+  __shared__ uint32_t k_cut[kMaxMembers];
+  __shared__ uint32_t cnt[kUnionThreads / 64][kMaxMembers + 1];
+  const int u = blockIdx.y, chunk = blockIdx.x;
   const int b = geo.b;
   const int F = has_parent ? b * (int)parent.count[u] : n_top;
-  const int c0 = chunk * kWideChunk;
+  const int c0 = chunk * kUnionChunk;
   if (c0 >= F) return;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const float* Sq = S + (int64_t)qh * S_stride;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int Mu = members_of(geo, u);
+  if (tid < Mu) {
+    const uint32_t* rec = w.cut + 4 * (int64_t)qh_of(geo, u, tid);
+    s_cut[tid] = __uint_as_float(rec[0]);
+    k_cut[tid] = rec[1];
+  }
+  int kk[8];
+  uint32_t pm[8];
   const uint32_t* pmask = has_parent ? parent.masks + u * parent.stride : nullptr;
-  const uint32_t* pnodes = has_parent ? parent.nodes + u * parent.stride : nullptr;
-  const int end = min(F, c0 + kWideChunk);
-  Quad q[kWideTiles];
+  const uint32_t all = (1u << Mu) - 1u;  // Mu <= 16
 #pragma unroll
-  for (int j = 0; j < kWideTiles; ++j)
-    q[j] = load_quad(Sq, pmask, m, geo.bdiv, c0 + j * kTileE + kVec * tid, end);
-  const uint32_t* rec = w.cut + 4 * (int64_t)qh;
-  const float s_cut = __uint_as_float(rec[0]);
-  const uint32_t k_cut = rec[1];
-  const int tok_base = (int)rec[2];
-  uint32_t running = w.choff[(int64_t)qh * w.nch + chunk];
-  uint32_t* kbits = kb.bits + (int64_t)qh * kb.words;
-  int32_t* sel = (level == 1 && sel_idx) ? sel_idx + (int64_t)qh * cap : nullptr;
+  for (int i = 0; i < 8; ++i) {
+    kk[i] = c0 + (i >> 2) * (kUnionChunk / 2) + 4 * tid + (i & 3);
+    pm[i] = kk[i] < F ? (pmask ? pmask[geo.bdiv.div((uint32_t)kk[i])] : all) : 0u;
+  }
+  __syncthreads();
+  uint32_t um[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int mm = 0; mm < Mu; ++mm) {
+    const float* Sq = S + (int64_t)qh_of(geo, u, mm) * S_stride + c0 + 4 * tid;
+    // rows are padded to a multiple of 4 and chunks start at multiples of 4, so a float4
+    // that starts below F stays inside the row
+    const float4 a = kk[0] < F ? *reinterpret_cast<const float4*>(Sq) : make_float4(0, 0, 0, 0);
+    const float4 c = kk[4] < F ? *reinterpret_cast<const float4*>(Sq + kUnionChunk / 2)
+                               : make_float4(0, 0, 0, 0);
+    const float sv[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+    const float sc = s_cut[mm];
+    const uint32_t kc = k_cut[mm];
+    uint32_t n = 0;
 #pragma unroll
-  for (int j = 0; j < kWideTiles; ++j) {
-    const int t0 = c0 + j * kTileE;
-    if (t0 >= end) break;
-    const int k0 = t0 + kVec * tid;
-    uint32_t bits = 0, cnt = 0;
-#pragma unroll
-    for (int i = 0; i < kVec; ++i) {
-      const float sv = q[j].s[i];
-      if (q[j].in[i] && (sv > s_cut || (sv == s_cut && (uint32_t)(k0 + i) <= k_cut))) {
-        bits |= 1u << i;
-        ++cnt;
-      }
+    for (int i = 0; i < 8; ++i) {
+      const bool keep = ((pm[i] >> mm) & 1u) &&
+                        (sv[i] > sc || (sv[i] == sc && (uint32_t)kk[i] <= kc));
+      um[i] |= (uint32_t)keep << mm;
+      n += keep;
     }
-    // eight lanes' nibbles make one 32-entry word
-    uint32_t word = bits << (4 * (lane & 7));
-    word |= __shfl_xor(word, 1, 64);
-    word |= __shfl_xor(word, 2, 64);
-    word |= __shfl_xor(word, 4, 64);
-    if ((lane & 7) == 0 && k0 < end) kbits[k0 / 32] = word;
-    if (sel) {
-      uint32_t tile_total;
-      uint32_t r = block_excl_scan<kWideThreads>(cnt, wave_sum, &tile_total);
 #pragma unroll
-      for (int i = 0; i < kVec; ++i)
-        if ((bits >> i) & 1u) tile_nodes[r++] = frontier_node(pnodes, k0 + i, geo.bdiv);
-      __syncthreads();
-      const int ntok = (int)tile_total * b;
-      for (int i = tid; i < ntok; i += kWideThreads) {
-        const int rr = (int)geo.bdiv.div((uint32_t)i), c = i - rr * b;
-        const int tok = (int)tile_nodes[rr] * b + c;
-        if (tok >= anchor) sel[tok_base + (int64_t)(running + rr) * b + c] = tok;
+    for (int off = 32; off >= 1; off >>= 1) n += __shfl_xor(n, off, 64);
+    if (lane == 0) cnt[wave][mm] = n;
+  }
+  uint32_t nz = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) nz += um[i] != 0u;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) nz += __shfl_xor(nz, off, 64);
+  if (lane == 0) cnt[wave][kMaxMembers] = nz;
+  uint32_t* umg = w.umask + (int64_t)u * w.ustride + c0 + 4 * tid;
+  *reinterpret_cast<uint4*>(umg) = make_uint4(um[0], um[1], um[2], um[3]);
+  *reinterpret_cast<uint4*>(umg + kUnionChunk / 2) = make_uint4(um[4], um[5], um[6], um[7]);
+  __syncthreads();
+  if (tid <= kMaxMembers && (tid < Mu || tid == kMaxMembers)) {
+    uint32_t tot = 0;
+#pragma unroll
+    for (int v = 0; v < kUnionThreads / 64; ++v) tot += cnt[v][tid];
+    if (tid == kMaxMembers) w.ucnt[(int64_t)u * w.nuc + chunk] = tot;
+    else w.mcnt[(int64_t)qh_of(geo, u, tid) * w.nuc + chunk] = tot;
+  }
+}
+
+// sum of cnt[0 .. n) across one wave (every lane gets it)
+__device__ __forceinline__ uint32_t wave_prefix_total(const uint32_t* cnt, int n, int lane) {
+  uint32_t acc = 0;
+  for (int c = lane; c < n; c += 64) acc += cnt[c];
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
+  return acc;
+}
+
+// write: per (chunk, unit). Each wave compacts a quarter of the chunk with ballots, and
+// then writes the token lists of members wave, wave + 4, ... (level 1 only).
+__global__ __launch_bounds__(kUnionThreads) void wide_write_kernel(
+    Geom geo, int level, LevelBufs parent, int has_parent, int n_top, LevelBufs cur,
+    int anchor, int32_t* __restrict__ sel_idx, int64_t cap, WideSel w) {
+  constexpr int NW = kUnionThreads / 64;
+  constexpr int kPerWave = kUnionChunk / NW;
+  __shared__ uint32_t s_um[kUnionChunk];
+  __shared__ uint32_t wtot[NW];
+  const int u = blockIdx.y, chunk = blockIdx.x;
+  const int b = geo.b;
+  const int F = has_parent ? b * (int)parent.count[u] : n_top;
+  const int c0 = chunk * kUnionChunk;
+  if (c0 >= F) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int Mu = members_of(geo, u);
+  const int nchunks = (F + kUnionChunk - 1) / kUnionChunk;
+  const uint32_t* pnodes = has_parent ? parent.nodes + u * parent.stride : nullptr;
+  const uint32_t* umg = w.umask + (int64_t)u * w.ustride + c0;
+  {
+    const uint4 a = *reinterpret_cast<const uint4*>(umg + 4 * tid);
+    const uint4 c = *reinterpret_cast<const uint4*>(umg + kUnionChunk / 2 + 4 * tid);
+    *reinterpret_cast<uint4*>(&s_um[4 * tid]) = a;
+    *reinterpret_cast<uint4*>(&s_um[kUnionChunk / 2 + 4 * tid]) = c;
+  }
+  const uint32_t before = wave_prefix_total(w.ucnt + (int64_t)u * w.nuc, chunk, lane);
+  __syncthreads();
+  // entries past F hold zero masks (the union kernel wrote them so)
+  const int e0 = wave * kPerWave;
+  uint32_t mine = 0;
+  for (int r = 0; r < kPerWave / 64; ++r)
+    mine += __popcll(__ballot(s_um[e0 + 64 * r + lane] != 0u));
+  if (lane == 0) wtot[wave] = mine;
+  __syncthreads();
+  uint32_t pos = before;
+  for (int v = 0; v < wave; ++v) pos += wtot[v];
+  uint32_t* onodes = cur.nodes + u * cur.stride;
+  uint32_t* omasks = cur.masks + u * cur.stride;
+  for (int r = 0; r < kPerWave / 64; ++r) {
+    const int e = e0 + 64 * r + lane;
+    const uint32_t msk = s_um[e];
+    const uint64_t bal = __ballot(msk != 0u);
+    if (msk) {
+      const uint32_t at = pos + (uint32_t)__popcll(bal & ((1ull << lane) - 1ull));
+      onodes[at] = frontier_node(pnodes, c0 + e, geo.bdiv);
+      omasks[at] = msk;
+    }
+    pos += (uint32_t)__popcll(bal);
+  }
+  if (chunk == nchunks - 1 && tid == kUnionThreads - 1) {
+    uint32_t tot = before;
+    for (int v = 0; v < NW; ++v) tot += wtot[v];
+    cur.count[u] = tot;
+  }
+  if (level != 1 || !sel_idx) return;
+  for (int mm = wave; mm < Mu; mm += NW) {
+    const int qh = qh_of(geo, u, mm);
+    const uint32_t* rec = w.cut + 4 * (int64_t)qh;
+    const int tok_base = (int)rec[2];
+    int32_t* sel = sel_idx + (int64_t)qh * cap;
+    uint32_t mpos = wave_prefix_total(w.mcnt + (int64_t)qh * w.nuc, chunk, lane);
+    for (int r = 0; r < kUnionChunk / 64; ++r) {
+      const int e = 64 * r + lane;
+      const bool kept = (s_um[e] >> mm) & 1u;
+      const uint64_t bal = __ballot(kept);
+      if (kept) {
+        const uint32_t at = mpos + (uint32_t)__popcll(bal & ((1ull << lane) - 1ull));
+        const int node = (int)frontier_node(pnodes, c0 + e, geo.bdiv);
+        for (int c = 0; c < b; ++c) {
+          const int tok = node * b + c;
+          if (tok >= anchor) sel[tok_base + (int64_t)at * b + c] = tok;
+        }
       }
-      __syncthreads();
-      running += tile_total;
+      mpos += (uint32_t)__popcll(bal);
     }
   }
 }
@@ -1225,6 +1298,12 @@ int64_t wide_partial_stride(int64_t cap_entries) {
   return (cap_entries + kScoreEntries - 1) / kScoreEntries;
 }
 int64_t wide_chunks(int64_t cap_entries) { return (cap_entries + kWideChunk - 1) / kWideChunk; }
+int64_t wide_union_chunks(int64_t cap_entries) {
+  return (cap_entries + kUnionChunk - 1) / kUnionChunk;
+}
+int64_t wide_union_stride(int64_t cap_entries) {
+  return wide_union_chunks(cap_entries) * kUnionChunk;
+}
 int wide_buckets() { return kWB; }
 
 hipError_t launch_select(const Geom& geo, int level, const float* S, int64_t S_stride,
@@ -1236,7 +1315,7 @@ hipError_t launch_select(const Geom& geo, int level, const float* S, int64_t S_s
   if (wide) {
     const int hp = parent ? 1 : 0;
     const int64_t cap_entries = parent ? geo.b * parent->stride : n_top;
-    const dim3 grid((unsigned)wide_chunks(cap_entries), QH);
+    const dim3 grid((unsigned)((cap_entries + kWideChunk - 1) / kWideChunk), QH);
     hipLaunchKernelGGL(wide_hist_kernel, grid, dim3(kWideThreads), 0, s, geo, S, S_stride, par,
                        hp, n_top, *wide);
     hipError_t e = hipGetLastError();
@@ -1244,10 +1323,6 @@ hipError_t launch_select(const Geom& geo, int level, const float* S, int64_t S_s
     hipLaunchKernelGGL(wide_cut_kernel, dim3(QH), dim3(kCutThreads), 0, s, geo, level, S,
                        S_stride, par, hp, n_top, p, anchor, sel_idx, cap, sel_count, lvl_kept,
                        *wide);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(wide_emit_kernel, grid, dim3(kWideThreads), 0, s, geo, level, S, S_stride,
-                       par, hp, n_top, kb, anchor, sel_idx, cap, *wide);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(select_kernel, dim3(QH), dim3(kSelThreads), 0, s, geo, level, S, S_stride,
@@ -1273,6 +1348,22 @@ hipError_t launch_compact(const Geom& geo, const LevelBufs* parent, int n_top, K
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(compact_kernel, dim3(max_chunks, geo.U), dim3(kCompactThreads), 0, s, geo,
                      par, hp, n_top, kb, cur, 2, chunk_cnt, max_chunks);
+  return hipGetLastError();
+}
+
+hipError_t launch_union(const Geom& geo, int level, const float* S, int64_t S_stride,
+                        const LevelBufs* parent, int n_top, const LevelBufs& cur, int anchor,
+                        int32_t* sel_idx, int64_t cap, const WideSel& wide, hipStream_t s) {
+  LevelBufs par = parent ? *parent : LevelBufs{};
+  const int hp = parent ? 1 : 0;
+  const int64_t cap_entries = parent ? geo.b * parent->stride : n_top;
+  const dim3 grid((unsigned)wide_union_chunks(cap_entries), geo.U);
+  hipLaunchKernelGGL(wide_union_kernel, grid, dim3(kUnionThreads), 0, s, geo, S, S_stride, par,
+                     hp, n_top, wide);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(wide_write_kernel, grid, dim3(kUnionThreads), 0, s, geo, level, par, hp,
+                     n_top, cur, anchor, sel_idx, cap, wide);
   return hipGetLastError();
 }
 
