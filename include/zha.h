@@ -23,6 +23,9 @@
  *     zha_status is returned and zha_last_error() describes the problem.
  *   - Shapes are row-major. A KV cache is [B][Hkv][N_cap][d]: N_cap is its allocated
  *     length, and tokens [0, N) are in use.
+ *   - K, V, Q, the reference queries, O and the pyramid must be 16-byte aligned and a
+ *     workspace 256-byte aligned (hipMalloc returns 256-byte aligned memory); other
+ *     pointers are rejected with ZHA_ERR_INVALID_ARG.
  *   - Supported: d in {64, 128}; dtype ZHA_F32 or ZHA_BF16 (K, V, Q and the reference
  *     queries share one dtype); b >= 2; 1 <= L <= ZHA_MAX_LEVELS; N % b^L == 0;
  *     Hq % Hkv == 0 and Hq / Hkv <= 16; N / b <= 2^21.
@@ -39,7 +42,8 @@ extern "C" {
 
 typedef enum {
   ZHA_OK = 0,
-  ZHA_ERR_INVALID_ARG = -1, /* null pointer, p not in (0, 1], anchor out of range, b < 2, L < 1 */
+  ZHA_ERR_INVALID_ARG = -1, /* null or misaligned pointer, p not in (0, 1], anchor out of
+                               range, b < 2, L < 1 */
   ZHA_ERR_SHAPE = -2,       /* N % b^L != 0, Hq % Hkv != 0, N > N_cap, buffer too small */
   ZHA_ERR_DTYPE = -3,       /* unknown dtype */
   ZHA_ERR_CAPACITY = -4,    /* selected-list capacity smaller than N */

@@ -13,6 +13,8 @@ from tree_indexed_sparse_amd import _lib as L
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "zha.h")
 FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation
+ODD8 = ctypes.c_void_p(0x1008)  # 8- but not 16-byte aligned
+ODD16 = ctypes.c_void_p(0x1010)  # 16- but not 256-byte aligned
 
 
 @pytest.fixture(scope="module")
@@ -60,6 +62,7 @@ def _build(lib, **kw):
     (dict(dtype=7), -3), (dict(d=96), -5), (dict(b=1), -1), (dict(L=0), -1), (dict(L=13), -5),
     (dict(N=4000), -2), (dict(N_cap=4000, N=0), -2), (dict(N=8192), -2), (dict(nbytes=1024), -2),
     (dict(B=0), -2), (dict(N_cap=4 * 2 ** 22, N=64, b=4, L=3), -5),
+    (dict(K=ODD8), -1), (dict(R=ODD8), -1), (dict(pyr=ODD8), -1),
 ])
 def test_build_rejects_bad_arguments(lib, kw, code):
     assert _build(lib, **kw) == code
@@ -93,6 +96,8 @@ def _attend(lib, t=None, **kw):
     (dict(anchor=-1), -1), (dict(anchor=4097), -1),
     (dict(cap=4095), -4), (dict(Hq=7), -2), (dict(Hq=64), -5), (dict(T=0), -2),
     (dict(wsb=1024), -2),
+    (dict(Q=ODD8), -1), (dict(K=ODD8), -1), (dict(V=ODD8), -1), (dict(O=ODD8), -1),
+    (dict(ws=ODD16), -1),
 ])
 def test_attend_rejects_bad_arguments(lib, kw, code):
     assert _attend(lib, **kw) == code

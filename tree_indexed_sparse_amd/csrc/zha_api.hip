@@ -71,6 +71,8 @@ hipError_t timed(int kind, int level, hipStream_t s, F&& launch) {
 
 int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
 
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
 int64_t ipow(int64_t b, int e) {
   int64_t r = 1;
   for (int i = 0; i < e; ++i) r *= b;
@@ -233,6 +235,8 @@ int zha_tree_append(zha_tree* t, const void* K, const void* R, int n_new, void* 
   int st = check_tree(t);
   if (st != ZHA_OK) return st;
   if (!K || !R) return fail(ZHA_ERR_INVALID_ARG, "K and ref_queries must not be NULL");
+  if (!aligned16(K) || !aligned16(R))
+    return fail(ZHA_ERR_INVALID_ARG, "K and ref_queries must be 16-byte aligned");
   const int64_t top = ipow(t->b, t->L);
   if (n_new < 0 || n_new % top != 0)
     return fail(ZHA_ERR_SHAPE, "n_new=%d must be a non-negative multiple of b^L=%lld", n_new,
@@ -282,6 +286,8 @@ int zha_build_tree(const void* K, const void* R, int dtype, int B, int Hkv, int 
                    void* stream) {
   if (!K || !R || !pyramid || !out)
     return fail(ZHA_ERR_INVALID_ARG, "K, ref_queries, pyramid and out must not be NULL");
+  if (!aligned16(K) || !aligned16(R) || !aligned16(pyramid))
+    return fail(ZHA_ERR_INVALID_ARG, "K, ref_queries and pyramid must be 16-byte aligned");
   if (dtype != ZHA_F32 && dtype != ZHA_BF16) return fail(ZHA_ERR_DTYPE, "unknown dtype %d", dtype);
   int st = check_geometry(B, Hkv, N, N_cap, d, b, L);
   if (st != ZHA_OK) return st;
@@ -349,6 +355,10 @@ int zha_attend(const zha_tree* t, const void* Q, int T, int Hq, const void* K, c
   if (st != ZHA_OK) return st;
   if (!Q || !K || !V || !O || !sel_count || !workspace)
     return fail(ZHA_ERR_INVALID_ARG, "Q, K, V, O, sel_count and workspace must not be NULL");
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) ||
+      ((uintptr_t)workspace & 255u) != 0)
+    return fail(ZHA_ERR_INVALID_ARG,
+                "Q, K, V and O must be 16-byte aligned and the workspace 256-byte aligned");
   if (t->N < 1) return fail(ZHA_ERR_SHAPE, "the tree covers no tokens");
   if (!(p > 0.0f && p <= 1.0f)) return fail(ZHA_ERR_INVALID_ARG, "p=%g must lie in (0, 1]", (double)p);
   if (anchor < 0 || anchor > t->N)

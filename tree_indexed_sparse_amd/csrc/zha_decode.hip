@@ -11,7 +11,7 @@
 // masked. Tokens below `anchor` are skipped inside nodes and attended once, for every
 // member, by split 0. The union token range is cut into `splits` equal pieces; each
 // workgroup writes one (max, sum, weighted-V) partial per member, and a separate combine
-// launch merges a unit's partials in split order, so the result does not depend on the
+// launch merges a unit's partials in a fixed order, so the result does not depend on the
 // order in which workgroups run.
 
 #include "zha_internal.h"
@@ -52,44 +52,63 @@ __device__ void write_partial(int u, int sp, int splits, int Mu, const float* sm
   }
 }
 
-// One workgroup per (unit, member): merge the member's partials of every split, in split
-// order, into its output row. Runs after the decode launch, which orders it.
-constexpr int kCombThreads = 128;
+// One workgroup per (unit, member): merge the member's partials of every split into its
+// output row, in a fixed order (wave 0 forms the split weights; thread (split lane, column
+// pair) accumulates splits lane, lane + SL, ...; the split lanes are then added in order),
+// so the result does not depend on the order in which workgroups run. Runs after the
+// decode launch, which orders it.
+constexpr int kCombThreads = 256;
 
 template <int D>
 __global__ __launch_bounds__(kCombThreads) void combine_kernel(Geom geo, int splits,
                                                                const float* __restrict__ part,
                                                                float* __restrict__ O) {
-  __shared__ float sw[kMaxSplits], sl[kMaxSplits];
-  __shared__ float sM, sL;
+  constexpr int DP = D / 2;                // float2 columns per partial row
+  constexpr int SL = kCombThreads / DP;    // split lanes
+  __shared__ float sw[kMaxSplits];
+  __shared__ float2 sacc[SL][DP];
   const int u = blockIdx.x, m = blockIdx.y;
   if (m >= members_of(geo, u)) return;
-  const int64_t pstride = (int64_t)(D + 2);
-  const int64_t sstride = kMaxMembers * pstride;  // between splits
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int64_t pstride = (int64_t)(D + 2);  // rows are 8-byte aligned: float2 loads
+  const int64_t sstride = kMaxMembers * pstride;
   const float* pm = part + ((int64_t)u * splits * kMaxMembers + m) * pstride;
-  for (int s2 = threadIdx.x; s2 < splits; s2 += kCombThreads) {
-    sw[s2] = pm[s2 * sstride + D];
-    sl[s2] = pm[s2 * sstride + D + 1];
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
+  if (tid < 64) {
     float M = -INFINITY;
-    for (int s2 = 0; s2 < splits; ++s2) M = fmaxf(M, sw[s2]);
+    for (int s2 = lane; s2 < splits; s2 += 64) M = fmaxf(M, pm[s2 * sstride + D]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
     float L = 0.f;
-    for (int s2 = 0; s2 < splits; ++s2)
-      if (sw[s2] != -INFINITY) L = fmaf(expf(sw[s2] - M), sl[s2], L);
-    sM = M;
-    sL = L;
+    for (int s2 = lane; s2 < splits; s2 += 64) {
+      const float w = pm[s2 * sstride + D];
+      if (w != -INFINITY) L = fmaf(expf(w - M), pm[s2 * sstride + D + 1], L);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) L += __shfl_xor(L, off, 64);
+    for (int s2 = lane; s2 < splits; s2 += 64) {
+      const float w = pm[s2 * sstride + D];
+      sw[s2] = (w == -INFINITY) ? 0.f : expf(w - M) / L;
+    }
   }
   __syncthreads();
-  for (int s2 = threadIdx.x; s2 < splits; s2 += kCombThreads)
-    sw[s2] = (sw[s2] == -INFINITY) ? 0.f : expf(sw[s2] - sM) / sL;
-  __syncthreads();
-  for (int k = threadIdx.x; k < D; k += kCombThreads) {
-    float acc = 0.f;
+  const int col = tid % DP, sl = tid / DP;
+  float ax = 0.f, ay = 0.f;
 #pragma unroll 8
-    for (int s2 = 0; s2 < splits; ++s2) acc = fmaf(sw[s2], pm[s2 * sstride + k], acc);
-    O[(int64_t)qh_of(geo, u, m) * D + k] = acc;
+  for (int s2 = sl; s2 < splits; s2 += SL) {
+    const float2 v = *reinterpret_cast<const float2*>(pm + s2 * sstride + 2 * col);
+    ax = fmaf(sw[s2], v.x, ax);
+    ay = fmaf(sw[s2], v.y, ay);
+  }
+  sacc[sl][col] = make_float2(ax, ay);
+  __syncthreads();
+  if (sl == 0) {
+    float2 r = sacc[0][col];
+#pragma unroll
+    for (int j = 1; j < SL; ++j) {
+      r.x += sacc[j][col].x;
+      r.y += sacc[j][col].y;
+    }
+    *reinterpret_cast<float2*>(O + (int64_t)qh_of(geo, u, m) * D + 2 * col) = r;
   }
 }
 
