@@ -44,10 +44,19 @@ def parse():
     return ap.parse_args()
 
 
-def kernel_sources_sha() -> str:
+# source files whose kernels a counter summary covers (a change to any of them voids it)
+KERNEL_FILES = {
+    "decode": ["zha_decode.hip", "zha_internal.h"],
+    "pool_l1": ["zha_build.hip", "zha_internal.h"],
+    "score_l1": ["zha_search.hip", "zha_internal.h"],
+}
+
+
+def kernel_sources_sha(kernel=None) -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "tree_indexed_sparse_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    files = KERNEL_FILES.get(kernel) or sorted(os.listdir(csrc))
+    for f in files:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode())
             h.update(fh.read())
@@ -289,7 +298,7 @@ def pmc_traffic(kernel, workload):
         return None
     with open(path) as fh:
         rec = json.load(fh)
-    if rec.get("kernel_sources") != kernel_sources_sha():
+    if rec.get("kernel_sources") != kernel_sources_sha(kernel):
         return None
     return rec.get("hbm_bytes_per_launch")
 

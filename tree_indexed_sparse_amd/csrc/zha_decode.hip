@@ -230,6 +230,15 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_ca
 
 __device__ __forceinline__ uint4 ld16(const bf16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// K and V rows are read once per call: non-temporal loads keep them from displacing
+// reusable lines in the caches.
+__device__ __forceinline__ uint4 ld16_stream(const bf16_t* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 template <int D>
 struct TileRegs {
   uint4 k[2][D / 32];
@@ -298,14 +307,14 @@ __global__ __launch_bounds__(kDecThreads) void decode_mfma_kernel(
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
       const int tok = token_at(base + lane / CH + RPI * j, anc, lim, nbase);
-      R.v[j] = ld16(Vu + (int64_t)tok * D + 8 * (lane % CH));
+      R.v[j] = ld16_stream(Vu + (int64_t)tok * D + 8 * (lane % CH));
     }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int tok = token_at(base + 16 * h + mem, anc, lim, nbase);
       const bf16_t* kr = Ku + (int64_t)tok * D + 8 * grp;
 #pragma unroll
-      for (int kc = 0; kc < KC; ++kc) R.k[h][kc] = ld16(kr + 32 * kc);
+      for (int kc = 0; kc < KC; ++kc) R.k[h][kc] = ld16_stream(kr + 32 * kc);
     }
   };
 
