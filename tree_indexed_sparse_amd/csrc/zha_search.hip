@@ -24,7 +24,7 @@ namespace {
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kScoreThreads = 256;
-constexpr int kScoreEntries = 256;  // frontier entries per workgroup (64 per wave)
+constexpr int kScoreEntries = 1024;  // most frontier entries per workgroup (256 per wave)
 
 constexpr int kSelThreads = 512;
 constexpr int kSelWaves = kSelThreads / 64;
@@ -49,13 +49,61 @@ __device__ __forceinline__ uint32_t frontier_node(const uint32_t* pnodes, int k,
 // 16q + 4 group + e as A and member `member`'s query at the same dims as B, so each
 // lane's 16-byte row loads are contiguous within the row. The C block leaves four
 // consecutive rows of one member per lane, stored as one 16-byte write.
+// Each wave walks its row blocks with the next block's loads in flight while the current
+// one is multiplied; summary rows are read once per call, with non-temporal loads.
+template <int D>
+struct ScoreRows {
+  f32x4_t a[D / 16];
+};
+
+template <int D>
+__device__ __forceinline__ void score_load(ScoreRows<D>& R, const float* __restrict__ Xu,
+                                           const uint32_t* sPn, int p0, int has_parent,
+                                           const FastDiv& bd, int k, int F, int grp) {
+  const bool ok = k < F;
+  const uint32_t kq = bd.div((uint32_t)k);
+  const uint32_t node =
+      ok ? (has_parent ? sPn[kq - p0] * bd.d + ((uint32_t)k - kq * bd.d) : (uint32_t)k) : 0u;
+  const f32x4_t* xr = reinterpret_cast<const f32x4_t*>(Xu + (int64_t)node * D + 4 * grp);
+#pragma unroll
+  for (int q = 0; q < D / 16; ++q)
+    R.a[q] = ok ? __builtin_nontemporal_load(xr + 4 * q) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+}
+
+// qf[q][e] = query dim 16q + e of the row at `qr` (already offset by 4 * group)
+template <int D>
+__device__ __forceinline__ void load_query_fragment(const float* qr, float (&qf)[D / 16][4]) {
+  f32x4_t v[D / 16];
+#pragma unroll
+  for (int q = 0; q < D / 16; ++q) v[q] = *reinterpret_cast<const f32x4_t*>(qr + 16 * q);
+#pragma unroll
+  for (int q = 0; q < D / 16; ++q)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) qf[q][e] = v[q][e];
+}
+template <int D>
+__device__ __forceinline__ void load_query_fragment(const bf16_t* qr, float (&qf)[D / 16][4]) {
+  typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+  u32x2_t v[D / 16];
+#pragma unroll
+  for (int q = 0; q < D / 16; ++q) v[q] = *reinterpret_cast<const u32x2_t*>(qr + 16 * q);
+#pragma unroll
+  for (int q = 0; q < D / 16; ++q) {
+    qf[q][0] = __uint_as_float(v[q].x << 16);
+    qf[q][1] = __uint_as_float(v[q].x & 0xffff0000u);
+    qf[q][2] = __uint_as_float(v[q].y << 16);
+    qf[q][3] = __uint_as_float(v[q].y & 0xffff0000u);
+  }
+}
+
 template <int D, typename Tq>
 __global__ __launch_bounds__(kScoreThreads) void score_kernel(
     Geom geo, const float* __restrict__ X, int64_t X_unit_stride, const Tq* __restrict__ Q,
     LevelBufs parent, int has_parent, int n_top, float* __restrict__ S, int64_t S_stride,
-    float sigma, float* __restrict__ pmax, float* __restrict__ pmin, int64_t pstride) {
+    float sigma, int ent, float* __restrict__ pmax, float* __restrict__ pmin, int64_t pstride) {
   constexpr int NQ = D / 16;
   constexpr int kMaxParents = kScoreEntries / 2 + 2;
+  const int kPerWave = ent / (kScoreThreads / 64);
   __shared__ uint32_t sPn[kMaxParents];
   __shared__ uint32_t sPm[kMaxParents];
   __shared__ float sRed[2][kScoreThreads / 64][16];
@@ -63,7 +111,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
   const int u = blockIdx.y;
   const int b = geo.b;
   const int F = has_parent ? b * (int)parent.count[u] : n_top;
-  const int k_wg = blockIdx.x * kScoreEntries;
+  const int k_wg = blockIdx.x * ent;
   if (k_wg >= F) return;
   const int Mu = members_of(geo, u);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -71,79 +119,80 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
 
   const int p0 = (int)geo.bdiv.div((uint32_t)k_wg);
   if (has_parent) {
-    const int np = (int)geo.bdiv.div((uint32_t)(min(k_wg + kScoreEntries, F) - 1)) - p0 + 1;
+    const int np = (int)geo.bdiv.div((uint32_t)(min(k_wg + ent, F) - 1)) - p0 + 1;
     for (int i = threadIdx.x; i < np; i += kScoreThreads) {
-      sPn[i] = parent.nodes[u * parent.stride + p0 + i];
-      if (pmax) sPm[i] = parent.masks[u * parent.stride + p0 + i];
+      const uint32_t nd = parent.nodes[u * parent.stride + p0 + i];
+      const uint32_t mk = parent.masks[u * parent.stride + p0 + i];
+      sPn[i] = nd;
+      sPm[i] = mk;
     }
   }
+  // query fragment: unconditional vector loads from a valid row, zeroed past the members
   float qf[NQ][4];
-  const Tq* qrow = Q + (int64_t)qh_of(geo, u, mem < Mu ? mem : 0) * D;
+  load_query_fragment<D>(Q + (int64_t)qh_of(geo, u, mem < Mu ? mem : 0) * D + 4 * grp, qf);
+  if (mem >= Mu) {
 #pragma unroll
-  for (int q = 0; q < NQ; ++q)
+    for (int q = 0; q < NQ; ++q)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) qf[q][e] = mem < Mu ? to_f32(qrow[16 * q + 4 * grp + e]) : 0.f;
+      for (int e = 0; e < 4; ++e) qf[q][e] = 0.f;
+  }
   __syncthreads();
   const float* Xu = X + (int64_t)bg_of(geo, u) * X_unit_stride;
   float* Srow = S + (int64_t)qh_of(geo, u, mem < Mu ? mem : 0) * S_stride;
-  const int k_wave = k_wg + wave * (kScoreEntries / 4);
+  const int k_wave = k_wg + wave * kPerWave;
+  const int nrb = k_wave < F ? min(kPerWave / 16, (F - k_wave + 15) / 16) : 0;
   float lmx = -INFINITY, lmn = INFINITY;  // over this lane's member rows
 
+  auto compute = [&](const ScoreRows<D>& R, int rb) {
+    f32x4_t c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    float4 a[2][NQ];
-#pragma unroll
-    for (int bb = 0; bb < 2; ++bb) {
-      const int k = k_wave + 16 * (2 * half + bb) + mem;
-      const bool ok = k < F;
-      const uint32_t kq = geo.bdiv.div((uint32_t)k);
-      const uint32_t node =
-          ok ? (has_parent ? sPn[kq - p0] * (uint32_t)b + ((uint32_t)k - kq * (uint32_t)b) : (uint32_t)k)
-             : 0u;
-      const float* xr = Xu + (int64_t)node * D + 4 * grp;
-#pragma unroll
-      for (int q = 0; q < NQ; ++q)
-        a[bb][q] = ok ? *reinterpret_cast<const float4*>(xr + 16 * q) : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int q = 0; q < NQ; ++q) {
+      c = __builtin_amdgcn_mfma_f32_16x16x4f32(R.a[q].x, qf[q][0], c, 0, 0, 0);
+      c = __builtin_amdgcn_mfma_f32_16x16x4f32(R.a[q].y, qf[q][1], c, 0, 0, 0);
+      c = __builtin_amdgcn_mfma_f32_16x16x4f32(R.a[q].z, qf[q][2], c, 0, 0, 0);
+      c = __builtin_amdgcn_mfma_f32_16x16x4f32(R.a[q].w, qf[q][3], c, 0, 0, 0);
     }
-#pragma unroll
-    for (int bb = 0; bb < 2; ++bb) {
-      f32x4_t c = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int q = 0; q < NQ; ++q) {
-        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[bb][q].x, qf[q][0], c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[bb][q].y, qf[q][1], c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[bb][q].z, qf[q][2], c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[bb][q].w, qf[q][3], c, 0, 0, 0);
+    // rows kb..kb+3 of member `mem`; + 0.0f turns a -0 score into +0 so float and bit
+    // orders agree
+    const int kb = k_wave + 16 * rb + 4 * grp;
+    if (mem < Mu && kb < F) {
+      const float4 o = make_float4(sigma * c[0] + 0.0f, sigma * c[1] + 0.0f,
+                                   sigma * c[2] + 0.0f, sigma * c[3] + 0.0f);
+      if (kb + 3 < F) {
+        *reinterpret_cast<float4*>(Srow + kb) = o;
+      } else {
+        Srow[kb] = o.x;
+        if (kb + 1 < F) Srow[kb + 1] = o.y;
+        if (kb + 2 < F) Srow[kb + 2] = o.z;
       }
-      // rows kb..kb+3 of member `mem`; + 0.0f turns a -0 score into +0 so float and bit
-      // orders agree
-      const int kb = k_wave + 16 * (2 * half + bb) + 4 * grp;
-      if (mem < Mu && kb < F) {
-        const float4 o = make_float4(sigma * c[0] + 0.0f, sigma * c[1] + 0.0f,
-                                     sigma * c[2] + 0.0f, sigma * c[3] + 0.0f);
-        if (kb + 3 < F) {
-          *reinterpret_cast<float4*>(Srow + kb) = o;
-        } else {
-          Srow[kb] = o.x;
-          if (kb + 1 < F) Srow[kb + 1] = o.y;
-          if (kb + 2 < F) Srow[kb + 2] = o.z;
-        }
-        if (pmax) {
-          const float ov[4] = {o.x, o.y, o.z, o.w};
+      if (pmax) {
+        const float ov[4] = {o.x, o.y, o.z, o.w};
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int k = kb + r;
-            const bool in = k < F && (!has_parent ||
-                                      ((sPm[geo.bdiv.div((uint32_t)k) - p0] >> mem) & 1u));
-            if (in) {
-              lmx = fmaxf(lmx, ov[r]);
-              lmn = fminf(lmn, ov[r]);
-            }
+        for (int r = 0; r < 4; ++r) {
+          const int k = kb + r;
+          const bool in = k < F && (!has_parent ||
+                                    ((sPm[geo.bdiv.div((uint32_t)k) - p0] >> mem) & 1u));
+          if (in) {
+            lmx = fmaxf(lmx, ov[r]);
+            lmn = fminf(lmn, ov[r]);
           }
         }
       }
     }
+  };
+
+  ScoreRows<D> A, Bv;
+  if (nrb > 0) score_load<D>(A, Xu, sPn, p0, has_parent, geo.bdiv, k_wave + mem, F, grp);
+  for (int rb = 0; rb < nrb; rb += 2) {
+    if (rb + 1 < nrb)
+      score_load<D>(Bv, Xu, sPn, p0, has_parent, geo.bdiv, k_wave + 16 * (rb + 1) + mem, F, grp);
+    compute(A, rb);
+    if (rb + 1 >= nrb) break;
+    if (rb + 2 < nrb)
+      score_load<D>(A, Xu, sPn, p0, has_parent, geo.bdiv, k_wave + 16 * (rb + 2) + mem, F, grp);
+    compute(Bv, rb + 1);
   }
+
   if (pmax) {
     // lanes l, l^16, l^32, l^48 hold one member; then the four waves
     lmx = fmaxf(lmx, __shfl_xor(lmx, 16, 64));
@@ -290,6 +339,28 @@ struct Quad {
   bool in[kVec];
 };
 
+// Four consecutive entries k0..k0+3 (k0 % 4 == 0) of member m's score row, below `end`
+// Every load is unconditional, from an index clamped into the row (row 0 when end is 0),
+// so the loads of several quads stay in flight together; entries at or past `end` are
+// not in.
+__device__ __forceinline__ Quad load_quad(const float* Sq, const uint32_t* pmask, int m,
+                                          const FastDiv& bd, int k0, int end) {
+  Quad q;
+  const int kc = k0 < end ? k0 : max((end - 1) & ~3, 0);  // rows are padded to a multiple of 4
+  const float4 v = *reinterpret_cast<const float4*>(Sq + kc);
+  q.s[0] = v.x;
+  q.s[1] = v.y;
+  q.s[2] = v.z;
+  q.s[3] = v.w;
+  uint32_t pw[kVec];
+#pragma unroll
+  for (int i = 0; i < kVec; ++i)
+    pw[i] = pmask ? pmask[bd.div((uint32_t)max(min(k0 + i, end - 1), 0))] : 0xffffffffu;
+#pragma unroll
+  for (int i = 0; i < kVec; ++i) q.in[i] = k0 + i < end && ((pw[i] >> m) & 1u);
+  return q;
+}
+
 __global__ __launch_bounds__(kSelThreads) void select_kernel(
     Geom geo, int level, const float* __restrict__ S, int64_t S_stride, LevelBufs parent,
     int has_parent, int n_top, KeepBits kb, float p, int anchor, int32_t* __restrict__ sel_idx,
@@ -314,22 +385,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     sh.scalar_u64[2] = ~0ull;
   }
 
-  auto load_global = [&](int k0) -> Quad {
-    Quad q;
-    const float4 v = (k0 + 3 < F) ? *reinterpret_cast<const float4*>(Sq + k0)
-                                  : make_float4(k0 < F ? Sq[k0] : 0.f, k0 + 1 < F ? Sq[k0 + 1] : 0.f,
-                                                k0 + 2 < F ? Sq[k0 + 2] : 0.f, 0.f);
-    q.s[0] = v.x;
-    q.s[1] = v.y;
-    q.s[2] = v.z;
-    q.s[3] = v.w;
-#pragma unroll
-    for (int i = 0; i < kVec; ++i) {
-      const int k = k0 + i;
-      q.in[i] = k < F && (!pmask || ((pmask[geo.bdiv.div((uint32_t)k)] >> m) & 1u));
-    }
-    return q;
-  };
+  auto load_global = [&](int k0) -> Quad { return load_quad(Sq, pmask, m, geo.bdiv, k0, F); };
   auto get = [&](int k0) -> Quad {
     if (!cached) return load_global(k0);
     Quad q;
@@ -659,33 +715,13 @@ static_assert(kWB == kCutThreads, "the cut kernel gives each thread one bucket")
 static_assert(kWideChunk % kTileE == 0, "histogram chunks hold whole tiles");
 static_assert(kUnionChunk == 8 * kUnionThreads, "union threads take two float4 per row");
 
-// Four consecutive entries k0..k0+3 of member m's score row, below `end`.
-__device__ __forceinline__ Quad load_quad(const float* Sq, const uint32_t* pmask, int m,
-                                          const FastDiv& bd, int k0, int end) {
-  Quad q;
-  const float4 v = (k0 + 3 < end)
-                       ? *reinterpret_cast<const float4*>(Sq + k0)
-                       : make_float4(k0 < end ? Sq[k0] : 0.f, k0 + 1 < end ? Sq[k0 + 1] : 0.f,
-                                     k0 + 2 < end ? Sq[k0 + 2] : 0.f, 0.f);
-  q.s[0] = v.x;
-  q.s[1] = v.y;
-  q.s[2] = v.z;
-  q.s[3] = v.w;
-#pragma unroll
-  for (int i = 0; i < kVec; ++i) {
-    const int k = k0 + i;
-    q.in[i] = k < end && (!pmask || ((pmask[bd.div((uint32_t)k)] >> m) & 1u));
-  }
-  return q;
-}
-
 // The head's max and min member score over a frontier of F entries, from the score
 // kernel's per-workgroup partials (block-wide, every thread gets both).
 template <int NT>
 __device__ __forceinline__ void partial_minmax(const WideSel& w, int qh, int F, float* red,
                                                float* omx, float* omn) {
   constexpr int NW = NT / 64;
-  const int np = (F + kScoreEntries - 1) / kScoreEntries;
+  const int np = (F + w.pent - 1) / w.pent;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   float mx = -INFINITY, mn = INFINITY;
   for (int i = threadIdx.x; i < np; i += NT) {
@@ -1087,14 +1123,16 @@ __device__ __forceinline__ uint32_t wave_prefix_total(const uint32_t* cnt, int n
   return acc;
 }
 
-// write: per (chunk, unit). Each wave compacts a quarter of the chunk with ballots, and
-// then writes the token lists of members wave, wave + 4, ... (level 1 only).
+// write: per (chunk, unit). The chunk's masks and node ids are staged in LDS; each wave
+// compacts a quarter of the chunk with ballots, then writes the token lists of members
+// wave, wave + 4, ... (level 1 only).
 __global__ __launch_bounds__(kUnionThreads) void wide_write_kernel(
     Geom geo, int level, LevelBufs parent, int has_parent, int n_top, LevelBufs cur,
     int anchor, int32_t* __restrict__ sel_idx, int64_t cap, WideSel w) {
   constexpr int NW = kUnionThreads / 64;
   constexpr int kPerWave = kUnionChunk / NW;
   __shared__ uint32_t s_um[kUnionChunk];
+  __shared__ uint32_t s_node[kUnionChunk];
   __shared__ uint32_t wtot[NW];
   const int u = blockIdx.y, chunk = blockIdx.x;
   const int b = geo.b;
@@ -1109,8 +1147,25 @@ __global__ __launch_bounds__(kUnionThreads) void wide_write_kernel(
   {
     const uint4 a = *reinterpret_cast<const uint4*>(umg + 4 * tid);
     const uint4 c = *reinterpret_cast<const uint4*>(umg + kUnionChunk / 2 + 4 * tid);
+    // node ids: parent loads from indices clamped below F (entries past F are never used)
+    uint32_t nd[8], kq[8], pn[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int e = (i >> 2) * (kUnionChunk / 2) + 4 * tid + (i & 3);
+      nd[i] = (uint32_t)min(c0 + e, F - 1);
+      kq[i] = geo.bdiv.div(nd[i]);
+    }
+    if (pnodes) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pn[i] = pnodes[kq[i]];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) nd[i] = pn[i] * (uint32_t)b + (nd[i] - kq[i] * (uint32_t)b);
+    }
     *reinterpret_cast<uint4*>(&s_um[4 * tid]) = a;
     *reinterpret_cast<uint4*>(&s_um[kUnionChunk / 2 + 4 * tid]) = c;
+    *reinterpret_cast<uint4*>(&s_node[4 * tid]) = make_uint4(nd[0], nd[1], nd[2], nd[3]);
+    *reinterpret_cast<uint4*>(&s_node[kUnionChunk / 2 + 4 * tid]) =
+        make_uint4(nd[4], nd[5], nd[6], nd[7]);
   }
   const uint32_t before = wave_prefix_total(w.ucnt + (int64_t)u * w.nuc, chunk, lane);
   __syncthreads();
@@ -1131,7 +1186,7 @@ __global__ __launch_bounds__(kUnionThreads) void wide_write_kernel(
     const uint64_t bal = __ballot(msk != 0u);
     if (msk) {
       const uint32_t at = pos + (uint32_t)__popcll(bal & ((1ull << lane) - 1ull));
-      onodes[at] = frontier_node(pnodes, c0 + e, geo.bdiv);
+      onodes[at] = s_node[e];
       omasks[at] = msk;
     }
     pos += (uint32_t)__popcll(bal);
@@ -1144,8 +1199,7 @@ __global__ __launch_bounds__(kUnionThreads) void wide_write_kernel(
   if (level != 1 || !sel_idx) return;
   for (int mm = wave; mm < Mu; mm += NW) {
     const int qh = qh_of(geo, u, mm);
-    const uint32_t* rec = w.cut + 4 * (int64_t)qh;
-    const int tok_base = (int)rec[2];
+    const int tok_base = (int)w.cut[4 * (int64_t)qh + 2];
     int32_t* sel = sel_idx + (int64_t)qh * cap;
     uint32_t mpos = wave_prefix_total(w.mcnt + (int64_t)qh * w.nuc, chunk, lane);
     for (int r = 0; r < kUnionChunk / 64; ++r) {
@@ -1154,7 +1208,7 @@ __global__ __launch_bounds__(kUnionThreads) void wide_write_kernel(
       const uint64_t bal = __ballot(kept);
       if (kept) {
         const uint32_t at = mpos + (uint32_t)__popcll(bal & ((1ull << lane) - 1ull));
-        const int node = (int)frontier_node(pnodes, c0 + e, geo.bdiv);
+        const int node = (int)s_node[e];
         for (int c = 0; c < b; ++c) {
           const int tok = node * b + c;
           if (tok >= anchor) sel[tok_base + (int64_t)at * b + c] = tok;
@@ -1178,10 +1232,21 @@ template <int EPT>
 __device__ __forceinline__ uint32_t chunk_masks(const Geom& geo, int u, int Mu, int F, int c0,
                                                 const KeepBits& kb, uint32_t (*sbits)[kCompactChunk / 32],
                                                 uint32_t (&msk)[EPT]) {
+  // stage the members' bit words of this chunk; every thread issues its loads together
+  constexpr int kPer = kMaxMembers * (kCompactChunk / 32) / kCompactThreads;
   const int words = (min(kCompactChunk, F - c0) + 31) / 32;
-  for (int i = threadIdx.x; i < Mu * words; i += kCompactThreads) {
-    const int mm = i / words, w = i % words;
-    sbits[mm][w] = kb.bits[(int64_t)qh_of(geo, u, mm) * kb.words + c0 / 32 + w];
+  uint32_t v[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int i = threadIdx.x + j * kCompactThreads;
+    const int mm = i / (kCompactChunk / 32), wd = i % (kCompactChunk / 32);
+    v[j] = (mm < Mu && wd < words)
+               ? kb.bits[(int64_t)qh_of(geo, u, mm) * kb.words + c0 / 32 + wd] : 0u;
+  }
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int i = threadIdx.x + j * kCompactThreads;
+    sbits[i / (kCompactChunk / 32)][i % (kCompactChunk / 32)] = v[j];
   }
   __syncthreads();
   const int e0 = EPT * threadIdx.x;
@@ -1203,14 +1268,30 @@ __device__ __forceinline__ uint32_t chunk_masks(const Geom& geo, int u, int Mu, 
   return cnt;
 }
 
+// Writes this thread's kept entries from position r on. Node ids come from parent loads
+// at indices clamped below F, issued together before any store.
 template <int EPT>
-__device__ __forceinline__ void chunk_write(const uint32_t* pnodes, const FastDiv& bd, int c0, uint32_t r,
-                                            const uint32_t (&msk)[EPT], const LevelBufs& cur, int u) {
+__device__ __forceinline__ void chunk_write(const uint32_t* pnodes, const FastDiv& bd, int F,
+                                            int c0, uint32_t r, const uint32_t (&msk)[EPT],
+                                            const LevelBufs& cur, int u) {
   const int e0 = EPT * threadIdx.x;
+  uint32_t nd[EPT];
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) nd[i] = (uint32_t)min(c0 + e0 + i, F - 1);
+  if (pnodes) {
+    uint32_t kq[EPT], pn[EPT];
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+      kq[i] = bd.div(nd[i]);
+      pn[i] = pnodes[kq[i]];
+    }
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) nd[i] = pn[i] * bd.d + (nd[i] - kq[i] * bd.d);
+  }
 #pragma unroll
   for (int i = 0; i < EPT; ++i) {
     if (msk[i]) {
-      cur.nodes[u * cur.stride + r] = frontier_node(pnodes, c0 + e0 + i, bd);
+      cur.nodes[u * cur.stride + r] = nd[i];
       cur.masks[u * cur.stride + r] = msk[i];
       ++r;
     }
@@ -1239,7 +1320,7 @@ __global__ __launch_bounds__(kCompactThreads) void compact_kernel(
       const uint32_t cnt = chunk_masks<kEPT>(geo, u, Mu, F, c0, kb, sbits, msk);
       uint32_t total;
       const uint32_t r = out + block_excl_scan<kCompactThreads>(cnt, wave_sum, &total);
-      chunk_write<kEPT>(pnodes, geo.bdiv, c0, r, msk, cur, u);
+      chunk_write<kEPT>(pnodes, geo.bdiv, F, c0, r, msk, cur, u);
       out += total;
     }
     if (threadIdx.x == 0) cur.count[u] = out;
@@ -1261,17 +1342,22 @@ __global__ __launch_bounds__(kCompactThreads) void compact_kernel(
   }
   uint32_t before = 0;
   for (int c = 0; c < chunk; ++c) before += chunk_cnt[u * max_chunks + c];
-  chunk_write<kEPT>(pnodes, geo.bdiv, c0, before + r, msk, cur, u);
+  chunk_write<kEPT>(pnodes, geo.bdiv, F, c0, before + r, msk, cur, u);
   if (chunk == nchunks - 1 && threadIdx.x == 0) cur.count[u] = before + total;
 }
 
 }  // namespace
 
+int score_entries(int64_t cap_entries) {
+  return cap_entries >= 65536 ? 1024 : (cap_entries >= 8192 ? 512 : 256);
+}
+
 hipError_t launch_score(const Geom& geo, const float* X, int64_t X_unit_stride, const void* Q,
                         int dtype, const LevelBufs* parent, int n_top, float* S,
                         int64_t S_stride, const WideSel* wide, hipStream_t s) {
   const int cap_entries = parent ? (int)(geo.b * parent->stride) : n_top;
-  dim3 grid((cap_entries + kScoreEntries - 1) / kScoreEntries, geo.U);
+  const int ent = score_entries(cap_entries);
+  dim3 grid((cap_entries + ent - 1) / ent, geo.U);
   const float sigma = 1.0f / sqrtf((float)geo.D);
   LevelBufs par = parent ? *parent : LevelBufs{};
   const int hp = parent ? 1 : 0;
@@ -1280,8 +1366,8 @@ hipError_t launch_score(const Geom& geo, const float* X, int64_t X_unit_stride, 
   const int64_t pstride = wide ? wide->pstride : 0;
 #define ZHA_SCORE(DD, TQ)                                                                     \
   hipLaunchKernelGGL((score_kernel<DD, TQ>), grid, dim3(kScoreThreads), 0, s, geo, X,          \
-                     X_unit_stride, (const TQ*)Q, par, hp, n_top, S, S_stride, sigma, pmax,    \
-                     pmin, pstride)
+                     X_unit_stride, (const TQ*)Q, par, hp, n_top, S, S_stride, sigma, ent,     \
+                     pmax, pmin, pstride)
   if (geo.D == 64) {
     if (dtype == ZHA_BF16) ZHA_SCORE(64, bf16_t);
     else ZHA_SCORE(64, float);
@@ -1295,7 +1381,7 @@ hipError_t launch_score(const Geom& geo, const float* X, int64_t X_unit_stride, 
 
 bool select_is_wide(int64_t cap_entries) { return cap_entries >= kWideMin; }
 int64_t wide_partial_stride(int64_t cap_entries) {
-  return (cap_entries + kScoreEntries - 1) / kScoreEntries;
+  return (cap_entries + 255) / 256;  // the smallest score workgroup takes 256 entries
 }
 int64_t wide_chunks(int64_t cap_entries) { return (cap_entries + kWideChunk - 1) / kWideChunk; }
 int64_t wide_union_chunks(int64_t cap_entries) {
