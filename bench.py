@@ -149,6 +149,7 @@ def main():
                                ("score", LB.ZHA_K_SCORE, range(1, L + 1)),
                                ("select", LB.ZHA_K_SELECT, range(1, L + 1)),
                                ("compact", LB.ZHA_K_COMPACT, range(1, L + 1)),
+                               ("descent_top", LB.ZHA_K_DESCENT, range(1, L + 1)),
                                ("decode", LB.ZHA_K_DECODE, [0]), ("combine", LB.ZHA_K_COMBINE, [0])):
         for lv in levels:
             tot, n = ktime(kind, lv)

@@ -149,8 +149,9 @@ int zha_attend_level_view(const zha_tree* t, int T, int Hq, int level, int64_t* 
  * pyramid level (level = -1: every level), the summed duration in milliseconds and the
  * number of launches. Kinds: ZHA_K_POOL (pooling; the level is the first level a launch
  * writes, level 1 reads the keys), ZHA_K_SCORE, ZHA_K_SELECT, ZHA_K_COMPACT (per level),
- * ZHA_K_DECODE and ZHA_K_COMBINE (level 0). Recording creates HIP events (host-side
- * objects), so it is off by default.
+ * ZHA_K_DECODE and ZHA_K_COMBINE (level 0), ZHA_K_DESCENT (the one launch that runs the
+ * top levels whose frontiers hold at most 1024 entries; its level is the lowest of them).
+ * Recording creates HIP events (host-side objects), so it is off by default.
  */
 enum {
   ZHA_K_POOL = 0,
@@ -158,7 +159,8 @@ enum {
   ZHA_K_SELECT = 3,
   ZHA_K_DECODE = 4,
   ZHA_K_COMPACT = 5,
-  ZHA_K_COMBINE = 6
+  ZHA_K_COMBINE = 6,
+  ZHA_K_DESCENT = 7
 };
 int zha_timing_enable(int on);
 int zha_timing_read(int kind, int level, double* total_ms, int64_t* launches);

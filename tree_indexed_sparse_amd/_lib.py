@@ -41,6 +41,7 @@ EXPORTS = (
 )
 
 ZHA_K_POOL, ZHA_K_SCORE, ZHA_K_SELECT, ZHA_K_DECODE, ZHA_K_COMPACT, ZHA_K_COMBINE = 0, 2, 3, 4, 5, 6
+ZHA_K_DESCENT = 7
 
 
 class ZhaError(RuntimeError):

@@ -105,7 +105,7 @@ struct WsLayout {
   int U, QH, splits;
   int64_t n[ZHA_MAX_LEVELS + 1];  // nodes per unit at each level (current N)
   int64_t off_count, off_lvl, off_S, off_bits, off_part, off_chunks;
-  int64_t off_pmax, off_pmin, off_hm, off_hc, off_cut, off_umask, off_ucnt, off_mcnt;
+  int64_t off_pmax, off_pmin, off_hm, off_hc, off_cut, off_umask, off_ucnt, off_mcnt, off_tbits;
   int64_t pstride, nch, ustride, nuc;
   int64_t off_nodes[ZHA_MAX_LEVELS + 1], off_masks[ZHA_MAX_LEVELS + 1];
   int64_t S_stride, bit_words;
@@ -191,6 +191,8 @@ WsLayout layout_of(const Geom& g) {
   off = align256(off + 4 * (int64_t)g.U * w.nuc);
   w.off_mcnt = off;
   off = align256(off + 4 * (int64_t)w.QH * w.nuc);
+  w.off_tbits = off;
+  off = align256(off + 4 * top_bitmap_words(w.QH, g.L));
   w.total = off;
   return w;
 }
@@ -396,9 +398,27 @@ int zha_attend(const zha_tree* t, const void* Q, int T, int Hq, const void* K, c
   wsel.nuc = w.nuc;
 
   hipError_t e = hipSuccess;
+  int64_t unit_stride[ZHA_MAX_LEVELS + 1] = {0};  // pyramid floats per (sequence, KV head)
+  {
+    int64_t c = t->N_cap;
+    for (int l = 1; l <= t->L; ++l) {
+      c /= t->b;
+      unit_stride[l] = c * t->d;
+    }
+  }
+  // the top levels with small frontiers run fused in one launch
+  const int l_top = top_levels_lowest(g, w.n);
+  if (l_top) {
+    e = timed(ZHA_K_DESCENT, l_top, s, [&] {
+      return launch_top_levels(g, t->pyramid, lv, t->level_off, unit_stride, l_top, Q, t->dtype,
+                               p, lvl, (uint32_t*)(ws + w.off_tbits), s);
+    });
+    if (e != hipSuccess) return hip_fail(e, "top-level descent launch");
+  }
   int64_t cap_l = t->N_cap;
   for (int l = 1; l <= t->L; ++l) cap_l /= t->b;  // capacity nodes at the top level
-  for (int l = t->L; l >= 1; --l) {
+  for (int l = l_top ? l_top - 1 : t->L; l < t->L; ++l) cap_l *= t->b;
+  for (int l = l_top ? l_top - 1 : t->L; l >= 1; --l) {
     const LevelBufs* parent = (l < t->L) ? &lv[l + 1] : nullptr;
     const int n_top = (l == t->L) ? (int)w.n[t->L] : 0;
     const float* X = t->pyramid + t->level_off[l];

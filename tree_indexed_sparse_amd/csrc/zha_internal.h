@@ -155,6 +155,17 @@ hipError_t launch_select(const Geom& geo, int level, const float* S, int64_t S_s
 hipError_t launch_compact(const Geom& geo, const LevelBufs* parent, int n_top, KeepBits kb,
                           const LevelBufs& cur, uint32_t* chunk_cnt, hipStream_t s);
 
+// Fused descent through the top levels (frontiers of at most 1024 entries): the lowest
+// such level >= 2 (0 if none; the top level must qualify), and the launches that walk
+// levels L .. l_lo per query head and write each level's union list. bitmaps: scratch of
+// top_bitmap_words(QH, L) words.
+int top_levels_lowest(const Geom& geo, const int64_t* nodes_per_level);
+hipError_t launch_top_levels(const Geom& geo, const float* pyramid, const LevelBufs* lv,
+                             const int64_t* level_off, const int64_t* unit_stride, int l_lo,
+                             const void* Q, int dtype, float p, int32_t* lvl_kept,
+                             uint32_t* bitmaps, hipStream_t s);
+int64_t top_bitmap_words(int QH, int L);
+
 // Compaction after the chunked selection: the members' keep flags straight from their
 // scores and cuts, the union list, and at level 1 the token lists.
 hipError_t launch_union(const Geom& geo, int level, const float* S, int64_t S_stride,

@@ -684,6 +684,243 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   }
 }
 
+// -------------------------------------------------------------- fused upper levels
+// The levels whose frontier holds at most kTopMax entries (the top levels of a deep tree)
+// run in two launches instead of three per level. Each query head walks them top-down in
+// its own workgroup, with its own frontier (the children of the nodes it kept one level
+// up), scores and kept list in LDS; it records the nodes it keeps at each level as a
+// bitmap. A second launch ORs the members' bitmaps of each unit into the level's union
+// list, which the lower levels (and diagnostics) read.
+// Per level and head:
+//   score:  sigma * q . X for every frontier row; a row is split over D / 4 lanes that
+//           each take four dims, and the partial sums are added across those lanes;
+//   select: a mass-weighted radix select over the 32-bit score ordinal finds the cut
+//           score (the lowest score whose cumulative mass, in descending order, reaches
+//           ceil(p Z)); the entries tied at the cut share one mass, so the first
+//           ceil(rest / mass) of them by index are kept. This is the same
+//           (score desc, index asc) prefix the other selection paths keep.
+constexpr int kTopThreads = 1024;
+constexpr int kTopWaves = kTopThreads / 64;
+constexpr int kTopMax = 1024;                 // frontier entries: one per thread
+constexpr int kTopUnroll = 8;                 // row loads in flight per lane
+
+struct TopLevels {
+  LevelBufs lv[ZHA_MAX_LEVELS + 1];
+  int64_t xoff[ZHA_MAX_LEVELS + 1];     // float offset of level l in the pyramid
+  int64_t xstride[ZHA_MAX_LEVELS + 1];  // floats per (sequence, KV head) at level l
+};
+
+struct HeadTopShared {
+  float S[kTopMax];
+  uint32_t kn[2][kTopMax];              // kept node lists (previous level / this level)
+  unsigned long long hist[256];
+  unsigned long long wsum[kTopWaves];
+  uint32_t wcnt[kTopWaves];
+  uint32_t bits[kTopMax / 32];
+  float red[kTopWaves];
+  unsigned long long scal64[2];
+  uint32_t scal32[2];
+};
+
+// sum over the block of one u64 per thread (every thread gets it)
+__device__ __forceinline__ uint64_t top_block_sum(uint64_t v, unsigned long long* wsum) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const uint32_t lo = __shfl_xor((uint32_t)v, off, 64);
+    const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), off, 64);
+    v += ((uint64_t)hi << 32) | lo;
+  }
+  __syncthreads();
+  if (lane == 0) wsum[wave] = v;
+  __syncthreads();
+  uint64_t t = 0;
+#pragma unroll
+  for (int w = 0; w < kTopWaves; ++w) t += wsum[w];
+  return t;
+}
+
+// exclusive prefix over the block of one flag per thread, in thread order; *total = count
+__device__ __forceinline__ uint32_t top_block_rank(bool f, uint32_t* wcnt, uint32_t* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint64_t bal = __ballot(f);
+  __syncthreads();
+  if (lane == 0) wcnt[wave] = (uint32_t)__popcll(bal);
+  __syncthreads();
+  uint32_t before = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kTopWaves; ++w) {
+    before += w < wave ? wcnt[w] : 0u;
+    tot += wcnt[w];
+  }
+  *total = tot;
+  return before + (uint32_t)__popcll(bal & ((1ull << lane) - 1ull));
+}
+
+template <int D, typename Tq>
+__global__ __launch_bounds__(kTopThreads) void head_top_kernel(
+    Geom geo, const float* __restrict__ pyramid, TopLevels tl, int l_hi, int l_lo,
+    const Tq* __restrict__ Q, float p, float sigma, int32_t* __restrict__ lvl_kept,
+    uint32_t* __restrict__ bitmaps) {
+  constexpr int LPR = D / 4;        // lanes per row
+  constexpr int RPW = 64 / LPR;     // rows per wave-wide load
+  constexpr int RPB = RPW * kTopWaves;  // rows per block-wide load
+  __shared__ HeadTopShared sh;
+  const int qh = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int u, m;
+  unit_member_of(geo, qh, &u, &m);
+  const int b = geo.b;
+  const bool keep_all = !(p < 1.0f);
+  const int sub = lane % LPR;
+  float qv[4];
+  {
+    const Tq* qr = Q + (int64_t)qh * D + 4 * sub;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) qv[e] = to_f32(qr[e]);
+  }
+  int cur = 0;
+  int F = (int)tl.lv[l_hi].stride;  // top level: every node
+  for (int l = l_hi; l >= l_lo; --l) {
+    const bool top = l == l_hi;
+    const float* Xu = pyramid + tl.xoff[l] + (int64_t)bg_of(geo, u) * tl.xstride[l];
+    const uint32_t* kn = sh.kn[cur];
+    // ---- score: row r = i * RPB + wave * RPW + lane / LPR
+    for (int r0 = 0; r0 < F; r0 += RPB * kTopUnroll) {
+      f32x4_t x[kTopUnroll];
+#pragma unroll
+      for (int i = 0; i < kTopUnroll; ++i) {
+        const int r = min(r0 + i * RPB + wave * RPW + lane / LPR, F - 1);
+        uint32_t node = (uint32_t)r;
+        if (!top) {
+          const uint32_t q = geo.bdiv.div((uint32_t)r);
+          node = kn[q] * (uint32_t)b + ((uint32_t)r - q * (uint32_t)b);
+        }
+        x[i] = __builtin_nontemporal_load(
+            reinterpret_cast<const f32x4_t*>(Xu + (int64_t)node * D + 4 * sub));
+      }
+#pragma unroll
+      for (int i = 0; i < kTopUnroll; ++i) {
+        float v = x[i].x * qv[0];
+        v = fmaf(x[i].y, qv[1], v);
+        v = fmaf(x[i].z, qv[2], v);
+        v = fmaf(x[i].w, qv[3], v);
+#pragma unroll
+        for (int off = LPR / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+        const int r = r0 + i * RPB + wave * RPW + lane / LPR;
+        if (sub == 0 && r < F) sh.S[r] = sigma * v + 0.0f;
+      }
+    }
+    __syncthreads();
+
+    // ---- select: thread tid takes entry tid
+    const bool in = tid < F;
+    const float sv = in ? sh.S[tid] : -INFINITY;
+    const uint32_t ord = ord_of(sv);
+    float mx = sv;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+    if (lane == 0) sh.red[wave] = mx;
+    __syncthreads();
+    mx = sh.red[0];
+#pragma unroll
+    for (int w = 1; w < kTopWaves; ++w) mx = fmaxf(mx, sh.red[w]);
+    const uint64_t ms = in ? mass_fixed(sv, mx) : 0ull;
+    bool keep = in;
+    if (!keep_all) {
+      const uint64_t Z = top_block_sum(ms, sh.wsum);
+      uint64_t need = ceil_mul_p(p, Z);
+      uint32_t prefix = 0u, pbits = 0u;
+      for (int shift = 24; shift >= 0; shift -= 8) {
+        if (tid < 256) sh.hist[tid] = 0ull;
+        __syncthreads();
+        if (in && (ord & pbits) == prefix)
+          atomicAdd(&sh.hist[(ord >> shift) & 255u], (unsigned long long)ms);
+        __syncthreads();
+        if (wave == 0) {
+          // lane l holds digits 255 - 4l .. 252 - 4l (descending); cumulative from the top
+          uint64_t hv[4], loc = 0;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            hv[i] = sh.hist[255 - 4 * lane - i];
+            loc += hv[i];
+          }
+          const uint64_t incl = wave_incl_scan_u64(loc, lane);
+          const uint64_t excl = incl - loc;
+          if (excl < need && incl >= need) {  // one lane: 1 <= need <= the group's mass
+            uint64_t run = excl;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              if (run + hv[i] >= need) {
+                sh.scal32[0] = 255u - 4u * lane - i;
+                sh.scal64[0] = run;
+                break;
+              }
+              run += hv[i];
+            }
+          }
+        }
+        __syncthreads();
+        need -= sh.scal64[0];
+        prefix |= sh.scal32[0] << shift;
+        pbits |= 255u << shift;
+      }
+      // ties at the cut score share one mass: keep the first ceil(need / mass) by index
+      const uint64_t mcut = mass_fixed(float_of_ord(prefix), mx);
+      const uint64_t ties = (need + mcut - 1) / mcut;
+      const bool tie = in && ord == prefix;
+      uint32_t ntie;
+      const uint32_t rank = top_block_rank(tie, sh.wcnt, &ntie);
+      keep = in && (ord > prefix || (tie && (uint64_t)rank < ties));
+    }
+    // ---- kept list (ascending) and bitmap of kept node ids
+    uint32_t kept;
+    const uint32_t pos = top_block_rank(keep, sh.wcnt, &kept);
+    if (tid < kTopMax / 32) sh.bits[tid] = 0u;
+    __syncthreads();
+    if (keep) {
+      uint32_t node = (uint32_t)tid;
+      if (!top) {
+        const uint32_t q = geo.bdiv.div((uint32_t)tid);
+        node = kn[q] * (uint32_t)b + ((uint32_t)tid - q * (uint32_t)b);
+      }
+      sh.kn[cur ^ 1][pos] = node;
+      atomicOr(&sh.bits[node >> 5], 1u << (node & 31));
+    }
+    __syncthreads();
+    if (tid < kTopMax / 32) bitmaps[((int64_t)qh * (geo.L + 1) + l) * (kTopMax / 32) + tid] = sh.bits[tid];
+    if (tid == 0) lvl_kept[(int64_t)qh * (geo.L + 1) + l] = (int32_t)kept;
+    cur ^= 1;
+    F = (int)kept * b;
+  }
+}
+
+// Union lists of the fused levels: workgroup (unit, level), thread j = node j of the level.
+__global__ __launch_bounds__(kTopThreads) void union_top_kernel(Geom geo, TopLevels tl, int l_lo,
+                                                                 const uint32_t* __restrict__ bitmaps) {
+  __shared__ uint32_t wcnt[kTopWaves];
+  const int u = blockIdx.x, l = l_lo + blockIdx.y;
+  const int tid = threadIdx.x;
+  const int Mu = members_of(geo, u);
+  const LevelBufs& cur = tl.lv[l];
+  const int n = (int)cur.stride;
+  uint32_t msk = 0u;
+  if (tid < n) {
+    for (int mm = 0; mm < Mu; ++mm) {
+      const uint32_t w =
+          bitmaps[((int64_t)qh_of(geo, u, mm) * (geo.L + 1) + l) * (kTopMax / 32) + (tid >> 5)];
+      msk |= ((w >> (tid & 31)) & 1u) << mm;
+    }
+  }
+  uint32_t total;
+  const uint32_t pos = top_block_rank(msk != 0u, wcnt, &total);
+  if (msk) {
+    cur.nodes[u * cur.stride + pos] = (uint32_t)tid;
+    cur.masks[u * cur.stride + pos] = msk;
+  }
+  if (tid == 0) cur.count[u] = total;
+}
+
 // ------------------------------------------------------------------ chunked selection
 // A large frontier runs its top-p and compaction in four launches whose workgroups each
 // take one chunk of the frontier:
@@ -1436,6 +1673,44 @@ hipError_t launch_compact(const Geom& geo, const LevelBufs* parent, int n_top, K
                      par, hp, n_top, kb, cur, 2, chunk_cnt, max_chunks);
   return hipGetLastError();
 }
+
+int top_levels_lowest(const Geom& geo, const int64_t* nodes_per_level) {
+  int lo = 0;
+  for (int l = geo.L; l >= 2 && nodes_per_level[l] <= kTopMax; --l) lo = l;
+  return lo;  // 0: no level qualifies
+}
+
+hipError_t launch_top_levels(const Geom& geo, const float* pyramid, const LevelBufs* lv,
+                             const int64_t* level_off, const int64_t* unit_stride, int l_lo,
+                             const void* Q, int dtype, float p, int32_t* lvl_kept,
+                             uint32_t* bitmaps, hipStream_t s) {
+  TopLevels tl{};
+  for (int l = l_lo; l <= geo.L; ++l) {
+    tl.lv[l] = lv[l];
+    tl.xoff[l] = level_off[l];
+    tl.xstride[l] = unit_stride[l];
+  }
+  const float sigma = 1.0f / sqrtf((float)geo.D);
+  const int QH = geo.B * geo.T * geo.Hq;
+#define ZHA_TOP(DD, TQ)                                                                       \
+  hipLaunchKernelGGL((head_top_kernel<DD, TQ>), dim3(QH), dim3(kTopThreads), 0, s, geo,        \
+                     pyramid, tl, geo.L, l_lo, (const TQ*)Q, p, sigma, lvl_kept, bitmaps)
+  if (geo.D == 64) {
+    if (dtype == ZHA_BF16) ZHA_TOP(64, bf16_t);
+    else ZHA_TOP(64, float);
+  } else {
+    if (dtype == ZHA_BF16) ZHA_TOP(128, bf16_t);
+    else ZHA_TOP(128, float);
+  }
+#undef ZHA_TOP
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(union_top_kernel, dim3(geo.U, geo.L - l_lo + 1), dim3(kTopThreads), 0, s,
+                     geo, tl, l_lo, bitmaps);
+  return hipGetLastError();
+}
+
+int64_t top_bitmap_words(int QH, int L) { return (int64_t)QH * (L + 1) * (kTopMax / 32); }
 
 hipError_t launch_union(const Geom& geo, int level, const float* S, int64_t S_stride,
                         const LevelBufs* parent, int n_top, const LevelBufs& cur, int anchor,
