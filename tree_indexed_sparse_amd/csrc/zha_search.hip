@@ -685,7 +685,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
 }
 
 // -------------------------------------------------------------- fused upper levels
-// The levels whose frontier holds at most kTopMax entries (the top levels of a deep tree)
+// The levels whose frontier holds at most kTopFuse entries (the top levels of a deep tree)
 // run in two launches instead of three per level. Each query head walks them top-down in
 // its own workgroup, with its own frontier (the children of the nodes it kept one level
 // up), scores and kept list in LDS; it records the nodes it keeps at each level as a
@@ -701,8 +701,11 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
 //           (score desc, index asc) prefix the other selection paths keep.
 constexpr int kTopThreads = 1024;
 constexpr int kTopWaves = kTopThreads / 64;
-constexpr int kTopMax = 1024;                 // frontier entries: one per thread
-constexpr int kTopUnroll = 8;                 // row loads in flight per lane
+constexpr int kTopMax = 4096;                    // frontier entries the kernel holds
+constexpr int kTopFuse = 1024;                   // levels of at most this many nodes are fused
+constexpr int kTopEPT = kTopMax / kTopThreads;   // entries per thread (4 consecutive)
+constexpr int kTopUnroll = 8;                    // row loads per lane per batch
+constexpr int kTopWords = kTopMax / 32;          // bitmap words per (head, level)
 
 struct TopLevels {
   LevelBufs lv[ZHA_MAX_LEVELS + 1];
@@ -716,7 +719,7 @@ struct HeadTopShared {
   unsigned long long hist[256];
   unsigned long long wsum[kTopWaves];
   uint32_t wcnt[kTopWaves];
-  uint32_t bits[kTopMax / 32];
+  uint32_t bits[kTopWords];
   float red[kTopWaves];
   unsigned long long scal64[2];
   uint32_t scal32[2];
@@ -740,21 +743,41 @@ __device__ __forceinline__ uint64_t top_block_sum(uint64_t v, unsigned long long
   return t;
 }
 
-// exclusive prefix over the block of one flag per thread, in thread order; *total = count
-__device__ __forceinline__ uint32_t top_block_rank(bool f, uint32_t* wcnt, uint32_t* total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const uint64_t bal = __ballot(f);
-  __syncthreads();
-  if (lane == 0) wcnt[wave] = (uint32_t)__popcll(bal);
-  __syncthreads();
-  uint32_t before = 0, tot = 0;
+template <int D>
+__device__ __forceinline__ void top_rows_load(f32x4_t (&x)[kTopUnroll], const float* Xu,
+                                              const uint32_t* kn, bool top, const FastDiv& bd,
+                                              int r0, int F, int sub, int row_in) {
+  constexpr int RPB = (64 / (D / 4)) * kTopWaves;  // rows per block-wide load
 #pragma unroll
-  for (int w = 0; w < kTopWaves; ++w) {
-    before += w < wave ? wcnt[w] : 0u;
-    tot += wcnt[w];
+  for (int i = 0; i < kTopUnroll; ++i) {
+    const uint32_t r = (uint32_t)min(r0 + i * RPB + row_in, F - 1);
+    uint32_t node = r;
+    if (!top) {
+      const uint32_t q = bd.div(r);
+      node = kn[q] * bd.d + (r - q * bd.d);
+    }
+    // plain loads: the unit's other heads read mostly the same rows, from the cache
+    x[i] = *reinterpret_cast<const f32x4_t*>(Xu + (int64_t)node * D + 4 * sub);
   }
-  *total = tot;
-  return before + (uint32_t)__popcll(bal & ((1ull << lane) - 1ull));
+}
+
+template <int D>
+__device__ __forceinline__ void top_rows_score(const f32x4_t (&x)[kTopUnroll], const float (&qv)[4],
+                                               float* S, float sigma, int r0, int F, int sub,
+                                               int row_in) {
+  constexpr int LPR = D / 4;
+  constexpr int RPB = (64 / LPR) * kTopWaves;
+#pragma unroll
+  for (int i = 0; i < kTopUnroll; ++i) {
+    float v = x[i].x * qv[0];
+    v = fmaf(x[i].y, qv[1], v);
+    v = fmaf(x[i].z, qv[2], v);
+    v = fmaf(x[i].w, qv[3], v);
+#pragma unroll
+    for (int off = LPR / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    const int r = r0 + i * RPB + row_in;
+    if (sub == 0 && r < F) S[r] = sigma * v + 0.0f;
+  }
 }
 
 template <int D, typename Tq>
@@ -762,9 +785,9 @@ __global__ __launch_bounds__(kTopThreads) void head_top_kernel(
     Geom geo, const float* __restrict__ pyramid, TopLevels tl, int l_hi, int l_lo,
     const Tq* __restrict__ Q, float p, float sigma, int32_t* __restrict__ lvl_kept,
     uint32_t* __restrict__ bitmaps) {
-  constexpr int LPR = D / 4;        // lanes per row
-  constexpr int RPW = 64 / LPR;     // rows per wave-wide load
-  constexpr int RPB = RPW * kTopWaves;  // rows per block-wide load
+  constexpr int LPR = D / 4;              // lanes per row
+  constexpr int RPW = 64 / LPR;           // rows per wave-wide load
+  constexpr int STEP = RPW * kTopWaves * kTopUnroll;  // rows per batch
   __shared__ HeadTopShared sh;
   const int qh = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -772,7 +795,7 @@ __global__ __launch_bounds__(kTopThreads) void head_top_kernel(
   unit_member_of(geo, qh, &u, &m);
   const int b = geo.b;
   const bool keep_all = !(p < 1.0f);
-  const int sub = lane % LPR;
+  const int sub = lane % LPR, row_in = wave * RPW + lane / LPR;
   float qv[4];
   {
     const Tq* qr = Q + (int64_t)qh * D + 4 * sub;
@@ -785,39 +808,40 @@ __global__ __launch_bounds__(kTopThreads) void head_top_kernel(
     const bool top = l == l_hi;
     const float* Xu = pyramid + tl.xoff[l] + (int64_t)bg_of(geo, u) * tl.xstride[l];
     const uint32_t* kn = sh.kn[cur];
-    // ---- score: row r = i * RPB + wave * RPW + lane / LPR
-    for (int r0 = 0; r0 < F; r0 += RPB * kTopUnroll) {
-      f32x4_t x[kTopUnroll];
-#pragma unroll
-      for (int i = 0; i < kTopUnroll; ++i) {
-        const int r = min(r0 + i * RPB + wave * RPW + lane / LPR, F - 1);
-        uint32_t node = (uint32_t)r;
-        if (!top) {
-          const uint32_t q = geo.bdiv.div((uint32_t)r);
-          node = kn[q] * (uint32_t)b + ((uint32_t)r - q * (uint32_t)b);
-        }
-        x[i] = __builtin_nontemporal_load(
-            reinterpret_cast<const f32x4_t*>(Xu + (int64_t)node * D + 4 * sub));
-      }
-#pragma unroll
-      for (int i = 0; i < kTopUnroll; ++i) {
-        float v = x[i].x * qv[0];
-        v = fmaf(x[i].y, qv[1], v);
-        v = fmaf(x[i].z, qv[2], v);
-        v = fmaf(x[i].w, qv[3], v);
-#pragma unroll
-        for (int off = LPR / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-        const int r = r0 + i * RPB + wave * RPW + lane / LPR;
-        if (sub == 0 && r < F) sh.S[r] = sigma * v + 0.0f;
+    // ---- score, two batches of rows in flight
+    {
+      f32x4_t xa[kTopUnroll], xb[kTopUnroll];
+      top_rows_load<D>(xa, Xu, kn, top, geo.bdiv, 0, F, sub, row_in);
+      for (int r0 = 0; r0 < F; r0 += 2 * STEP) {
+        if (r0 + STEP < F) top_rows_load<D>(xb, Xu, kn, top, geo.bdiv, r0 + STEP, F, sub, row_in);
+        top_rows_score<D>(xa, qv, sh.S, sigma, r0, F, sub, row_in);
+        if (r0 + STEP >= F) break;
+        if (r0 + 2 * STEP < F)
+          top_rows_load<D>(xa, Xu, kn, top, geo.bdiv, r0 + 2 * STEP, F, sub, row_in);
+        top_rows_score<D>(xb, qv, sh.S, sigma, r0 + STEP, F, sub, row_in);
       }
     }
     __syncthreads();
 
-    // ---- select: thread tid takes entry tid
-    const bool in = tid < F;
-    const float sv = in ? sh.S[tid] : -INFINITY;
-    const uint32_t ord = ord_of(sv);
-    float mx = sv;
+    // ---- select: thread tid takes entries k0 .. k0 + 3 (k0 = 4 tid)
+    const int k0 = kTopEPT * tid;
+    float sv[kTopEPT];
+    {
+      const float4 v = *reinterpret_cast<const float4*>(&sh.S[k0]);
+      sv[0] = v.x;
+      sv[1] = v.y;
+      sv[2] = v.z;
+      sv[3] = v.w;
+    }
+    uint32_t ord[kTopEPT];
+    bool in[kTopEPT];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < kTopEPT; ++i) {
+      in[i] = k0 + i < F;
+      ord[i] = ord_of(sv[i]);
+      if (in[i]) mx = fmaxf(mx, sv[i]);
+    }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
     if (lane == 0) sh.red[wave] = mx;
@@ -825,17 +849,27 @@ __global__ __launch_bounds__(kTopThreads) void head_top_kernel(
     mx = sh.red[0];
 #pragma unroll
     for (int w = 1; w < kTopWaves; ++w) mx = fmaxf(mx, sh.red[w]);
-    const uint64_t ms = in ? mass_fixed(sv, mx) : 0ull;
-    bool keep = in;
+    uint64_t ms[kTopEPT];
+    uint64_t msum = 0;
+#pragma unroll
+    for (int i = 0; i < kTopEPT; ++i) {
+      ms[i] = in[i] ? mass_fixed(sv[i], mx) : 0ull;
+      msum += ms[i];
+    }
+    bool keep[kTopEPT];
+#pragma unroll
+    for (int i = 0; i < kTopEPT; ++i) keep[i] = in[i];
     if (!keep_all) {
-      const uint64_t Z = top_block_sum(ms, sh.wsum);
+      const uint64_t Z = top_block_sum(msum, sh.wsum);
       uint64_t need = ceil_mul_p(p, Z);
       uint32_t prefix = 0u, pbits = 0u;
       for (int shift = 24; shift >= 0; shift -= 8) {
         if (tid < 256) sh.hist[tid] = 0ull;
         __syncthreads();
-        if (in && (ord & pbits) == prefix)
-          atomicAdd(&sh.hist[(ord >> shift) & 255u], (unsigned long long)ms);
+#pragma unroll
+        for (int i = 0; i < kTopEPT; ++i)
+          if (in[i] && (ord[i] & pbits) == prefix)
+            atomicAdd(&sh.hist[(ord[i] >> shift) & 255u], (unsigned long long)ms[i]);
         __syncthreads();
         if (wave == 0) {
           // lane l holds digits 255 - 4l .. 252 - 4l (descending); cumulative from the top
@@ -868,34 +902,48 @@ __global__ __launch_bounds__(kTopThreads) void head_top_kernel(
       // ties at the cut score share one mass: keep the first ceil(need / mass) by index
       const uint64_t mcut = mass_fixed(float_of_ord(prefix), mx);
       const uint64_t ties = (need + mcut - 1) / mcut;
-      const bool tie = in && ord == prefix;
-      uint32_t ntie;
-      const uint32_t rank = top_block_rank(tie, sh.wcnt, &ntie);
-      keep = in && (ord > prefix || (tie && (uint64_t)rank < ties));
+      uint32_t ntie = 0;
+#pragma unroll
+      for (int i = 0; i < kTopEPT; ++i) ntie += (in[i] && ord[i] == prefix);
+      uint32_t tot;
+      uint32_t rank = block_excl_scan<kTopThreads>(ntie, sh.wcnt, &tot);
+#pragma unroll
+      for (int i = 0; i < kTopEPT; ++i) {
+        const bool tie = in[i] && ord[i] == prefix;
+        keep[i] = in[i] && (ord[i] > prefix || (tie && (uint64_t)rank < ties));
+        rank += tie;
+      }
     }
     // ---- kept list (ascending) and bitmap of kept node ids
+    uint32_t nk = 0;
+#pragma unroll
+    for (int i = 0; i < kTopEPT; ++i) nk += keep[i];
     uint32_t kept;
-    const uint32_t pos = top_block_rank(keep, sh.wcnt, &kept);
-    if (tid < kTopMax / 32) sh.bits[tid] = 0u;
+    uint32_t pos = block_excl_scan<kTopThreads>(nk, sh.wcnt, &kept);
+    if (tid < kTopWords) sh.bits[tid] = 0u;
     __syncthreads();
-    if (keep) {
-      uint32_t node = (uint32_t)tid;
-      if (!top) {
-        const uint32_t q = geo.bdiv.div((uint32_t)tid);
-        node = kn[q] * (uint32_t)b + ((uint32_t)tid - q * (uint32_t)b);
+#pragma unroll
+    for (int i = 0; i < kTopEPT; ++i) {
+      if (keep[i]) {
+        uint32_t node = (uint32_t)(k0 + i);
+        if (!top) {
+          const uint32_t q = geo.bdiv.div(node);
+          node = kn[q] * (uint32_t)b + (node - q * (uint32_t)b);
+        }
+        sh.kn[cur ^ 1][pos++] = node;
+        atomicOr(&sh.bits[node >> 5], 1u << (node & 31));
       }
-      sh.kn[cur ^ 1][pos] = node;
-      atomicOr(&sh.bits[node >> 5], 1u << (node & 31));
     }
     __syncthreads();
-    if (tid < kTopMax / 32) bitmaps[((int64_t)qh * (geo.L + 1) + l) * (kTopMax / 32) + tid] = sh.bits[tid];
+    if (tid < kTopWords)
+      bitmaps[((int64_t)qh * (geo.L + 1) + l) * kTopWords + tid] = sh.bits[tid];
     if (tid == 0) lvl_kept[(int64_t)qh * (geo.L + 1) + l] = (int32_t)kept;
     cur ^= 1;
     F = (int)kept * b;
   }
 }
 
-// Union lists of the fused levels: workgroup (unit, level), thread j = node j of the level.
+// Union lists of the fused levels: workgroup (unit, level); thread t takes nodes 4t .. 4t+3.
 __global__ __launch_bounds__(kTopThreads) void union_top_kernel(Geom geo, TopLevels tl, int l_lo,
                                                                  const uint32_t* __restrict__ bitmaps) {
   __shared__ uint32_t wcnt[kTopWaves];
@@ -904,19 +952,31 @@ __global__ __launch_bounds__(kTopThreads) void union_top_kernel(Geom geo, TopLev
   const int Mu = members_of(geo, u);
   const LevelBufs& cur = tl.lv[l];
   const int n = (int)cur.stride;
-  uint32_t msk = 0u;
-  if (tid < n) {
+  const int j0 = kTopEPT * tid;
+  uint32_t msk[kTopEPT] = {0u, 0u, 0u, 0u};
+  if (j0 < n) {
     for (int mm = 0; mm < Mu; ++mm) {
       const uint32_t w =
-          bitmaps[((int64_t)qh_of(geo, u, mm) * (geo.L + 1) + l) * (kTopMax / 32) + (tid >> 5)];
-      msk |= ((w >> (tid & 31)) & 1u) << mm;
+          bitmaps[((int64_t)qh_of(geo, u, mm) * (geo.L + 1) + l) * kTopWords + (j0 >> 5)];
+#pragma unroll
+      for (int i = 0; i < kTopEPT; ++i) msk[i] |= ((w >> ((j0 + i) & 31)) & 1u) << mm;
     }
   }
+  uint32_t nz = 0;
+#pragma unroll
+  for (int i = 0; i < kTopEPT; ++i) {
+    if (j0 + i >= n) msk[i] = 0u;
+    nz += msk[i] != 0u;
+  }
   uint32_t total;
-  const uint32_t pos = top_block_rank(msk != 0u, wcnt, &total);
-  if (msk) {
-    cur.nodes[u * cur.stride + pos] = (uint32_t)tid;
-    cur.masks[u * cur.stride + pos] = msk;
+  uint32_t pos = block_excl_scan<kTopThreads>(nz, wcnt, &total);
+#pragma unroll
+  for (int i = 0; i < kTopEPT; ++i) {
+    if (msk[i]) {
+      cur.nodes[u * cur.stride + pos] = (uint32_t)(j0 + i);
+      cur.masks[u * cur.stride + pos] = msk[i];
+      ++pos;
+    }
   }
   if (tid == 0) cur.count[u] = total;
 }
@@ -1676,7 +1736,7 @@ hipError_t launch_compact(const Geom& geo, const LevelBufs* parent, int n_top, K
 
 int top_levels_lowest(const Geom& geo, const int64_t* nodes_per_level) {
   int lo = 0;
-  for (int l = geo.L; l >= 2 && nodes_per_level[l] <= kTopMax; --l) lo = l;
+  for (int l = geo.L; l >= 2 && nodes_per_level[l] <= kTopFuse; --l) lo = l;
   return lo;  // 0: no level qualifies
 }
 
@@ -1710,7 +1770,7 @@ hipError_t launch_top_levels(const Geom& geo, const float* pyramid, const LevelB
   return hipGetLastError();
 }
 
-int64_t top_bitmap_words(int QH, int L) { return (int64_t)QH * (L + 1) * (kTopMax / 32); }
+int64_t top_bitmap_words(int QH, int L) { return (int64_t)QH * (L + 1) * kTopWords; }
 
 hipError_t launch_union(const Geom& geo, int level, const float* S, int64_t S_stride,
                         const LevelBufs* parent, int n_top, const LevelBufs& cur, int anchor,
