@@ -190,6 +190,32 @@ def test_exact_ties_broken_by_lowest_index(N):
     Z.attend.last_workspace = None
 
 
+def test_tied_groups_in_chunked_selection():
+    """Keys repeat in groups of 512 nodes (2048 tokens), so the 16384-node top frontier
+    (chunked selection) has 32 distinct scores, each shared by 512 nodes: the cut falls
+    inside a tied group and must keep its lowest node ids, a count taken from the mass."""
+    import tree_indexed_sparse_amd as Z
+    import oracle as O
+
+    spec = W.spec("tiny", N=65536, b=4, L=1, T=2, needles="none")
+    inp = W.gen_all(spec, device="cuda")
+    K = inp["K"]
+    groups = K[0, 0, ::2048].clone()                      # 32 distinct key vectors
+    K[0, 0] = groups.repeat_interleave(2048, dim=0)
+    for p in (0.5, 0.9):
+        res = H.run_gpu(spec, p, inputs=inp)
+        K_u = K[0, 0].cpu().numpy()
+        V_u = inp["V"][0, 0].cpu().numpy()
+        levels = O.build_tree_unit(K_u, inp["R"][0].cpu().numpy(), 4, 1)
+        for t in range(2):
+            r = O.attend_head(inp["Q"][0, t, 0].cpu().numpy(), levels, K_u, V_u, 4, 1, p, 1)
+            n = int(res["cnt"][0, t, 0])
+            assert n == len(r.S), (p, t, n, len(r.S))
+            assert np.array_equal(res["sel"][0, t, 0, :n], r.S)
+            assert np.max(np.abs(res["O"][0, t, 0] - r.O)) < 1e-4
+    Z.attend.last_workspace = None
+
+
 def test_deterministic_repeat():
     spec = W.spec("32k_deep", N=8192, B=2)
     inp = W.gen_all(spec, device="cuda")

@@ -1097,6 +1097,7 @@ struct CutShared {
   unsigned long long cand[kCand];
   unsigned long long radix[256];
   unsigned long long wsum[kCutWaves];
+  uint32_t redu[4][kCutWaves];
   float red[2 * kCutWaves];
   unsigned long long scalar_u64[4];
   uint32_t scalar_u32[4];
@@ -1127,7 +1128,7 @@ __global__ __launch_bounds__(kCutThreads) void wide_cut_kernel(
     int32_t* __restrict__ sel_count, int32_t* __restrict__ lvl_kept, WideSel w) {
   __shared__ CutShared sh;
   const int qh = blockIdx.x;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int u, m;
   unit_member_of(geo, qh, &u, &m);
   const int b = geo.b;
@@ -1211,52 +1212,146 @@ __global__ __launch_bounds__(kCutThreads) void wide_cut_kernel(
         }
       }
       __syncthreads();
-      int P2 = 1;
-      while (P2 < (int)nb) P2 <<= 1;
-      for (int i = nb + tid; i < P2; i += kCutThreads) sh.cand[i] = 0ull;
+      // the exact cut among the gathered candidates: a mass-weighted radix select on the
+      // score ordinal (4 passes of 8 bits) finds the cut score; the candidates tied at it
+      // share one mass, and the first ceil(rest / mass) of them by index are kept
+      constexpr int per = kCand / kCutThreads;
+      uint32_t cord[per], cidx[per];
+      uint64_t cm[per];
+      bool cv[per];
+#pragma unroll
+      for (int i = 0; i < per; ++i) {
+        const int idx = per * tid + i;
+        cv[i] = idx < (int)nb;
+        const uint64_t kk = cv[i] ? sh.cand[idx] : 0ull;
+        cord[i] = (uint32_t)(kk >> 32);
+        cidx[i] = 0xffffffffu - (uint32_t)kk;
+        cm[i] = cv[i] ? mass_fixed(float_of_ord(cord[i]), mx) : 0ull;
+      }
+      uint64_t need = T - before;  // 1 <= need <= the boundary bucket's mass
+      uint32_t prefix = 0u, pbits = 0u;
+      for (int shift = 24; shift >= 0; shift -= 8) {
+        if (tid < 256) sh.radix[tid] = 0ull;
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < per; ++i)
+          if (cv[i] && (cord[i] & pbits) == prefix)
+            atomicAdd(&sh.radix[(cord[i] >> shift) & 255u], (unsigned long long)cm[i]);
+        __syncthreads();
+        if (wave == 0) {
+          // lane l holds digits 255 - 4l .. 252 - 4l (descending); cumulative from the top
+          uint64_t hv[4], loc = 0;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            hv[i] = sh.radix[255 - 4 * lane - i];
+            loc += hv[i];
+          }
+          const uint64_t incl = wave_incl_scan_u64(loc, lane);
+          const uint64_t excl = incl - loc;
+          if (excl < need && incl >= need) {
+            uint64_t run = excl;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              if (run + hv[i] >= need) {
+                sh.scalar_u32[0] = 255u - 4u * lane - i;
+                sh.scalar_u64[1] = run;
+                break;
+              }
+              run += hv[i];
+            }
+          }
+        }
+        __syncthreads();
+        need -= sh.scalar_u64[1];
+        prefix |= sh.scalar_u32[0] << shift;
+        pbits |= 255u << shift;
+      }
+      const uint64_t mcut = mass_fixed(float_of_ord(prefix), mx);
+      const uint64_t ties = (need + mcut - 1) / mcut;
+      // candidates above the cut score, and the tied ones' count / lowest / highest index
+      uint32_t nabove = 0, ntie = 0, imin = 0xffffffffu, imax = 0u;
+#pragma unroll
+      for (int i = 0; i < per; ++i) {
+        nabove += cv[i] && cord[i] > prefix;
+        if (cv[i] && cord[i] == prefix) {
+          ++ntie;
+          imin = min(imin, cidx[i]);
+          imax = max(imax, cidx[i]);
+        }
+      }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        nabove += __shfl_xor(nabove, off, 64);
+        ntie += __shfl_xor(ntie, off, 64);
+        imin = min(imin, (uint32_t)__shfl_xor(imin, off, 64));
+        imax = max(imax, (uint32_t)__shfl_xor(imax, off, 64));
+      }
+      if (lane == 0) {
+        sh.redu[0][wave] = nabove;
+        sh.redu[1][wave] = ntie;
+        sh.redu[2][wave] = imin;
+        sh.redu[3][wave] = imax;
+      }
       __syncthreads();
-      for (int size = 2; size <= P2; size <<= 1) {
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-          for (int i = tid; i < P2; i += kCutThreads) {
-            const int j = i ^ stride;
-            if (j > i) {
-              const unsigned long long x = sh.cand[i], y = sh.cand[j];
-              const bool desc = (i & size) == 0;
-              if (desc ? (x < y) : (x > y)) {
-                sh.cand[i] = y;
-                sh.cand[j] = x;
+      nabove = ntie = imax = 0u;
+      imin = 0xffffffffu;
+#pragma unroll
+      for (int v = 0; v < kCutWaves; ++v) {
+        nabove += sh.redu[0][v];
+        ntie += sh.redu[1][v];
+        imin = min(imin, sh.redu[2][v]);
+        imax = max(imax, sh.redu[3][v]);
+      }
+      uint32_t kc;
+      if (ties <= 1) {
+        kc = imin;
+      } else if (ties >= ntie) {
+        kc = imax;
+      } else {
+        // the ties-th lowest index among the tied candidates: count radix, low digits first
+        uint32_t ip = 0u, ib = 0u, rest = (uint32_t)ties;
+        for (int shift = 24; shift >= 0; shift -= 8) {
+          __syncthreads();
+          if (tid < 256) sh.radix[tid] = 0ull;
+          __syncthreads();
+#pragma unroll
+          for (int i = 0; i < per; ++i)
+            if (cv[i] && cord[i] == prefix && (cidx[i] & ib) == ip)
+              atomicAdd(&sh.radix[(cidx[i] >> shift) & 255u], 1ull);
+          __syncthreads();
+          if (wave == 0) {
+            // lane l holds digits 4l .. 4l + 3 (ascending)
+            uint64_t hv[4], loc = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              hv[i] = sh.radix[4 * lane + i];
+              loc += hv[i];
+            }
+            const uint64_t incl = wave_incl_scan_u64(loc, lane);
+            const uint64_t excl = incl - loc;
+            if (excl < rest && incl >= rest) {
+              uint64_t run = excl;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                if (run + hv[i] >= rest) {
+                  sh.scalar_u32[0] = 4u * lane + i;
+                  sh.scalar_u64[1] = run;
+                  break;
+                }
+                run += hv[i];
               }
             }
           }
           __syncthreads();
+          rest -= (uint32_t)sh.scalar_u64[1];
+          ip |= sh.scalar_u32[0] << shift;
+          ib |= 255u << shift;
         }
+        kc = ip;
       }
-      // cumulative mass in rank order from `before`: two candidates per thread
-      constexpr int per = kCand / kCutThreads;
-      uint64_t mloc[per];
-      uint64_t loc = 0;
-#pragma unroll
-      for (int i = 0; i < per; ++i) {
-        const int idx = per * tid + i;
-        mloc[i] = idx < (int)nb ? mass_fixed(float_of_ord((uint32_t)(sh.cand[idx] >> 32)), mx) : 0ull;
-        loc += mloc[i];
-      }
-      uint64_t tot;
-      const uint64_t cin = cut_block_scan(loc, sh.wsum, &tot) + before;
-      uint64_t run = cin - loc;
-      if (run < T && cin >= T) {
-#pragma unroll
-        for (int i = 0; i < per; ++i) {
-          run += mloc[i];
-          if (run >= T) {
-            sh.scalar_u64[2] = sh.cand[per * tid + i];
-            sh.scalar_u32[3] = (uint32_t)(per * tid + i + 1);
-            break;
-          }
-        }
-      }
+      if (tid == 0) sh.scalar_u32[3] = nabove + (uint32_t)ties;
       __syncthreads();
-      key = sh.scalar_u64[2];
+      key = ((uint64_t)prefix << 32) | (uint64_t)(0xffffffffu - kc);
     } else {
       // boundary bucket too large to sort: exact MSD radix select on the rank key,
       // restricted to the boundary bucket, 8 bits per pass
@@ -1370,27 +1465,38 @@ __global__ __launch_bounds__(kUnionThreads) void wide_union_kernel(
   }
   __syncthreads();
   uint32_t um[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int mm = 0; mm < Mu; ++mm) {
-    const float* Sq = S + (int64_t)qh_of(geo, u, mm) * S_stride + c0 + 4 * tid;
-    // rows are padded to a multiple of 4 and chunks start at multiples of 4, so a float4
-    // that starts below F stays inside the row
-    const float4 a = kk[0] < F ? *reinterpret_cast<const float4*>(Sq) : make_float4(0, 0, 0, 0);
-    const float4 c = kk[4] < F ? *reinterpret_cast<const float4*>(Sq + kUnionChunk / 2)
-                               : make_float4(0, 0, 0, 0);
-    const float sv[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
-    const float sc = s_cut[mm];
-    const uint32_t kc = k_cut[mm];
-    uint32_t n = 0;
+  // members in groups of four, all eight row loads of a group issued together; rows are
+  // padded to a multiple of 4 and chunks start at multiples of 4, so a float4 that starts
+  // below F stays inside the row (past F the row's first float4 is read and ignored)
+  const int off_a = kk[0] < F ? c0 + 4 * tid : 0;
+  const int off_c = kk[4] < F ? c0 + kUnionChunk / 2 + 4 * tid : 0;
+  for (int g0 = 0; g0 < Mu; g0 += 4) {
+    float4 a[4], c[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const bool keep = ((pm[i] >> mm) & 1u) &&
-                        (sv[i] > sc || (sv[i] == sc && (uint32_t)kk[i] <= kc));
-      um[i] |= (uint32_t)keep << mm;
-      n += keep;
+    for (int j = 0; j < 4; ++j) {
+      const float* Sq = S + (int64_t)qh_of(geo, u, min(g0 + j, Mu - 1)) * S_stride;
+      a[j] = *reinterpret_cast<const float4*>(Sq + off_a);
+      c[j] = *reinterpret_cast<const float4*>(Sq + off_c);
     }
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) n += __shfl_xor(n, off, 64);
-    if (lane == 0) cnt[wave][mm] = n;
+    for (int j = 0; j < 4; ++j) {
+      const int mm = g0 + j;
+      if (mm >= Mu) break;
+      const float sv[8] = {a[j].x, a[j].y, a[j].z, a[j].w, c[j].x, c[j].y, c[j].z, c[j].w};
+      const float sc = s_cut[mm];
+      const uint32_t kc = k_cut[mm];
+      uint32_t n = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const bool keep = ((pm[i] >> mm) & 1u) &&
+                          (sv[i] > sc || (sv[i] == sc && (uint32_t)kk[i] <= kc));
+        um[i] |= (uint32_t)keep << mm;
+        n += keep;
+      }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) n += __shfl_xor(n, off, 64);
+      if (lane == 0) cnt[wave][mm] = n;
+    }
   }
   uint32_t nz = 0;
 #pragma unroll
@@ -1506,9 +1612,15 @@ __global__ __launch_bounds__(kUnionThreads) void wide_write_kernel(
       if (kept) {
         const uint32_t at = mpos + (uint32_t)__popcll(bal & ((1ull << lane) - 1ull));
         const int node = (int)s_node[e];
-        for (int c = 0; c < b; ++c) {
-          const int tok = node * b + c;
-          if (tok >= anchor) sel[tok_base + (int64_t)at * b + c] = tok;
+        int32_t* dst = sel + tok_base + (int64_t)at * b;
+        if (b == 4 && node * 4 >= anchor && ((uintptr_t)dst & 15u) == 0) {
+          *reinterpret_cast<int4*>(dst) = make_int4(4 * node, 4 * node + 1, 4 * node + 2,
+                                                    4 * node + 3);
+        } else {
+          for (int c = 0; c < b; ++c) {
+            const int tok = node * b + c;
+            if (tok >= anchor) dst[c] = tok;
+          }
         }
       }
       mpos += (uint32_t)__popcll(bal);
