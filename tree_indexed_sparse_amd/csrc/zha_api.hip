@@ -423,7 +423,7 @@ int zha_attend(const zha_tree* t, const void* Q, int T, int Hq, const void* K, c
     const int n_top = (l == t->L) ? (int)w.n[t->L] : 0;
     const float* X = t->pyramid + t->level_off[l];
     const int64_t frontier_cap = parent ? t->b * parent->stride : n_top;
-    wsel.pent = score_entries(frontier_cap);
+    wsel.pent = score_entries(frontier_cap, g.U);
     const WideSel* wide = select_is_wide(frontier_cap) ? &wsel : nullptr;
     e = timed(ZHA_K_SCORE, l, s, [&] {
       return launch_score(g, X, cap_l * t->d, Q, t->dtype, parent, n_top, S, w.S_stride, wide,

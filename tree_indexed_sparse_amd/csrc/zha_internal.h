@@ -138,7 +138,7 @@ hipError_t launch_score(const Geom& geo, const float* X, int64_t X_unit_stride, 
 // sizes of its scratch for frontiers up to `cap_entries`.
 bool select_is_wide(int64_t cap_entries);
 int64_t wide_partial_stride(int64_t cap_entries);
-int score_entries(int64_t cap_entries);        // frontier entries per score workgroup
+int score_entries(int64_t cap_entries, int units);  // frontier entries per score workgroup
 int64_t wide_chunks(int64_t cap_entries);      // histogram chunks
 int64_t wide_union_chunks(int64_t cap_entries);  // compaction chunks
 int64_t wide_union_stride(int64_t cap_entries);  // umask row length
