@@ -181,7 +181,7 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kTileRows = 64;
 constexpr int kMaxFuse = 6;  // 2^6 = 64 rows
-constexpr int kTilesPerWG = 4;
+constexpr int kTilesPerWG = 1;
 
 struct PoolOut {
   float* ptr[kMaxFuse];
