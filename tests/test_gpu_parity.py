@@ -249,3 +249,59 @@ def test_256k_deep_sampled_units():
     summ = C.summarize(reps)
     _report("256k deep sampled", summ, pyr)
     _assert_ok(spec, summ, pyr)
+
+
+def test_graph_replay_matches_eager():
+    """The whole step (pyramid build + attend) captured as a HIP graph: three replays, with
+    eager library work and synchronisation between them, each equal bit for bit to the
+    eager result."""
+    import ctypes
+    import tree_indexed_sparse_amd as Z
+    from tree_indexed_sparse_amd import _lib as LB
+
+    spec = W.spec("32k_deep", N=65536, B=2)
+    inp = W.gen_all(spec, device="cuda")
+    K, V, Q, R = inp["K"], inp["V"], inp["Q"], inp["R"]
+    B, T, Hq, Hkv, d, N, b, L = (spec[k] for k in ("B", "T", "Hq", "Hkv", "d", "N", "b", "L"))
+    lib = Z.load()
+    tree = Z.build_tree(K, R, b, L)
+    O = torch.empty((B, T, Hq, d), dtype=torch.float32, device="cuda")
+    sel = torch.full((B, T, Hq, N), -1, dtype=torch.int32, device="cuda")
+    cnt = torch.empty((B, T, Hq), dtype=torch.int32, device="cuda")
+    ws = torch.empty(Z.workspace_bytes(tree, T, Hq), dtype=torch.uint8, device="cuda")
+    c_tree = tree.c
+
+    def step():
+        LB.check(lib.zha_build_tree(K.data_ptr(), R.data_ptr(), c_tree.dtype, B, Hkv, N, N, d, b,
+                                    L, tree.storage.data_ptr(), tree.storage.numel(),
+                                    ctypes.byref(c_tree), torch.cuda.current_stream().cuda_stream))
+        Z.attend(Q, K, V, tree, 0.95, 1, out=O, sel_idx=sel, sel_count=cnt, workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    ref = (O.clone(), sel.clone(), cnt.clone(), tree.storage.clone())
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for i in range(3):
+        # eager work in between: a different p into the same buffers, then garbage
+        Z.attend(Q, K, V, tree, 0.5, 1, out=O, sel_idx=sel, sel_count=cnt, workspace=ws)
+        O.fill_(float("nan"))
+        cnt.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(tree.storage, ref[3]), i
+        assert torch.equal(cnt, ref[2]), i
+        assert torch.equal(O, ref[0]), i
+        n = cnt.cpu().numpy()
+        s_now, s_ref = sel.cpu().numpy(), ref[1].cpu().numpy()
+        for idx in np.ndindex(*n.shape):
+            assert np.array_equal(s_now[idx][:n[idx]], s_ref[idx][:n[idx]]), (i, idx)
+    Z.attend.last_workspace = None
