@@ -127,6 +127,20 @@ int zha_attend(const zha_tree* t, const void* Q, int T, int Hq, const void* K, c
                int32_t* sel_count, void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * Dense comparator: exact softmax attention of every query head over all N cached keys of
+ * its KV head, with the same decode and combine kernels zha_attend uses (every member
+ * reads every token; there is no tree and no search). It is what the tree-indexed path is
+ * measured against (page 3, paragraph 4: the pages' speedups are relative to dense
+ * attention). Q, K, V, O and the workspace as for zha_attend; the shapes are given
+ * directly. 1 <= N <= N_cap, N <= 2^21, d in {64, 128}, Hq % Hkv == 0, Hq / Hkv <= 16.
+ * zha_dense_workspace_bytes returns 0 for an invalid shape.
+ */
+size_t zha_dense_workspace_bytes(int B, int Hkv, int N, int N_cap, int d, int T, int Hq);
+int zha_dense_attend(const void* Q, int T, int Hq, const void* K, const void* V, int dtype,
+                     int B, int Hkv, int N, int N_cap, int d, float* O, void* workspace,
+                     size_t ws_bytes, void* stream);
+
+/*
  * Diagnostics of the last zha_attend that used `workspace` (valid once it completed).
  * The G = Hq / Hkv heads of one KV head (and up to 16 / G queries of one sequence) form a
  * "unit" that shares one union list per level: unit u = ((b * Hkv + g) * nTB + tb), with

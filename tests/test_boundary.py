@@ -138,3 +138,25 @@ def test_level_view_offsets_are_inside_the_workspace(lib):
         assert max(o_n, o_m) + 4 * units * stride <= need and o_c + 4 * units <= need
     assert lib.zha_attend_level_view(ctypes.byref(t), 3, 8, 4,
                                      *[ctypes.byref(v) for v in vals]) == -1
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Q=None), -1), (dict(O=None), -1), (dict(ws=None), -1), (dict(K=ODD8), -1),
+    (dict(dtype=5), -3), (dict(d=80), -5), (dict(N=0), -2), (dict(N=5000), -2),
+    (dict(Hq=7), -2), (dict(Hq=64), -5), (dict(wsb=1024), -2), (dict(B=0), -2),
+])
+def test_dense_rejects_bad_arguments(lib, kw, code):
+    a = dict(Q=FAKE, T=1, Hq=8, K=FAKE, V=FAKE, dtype=1, B=1, Hkv=2, N=4096, N_cap=4096, d=64,
+             O=FAKE, ws=FAKE, wsb=1 << 40)
+    a.update(kw)
+    assert lib.zha_dense_attend(a["Q"], a["T"], a["Hq"], a["K"], a["V"], a["dtype"], a["B"],
+                                a["Hkv"], a["N"], a["N_cap"], a["d"], a["O"], a["ws"], a["wsb"],
+                                None) == code
+    assert len(lib.zha_last_error()) > 0
+
+
+def test_dense_workspace_bytes(lib):
+    n = lib.zha_dense_workspace_bytes(4, 4, 262144, 262144, 128, 1, 32)
+    assert n >= 2 * 4 * 16 * 262144
+    assert lib.zha_dense_workspace_bytes(1, 1, 0, 4096, 64, 1, 1) == 0
+    assert lib.zha_dense_workspace_bytes(1, 1, 4096, 4096, 96, 1, 1) == 0

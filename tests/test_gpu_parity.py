@@ -305,3 +305,40 @@ def test_graph_replay_matches_eager():
         for idx in np.ndindex(*n.shape):
             assert np.array_equal(s_now[idx][:n[idx]], s_ref[idx][:n[idx]]), (i, idx)
     Z.attend.last_workspace = None
+
+
+@pytest.mark.parametrize("case", [
+    dict(name="tiny fp32, N not a multiple of any tile", wl="tiny", N=4000, N_cap=4096),
+    dict(name="32k bf16 G8", wl="32k_deep", B=2),
+    dict(name="bf16 d64, T3 G4", wl="32k_deep", B=1, d=64, T=3, Hq=8, Hkv=2, N=8192),
+])
+def test_dense_comparator(case):
+    """zha_dense_attend: every query head attends over all N keys of its KV head."""
+    import tree_indexed_sparse_amd as Z
+    import oracle as O
+
+    case = dict(case)
+    name = case.pop("name")
+    wl = case.pop("wl")
+    N_cap = case.pop("N_cap", None)
+    spec = W.spec(wl, **case)
+    if N_cap is not None:
+        spec["N"] = N_cap
+    inp = W.gen_all(spec, device="cuda")
+    N = case.get("N", spec["N"])
+    out = Z.dense_attend(inp["Q"], inp["K"], inp["V"], N)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    Q = inp["Q"].float().cpu().numpy()
+    K = inp["K"].float().cpu().numpy()
+    V = inp["V"].float().cpu().numpy()
+    G = spec["Hq"] // spec["Hkv"]
+    err = 0.0
+    S = np.arange(N)
+    for b in range(spec["B"]):
+        for t in range(spec["T"]):
+            for h in range(spec["Hq"]):
+                ref = O.attention_over(Q[b, t, h], K[b, h // G], V[b, h // G], S)
+                err = max(err, float(np.max(np.abs(got[b, t, h] - ref))))
+    print(f"[dense {name}] max |O - oracle| {err:.2e}", flush=True)
+    assert err <= O_TOL[spec["dtype"]], err

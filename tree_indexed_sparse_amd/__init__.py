@@ -130,6 +130,31 @@ def attend(Q, K, V, tree: Tree, p: float, anchor: int = 1, *, want_lists: bool =
     return out, sel_idx, sel_count
 
 
+def dense_workspace_bytes(B: int, Hkv: int, N: int, N_cap: int, d: int, T: int, Hq: int) -> int:
+    return int(load().zha_dense_workspace_bytes(B, Hkv, N, N_cap, d, T, Hq))
+
+
+def dense_attend(Q, K, V, N: int | None = None, *, out=None, workspace=None):
+    """zha_dense_attend: exact attention over all N cached keys (the dense comparator).
+    K, V [B,Hkv,N_cap,d]; returns O [B,T,Hq,d] float32."""
+    lib = load()
+    B, T, Hq, d = Q.shape
+    _, Hkv, N_cap, _ = K.shape
+    N = N_cap if N is None else N
+    dev = Q.device
+    if Q.dtype != K.dtype or V.dtype != K.dtype:
+        raise ZhaError(-3, "Q, K and V must share a dtype")
+    if out is None:
+        out = torch.empty((B, T, Hq, d), dtype=torch.float32, device=dev)
+    need = dense_workspace_bytes(B, Hkv, N, N_cap, d, T, Hq)
+    if workspace is None:
+        workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=dev)
+    check(lib.zha_dense_attend(_dev(Q, "Q"), T, Hq, _dev(K, "K"), _dev(V, "V"), _dt(K), B, Hkv,
+                               N, N_cap, d, _dev(out, "O"), _dev(workspace, "workspace"),
+                               workspace.numel(), _stream(dev)))
+    return out
+
+
 def level_view(tree: Tree, T: int, Hq: int, level: int, workspace: torch.Tensor):
     """Per-level union lists a finished zha_attend left in `workspace`:
     (nodes [U, stride] int64, masks [U, stride] int64, count [U] int64) on the host."""

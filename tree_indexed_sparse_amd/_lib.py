@@ -35,6 +35,8 @@ EXPORTS = (
     "zha_attend_workspace_bytes",
     "zha_attend",
     "zha_attend_level_view",
+    "zha_dense_workspace_bytes",
+    "zha_dense_attend",
     "zha_timing_enable",
     "zha_timing_read",
     "zha_last_error",
@@ -95,6 +97,11 @@ def load() -> ctypes.CDLL:
     lib.zha_attend_level_view.argtypes = [P(ZhaTree), i32, i32, i32, P(i64), P(i64), P(i64),
                                           P(i64), P(i64)]
     lib.zha_attend_level_view.restype = i32
+    lib.zha_dense_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+    lib.zha_dense_workspace_bytes.restype = sz
+    lib.zha_dense_attend.argtypes = [vp, i32, i32, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp,
+                                     sz, vp]
+    lib.zha_dense_attend.restype = i32
     lib.zha_timing_enable.argtypes = [i32]
     lib.zha_timing_enable.restype = i32
     lib.zha_timing_read.argtypes = [i32, i32, P(ctypes.c_double), P(i64)]

@@ -329,6 +329,89 @@ size_t zha_attend_workspace_bytes(const zha_tree* t, int T, int Hq) {
   return (size_t)layout_of(g).total;
 }
 
+// ---- dense comparator: the decode kernels over every cached key, no search
+namespace {
+struct DenseLayout {
+  int64_t off_nodes, off_masks, off_count, off_part, total;
+  int splits;
+};
+int dense_geom(int B, int Hkv, int N, int N_cap, int d, int T, int Hq, Geom* g) {
+  if (B < 1 || Hkv < 1) return fail(ZHA_ERR_SHAPE, "B and Hkv must be >= 1 (got %d, %d)", B, Hkv);
+  if (d != 64 && d != 128) return fail(ZHA_ERR_UNSUPPORTED, "head dim must be 64 or 128 (got %d)", d);
+  if (N < 1 || N > N_cap) return fail(ZHA_ERR_SHAPE, "N=%d must lie in [1, N_cap=%d]", N, N_cap);
+  if (N > (1 << kMaxLog2Nodes))
+    return fail(ZHA_ERR_UNSUPPORTED, "N must be <= 2^%d", kMaxLog2Nodes);
+  zha_tree t{};
+  t.B = B;
+  t.Hkv = Hkv;
+  t.N = N;
+  t.N_cap = N_cap;
+  t.d = d;
+  t.b = 1;
+  t.L = 1;
+  return make_geom(&t, T, Hq, g);
+}
+DenseLayout dense_layout(const Geom& g) {
+  DenseLayout w{};
+  w.splits = (2048 + g.U - 1) / g.U;
+  if (w.splits > kMaxSplits) w.splits = kMaxSplits;
+  int64_t off = 0;
+  w.off_nodes = off;
+  off = align256(off + 4 * (int64_t)g.U * g.N);
+  w.off_masks = off;
+  off = align256(off + 4 * (int64_t)g.U * g.N);
+  w.off_count = off;
+  off = align256(off + 4 * (int64_t)g.U);
+  w.off_part = off;
+  off = align256(off + 4 * (int64_t)g.U * w.splits * kMaxMembers * (g.D + 2));
+  w.total = off;
+  return w;
+}
+}  // namespace
+
+size_t zha_dense_workspace_bytes(int B, int Hkv, int N, int N_cap, int d, int T, int Hq) {
+  const std::string saved = g_err;
+  Geom g;
+  const int st = dense_geom(B, Hkv, N, N_cap, d, T, Hq, &g);
+  g_err = saved;
+  if (st != ZHA_OK) return 0;
+  return (size_t)dense_layout(g).total;
+}
+
+int zha_dense_attend(const void* Q, int T, int Hq, const void* K, const void* V, int dtype,
+                     int B, int Hkv, int N, int N_cap, int d, float* O, void* workspace,
+                     size_t ws_bytes, void* stream) {
+  if (!Q || !K || !V || !O || !workspace)
+    return fail(ZHA_ERR_INVALID_ARG, "Q, K, V, O and workspace must not be NULL");
+  if (dtype != ZHA_F32 && dtype != ZHA_BF16) return fail(ZHA_ERR_DTYPE, "unknown dtype %d", dtype);
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) ||
+      ((uintptr_t)workspace & 255u) != 0)
+    return fail(ZHA_ERR_INVALID_ARG,
+                "Q, K, V and O must be 16-byte aligned and the workspace 256-byte aligned");
+  Geom g;
+  int st = dense_geom(B, Hkv, N, N_cap, d, T, Hq, &g);
+  if (st != ZHA_OK) return st;
+  const DenseLayout w = dense_layout(g);
+  if ((int64_t)ws_bytes < w.total)
+    return fail(ZHA_ERR_SHAPE, "workspace has %zu bytes, needs %lld", ws_bytes,
+                (long long)w.total);
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  LevelBufs l1;
+  l1.nodes = (uint32_t*)(ws + w.off_nodes);
+  l1.masks = (uint32_t*)(ws + w.off_masks);
+  l1.count = (uint32_t*)(ws + w.off_count);
+  l1.stride = g.N;
+  float* part = (float*)(ws + w.off_part);
+  hipError_t e = timed(ZHA_K_DECODE, 1, s, [&] { return launch_dense_list(g, l1, s); });
+  if (e != hipSuccess) return hip_fail(e, "dense list launch");
+  e = timed(ZHA_K_DECODE, 0, s, [&] { return launch_decode(g, dtype, K, V, Q, l1, 0, w.splits, part, s); });
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  e = timed(ZHA_K_COMBINE, 0, s, [&] { return launch_combine(g, w.splits, part, O, s); });
+  if (e != hipSuccess) return hip_fail(e, "combine launch");
+  return ZHA_OK;
+}
+
 int zha_attend_level_view(const zha_tree* t, int T, int Hq, int level, int64_t* off_nodes,
                           int64_t* off_masks, int64_t* off_count, int64_t* stride,
                           int64_t* units) {

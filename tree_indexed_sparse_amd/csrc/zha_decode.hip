@@ -464,6 +464,25 @@ __global__ __launch_bounds__(kDecThreads) void decode_mfma_kernel(
 
 }  // namespace
 
+namespace {
+// Dense work list: token j is node j (b = 1) and every member reads it.
+__global__ __launch_bounds__(256) void dense_list_kernel(Geom geo, LevelBufs l1) {
+  const int u = blockIdx.y;
+  const int j = blockIdx.x * 256 + threadIdx.x;
+  if (j < geo.N) {
+    l1.nodes[u * l1.stride + j] = (uint32_t)j;
+    l1.masks[u * l1.stride + j] = (1u << members_of(geo, u)) - 1u;
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) l1.count[u] = (uint32_t)geo.N;
+}
+}  // namespace
+
+hipError_t launch_dense_list(const Geom& geo, const LevelBufs& l1, hipStream_t s) {
+  hipLaunchKernelGGL(dense_list_kernel, dim3((geo.N + 255) / 256, geo.U), dim3(256), 0, s, geo,
+                     l1);
+  return hipGetLastError();
+}
+
 hipError_t launch_decode(const Geom& geo, int dtype, const void* K, const void* V,
                          const void* Q, const LevelBufs& l1, int anchor, int splits,
                          float* partials, hipStream_t s) {

@@ -173,6 +173,9 @@ hipError_t launch_union(const Geom& geo, int level, const float* S, int64_t S_st
                         int32_t* sel_idx, int64_t cap, const WideSel& wide, hipStream_t s);
 int64_t compact_counter_words(int U, int64_t n);
 
+// Work list of dense attention (geo.b = 1): nodes[u][j] = j with every member's bit.
+hipError_t launch_dense_list(const Geom& geo, const LevelBufs& l1, hipStream_t s);
+
 hipError_t launch_decode(const Geom& geo, int dtype, const void* K, const void* V,
                          const void* Q, const LevelBufs& l1, int anchor, int splits,
                          float* partials, hipStream_t s);
