@@ -164,6 +164,31 @@ def main():
         print(f"# graph step {ms_step:.3f} ms (wall {wall_step:.3f} ms)", file=sys.stderr,
               flush=True)
 
+    # dense comparator (every head over all N keys, same decode kernels) and the build:
+    # one shot versus whole-top-node appends
+    dws = torch.empty(Z.dense_workspace_bytes(B, Hkv, N, N, d, T, Hq), dtype=torch.uint8,
+                      device=dev)
+    O_dense = torch.empty_like(O)
+
+    def dense():
+        Z.dense_attend(Q, K, V, N, out=O_dense, workspace=dws)
+
+    dense()
+    ms_dense, _ = timed(dense, args.steps)
+    top = b ** L
+    n_app = N // top
+
+    def appends():
+        c_tree.N = 0
+        for i in range(n_app):
+            LB.check(lib.zha_tree_append(ctypes.byref(c_tree), K.data_ptr(), R.data_ptr(), top,
+                                         torch.cuda.current_stream().cuda_stream))
+
+    appends()
+    ms_appends, _ = timed(appends, max(1, args.steps // 4))
+    ms_build, _ = timed(build_into, args.steps)
+    torch.cuda.synchronize()
+
     # per-kernel durations: HIP events the library records around each of its launches
     lib.zha_timing_enable(1)
     ms_timed_pass, _ = timed(full_step, args.steps)
@@ -280,6 +305,13 @@ def main():
                         "alg_bytes": attend_alg,
                         "alg_gbs": round(attend_alg / (ms_attend * 1e-3) / 1e9, 1),
                         "hbm_frac": round(attend_alg / (ms_attend * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "dense": {"ms": round(ms_dense, 4),
+                  "kv_gbs": round(B * Hkv * N * 2 * d * elem / (ms_dense * 1e-3) / 1e9, 1),
+                  "query_heads_per_s": round(QH / (ms_dense * 1e-3), 1),
+                  "speedup_of_attend": round(ms_dense / ms_attend, 3)},
+        "build": {"oneshot_ms": round(ms_build, 4), "appends": n_app,
+                  "appends_ms": round(ms_appends, 4),
+                  "oneshot_in_dense_decodes": round(ms_build / ms_dense, 3)},
         "step_alg_gbs": round(step_alg / (ms_step * 1e-3) / 1e9, 1),
         "step_hbm_frac": round(step_alg / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "keys_read_pct": keys,

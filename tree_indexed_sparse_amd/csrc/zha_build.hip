@@ -506,6 +506,150 @@ __global__ __launch_bounds__(kPoolThreads) void pool_wave_b4_kernel(
   }
 }
 
+// ------------------------------------------------------------------------------------
+// Wide nodes (64 < b <= 256) over bf16 keys: one workgroup per node, wave w owns children
+// 64 w .. 64 w + 63, loaded straight into the A operand of v_mfma_f32_16x16x32_bf16
+// (z = tau R x^T, 16 children x 16 references per block). Each reference's softmax max
+// and normaliser over all b children combine across the four waves through LDS; each
+// child's weight (mean over references) is formed on the MFMA C layout, moved to the
+// A-layout lanes by shuffles, and the weighted sum of the wave's children is reduced
+// across lanes and then across waves in a fixed order.
+constexpr int kWideNodeMax = 256;
+
+template <int D>
+__global__ __launch_bounds__(kPoolThreads) void pool_wide_kernel(
+    const bf16_t* __restrict__ child, int64_t in_unit_stride, const bf16_t* __restrict__ Rall,
+    float* __restrict__ out, int64_t out_unit_stride, int Hkv, int node_begin, int node_end,
+    int b, float tau) {
+  constexpr int KC = D / 32;
+  constexpr int NW = kPoolThreads / 64;
+  __shared__ float sMax[NW][kNRef], sSum[NW][kNRef];
+  __shared__ float sPart[NW][D];
+  const int unit = blockIdx.y;
+  const int node = node_begin + blockIdx.x;
+  if (node >= node_end) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int mem = lane & 15, grp = lane >> 4;
+  const bf16_t* R = Rall + (int64_t)(unit % Hkv) * kNRef * D;
+  bf16x8_t rb[KC];
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc)
+    rb[kc] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(R + mem * D + 32 * kc + 8 * grp));
+
+  // child rows c = 64 wave + 16 blk + mem (rows at or past b: row 0, masked)
+  const bf16_t* base = child + unit * in_unit_stride + (int64_t)node * b * D;
+  uint4 a[4][KC];
+#pragma unroll
+  for (int blk = 0; blk < 4; ++blk) {
+    const int c = 64 * wave + 16 * blk + mem;
+    const bf16_t* row = base + (int64_t)(c < b ? c : 0) * D + 8 * grp;
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) a[blk][kc] = *reinterpret_cast<const uint4*>(row + 32 * kc);
+  }
+  // z for rows 16 blk + 4 grp + r and reference `mem`
+  float z[4][4];
+#pragma unroll
+  for (int blk = 0; blk < 4; ++blk) {
+    f32x4_t zc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc)
+      zc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[blk][kc]),
+                                                   rb[kc], zc, 0, 0, 0);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int c = 64 * wave + 16 * blk + 4 * grp + r;
+      z[blk][r] = c < b ? tau * zc[r] : -INFINITY;
+    }
+  }
+  // per-reference max and normaliser over all children
+  float m = -INFINITY;
+#pragma unroll
+  for (int blk = 0; blk < 4; ++blk)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) m = fmaxf(m, z[blk][r]);
+  m = fmaxf(m, __shfl_xor(m, 16, 64));
+  m = fmaxf(m, __shfl_xor(m, 32, 64));
+  if (grp == 0) sMax[wave][mem] = m;
+  __syncthreads();
+  float M = sMax[0][mem];
+#pragma unroll
+  for (int v = 1; v < NW; ++v) M = fmaxf(M, sMax[v][mem]);
+  float e[4][4], ssum = 0.f;
+#pragma unroll
+  for (int blk = 0; blk < 4; ++blk)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      e[blk][r] = expf(z[blk][r] - M);
+      ssum += e[blk][r];
+    }
+  ssum += __shfl_xor(ssum, 16, 64);
+  ssum += __shfl_xor(ssum, 32, 64);
+  if (grp == 0) sSum[wave][mem] = ssum;
+  __syncthreads();
+  float S = 0.f;
+#pragma unroll
+  for (int v = 0; v < NW; ++v) S += sSum[v][mem];
+  // weight of rows 16 blk + 4 grp + r: mean over the 16 references (lanes mem = 0..15)
+  float w[4][4];
+#pragma unroll
+  for (int blk = 0; blk < 4; ++blk)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float t = e[blk][r] / S;
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) t += __shfl_xor(t, off, 64);
+      w[blk][r] = t * (1.f / kNRef);
+    }
+  // this lane's A row is 16 blk + mem: its weight sits in lanes of group mem / 4, entry
+  // mem % 4
+  float acc[KC][8];
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[kc][i] = 0.f;
+#pragma unroll
+  for (int blk = 0; blk < 4; ++blk) {
+    const int src = 16 * (mem >> 2);
+    const float w0 = __shfl(w[blk][0], src, 64), w1 = __shfl(w[blk][1], src, 64);
+    const float w2 = __shfl(w[blk][2], src, 64), w3 = __shfl(w[blk][3], src, 64);
+    const int rsel = mem & 3;
+    const float wr = rsel == 0 ? w0 : (rsel == 1 ? w1 : (rsel == 2 ? w2 : w3));
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      const uint4 v = a[blk][kc];
+      const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[kc][2 * i] = fmaf(wr, __uint_as_float(wd[i] << 16), acc[kc][2 * i]);
+        acc[kc][2 * i + 1] = fmaf(wr, __uint_as_float(wd[i] & 0xffff0000u), acc[kc][2 * i + 1]);
+      }
+    }
+  }
+  // sum over the 16 rows (lanes mem = 0..15) of each group: dims 32 kc + 8 grp + i
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float t = acc[kc][i];
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) t += __shfl_xor(t, off, 64);
+      acc[kc][i] = t;
+    }
+  if (mem == 0) {
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sPart[wave][32 * kc + 8 * grp + i] = acc[kc][i];
+  }
+  __syncthreads();
+  for (int k = threadIdx.x; k < D; k += kPoolThreads) {
+    float t = sPart[0][k];
+#pragma unroll
+    for (int v = 1; v < NW; ++v) t += sPart[v][k];
+    out[unit * out_unit_stride + (int64_t)node * D + k] = t;
+  }
+}
+
 template <int D>
 hipError_t launch_wave_b4(const void* child, int64_t in_unit_stride, const void* R,
                           const PoolOut& out, int nlev, int units, int Hkv, int row_begin,
@@ -533,6 +677,12 @@ hipError_t launch_pool_t(const void* child, int64_t in_unit_stride, const void* 
     hipLaunchKernelGGL((pool_small_kernel<Tin, Tr, D>), grid, dim3(kPoolThreads), 0, s,
                        (const Tin*)child, in_unit_stride, (const Tr*)R, out, out_unit_stride,
                        Hkv, node_begin, node_end, b, tau);
+  } else if (sizeof(Tin) == 2 && sizeof(Tr) == 2 && b <= kWideNodeMax) {
+    // bf16 keys: the wave-centric wide-node kernel
+    dim3 grid(nodes, units);
+    hipLaunchKernelGGL((pool_wide_kernel<D>), grid, dim3(kPoolThreads), 0, s,
+                       (const bf16_t*)child, in_unit_stride, (const bf16_t*)R, out,
+                       out_unit_stride, Hkv, node_begin, node_end, b, tau);
   } else {
     dim3 grid(nodes, units);
     hipLaunchKernelGGL((pool_large_kernel<Tin, Tr, D>), grid, dim3(kPoolThreads), 0, s,
