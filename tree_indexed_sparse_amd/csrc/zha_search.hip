@@ -669,10 +669,27 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     if (tid < words) kbits[t0 / 32 + tid] = sh.tile_bits[tid];
     if (level == 1 && sel) {
       const int ntok = (int)tile_total * b;
-      for (int i = tid; i < ntok; i += kSelThreads) {
-        const int rr = (int)geo.bdiv.div((uint32_t)i), c = i - rr * b;
-        const int tok = (int)sh.tile_nodes[rr] * b + c;
-        if (tok >= anchor) sel[anchor + (int64_t)(running + rr) * b + c - dup] = tok;
+      int32_t* dst0 = sel + anchor - dup + (int64_t)running * b;
+      if ((b & 3) == 0) {
+        // four tokens of one node per 16-byte store where the run is aligned and past the
+        // anchor
+        for (int i = 4 * tid; i < ntok; i += 4 * kSelThreads) {
+          const int rr = (int)geo.bdiv.div((uint32_t)i), c = i - rr * b;
+          const int tok = (int)sh.tile_nodes[rr] * b + c;
+          int32_t* dst = dst0 + (int64_t)rr * b + c;
+          if (tok >= anchor && ((uintptr_t)dst & 15u) == 0) {
+            *reinterpret_cast<int4*>(dst) = make_int4(tok, tok + 1, tok + 2, tok + 3);
+          } else {
+            for (int j = 0; j < 4; ++j)
+              if (tok + j >= anchor) dst[j] = tok + j;
+          }
+        }
+      } else {
+        for (int i = tid; i < ntok; i += kSelThreads) {
+          const int rr = (int)geo.bdiv.div((uint32_t)i), c = i - rr * b;
+          const int tok = (int)sh.tile_nodes[rr] * b + c;
+          if (tok >= anchor) dst0[(int64_t)rr * b + c] = tok;
+        }
       }
     }
     __syncthreads();
@@ -1613,9 +1630,11 @@ __global__ __launch_bounds__(kUnionThreads) void wide_write_kernel(
         const uint32_t at = mpos + (uint32_t)__popcll(bal & ((1ull << lane) - 1ull));
         const int node = (int)s_node[e];
         int32_t* dst = sel + tok_base + (int64_t)at * b;
-        if (b == 4 && node * 4 >= anchor && ((uintptr_t)dst & 15u) == 0) {
-          *reinterpret_cast<int4*>(dst) = make_int4(4 * node, 4 * node + 1, 4 * node + 2,
-                                                    4 * node + 3);
+        if ((b & 3) == 0 && node * b >= anchor && ((uintptr_t)dst & 15u) == 0) {
+          for (int c = 0; c < b; c += 4) {
+            const int tok = node * b + c;
+            *reinterpret_cast<int4*>(dst + c) = make_int4(tok, tok + 1, tok + 2, tok + 3);
+          }
         } else {
           for (int c = 0; c < b; ++c) {
             const int tok = node * b + c;
