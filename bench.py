@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--cpu-units", type=int, default=16,
                     help="(sequence, KV head) units the CPU oracle baseline runs on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the dense comparator and the append-build timings (profiling "
+                         "runs: every decode dispatch is then the tree-indexed attend's)")
     ap.add_argument("--no-graph", action="store_true",
                     help="time eager launches only (by default the step is also captured as a "
                          "HIP graph and its replays are the headline timing)")
@@ -173,10 +176,12 @@ def main():
     def dense():
         Z.dense_attend(Q, K, V, N, out=O_dense, workspace=dws)
 
-    dense()
-    ms_dense, _ = timed(dense, args.steps)
     top = b ** L
     n_app = N // top
+    ms_dense = ms_appends = float("nan")
+    if not args.no_extras:
+        dense()
+        ms_dense, _ = timed(dense, args.steps)
 
     def appends():
         c_tree.N = 0
@@ -184,8 +189,9 @@ def main():
             LB.check(lib.zha_tree_append(ctypes.byref(c_tree), K.data_ptr(), R.data_ptr(), top,
                                          torch.cuda.current_stream().cuda_stream))
 
-    appends()
-    ms_appends, _ = timed(appends, max(1, args.steps // 4))
+    if not args.no_extras:
+        appends()
+        ms_appends, _ = timed(appends, max(1, args.steps // 4))
     ms_build, _ = timed(build_into, args.steps)
     torch.cuda.synchronize()
 
@@ -305,13 +311,15 @@ def main():
                         "alg_bytes": attend_alg,
                         "alg_gbs": round(attend_alg / (ms_attend * 1e-3) / 1e9, 1),
                         "hbm_frac": round(attend_alg / (ms_attend * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
-        "dense": {"ms": round(ms_dense, 4),
-                  "kv_gbs": round(B * Hkv * N * 2 * d * elem / (ms_dense * 1e-3) / 1e9, 1),
-                  "query_heads_per_s": round(QH / (ms_dense * 1e-3), 1),
-                  "speedup_of_attend": round(ms_dense / ms_attend, 3)},
+        "dense": None if args.no_extras else {
+            "ms": round(ms_dense, 4),
+            "kv_gbs": round(B * Hkv * N * 2 * d * elem / (ms_dense * 1e-3) / 1e9, 1),
+            "query_heads_per_s": round(QH / (ms_dense * 1e-3), 1),
+            "speedup_of_attend": round(ms_dense / ms_attend, 3)},
         "build": {"oneshot_ms": round(ms_build, 4), "appends": n_app,
-                  "appends_ms": round(ms_appends, 4),
-                  "oneshot_in_dense_decodes": round(ms_build / ms_dense, 3)},
+                  "appends_ms": None if args.no_extras else round(ms_appends, 4),
+                  "oneshot_in_dense_decodes":
+                      None if args.no_extras else round(ms_build / ms_dense, 3)},
         "step_alg_gbs": round(step_alg / (ms_step * 1e-3) / 1e9, 1),
         "step_hbm_frac": round(step_alg / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "keys_read_pct": keys,
