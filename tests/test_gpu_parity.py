@@ -342,3 +342,24 @@ def test_dense_comparator(case):
                 err = max(err, float(np.max(np.abs(got[b, t, h] - ref))))
     print(f"[dense {name}] max |O - oracle| {err:.2e}", flush=True)
     assert err <= O_TOL[spec["dtype"]], err
+
+
+@pytest.mark.parametrize("p", [0.8, 0.99])
+def test_256k_wide_sampled_units(p):
+    """The wide tree (b = 256, L = 1) at full size, as the benchmark runs it; two units."""
+    spec = W.spec("256k_wide")
+    res = H.run_gpu(spec, p)
+    reps, pyr = H.check_units(spec, res, p, units=[(1, 0), (2, 3)])
+    summ = C.summarize(reps)
+    _report(f"256k wide sampled p={p}", summ, pyr)
+    _assert_ok(spec, summ, pyr)
+
+
+def test_1m_deep_sampled_units():
+    """1M keys, b = 4, L = 7, B = 8 (the benchmark's launch configuration); two units."""
+    spec = W.spec("1m_deep")
+    res = H.run_gpu(spec, 0.95)
+    reps, pyr = H.check_units(spec, res, 0.95, units=[(0, 0), (7, 2)])
+    summ = C.summarize(reps)
+    _report("1m deep sampled", summ, pyr)
+    _assert_ok(spec, summ, pyr)
