@@ -280,9 +280,20 @@ def main():
 
     copy_gbs = copy_probe(torch, dev)
 
-    cpu = None
+    # needle recall: each planted key, in the selected list of the query head aimed at it
+    sel_h = sel.cpu().numpy()
+    cnt_h = cnt.cpu().numpy()
+    hits = total = 0
+    for bb in range(B):
+        for pos, t, h in W.needle_plan(spec, bb):
+            total += 1
+            hits += int(pos in set(sel_h[bb, t, h, :cnt_h[bb, t, h]].tolist()))
+    needles = {"planted": total, "kept_by_aimed_head": hits,
+               "recall": round(hits / total, 4) if total else None}
+
+    cpu = near_ties = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(spec, p, anchor, args.cpu_units)
+        cpu, near_ties = cpu_baseline(spec, p, anchor, args.cpu_units)
 
     qhs = QH / (ms_step * 1e-3)
     out = {
@@ -306,6 +317,8 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "needles": needles,
+        "near_ties": near_ties,
         "decode_only": {"ms": round(ms_attend, 4), "eager_ms": round(ms_attend_eager, 4),
                         "query_heads_per_s": round(QH / (ms_attend * 1e-3), 1),
                         "alg_bytes": attend_alg,
@@ -395,20 +408,27 @@ def cpu_baseline(spec, p, anchor, n_units):
     threads = max([i.get("num_threads", 1) for i in info] or [1])
     t0 = time.perf_counter()
     heads = 0
+    results = []
     for (bb, g) in units:
         K_u, V_u = data[(bb, g)]
         levels = O.build_tree_unit(K_u, R[g], spec["b"], spec["L"])
         for t in range(spec["T"]):
             for h in range(g * G, (g + 1) * G):
-                O.attend_head(Q[bb, t, h], levels, K_u, V_u, spec["b"], spec["L"], p, anchor)
+                results.append(O.attend_head(Q[bb, t, h], levels, K_u, V_u, spec["b"],
+                                             spec["L"], p, anchor))
                 heads += 1
     sec = time.perf_counter() - t0
+    decisions = sum(len(r.levels) for r in results)
+    fragile = sum(1 for r in results for lv in r.levels if lv.fragile)
+    ties = {"decisions": decisions, "fragile_decisions": fragile,
+            "heads_with_any": sum(1 for r in results if r.fragile),
+            "heads": heads, "sample": "the oracle's own decisions on the cpu_baseline units"}
     return {"value": round(heads / sec, 3), "unit": "query-heads/s", "cores": threads,
             "kind": "oracle",
             "sample": f"{n_units} (sequence, KV head) units = {heads} query heads of "
                       f"{spec['name']}, full path per unit (pyramid build + descent + "
                       f"attention), {sec:.1f}s",
-            "cpu": cpu_model()}
+            "cpu": cpu_model()}, ties
 
 
 def cpu_model():
