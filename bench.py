@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--cpu-units", type=int, default=16,
                     help="(sequence, KV head) units the CPU oracle baseline runs on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="geometry sweep on the workload's tensors instead of the benchmark: "
+                         "keys read, retained attention mass and needle recall per (b, L, p)")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the dense comparator and the append-build timings (profiling "
                          "runs: every decode dispatch is then the tree-indexed attend's)")
@@ -71,6 +74,8 @@ def kernel_sources_sha(kernel=None) -> str:
 
 def main():
     args = parse()
+    if args.sweep and args.gpus == 1:
+        return sweep(args)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
               f"(asked for --gpus {args.gpus}). The (sequence, KV head) units shard with no "
@@ -349,6 +354,92 @@ def main():
         "kernel_sources": kernel_sources_sha(),
     }
     print(json.dumps(out), flush=True)
+
+
+SWEEP_GEOMETRIES = [(2, 12), (4, 6), (4, 8), (8, 4), (16, 3), (16, 4), (64, 2), (256, 1),
+                    (1024, 1)]
+SWEEP_P = [0.8, 0.9, 0.95, 0.99]
+
+
+def sweep(args):
+    """Selection quality over tree geometries on one workload's tensors (same keys, values,
+    queries and reference queries for every geometry): per (b, L, p) the keys each query
+    head reads, the union over a KV head's heads, the true attention mass of the selected
+    set (from dense softmax weights over all N keys), needle recall, and the attend time.
+    Prints one JSON line."""
+    import numpy as np
+    import torch
+
+    import tree_indexed_sparse_amd as Z
+    import workloads as W
+
+    Z.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    spec = W.spec(args.workload)
+    B, T, Hq, Hkv, d, N = (spec[k] for k in ("B", "T", "Hq", "Hkv", "d", "N"))
+    G = Hq // Hkv
+    anchor = spec["anchor"]
+    inp = W.gen_all(spec, device=dev)
+    K, V, Q, R = inp["K"], inp["V"], inp["Q"], inp["R"]
+    QH = B * T * Hq
+    # dense attention weights of every head over all N keys (measurement only)
+    wts = torch.empty((B, T, Hq, N), dtype=torch.float32, device=dev)
+    for bb in range(B):
+        for g in range(Hkv):
+            q = Q[bb, :, g * G:(g + 1) * G, :].float().reshape(T * G, d)
+            sc = (q @ K[bb, g].float().T) / np.sqrt(d)
+            wts[bb, :, g * G:(g + 1) * G, :] = torch.softmax(sc, dim=-1).reshape(T, G, N)
+    wts = wts.reshape(QH, N)
+    O = torch.empty((B, T, Hq, d), dtype=torch.float32, device=dev)
+    sel = torch.empty((B, T, Hq, N), dtype=torch.int32, device=dev)
+    cnt = torch.empty((B, T, Hq), dtype=torch.int32, device=dev)
+    plan = [(bb, pos, t, h) for bb in range(B) for pos, t, h in W.needle_plan(spec, bb)]
+    ar = torch.arange(N, device=dev).view(1, N)
+    rows = []
+    for (b, L) in SWEEP_GEOMETRIES:
+        if N % (b ** L) or N // b > (1 << 21):
+            continue
+        tree = Z.build_tree(K, R, b, L)
+        ws = torch.empty(Z.workspace_bytes(tree, T, Hq), dtype=torch.uint8, device=dev)
+        for p in SWEEP_P:
+            def run():
+                Z.attend(Q, K, V, tree, p, anchor, out=O, sel_idx=sel, sel_count=cnt,
+                         workspace=ws)
+            run()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(5):
+                run()
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / 5
+            c = cnt.view(QH, 1).long()
+            idx = sel.view(QH, N).long()
+            valid = ar < c
+            mask = torch.zeros((QH, N), dtype=torch.float32, device=dev)
+            mask.scatter_add_(1, torch.where(valid, idx, torch.zeros_like(idx)), valid.float())
+            kept_mass = (wts * (mask > 0)).sum(-1).cpu().numpy()
+            kr = (c.view(-1).float() / N).cpu().numpy()
+            c1 = Z.level_view(tree, T, Hq, 1, ws)[2]
+            sel_h, cnt_h = sel.cpu().numpy(), cnt.cpu().numpy()
+            hits = sum(int(pos in set(sel_h[bb, t, h, :cnt_h[bb, t, h]].tolist()))
+                       for bb, pos, t, h in plan)
+            rows.append({"b": b, "L": L, "p": p, "top_node_tokens": b ** L,
+                         "keys_read_pct": round(100 * float(kr.mean()), 2),
+                         "keys_read_pct_min": round(100 * float(kr.min()), 2),
+                         "keys_read_pct_max": round(100 * float(kr.max()), 2),
+                         "union_pct": round(100 * float(c1.sum()) * b / (c1.size * N), 2),
+                         "attention_mass_kept_mean": round(float(kept_mass.mean()), 4),
+                         "attention_mass_kept_min": round(float(kept_mass.min()), 4),
+                         "needle_recall": round(hits / len(plan), 4) if plan else None,
+                         "attend_ms": round(ms, 4)})
+            print(f"# b={b} L={L} p={p}: {rows[-1]}", file=sys.stderr, flush=True)
+        del tree, ws
+        torch.cuda.empty_cache()
+    print(json.dumps({"sweep": args.workload, "query_heads": QH, "N": N, "rows": rows}),
+          flush=True)
 
 
 def tree_bytes_written(B, Hkv, N, d, b, L):
