@@ -77,9 +77,10 @@ def check_head(q, levels, K_u, V_u, b, L, p, anchor, lists_by_level, u, m, sel_r
     """Guided comparison of one query head. lists_by_level[l] = level_view(...) at level l."""
     p = float(np.float32(p))
     rep = HeadReport(qh=qh, exact_unguided=None)
-    F = np.arange(levels[L].shape[0], dtype=np.int64)
+    n_top = levels[L].shape[0]
+    F = np.arange(n_top, dtype=np.int64)
     kept = F
-    for l in range(L, 0, -1):
+    for l in (range(L, 0, -1) if n_top else ()):
         Gk = gpu_kept(lists_by_level[l], u, m)
         s = O.node_scores(levels[l][F], q)
         kept_o, fragile = O.select_top_p(F, s, p)
@@ -96,6 +97,7 @@ def check_head(q, levels, K_u, V_u, b, L, p, anchor, lists_by_level, u, m, sel_r
             F = O.expand(kept, b)
     N = K_u.shape[0]
     S_want = np.union1d(np.arange(min(anchor, N), dtype=np.int64), O.expand(kept, b))
+    S_want = np.union1d(S_want, O.tail_tokens(N, n_top, b, L))
     S_gpu = np.asarray(sel_row[:count], np.int64) if sel_row is not None else None
     if int(count) != S_want.size:
         rep.mismatch = f"count {int(count)} != {S_want.size}"

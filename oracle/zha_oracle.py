@@ -35,6 +35,12 @@ Readings where the page is silent (each is listed in the design doc):
 * anchor: tokens 0 .. anchor-1 are added after the selection (anchor = 1 is the
   page's rule); they take no part in the mass.
 * final attention: exact softmax attention at scale sigma over the gathered keys.
+* a cache that does not fill whole top nodes (the page is silent; needed to use the
+  tree while tokens are appended one at a time): a node exists once every token under
+  it is cached, and is pooled from its complete children; the search runs over the
+  complete top nodes, and the tail (tokens after the last complete top node) is always
+  attended, like the anchor, taking no part in the mass. With no complete top node the
+  whole cache is the tail.
 
 Precision: inputs are upcast exactly to float64 and every sum is float64. The
 method stores two float32 quantities that decide integers downstream, and the
@@ -93,23 +99,28 @@ def pool(children: np.ndarray, R: np.ndarray, tau: float) -> np.ndarray:
 
 
 def build_tree_unit(K_u: np.ndarray, R_g: np.ndarray, b: int, L: int) -> list:
-    """Pyramid of one (sequence, KV head): levels[l] is the float32 [N / b^l, d]
-    array of level-l summary keys for l = 1..L (levels[0] is the raw keys).
-
-    The node count at every level must be a whole number (N % b^L == 0)."""
+    """Pyramid of one (sequence, KV head): levels[l] is the float32 [N // b^l, d]
+    array of level-l summary keys for l = 1..L (levels[0] is the raw keys). Only
+    complete nodes exist: node j of level l is pooled from children j b .. j b + b - 1
+    of level l - 1, all of which exist."""
     N, d = K_u.shape
-    if b < 2 or L < 1 or N % (b ** L) != 0:
-        raise ValueError("need b >= 2, L >= 1 and N divisible by b^L")
+    if b < 2 or L < 1:
+        raise ValueError("need b >= 2 and L >= 1")
     tau = sigma(d)
     R64 = np.asarray(R_g, np.float64)
     levels = [np.asarray(K_u, np.float32)]
     X = np.asarray(K_u, np.float64)
     for _ in range(L):
         n = X.shape[0] // b
-        Xn = pool(X.reshape(n, b, d), R64, tau).astype(np.float32)   # stored float32
+        Xn = pool(X[:n * b].reshape(n, b, d), R64, tau).astype(np.float32)   # stored float32
         levels.append(Xn)
         X = Xn.astype(np.float64)
     return levels
+
+
+def tail_tokens(N: int, n_top: int, b: int, L: int) -> np.ndarray:
+    """Tokens after the last complete top node: always attended."""
+    return np.arange(n_top * b ** L, N, dtype=np.int64)
 
 
 def build_tree(K: np.ndarray, R: np.ndarray, b: int, L: int) -> list:
@@ -199,16 +210,19 @@ def search(q: np.ndarray, levels: list, b: int, L: int, p: float, anchor: int):
     Returns (S, [LevelDecision for l = L .. 1])."""
     N = levels[0].shape[0]
     p = float(np.float32(p))          # p is a float32 argument on the C boundary
-    F = np.arange(levels[L].shape[0], dtype=np.int64)
+    n_top = levels[L].shape[0]
+    F = np.arange(n_top, dtype=np.int64)
     decisions = []
     kept = F
-    for l in range(L, 0, -1):
-        s = node_scores(levels[l][F], q)
-        kept, fragile = select_top_p(F, s, p)
-        decisions.append(LevelDecision(l, F, s, kept, fragile))
-        if l > 1:
-            F = expand(kept, b)
+    if n_top:
+        for l in range(L, 0, -1):
+            s = node_scores(levels[l][F], q)
+            kept, fragile = select_top_p(F, s, p)
+            decisions.append(LevelDecision(l, F, s, kept, fragile))
+            if l > 1:
+                F = expand(kept, b)
     S = np.union1d(np.arange(min(anchor, N), dtype=np.int64), expand(kept, b))
+    S = np.union1d(S, tail_tokens(N, n_top, b, L))
     return S, decisions
 
 

@@ -348,3 +348,64 @@ def test_workload_recipe_shapes_and_needles():
     assert K2.dtype == np.float32
     import torch
     assert torch.equal(torch.from_numpy(K2).to(torch.bfloat16).float(), torch.from_numpy(K2))
+
+
+# ------------------------------------------------------------- ragged caches (tail)
+
+@pytest.mark.parametrize("b,L", [(4, 3), (2, 5), (8, 2)])
+def test_complete_nodes_do_not_change_when_tokens_are_appended(b, L):
+    """A node depends only on the tokens under it: the pyramid of a shorter cache is a
+    bit-identical prefix of the pyramid of a longer one, at every level."""
+    rng = _rng(20)
+    d = 16
+    top = b ** L
+    K = rng.standard_normal((3 * top + top // 2 + 3, d)).astype(np.float32)
+    R = rng.standard_normal((16, d)).astype(np.float32)
+    full = O.build_tree_unit(K, R, b, L)
+    for n in (1, b - 1, b, top - 1, top, top + 1, 2 * top + b + 1, K.shape[0]):
+        part = O.build_tree_unit(K[:n], R, b, L)
+        for l in range(1, L + 1):
+            assert part[l].shape[0] == n // b ** l
+            assert np.array_equal(part[l], full[l][:n // b ** l])
+
+
+@pytest.mark.parametrize("r", [1, 3, 17, 63])
+def test_ragged_cache_searches_complete_top_nodes_and_attends_the_tail(r):
+    """N = (whole top nodes) + r: the decisions are those of the complete part, and the
+    tail [N_full, N) is added to every head's set; O is masked SDPA over that set."""
+    import workloads as W
+
+    s = W.spec("tiny")
+    Q = W.gen_Q(s)
+    R = W.gen_R(s)
+    K, V = W.gen_KV_unit(s, 0, 0, Q)
+    b, L, top = s["b"], s["L"], s["b"] ** s["L"]
+    N_full = 40 * top
+    N = N_full + r
+    lv_full = O.build_tree_unit(K[:N_full], R[0], b, L)
+    lv = O.build_tree_unit(K[:N], R[0], b, L)
+    for t in range(s["T"]):
+        S_f, dec_f = O.search(Q[0, t, 0], lv_full, b, L, 0.9, 1)
+        S, dec = O.search(Q[0, t, 0], lv, b, L, 0.9, 1)
+        assert [d.kept.tolist() for d in dec] == [d.kept.tolist() for d in dec_f]
+        assert S.tolist() == S_f.tolist() + list(range(N_full, N))
+        res = O.attend_head(Q[0, t, 0], lv, K[:N], V[:N], b, L, 0.9, 1)
+        mask = np.zeros(N, bool)
+        mask[S] = True
+        np.testing.assert_allclose(res.O, _sdpa(Q[0, t, 0], K[:N], V[:N], mask),
+                                   rtol=1e-10, atol=1e-12)
+
+
+@pytest.mark.parametrize("N,L", [(1, 3), (5, 3), (63, 3), (4095, 6)])
+def test_no_complete_top_node_is_dense_attention(N, L):
+    """Below one top node (b^L tokens) there is nothing to search: every token is the tail."""
+    rng = _rng(21)
+    d, b = 16, 4
+    K = rng.standard_normal((N, d)).astype(np.float32)
+    V = rng.standard_normal((N, d)).astype(np.float32)
+    R = rng.standard_normal((16, d)).astype(np.float32)
+    levels = O.build_tree_unit(K, R, b, L)
+    q = rng.standard_normal(d).astype(np.float32)
+    r = O.attend_head(q, levels, K, V, b, L, 0.5, anchor=1)
+    assert r.S.tolist() == list(range(N)) and r.levels == []
+    np.testing.assert_allclose(r.O, _sdpa(q, K, V), rtol=1e-12, atol=1e-12)
