@@ -27,8 +27,8 @@
  *     workspace 256-byte aligned (hipMalloc returns 256-byte aligned memory); other
  *     pointers are rejected with ZHA_ERR_INVALID_ARG.
  *   - Supported: d in {64, 128}; dtype ZHA_F32 or ZHA_BF16 (K, V, Q and the reference
- *     queries share one dtype); b >= 2; 1 <= L <= ZHA_MAX_LEVELS; N % b^L == 0;
- *     Hq % Hkv == 0 and Hq / Hkv <= 16; N / b <= 2^21.
+ *     queries share one dtype); b >= 2; 1 <= L <= ZHA_MAX_LEVELS; N_cap % b^L == 0 (any
+ *     N <= N_cap); Hq % Hkv == 0 and Hq / Hkv <= 16; N_cap / b <= 2^21.
  */
 #ifndef ZHA_H_
 #define ZHA_H_
@@ -44,7 +44,7 @@ typedef enum {
   ZHA_OK = 0,
   ZHA_ERR_INVALID_ARG = -1, /* null or misaligned pointer, p not in (0, 1], anchor out of
                                range, b < 2, L < 1 */
-  ZHA_ERR_SHAPE = -2,       /* N % b^L != 0, Hq % Hkv != 0, N > N_cap, buffer too small */
+  ZHA_ERR_SHAPE = -2,       /* N_cap % b^L != 0, Hq % Hkv != 0, N > N_cap, buffer too small */
   ZHA_ERR_DTYPE = -3,       /* unknown dtype */
   ZHA_ERR_CAPACITY = -4,    /* selected-list capacity smaller than N */
   ZHA_ERR_UNSUPPORTED = -5, /* d not in {64, 128}, Hq / Hkv > 16, L > ZHA_MAX_LEVELS, N / b > 2^21 */
@@ -60,7 +60,9 @@ typedef enum { ZHA_F32 = 0, ZHA_BF16 = 1 } zha_dtype;
  * Summary-key pyramid: a plain view of caller-owned device memory; nothing to free.
  * Level l (1..L) holds float32 summary keys [B][Hkv][N_cap / b^l][d] starting at
  * pyramid + level_off[l] (float elements). Node j of level l covers tokens
- * [j * b^l, (j + 1) * b^l). Levels are written by zha_build_tree / zha_tree_append.
+ * [j * b^l, (j + 1) * b^l) and exists once all of them are cached: with N cached tokens,
+ * nodes 0 .. N / b^l - 1 (integer division) are valid. Levels are written by
+ * zha_build_tree / zha_tree_append.
  */
 typedef struct {
   int32_t B, Hkv, N, N_cap, d, b, L;
@@ -89,9 +91,12 @@ int zha_build_tree(const void* K, const void* ref_queries, int dtype, int B, int
                    zha_tree* out, void* stream);
 
 /*
- * Extend a tree by whole top nodes: pools tokens [t->N, t->N + n_new) at every level and
- * then sets t->N += n_new. n_new % b^L == 0 and t->N + n_new <= t->N_cap. K and
- * ref_queries as for zha_build_tree (same cache, same reference queries).
+ * Extend a tree by n_new >= 0 tokens (one at a time during generation, or in chunks):
+ * pools, at every level, exactly the nodes the new tokens complete, then sets
+ * t->N += n_new; t->N + n_new <= t->N_cap. A node's summary depends only on the tokens
+ * under it, so any sequence of appends gives the pyramid one zha_build_tree over the same
+ * tokens gives. K and ref_queries as for zha_build_tree (same cache, same reference
+ * queries).
  */
 int zha_tree_append(zha_tree* t, const void* K, const void* ref_queries, int n_new, void* stream);
 
@@ -119,8 +124,11 @@ size_t zha_attend_workspace_bytes(const zha_tree* t, int T, int Hq);
  * the frontier, and the kept set is the shortest prefix of the frontier in order of
  * descending score (ties: lower node id first) whose mass reaches p; the next frontier
  * is the children of the kept nodes. The selected tokens are the b tokens of every kept
- * level-1 node plus tokens [0, anchor). O is exact softmax attention at scale sigma over
- * them, accumulated in float32. Calls that share a workspace must not overlap.
+ * level-1 node plus tokens [0, anchor). The search runs over the complete top nodes
+ * (N / b^L of them); the tail, tokens [(N / b^L) * b^L, N), is selected for every head
+ * (with no complete top node, every token is). O is exact softmax attention at scale
+ * sigma over the selected tokens, accumulated in float32. Calls that share a workspace
+ * must not overlap.
  */
 int zha_attend(const zha_tree* t, const void* Q, int T, int Hq, const void* K, const void* V,
                float p, int anchor, float* O, int32_t* sel_idx, int64_t cap,

@@ -18,10 +18,11 @@ import tree_indexed_sparse_amd as Z  # noqa: E402
 import workloads as W  # noqa: E402
 
 
-def run_gpu(spec, p, anchor=1, inputs=None, want_lists=True, tree=None, device="cuda"):
+def run_gpu(spec, p, anchor=1, inputs=None, want_lists=True, tree=None, device="cuda", N=None):
+    """N: tokens in use (default: the whole generated cache, its capacity)."""
     inp = inputs if inputs is not None else W.gen_all(spec, device=device)
     if tree is None:
-        tree = Z.build_tree(inp["K"], inp["R"], spec["b"], spec["L"])
+        tree = Z.build_tree(inp["K"], inp["R"], spec["b"], spec["L"], N=N)
     O_, sel, cnt = Z.attend(inp["Q"], inp["K"], inp["V"], tree, p, anchor, want_lists=want_lists)
     ws = Z.attend.last_workspace
     torch.cuda.synchronize()
@@ -39,8 +40,10 @@ def oracle_unit(spec, b, g, Q=None, R=None):
     return K_u, V_u, levels
 
 
-def check_units(spec, res, p, anchor=1, units=None, check_pyramid=True, oracle_levels=None):
+def check_units(spec, res, p, anchor=1, units=None, check_pyramid=True, oracle_levels=None,
+                n_tokens=None):
     """Guided comparison of every query head of the given (sequence, KV head) units.
+    n_tokens: the cache holds only the first n_tokens generated tokens (a ragged cache).
     Returns (list of HeadReport, max pyramid relative error)."""
     B, T, Hq, Hkv = spec["B"], spec["T"], spec["Hq"], spec["Hkv"]
     G = Hq // Hkv
@@ -52,11 +55,18 @@ def check_units(spec, res, p, anchor=1, units=None, check_pyramid=True, oracle_l
         if oracle_levels is not None:
             K_u, V_u = W.gen_KV_unit(spec, b, g, Q)
             levels = oracle_levels[(b, g)]
+        elif n_tokens is not None:
+            K_u, V_u = W.gen_KV_unit(spec, b, g, Q)
+            K_u, V_u = K_u[:n_tokens], V_u[:n_tokens]
+            levels = O.build_tree_unit(K_u, R[g], spec["b"], spec["L"])
         else:
             K_u, V_u, levels = oracle_unit(spec, b, g, Q, R)
+        n_tok = spec["N"] if n_tokens is None else n_tokens
         if check_pyramid:
             for l in range(1, spec["L"] + 1):
-                n = spec["N"] // spec["b"] ** l
+                n = n_tok // spec["b"] ** l
+                if n == 0:
+                    continue
                 gl = Z.pyramid_level(res["tree"], l)[b, g, :n].cpu().numpy()
                 pyr_err = max(pyr_err, C.pyramid_rel_err(gl, levels[l]))
         for t in range(T):

@@ -363,3 +363,57 @@ def test_1m_deep_sampled_units():
     summ = C.summarize(reps)
     _report("1m deep sampled", summ, pyr)
     _assert_ok(spec, summ, pyr)
+
+
+@pytest.mark.parametrize("case", [
+    dict(name="32k + 1 token", extra=1),
+    dict(name="32k + 77 tokens, anchor 5", extra=77, anchor=5),
+    dict(name="32k + 4095 tokens", extra=4095),
+    dict(name="below one top node (N = 3000)", total=3000),
+    dict(name="tiny fp32 + 13 tokens", wl="tiny", extra=13),
+])
+def test_ragged_cache(case):
+    """Caches that do not fill whole top nodes: the search runs over the complete top nodes
+    and the tail after them is attended by every head."""
+    wl = case.get("wl", "32k_deep")
+    kw = {"B": 1} if wl == "32k_deep" else {}
+    base = W.spec(wl, **kw)
+    top = base["b"] ** base["L"]
+    N = case.get("total", base["N"] + case.get("extra", 0))
+    anchor = case.get("anchor", 1)
+    spec = W.spec(wl, N=-(-N // top) * top, **kw)
+    res = H.run_gpu(spec, 0.9, anchor=anchor, N=N)
+    assert int(res["tree"].N) == N
+    reps, pyr = H.check_units(spec, res, 0.9, anchor=anchor, n_tokens=N)
+    summ = C.summarize(reps)
+    _report(f"ragged {case['name']}", summ, pyr)
+    _assert_ok(spec, summ, pyr)
+
+
+def test_token_by_token_appends_match_one_shot_build():
+    """Appends of one token at a time (then chunks of assorted sizes, across top-node
+    boundaries) write the pyramid a one-shot build over the same tokens writes, bit for
+    bit; the attend over the appended tree matches the oracle."""
+    import tree_indexed_sparse_amd as Z
+
+    spec = W.spec("32k_deep", B=2, N=16384)
+    inp = W.gen_all(spec, device="cuda")
+    K, R = inp["K"], inp["R"]
+    n = 8192 - 37
+    tree = Z.build_tree(K, R, 4, 6, N=n)
+    for k in [1] * 300 + [5, 64, 1000, 3, 4097]:
+        Z.tree_append(tree, K, R, k)
+        n += k
+    torch.cuda.synchronize()
+    assert tree.N == n
+    one = Z.build_tree(K, R, 4, 6, N=n)
+    torch.cuda.synchronize()
+    for l in range(1, 7):
+        valid = n // 4 ** l
+        assert torch.equal(Z.pyramid_level(tree, l)[:, :, :valid],
+                           Z.pyramid_level(one, l)[:, :, :valid]), l
+    res = H.run_gpu(spec, 0.95, inputs=inp, tree=tree)
+    reps, pyr = H.check_units(spec, res, 0.95, units=[(1, 2)], n_tokens=n)
+    summ = C.summarize(reps)
+    _report(f"appended to N={n}", summ, pyr)
+    _assert_ok(spec, summ, pyr)

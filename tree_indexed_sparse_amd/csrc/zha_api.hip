@@ -93,8 +93,6 @@ int check_geometry(int B, int Hkv, int N, int N_cap, int d, int b, int L) {
     return fail(ZHA_ERR_SHAPE, "cache capacity N_cap=%d must be a positive multiple of b^L=%lld",
                 N_cap, (long long)top);
   if (N < 0 || N > N_cap) return fail(ZHA_ERR_SHAPE, "N=%d must lie in [0, N_cap=%d]", N, N_cap);
-  if (N % top != 0)
-    return fail(ZHA_ERR_SHAPE, "N=%d must be a multiple of b^L=%lld", N, (long long)top);
   if (N_cap / b > (1 << kMaxLog2Nodes))
     return fail(ZHA_ERR_UNSUPPORTED, "N_cap / b must be <= 2^%d", kMaxLog2Nodes);
   return ZHA_OK;
@@ -239,10 +237,7 @@ int zha_tree_append(zha_tree* t, const void* K, const void* R, int n_new, void* 
   if (!K || !R) return fail(ZHA_ERR_INVALID_ARG, "K and ref_queries must not be NULL");
   if (!aligned16(K) || !aligned16(R))
     return fail(ZHA_ERR_INVALID_ARG, "K and ref_queries must be 16-byte aligned");
-  const int64_t top = ipow(t->b, t->L);
-  if (n_new < 0 || n_new % top != 0)
-    return fail(ZHA_ERR_SHAPE, "n_new=%d must be a non-negative multiple of b^L=%lld", n_new,
-                (long long)top);
+  if (n_new < 0) return fail(ZHA_ERR_SHAPE, "n_new=%d must be >= 0", n_new);
   if ((int64_t)t->N + n_new > t->N_cap)
     return fail(ZHA_ERR_SHAPE, "N + n_new = %lld exceeds N_cap=%d", (long long)t->N + n_new,
                 t->N_cap);
@@ -250,34 +245,46 @@ int zha_tree_append(zha_tree* t, const void* K, const void* R, int n_new, void* 
   const int units = t->B * t->Hkv;
   // level l has N_cap / b^l nodes of capacity per (sequence, KV head)
   auto cap_nodes = [&](int l) { return (int64_t)t->N_cap / ipow(t->b, l); };
+  // Nodes of level j that the append completes: [N_old / b^j, N_new / b^j). A fused launch
+  // pools whole tiles of b^k child rows (k levels) that contain such nodes, with the
+  // child rows cached so far as its limit: it stores every complete node of those tiles
+  // (re-pooling a node that was already complete rewrites the same value, with the same
+  // arithmetic) and none that is incomplete. Any sequence of appends therefore writes the
+  // pyramid a one-shot build writes.
+  const int64_t n_old = t->N, n_end = (int64_t)t->N + n_new;
+  auto lo = [&](int j) { return n_old / ipow(t->b, j); };
+  auto hi = [&](int j) { return n_end / ipow(t->b, j); };
   for (int l = 1; l <= t->L;) {
     const void* child = (l == 1) ? K : (const void*)(t->pyramid + t->level_off[l - 1]);
     const int dt_in = (l == 1) ? t->dtype : ZHA_F32;
-    const int64_t b_prev = ipow(t->b, l - 1);
-    const int row_begin = (int)(t->N / b_prev), row_end = (int)((t->N + (int64_t)n_new) / b_prev);
     const int k = fused_levels(t->b, t->L - l + 1);
-    hipError_t e;
-    if (k >= 1) {
-      float* outs[ZHA_MAX_LEVELS];
-      int64_t strides[ZHA_MAX_LEVELS];
-      for (int j = 0; j < k; ++j) {
-        outs[j] = t->pyramid + t->level_off[l + j];
-        strides[j] = cap_nodes(l + j) * t->d;
+    hipError_t e = hipSuccess;
+    if (hi(l) > lo(l)) {
+      if (k >= 1) {
+        const int64_t tr = ipow(t->b, k);  // child rows (level l - 1) per tile
+        const int64_t rows = hi(l - 1);    // child rows cached after the append
+        const int64_t r0 = (lo(l - 1) / tr) * tr, r1 = (rows + tr - 1) / tr * tr;
+        float* outs[ZHA_MAX_LEVELS];
+        int64_t strides[ZHA_MAX_LEVELS];
+        for (int j = 0; j < k; ++j) {
+          outs[j] = t->pyramid + t->level_off[l + j];
+          strides[j] = cap_nodes(l + j) * t->d;
+        }
+        e = timed(ZHA_K_POOL, l, s, [&] {
+          return launch_pool_fused(dt_in, child, cap_nodes(l - 1) * t->d, R, t->dtype, outs,
+                                   strides, k, units, t->Hkv, (int)r0, (int)r1, (int)rows, t->b,
+                                   t->d, s);
+        });
+      } else {
+        e = timed(ZHA_K_POOL, l, s, [&] {
+          return launch_pool_level(dt_in, child, cap_nodes(l - 1) * t->d, R, t->dtype,
+                                   t->pyramid + t->level_off[l], cap_nodes(l) * t->d, units,
+                                   t->Hkv, (int)lo(l), (int)hi(l), t->b, t->d, s);
+        });
       }
-      e = timed(ZHA_K_POOL, l, s, [&] {
-        return launch_pool_fused(dt_in, child, cap_nodes(l - 1) * t->d, R, t->dtype, outs, strides,
-                                 k, units, t->Hkv, row_begin, row_end, t->b, t->d, s);
-      });
-      l += k;
-    } else {
-      e = timed(ZHA_K_POOL, l, s, [&] {
-        return launch_pool_level(dt_in, child, cap_nodes(l - 1) * t->d, R, t->dtype,
-                                 t->pyramid + t->level_off[l], cap_nodes(l) * t->d, units, t->Hkv,
-                                 row_begin / t->b, row_end / t->b, t->b, t->d, s);
-      });
-      l += 1;
     }
     if (e != hipSuccess) return hip_fail(e, "pooling launch");
+    l += k >= 1 ? k : 1;
   }
   t->N += n_new;
   return ZHA_OK;
@@ -332,22 +339,20 @@ size_t zha_attend_workspace_bytes(const zha_tree* t, int T, int Hq) {
 // ---- dense comparator: the decode kernels over every cached key, no search
 namespace {
 struct DenseLayout {
-  int64_t off_nodes, off_masks, off_count, off_part, total;
+  int64_t off_part, total;
   int splits;
 };
 int dense_geom(int B, int Hkv, int N, int N_cap, int d, int T, int Hq, Geom* g) {
   if (B < 1 || Hkv < 1) return fail(ZHA_ERR_SHAPE, "B and Hkv must be >= 1 (got %d, %d)", B, Hkv);
   if (d != 64 && d != 128) return fail(ZHA_ERR_UNSUPPORTED, "head dim must be 64 or 128 (got %d)", d);
   if (N < 1 || N > N_cap) return fail(ZHA_ERR_SHAPE, "N=%d must lie in [1, N_cap=%d]", N, N_cap);
-  if (N > (1 << kMaxLog2Nodes))
-    return fail(ZHA_ERR_UNSUPPORTED, "N must be <= 2^%d", kMaxLog2Nodes);
   zha_tree t{};
   t.B = B;
   t.Hkv = Hkv;
   t.N = N;
   t.N_cap = N_cap;
   t.d = d;
-  t.b = 1;
+  t.b = 2;
   t.L = 1;
   return make_geom(&t, T, Hq, g);
 }
@@ -355,16 +360,8 @@ DenseLayout dense_layout(const Geom& g) {
   DenseLayout w{};
   w.splits = (2048 + g.U - 1) / g.U;
   if (w.splits > kMaxSplits) w.splits = kMaxSplits;
-  int64_t off = 0;
-  w.off_nodes = off;
-  off = align256(off + 4 * (int64_t)g.U * g.N);
-  w.off_masks = off;
-  off = align256(off + 4 * (int64_t)g.U * g.N);
-  w.off_count = off;
-  off = align256(off + 4 * (int64_t)g.U);
-  w.off_part = off;
-  off = align256(off + 4 * (int64_t)g.U * w.splits * kMaxMembers * (g.D + 2));
-  w.total = off;
+  w.off_part = 0;
+  w.total = align256(4 * (int64_t)g.U * w.splits * kMaxMembers * (g.D + 2));
   return w;
 }
 }  // namespace
@@ -396,16 +393,11 @@ int zha_dense_attend(const void* Q, int T, int Hq, const void* K, const void* V,
     return fail(ZHA_ERR_SHAPE, "workspace has %zu bytes, needs %lld", ws_bytes,
                 (long long)w.total);
   hipStream_t s = (hipStream_t)stream;
-  char* ws = (char*)workspace;
-  LevelBufs l1;
-  l1.nodes = (uint32_t*)(ws + w.off_nodes);
-  l1.masks = (uint32_t*)(ws + w.off_masks);
-  l1.count = (uint32_t*)(ws + w.off_count);
-  l1.stride = g.N;
-  float* part = (float*)(ws + w.off_part);
-  hipError_t e = timed(ZHA_K_DECODE, 1, s, [&] { return launch_dense_list(g, l1, s); });
-  if (e != hipSuccess) return hip_fail(e, "dense list launch");
-  e = timed(ZHA_K_DECODE, 0, s, [&] { return launch_decode(g, dtype, K, V, Q, l1, 0, w.splits, part, s); });
+  float* part = (float*)((char*)workspace + w.off_part);
+  // no list: every token is the tail, read by every member
+  hipError_t e = timed(ZHA_K_DECODE, 0, s, [&] {
+    return launch_decode(g, dtype, K, V, Q, LevelBufs{}, 0, 0, 0, N, w.splits, part, s);
+  });
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   e = timed(ZHA_K_COMBINE, 0, s, [&] { return launch_combine(g, w.splits, part, O, s); });
   if (e != hipSuccess) return hip_fail(e, "combine launch");
@@ -489,8 +481,15 @@ int zha_attend(const zha_tree* t, const void* Q, int T, int Hq, const void* K, c
       unit_stride[l] = c * t->d;
     }
   }
+  // The search runs over the complete top nodes; the tail (tokens after the last of them)
+  // is attended by every head. With no complete top node the whole cache is the tail.
+  const int n_top_nodes = (int)w.n[t->L];
+  const bool searched = n_top_nodes > 0;
+  const int64_t n_full = (int64_t)n_top_nodes * ipow(t->b, t->L);
+  const int tail_lo = searched ? (int)std::max<int64_t>(n_full, anchor) : 0;
+  const int n_tail = t->N - tail_lo;
   // the top levels with small frontiers run fused in one launch
-  const int l_top = top_levels_lowest(g, w.n);
+  const int l_top = searched ? top_levels_lowest(g, w.n) : 0;
   if (l_top) {
     e = timed(ZHA_K_DESCENT, l_top, s, [&] {
       return launch_top_levels(g, t->pyramid, lv, t->level_off, unit_stride, l_top, Q, t->dtype,
@@ -501,7 +500,7 @@ int zha_attend(const zha_tree* t, const void* Q, int T, int Hq, const void* K, c
   int64_t cap_l = t->N_cap;
   for (int l = 1; l <= t->L; ++l) cap_l /= t->b;  // capacity nodes at the top level
   for (int l = l_top ? l_top - 1 : t->L; l < t->L; ++l) cap_l *= t->b;
-  for (int l = l_top ? l_top - 1 : t->L; l >= 1; --l) {
+  for (int l = l_top ? l_top - 1 : t->L; searched && l >= 1; --l) {
     const LevelBufs* parent = (l < t->L) ? &lv[l + 1] : nullptr;
     const int n_top = (l == t->L) ? (int)w.n[t->L] : 0;
     const float* X = t->pyramid + t->level_off[l];
@@ -527,9 +526,17 @@ int zha_attend(const zha_tree* t, const void* Q, int T, int Hq, const void* K, c
     if (e != hipSuccess) return hip_fail(e, "compact launch");
     cap_l *= t->b;
   }
+  if (!searched || n_tail > 0) {
+    e = timed(ZHA_K_SELECT, 0, s, [&] {
+      return launch_tail(g, searched ? 1 : 0, tail_lo, n_tail, sel_idx, cap, sel_count,
+                         (uint32_t*)(ws + w.off_count), (t->L + 1) * g.U, s);
+    });
+    if (e != hipSuccess) return hip_fail(e, "tail launch");
+  }
   float* part = (float*)(ws + w.off_part);
   e = timed(ZHA_K_DECODE, 0, s, [&] {
-    return launch_decode(g, t->dtype, K, V, Q, lv[1], anchor, w.splits, part, s);
+    return launch_decode(g, t->dtype, K, V, Q, lv[1], searched ? 1 : 0, searched ? anchor : 0,
+                         tail_lo, n_tail, w.splits, part, s);
   });
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   e = timed(ZHA_K_COMBINE, 0, s, [&] { return launch_combine(g, w.splits, part, O, s); });

@@ -193,7 +193,8 @@ __device__ __forceinline__ uint4 lds16(const uint32_t* p) { return *reinterpret_
 template <typename Tin, typename Tr, int D>
 __global__ __launch_bounds__(kPoolThreads) void pool_tile_kernel(
     const Tin* __restrict__ child, int64_t in_unit_stride, const Tr* __restrict__ Rall,
-    PoolOut out, int nlev, int Hkv, int tile_begin, int tile_end, int b, float tau) {
+    PoolOut out, int nlev, int Hkv, int tile_begin, int tile_end, int row_limit, int b,
+    float tau) {
   constexpr bool kBF = sizeof(Tin) == 2;
   constexpr int RWb = D / 2 + 4;  // bf16 row stride in dwords (padding spreads banks)
   constexpr int RWf = D + 4;      // fp32 row stride in floats
@@ -263,6 +264,9 @@ __global__ __launch_bounds__(kPoolThreads) void pool_tile_kernel(
     }
 
     int rows = TR;
+    // child rows at or past row_limit are not cached yet: only nodes whose children are all
+    // valid are stored (the others only feed nodes that are not stored either)
+    int vrows = min(TR, row_limit - t * TR);
     for (int j = 0; j < nlev; ++j) {
       const bool bf_in = kBF && j == 0;
       const float* inF = (j == 0) ? reinterpret_cast<const float*>(sIn) : sY[(j - 1) & 1];
@@ -316,6 +320,7 @@ __global__ __launch_bounds__(kPoolThreads) void pool_tile_kernel(
       __syncthreads();
       float* dst = out.ptr[j] + unit * out.unit_stride[j] + (int64_t)t * nodes * D;
       float* ynext = sY[j & 1];
+      const int vnodes = vrows / b;
       for (int i = threadIdx.x; i < nodes * D; i += kPoolThreads) {
         const int nd = i / D, k = i % D;
         float acc = 0.f;
@@ -330,11 +335,12 @@ __global__ __launch_bounds__(kPoolThreads) void pool_tile_kernel(
           }
           acc = fmaf(sw[r], x, acc);
         }
-        dst[(int64_t)nd * D + k] = acc;
+        if (nd < vnodes) dst[(int64_t)nd * D + k] = acc;
         if (j + 1 < nlev) ynext[nd * RWf + k] = acc;
       }
       __syncthreads();
       rows = nodes;
+      vrows = vnodes;
     }
   }
 }
@@ -358,7 +364,7 @@ constexpr int kWaveTilesPerWave = 2;
 template <int D>
 __global__ __launch_bounds__(kPoolThreads) void pool_wave_b4_kernel(
     const bf16_t* __restrict__ child, int64_t in_unit_stride, const bf16_t* __restrict__ Rall,
-    PoolOut out, int nlev, int Hkv, int tile_begin, int tile_end, float tau) {
+    PoolOut out, int nlev, int Hkv, int tile_begin, int tile_end, int row_limit, float tau) {
   constexpr int KC = D / 32;
   constexpr int NQ = D / 16;
   constexpr int RWb = D / 2 + 4;  // bf16 raw-row stride in dwords
@@ -414,6 +420,8 @@ __global__ __launch_bounds__(kPoolThreads) void pool_wave_b4_kernel(
     const int t = tile_begin + (blockIdx.x * (kPoolThreads / 64) + wave) * kWaveTilesPerWave + it;
     if (t >= tile_end) break;
     const bf16_t* src = child + unit * in_unit_stride + (int64_t)t * kWaveRows * D;
+    // rows at or past row_limit are not cached yet: only complete nodes are stored
+    const int vrows = min(kWaveRows, row_limit - t * kWaveRows);
     uint4 a[4][KC];
 #pragma unroll
     for (int blk = 0; blk < 4; ++blk)
@@ -454,10 +462,11 @@ __global__ __launch_bounds__(kPoolThreads) void pool_wave_b4_kernel(
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       const int node = 4 * blk + grp;
+      const bool st1 = 4 * (node + 1) <= vrows;
 #pragma unroll
       for (int i = 0; i < DL; i += 4) {
         const float4 o = make_float4(acc[i], acc[i + 1], acc[i + 2], acc[i + 3]);
-        *reinterpret_cast<float4*>(dst1 + (int64_t)node * D + DL * mem + i) = o;
+        if (st1) *reinterpret_cast<float4*>(dst1 + (int64_t)node * D + DL * mem + i) = o;
         *reinterpret_cast<float4*>(&l1[node * RWf + DL * mem + i]) = o;
       }
     }
@@ -493,10 +502,12 @@ __global__ __launch_bounds__(kPoolThreads) void pool_wave_b4_kernel(
           for (int i = 0; i < DL; ++i) acc[i] = fmaf(w[c], rp[i], acc[i]);
         }
         float* dst = out.ptr[j] + unit * out.unit_stride[j] + ((int64_t)t * nodes + grp) * D;
+        const int span = j == 1 ? 16 : 64;  // key rows under one node of this level
+        const bool stj = span * (grp + 1) <= vrows;
 #pragma unroll
         for (int i = 0; i < DL; i += 4) {
           const float4 o = make_float4(acc[i], acc[i + 1], acc[i + 2], acc[i + 3]);
-          *reinterpret_cast<float4*>(dst + DL * mem + i) = o;
+          if (stj) *reinterpret_cast<float4*>(dst + DL * mem + i) = o;
           if (j == 1) *reinterpret_cast<float4*>(&l2[grp * RWf + DL * mem + i]) = o;
         }
       }
@@ -653,14 +664,14 @@ __global__ __launch_bounds__(kPoolThreads) void pool_wide_kernel(
 template <int D>
 hipError_t launch_wave_b4(const void* child, int64_t in_unit_stride, const void* R,
                           const PoolOut& out, int nlev, int units, int Hkv, int row_begin,
-                          int row_end, hipStream_t s) {
+                          int row_end, int row_limit, hipStream_t s) {
   const int t0 = row_begin / kWaveRows, t1 = row_end / kWaveRows;
   if (t1 <= t0) return hipSuccess;
   const int per_wg = (kPoolThreads / 64) * kWaveTilesPerWave;
   dim3 grid((t1 - t0 + per_wg - 1) / per_wg, units);
   hipLaunchKernelGGL((pool_wave_b4_kernel<D>), grid, dim3(kPoolThreads), 0, s,
                      (const bf16_t*)child, in_unit_stride, (const bf16_t*)R, out, nlev, Hkv, t0,
-                     t1, 1.0f / sqrtf((float)D));
+                     t1, row_limit, 1.0f / sqrtf((float)D));
   return hipGetLastError();
 }
 
@@ -706,27 +717,27 @@ hipError_t launch_pool_d(int D, const void* child, int64_t in_unit_stride, const
 template <typename Tin, typename Tr, int D>
 hipError_t launch_tile_t(const void* child, int64_t in_unit_stride, const void* R,
                          const PoolOut& out, int nlev, int units, int Hkv, int row_begin,
-                         int row_end, int b, hipStream_t s) {
+                         int row_end, int row_limit, int b, hipStream_t s) {
   int TR = 1;
   for (int j = 0; j < nlev; ++j) TR *= b;
   const int t0 = row_begin / TR, t1 = row_end / TR;
   if (t1 <= t0) return hipSuccess;
   dim3 grid((t1 - t0 + kTilesPerWG - 1) / kTilesPerWG, units);
   hipLaunchKernelGGL((pool_tile_kernel<Tin, Tr, D>), grid, dim3(kPoolThreads), 0, s,
-                     (const Tin*)child, in_unit_stride, (const Tr*)R, out, nlev, Hkv, t0, t1, b,
-                     1.0f / sqrtf((float)D));
+                     (const Tin*)child, in_unit_stride, (const Tr*)R, out, nlev, Hkv, t0, t1,
+                     row_limit, b, 1.0f / sqrtf((float)D));
   return hipGetLastError();
 }
 
 template <typename Tin, typename Tr>
 hipError_t launch_tile_d(int D, const void* child, int64_t in_unit_stride, const void* R,
                          const PoolOut& out, int nlev, int units, int Hkv, int row_begin,
-                         int row_end, int b, hipStream_t s) {
+                         int row_end, int row_limit, int b, hipStream_t s) {
   if (D == 64)
     return launch_tile_t<Tin, Tr, 64>(child, in_unit_stride, R, out, nlev, units, Hkv,
-                                      row_begin, row_end, b, s);
+                                      row_begin, row_end, row_limit, b, s);
   return launch_tile_t<Tin, Tr, 128>(child, in_unit_stride, R, out, nlev, units, Hkv, row_begin,
-                                     row_end, b, s);
+                                     row_end, row_limit, b, s);
 }
 
 }  // namespace
@@ -743,7 +754,8 @@ int fused_levels(int b, int levels_left) {
 hipError_t launch_pool_fused(int dtype_in, const void* child, int64_t in_unit_stride,
                              const void* R, int dtype_r, float* const* outs,
                              const int64_t* out_unit_strides, int nlev, int units, int Hkv,
-                             int row_begin, int row_end, int b, int D, hipStream_t s) {
+                             int row_begin, int row_end, int row_limit, int b, int D,
+                             hipStream_t s) {
   if (nlev < 1 || nlev > kMaxFuse) return hipErrorInvalidValue;
   PoolOut out{};
   for (int j = 0; j < nlev; ++j) {
@@ -756,18 +768,18 @@ hipError_t launch_pool_fused(int dtype_in, const void* child, int64_t in_unit_st
         row_end % kWaveRows == 0) {
       if (D == 64)
         return launch_wave_b4<64>(child, in_unit_stride, R, out, nlev, units, Hkv, row_begin,
-                                  row_end, s);
+                                  row_end, row_limit, s);
       return launch_wave_b4<128>(child, in_unit_stride, R, out, nlev, units, Hkv, row_begin,
-                                 row_end, s);
+                                 row_end, row_limit, s);
     }
     if (dtype_in == ZHA_BF16)
       return launch_tile_d<bf16_t, bf16_t>(D, child, in_unit_stride, R, out, nlev, units, Hkv,
-                                           row_begin, row_end, b, s);
+                                           row_begin, row_end, row_limit, b, s);
     return launch_tile_d<float, bf16_t>(D, child, in_unit_stride, R, out, nlev, units, Hkv,
-                                        row_begin, row_end, b, s);
+                                        row_begin, row_end, row_limit, b, s);
   }
   return launch_tile_d<float, float>(D, child, in_unit_stride, R, out, nlev, units, Hkv,
-                                     row_begin, row_end, b, s);
+                                     row_begin, row_end, row_limit, b, s);
 }
 
 hipError_t launch_pool_level(int dtype_in, const void* child, int64_t in_unit_stride,

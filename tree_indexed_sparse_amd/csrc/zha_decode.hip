@@ -9,7 +9,9 @@
 // with a member bitmask each), expanded to b contiguous tokens per node. Each K/V row is
 // read once per unit and scored for every member; tokens outside a member's own set are
 // masked. Tokens below `anchor` are skipped inside nodes and attended once, for every
-// member, by split 0. The union token range is cut into `splits` equal pieces; each
+// member, by split 0. A tail range of tokens (those after the last complete top node, or
+// the whole cache for dense attention) follows the list and is read by every member.
+// The work range (list tokens, then tail) is cut into `splits` equal pieces; each
 // workgroup writes one (max, sum, weighted-V) partial per member, and a separate combine
 // launch merges a unit's partials in a fixed order, so the result does not depend on the
 // order in which workgroups run.
@@ -124,14 +126,16 @@ __device__ __forceinline__ void split_range(int ntok, int splits, int sp, int al
 template <typename T, int D>
 __global__ __launch_bounds__(kDecThreads) void decode_valu_kernel(
     Geom geo, const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ Q,
-    LevelBufs l1, int anchor, int splits, float* __restrict__ part, float sigma) {
+    LevelBufs l1, int has_list, int anchor, int tail_lo, int n_tail, int splits,
+    float* __restrict__ part, float sigma) {
   constexpr int DPL = D / 64;  // dims per lane
   const int u = blockIdx.y, sp = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int Mu = members_of(geo, u);
   const int b = geo.b;
+  const int nnode = has_list ? (int)l1.count[u] * b : 0;  // work items from the list
   int t0, t1;
-  split_range((int)l1.count[u] * b, splits, sp, 1, &t0, &t1);
+  split_range(nnode + n_tail, splits, sp, 1, &t0, &t1);
   const int64_t row0 = (int64_t)bg_of(geo, u) * geo.Ncap;
   const T* Ku = K + row0 * D;
   const T* Vu = V + row0 * D;
@@ -180,6 +184,10 @@ __global__ __launch_bounds__(kDecThreads) void decode_valu_kernel(
   if (sp == 0 && wave == 0)
     for (int tok = 0; tok < anchor; ++tok) consume(tok, full);
   for (int i = t0 + wave; i < t1; i += kDecWaves) {
+    if (i >= nnode) {  // the tail: every member
+      consume(tail_lo + (i - nnode), full);
+      continue;
+    }
     const int nd = (int)geo.bdiv.div((uint32_t)i), c = i - nd * b;
     const int tok = (int)l1.nodes[u * l1.stride + nd] * b + c;
     if (tok < anchor) continue;
@@ -248,8 +256,8 @@ struct TileRegs {
 template <int D>
 __global__ __launch_bounds__(kDecThreads) void decode_mfma_kernel(
     Geom geo, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
-    const bf16_t* __restrict__ Q, LevelBufs l1, int anchor, int splits, float* __restrict__ part,
-    float sigma) {
+    const bf16_t* __restrict__ Q, LevelBufs l1, int has_list, int anchor, int tail_lo, int n_tail,
+    int splits, float* __restrict__ part, float sigma) {
   constexpr int KC = D / 32;          // 32-dim chunks: QK k-steps and PV column blocks
   constexpr int RW = D / 2 + 4;       // LDS row stride in dwords (padding spreads banks)
   constexpr int CH = D / 8;           // 16-byte chunks per row
@@ -265,8 +273,10 @@ __global__ __launch_bounds__(kDecThreads) void decode_mfma_kernel(
   const int mem = lane & 15, grp = lane >> 4;
   const int Mu = members_of(geo, u);
   const int b = geo.b;
+  const int ncount = has_list ? (int)l1.count[u] : 0;
+  const int nnode = ncount * b;  // work items from the list; the tail follows them
   int t0, t1;
-  split_range((int)l1.count[u] * b, splits, sp, kTile, &t0, &t1);
+  split_range(nnode + n_tail, splits, sp, kTile, &t0, &t1);
   const int64_t row0 = (int64_t)bg_of(geo, u) * geo.Ncap;
   const bf16_t* Ku = K + row0 * D;
   const bf16_t* Vu = V + row0 * D;
@@ -292,12 +302,13 @@ __global__ __launch_bounds__(kDecThreads) void decode_mfma_kernel(
   auto token_at = [&](int i, bool anc, int lim, int nbase) -> int {
     if (i >= lim) return 0;
     if (anc) return i;
+    if (i >= nnode) return tail_lo + (i - nnode);
     const int nd = (int)geo.bdiv.div((uint32_t)i);
     return (int)s_nodes[nd - nbase] * b + (i - nd * b);
   };
   auto mask_at = [&](int i, bool anc, int lim, int nbase) -> uint32_t {
     if (i >= lim) return 0u;
-    if (anc) return 0xffffu;
+    if (anc || i >= nnode) return 0xffffu;
     const int nd = (int)geo.bdiv.div((uint32_t)i);
     const int t = (int)s_nodes[nd - nbase] * b + (i - nd * b);
     return t < anchor ? 0u : s_masks[nd - nbase];
@@ -416,7 +427,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_mfma_kernel(
   const int step = kDecWaves * kTile;
   for (int c0 = t0; c0 < t1; c0 += span) {
     const int c1 = min(c0 + span, t1);
-    const int nbase = c0 / b, nend = (c1 - 1) / b + 1;
+    const int nbase = c0 / b, nend = min((c1 - 1) / b + 1, ncount);  // list part only
     __syncthreads();
     for (int i = threadIdx.x; i < nend - nbase; i += kDecThreads) {
       s_nodes[i] = nodes[nbase + i];
@@ -464,34 +475,16 @@ __global__ __launch_bounds__(kDecThreads) void decode_mfma_kernel(
 
 }  // namespace
 
-namespace {
-// Dense work list: token j is node j (b = 1) and every member reads it.
-__global__ __launch_bounds__(256) void dense_list_kernel(Geom geo, LevelBufs l1) {
-  const int u = blockIdx.y;
-  const int j = blockIdx.x * 256 + threadIdx.x;
-  if (j < geo.N) {
-    l1.nodes[u * l1.stride + j] = (uint32_t)j;
-    l1.masks[u * l1.stride + j] = (1u << members_of(geo, u)) - 1u;
-  }
-  if (blockIdx.x == 0 && threadIdx.x == 0) l1.count[u] = (uint32_t)geo.N;
-}
-}  // namespace
-
-hipError_t launch_dense_list(const Geom& geo, const LevelBufs& l1, hipStream_t s) {
-  hipLaunchKernelGGL(dense_list_kernel, dim3((geo.N + 255) / 256, geo.U), dim3(256), 0, s, geo,
-                     l1);
-  return hipGetLastError();
-}
-
 hipError_t launch_decode(const Geom& geo, int dtype, const void* K, const void* V,
-                         const void* Q, const LevelBufs& l1, int anchor, int splits,
-                         float* partials, hipStream_t s) {
+                         const void* Q, const LevelBufs& l1, int has_list, int anchor,
+                         int tail_lo, int n_tail, int splits, float* partials, hipStream_t s) {
   if (splits < 1 || splits > kMaxSplits) return hipErrorInvalidValue;
   dim3 grid(splits, geo.U);
   const float sigma = 1.0f / sqrtf((float)geo.D);
 #define ZHA_DEC(KERNEL, T)                                                                    \
   hipLaunchKernelGGL(KERNEL, grid, dim3(kDecThreads), 0, s, geo, (const T*)K, (const T*)V,     \
-                     (const T*)Q, l1, anchor, splits, partials, sigma)
+                     (const T*)Q, l1, has_list, anchor, tail_lo, n_tail, splits, partials,  \
+                     sigma)
   if (dtype == ZHA_BF16) {
     if (geo.D == 64) ZHA_DEC((decode_mfma_kernel<64>), bf16_t);
     else ZHA_DEC((decode_mfma_kernel<128>), bf16_t);

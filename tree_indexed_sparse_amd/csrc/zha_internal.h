@@ -126,7 +126,8 @@ int fused_levels(int b, int levels_left);
 hipError_t launch_pool_fused(int dtype_in, const void* child, int64_t in_unit_stride,
                              const void* R, int dtype_r, float* const* outs,
                              const int64_t* out_unit_strides, int nlev, int units, int Hkv,
-                             int row_begin, int row_end, int b, int D, hipStream_t s);
+                             int row_begin, int row_end, int row_limit, int b, int D,
+                             hipStream_t s);
 
 // Scores of a level's union frontier for every member: S[qh][k].
 // wide != nullptr: also write the per-workgroup member max/min the chunked selection reads.
@@ -173,12 +174,18 @@ hipError_t launch_union(const Geom& geo, int level, const float* S, int64_t S_st
                         int32_t* sel_idx, int64_t cap, const WideSel& wide, hipStream_t s);
 int64_t compact_counter_words(int U, int64_t n);
 
-// Work list of dense attention (geo.b = 1): nodes[u][j] = j with every member's bit.
-hipError_t launch_dense_list(const Geom& geo, const LevelBufs& l1, hipStream_t s);
-
+// Sparse GQA decode: the tokens of the level-1 union list (has_list), then the tail
+// [tail_lo, tail_lo + n_tail) for every member, plus tokens [0, anchor) for every member.
 hipError_t launch_decode(const Geom& geo, int dtype, const void* K, const void* V,
-                         const void* Q, const LevelBufs& l1, int anchor, int splits,
-                         float* partials, hipStream_t s);
+                         const void* Q, const LevelBufs& l1, int has_list, int anchor,
+                         int tail_lo, int n_tail, int splits, float* partials, hipStream_t s);
+
+// Appends the tail [tail_lo, tail_lo + n_tail) to every head's token list and count (after
+// the level-1 selection wrote them; searched = 0: the list is the tail alone and every
+// level's union count is zeroed).
+hipError_t launch_tail(const Geom& geo, int searched, int tail_lo, int n_tail,
+                       int32_t* sel_idx, int64_t cap, int32_t* sel_count, uint32_t* counts,
+                       int count_words, hipStream_t s);
 
 // Merge the decode partials of every split, in split order, into O.
 hipError_t launch_combine(const Geom& geo, int splits, const float* partials, float* O,

@@ -1647,6 +1647,28 @@ __global__ __launch_bounds__(kUnionThreads) void wide_write_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------------- tail
+// Tokens after the last complete top node are attended by every head: appended to each
+// head's ascending token list (after the level-1 selection, which wrote tokens below the
+// tail only) and to its count. Without a search the list is the tail alone, and every
+// level's union count is zeroed so that the per-level lists read as empty.
+__global__ __launch_bounds__(256) void tail_kernel(Geom geo, int searched, int tail_lo,
+                                                   int n_tail, int32_t* __restrict__ sel_idx,
+                                                   int64_t cap, int32_t* __restrict__ sel_count,
+                                                   uint32_t* __restrict__ counts,
+                                                   int count_words) {
+  const int qh = blockIdx.x;
+  const int base = searched ? sel_count[qh] : 0;
+  if (!searched && qh == 0)
+    for (int i = threadIdx.x; i < count_words; i += 256) counts[i] = 0u;
+  if (sel_idx) {
+    int32_t* sel = sel_idx + (int64_t)qh * cap + base;
+    for (int i = threadIdx.x; i < n_tail; i += 256) sel[i] = tail_lo + i;
+  }
+  __syncthreads();  // every thread has read the count
+  if (threadIdx.x == 0) sel_count[qh] = base + n_tail;
+}
+
 // --------------------------------------------------------------------------- compaction
 // The members' kept-flag rows are ORed into a member mask per frontier entry; entries with
 // a non-empty mask, in ascending order, form the level's union list. The frontier is cut
@@ -1906,6 +1928,15 @@ hipError_t launch_top_levels(const Geom& geo, const float* pyramid, const LevelB
 }
 
 int64_t top_bitmap_words(int QH, int L) { return (int64_t)QH * (L + 1) * kTopWords; }
+
+hipError_t launch_tail(const Geom& geo, int searched, int tail_lo, int n_tail,
+                       int32_t* sel_idx, int64_t cap, int32_t* sel_count, uint32_t* counts,
+                       int count_words, hipStream_t s) {
+  const int QH = geo.B * geo.T * geo.Hq;
+  hipLaunchKernelGGL(tail_kernel, dim3(QH), dim3(256), 0, s, geo, searched, tail_lo, n_tail,
+                     sel_idx, cap, sel_count, counts, count_words);
+  return hipGetLastError();
+}
 
 hipError_t launch_union(const Geom& geo, int level, const float* S, int64_t S_stride,
                         const LevelBufs* parent, int n_top, const LevelBufs& cur, int anchor,
