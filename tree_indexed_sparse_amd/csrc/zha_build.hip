@@ -190,7 +190,7 @@ struct PoolOut {
 
 __device__ __forceinline__ uint4 lds16(const uint32_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
-template <typename Tin, typename Tr, int D>
+template <typename Tin, typename Tr, int D, bool MASKED>
 __global__ __launch_bounds__(kPoolThreads) void pool_tile_kernel(
     const Tin* __restrict__ child, int64_t in_unit_stride, const Tr* __restrict__ Rall,
     PoolOut out, int nlev, int Hkv, int tile_begin, int tile_end, int row_limit, int b,
@@ -266,7 +266,7 @@ __global__ __launch_bounds__(kPoolThreads) void pool_tile_kernel(
     int rows = TR;
     // child rows at or past row_limit are not cached yet: only nodes whose children are all
     // valid are stored (the others only feed nodes that are not stored either)
-    int vrows = min(TR, row_limit - t * TR);
+    int vrows = MASKED ? min(TR, row_limit - t * TR) : TR;
     for (int j = 0; j < nlev; ++j) {
       const bool bf_in = kBF && j == 0;
       const float* inF = (j == 0) ? reinterpret_cast<const float*>(sIn) : sY[(j - 1) & 1];
@@ -361,7 +361,7 @@ __global__ __launch_bounds__(kPoolThreads) void pool_tile_kernel(
 constexpr int kWaveRows = 64;
 constexpr int kWaveTilesPerWave = 2;
 
-template <int D>
+template <int D, bool MASKED>
 __global__ __launch_bounds__(kPoolThreads) void pool_wave_b4_kernel(
     const bf16_t* __restrict__ child, int64_t in_unit_stride, const bf16_t* __restrict__ Rall,
     PoolOut out, int nlev, int Hkv, int tile_begin, int tile_end, int row_limit, float tau) {
@@ -421,7 +421,7 @@ __global__ __launch_bounds__(kPoolThreads) void pool_wave_b4_kernel(
     if (t >= tile_end) break;
     const bf16_t* src = child + unit * in_unit_stride + (int64_t)t * kWaveRows * D;
     // rows at or past row_limit are not cached yet: only complete nodes are stored
-    const int vrows = min(kWaveRows, row_limit - t * kWaveRows);
+    const int vrows = MASKED ? min(kWaveRows, row_limit - t * kWaveRows) : kWaveRows;
     uint4 a[4][KC];
 #pragma unroll
     for (int blk = 0; blk < 4; ++blk)
@@ -669,9 +669,15 @@ hipError_t launch_wave_b4(const void* child, int64_t in_unit_stride, const void*
   if (t1 <= t0) return hipSuccess;
   const int per_wg = (kPoolThreads / 64) * kWaveTilesPerWave;
   dim3 grid((t1 - t0 + per_wg - 1) / per_wg, units);
-  hipLaunchKernelGGL((pool_wave_b4_kernel<D>), grid, dim3(kPoolThreads), 0, s,
-                     (const bf16_t*)child, in_unit_stride, (const bf16_t*)R, out, nlev, Hkv, t0,
-                     t1, row_limit, 1.0f / sqrtf((float)D));
+  // tiles that all lie below row_limit store every node: the unmasked form
+  if (row_limit >= row_end)
+    hipLaunchKernelGGL((pool_wave_b4_kernel<D, false>), grid, dim3(kPoolThreads), 0, s,
+                       (const bf16_t*)child, in_unit_stride, (const bf16_t*)R, out, nlev, Hkv, t0,
+                       t1, row_limit, 1.0f / sqrtf((float)D));
+  else
+    hipLaunchKernelGGL((pool_wave_b4_kernel<D, true>), grid, dim3(kPoolThreads), 0, s,
+                       (const bf16_t*)child, in_unit_stride, (const bf16_t*)R, out, nlev, Hkv, t0,
+                       t1, row_limit, 1.0f / sqrtf((float)D));
   return hipGetLastError();
 }
 
@@ -723,9 +729,14 @@ hipError_t launch_tile_t(const void* child, int64_t in_unit_stride, const void* 
   const int t0 = row_begin / TR, t1 = row_end / TR;
   if (t1 <= t0) return hipSuccess;
   dim3 grid((t1 - t0 + kTilesPerWG - 1) / kTilesPerWG, units);
-  hipLaunchKernelGGL((pool_tile_kernel<Tin, Tr, D>), grid, dim3(kPoolThreads), 0, s,
-                     (const Tin*)child, in_unit_stride, (const Tr*)R, out, nlev, Hkv, t0, t1,
-                     row_limit, b, 1.0f / sqrtf((float)D));
+  if (row_limit >= row_end)
+    hipLaunchKernelGGL((pool_tile_kernel<Tin, Tr, D, false>), grid, dim3(kPoolThreads), 0, s,
+                       (const Tin*)child, in_unit_stride, (const Tr*)R, out, nlev, Hkv, t0, t1,
+                       row_limit, b, 1.0f / sqrtf((float)D));
+  else
+    hipLaunchKernelGGL((pool_tile_kernel<Tin, Tr, D, true>), grid, dim3(kPoolThreads), 0, s,
+                       (const Tin*)child, in_unit_stride, (const Tr*)R, out, nlev, Hkv, t0, t1,
+                       row_limit, b, 1.0f / sqrtf((float)D));
   return hipGetLastError();
 }
 

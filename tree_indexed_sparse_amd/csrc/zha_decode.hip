@@ -254,7 +254,7 @@ struct TileRegs {
 };
 
 template <int D>
-__global__ __launch_bounds__(kDecThreads) void decode_mfma_kernel(
+__global__ __launch_bounds__(kDecThreads, 2) void decode_mfma_kernel(
     Geom geo, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
     const bf16_t* __restrict__ Q, LevelBufs l1, int has_list, int anchor, int tail_lo, int n_tail,
     int splits, float* __restrict__ part, float sigma) {
@@ -267,6 +267,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_mfma_kernel(
   constexpr int MWORDS = kDecWaves * kMaxMembers * (D + 2);
   __shared__ uint32_t smem[VWORDS > MWORDS ? VWORDS : MWORDS];
   __shared__ uint32_t s_nodes[kNodeChunk], s_masks[kNodeChunk];
+  __shared__ __align__(16) int s_tt[kDecWaves * 2 * kTile];
+  __shared__ __align__(16) uint32_t s_tm[kDecWaves * 2 * kTile];
 
   const int u = blockIdx.y, sp = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -296,40 +298,61 @@ __global__ __launch_bounds__(kDecThreads) void decode_mfma_kernel(
   for (int c = 0; c < KC; ++c) acc[c][0] = acc[c][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_part = 0.f;
 
-  // Token id and member mask of work index i. Anchor tiles cover tokens [0, anchor) for
-  // every member; node tiles read the staged list (entry i / b - nbase) and skip tokens
-  // below the anchor. Past `lim`: token 0, no member (its loads stay in bounds).
-  auto token_at = [&](int i, bool anc, int lim, int nbase) -> int {
-    if (i >= lim) return 0;
-    if (anc) return i;
-    if (i >= nnode) return tail_lo + (i - nnode);
-    const int nd = (int)geo.bdiv.div((uint32_t)i);
-    return (int)s_nodes[nd - nbase] * b + (i - nd * b);
-  };
-  auto mask_at = [&](int i, bool anc, int lim, int nbase) -> uint32_t {
-    if (i >= lim) return 0u;
-    if (anc || i >= nnode) return 0xffffu;
-    const int nd = (int)geo.bdiv.div((uint32_t)i);
-    const int t = (int)s_nodes[nd - nbase] * b + (i - nd * b);
-    return t < anchor ? 0u : s_masks[nd - nbase];
+  // Token ids and member masks of a tile are worked out once, one lane per row (lanes
+  // 0..31), by region (uniform across the wave, so the branches are scalar): anchor tiles (0)
+  // cover tokens [0, anchor) for every member; list tiles (1) read the staged list (entry
+  // i / b - nbase) and skip tokens below the anchor; tail tiles (2) map work index i to token
+  // tail_lo + (i - nnode) for every member. Past `lim`: token 0, no member (its loads stay in
+  // bounds). They go to this wave's slot in LDS; token ids are stored row-permuted so that
+  // each lane's V rows (lane / CH + RPI j) sit in adjacent words.
+  int* s_tok = s_tt + wave * 2 * kTile;
+  uint32_t* s_mk = s_tm + wave * 2 * kTile;
+  auto prepare = [&](int region, int slot, int base, int lim, int nbase) {
+    if (lane < kTile) {
+      const int i = base + lane;
+      int tok = 0;
+      uint32_t mk = 0u;
+      if (i < lim) {
+        if (region == 1) {
+          const int nd = (int)geo.bdiv.div((uint32_t)i);
+          tok = (int)s_nodes[nd - nbase] * b + (i - nd * b);
+          mk = tok < anchor ? 0u : s_masks[nd - nbase];
+        } else {
+          tok = region == 0 ? i : tail_lo + (i - nnode);
+          mk = 0xffffu;
+        }
+      }
+      s_tok[slot * kTile + (lane % RPI) * NI + lane / RPI] = tok;
+      s_mk[slot * kTile + lane] = mk;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
 
-  auto issue = [&](TileRegs<D>& R, int base, bool anc, int lim, int nbase) {
+  auto issue = [&](int region, TileRegs<D>& R, int slot, int base, int lim, int nbase) {
+    prepare(region, slot, base, lim, nbase);
+    int tv[NI];
 #pragma unroll
-    for (int j = 0; j < NI; ++j) {
-      const int tok = token_at(base + lane / CH + RPI * j, anc, lim, nbase);
-      R.v[j] = ld16_stream(Vu + (int64_t)tok * D + 8 * (lane % CH));
+    for (int j = 0; j < NI; j += 4) {
+      const int4 t4 = *reinterpret_cast<const int4*>(&s_tok[slot * kTile + (lane / CH) * NI + j]);
+      tv[j] = t4.x;
+      tv[j + 1] = t4.y;
+      tv[j + 2] = t4.z;
+      tv[j + 3] = t4.w;
     }
 #pragma unroll
+    for (int j = 0; j < NI; ++j) R.v[j] = ld16_stream(Vu + (int64_t)tv[j] * D + 8 * (lane % CH));
+#pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const int tok = token_at(base + 16 * h + mem, anc, lim, nbase);
+      const int row = 16 * h + mem;
+      const int tok = s_tok[slot * kTile + (row % RPI) * NI + row / RPI];
       const bf16_t* kr = Ku + (int64_t)tok * D + 8 * grp;
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) R.k[h][kc] = ld16_stream(kr + 32 * kc);
     }
   };
 
-  auto compute = [&](const TileRegs<D>& R, int base, bool anc, int lim, int nbase) {
+  auto compute = [&](const TileRegs<D>& R, int slot) {
     f32x4_t sc[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -348,10 +371,11 @@ __global__ __launch_bounds__(kDecThreads) void decode_mfma_kernel(
     float mloc = -INFINITY;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
+      const uint4 m4 = *reinterpret_cast<const uint4*>(&s_mk[slot * kTile + 16 * h + 4 * grp]);
+      const uint32_t mrow[4] = {m4.x, m4.y, m4.z, m4.w};
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const uint32_t mk = mask_at(base + 16 * h + 4 * grp + r, anc, lim, nbase);
-        const bool ok = mem < Mu && ((mk >> mem) & 1u);
+        const bool ok = mem < Mu && ((mrow[r] >> mem) & 1u);
         const float v = ok ? sigma * sc[h][r] : -INFINITY;
         p[4 * h + r] = v;
         mloc = fmaxf(mloc, v);
@@ -414,41 +438,54 @@ __global__ __launch_bounds__(kDecThreads) void decode_mfma_kernel(
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
 
+  // wave tiles from `base` to `lim`, step kDecWaves tiles, the next tile's loads in flight
+  const int step = kDecWaves * kTile;
+  auto run_tiles = [&](int region, int base, int lim, int nbase) {
+    if (base >= lim) return;
+    TileRegs<D> A, Bq;
+    issue(region, A, 0, base, lim, nbase);
+    while (true) {
+      const int n1 = base + step;
+      issue(region, Bq, 1, n1, lim, nbase);  // past lim this reads token 0, masked out
+      compute(A, 0);
+      if (n1 >= lim) break;
+      const int n2 = n1 + step;
+      issue(region, A, 0, n2, lim, nbase);
+      compute(Bq, 1);
+      if (n2 >= lim) break;
+      base = n2;
+    }
+  };
+
   if (sp == 0 && wave == 0) {
     for (int base = 0; base < anchor; base += kTile) {
       TileRegs<D> R;
-      issue(R, base, true, anchor, 0);
-      compute(R, base, true, anchor, 0);
+      issue(0, R, 0, base, anchor, 0);
+      compute(R, 0);
     }
   }
 
-  // node tiles, in chunks of the union list small enough to stage in LDS
+  // list tiles, in chunks of the union list small enough to stage in LDS, then the tail
+  // (region 2) as one more chunk that stages nothing
   const int span = ((kNodeChunk - 1) * b) / kTile * kTile;  // tokens per chunk
-  const int step = kDecWaves * kTile;
-  for (int c0 = t0; c0 < t1; c0 += span) {
-    const int c1 = min(c0 + span, t1);
-    const int nbase = c0 / b, nend = min((c1 - 1) / b + 1, ncount);  // list part only
-    __syncthreads();
-    for (int i = threadIdx.x; i < nend - nbase; i += kDecThreads) {
-      s_nodes[i] = nodes[nbase + i];
-      s_masks[i] = masks[nbase + i];
+  const int l_end = min(t1, nnode);
+  const int a0 = max(t0, nnode);
+  for (int c0 = t0; c0 < t1;) {
+    const bool tail = c0 >= l_end;
+    const int c1 = tail ? t1 : min(c0 + span, l_end);
+    const int nbase = c0 / b;
+    if (!tail) {
+      const int nend = (c1 - 1) / b + 1;
+      __syncthreads();
+      for (int i = threadIdx.x; i < nend - nbase; i += kDecThreads) {
+        s_nodes[i] = nodes[nbase + i];
+        s_masks[i] = masks[nbase + i];
+      }
+      __syncthreads();
     }
-    __syncthreads();
-    int base = c0 + wave * kTile;
-    if (base >= c1) continue;
-    TileRegs<D> A, Bq;
-    issue(A, base, false, c1, nbase);
-    while (true) {
-      const int n1 = base + step;
-      issue(Bq, n1, false, c1, nbase);  // past c1 this reads token 0, masked out
-      compute(A, base, false, c1, nbase);
-      if (n1 >= c1) break;
-      const int n2 = n1 + step;
-      issue(A, n2, false, c1, nbase);
-      compute(Bq, n1, false, c1, nbase);
-      if (n2 >= c1) break;
-      base = n2;
-    }
+    const int start = tail ? a0 : c0;
+    run_tiles(tail ? 2 : 1, start + wave * kTile, c1, nbase);
+    c0 = tail ? t1 : c1;
   }
 
   // per-member totals over the 4 lanes of a member, then hand the states to LDS
