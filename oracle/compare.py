@@ -73,16 +73,19 @@ class HeadReport:
 
 
 def check_head(q, levels, K_u, V_u, b, L, p, anchor, lists_by_level, u, m, sel_row, count,
-               O_gpu, qh=None) -> HeadReport:
-    """Guided comparison of one query head. lists_by_level[l] = level_view(...) at level l."""
+               O_gpu, qh=None, fp4=False) -> HeadReport:
+    """Guided comparison of one query head. lists_by_level[l] = level_view(...) at level l.
+    fp4: the descent scored MXFP4 summaries with an MXFP4 query (the FP4 router); the
+    final attention uses the unquantised query either way."""
     p = float(np.float32(p))
     rep = HeadReport(qh=qh, exact_unguided=None)
     n_top = levels[L].shape[0]
+    q_r, levels_r = (O.mxfp4_round_trip(q), O.router_levels(levels)) if fp4 else (q, levels)
     F = np.arange(n_top, dtype=np.int64)
     kept = F
     for l in (range(L, 0, -1) if n_top else ()):
         Gk = gpu_kept(lists_by_level[l], u, m)
-        s = O.node_scores(levels[l][F], q)
+        s = O.node_scores(levels_r[l][F], q_r)
         kept_o, fragile = O.select_top_p(F, s, p)
         if not np.array_equal(Gk, kept_o):
             if not fragile or not _fragile_ok(F, s, kept_o, Gk):
@@ -108,7 +111,7 @@ def check_head(q, levels, K_u, V_u, b, L, p, anchor, lists_by_level, u, m, sel_r
     rep.keys = S_want.size
     O_want = O.attention_over(q, K_u, V_u, S_want)
     rep.o_err = float(np.max(np.abs(np.asarray(O_gpu, np.float64) - O_want)))
-    S_own, decs = O.search(q, levels, b, L, p, anchor)
+    S_own, decs = O.search(q_r, levels_r, b, L, p, anchor)
     if not any(d.fragile for d in decs):
         rep.exact_unguided = bool(np.array_equal(S_own, S_want))
         if not rep.exact_unguided:

@@ -226,6 +226,100 @@ def search(q: np.ndarray, levels: list, b: int, L: int, p: float, anchor: int):
     return S, decisions
 
 
+# ---------------------------------------------------------------------------
+# Router in FP4 (page 3, paragraph 4: a variant of the router in FP4 was also
+# tested; nothing more is said). Reading: the router is what decides which keys a
+# query reads, i.e. the summary keys and the node scores. Both operands of every
+# node score are held in MXFP4 (OCP Microscaling Formats v1.0: blocks of 32
+# elements along d, E2M1 elements, one E8M0 power-of-two scale per block) and the
+# dot products are exact sums of their products, stored float32 like the float32
+# router's scores. The pyramid itself is built in float32 as above and quantised
+# level by level; the final attention still uses the unquantised query and keys.
+# ---------------------------------------------------------------------------
+
+MX_BLOCK = 32          # elements per shared scale (OCP MX v1.0)
+E2M1_EMAX = 2          # exponent of the largest normal E2M1 value (6 = 1.5 * 2^2)
+
+
+def e2m1_value(code: int) -> float:
+    """Value of a 4-bit E2M1 code from the format's definition: sign bit 3,
+    exponent bits 2..1 (bias 1), mantissa bit 0; exponent 0 is subnormal
+    (0.5 * mantissa)."""
+    sign = -1.0 if code & 8 else 1.0
+    e, m = (code >> 1) & 3, code & 1
+    mag = 0.5 * m if e == 0 else 2.0 ** (e - 1) * (1.0 + 0.5 * m)
+    return sign * mag
+
+
+def _e2m1_round(v: np.ndarray) -> np.ndarray:
+    """E2M1 code of each value v (float64, already divided by its block scale):
+    the nearest of the 8 magnitudes after clamping to the largest (6), ties to the
+    magnitude whose mantissa bit is 0; the sign bit is the sign of v."""
+    mags = [e2m1_value(c) for c in range(8)]
+    a = np.minimum(np.abs(v), mags[-1])
+    idx = np.zeros(a.shape, np.int64)
+    best = np.abs(a - mags[0])
+    for c in range(1, 8):
+        dist = np.abs(a - mags[c])
+        # strictly nearer, or equally near with mantissa bit 0 (the even one)
+        take = (dist < best) | ((dist == best) & (c % 2 == 0))
+        idx = np.where(take, c, idx)
+        best = np.where(take, dist, best)
+    return (idx | np.where(np.signbit(v), 8, 0)).astype(np.uint8)
+
+
+def mxfp4_quantize(x: np.ndarray):
+    """MXFP4 encoding of float32 rows x [..., d] (d a multiple of 32).
+
+    Returns (codes uint8 [..., d], one 4-bit code per element, and scale exponents
+    int16 [..., d / 32]). Per block: X = floor(log2(max |x|)) - 2 clamped to
+    [-127, 127] (X = -127 for an all-zero block), and each element is the E2M1
+    rounding of x / 2^X (OCP MX v1.0, conversion of a vector to MX format)."""
+    x = np.asarray(x, np.float32).astype(np.float64)
+    d = x.shape[-1]
+    blocks = x.reshape(x.shape[:-1] + (d // MX_BLOCK, MX_BLOCK))
+    amax = np.abs(blocks).max(axis=-1)
+    with np.errstate(divide="ignore"):
+        e = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))), -1000.0)
+    X = np.clip(e - E2M1_EMAX, -127, 127).astype(np.int16)
+    scaled = blocks / np.ldexp(1.0, X.astype(np.int64))[..., None]
+    codes = _e2m1_round(scaled).reshape(x.shape)
+    return codes, X
+
+
+def mxfp4_dequantize(codes: np.ndarray, X: np.ndarray) -> np.ndarray:
+    """float64 values of MXFP4 codes [..., d] with scale exponents [..., d / 32]."""
+    table = np.array([e2m1_value(c) for c in range(16)])
+    v = table[np.asarray(codes, np.int64)]
+    d = v.shape[-1]
+    v = v.reshape(v.shape[:-1] + (d // MX_BLOCK, MX_BLOCK))
+    return (v * np.ldexp(1.0, np.asarray(X, np.int64))[..., None]).reshape(codes.shape)
+
+
+def mxfp4_round_trip(x: np.ndarray) -> np.ndarray:
+    """x quantised to MXFP4 and read back (float64)."""
+    return mxfp4_dequantize(*mxfp4_quantize(x))
+
+
+def router_levels(levels: list) -> list:
+    """The FP4 router's view of one unit's pyramid: levels[0] (raw keys) unchanged,
+    every summary level replaced by its MXFP4 round trip."""
+    return [levels[0]] + [mxfp4_round_trip(lv) for lv in levels[1:]]
+
+
+def search_fp4(q: np.ndarray, levels: list, b: int, L: int, p: float, anchor: int):
+    """Tree descent with the FP4 router: the same search, with the query and every
+    summary level quantised to MXFP4 for the node scores."""
+    return search(mxfp4_round_trip(q), router_levels(levels), b, L, p, anchor)
+
+
+def attend_head_fp4(q, levels, K_u, V_u, b, L, p, anchor=1) -> HeadResult:
+    """FP4-router search, then exact attention of the unquantised query over the
+    selected keys."""
+    S, decisions = search_fp4(q, levels, b, L, p, anchor)
+    return HeadResult(attention_over(q, K_u, V_u, S), S, decisions)
+
+
 def attention_over(q: np.ndarray, K_u: np.ndarray, V_u: np.ndarray, S: np.ndarray) -> np.ndarray:
     """Exact softmax attention of q over the keys/values with ids in S
     (scale sigma), float64."""

@@ -409,3 +409,154 @@ def test_no_complete_top_node_is_dense_attention(N, L):
     r = O.attend_head(q, levels, K, V, b, L, 0.5, anchor=1)
     assert r.S.tolist() == list(range(N)) and r.levels == []
     np.testing.assert_allclose(r.O, _sdpa(q, K, V), rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# FP4 router: MXFP4 encoding (OCP Microscaling Formats v1.0), pinned to the
+# specification's stated properties and to numpy's IEEE round-half-even.
+# ---------------------------------------------------------------------------
+
+MX_GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "e2m1_mx.txt")
+
+
+def _mx_facts():
+    out = {}
+    for line in open(MX_GOLDEN):
+        if line.startswith("#") or not line.strip():
+            continue
+        k, v = line.split()
+        out[k] = float(v)
+    return out
+
+
+def test_e2m1_values_match_the_specification():
+    f = _mx_facts()
+    vals = [O.e2m1_value(c) for c in range(16)]
+    mags = sorted(set(abs(v) for v in vals))
+    assert len(mags) == 8 and mags[0] == 0.0
+    assert max(mags) == f["e2m1_max_normal"]
+    normals = [O.e2m1_value(c) for c in range(8) if (c >> 1) & 3]
+    subnormals = [O.e2m1_value(c) for c in range(8) if not (c >> 1) & 3 and c & 1]
+    assert min(normals) == f["e2m1_min_normal"]
+    assert subnormals == [f["e2m1_max_subnormal"]] == [f["e2m1_min_subnormal"]]
+    assert np.log2(f["e2m1_max_normal"] / 1.5) == f["e2m1_emax"]
+    for c in range(8):   # sign bit mirrors every magnitude
+        assert O.e2m1_value(c | 8) == -O.e2m1_value(c)
+    assert O.MX_BLOCK == f["mx_block_size"]
+
+
+def _rne_binade(a):
+    """E2M1 rounding of magnitudes a (already scaled) by numpy's round-half-even on each
+    binade's uniform grid: spacing 0.5 below 2, 1 in [2, 4), 2 in [4, 8); clamp to 6."""
+    r = np.where(a < 2, np.rint(a * 2) / 2, np.where(a < 4, np.rint(a), 2 * np.rint(a / 2)))
+    return np.minimum(r, 6.0)
+
+
+def test_e2m1_rounding_is_round_half_even():
+    rng = _rng(71)
+    ties = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 7.0])
+    a = np.concatenate([ties, rng.uniform(0, 7.99, 4000), np.arange(0, 8, 0.125)])
+    a = a[: (a.size // 32) * 32]
+    # one element of 6 per block fixes the scale at 2^0 whatever the others are
+    blocks = a.reshape(-1, 32).copy()
+    blocks[:, 0] = 6.0
+    codes, X = O.mxfp4_quantize(blocks.astype(np.float32))
+    assert np.all(X == 0)
+    got = np.abs(O.mxfp4_dequantize(codes, X))
+    np.testing.assert_array_equal(got, _rne_binade(blocks.astype(np.float32).astype(np.float64)))
+
+
+def test_mxfp4_shared_scale():
+    f = _mx_facts()
+    lo, hi = int(f["e8m0_min_exponent"]), int(f["e8m0_max_exponent"])
+    emax = int(f["e2m1_emax"])
+    for k in (-20, -3, 0, 1, 7, 30):
+        for m in (1.0, 1.5, 1.999):
+            x = np.zeros((1, 32), np.float32)
+            x[0, 5] = -m * 2.0 ** k
+            x[0, 9] = 0.3 * 2.0 ** k
+            _, X = O.mxfp4_quantize(x)
+            assert int(X[0, 0]) == k - emax
+    _, X = O.mxfp4_quantize(np.zeros((1, 32), np.float32))
+    assert int(X[0, 0]) == lo
+    # float32 stays below 2^128, so the upper clamp is never reached: X <= 125
+    big = np.full((1, 32), 2.0 ** 127, np.float32)
+    codes, X = O.mxfp4_quantize(big)
+    assert int(X[0, 0]) == 127 - emax < hi
+    assert np.all(O.mxfp4_dequantize(codes, X) == 2.0 ** 127)
+    tiny = np.full((1, 32), 2.0 ** -140, np.float32)
+    _, X = O.mxfp4_quantize(tiny)
+    assert int(X[0, 0]) == lo
+
+
+def test_mxfp4_round_trip_of_representable_blocks():
+    rng = _rng(72)
+    codes = rng.integers(0, 16, size=(200, 128)).astype(np.uint8)
+    codes[:, ::32] = rng.choice([6, 7, 14, 15], size=(200, 4))   # a magnitude of 4 or 6
+    X = rng.integers(-40, 40, size=(200, 4)).astype(np.int16)
+    x = O.mxfp4_dequantize(codes, X)
+    assert np.all(x.astype(np.float32).astype(np.float64) == x)
+    c2, X2 = O.mxfp4_quantize(x.astype(np.float32))
+    np.testing.assert_array_equal(X2, X)
+    np.testing.assert_array_equal(c2, codes)
+
+
+def test_mxfp4_error_bound_and_sign_symmetry():
+    rng = _rng(73)
+    x = (rng.standard_normal((300, 64)) * np.exp(rng.uniform(-8, 8, (300, 1)))).astype(np.float32)
+    codes, X = O.mxfp4_quantize(x)
+    deq = O.mxfp4_dequantize(codes, X)
+    unit = np.repeat(np.ldexp(1.0, X.astype(np.int64)), 32, axis=1)
+    err = np.abs(deq - x.astype(np.float64))
+    scaled = np.abs(x.astype(np.float64)) / unit
+    # half the grid spacing of the element's binade; the clamp above 6 costs at most 2
+    half = np.where(scaled < 2, 0.25, np.where(scaled < 4, 0.5, 1.0))
+    assert np.all(err[scaled <= 6] <= half[scaled <= 6] * unit[scaled <= 6])
+    assert np.all(err <= 2 * unit)
+    amax = np.repeat(np.abs(x).reshape(300, 2, 32).max(axis=2), 32, axis=1)
+    assert np.all(err <= amax / 4 + 1e-300)
+    cn, Xn = O.mxfp4_quantize(-x)
+    np.testing.assert_array_equal(Xn, X)
+    np.testing.assert_array_equal(cn, codes ^ 8)
+
+
+def test_fp4_router_search_reduces_to_the_float_search_on_representable_inputs():
+    """When the query and every summary row are already MXFP4 values, quantising changes
+    nothing, so the FP4-router descent must be the float32-router descent."""
+    rng = _rng(74)
+    b, L, d = 4, 3, 64
+    N = 2 * b ** L
+    K = rng.standard_normal((N, d)).astype(np.float32)
+    levels = [K]
+    for l in range(1, L + 1):
+        n = N // b ** l
+        c = rng.integers(0, 16, size=(n, d)).astype(np.uint8)
+        Xs = rng.integers(-6, 2, size=(n, d // 32)).astype(np.int16)
+        levels.append(O.mxfp4_dequantize(c, Xs).astype(np.float32))
+    for t in range(20):
+        cq = rng.integers(0, 16, size=(1, d)).astype(np.uint8)
+        q = O.mxfp4_dequantize(cq, np.zeros((1, d // 32), np.int16))[0].astype(np.float32)
+        S_f, dec_f = O.search(q, levels, b, L, 0.9, 1)
+        S_4, dec_4 = O.search_fp4(q, levels, b, L, 0.9, 1)
+        np.testing.assert_array_equal(S_f, S_4)
+        for a, c in zip(dec_f, dec_4):
+            np.testing.assert_array_equal(a.scores, c.scores)
+
+
+def test_fp4_router_quantises_the_router_only():
+    """The FP4 descent scores quantised rows with a quantised query, and the final
+    attention is exact over the keys it selects with the unquantised query."""
+    rng = _rng(75)
+    b, L, d, N = 4, 2, 64, 256
+    K = rng.standard_normal((N, d)).astype(np.float32)
+    V = rng.standard_normal((N, d)).astype(np.float32)
+    R = (rng.standard_normal((16, d)) / np.sqrt(d)).astype(np.float32)
+    levels = O.build_tree_unit(K, R, b, L)
+    q = rng.standard_normal(d).astype(np.float32)
+    res = O.attend_head_fp4(q, levels, K, V, b, L, 0.9, 1)
+    mask = np.zeros(N, bool)
+    mask[res.S] = True
+    np.testing.assert_allclose(res.O, _sdpa(q, K, V, mask), rtol=1e-12, atol=1e-12)
+    top = res.levels[0]
+    want = O.node_scores(O.mxfp4_round_trip(levels[L]), O.mxfp4_round_trip(q))
+    np.testing.assert_array_equal(top.scores, want)
