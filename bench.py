@@ -138,6 +138,21 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / steps, (time.perf_counter() - w0) * 1e3 / steps
 
+    def per_step(fn, steps):
+        # each repetition between its own pair of events: spread of the step time
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        torch.cuda.synchronize()
+        for a, z in ev:
+            a.record()
+            fn()
+            z.record()
+        torch.cuda.synchronize()
+        t = np.array([a.elapsed_time(z) for a, z in ev])
+        return {"p10": round(float(np.percentile(t, 10)), 4),
+                "median": round(float(np.median(t)), 4),
+                "p90": round(float(np.percentile(t, 90)), 4), "reps": steps}
+
     for _ in range(args.warmup):
         full_step()
     torch.cuda.synchronize()
@@ -149,6 +164,7 @@ def main():
     # of the build and of the attend) is captured once as a HIP graph and replayed: the
     # launch-bound small kernels of the search then run without per-launch host overhead.
     ms_step, ms_attend, graph = ms_eager, ms_attend_eager, False
+    dist = None
     if not args.no_graph:
         def capture(fn):
             side = torch.cuda.Stream()
@@ -168,6 +184,7 @@ def main():
             g_step.replay()
         ms_step, wall_step = timed(g_step.replay, args.steps)
         ms_attend, _ = timed(g_attend.replay, args.steps)
+        dist = per_step(g_step.replay, args.steps)
         graph = True
         print(f"# graph step {ms_step:.3f} ms (wall {wall_step:.3f} ms)", file=sys.stderr,
               flush=True)
@@ -311,6 +328,7 @@ def main():
         "ms_per_step": round(ms_step, 4),
         "timing": "HIP graph replay of the captured step" if graph else "eager launches",
         "eager_ms_per_step": round(ms_eager, 4),
+        "step_ms_spread": dist if dist is not None else per_step(full_step, args.steps),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -344,7 +362,7 @@ def main():
         "time_split_ms": {
             "build": round(sum(v["avg_ms"] for k, v in kernels.items() if k.startswith("pool")), 4),
             "index": round(sum(v["avg_ms"] for k, v in kernels.items()
-                               if k.startswith(("score", "select", "compact"))), 4),
+                               if k.startswith(("score", "select", "compact", "descent"))), 4),
             "attend": round(sum(v["avg_ms"] for k, v in kernels.items()
                                 if k in ("decode", "combine")), 4),
             "timed_pass_ms_per_step": round(ms_timed_pass, 4)},
