@@ -43,7 +43,7 @@ extern "C" {
 typedef enum {
   ZHA_OK = 0,
   ZHA_ERR_INVALID_ARG = -1, /* null or misaligned pointer, p not in (0, 1], anchor out of
-                               range, b < 2, L < 1 */
+                               range, b < 2, L < 1, unknown router or no router copy */
   ZHA_ERR_SHAPE = -2,       /* N_cap % b^L != 0, Hq % Hkv != 0, N > N_cap, buffer too small */
   ZHA_ERR_DTYPE = -3,       /* unknown dtype */
   ZHA_ERR_CAPACITY = -4,    /* selected-list capacity smaller than N */
@@ -52,6 +52,14 @@ typedef enum {
 } zha_status;
 
 typedef enum { ZHA_F32 = 0, ZHA_BF16 = 1 } zha_dtype;
+
+/*
+ * Which copy of the summary keys the search scores (page 3, paragraph 4: a variant of the
+ * router in FP4 was also tested). ZHA_ROUTER_F32: the float32 pyramid. ZHA_ROUTER_MXFP4:
+ * an MXFP4 copy written by zha_router_quantize; the query is quantised the same way and
+ * every node score is sigma times the float32-accumulated dot product of the two.
+ */
+typedef enum { ZHA_ROUTER_F32 = 0, ZHA_ROUTER_MXFP4 = 1 } zha_router;
 
 #define ZHA_MAX_LEVELS 12
 #define ZHA_N_REF 16 /* reference queries per KV head (page 3, paragraph 1) */
@@ -63,12 +71,24 @@ typedef enum { ZHA_F32 = 0, ZHA_BF16 = 1 } zha_dtype;
  * [j * b^l, (j + 1) * b^l) and exists once all of them are cached: with N cached tokens,
  * nodes 0 .. N / b^l - 1 (integer division) are valid. Levels are written by
  * zha_build_tree / zha_tree_append.
+ *
+ * MXFP4 router copy (zha_router_quantize): level l's node j, in unit u = b * Hkv + g, has
+ * d / 2 code bytes at router_data + router_code_off[l] + (u * (N_cap / b^l) + j) * d / 2
+ * (element 2i in the low nibble of byte i, element 2i + 1 in the high nibble; E2M1 codes:
+ * sign bit 3, exponent bits 2..1 with bias 1, mantissa bit 0) and d / 32 scale bytes at
+ * router_data + router_scale_off[l] + (u * (N_cap / b^l) + j) * d / 32 (E8M0: the block of
+ * elements 32k .. 32k + 31 is scaled by 2^(byte - 127)). zha_build_tree sets router to
+ * ZHA_ROUTER_F32 and router_data to NULL.
  */
 typedef struct {
   int32_t B, Hkv, N, N_cap, d, b, L;
   int32_t dtype;                              /* zha_dtype of the keys it was built from */
   int64_t level_off[ZHA_MAX_LEVELS + 1];      /* float offset of level l; [0] unused (= 0) */
   float* pyramid;                             /* device */
+  int32_t router;                             /* zha_router: the copy zha_attend scores */
+  int64_t router_code_off[ZHA_MAX_LEVELS + 1];  /* byte offsets into router_data */
+  int64_t router_scale_off[ZHA_MAX_LEVELS + 1];
+  uint8_t* router_data;                       /* device, or NULL: no MXFP4 copy */
 } zha_tree;
 
 /* Bytes of pyramid storage for a cache of capacity N_cap (0 if the geometry is invalid). */
@@ -90,13 +110,33 @@ int zha_build_tree(const void* K, const void* ref_queries, int dtype, int B, int
                    int N_cap, int d, int b, int L, void* pyramid, size_t pyramid_bytes,
                    zha_tree* out, void* stream);
 
+/* Bytes of MXFP4 router storage for a tree of this geometry (0 if the geometry is invalid). */
+size_t zha_router_bytes(int B, int Hkv, int N_cap, int d, int b, int L);
+
+/*
+ * Write the MXFP4 copy of the pyramid the FP4 router scores (page 3, paragraph 4), and
+ * select it: t->router = ZHA_ROUTER_MXFP4, t->router_data = router_data, offsets set.
+ * Encodes, at every level l, the nodes complete at t->N tokens that were not complete at
+ * n_from tokens (nodes [n_from / b^l, N / b^l); n_from = 0 encodes every node), from the
+ * float32 pyramid, following OCP Microscaling Formats v1.0: per block of 32 elements,
+ * X = floor(log2(max |x|)) - 2 (clamped to >= -127; -127 for an all-zero block), and each
+ * element is x / 2^X rounded to the nearest E2M1 value (ties to the even mantissa) after
+ * clamping to +-6, with the sign of x.
+ *   router_data  device, 16-byte aligned, at least zha_router_bytes(...) bytes
+ *   0 <= n_from <= t->N
+ * Once a tree has a router copy, zha_tree_append encodes the nodes it completes. Setting
+ * t->router back to ZHA_ROUTER_F32 makes zha_attend score the float32 pyramid again.
+ */
+int zha_router_quantize(zha_tree* t, int n_from, void* router_data, size_t router_bytes,
+                        void* stream);
+
 /*
  * Extend a tree by n_new >= 0 tokens (one at a time during generation, or in chunks):
  * pools, at every level, exactly the nodes the new tokens complete, then sets
  * t->N += n_new; t->N + n_new <= t->N_cap. A node's summary depends only on the tokens
  * under it, so any sequence of appends gives the pyramid one zha_build_tree over the same
  * tokens gives. K and ref_queries as for zha_build_tree (same cache, same reference
- * queries).
+ * queries). With an MXFP4 router copy (t->router_data set), the new nodes are encoded too.
  */
 int zha_tree_append(zha_tree* t, const void* K, const void* ref_queries, int n_new, void* stream);
 
@@ -128,7 +168,9 @@ size_t zha_attend_workspace_bytes(const zha_tree* t, int T, int Hq);
  * (N / b^L of them); the tail, tokens [(N / b^L) * b^L, N), is selected for every head
  * (with no complete top node, every token is). O is exact softmax attention at scale
  * sigma over the selected tokens, accumulated in float32. Calls that share a workspace
- * must not overlap.
+ * must not overlap. With t->router == ZHA_ROUTER_MXFP4 the node scores are computed from
+ * the MXFP4 copy and the query quantised the same way (t->router_data must be set); the
+ * final attention is unchanged.
  */
 int zha_attend(const zha_tree* t, const void* Q, int T, int Hq, const void* K, const void* V,
                float p, int anchor, float* O, int32_t* sel_idx, int64_t cap,
@@ -182,7 +224,8 @@ enum {
   ZHA_K_DECODE = 4,
   ZHA_K_COMPACT = 5,
   ZHA_K_COMBINE = 6,
-  ZHA_K_DESCENT = 7
+  ZHA_K_DESCENT = 7,
+  ZHA_K_ROUTER = 8 /* MXFP4 encoding of pyramid rows (level 0: every level of one call) */
 };
 int zha_timing_enable(int on);
 int zha_timing_read(int kind, int level, double* total_ms, int64_t* launches);

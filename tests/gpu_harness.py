@@ -19,7 +19,8 @@ import workloads as W  # noqa: E402
 
 
 def run_gpu(spec, p, anchor=1, inputs=None, want_lists=True, tree=None, device="cuda", N=None):
-    """N: tokens in use (default: the whole generated cache, its capacity)."""
+    """N: tokens in use (default: the whole generated cache, its capacity). The tree's
+    router field decides which copy of the summaries the search scores."""
     inp = inputs if inputs is not None else W.gen_all(spec, device=device)
     if tree is None:
         tree = Z.build_tree(inp["K"], inp["R"], spec["b"], spec["L"], N=N)
@@ -41,9 +42,10 @@ def oracle_unit(spec, b, g, Q=None, R=None):
 
 
 def check_units(spec, res, p, anchor=1, units=None, check_pyramid=True, oracle_levels=None,
-                n_tokens=None):
+                n_tokens=None, fp4=False):
     """Guided comparison of every query head of the given (sequence, KV head) units.
     n_tokens: the cache holds only the first n_tokens generated tokens (a ragged cache).
+    fp4: the search scored the MXFP4 router (the oracle's reading of the FP4 router).
     Returns (list of HeadReport, max pyramid relative error)."""
     B, T, Hq, Hkv = spec["B"], spec["T"], spec["Hq"], spec["Hkv"]
     G = Hq // Hkv
@@ -75,5 +77,6 @@ def check_units(spec, res, p, anchor=1, units=None, check_pyramid=True, oracle_l
                 sel_row = None if res["sel"] is None else res["sel"][b, t, h]
                 reports.append(C.check_head(Q[b, t, h], levels, K_u, V_u, spec["b"], spec["L"], p,
                                             anchor, res["lists"], u, m, sel_row,
-                                            res["cnt"][b, t, h], res["O"][b, t, h], qh=(b, t, h)))
+                                            res["cnt"][b, t, h], res["O"][b, t, h], qh=(b, t, h),
+                                            fp4=fp4))
     return reports, pyr_err

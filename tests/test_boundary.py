@@ -160,3 +160,47 @@ def test_dense_workspace_bytes(lib):
     assert n >= 16 * 16 * 130 * 4          # one (d + 2)-float partial per member and split
     assert lib.zha_dense_workspace_bytes(1, 1, 0, 4096, 64, 1, 1) == 0
     assert lib.zha_dense_workspace_bytes(1, 1, 4096, 4096, 96, 1, 1) == 0
+
+
+def test_router_bytes_closed_form(lib):
+    # per level: d/2 code bytes and d/32 scale bytes per node, each array rounded to 256 B
+    def want(B, H, N, d, b, Ll):
+        tot = 0
+        for l in range(1, Ll + 1):
+            rows = B * H * (N // b ** l)
+            tot = (tot + rows * d // 2 + 255) // 256 * 256
+            tot = (tot + rows * d // 32 + 255) // 256 * 256
+        return tot
+    assert lib.zha_router_bytes(4, 4, 262144, 128, 4, 6) == want(4, 4, 262144, 128, 4, 6)
+    assert lib.zha_router_bytes(1, 1, 4096, 64, 4, 3) == want(1, 1, 4096, 64, 4, 3)
+    assert lib.zha_router_bytes(1, 1, 4096, 96, 4, 3) == 0
+    assert lib.zha_router_bytes(1, 1, 4000, 64, 4, 3) == 0
+    # the MXFP4 copy is 17/128 of the float32 pyramid at d = 128 (68 of 512 bytes per node)
+    r = lib.zha_router_bytes(4, 4, 262144, 128, 4, 6) / lib.zha_tree_bytes(4, 4, 262144, 128, 4, 6)
+    assert abs(r - 68 / 512) < 1e-3
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(data=None), -1), (dict(data=ODD8), -1), (dict(nbytes=1024), -2),
+    (dict(n_from=-1), -2), (dict(n_from=4097), -2),
+])
+def test_router_quantize_rejects_bad_arguments(lib, kw, code):
+    a = dict(data=FAKE, nbytes=1 << 30, n_from=0)
+    a.update(kw)
+    t = _tree()
+    before = bytes(t)
+    assert lib.zha_router_quantize(ctypes.byref(t), a["n_from"], a["data"], a["nbytes"],
+                                   None) == code
+    assert len(lib.zha_last_error()) > 0
+    assert bytes(t) == before          # a rejected call leaves the tree as it was
+    assert lib.zha_router_quantize(None, 0, FAKE, 1 << 30, None) == -1
+
+
+def test_attend_rejects_bad_router_fields(lib):
+    t = _tree()
+    t.router = 1                       # MXFP4 without a copy
+    assert _attend(lib, t=t) == -1
+    t.router = 2                       # unknown
+    t.router_data = 0x3000
+    assert _attend(lib, t=t) == -1
+    assert b"router" in lib.zha_last_error()

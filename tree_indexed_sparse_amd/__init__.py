@@ -6,6 +6,7 @@ library's hand-written gfx950 kernels (libzha.so). Names follow the C entry poin
 
     tree = build_tree(K, R, b, L)             # zha_build_tree
     tree_append(tree, K, R, n_new)            # zha_tree_append
+    quantize_router(tree)                     # zha_router_quantize (the FP4 router)
     O, sel_idx, sel_count = attend(Q, K, V, tree, p, anchor=1)   # zha_attend
 """
 
@@ -16,10 +17,21 @@ from dataclasses import dataclass
 
 import torch
 
-from ._lib import ZHA_BF16, ZHA_F32, ZHA_N_REF, ZhaError, ZhaTree, check, load  # noqa: F401
+from ._lib import (  # noqa: F401
+    ZHA_BF16,
+    ZHA_F32,
+    ZHA_N_REF,
+    ZHA_ROUTER_F32,
+    ZHA_ROUTER_MXFP4,
+    ZhaError,
+    ZhaTree,
+    check,
+    load,
+)
 
 __all__ = ["Tree", "build_tree", "tree_append", "attend", "workspace_bytes", "level_view",
-           "tree_bytes", "pyramid_level", "ZhaError", "load"]
+           "tree_bytes", "pyramid_level", "router_bytes", "quantize_router", "set_router",
+           "router_level", "ZhaError", "load"]
 
 _DTYPES = {torch.float32: ZHA_F32, torch.bfloat16: ZHA_BF16}
 
@@ -48,9 +60,11 @@ def tree_bytes(B: int, Hkv: int, N_cap: int, d: int, b: int, L: int) -> int:
 
 @dataclass
 class Tree:
-    """A built pyramid: the C view plus the tensor that owns its storage."""
+    """A built pyramid: the C view plus the tensors that own its storage (the float32
+    pyramid, and the MXFP4 router copy once quantize_router made one)."""
     c: ZhaTree
     storage: torch.Tensor
+    router_storage: torch.Tensor | None = None
 
     @property
     def N(self) -> int:
@@ -94,6 +108,54 @@ def tree_append(tree: Tree, K: torch.Tensor, R: torch.Tensor, n_new: int) -> Non
     """zha_tree_append: pool tokens [N, N + n_new) and extend the tree."""
     check(load().zha_tree_append(ctypes.byref(tree.c), _dev(K, "K"), _dev(R, "R"), n_new,
                                  _stream(K.device)))
+
+
+def router_bytes(B: int, Hkv: int, N_cap: int, d: int, b: int, L: int) -> int:
+    return int(load().zha_router_bytes(B, Hkv, N_cap, d, b, L))
+
+
+def quantize_router(tree: Tree, n_from: int = 0) -> None:
+    """zha_router_quantize: encode the pyramid's nodes complete at tree.N (those not yet
+    complete at n_from tokens) as MXFP4 and make zha_attend score that copy. The copy's
+    storage is allocated on the first call and kept with the tree; later appends encode
+    the nodes they complete."""
+    c = tree.c
+    nbytes = router_bytes(c.B, c.Hkv, c.N_cap, c.d, c.b, c.L)
+    if tree.router_storage is None:
+        tree.router_storage = torch.empty(max(nbytes, 4), dtype=torch.uint8,
+                                          device=tree.storage.device)
+    check(load().zha_router_quantize(ctypes.byref(c), int(n_from),
+                                     tree.router_storage.data_ptr(), tree.router_storage.numel(),
+                                     _stream(tree.storage.device)))
+
+
+def set_router(tree: Tree, router: str) -> None:
+    """Choose which copy zha_attend scores: "f32" (the float32 pyramid) or "mxfp4" (the
+    copy quantize_router wrote)."""
+    if router == "f32":
+        tree.c.router = ZHA_ROUTER_F32
+    elif router == "mxfp4":
+        if tree.router_storage is None:
+            raise ZhaError(-1, "the tree has no MXFP4 router copy; call quantize_router")
+        tree.c.router = ZHA_ROUTER_MXFP4
+    else:
+        raise ZhaError(-1, f"unknown router {router!r}")
+
+
+def router_level(tree: Tree, level: int):
+    """Views of one level of the MXFP4 router copy: (codes [B, Hkv, N_cap / b^level, d / 2]
+    uint8, two E2M1 codes per byte, low nibble first; scales [B, Hkv, N_cap / b^level,
+    d / 32] uint8, E8M0)."""
+    c = tree.c
+    if tree.router_storage is None:
+        raise ZhaError(-1, "the tree has no MXFP4 router copy")
+    n = c.N_cap // c.b ** level
+    rows = c.B * c.Hkv * n
+    co, so = int(c.router_code_off[level]), int(c.router_scale_off[level])
+    w = tree.router_storage
+    codes = w[co:co + rows * (c.d // 2)].view(c.B, c.Hkv, n, c.d // 2)
+    scales = w[so:so + rows * (c.d // 32)].view(c.B, c.Hkv, n, c.d // 32)
+    return codes, scales
 
 
 def workspace_bytes(tree: Tree, T: int, Hq: int) -> int:

@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(HERE, "libzha.so")
 ZHA_MAX_LEVELS = 12
 ZHA_N_REF = 16
 ZHA_F32, ZHA_BF16 = 0, 1
+ZHA_ROUTER_F32, ZHA_ROUTER_MXFP4 = 0, 1
 
 STATUS = {
     0: "ZHA_OK",
@@ -32,6 +33,8 @@ EXPORTS = (
     "zha_tree_bytes",
     "zha_build_tree",
     "zha_tree_append",
+    "zha_router_bytes",
+    "zha_router_quantize",
     "zha_attend_workspace_bytes",
     "zha_attend",
     "zha_attend_level_view",
@@ -44,6 +47,7 @@ EXPORTS = (
 
 ZHA_K_POOL, ZHA_K_SCORE, ZHA_K_SELECT, ZHA_K_DECODE, ZHA_K_COMPACT, ZHA_K_COMBINE = 0, 2, 3, 4, 5, 6
 ZHA_K_DESCENT = 7
+ZHA_K_ROUTER = 8
 
 
 class ZhaError(RuntimeError):
@@ -64,6 +68,10 @@ class ZhaTree(ctypes.Structure):
         ("dtype", ctypes.c_int32),
         ("level_off", ctypes.c_int64 * (ZHA_MAX_LEVELS + 1)),
         ("pyramid", ctypes.c_void_p),
+        ("router", ctypes.c_int32),
+        ("router_code_off", ctypes.c_int64 * (ZHA_MAX_LEVELS + 1)),
+        ("router_scale_off", ctypes.c_int64 * (ZHA_MAX_LEVELS + 1)),
+        ("router_data", ctypes.c_void_p),
     ]
 
 
@@ -89,6 +97,10 @@ def load() -> ctypes.CDLL:
     lib.zha_build_tree.restype = i32
     lib.zha_tree_append.argtypes = [P(ZhaTree), vp, vp, i32, vp]
     lib.zha_tree_append.restype = i32
+    lib.zha_router_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
+    lib.zha_router_bytes.restype = sz
+    lib.zha_router_quantize.argtypes = [P(ZhaTree), i32, vp, sz, vp]
+    lib.zha_router_quantize.restype = i32
     lib.zha_attend_workspace_bytes.argtypes = [P(ZhaTree), i32, i32]
     lib.zha_attend_workspace_bytes.restype = sz
     lib.zha_attend.argtypes = [P(ZhaTree), vp, i32, i32, vp, vp, f32, i32, vp, vp, i64, vp, vp,

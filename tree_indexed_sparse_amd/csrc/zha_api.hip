@@ -209,7 +209,54 @@ int check_tree(const zha_tree* t) {
   if (!t->pyramid) return fail(ZHA_ERR_INVALID_ARG, "tree has no pyramid");
   if (t->dtype != ZHA_F32 && t->dtype != ZHA_BF16)
     return fail(ZHA_ERR_DTYPE, "unknown dtype %d", t->dtype);
+  if (t->router != ZHA_ROUTER_F32 && t->router != ZHA_ROUTER_MXFP4)
+    return fail(ZHA_ERR_INVALID_ARG, "unknown router %d", t->router);
+  if (t->router == ZHA_ROUTER_MXFP4 && !t->router_data)
+    return fail(ZHA_ERR_INVALID_ARG, "router is MXFP4 but the tree has no router copy");
   return check_geometry(t->B, t->Hkv, t->N, t->N_cap, t->d, t->b, t->L);
+}
+
+// Byte offsets of the MXFP4 router copy: per level the codes, then the scales, each
+// 256-byte aligned. Returns the total size.
+int64_t router_layout(int B, int Hkv, int N_cap, int d, int b, int L, int64_t* code_off,
+                      int64_t* scale_off) {
+  int64_t off = 0, nl = N_cap;
+  for (int l = 1; l <= L; ++l) {
+    nl /= b;
+    const int64_t rows = (int64_t)B * Hkv * nl;
+    if (code_off) code_off[l] = off;
+    off = align256(off + rows * (d / 2));
+    if (scale_off) scale_off[l] = off;
+    off = align256(off + rows * (d / 32));
+  }
+  return off;
+}
+
+// Encode, at every level, rows [n_lo / b^l, n_hi / b^l) of each unit into the router copy.
+hipError_t encode_router(const zha_tree* t, int64_t n_lo, int64_t n_hi, hipStream_t s) {
+  RouterJob job{};
+  const int rpw = router_rows_per_workgroup(t->d);
+  int wgs = 0;
+  int64_t cap = t->N_cap, div = 1;
+  for (int l = 1; l <= t->L; ++l) {
+    cap /= t->b;
+    div *= t->b;
+    const int r0 = (int)(n_lo / div), r1 = (int)(n_hi / div);
+    if (r1 <= r0) continue;
+    const int i = job.n++;
+    job.src[i] = t->pyramid + t->level_off[l];
+    job.codes[i] = t->router_data + t->router_code_off[l];
+    job.scales[i] = t->router_data + t->router_scale_off[l];
+    job.rows_cap[i] = cap;
+    job.row0[i] = r0;
+    job.row1[i] = r1;
+    job.wg0[i] = wgs;
+    wgs += (r1 - r0 + rpw - 1) / rpw;
+  }
+  if (job.n == 0) return hipSuccess;
+  return timed(ZHA_K_ROUTER, 0, s, [&] {
+    return launch_router_encode(job, t->B * t->Hkv, t->d, wgs, s);
+  });
 }
 
 }  // namespace
@@ -229,6 +276,38 @@ size_t zha_tree_bytes(int B, int Hkv, int N_cap, int d, int b, int L) {
     total = align256(total + 4 * (int64_t)B * Hkv * nl * d);
   }
   return (size_t)total;
+}
+
+size_t zha_router_bytes(int B, int Hkv, int N_cap, int d, int b, int L) {
+  const std::string saved = g_err;
+  const int st = check_geometry(B, Hkv, 0, N_cap, d, b, L);
+  g_err = saved;
+  if (st != ZHA_OK) return 0;
+  return (size_t)router_layout(B, Hkv, N_cap, d, b, L, nullptr, nullptr);
+}
+
+int zha_router_quantize(zha_tree* t, int n_from, void* router_data, size_t router_bytes,
+                        void* stream) {
+  if (!t) return fail(ZHA_ERR_INVALID_ARG, "tree is NULL");
+  if (!router_data) return fail(ZHA_ERR_INVALID_ARG, "router_data must not be NULL");
+  if (!aligned16(router_data))
+    return fail(ZHA_ERR_INVALID_ARG, "router_data must be 16-byte aligned");
+  zha_tree v = *t;  // checked as it will be once the copy is attached
+  v.router = ZHA_ROUTER_MXFP4;
+  v.router_data = (uint8_t*)router_data;
+  int st = check_tree(&v);
+  if (st != ZHA_OK) return st;
+  if (n_from < 0 || n_from > t->N)
+    return fail(ZHA_ERR_SHAPE, "n_from=%d must lie in [0, N=%d]", n_from, t->N);
+  const int64_t need = router_layout(t->B, t->Hkv, t->N_cap, t->d, t->b, t->L,
+                                     v.router_code_off, v.router_scale_off);
+  if ((int64_t)router_bytes < need)
+    return fail(ZHA_ERR_SHAPE, "router buffer has %zu bytes, needs %lld", router_bytes,
+                (long long)need);
+  const hipError_t e = encode_router(&v, n_from, v.N, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "router encode launch");
+  *t = v;
+  return ZHA_OK;
 }
 
 int zha_tree_append(zha_tree* t, const void* K, const void* R, int n_new, void* stream) {
@@ -285,6 +364,10 @@ int zha_tree_append(zha_tree* t, const void* K, const void* R, int n_new, void* 
     }
     if (e != hipSuccess) return hip_fail(e, "pooling launch");
     l += k >= 1 ? k : 1;
+  }
+  if (t->router_data) {
+    const hipError_t e = encode_router(t, n_old, n_end, s);
+    if (e != hipSuccess) return hip_fail(e, "router encode launch");
   }
   t->N += n_new;
   return ZHA_OK;
@@ -488,12 +571,21 @@ int zha_attend(const zha_tree* t, const void* Q, int T, int Hq, const void* K, c
   const int64_t n_full = (int64_t)n_top_nodes * ipow(t->b, t->L);
   const int tail_lo = searched ? (int)std::max<int64_t>(n_full, anchor) : 0;
   const int n_tail = t->N - tail_lo;
+  // FP4 router: every level is scored from the MXFP4 copy
+  const bool fp4 = t->router == ZHA_ROUTER_MXFP4;
+  RouterView rv{};
+  if (fp4) {
+    for (int l = 1; l <= t->L; ++l) {
+      rv.codes[l] = t->router_data + t->router_code_off[l];
+      rv.scales[l] = t->router_data + t->router_scale_off[l];
+    }
+  }
   // the top levels with small frontiers run fused in one launch
   const int l_top = searched ? top_levels_lowest(g, w.n) : 0;
   if (l_top) {
     e = timed(ZHA_K_DESCENT, l_top, s, [&] {
       return launch_top_levels(g, t->pyramid, lv, t->level_off, unit_stride, l_top, Q, t->dtype,
-                               p, lvl, (uint32_t*)(ws + w.off_tbits), s);
+                               p, lvl, (uint32_t*)(ws + w.off_tbits), fp4 ? &rv : nullptr, s);
     });
     if (e != hipSuccess) return hip_fail(e, "top-level descent launch");
   }
@@ -509,7 +601,7 @@ int zha_attend(const zha_tree* t, const void* Q, int T, int Hq, const void* K, c
     const WideSel* wide = select_is_wide(frontier_cap) ? &wsel : nullptr;
     e = timed(ZHA_K_SCORE, l, s, [&] {
       return launch_score(g, X, cap_l * t->d, Q, t->dtype, parent, n_top, S, w.S_stride, wide,
-                          s);
+                          fp4 ? rv.codes[l] : nullptr, fp4 ? rv.scales[l] : nullptr, cap_l, s);
     });
     if (e != hipSuccess) return hip_fail(e, "score launch");
     e = timed(ZHA_K_SELECT, l, s, [&] {

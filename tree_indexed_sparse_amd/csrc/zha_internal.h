@@ -108,6 +108,24 @@ struct WideSel {
   int64_t nuc;
 };
 
+// MXFP4 copy of the pyramid that the FP4 router scores (codes: d / 2 bytes per node, two
+// elements per byte, low nibble first; scales: d / 32 E8M0 bytes per node).
+struct RouterView {
+  const uint8_t* codes[ZHA_MAX_LEVELS + 1];   // level l base, [B*Hkv][N_cap / b^l][d / 2]
+  const uint8_t* scales[ZHA_MAX_LEVELS + 1];  // level l base, [B*Hkv][N_cap / b^l][d / 32]
+};
+
+// One router-encoding launch: rows [row0, row1) of every (sequence, KV head) at each of
+// n levels; workgroups wg0[i] .. wg0[i + 1] - 1 take level i.
+struct RouterJob {
+  const float* src[ZHA_MAX_LEVELS];
+  uint8_t* codes[ZHA_MAX_LEVELS];
+  uint8_t* scales[ZHA_MAX_LEVELS];
+  int64_t rows_cap[ZHA_MAX_LEVELS];  // rows per (sequence, KV head) of the level's storage
+  int row0[ZHA_MAX_LEVELS], row1[ZHA_MAX_LEVELS], wg0[ZHA_MAX_LEVELS];
+  int n;
+};
+
 // ---------------------------------------------------------------------------------------
 // launchers (defined in the .hip files; all enqueue on `s`, return hipGetLastError())
 // ---------------------------------------------------------------------------------------
@@ -131,9 +149,12 @@ hipError_t launch_pool_fused(int dtype_in, const void* child, int64_t in_unit_st
 
 // Scores of a level's union frontier for every member: S[qh][k].
 // wide != nullptr: also write the per-workgroup member max/min the chunked selection reads.
+// rcodes != nullptr: score the level's MXFP4 copy (rcodes / rscales, rows_cap rows per
+// unit) with the query quantised to MXFP4, instead of the float32 rows X.
 hipError_t launch_score(const Geom& geo, const float* X, int64_t X_unit_stride, const void* Q,
                         int dtype, const LevelBufs* parent, int n_top, float* S,
-                        int64_t S_stride, const WideSel* wide, hipStream_t s);
+                        int64_t S_stride, const WideSel* wide, const uint8_t* rcodes,
+                        const uint8_t* rscales, int64_t rows_cap, hipStream_t s);
 
 // Whether a frontier of up to `cap_entries` entries takes the chunked selection, and the
 // sizes of its scratch for frontiers up to `cap_entries`.
@@ -161,10 +182,11 @@ hipError_t launch_compact(const Geom& geo, const LevelBufs* parent, int n_top, K
 // levels L .. l_lo per query head and write each level's union list. bitmaps: scratch of
 // top_bitmap_words(QH, L) words.
 int top_levels_lowest(const Geom& geo, const int64_t* nodes_per_level);
+// router != nullptr: the levels are scored from the MXFP4 copy.
 hipError_t launch_top_levels(const Geom& geo, const float* pyramid, const LevelBufs* lv,
                              const int64_t* level_off, const int64_t* unit_stride, int l_lo,
                              const void* Q, int dtype, float p, int32_t* lvl_kept,
-                             uint32_t* bitmaps, hipStream_t s);
+                             uint32_t* bitmaps, const RouterView* router, hipStream_t s);
 int64_t top_bitmap_words(int QH, int L);
 
 // Compaction after the chunked selection: the members' keep flags straight from their
@@ -186,6 +208,11 @@ hipError_t launch_decode(const Geom& geo, int dtype, const void* K, const void* 
 hipError_t launch_tail(const Geom& geo, int searched, int tail_lo, int n_tail,
                        int32_t* sel_idx, int64_t cap, int32_t* sel_count, uint32_t* counts,
                        int count_words, hipStream_t s);
+
+// MXFP4 encoding of pyramid rows (the FP4 router's copy), every level of `job` at once.
+int router_rows_per_workgroup(int D);
+hipError_t launch_router_encode(const RouterJob& job, int units, int D, int workgroups,
+                                hipStream_t s);
 
 // Merge the decode partials of every split, in split order, into O.
 hipError_t launch_combine(const Geom& geo, int splits, const float* partials, float* O,

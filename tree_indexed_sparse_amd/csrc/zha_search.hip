@@ -16,12 +16,16 @@
 // One level = three launches (score, select, compact). Kernel boundaries order them; no
 // kernel here uses a device-scope fence.
 
+#include <type_traits>
+
 #include "zha_internal.h"
+#include "zha_mxfp4.h"
 
 namespace zha {
 namespace {
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kScoreThreads = 256;
 constexpr int kScoreEntries = 2048;  // most frontier entries per workgroup (512 per wave)
@@ -96,11 +100,85 @@ __device__ __forceinline__ void load_query_fragment(const bf16_t* qr, float (&qf
   }
 }
 
+// ---- FP4 router: the query and the summary rows as MXFP4 operands of
+// v_mfma_scale_f32_16x16x128_f8f6f4 (both in E2M1). Lane l (row or query column l % 16,
+// 32-element block l / 16) holds that block's 16 code bytes and its E8M0 scale byte; for
+// d = 64 the blocks 2 and 3 are zero.
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
+struct Fp4Rows {
+  uint4 c;
+  uint32_t s;
+};
+
+__device__ __forceinline__ void load_q_block(const float* qr, float (&x)[kMxBlock]) {
+#pragma unroll
+  for (int j = 0; j < kMxBlock / 4; ++j) {
+    const float4 v = reinterpret_cast<const float4*>(qr)[j];
+    x[4 * j] = v.x;
+    x[4 * j + 1] = v.y;
+    x[4 * j + 2] = v.z;
+    x[4 * j + 3] = v.w;
+  }
+}
+__device__ __forceinline__ void load_q_block(const bf16_t* qr, float (&x)[kMxBlock]) {
+#pragma unroll
+  for (int j = 0; j < kMxBlock / 8; ++j) {
+    const uint4 v = reinterpret_cast<const uint4*>(qr)[j];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[8 * j + 2 * i] = __uint_as_float(w[i] << 16);
+      x[8 * j + 2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+}
+
+// This lane's B operand: block `blk` of the query row `qr` (or zero when !active).
 template <int D, typename Tq>
+__device__ __forceinline__ void fp4_query_operand(const Tq* qr, int blk, bool active,
+                                                  uint4* codes, uint32_t* scale) {
+  float x[kMxBlock];
+  load_q_block(qr + kMxBlock * (blk % (D / kMxBlock)), x);
+  uint32_t sb;
+  const uint4 c = mx_encode_block(x, &sb);
+  const bool on = active && blk < D / kMxBlock;
+  *codes = on ? c : make_uint4(0u, 0u, 0u, 0u);
+  *scale = on ? sb : 127u;
+}
+
+// This lane's A operand: block `blk` of row `node` (a valid row). Nothing is masked: for
+// d = 64 the query's blocks 2 and 3 are zero, so those lanes' codes (re-read from blocks
+// 0 and 1) add nothing, and rows past the frontier are scored but never stored. Selecting
+// on the loaded values would make every load wait at once.
+template <int D>
+__device__ __forceinline__ void fp4_row_operand(const uint8_t* codes, const uint8_t* scales,
+                                                uint32_t node, int blk, Fp4Rows& R) {
+  constexpr int NB = D / kMxBlock;
+  R.c = __builtin_bit_cast(
+      uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(
+                 codes + (int64_t)node * (D / 2) + 16 * (blk % NB))));
+  R.s = scales[(int64_t)node * NB + blk % NB];
+}
+
+// The empty asm statement consumes the product where it is computed: without it the
+// compiler may sink the MFMA, and the selects that build its operands, into a branch that
+// only some lanes take (the score stores), although the instruction reads every lane.
+__device__ __forceinline__ f32x4_t fp4_mfma(const Fp4Rows& R, uint4 qc, uint32_t qs, f32x4_t c) {
+  const i32x8_t a = {(int)R.c.x, (int)R.c.y, (int)R.c.z, (int)R.c.w, 0, 0, 0, 0};
+  const i32x8_t b = {(int)qc.x, (int)qc.y, (int)qc.z, (int)qc.w, 0, 0, 0, 0};
+  f32x4_t d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 4, 0, (int)R.s, 0,
+                                                               (int)qs);
+  asm volatile("" : "+v"(d));
+  return d;
+}
+
+template <int D, typename Tq, bool FP4>
 __global__ __launch_bounds__(kScoreThreads) void score_kernel(
     Geom geo, const float* __restrict__ X, int64_t X_unit_stride, const Tq* __restrict__ Q,
     LevelBufs parent, int has_parent, int n_top, float* __restrict__ S, int64_t S_stride,
-    float sigma, int ent, float* __restrict__ pmax, float* __restrict__ pmin, int64_t pstride) {
+    float sigma, int ent, float* __restrict__ pmax, float* __restrict__ pmin, int64_t pstride,
+    const uint8_t* __restrict__ RC, const uint8_t* __restrict__ RS, int64_t rows_cap) {
   constexpr int NQ = D / 16;
   constexpr int kMaxParents = kScoreEntries / 2 + 2;
   const int kPerWave = ent / (kScoreThreads / 64);
@@ -129,28 +207,56 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
   }
   // query fragment: unconditional vector loads from a valid row, zeroed past the members
   float qf[NQ][4];
-  load_query_fragment<D>(Q + (int64_t)qh_of(geo, u, mem < Mu ? mem : 0) * D + 4 * grp, qf);
-  if (mem >= Mu) {
+  uint4 qc = make_uint4(0u, 0u, 0u, 0u);
+  uint32_t qs = 127u;
+  if constexpr (FP4) {
+    fp4_query_operand<D, Tq>(Q + (int64_t)qh_of(geo, u, mem < Mu ? mem : 0) * D, grp, mem < Mu,
+                             &qc, &qs);
+  } else {
+    load_query_fragment<D>(Q + (int64_t)qh_of(geo, u, mem < Mu ? mem : 0) * D + 4 * grp, qf);
+    if (mem >= Mu) {
 #pragma unroll
-    for (int q = 0; q < NQ; ++q)
+      for (int q = 0; q < NQ; ++q)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) qf[q][e] = 0.f;
+        for (int e = 0; e < 4; ++e) qf[q][e] = 0.f;
+    }
   }
   __syncthreads();
   const float* Xu = X + (int64_t)bg_of(geo, u) * X_unit_stride;
+  const uint8_t* RCu = FP4 ? RC + (int64_t)bg_of(geo, u) * rows_cap * (D / 2) : nullptr;
+  const uint8_t* RSu = FP4 ? RS + (int64_t)bg_of(geo, u) * rows_cap * (D / kMxBlock) : nullptr;
   float* Srow = S + (int64_t)qh_of(geo, u, mem < Mu ? mem : 0) * S_stride;
   const int k_wave = k_wg + wave * kPerWave;
   const int nrb = k_wave < F ? min(kPerWave / 16, (F - k_wave + 15) / 16) : 0;
   float lmx = -INFINITY, lmn = INFINITY;  // over this lane's member rows
 
-  auto compute = [&](const ScoreRows<D>& R, int rb) {
+  using Rows = typename std::conditional<FP4, Fp4Rows, ScoreRows<D>>::type;
+  auto load_rows = [&](Rows& R, int k) {
+    if constexpr (FP4) {
+      const bool ok = k < F;
+      const uint32_t kq = geo.bdiv.div((uint32_t)k);
+      const uint32_t node =
+          ok ? (has_parent ? sPn[kq - p0] * geo.bdiv.d + ((uint32_t)k - kq * geo.bdiv.d)
+                           : (uint32_t)k)
+             : 0u;
+      fp4_row_operand<D>(RCu, RSu, node, grp, R);
+    } else {
+      score_load<D>(R, Xu, sPn, p0, has_parent, geo.bdiv, k, F, grp);
+    }
+  };
+
+  auto compute = [&](const Rows& R, int rb) {
     f32x4_t c = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (FP4) {
+      c = fp4_mfma(R, qc, qs, c);
+    } else {
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-      c = __builtin_amdgcn_mfma_f32_16x16x4f32(R.a[q].x, qf[q][0], c, 0, 0, 0);
-      c = __builtin_amdgcn_mfma_f32_16x16x4f32(R.a[q].y, qf[q][1], c, 0, 0, 0);
-      c = __builtin_amdgcn_mfma_f32_16x16x4f32(R.a[q].z, qf[q][2], c, 0, 0, 0);
-      c = __builtin_amdgcn_mfma_f32_16x16x4f32(R.a[q].w, qf[q][3], c, 0, 0, 0);
+      for (int q = 0; q < NQ; ++q) {
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(R.a[q].x, qf[q][0], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(R.a[q].y, qf[q][1], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(R.a[q].z, qf[q][2], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(R.a[q].w, qf[q][3], c, 0, 0, 0);
+      }
     }
     // rows kb..kb+3 of member `mem`; + 0.0f turns a -0 score into +0 so float and bit
     // orders agree
@@ -181,15 +287,13 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
     }
   };
 
-  ScoreRows<D> A, Bv;
-  if (nrb > 0) score_load<D>(A, Xu, sPn, p0, has_parent, geo.bdiv, k_wave + mem, F, grp);
+  Rows A, Bv;
+  if (nrb > 0) load_rows(A, k_wave + mem);
   for (int rb = 0; rb < nrb; rb += 2) {
-    if (rb + 1 < nrb)
-      score_load<D>(Bv, Xu, sPn, p0, has_parent, geo.bdiv, k_wave + 16 * (rb + 1) + mem, F, grp);
+    if (rb + 1 < nrb) load_rows(Bv, k_wave + 16 * (rb + 1) + mem);
     compute(A, rb);
     if (rb + 1 >= nrb) break;
-    if (rb + 2 < nrb)
-      score_load<D>(A, Xu, sPn, p0, has_parent, geo.bdiv, k_wave + 16 * (rb + 2) + mem, F, grp);
+    if (rb + 2 < nrb) load_rows(A, k_wave + 16 * (rb + 2) + mem);
     compute(Bv, rb + 1);
   }
 
@@ -797,11 +901,51 @@ __device__ __forceinline__ void top_rows_score(const f32x4_t (&x)[kTopUnroll], c
   }
 }
 
-template <int D, typename Tq>
+// FP4 router: one 16-row block per MFMA, the head's quantised query in every B column,
+// so the lanes of column 0 hold the block's 16 dot products (rows 4 (l / 16) + r).
+constexpr int kTopFp4Batch = 4;  // row blocks per wave in flight
+
+template <int D>
+__device__ __forceinline__ void top_fp4_score(const uint8_t* RCu, const uint8_t* RSu,
+                                              const uint32_t* kn, bool top, const FastDiv& bd,
+                                              int F, uint4 qc, uint32_t qs, float* S,
+                                              float sigma) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int mem = lane & 15, grp = lane >> 4;
+  const int nblk = (F + 15) / 16;
+  for (int b0 = wave; b0 < nblk; b0 += kTopWaves * kTopFp4Batch) {
+    Fp4Rows R[kTopFp4Batch];
+#pragma unroll
+    for (int j = 0; j < kTopFp4Batch; ++j) {
+      const int blk = b0 + j * kTopWaves;
+      const uint32_t r = (uint32_t)min(16 * blk + mem, F - 1);
+      uint32_t node = r;
+      if (!top) {
+        const uint32_t q = bd.div(r);
+        node = kn[q] * bd.d + (r - q * bd.d);
+      }
+      fp4_row_operand<D>(RCu, RSu, node, grp, R[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < kTopFp4Batch; ++j) {
+      const int blk = b0 + j * kTopWaves;
+      const f32x4_t c = fp4_mfma(R[j], qc, qs, f32x4_t{0.f, 0.f, 0.f, 0.f});
+      if (mem == 0 && blk < nblk) {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int r = 16 * blk + 4 * grp + rr;
+          if (r < F) S[r] = sigma * c[rr] + 0.0f;
+        }
+      }
+    }
+  }
+}
+
+template <int D, typename Tq, bool FP4>
 __global__ __launch_bounds__(kTopThreads) void head_top_kernel(
     Geom geo, const float* __restrict__ pyramid, TopLevels tl, int l_hi, int l_lo,
     const Tq* __restrict__ Q, float p, float sigma, int32_t* __restrict__ lvl_kept,
-    uint32_t* __restrict__ bitmaps) {
+    uint32_t* __restrict__ bitmaps, RouterView rv) {
   constexpr int LPR = D / 4;              // lanes per row
   constexpr int RPW = 64 / LPR;           // rows per wave-wide load
   constexpr int STEP = RPW * kTopWaves * kTopUnroll;  // rows per batch
@@ -814,7 +958,11 @@ __global__ __launch_bounds__(kTopThreads) void head_top_kernel(
   const bool keep_all = !(p < 1.0f);
   const int sub = lane % LPR, row_in = wave * RPW + lane / LPR;
   float qv[4];
-  {
+  uint4 qc = make_uint4(0u, 0u, 0u, 0u);
+  uint32_t qs = 127u;
+  if constexpr (FP4) {
+    fp4_query_operand<D, Tq>(Q + (int64_t)qh * D, lane >> 4, true, &qc, &qs);
+  } else {
     const Tq* qr = Q + (int64_t)qh * D + 4 * sub;
 #pragma unroll
     for (int e = 0; e < 4; ++e) qv[e] = to_f32(qr[e]);
@@ -826,7 +974,12 @@ __global__ __launch_bounds__(kTopThreads) void head_top_kernel(
     const float* Xu = pyramid + tl.xoff[l] + (int64_t)bg_of(geo, u) * tl.xstride[l];
     const uint32_t* kn = sh.kn[cur];
     // ---- score, two batches of rows in flight
-    {
+    if constexpr (FP4) {
+      const int64_t rows = tl.xstride[l] / D;
+      top_fp4_score<D>(rv.codes[l] + (int64_t)bg_of(geo, u) * rows * (D / 2),
+                       rv.scales[l] + (int64_t)bg_of(geo, u) * rows * (D / kMxBlock), kn, top,
+                       geo.bdiv, F, qc, qs, sh.S, sigma);
+    } else {
       f32x4_t xa[kTopUnroll], xb[kTopUnroll];
       top_rows_load<D>(xa, Xu, kn, top, geo.bdiv, 0, F, sub, row_in);
       for (int r0 = 0; r0 < F; r0 += 2 * STEP) {
@@ -1808,7 +1961,8 @@ int score_entries(int64_t cap_entries, int units) {
 
 hipError_t launch_score(const Geom& geo, const float* X, int64_t X_unit_stride, const void* Q,
                         int dtype, const LevelBufs* parent, int n_top, float* S,
-                        int64_t S_stride, const WideSel* wide, hipStream_t s) {
+                        int64_t S_stride, const WideSel* wide, const uint8_t* rcodes,
+                        const uint8_t* rscales, int64_t rows_cap, hipStream_t s) {
   const int cap_entries = parent ? (int)(geo.b * parent->stride) : n_top;
   const int ent = score_entries(cap_entries, geo.U);
   dim3 grid((cap_entries + ent - 1) / ent, geo.U);
@@ -1818,17 +1972,21 @@ hipError_t launch_score(const Geom& geo, const float* X, int64_t X_unit_stride, 
   float* pmax = wide ? wide->pmax : nullptr;
   float* pmin = wide ? wide->pmin : nullptr;
   const int64_t pstride = wide ? wide->pstride : 0;
-#define ZHA_SCORE(DD, TQ)                                                                     \
-  hipLaunchKernelGGL((score_kernel<DD, TQ>), grid, dim3(kScoreThreads), 0, s, geo, X,          \
+#define ZHA_SCORE(DD, TQ, F4)                                                                 \
+  hipLaunchKernelGGL((score_kernel<DD, TQ, F4>), grid, dim3(kScoreThreads), 0, s, geo, X,      \
                      X_unit_stride, (const TQ*)Q, par, hp, n_top, S, S_stride, sigma, ent,     \
-                     pmax, pmin, pstride)
+                     pmax, pmin, pstride, rcodes, rscales, rows_cap)
+#define ZHA_SCORE_D(DD, TQ)          \
+  if (rcodes) ZHA_SCORE(DD, TQ, true); \
+  else ZHA_SCORE(DD, TQ, false)
   if (geo.D == 64) {
-    if (dtype == ZHA_BF16) ZHA_SCORE(64, bf16_t);
-    else ZHA_SCORE(64, float);
+    if (dtype == ZHA_BF16) { ZHA_SCORE_D(64, bf16_t); }
+    else { ZHA_SCORE_D(64, float); }
   } else {
-    if (dtype == ZHA_BF16) ZHA_SCORE(128, bf16_t);
-    else ZHA_SCORE(128, float);
+    if (dtype == ZHA_BF16) { ZHA_SCORE_D(128, bf16_t); }
+    else { ZHA_SCORE_D(128, float); }
   }
+#undef ZHA_SCORE_D
 #undef ZHA_SCORE
   return hipGetLastError();
 }
@@ -1900,7 +2058,7 @@ int top_levels_lowest(const Geom& geo, const int64_t* nodes_per_level) {
 hipError_t launch_top_levels(const Geom& geo, const float* pyramid, const LevelBufs* lv,
                              const int64_t* level_off, const int64_t* unit_stride, int l_lo,
                              const void* Q, int dtype, float p, int32_t* lvl_kept,
-                             uint32_t* bitmaps, hipStream_t s) {
+                             uint32_t* bitmaps, const RouterView* router, hipStream_t s) {
   TopLevels tl{};
   for (int l = l_lo; l <= geo.L; ++l) {
     tl.lv[l] = lv[l];
@@ -1909,16 +2067,21 @@ hipError_t launch_top_levels(const Geom& geo, const float* pyramid, const LevelB
   }
   const float sigma = 1.0f / sqrtf((float)geo.D);
   const int QH = geo.B * geo.T * geo.Hq;
-#define ZHA_TOP(DD, TQ)                                                                       \
-  hipLaunchKernelGGL((head_top_kernel<DD, TQ>), dim3(QH), dim3(kTopThreads), 0, s, geo,        \
-                     pyramid, tl, geo.L, l_lo, (const TQ*)Q, p, sigma, lvl_kept, bitmaps)
+  const RouterView rv = router ? *router : RouterView{};
+#define ZHA_TOP(DD, TQ, F4)                                                                   \
+  hipLaunchKernelGGL((head_top_kernel<DD, TQ, F4>), dim3(QH), dim3(kTopThreads), 0, s, geo,    \
+                     pyramid, tl, geo.L, l_lo, (const TQ*)Q, p, sigma, lvl_kept, bitmaps, rv)
+#define ZHA_TOP_D(DD, TQ)          \
+  if (router) ZHA_TOP(DD, TQ, true); \
+  else ZHA_TOP(DD, TQ, false)
   if (geo.D == 64) {
-    if (dtype == ZHA_BF16) ZHA_TOP(64, bf16_t);
-    else ZHA_TOP(64, float);
+    if (dtype == ZHA_BF16) { ZHA_TOP_D(64, bf16_t); }
+    else { ZHA_TOP_D(64, float); }
   } else {
-    if (dtype == ZHA_BF16) ZHA_TOP(128, bf16_t);
-    else ZHA_TOP(128, float);
+    if (dtype == ZHA_BF16) { ZHA_TOP_D(128, bf16_t); }
+    else { ZHA_TOP_D(128, float); }
   }
+#undef ZHA_TOP_D
 #undef ZHA_TOP
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
