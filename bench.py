@@ -165,19 +165,20 @@ def main():
     # launch-bound small kernels of the search then run without per-launch host overhead.
     ms_step, ms_attend, graph = ms_eager, ms_attend_eager, False
     dist = None
+    def capture(fn):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        torch.cuda.synchronize()
+        return g
+
     if not args.no_graph:
-        def capture(fn):
-            side = torch.cuda.Stream()
-            side.wait_stream(torch.cuda.current_stream())
-            with torch.cuda.stream(side):
-                fn()
-            torch.cuda.current_stream().wait_stream(side)
-            torch.cuda.synchronize()
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                fn()
-            torch.cuda.synchronize()
-            return g
         g_step = capture(full_step)
         g_attend = capture(attend_only)
         for _ in range(args.warmup):
@@ -313,6 +314,88 @@ def main():
     needles = {"planted": total, "kept_by_aimed_head": hits,
                "recall": round(hits / total, 4) if total else None}
 
+    # FP4 router (the pages' FP4 router variant): the pyramid's MXFP4 copy written after the
+    # build and scored with an MXFP4 query; the float32-router figures above are untouched
+    fp4 = None
+    if not args.no_extras:
+        rbytes = Z.router_bytes(B, Hkv, N, d, b, L)
+        rstore = torch.empty(rbytes, dtype=torch.uint8, device=dev)
+
+        def quantize():
+            LB.check(lib.zha_router_quantize(ctypes.byref(c_tree), 0, rstore.data_ptr(), rbytes,
+                                             torch.cuda.current_stream().cuda_stream))
+
+        def build_fp4():
+            # an empty tree given its copy, then extended by the whole cache: the pooling
+            # launches write the MXFP4 rows along with the float32 ones
+            LB.check(lib.zha_build_tree(K.data_ptr(), R.data_ptr(), c_tree.dtype, B, Hkv, 0, N, d,
+                                        b, L, tree.storage.data_ptr(), tree.storage.numel(),
+                                        ctypes.byref(c_tree),
+                                        torch.cuda.current_stream().cuda_stream))
+            quantize()
+            LB.check(lib.zha_tree_append(ctypes.byref(c_tree), K.data_ptr(), R.data_ptr(), N,
+                                         torch.cuda.current_stream().cuda_stream))
+
+        def step_fp4():
+            build_fp4()
+            attend_only()
+
+        step_fp4()
+        ms4_quant, _ = timed(quantize, args.steps)
+        ms4_build, _ = timed(build_fp4, args.steps)
+        if args.no_graph:
+            ms4_step, _ = timed(step_fp4, args.steps)
+            ms4_attend, _ = timed(attend_only, args.steps)
+        else:
+            g4_step = capture(step_fp4)
+            g4_attend = capture(attend_only)
+            ms4_step, _ = timed(g4_step.replay, args.steps)
+            ms4_attend, _ = timed(g4_attend.replay, args.steps)
+        lib.zha_timing_enable(1)
+        timed(step_fp4, args.steps)
+        lib.zha_timing_enable(0)
+        k4 = {}
+        for name, kind, levels in (("router", LB.ZHA_K_ROUTER, [0]),
+                                   ("pool", LB.ZHA_K_POOL, range(1, L + 1)),
+                                   ("score", LB.ZHA_K_SCORE, range(1, L + 1)),
+                                   ("descent_top", LB.ZHA_K_DESCENT, range(1, L + 1)),
+                                   ("decode", LB.ZHA_K_DECODE, [0])):
+            for lv in levels:
+                tot, n = ktime(kind, lv)
+                if n:
+                    k4[f"{name}_l{lv}" if lv else name] = round(tot / n, 4)
+        attend_only()
+        torch.cuda.synchronize()
+        c4 = cnt.cpu().numpy()
+        s4 = sel.cpu().numpy()
+        n1_4, _, c1_4 = Z.level_view(tree, T, Hq, 1, ws)
+        union4 = sum(int(c1_4[u]) for u in range(U)) * b
+        hits4 = 0
+        for bb in range(B):
+            for pos, t, h in W.needle_plan(spec, bb):
+                hits4 += int(pos in set(s4[bb, t, h, :c4[bb, t, h]].tolist()))
+        # share of each head's float32-router selection that the FP4 router also selects
+        keep = []
+        for bb in range(B):
+            for t in range(T):
+                for h in range(Hq):
+                    a = sel_h[bb, t, h, :cnt_h[bb, t, h]]
+                    z = s4[bb, t, h, :c4[bb, t, h]]
+                    keep.append(np.intersect1d(a, z, assume_unique=True).size / max(a.size, 1))
+        kr4 = c4.reshape(-1) / N
+        fp4 = {"router_bytes": rbytes, "encode_pass_ms": round(ms4_quant, 4),
+               "build_ms": round(ms4_build, 4),
+               "step_ms": round(ms4_step, 4),
+               "query_heads_per_s": round(QH / (ms4_step * 1e-3), 1),
+               "attend_ms": round(ms4_attend, 4),
+               "keys_read_pct": {"mean": round(100 * kr4.mean(), 3),
+                                 "union": round(100 * union4 / (U * N), 3)},
+               "needle_recall": round(hits4 / needles["planted"], 4) if needles["planted"] else None,
+               "f32_selection_kept": {"mean": round(float(np.mean(keep)), 4),
+                                      "min": round(float(np.min(keep)), 4)},
+               "kernels_ms": k4}
+        c_tree.router = LB.ZHA_ROUTER_F32
+
     cpu = near_ties = None
     if not args.no_cpu_baseline:
         cpu, near_ties = cpu_baseline(spec, p, anchor, args.cpu_units)
@@ -368,6 +451,7 @@ def main():
             "timed_pass_ms_per_step": round(ms_timed_pass, 4)},
         "kernels": {k: {"avg_ms": round(v["avg_ms"], 4), "launches": v["launches"]}
                     for k, v in kernels.items()},
+        "fp4_router": fp4,
         "copy_probe_gbs": copy_gbs,
         "kernel_sources": kernel_sources_sha(),
     }

@@ -279,6 +279,31 @@ def test_appends_encode_the_nodes_they_complete():
         assert torch.equal(a_c, m_c) and torch.equal(a_s, m_s), f"level {l}"
 
 
+@pytest.mark.parametrize("wl,kw", [
+    ("32k_deep", dict(N=16384, B=2, Hq=8, Hkv=2)),           # bf16 b = 4: pooling encodes
+    ("32k_deep", dict(N=8192, B=1, Hq=8, Hkv=2, L=4, d=64)),
+    ("tiny", {}),                                            # fp32: the encoder pass
+    ("32k_deep", dict(N=4096, B=1, Hq=8, Hkv=2, L=3, b=8)),  # b = 8: the encoder pass
+])
+def test_build_with_router_equals_encoding_the_built_pyramid(wl, kw):
+    """build_tree(router=True) (pooling launches that write the MXFP4 rows themselves,
+    the encoder for the levels they do not cover) equals the standalone encoder run over
+    the one-shot pyramid, bit for bit, and both pyramids are equal."""
+    Z = _Z()
+    spec = W.spec(wl, **kw)
+    inp = W.gen_all(spec, device="cuda")
+    a = Z.build_tree(inp["K"], inp["R"], spec["b"], spec["L"], router=True)
+    ref = Z.build_tree(inp["K"], inp["R"], spec["b"], spec["L"])
+    Z.quantize_router(ref)
+    torch.cuda.synchronize()
+    assert a.c.router == ref.c.router == 1
+    for l in range(1, spec["L"] + 1):
+        assert torch.equal(Z.pyramid_level(a, l), Z.pyramid_level(ref, l)), f"pyramid level {l}"
+        x_c, x_s = Z.router_level(a, l)
+        y_c, y_s = Z.router_level(ref, l)
+        assert torch.equal(x_c, y_c) and torch.equal(x_s, y_s), f"router level {l}"
+
+
 def test_256k_deep_fp4_sampled_units():
     """The benchmark workload at full size with the FP4 router: two (sequence, KV head)
     units carry the oracle's pyramid and MXFP4 codes; every head of them is checked."""

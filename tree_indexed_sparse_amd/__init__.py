@@ -89,8 +89,12 @@ def pyramid_level(tree: Tree, level: int) -> torch.Tensor:
     return flat[off:off + numel].view(c.B, c.Hkv, n, c.d)
 
 
-def build_tree(K: torch.Tensor, R: torch.Tensor, b: int, L: int, N: int | None = None) -> Tree:
-    """zha_build_tree over tokens [0, N) of the cache K [B, Hkv, N_cap, d]."""
+def build_tree(K: torch.Tensor, R: torch.Tensor, b: int, L: int, N: int | None = None,
+               router: bool = False) -> Tree:
+    """zha_build_tree over tokens [0, N) of the cache K [B, Hkv, N_cap, d].
+    router=True also writes the MXFP4 router copy and selects it: the tree is started
+    empty, given its copy (zha_router_quantize), and extended by N tokens
+    (zha_tree_append), so the pooling launches encode the rows they write."""
     lib = load()
     B, Hkv, N_cap, d = K.shape
     N = N_cap if N is None else N
@@ -99,9 +103,14 @@ def build_tree(K: torch.Tensor, R: torch.Tensor, b: int, L: int, N: int | None =
     nbytes = tree_bytes(B, Hkv, N_cap, d, b, L)
     storage = torch.empty(max(nbytes, 4), dtype=torch.uint8, device=K.device)
     c = ZhaTree()
-    check(lib.zha_build_tree(_dev(K, "K"), _dev(R, "R"), _dt(K), B, Hkv, N, N_cap, d, b, L,
-                             storage.data_ptr(), nbytes, ctypes.byref(c), _stream(K.device)))
-    return Tree(c, storage)
+    check(lib.zha_build_tree(_dev(K, "K"), _dev(R, "R"), _dt(K), B, Hkv, 0 if router else N,
+                             N_cap, d, b, L, storage.data_ptr(), nbytes, ctypes.byref(c),
+                             _stream(K.device)))
+    tree = Tree(c, storage)
+    if router:
+        quantize_router(tree)
+        tree_append(tree, K, R, N)
+    return tree
 
 
 def tree_append(tree: Tree, K: torch.Tensor, R: torch.Tensor, n_new: int) -> None:

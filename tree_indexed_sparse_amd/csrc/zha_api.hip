@@ -232,8 +232,10 @@ int64_t router_layout(int B, int Hkv, int N_cap, int d, int b, int L, int64_t* c
   return off;
 }
 
-// Encode, at every level, rows [n_lo / b^l, n_hi / b^l) of each unit into the router copy.
-hipError_t encode_router(const zha_tree* t, int64_t n_lo, int64_t n_hi, hipStream_t s) {
+// Encode, at every level not marked in `skip`, rows [n_lo / b^l, n_hi / b^l) of each unit
+// into the router copy.
+hipError_t encode_router(const zha_tree* t, int64_t n_lo, int64_t n_hi, hipStream_t s,
+                         const bool* skip = nullptr) {
   RouterJob job{};
   const int rpw = router_rows_per_workgroup(t->d);
   int wgs = 0;
@@ -242,7 +244,7 @@ hipError_t encode_router(const zha_tree* t, int64_t n_lo, int64_t n_hi, hipStrea
     cap /= t->b;
     div *= t->b;
     const int r0 = (int)(n_lo / div), r1 = (int)(n_hi / div);
-    if (r1 <= r0) continue;
+    if (r1 <= r0 || (skip && skip[l])) continue;
     const int i = job.n++;
     job.src[i] = t->pyramid + t->level_off[l];
     job.codes[i] = t->router_data + t->router_code_off[l];
@@ -333,6 +335,8 @@ int zha_tree_append(zha_tree* t, const void* K, const void* R, int n_new, void* 
   const int64_t n_old = t->N, n_end = (int64_t)t->N + n_new;
   auto lo = [&](int j) { return n_old / ipow(t->b, j); };
   auto hi = [&](int j) { return n_end / ipow(t->b, j); };
+  // levels whose router rows the pooling launches encode themselves
+  bool encoded[ZHA_MAX_LEVELS + 1] = {false};
   for (int l = 1; l <= t->L;) {
     const void* child = (l == 1) ? K : (const void*)(t->pyramid + t->level_off[l - 1]);
     const int dt_in = (l == 1) ? t->dtype : ZHA_F32;
@@ -345,14 +349,23 @@ int zha_tree_append(zha_tree* t, const void* K, const void* R, int n_new, void* 
         const int64_t r0 = (lo(l - 1) / tr) * tr, r1 = (rows + tr - 1) / tr * tr;
         float* outs[ZHA_MAX_LEVELS];
         int64_t strides[ZHA_MAX_LEVELS];
+        uint8_t* rc[ZHA_MAX_LEVELS];
+        uint8_t* rs[ZHA_MAX_LEVELS];
         for (int j = 0; j < k; ++j) {
           outs[j] = t->pyramid + t->level_off[l + j];
           strides[j] = cap_nodes(l + j) * t->d;
+          if (t->router_data) {
+            rc[j] = t->router_data + t->router_code_off[l + j];
+            rs[j] = t->router_data + t->router_scale_off[l + j];
+          }
         }
+        const bool enc = t->router_data &&
+                         pool_fused_encodes(dt_in, t->dtype, t->b, k, (int)r0, (int)r1);
+        for (int j = 0; j < k && enc; ++j) encoded[l + j] = true;
         e = timed(ZHA_K_POOL, l, s, [&] {
           return launch_pool_fused(dt_in, child, cap_nodes(l - 1) * t->d, R, t->dtype, outs,
                                    strides, k, units, t->Hkv, (int)r0, (int)r1, (int)rows, t->b,
-                                   t->d, s);
+                                   t->d, enc ? rc : nullptr, enc ? rs : nullptr, s);
         });
       } else {
         e = timed(ZHA_K_POOL, l, s, [&] {
@@ -366,7 +379,7 @@ int zha_tree_append(zha_tree* t, const void* K, const void* R, int n_new, void* 
     l += k >= 1 ? k : 1;
   }
   if (t->router_data) {
-    const hipError_t e = encode_router(t, n_old, n_end, s);
+    const hipError_t e = encode_router(t, n_old, n_end, s, encoded);
     if (e != hipSuccess) return hip_fail(e, "router encode launch");
   }
   t->N += n_new;

@@ -10,6 +10,7 @@
 // subtrees give bit-identical summaries.
 
 #include "zha_internal.h"
+#include "zha_mxfp4.h"
 
 namespace zha {
 namespace {
@@ -186,6 +187,10 @@ constexpr int kTilesPerWG = 1;
 struct PoolOut {
   float* ptr[kMaxFuse];
   int64_t unit_stride[kMaxFuse];
+  // MXFP4 router copy of the same levels (null: none): codes [unit][rows][D/2] and scales
+  // [unit][rows][D/32], rows = unit_stride / D
+  uint8_t* codes[kMaxFuse];
+  uint8_t* scales[kMaxFuse];
 };
 
 __device__ __forceinline__ uint4 lds16(const uint32_t* p) { return *reinterpret_cast<const uint4*>(p); }
@@ -361,7 +366,36 @@ __global__ __launch_bounds__(kPoolThreads) void pool_tile_kernel(
 constexpr int kWaveRows = 64;
 constexpr int kWaveTilesPerWave = 2;
 
-template <int D, bool MASKED>
+// MXFP4 encoding of a row the wave kernel just pooled, where each of 16 lanes (one lane
+// group) holds DL = D / 16 consecutive elements: the lanes of a 32-element block agree on
+// its largest magnitude by shuffles, each writes its DL codes, the block's first lane the
+// scale. The values are the float32 results stored to the pyramid, so the codes equal
+// those the standalone encoder writes from the stored rows.
+template <int D>
+__device__ __forceinline__ void wave_encode_row(const float* acc, int mem, bool store,
+                                                uint8_t* codes_row, uint8_t* scales_row) {
+  constexpr int DL = D / 16;
+  constexpr int LPB = kMxBlock / DL;  // lanes per block
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < DL; ++i) amax = fmaxf(amax, fabsf(acc[i]));
+#pragma unroll
+  for (int off = 1; off < LPB; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+  const uint32_t sb = mx_scale_byte(amax);
+  const float inv = mx_inv_scale(sb);
+  uint32_t w = 0;
+#pragma unroll
+  for (int i = 0; i < DL; ++i) w |= e2m1_code(acc[i], inv) << (4 * i);
+  if (store) {
+    if constexpr (DL == 8)
+      reinterpret_cast<uint32_t*>(codes_row)[mem] = w;
+    else
+      reinterpret_cast<uint16_t*>(codes_row)[mem] = (uint16_t)w;
+    if (mem % LPB == 0) scales_row[mem / LPB] = (uint8_t)sb;
+  }
+}
+
+template <int D, bool MASKED, bool ENC>
 __global__ __launch_bounds__(kPoolThreads) void pool_wave_b4_kernel(
     const bf16_t* __restrict__ child, int64_t in_unit_stride, const bf16_t* __restrict__ Rall,
     PoolOut out, int nlev, int Hkv, int tile_begin, int tile_end, int row_limit, float tau) {
@@ -469,6 +503,11 @@ __global__ __launch_bounds__(kPoolThreads) void pool_wave_b4_kernel(
         if (st1) *reinterpret_cast<float4*>(dst1 + (int64_t)node * D + DL * mem + i) = o;
         *reinterpret_cast<float4*>(&l1[node * RWf + DL * mem + i]) = o;
       }
+      if constexpr (ENC) {
+        const int64_t row = unit * (out.unit_stride[0] / D) + (int64_t)t * 16 + node;
+        wave_encode_row<D>(acc, mem, st1, out.codes[0] + row * (D / 2),
+                           out.scales[0] + row * (D / kMxBlock));
+      }
     }
     if (nlev < 2) continue;
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -509,6 +548,11 @@ __global__ __launch_bounds__(kPoolThreads) void pool_wave_b4_kernel(
           const float4 o = make_float4(acc[i], acc[i + 1], acc[i + 2], acc[i + 3]);
           if (stj) *reinterpret_cast<float4*>(dst + DL * mem + i) = o;
           if (j == 1) *reinterpret_cast<float4*>(&l2[grp * RWf + DL * mem + i]) = o;
+        }
+        if constexpr (ENC) {
+          const int64_t row = unit * (out.unit_stride[j] / D) + (int64_t)t * nodes + grp;
+          wave_encode_row<D>(acc, mem, stj, out.codes[j] + row * (D / 2),
+                             out.scales[j] + row * (D / kMxBlock));
         }
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -670,14 +714,17 @@ hipError_t launch_wave_b4(const void* child, int64_t in_unit_stride, const void*
   const int per_wg = (kPoolThreads / 64) * kWaveTilesPerWave;
   dim3 grid((t1 - t0 + per_wg - 1) / per_wg, units);
   // tiles that all lie below row_limit store every node: the unmasked form
-  if (row_limit >= row_end)
-    hipLaunchKernelGGL((pool_wave_b4_kernel<D, false>), grid, dim3(kPoolThreads), 0, s,
-                       (const bf16_t*)child, in_unit_stride, (const bf16_t*)R, out, nlev, Hkv, t0,
-                       t1, row_limit, 1.0f / sqrtf((float)D));
-  else
-    hipLaunchKernelGGL((pool_wave_b4_kernel<D, true>), grid, dim3(kPoolThreads), 0, s,
-                       (const bf16_t*)child, in_unit_stride, (const bf16_t*)R, out, nlev, Hkv, t0,
-                       t1, row_limit, 1.0f / sqrtf((float)D));
+  const float tau = 1.0f / sqrtf((float)D);
+#define ZHA_WAVE(M, E)                                                                        \
+  hipLaunchKernelGGL((pool_wave_b4_kernel<D, M, E>), grid, dim3(kPoolThreads), 0, s,           \
+                     (const bf16_t*)child, in_unit_stride, (const bf16_t*)R, out, nlev, Hkv, t0, \
+                     t1, row_limit, tau)
+  const bool masked = row_limit < row_end, enc = out.codes[0] != nullptr;
+  if (!masked && !enc) ZHA_WAVE(false, false);
+  else if (!masked) ZHA_WAVE(false, true);
+  else if (!enc) ZHA_WAVE(true, false);
+  else ZHA_WAVE(true, true);
+#undef ZHA_WAVE
   return hipGetLastError();
 }
 
@@ -762,21 +809,29 @@ int fused_levels(int b, int levels_left) {
   return k;
 }
 
+bool pool_fused_encodes(int dtype_in, int dtype_r, int b, int nlev, int row_begin,
+                        int row_end) {
+  return dtype_r == ZHA_BF16 && dtype_in == ZHA_BF16 && b == 4 && nlev <= 3 &&
+         row_begin % kWaveRows == 0 && row_end % kWaveRows == 0;
+}
+
 hipError_t launch_pool_fused(int dtype_in, const void* child, int64_t in_unit_stride,
                              const void* R, int dtype_r, float* const* outs,
                              const int64_t* out_unit_strides, int nlev, int units, int Hkv,
                              int row_begin, int row_end, int row_limit, int b, int D,
-                             hipStream_t s) {
+                             uint8_t* const* rcodes, uint8_t* const* rscales, hipStream_t s) {
   if (nlev < 1 || nlev > kMaxFuse) return hipErrorInvalidValue;
   PoolOut out{};
   for (int j = 0; j < nlev; ++j) {
     out.ptr[j] = outs[j];
     out.unit_stride[j] = out_unit_strides[j];
+    out.codes[j] = rcodes ? rcodes[j] : nullptr;
+    out.scales[j] = rscales ? rscales[j] : nullptr;
   }
   if (dtype_r == ZHA_BF16) {
-    // bf16 keys, b = 4, rows in whole 64-row wave tiles: the wave-centric kernel
-    if (dtype_in == ZHA_BF16 && b == 4 && nlev <= 3 && row_begin % kWaveRows == 0 &&
-        row_end % kWaveRows == 0) {
+    // bf16 keys, b = 4, rows in whole 64-row wave tiles: the wave-centric kernel (the
+    // only one that also writes the router copy)
+    if (pool_fused_encodes(dtype_in, dtype_r, b, nlev, row_begin, row_end)) {
       if (D == 64)
         return launch_wave_b4<64>(child, in_unit_stride, R, out, nlev, units, Hkv, row_begin,
                                   row_end, row_limit, s);

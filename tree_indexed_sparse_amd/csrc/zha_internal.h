@@ -141,11 +141,15 @@ int fused_levels(int b, int levels_left);
 
 // `nlev` consecutive levels pooled from one child level in one launch (b^nlev <= 64):
 // child rows [row_begin, row_end) -> outs[j] (level j + 1 above the child level).
+// rcodes / rscales (per fused level, or null): the MXFP4 router copy of those levels,
+// written by the launch only when pool_fused_encodes() says so for its arguments.
 hipError_t launch_pool_fused(int dtype_in, const void* child, int64_t in_unit_stride,
                              const void* R, int dtype_r, float* const* outs,
                              const int64_t* out_unit_strides, int nlev, int units, int Hkv,
                              int row_begin, int row_end, int row_limit, int b, int D,
-                             hipStream_t s);
+                             uint8_t* const* rcodes, uint8_t* const* rscales, hipStream_t s);
+bool pool_fused_encodes(int dtype_in, int dtype_r, int b, int nlev, int row_begin,
+                        int row_end);
 
 // Scores of a level's union frontier for every member: S[qh][k].
 // wide != nullptr: also write the per-workgroup member max/min the chunked selection reads.
