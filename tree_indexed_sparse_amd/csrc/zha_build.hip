@@ -383,9 +383,7 @@ __device__ __forceinline__ void wave_encode_row(const float* acc, int mem, bool 
   for (int off = 1; off < LPB; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
   const uint32_t sb = mx_scale_byte(amax);
   const float inv = mx_inv_scale(sb);
-  uint32_t w = 0;
-#pragma unroll
-  for (int i = 0; i < DL; ++i) w |= e2m1_code(acc[i], inv) << (4 * i);
+  const uint32_t w = e2m1_pack(acc, DL, inv);
   if (store) {
     if constexpr (DL == 8)
       reinterpret_cast<uint32_t*>(codes_row)[mem] = w;

@@ -27,23 +27,21 @@ __device__ __forceinline__ float mx_inv_scale(uint32_t byte) {
   return __uint_as_float((254u - byte) << 23);
 }
 
-// E2M1 code of x / 2^X: the nearest magnitude after clamping to 6, ties to the even
-// mantissa (the thresholds are the midpoints between neighbouring magnitudes; a tie
-// belongs to the magnitude whose code is even), and the sign bit of x.
-__device__ __forceinline__ uint32_t e2m1_code(float x, float inv) {
-  const float a = fabsf(x) * inv;
-  const uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
-                     (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
-                     (uint32_t)(a > 5.0f);
-  return c | ((__float_as_uint(x) >> 28) & 8u);
-}
-
-// Eight consecutive elements -> one 32-bit word of codes (element i in bits 4i .. 4i + 3).
-__device__ __forceinline__ uint32_t e2m1_pack8(const float (&x)[8], float inv) {
+// E2M1 codes of x / 2^X for eight consecutive elements, packed into one word (element i
+// in bits 4i .. 4i + 3). x * 2^-X is exact; v_cvt_scalef32_pk_fp4_f32 (scale 1) then
+// rounds it to the nearest E2M1 value with ties to the even mantissa, saturates at +-6
+// and keeps the sign (zeros included): the format's rounding, checked against the
+// definition on every tie and on both sides of the clamp.
+__device__ __forceinline__ uint32_t e2m1_pack(const float* x, int n, float inv) {
   uint32_t w = 0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) w |= e2m1_code(x[i], inv) << (4 * i);
+  if (n > 0) w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[0] * inv, x[1] * inv, 1.0f, 0);
+  if (n > 2) w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[2] * inv, x[3] * inv, 1.0f, 1);
+  if (n > 4) w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[4] * inv, x[5] * inv, 1.0f, 2);
+  if (n > 6) w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[6] * inv, x[7] * inv, 1.0f, 3);
   return w;
+}
+__device__ __forceinline__ uint32_t e2m1_pack8(const float (&x)[8], float inv) {
+  return e2m1_pack(x, 8, inv);
 }
 
 // One whole block held by one lane: 32 values -> 16 code bytes (uint4) and the scale byte.
