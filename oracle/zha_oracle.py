@@ -335,6 +335,34 @@ def attend_head(q, levels, K_u, V_u, b, L, p, anchor=1) -> HeadResult:
     return HeadResult(attention_over(q, K_u, V_u, S), S, decisions)
 
 
+# ---------------------------------------------------------------------------
+# Several queries of one sequence at different positions, causally masked (page 3,
+# paragraph 3: making the search itself sparse opens the way to attention that is truly
+# sub-quadratic, i.e. to running it for every position of a sequence). Reading: the
+# query at position t (0-based) sees exactly the cache of its first t + 1 tokens; its
+# search, anchor and tail are those of that cache (the reading for a cache that does not
+# fill whole top nodes): nodes that reach past t are not complete for it and are not
+# searched, and the tokens after its last complete top node are attended like the anchor.
+# The pyramid is built once over the whole cache; a node's summary depends only on the
+# tokens under it, so the prefix of the full pyramid is the pyramid of the prefix.
+# ---------------------------------------------------------------------------
+
+def causal_view(levels: list, K_u: np.ndarray, V_u: np.ndarray, b: int, L: int, pos: int):
+    """The pyramid levels and K, V that a query at position `pos` sees (tokens
+    0 .. pos)."""
+    n = int(pos) + 1
+    if not 1 <= n <= K_u.shape[0]:
+        raise ValueError("position outside the cache")
+    lv = [levels[0][:n]] + [levels[l][: n // b ** l] for l in range(1, L + 1)]
+    return lv, K_u[:n], V_u[:n]
+
+
+def attend_head_causal(q, levels, K_u, V_u, b, L, p, anchor, pos) -> HeadResult:
+    """Search and exact attention of the query at position `pos` over what it sees."""
+    lv, Kc, Vc = causal_view(levels, K_u, V_u, b, L, pos)
+    return attend_head(q, lv, Kc, Vc, b, L, p, anchor)
+
+
 def attend(Q, K, V, tree, b, L, p, anchor=1):
     """Every query head: Q [B, T, Hq, d]; K, V [B, Hkv, N, d]; tree from
     build_tree. Returns a nested list res[b][t][h] of HeadResult."""

@@ -560,3 +560,66 @@ def test_fp4_router_quantises_the_router_only():
     top = res.levels[0]
     want = O.node_scores(O.mxfp4_round_trip(levels[L]), O.mxfp4_round_trip(q))
     np.testing.assert_array_equal(top.scores, want)
+
+
+# ---------------------------------------------------------------------------
+# Causal multi-query: a query at position t sees tokens 0 .. t only.
+# ---------------------------------------------------------------------------
+
+def _causal_unit(seed, N=512, d=32, b=4, L=3):
+    rng = _rng(seed)
+    K = rng.standard_normal((N, d)).astype(np.float32)
+    V = rng.standard_normal((N, d)).astype(np.float32)
+    R = (rng.standard_normal((16, d)) / np.sqrt(d)).astype(np.float32)
+    return rng, K, V, R, O.build_tree_unit(K, R, b, L)
+
+
+def test_causal_p_one_is_causally_masked_sdpa():
+    rng, K, V, R, levels = _causal_unit(90)
+    for pos in (0, 1, 5, 63, 64, 200, 511):
+        q = rng.standard_normal(K.shape[1]).astype(np.float32)
+        res = O.attend_head_causal(q, levels, K, V, 4, 3, 1.0, 1, pos)
+        mask = np.arange(K.shape[0]) <= pos
+        np.testing.assert_allclose(res.O, _sdpa(q, K, V, mask), rtol=1e-12, atol=1e-12)
+        np.testing.assert_array_equal(res.S, np.arange(pos + 1))
+
+
+def test_causal_result_does_not_depend_on_later_tokens():
+    """Rewriting every key and value after the query's position (and so the pyramid
+    nodes over them) changes nothing the query selects or outputs."""
+    rng, K, V, R, levels = _causal_unit(91)
+    for pos in (70, 130, 300, 448):
+        K2, V2 = K.copy(), V.copy()
+        K2[pos + 1:] = rng.standard_normal(K2[pos + 1:].shape).astype(np.float32) * 3
+        V2[pos + 1:] = rng.standard_normal(V2[pos + 1:].shape).astype(np.float32)
+        levels2 = O.build_tree_unit(K2, R, 4, 3)
+        q = rng.standard_normal(K.shape[1]).astype(np.float32)
+        a = O.attend_head_causal(q, levels, K, V, 4, 3, 0.9, 1, pos)
+        c = O.attend_head_causal(q, levels2, K2, V2, 4, 3, 0.9, 1, pos)
+        np.testing.assert_array_equal(a.S, c.S)
+        np.testing.assert_array_equal(a.O, c.O)
+
+
+def test_causal_last_position_is_the_decode_query():
+    rng, K, V, R, levels = _causal_unit(92)
+    q = rng.standard_normal(K.shape[1]).astype(np.float32)
+    a = O.attend_head_causal(q, levels, K, V, 4, 3, 0.9, 1, K.shape[0] - 1)
+    c = O.attend_head(q, levels, K, V, 4, 3, 0.9, 1)
+    np.testing.assert_array_equal(a.S, c.S)
+    np.testing.assert_array_equal(a.O, c.O)
+
+
+def test_causal_selection_structure():
+    """Tokens selected: never past the position; the anchor and the query's own tail
+    (after its last complete top node, 64 tokens here) always; a position before the first
+    complete top node attends densely."""
+    rng, K, V, R, levels = _causal_unit(93)
+    for pos in range(0, 512, 7):
+        q = rng.standard_normal(K.shape[1]).astype(np.float32)
+        res = O.attend_head_causal(q, levels, K, V, 4, 3, 0.8, 2, pos)
+        assert res.S.max() <= pos and np.all(np.diff(res.S) > 0)
+        assert set(range(min(2, pos + 1))) <= set(res.S.tolist())
+        full = (pos + 1) // 64 * 64
+        assert set(range(max(full, 2), pos + 1)) <= set(res.S.tolist())
+        if pos < 63:
+            np.testing.assert_array_equal(res.S, np.arange(pos + 1))
