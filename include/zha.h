@@ -177,6 +177,25 @@ int zha_attend(const zha_tree* t, const void* Q, int T, int Hq, const void* K, c
                int32_t* sel_count, void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * zha_attend for T queries of each sequence that sit at their own positions, causally
+ * masked (page 3, paragraph 3: a search that is itself sparse is what makes attention over
+ * a whole sequence sub-quadratic).
+ *   positions  device, int32, [B][T], 4-byte aligned: the 0-based position of query t of
+ *              sequence b; values outside [0, N - 1] are clamped into it
+ * The query at position t sees exactly the first t + 1 cached tokens, as if the cache
+ * held only those: its search runs over the top nodes complete within them
+ * ((t + 1) / b^L of them), its anchor is tokens [0, min(anchor, t + 1)), and the tokens it
+ * sees after its last complete top node are selected; it never reads a later token. The
+ * queries of one unit share one union list per level (each keeps its own set). Every
+ * other argument, output and rule is that of zha_attend; with every position at N - 1 the
+ * result is zha_attend's.
+ */
+int zha_attend_causal(const zha_tree* t, const void* Q, int T, int Hq, const int32_t* positions,
+                      const void* K, const void* V, float p, int anchor, float* O,
+                      int32_t* sel_idx, int64_t cap, int32_t* sel_count, void* workspace,
+                      size_t ws_bytes, void* stream);
+
+/*
  * Dense comparator: exact softmax attention of every query head over all N cached keys of
  * its KV head, with the same decode and combine kernels zha_attend uses (every member
  * reads every token; there is no tree and no search). It is what the tree-indexed path is
@@ -189,6 +208,13 @@ size_t zha_dense_workspace_bytes(int B, int Hkv, int N, int N_cap, int d, int T,
 int zha_dense_attend(const void* Q, int T, int Hq, const void* K, const void* V, int dtype,
                      int B, int Hkv, int N, int N_cap, int d, float* O, void* workspace,
                      size_t ws_bytes, void* stream);
+
+/* The dense comparator with query positions (as for zha_attend_causal): each query
+ * attends exactly to tokens [0, position]. positions: device, int32, [B][T], non-NULL. */
+int zha_dense_attend_causal(const void* Q, int T, int Hq, const int32_t* positions,
+                            const void* K, const void* V, int dtype, int B, int Hkv, int N,
+                            int N_cap, int d, float* O, void* workspace, size_t ws_bytes,
+                            void* stream);
 
 /*
  * Diagnostics of the last zha_attend that used `workspace` (valid once it completed).

@@ -18,13 +18,19 @@ import tree_indexed_sparse_amd as Z  # noqa: E402
 import workloads as W  # noqa: E402
 
 
-def run_gpu(spec, p, anchor=1, inputs=None, want_lists=True, tree=None, device="cuda", N=None):
+def run_gpu(spec, p, anchor=1, inputs=None, want_lists=True, tree=None, device="cuda", N=None,
+            positions=None):
     """N: tokens in use (default: the whole generated cache, its capacity). The tree's
-    router field decides which copy of the summaries the search scores."""
+    router field decides which copy of the summaries the search scores. positions: [B, T]
+    query positions (numpy), for the causal entry point."""
     inp = inputs if inputs is not None else W.gen_all(spec, device=device)
     if tree is None:
         tree = Z.build_tree(inp["K"], inp["R"], spec["b"], spec["L"], N=N)
-    O_, sel, cnt = Z.attend(inp["Q"], inp["K"], inp["V"], tree, p, anchor, want_lists=want_lists)
+    pos_t = None
+    if positions is not None:
+        pos_t = torch.from_numpy(np.asarray(positions, np.int32)).to(inp["Q"].device)
+    O_, sel, cnt = Z.attend(inp["Q"], inp["K"], inp["V"], tree, p, anchor, want_lists=want_lists,
+                            positions=pos_t)
     ws = Z.attend.last_workspace
     torch.cuda.synchronize()
     T, Hq = spec["T"], spec["Hq"]
@@ -42,10 +48,12 @@ def oracle_unit(spec, b, g, Q=None, R=None):
 
 
 def check_units(spec, res, p, anchor=1, units=None, check_pyramid=True, oracle_levels=None,
-                n_tokens=None, fp4=False):
+                n_tokens=None, fp4=False, positions=None):
     """Guided comparison of every query head of the given (sequence, KV head) units.
     n_tokens: the cache holds only the first n_tokens generated tokens (a ragged cache).
     fp4: the search scored the MXFP4 router (the oracle's reading of the FP4 router).
+    positions: [B, T] query positions (each head is compared with the oracle's view of
+    the cache up to its position).
     Returns (list of HeadReport, max pyramid relative error)."""
     B, T, Hq, Hkv = spec["B"], spec["T"], spec["Hq"], spec["Hkv"]
     G = Hq // Hkv
@@ -72,10 +80,14 @@ def check_units(spec, res, p, anchor=1, units=None, check_pyramid=True, oracle_l
                 gl = Z.pyramid_level(res["tree"], l)[b, g, :n].cpu().numpy()
                 pyr_err = max(pyr_err, C.pyramid_rel_err(gl, levels[l]))
         for t in range(T):
+            lv, Kc, Vc = levels, K_u, V_u
+            if positions is not None:
+                pos = min(max(int(positions[b][t]), 0), K_u.shape[0] - 1)
+                lv, Kc, Vc = O.causal_view(levels, K_u, V_u, spec["b"], spec["L"], pos)
             for h in range(g * G, (g + 1) * G):
                 u, m = C.unit_member(b, t, h, T, Hq, Hkv)
                 sel_row = None if res["sel"] is None else res["sel"][b, t, h]
-                reports.append(C.check_head(Q[b, t, h], levels, K_u, V_u, spec["b"], spec["L"], p,
+                reports.append(C.check_head(Q[b, t, h], lv, Kc, Vc, spec["b"], spec["L"], p,
                                             anchor, res["lists"], u, m, sel_row,
                                             res["cnt"][b, t, h], res["O"][b, t, h], qh=(b, t, h),
                                             fp4=fp4))

@@ -204,3 +204,16 @@ def test_attend_rejects_bad_router_fields(lib):
     t.router_data = 0x3000
     assert _attend(lib, t=t) == -1
     assert b"router" in lib.zha_last_error()
+
+
+def test_causal_entry_points_reject_bad_positions(lib):
+    t = _tree()
+    args = (1, 8)
+    for pos, code in ((None, -1), (ctypes.c_void_p(0x1002), -1)):
+        assert lib.zha_attend_causal(ctypes.byref(t), FAKE, *args, pos, FAKE, FAKE, 0.9, 1, FAKE,
+                                     FAKE, 4096, FAKE, FAKE, 1 << 40, None) == code
+        assert lib.zha_dense_attend_causal(FAKE, 1, 8, pos, FAKE, FAKE, 1, 1, 2, 4096, 4096, 64,
+                                           FAKE, FAKE, 1 << 40, None) == code
+    # the other checks are zha_attend's
+    assert lib.zha_attend_causal(ctypes.byref(t), FAKE, 1, 7, FAKE, FAKE, FAKE, 0.9, 1, FAKE,
+                                 FAKE, 4096, FAKE, FAKE, 1 << 40, None) == -2

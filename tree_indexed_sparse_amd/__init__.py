@@ -172,9 +172,10 @@ def workspace_bytes(tree: Tree, T: int, Hq: int) -> int:
 
 
 def attend(Q, K, V, tree: Tree, p: float, anchor: int = 1, *, want_lists: bool = True,
-           out=None, sel_idx=None, sel_count=None, workspace=None):
-    """zha_attend. Returns (O [B,T,Hq,d] float32, sel_idx [B,T,Hq,N] int32 or None,
-    sel_count [B,T,Hq] int32). Buffers may be passed in to avoid allocation."""
+           out=None, sel_idx=None, sel_count=None, workspace=None, positions=None):
+    """zha_attend (or zha_attend_causal when `positions`, an int32 device tensor [B, T] of
+    query positions, is given). Returns (O [B,T,Hq,d] float32, sel_idx [B,T,Hq,N] int32 or
+    None, sel_count [B,T,Hq] int32). Buffers may be passed in to avoid allocation."""
     lib = load()
     B, T, Hq, d = Q.shape
     dev = Q.device
@@ -192,11 +193,18 @@ def attend(Q, K, V, tree: Tree, p: float, anchor: int = 1, *, want_lists: bool =
     need = workspace_bytes(tree, T, Hq)
     if workspace is None:
         workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=dev)
-    check(lib.zha_attend(ctypes.byref(tree.c), _dev(Q, "Q"), T, Hq, _dev(K, "K"), _dev(V, "V"),
-                         float(p), int(anchor), _dev(out, "O"),
-                         _dev(sel_idx, "sel_idx") if sel_idx is not None else None, cap,
-                         _dev(sel_count, "sel_count"), _dev(workspace, "workspace"),
-                         workspace.numel(), _stream(dev)))
+    sel_ptr = _dev(sel_idx, "sel_idx") if sel_idx is not None else None
+    if positions is None:
+        check(lib.zha_attend(ctypes.byref(tree.c), _dev(Q, "Q"), T, Hq, _dev(K, "K"),
+                             _dev(V, "V"), float(p), int(anchor), _dev(out, "O"), sel_ptr, cap,
+                             _dev(sel_count, "sel_count"), _dev(workspace, "workspace"),
+                             workspace.numel(), _stream(dev)))
+    else:
+        check(lib.zha_attend_causal(ctypes.byref(tree.c), _dev(Q, "Q"), T, Hq,
+                                    _positions(positions, B, T), _dev(K, "K"), _dev(V, "V"),
+                                    float(p), int(anchor), _dev(out, "O"), sel_ptr, cap,
+                                    _dev(sel_count, "sel_count"), _dev(workspace, "workspace"),
+                                    workspace.numel(), _stream(dev)))
     attend.last_workspace = workspace
     return out, sel_idx, sel_count
 
@@ -205,8 +213,15 @@ def dense_workspace_bytes(B: int, Hkv: int, N: int, N_cap: int, d: int, T: int, 
     return int(load().zha_dense_workspace_bytes(B, Hkv, N, N_cap, d, T, Hq))
 
 
-def dense_attend(Q, K, V, N: int | None = None, *, out=None, workspace=None):
-    """zha_dense_attend: exact attention over all N cached keys (the dense comparator).
+def _positions(positions, B: int, T: int) -> int:
+    if positions.dtype != torch.int32 or tuple(positions.shape) != (B, T):
+        raise ZhaError(-2, f"positions must be int32 [{B}, {T}]")
+    return _dev(positions, "positions")
+
+
+def dense_attend(Q, K, V, N: int | None = None, *, out=None, workspace=None, positions=None):
+    """zha_dense_attend: exact attention over all N cached keys (the dense comparator), or
+    zha_dense_attend_causal over keys [0, position] when `positions` [B, T] is given.
     K, V [B,Hkv,N_cap,d]; returns O [B,T,Hq,d] float32."""
     lib = load()
     B, T, Hq, d = Q.shape
@@ -220,9 +235,15 @@ def dense_attend(Q, K, V, N: int | None = None, *, out=None, workspace=None):
     need = dense_workspace_bytes(B, Hkv, N, N_cap, d, T, Hq)
     if workspace is None:
         workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=dev)
-    check(lib.zha_dense_attend(_dev(Q, "Q"), T, Hq, _dev(K, "K"), _dev(V, "V"), _dt(K), B, Hkv,
-                               N, N_cap, d, _dev(out, "O"), _dev(workspace, "workspace"),
-                               workspace.numel(), _stream(dev)))
+    if positions is None:
+        check(lib.zha_dense_attend(_dev(Q, "Q"), T, Hq, _dev(K, "K"), _dev(V, "V"), _dt(K), B,
+                                   Hkv, N, N_cap, d, _dev(out, "O"), _dev(workspace, "workspace"),
+                                   workspace.numel(), _stream(dev)))
+    else:
+        check(lib.zha_dense_attend_causal(_dev(Q, "Q"), T, Hq, _positions(positions, B, T),
+                                          _dev(K, "K"), _dev(V, "V"), _dt(K), B, Hkv, N, N_cap, d,
+                                          _dev(out, "O"), _dev(workspace, "workspace"),
+                                          workspace.numel(), _stream(dev)))
     return out
 
 

@@ -37,9 +37,11 @@ EXPORTS = (
     "zha_router_quantize",
     "zha_attend_workspace_bytes",
     "zha_attend",
+    "zha_attend_causal",
     "zha_attend_level_view",
     "zha_dense_workspace_bytes",
     "zha_dense_attend",
+    "zha_dense_attend_causal",
     "zha_timing_enable",
     "zha_timing_read",
     "zha_last_error",
@@ -106,6 +108,9 @@ def load() -> ctypes.CDLL:
     lib.zha_attend.argtypes = [P(ZhaTree), vp, i32, i32, vp, vp, f32, i32, vp, vp, i64, vp, vp,
                                sz, vp]
     lib.zha_attend.restype = i32
+    lib.zha_attend_causal.argtypes = [P(ZhaTree), vp, i32, i32, vp, vp, vp, f32, i32, vp, vp, i64,
+                                      vp, vp, sz, vp]
+    lib.zha_attend_causal.restype = i32
     lib.zha_attend_level_view.argtypes = [P(ZhaTree), i32, i32, i32, P(i64), P(i64), P(i64),
                                           P(i64), P(i64)]
     lib.zha_attend_level_view.restype = i32
@@ -114,6 +119,9 @@ def load() -> ctypes.CDLL:
     lib.zha_dense_attend.argtypes = [vp, i32, i32, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp,
                                      sz, vp]
     lib.zha_dense_attend.restype = i32
+    lib.zha_dense_attend_causal.argtypes = [vp, i32, i32, vp, vp, vp, i32, i32, i32, i32, i32,
+                                            i32, vp, vp, sz, vp]
+    lib.zha_dense_attend_causal.restype = i32
     lib.zha_timing_enable.argtypes = [i32]
     lib.zha_timing_enable.restype = i32
     lib.zha_timing_read.argtypes = [i32, i32, P(ctypes.c_double), P(i64)]

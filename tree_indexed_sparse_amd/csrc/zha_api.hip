@@ -131,6 +131,8 @@ int make_geom(const zha_tree* t, int T, int Hq, Geom* g) {
   g->N = t->N;
   g->Ncap = t->N_cap;
   g->bdiv = make_fastdiv((uint32_t)t->b);
+  g->top_span = (int)ipow(t->b, t->L);
+  g->pos = nullptr;
   return ZHA_OK;
 }
 
@@ -471,9 +473,10 @@ size_t zha_dense_workspace_bytes(int B, int Hkv, int N, int N_cap, int d, int T,
   return (size_t)dense_layout(g).total;
 }
 
-int zha_dense_attend(const void* Q, int T, int Hq, const void* K, const void* V, int dtype,
-                     int B, int Hkv, int N, int N_cap, int d, float* O, void* workspace,
-                     size_t ws_bytes, void* stream) {
+namespace {
+int dense_impl(const void* Q, int T, int Hq, const int32_t* positions, const void* K,
+               const void* V, int dtype, int B, int Hkv, int N, int N_cap, int d, float* O,
+               void* workspace, size_t ws_bytes, void* stream) {
   if (!Q || !K || !V || !O || !workspace)
     return fail(ZHA_ERR_INVALID_ARG, "Q, K, V, O and workspace must not be NULL");
   if (dtype != ZHA_F32 && dtype != ZHA_BF16) return fail(ZHA_ERR_DTYPE, "unknown dtype %d", dtype);
@@ -481,23 +484,43 @@ int zha_dense_attend(const void* Q, int T, int Hq, const void* K, const void* V,
       ((uintptr_t)workspace & 255u) != 0)
     return fail(ZHA_ERR_INVALID_ARG,
                 "Q, K, V and O must be 16-byte aligned and the workspace 256-byte aligned");
+  if (positions && ((uintptr_t)positions & 3u) != 0)
+    return fail(ZHA_ERR_INVALID_ARG, "positions must be 4-byte aligned");
   Geom g;
   int st = dense_geom(B, Hkv, N, N_cap, d, T, Hq, &g);
   if (st != ZHA_OK) return st;
+  g.pos = positions;
   const DenseLayout w = dense_layout(g);
   if ((int64_t)ws_bytes < w.total)
     return fail(ZHA_ERR_SHAPE, "workspace has %zu bytes, needs %lld", ws_bytes,
                 (long long)w.total);
   hipStream_t s = (hipStream_t)stream;
   float* part = (float*)((char*)workspace + w.off_part);
-  // no list: every token is the tail, read by every member
+  // no list: every token a member sees is its tail
   hipError_t e = timed(ZHA_K_DECODE, 0, s, [&] {
-    return launch_decode(g, dtype, K, V, Q, LevelBufs{}, 0, 0, 0, N, w.splits, part, s);
+    return launch_decode(g, dtype, K, V, Q, LevelBufs{}, 0, 0, w.splits, part, s);
   });
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   e = timed(ZHA_K_COMBINE, 0, s, [&] { return launch_combine(g, w.splits, part, O, s); });
   if (e != hipSuccess) return hip_fail(e, "combine launch");
   return ZHA_OK;
+}
+}  // namespace
+
+int zha_dense_attend(const void* Q, int T, int Hq, const void* K, const void* V, int dtype,
+                     int B, int Hkv, int N, int N_cap, int d, float* O, void* workspace,
+                     size_t ws_bytes, void* stream) {
+  return dense_impl(Q, T, Hq, nullptr, K, V, dtype, B, Hkv, N, N_cap, d, O, workspace, ws_bytes,
+                    stream);
+}
+
+int zha_dense_attend_causal(const void* Q, int T, int Hq, const int32_t* positions,
+                            const void* K, const void* V, int dtype, int B, int Hkv, int N,
+                            int N_cap, int d, float* O, void* workspace, size_t ws_bytes,
+                            void* stream) {
+  if (!positions) return fail(ZHA_ERR_INVALID_ARG, "positions must not be NULL");
+  return dense_impl(Q, T, Hq, positions, K, V, dtype, B, Hkv, N, N_cap, d, O, workspace,
+                    ws_bytes, stream);
 }
 
 int zha_attend_level_view(const zha_tree* t, int T, int Hq, int level, int64_t* off_nodes,
@@ -521,9 +544,11 @@ int zha_attend_level_view(const zha_tree* t, int T, int Hq, int level, int64_t* 
   return ZHA_OK;
 }
 
-int zha_attend(const zha_tree* t, const void* Q, int T, int Hq, const void* K, const void* V,
-               float p, int anchor, float* O, int32_t* sel_idx, int64_t cap, int32_t* sel_count,
-               void* workspace, size_t ws_bytes, void* stream) {
+namespace {
+int attend_impl(const zha_tree* t, const void* Q, int T, int Hq, const int32_t* positions,
+                const void* K, const void* V, float p, int anchor, float* O, int32_t* sel_idx,
+                int64_t cap, int32_t* sel_count, void* workspace, size_t ws_bytes,
+                void* stream) {
   int st = check_tree(t);
   if (st != ZHA_OK) return st;
   if (!Q || !K || !V || !O || !sel_count || !workspace)
@@ -539,9 +564,12 @@ int zha_attend(const zha_tree* t, const void* Q, int T, int Hq, const void* K, c
   if (sel_idx && cap < t->N)
     return fail(ZHA_ERR_CAPACITY, "sel_idx row length cap=%lld is smaller than N=%d",
                 (long long)cap, t->N);
+  if (positions && ((uintptr_t)positions & 3u) != 0)
+    return fail(ZHA_ERR_INVALID_ARG, "positions must be 4-byte aligned");
   Geom g;
   st = make_geom(t, T, Hq, &g);
   if (st != ZHA_OK) return st;
+  g.pos = positions;
   const WsLayout w = layout_of(g);
   if ((int64_t)ws_bytes < w.total)
     return fail(ZHA_ERR_SHAPE, "workspace has %zu bytes, needs %lld", ws_bytes,
@@ -631,9 +659,9 @@ int zha_attend(const zha_tree* t, const void* Q, int T, int Hq, const void* K, c
     if (e != hipSuccess) return hip_fail(e, "compact launch");
     cap_l *= t->b;
   }
-  if (!searched || n_tail > 0) {
+  if (!searched || n_tail > 0 || positions) {
     e = timed(ZHA_K_SELECT, 0, s, [&] {
-      return launch_tail(g, searched ? 1 : 0, tail_lo, n_tail, sel_idx, cap, sel_count,
+      return launch_tail(g, searched ? 1 : 0, anchor, sel_idx, cap, sel_count,
                          (uint32_t*)(ws + w.off_count), (t->L + 1) * g.U, s);
     });
     if (e != hipSuccess) return hip_fail(e, "tail launch");
@@ -641,12 +669,29 @@ int zha_attend(const zha_tree* t, const void* Q, int T, int Hq, const void* K, c
   float* part = (float*)(ws + w.off_part);
   e = timed(ZHA_K_DECODE, 0, s, [&] {
     return launch_decode(g, t->dtype, K, V, Q, lv[1], searched ? 1 : 0, searched ? anchor : 0,
-                         tail_lo, n_tail, w.splits, part, s);
+                         w.splits, part, s);
   });
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   e = timed(ZHA_K_COMBINE, 0, s, [&] { return launch_combine(g, w.splits, part, O, s); });
   if (e != hipSuccess) return hip_fail(e, "combine launch");
   return ZHA_OK;
+}
+}  // namespace
+
+int zha_attend(const zha_tree* t, const void* Q, int T, int Hq, const void* K, const void* V,
+               float p, int anchor, float* O, int32_t* sel_idx, int64_t cap, int32_t* sel_count,
+               void* workspace, size_t ws_bytes, void* stream) {
+  return attend_impl(t, Q, T, Hq, nullptr, K, V, p, anchor, O, sel_idx, cap, sel_count,
+                     workspace, ws_bytes, stream);
+}
+
+int zha_attend_causal(const zha_tree* t, const void* Q, int T, int Hq, const int32_t* positions,
+                      const void* K, const void* V, float p, int anchor, float* O,
+                      int32_t* sel_idx, int64_t cap, int32_t* sel_count, void* workspace,
+                      size_t ws_bytes, void* stream) {
+  if (!positions) return fail(ZHA_ERR_INVALID_ARG, "positions must not be NULL");
+  return attend_impl(t, Q, T, Hq, positions, K, V, p, anchor, O, sel_idx, cap, sel_count,
+                     workspace, ws_bytes, stream);
 }
 
 int zha_timing_enable(int on) {

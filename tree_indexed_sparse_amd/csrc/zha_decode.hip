@@ -8,9 +8,11 @@
 // Work list: the union, over a unit's members, of the kept level-1 nodes (ascending,
 // with a member bitmask each), expanded to b contiguous tokens per node. Each K/V row is
 // read once per unit and scored for every member; tokens outside a member's own set are
-// masked. Tokens below `anchor` are skipped inside nodes and attended once, for every
-// member, by split 0. A tail range of tokens (those after the last complete top node, or
-// the whole cache for dense attention) follows the list and is read by every member.
+// masked. Tokens below `anchor` are skipped inside nodes and attended once, by split 0,
+// for every member that sees them. Each member's tail (the tokens it sees after its last
+// complete top node and its anchor, or every token it sees for dense attention) is
+// covered by one range that follows the list, masked per member. Without query positions
+// every member sees all N tokens and these ranges are the same for all of them.
 // The work range (list tokens, then tail) is cut into `splits` equal pieces; each
 // workgroup writes one (max, sum, weighted-V) partial per member, and a separate combine
 // launch merges a unit's partials in a fixed order, so the result does not depend on the
@@ -24,6 +26,55 @@ namespace {
 constexpr int kDecThreads = 256;
 constexpr int kDecWaves = kDecThreads / 64;
 constexpr int kNodeChunk = 2048;  // union-list entries staged in LDS at a time
+
+// What the members of a unit see: anchor tokens [0, anc[m]), tail [tlo[m], vis[m]).
+// Written by threads 0 .. kMaxMembers - 1; read after a barrier.
+struct UnitRanges {
+  int anc[kMaxMembers], tlo[kMaxMembers], vis[kMaxMembers];
+};
+
+__device__ __forceinline__ void unit_ranges_fill(const Geom& geo, int u, int Mu, int has_list,
+                                                 int anchor, UnitRanges& r) {
+  const int m = threadIdx.x;
+  if (m >= kMaxMembers) return;
+  int vis = 0, an = 0, tlo = 0;
+  if (m < Mu) {
+    vis = head_vis(geo, qh_of(geo, u, m));
+    an = min(anchor, vis);
+    tlo = has_list ? max((vis / geo.top_span) * geo.top_span, an) : 0;
+  }
+  r.anc[m] = an;
+  r.tlo[m] = tlo;
+  r.vis[m] = vis;
+}
+
+// The unit's tail span [*lo, *lo + *n) (the members' tails together) and anchor span.
+__device__ __forceinline__ void unit_spans(const UnitRanges& r, int Mu, int* lo, int* n,
+                                           int* anc) {
+  int a = 0, l = 0x7fffffff, h = 0;
+  for (int m = 0; m < Mu; ++m) {
+    a = max(a, r.anc[m]);
+    if (r.vis[m] > r.tlo[m]) {
+      l = min(l, r.tlo[m]);
+      h = max(h, r.vis[m]);
+    }
+  }
+  *anc = a;
+  *lo = h > 0 ? l : 0;
+  *n = h > 0 ? h - l : 0;
+}
+
+// Members for whom token `tok` is an anchor token / a tail token.
+__device__ __forceinline__ uint32_t anchor_members(const UnitRanges& r, int Mu, int tok) {
+  uint32_t mk = 0u;
+  for (int m = 0; m < Mu; ++m) mk |= (uint32_t)(tok < r.anc[m]) << m;
+  return mk;
+}
+__device__ __forceinline__ uint32_t tail_members(const UnitRanges& r, int Mu, int tok) {
+  uint32_t mk = 0u;
+  for (int m = 0; m < Mu; ++m) mk |= (uint32_t)(tok >= r.tlo[m] && tok < r.vis[m]) << m;
+  return mk;
+}
 
 // Merge the per-wave states (sm, sl: [wave][member], so: [wave][member][D], in LDS) into
 // this split's partial (max, sum, sum of p * v per member). Every thread calls this.
@@ -126,14 +177,19 @@ __device__ __forceinline__ void split_range(int ntok, int splits, int sp, int al
 template <typename T, int D>
 __global__ __launch_bounds__(kDecThreads) void decode_valu_kernel(
     Geom geo, const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ Q,
-    LevelBufs l1, int has_list, int anchor, int tail_lo, int n_tail, int splits,
-    float* __restrict__ part, float sigma) {
+    LevelBufs l1, int has_list, int anchor, int splits, float* __restrict__ part,
+    float sigma) {
   constexpr int DPL = D / 64;  // dims per lane
+  __shared__ UnitRanges rg;
   const int u = blockIdx.y, sp = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int Mu = members_of(geo, u);
   const int b = geo.b;
   const int nnode = has_list ? (int)l1.count[u] * b : 0;  // work items from the list
+  unit_ranges_fill(geo, u, Mu, has_list, anchor, rg);
+  __syncthreads();
+  int tail_lo, n_tail, anc_u;
+  unit_spans(rg, Mu, &tail_lo, &n_tail, &anc_u);
   int t0, t1;
   split_range(nnode + n_tail, splits, sp, 1, &t0, &t1);
   const int64_t row0 = (int64_t)bg_of(geo, u) * geo.Ncap;
@@ -152,7 +208,6 @@ __global__ __launch_bounds__(kDecThreads) void decode_valu_kernel(
       q[m][i] = (m < Mu) ? to_f32(Q[(int64_t)qh_of(geo, u, m) * D + lane * DPL + i]) : 0.f;
     }
   }
-  const uint32_t full = (1u << Mu) - 1u;
 
   auto consume = [&](int tok, uint32_t mask) {
     float kx[DPL], vx[DPL];
@@ -182,10 +237,11 @@ __global__ __launch_bounds__(kDecThreads) void decode_valu_kernel(
   };
 
   if (sp == 0 && wave == 0)
-    for (int tok = 0; tok < anchor; ++tok) consume(tok, full);
+    for (int tok = 0; tok < anc_u; ++tok) consume(tok, anchor_members(rg, Mu, tok));
   for (int i = t0 + wave; i < t1; i += kDecWaves) {
-    if (i >= nnode) {  // the tail: every member
-      consume(tail_lo + (i - nnode), full);
+    if (i >= nnode) {  // the tail: the members whose tail holds the token
+      const int tok = tail_lo + (i - nnode);
+      consume(tok, tail_members(rg, Mu, tok));
       continue;
     }
     const int nd = (int)geo.bdiv.div((uint32_t)i), c = i - nd * b;
@@ -256,7 +312,7 @@ struct TileRegs {
 template <int D>
 __global__ __launch_bounds__(kDecThreads, 2) void decode_mfma_kernel(
     Geom geo, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
-    const bf16_t* __restrict__ Q, LevelBufs l1, int has_list, int anchor, int tail_lo, int n_tail,
+    const bf16_t* __restrict__ Q, LevelBufs l1, int has_list, int anchor,
     int splits, float* __restrict__ part, float sigma) {
   constexpr int KC = D / 32;          // 32-dim chunks: QK k-steps and PV column blocks
   constexpr int RW = D / 2 + 4;       // LDS row stride in dwords (padding spreads banks)
@@ -277,6 +333,11 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_mfma_kernel(
   const int b = geo.b;
   const int ncount = has_list ? (int)l1.count[u] : 0;
   const int nnode = ncount * b;  // work items from the list; the tail follows them
+  __shared__ UnitRanges rg;
+  unit_ranges_fill(geo, u, Mu, has_list, anchor, rg);
+  __syncthreads();
+  int tail_lo, n_tail, anc_u;
+  unit_spans(rg, Mu, &tail_lo, &n_tail, &anc_u);
   int t0, t1;
   split_range(nnode + n_tail, splits, sp, kTile, &t0, &t1);
   const int64_t row0 = (int64_t)bg_of(geo, u) * geo.Ncap;
@@ -300,9 +361,10 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_mfma_kernel(
 
   // Token ids and member masks of a tile are worked out once, one lane per row (lanes
   // 0..31), by region (uniform across the wave, so the branches are scalar): anchor tiles (0)
-  // cover tokens [0, anchor) for every member; list tiles (1) read the staged list (entry
-  // i / b - nbase) and skip tokens below the anchor; tail tiles (2) map work index i to token
-  // tail_lo + (i - nnode) for every member. Past `lim`: token 0, no member (its loads stay in
+  // cover tokens [0, anchor) for the members that see them; list tiles (1) read the staged
+  // list (entry i / b - nbase) and skip tokens below the anchor; tail tiles (2) map work
+  // index i to token tail_lo + (i - nnode) for the members whose tail holds it (every
+  // member without query positions). Past `lim`: token 0, no member (its loads stay in
   // bounds). They go to this wave's slot in LDS; token ids are stored row-permuted so that
   // each lane's V rows (lane / CH + RPI j) sit in adjacent words.
   int* s_tok = s_tt + wave * 2 * kTile;
@@ -319,7 +381,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_mfma_kernel(
           mk = tok < anchor ? 0u : s_masks[nd - nbase];
         } else {
           tok = region == 0 ? i : tail_lo + (i - nnode);
-          mk = 0xffffu;
+          mk = region == 0 ? anchor_members(rg, Mu, tok) : tail_members(rg, Mu, tok);
         }
       }
       s_tok[slot * kTile + (lane % RPI) * NI + lane / RPI] = tok;
@@ -458,9 +520,9 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_mfma_kernel(
   };
 
   if (sp == 0 && wave == 0) {
-    for (int base = 0; base < anchor; base += kTile) {
+    for (int base = 0; base < anc_u; base += kTile) {
       TileRegs<D> R;
-      issue(0, R, 0, base, anchor, 0);
+      issue(0, R, 0, base, anc_u, 0);
       compute(R, 0);
     }
   }
@@ -514,13 +576,13 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_mfma_kernel(
 
 hipError_t launch_decode(const Geom& geo, int dtype, const void* K, const void* V,
                          const void* Q, const LevelBufs& l1, int has_list, int anchor,
-                         int tail_lo, int n_tail, int splits, float* partials, hipStream_t s) {
+                         int splits, float* partials, hipStream_t s) {
   if (splits < 1 || splits > kMaxSplits) return hipErrorInvalidValue;
   dim3 grid(splits, geo.U);
   const float sigma = 1.0f / sqrtf((float)geo.D);
 #define ZHA_DEC(KERNEL, T)                                                                    \
   hipLaunchKernelGGL(KERNEL, grid, dim3(kDecThreads), 0, s, geo, (const T*)K, (const T*)V,     \
-                     (const T*)Q, l1, has_list, anchor, tail_lo, n_tail, splits, partials,  \
+                     (const T*)Q, l1, has_list, anchor, splits, partials,  \
                      sigma)
   if (dtype == ZHA_BF16) {
     if (geo.D == 64) ZHA_DEC((decode_mfma_kernel<64>), bf16_t);

@@ -44,6 +44,8 @@ struct Geom {
   int B, T, Hq, Hkv, G, Tb, nTB, U;
   int D, b, L, N, Ncap;
   FastDiv bdiv;  // division by b
+  int top_span;        // b^L: tokens under one top node
+  const int32_t* pos;  // [B][T] query positions, or null: every query sees all N tokens
 };
 
 __host__ __device__ __forceinline__ int members_of(const Geom& g, int u) {
@@ -70,6 +72,18 @@ __host__ __device__ __forceinline__ int qh_of(const Geom& g, int u, int m) {
   const int t = tb * g.Tb + m / g.G;
   const int h = kv * g.G + m % g.G;
   return (bb * g.T + t) * g.Hq + h;
+}
+
+// Tokens query head qh sees: its position + 1 (positions clamped into [0, N - 1]), or N
+// without positions. Its search runs over the top nodes complete within them.
+__device__ __forceinline__ int head_vis(const Geom& g, int qh) {
+  if (!g.pos) return g.N;
+  const int t = (qh / g.Hq) % g.T, bb = qh / (g.Hq * g.T);
+  const int p = g.pos[bb * g.T + t];
+  return (p < 0 ? 0 : (p >= g.N ? g.N - 1 : p)) + 1;
+}
+__device__ __forceinline__ int head_ntop(const Geom& g, int qh) {
+  return head_vis(g, qh) / g.top_span;
 }
 
 // (sequence, KV head) index of a unit: selects the K/V/pyramid slice.
@@ -200,18 +214,19 @@ hipError_t launch_union(const Geom& geo, int level, const float* S, int64_t S_st
                         int32_t* sel_idx, int64_t cap, const WideSel& wide, hipStream_t s);
 int64_t compact_counter_words(int U, int64_t n);
 
-// Sparse GQA decode: the tokens of the level-1 union list (has_list), then the tail
-// [tail_lo, tail_lo + n_tail) for every member, plus tokens [0, anchor) for every member.
+// Sparse GQA decode: the tokens of the level-1 union list (has_list), the anchor tokens
+// [0, min(anchor, seen)) and each member's tail: the tokens it sees after its last
+// complete top node (has_list), or every token it sees (no list: dense attention).
 hipError_t launch_decode(const Geom& geo, int dtype, const void* K, const void* V,
                          const void* Q, const LevelBufs& l1, int has_list, int anchor,
-                         int tail_lo, int n_tail, int splits, float* partials, hipStream_t s);
+                         int splits, float* partials, hipStream_t s);
 
-// Appends the tail [tail_lo, tail_lo + n_tail) to every head's token list and count (after
-// the level-1 selection wrote them; searched = 0: the list is the tail alone and every
-// level's union count is zeroed).
-hipError_t launch_tail(const Geom& geo, int searched, int tail_lo, int n_tail,
-                       int32_t* sel_idx, int64_t cap, int32_t* sel_count, uint32_t* counts,
-                       int count_words, hipStream_t s);
+// Appends each head's tail (the tokens it sees after its last complete top node and the
+// anchor) to its token list and count, after the level-1 selection wrote them; searched =
+// 0: the list is every token the head sees, and every level's union count is zeroed.
+hipError_t launch_tail(const Geom& geo, int searched, int anchor, int32_t* sel_idx,
+                       int64_t cap, int32_t* sel_count, uint32_t* counts, int count_words,
+                       hipStream_t s);
 
 // MXFP4 encoding of pyramid rows (the FP4 router's copy), every level of `job` at once.
 int router_rows_per_workgroup(int D);

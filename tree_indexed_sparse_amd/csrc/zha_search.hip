@@ -229,6 +229,8 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
   const int k_wave = k_wg + wave * kPerWave;
   const int nrb = k_wave < F ? min(kPerWave / 16, (F - k_wave + 15) / 16) : 0;
   float lmx = -INFINITY, lmn = INFINITY;  // over this lane's member rows
+  // at the top level a member's frontier is the top nodes complete for it
+  const int f_mem = has_parent ? F : (mem < Mu ? min(F, head_ntop(geo, qh_of(geo, u, mem))) : 0);
 
   using Rows = typename std::conditional<FP4, Fp4Rows, ScoreRows<D>>::type;
   auto load_rows = [&](Rows& R, int k) {
@@ -276,8 +278,8 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int k = kb + r;
-          const bool in = k < F && (!has_parent ||
-                                    ((sPm[geo.bdiv.div((uint32_t)k) - p0] >> mem) & 1u));
+          const bool in = k < f_mem && (!has_parent ||
+                                        ((sPm[geo.bdiv.div((uint32_t)k) - p0] >> mem) & 1u));
           if (in) {
             lmx = fmaxf(lmx, ov[r]);
             lmn = fminf(lmn, ov[r]);
@@ -476,6 +478,10 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   unit_member_of(geo, qh, &u, &m);
   const int b = geo.b;
   const int F = has_parent ? b * (int)parent.count[u] : n_top;
+  // the member's own frontier: at the top level, the top nodes complete for it
+  const int vis = head_vis(geo, qh);
+  const int Fm = has_parent ? F : min(F, vis / geo.top_span);
+  anchor = min(anchor, vis);
   const float* Sq = S + (int64_t)qh * S_stride;
   const uint32_t* pmask = has_parent ? parent.masks + u * parent.stride : nullptr;
   const uint32_t* pnodes = has_parent ? parent.nodes + u * parent.stride : nullptr;
@@ -489,7 +495,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     sh.scalar_u64[2] = ~0ull;
   }
 
-  auto load_global = [&](int k0) -> Quad { return load_quad(Sq, pmask, m, geo.bdiv, k0, F); };
+  auto load_global = [&](int k0) -> Quad { return load_quad(Sq, pmask, m, geo.bdiv, k0, Fm); };
   auto get = [&](int k0) -> Quad {
     if (!cached) return load_global(k0);
     Quad q;
@@ -728,7 +734,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     int dup = 0;
     const int lim = min(F, (anchor + b - 1) / b);
     for (int k = 0; k < lim; ++k) {
-      const bool in = !pmask || ((pmask[geo.bdiv.div((uint32_t)k)] >> m) & 1u);
+      const bool in = pmask ? ((pmask[geo.bdiv.div((uint32_t)k)] >> m) & 1u) : k < Fm;
       if (keep_of(Sq[k], in, k)) {
         const int node = (int)frontier_node(pnodes, k, geo.bdiv);
         if (node * b < anchor) dup += min(b, anchor - node * b);
@@ -968,9 +974,15 @@ __global__ __launch_bounds__(kTopThreads) void head_top_kernel(
     for (int e = 0; e < 4; ++e) qv[e] = to_f32(qr[e]);
   }
   int cur = 0;
-  int F = (int)tl.lv[l_hi].stride;  // top level: every node
+  // top level: every node complete for this head
+  int F = min((int)tl.lv[l_hi].stride, head_ntop(geo, qh));
   for (int l = l_hi; l >= l_lo; --l) {
     const bool top = l == l_hi;
+    if (F == 0) {  // an empty frontier keeps nothing (uniform across the workgroup)
+      if (tid < kTopWords) bitmaps[((int64_t)qh * (geo.L + 1) + l) * kTopWords + tid] = 0u;
+      if (tid == 0) lvl_kept[(int64_t)qh * (geo.L + 1) + l] = 0;
+      continue;
+    }
     const float* Xu = pyramid + tl.xoff[l] + (int64_t)bg_of(geo, u) * tl.xstride[l];
     const uint32_t* kn = sh.kn[cur];
     // ---- score, two batches of rows in flight
@@ -1231,7 +1243,8 @@ __global__ __launch_bounds__(kWideThreads) void wide_hist_kernel(
   const int tid = threadIdx.x;
   const float* Sq = S + (int64_t)qh * S_stride;
   const uint32_t* pmask = has_parent ? parent.masks + u * parent.stride : nullptr;
-  const int end = min(F, c0 + kWideChunk);
+  const int Fm = has_parent ? F : min(F, head_ntop(geo, qh));  // the member's frontier
+  const int end = min(Fm, c0 + kWideChunk);
   Quad q[kWideTiles];
 #pragma unroll
   for (int j = 0; j < kWideTiles; ++j)
@@ -1307,6 +1320,24 @@ __global__ __launch_bounds__(kCutThreads) void wide_cut_kernel(
   const float* Sq = S + (int64_t)qh * S_stride;
   const uint32_t* pmask = has_parent ? parent.masks + u * parent.stride : nullptr;
   const uint32_t* pnodes = has_parent ? parent.nodes + u * parent.stride : nullptr;
+  // the member's own frontier: at the top level, the top nodes complete for it
+  const int vis = head_vis(geo, qh);
+  const int Fm = has_parent ? F : min(F, vis / geo.top_span);
+  anchor = min(anchor, vis);
+  if (Fm == 0) {  // nothing to select: no entry scores above an infinite cut
+    if (tid == 0) {
+      uint32_t* rec = w.cut + 4 * (int64_t)qh;
+      rec[0] = __float_as_uint(INFINITY);
+      rec[1] = 0u;
+      rec[2] = (uint32_t)anchor;
+      rec[3] = 0u;
+      lvl_kept[(int64_t)qh * (geo.L + 1) + level] = 0;
+      if (level == 1) sel_count[qh] = anchor;
+    }
+    if (level == 1 && sel_idx)
+      for (int i = tid; i < anchor; i += kCutThreads) sel_idx[(int64_t)qh * cap + i] = i;
+    return;
+  }
 
   // bucket totals over the chunks (thread `tid` owns bucket `tid`); loads issued first
   uint64_t hsum = 0;
@@ -1368,7 +1399,7 @@ __global__ __launch_bounds__(kCutThreads) void wide_cut_kernel(
         Quad q[kUnroll];
 #pragma unroll
         for (int j = 0; j < kUnroll; ++j)
-          q[j] = load_quad(Sq, pmask, m, geo.bdiv, base + j * kVec * kCutThreads, F);
+          q[j] = load_quad(Sq, pmask, m, geo.bdiv, base + j * kVec * kCutThreads, Fm);
 #pragma unroll
         for (int j = 0; j < kUnroll; ++j) {
 #pragma unroll
@@ -1530,7 +1561,7 @@ __global__ __launch_bounds__(kCutThreads) void wide_cut_kernel(
         for (int i = tid; i < 256; i += kCutThreads) sh.radix[i] = 0ull;
         __syncthreads();
         for (int k0 = kVec * tid; k0 < F; k0 += kVec * kCutThreads) {
-          const Quad q = load_quad(Sq, pmask, m, geo.bdiv, k0, F);
+          const Quad q = load_quad(Sq, pmask, m, geo.bdiv, k0, Fm);
 #pragma unroll
           for (int i = 0; i < kVec; ++i) {
             if (!q.in[i] || bucket_of<kWB>(q.s[i], mx, scale, spread) != bstar) continue;
@@ -1562,7 +1593,7 @@ __global__ __launch_bounds__(kCutThreads) void wide_cut_kernel(
       key = prefix;
       uint32_t nk = 0;
       for (int k0 = kVec * tid; k0 < F; k0 += kVec * kCutThreads) {
-        const Quad q = load_quad(Sq, pmask, m, geo.bdiv, k0, F);
+        const Quad q = load_quad(Sq, pmask, m, geo.bdiv, k0, Fm);
 #pragma unroll
         for (int i = 0; i < kVec; ++i)
           nk += (q.in[i] && bucket_of<kWB>(q.s[i], mx, scale, spread) == bstar &&
@@ -1584,7 +1615,7 @@ __global__ __launch_bounds__(kCutThreads) void wide_cut_kernel(
     if (level == 1) {
       const int lim = min(F, (anchor + b - 1) / b);
       for (int k = 0; k < lim; ++k) {
-        const bool in = !pmask || ((pmask[geo.bdiv.div((uint32_t)k)] >> m) & 1u);
+        const bool in = pmask ? ((pmask[geo.bdiv.div((uint32_t)k)] >> m) & 1u) : k < Fm;
         const float sk = Sq[k];
         if (in && (sk > s_cut || (sk == s_cut && (uint32_t)k <= k_cut))) {
           const int node = (int)frontier_node(pnodes, k, geo.bdiv);
@@ -1611,6 +1642,7 @@ __global__ __launch_bounds__(kUnionThreads) void wide_union_kernel(
     int n_top, WideSel w) {
   __shared__ float s_cut[kMaxMembers];
   __shared__ uint32_t k_cut[kMaxMembers];
+  __shared__ int s_lim[kMaxMembers];
   __shared__ uint32_t cnt[kUnionThreads / 64][kMaxMembers + 1];
   const int u = blockIdx.y, chunk = blockIdx.x;
   const int b = geo.b;
@@ -1620,20 +1652,29 @@ __global__ __launch_bounds__(kUnionThreads) void wide_union_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int Mu = members_of(geo, u);
   if (tid < Mu) {
-    const uint32_t* rec = w.cut + 4 * (int64_t)qh_of(geo, u, tid);
+    const int qh = qh_of(geo, u, tid);
+    const uint32_t* rec = w.cut + 4 * (int64_t)qh;
     s_cut[tid] = __uint_as_float(rec[0]);
     k_cut[tid] = rec[1];
+    s_lim[tid] = has_parent ? F : min(F, head_ntop(geo, qh));  // member's top frontier
   }
   int kk[8];
   uint32_t pm[8];
   const uint32_t* pmask = has_parent ? parent.masks + u * parent.stride : nullptr;
-  const uint32_t all = (1u << Mu) - 1u;  // Mu <= 16
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     kk[i] = c0 + (i >> 2) * (kUnionChunk / 2) + 4 * tid + (i & 3);
-    pm[i] = kk[i] < F ? (pmask ? pmask[geo.bdiv.div((uint32_t)kk[i])] : all) : 0u;
+    pm[i] = (kk[i] < F && pmask) ? pmask[geo.bdiv.div((uint32_t)kk[i])] : 0u;
   }
   __syncthreads();
+  if (!pmask) {  // top level: the members for whom the entry is a complete top node
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      uint32_t msk = 0u;
+      for (int mm = 0; mm < Mu; ++mm) msk |= (uint32_t)(kk[i] < s_lim[mm]) << mm;
+      pm[i] = msk;
+    }
+  }
   uint32_t um[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   // members in groups of four, all eight row loads of a group issued together; rows are
   // padded to a multiple of 4 and chunks start at multiples of 4, so a float4 that starts
@@ -1772,6 +1813,7 @@ __global__ __launch_bounds__(kUnionThreads) void wide_write_kernel(
   if (level != 1 || !sel_idx) return;
   for (int mm = wave; mm < Mu; mm += NW) {
     const int qh = qh_of(geo, u, mm);
+    const int anc = min(anchor, head_vis(geo, qh));  // the member's anchor tokens
     const int tok_base = (int)w.cut[4 * (int64_t)qh + 2];
     int32_t* sel = sel_idx + (int64_t)qh * cap;
     uint32_t mpos = wave_prefix_total(w.mcnt + (int64_t)qh * w.nuc, chunk, lane);
@@ -1783,7 +1825,7 @@ __global__ __launch_bounds__(kUnionThreads) void wide_write_kernel(
         const uint32_t at = mpos + (uint32_t)__popcll(bal & ((1ull << lane) - 1ull));
         const int node = (int)s_node[e];
         int32_t* dst = sel + tok_base + (int64_t)at * b;
-        if ((b & 3) == 0 && node * b >= anchor && ((uintptr_t)dst & 15u) == 0) {
+        if ((b & 3) == 0 && node * b >= anc && ((uintptr_t)dst & 15u) == 0) {
           for (int c = 0; c < b; c += 4) {
             const int tok = node * b + c;
             *reinterpret_cast<int4*>(dst + c) = make_int4(tok, tok + 1, tok + 2, tok + 3);
@@ -1791,7 +1833,7 @@ __global__ __launch_bounds__(kUnionThreads) void wide_write_kernel(
         } else {
           for (int c = 0; c < b; ++c) {
             const int tok = node * b + c;
-            if (tok >= anchor) dst[c] = tok;
+            if (tok >= anc) dst[c] = tok;
           }
         }
       }
@@ -1801,16 +1843,22 @@ __global__ __launch_bounds__(kUnionThreads) void wide_write_kernel(
 }
 
 // ---------------------------------------------------------------------------------- tail
-// Tokens after the last complete top node are attended by every head: appended to each
-// head's ascending token list (after the level-1 selection, which wrote tokens below the
-// tail only) and to its count. Without a search the list is the tail alone, and every
-// level's union count is zeroed so that the per-level lists read as empty.
-__global__ __launch_bounds__(256) void tail_kernel(Geom geo, int searched, int tail_lo,
-                                                   int n_tail, int32_t* __restrict__ sel_idx,
+// The tokens a head sees after its last complete top node (and after its anchor tokens)
+// are attended like the anchor: appended to its ascending token list (after the level-1
+// selection, which wrote tokens below them only) and to its count. Without a search the
+// list is every token the head sees, and every level's union count is zeroed so that the
+// per-level lists read as empty.
+__global__ __launch_bounds__(256) void tail_kernel(Geom geo, int searched, int anchor,
+                                                   int32_t* __restrict__ sel_idx,
                                                    int64_t cap, int32_t* __restrict__ sel_count,
                                                    uint32_t* __restrict__ counts,
                                                    int count_words) {
   const int qh = blockIdx.x;
+  // the head's tail: after its last complete top node and its anchor tokens
+  const int vis = head_vis(geo, qh);
+  const int tail_lo =
+      searched ? max((vis / geo.top_span) * geo.top_span, min(anchor, vis)) : 0;
+  const int n_tail = vis - tail_lo;
   const int base = searched ? sel_count[qh] : 0;
   if (!searched && qh == 0)
     for (int i = threadIdx.x; i < count_words; i += 256) counts[i] = 0u;
@@ -2092,12 +2140,12 @@ hipError_t launch_top_levels(const Geom& geo, const float* pyramid, const LevelB
 
 int64_t top_bitmap_words(int QH, int L) { return (int64_t)QH * (L + 1) * kTopWords; }
 
-hipError_t launch_tail(const Geom& geo, int searched, int tail_lo, int n_tail,
-                       int32_t* sel_idx, int64_t cap, int32_t* sel_count, uint32_t* counts,
-                       int count_words, hipStream_t s) {
+hipError_t launch_tail(const Geom& geo, int searched, int anchor, int32_t* sel_idx,
+                       int64_t cap, int32_t* sel_count, uint32_t* counts, int count_words,
+                       hipStream_t s) {
   const int QH = geo.B * geo.T * geo.Hq;
-  hipLaunchKernelGGL(tail_kernel, dim3(QH), dim3(256), 0, s, geo, searched, tail_lo, n_tail,
-                     sel_idx, cap, sel_count, counts, count_words);
+  hipLaunchKernelGGL(tail_kernel, dim3(QH), dim3(256), 0, s, geo, searched, anchor, sel_idx,
+                     cap, sel_count, counts, count_words);
   return hipGetLastError();
 }
 
