@@ -236,12 +236,14 @@ __global__ __launch_bounds__(kDecThreads) void decode_valu_kernel(
     }
   };
 
+  const uint32_t full = (1u << Mu) - 1u;  // without query positions: every member
   if (sp == 0 && wave == 0)
-    for (int tok = 0; tok < anc_u; ++tok) consume(tok, anchor_members(rg, Mu, tok));
+    for (int tok = 0; tok < anc_u; ++tok)
+      consume(tok, geo.pos ? anchor_members(rg, Mu, tok) : full);
   for (int i = t0 + wave; i < t1; i += kDecWaves) {
     if (i >= nnode) {  // the tail: the members whose tail holds the token
       const int tok = tail_lo + (i - nnode);
-      consume(tok, tail_members(rg, Mu, tok));
+      consume(tok, geo.pos ? tail_members(rg, Mu, tok) : full);
       continue;
     }
     const int nd = (int)geo.bdiv.div((uint32_t)i), c = i - nd * b;
@@ -381,7 +383,9 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_mfma_kernel(
           mk = tok < anchor ? 0u : s_masks[nd - nbase];
         } else {
           tok = region == 0 ? i : tail_lo + (i - nnode);
-          mk = region == 0 ? anchor_members(rg, Mu, tok) : tail_members(rg, Mu, tok);
+          // without query positions every member sees the same anchor and tail
+          mk = !geo.pos ? 0xffffu
+                        : (region == 0 ? anchor_members(rg, Mu, tok) : tail_members(rg, Mu, tok));
         }
       }
       s_tok[slot * kTile + (lane % RPI) * NI + lane / RPI] = tok;

@@ -976,13 +976,17 @@ __global__ __launch_bounds__(kTopThreads) void head_top_kernel(
   int cur = 0;
   // top level: every node complete for this head
   int F = min((int)tl.lv[l_hi].stride, head_ntop(geo, qh));
-  for (int l = l_hi; l >= l_lo; --l) {
-    const bool top = l == l_hi;
-    if (F == 0) {  // an empty frontier keeps nothing (uniform across the workgroup)
+  if (F == 0) {
+    // no complete top node: the head keeps nothing at any of these levels. (A non-empty
+    // frontier always keeps at least one node, so below the top no frontier is empty.)
+    for (int l = l_hi; l >= l_lo; --l) {
       if (tid < kTopWords) bitmaps[((int64_t)qh * (geo.L + 1) + l) * kTopWords + tid] = 0u;
       if (tid == 0) lvl_kept[(int64_t)qh * (geo.L + 1) + l] = 0;
-      continue;
     }
+    return;
+  }
+  for (int l = l_hi; l >= l_lo; --l) {
+    const bool top = l == l_hi;
     const float* Xu = pyramid + tl.xoff[l] + (int64_t)bg_of(geo, u) * tl.xstride[l];
     const uint32_t* kn = sh.kn[cur];
     // ---- score, two batches of rows in flight
