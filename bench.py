@@ -396,6 +396,52 @@ def main():
                "kernels_ms": k4}
         c_tree.router = LB.ZHA_ROUTER_F32
 
+    # causal multi-query: 16 queries per sequence at positions (i + 1) N / 16 - 1, each
+    # searching the tree over the tokens up to its position (tree prebuilt), against the
+    # dense causal comparator on the same queries
+    causal = None
+    if not args.no_extras:
+        Tc = 16
+        Qc = torch.from_numpy(W.gen_Q(dict(spec, T=Tc))).to(dev).to(K.dtype)
+        posn = ((np.arange(Tc) + 1) * (N // Tc) - 1).astype(np.int32)
+        posc = torch.from_numpy(np.tile(posn, (B, 1))).to(dev)
+        QHc = B * Tc * Hq
+        Oc = torch.empty((B, Tc, Hq, d), dtype=torch.float32, device=dev)
+        selc = torch.empty((B, Tc, Hq, N), dtype=torch.int32, device=dev)
+        cntc = torch.empty((B, Tc, Hq), dtype=torch.int32, device=dev)
+        wsc = torch.empty(Z.workspace_bytes(tree, Tc, Hq), dtype=torch.uint8, device=dev)
+        Odc = torch.empty_like(Oc)
+        dwsc = torch.empty(Z.dense_workspace_bytes(B, Hkv, N, N, d, Tc, Hq), dtype=torch.uint8,
+                           device=dev)
+        build_into()
+
+        def attend_c():
+            Z.attend(Qc, K, V, tree, p, anchor, out=Oc, sel_idx=selc, sel_count=cntc,
+                     workspace=wsc, positions=posc)
+
+        def dense_c():
+            Z.dense_attend(Qc, K, V, N, out=Odc, workspace=dwsc, positions=posc)
+
+        attend_c()
+        dense_c()
+        if args.no_graph:
+            ms_c, _ = timed(attend_c, args.steps)
+            ms_dc, _ = timed(dense_c, args.steps)
+        else:
+            ms_c, _ = timed(capture(attend_c).replay, args.steps)
+            ms_dc, _ = timed(capture(dense_c).replay, args.steps)
+        attend_c()
+        torch.cuda.synchronize()
+        cc = cntc.cpu().numpy().astype(np.float64)
+        vis = (posn + 1).astype(np.float64)[None, :, None]
+        causal = {"queries_per_sequence": Tc, "positions": "(i + 1) N / 16 - 1, i < 16",
+                  "attend_ms": round(ms_c, 4),
+                  "query_heads_per_s": round(QHc / (ms_c * 1e-3), 1),
+                  "dense_causal_ms": round(ms_dc, 4),
+                  "speedup_of_attend": round(ms_dc / ms_c, 3),
+                  "keys_read_pct_of_seen": round(100 * float(np.mean(cc / vis)), 3),
+                  "keys_read_pct_of_cache": round(100 * float(np.mean(cc / N)), 3)}
+
     cpu = near_ties = None
     if not args.no_cpu_baseline:
         cpu, near_ties = cpu_baseline(spec, p, anchor, args.cpu_units)
@@ -452,6 +498,7 @@ def main():
         "kernels": {k: {"avg_ms": round(v["avg_ms"], 4), "launches": v["launches"]}
                     for k, v in kernels.items()},
         "fp4_router": fp4,
+        "causal_multi_query": causal,
         "copy_probe_gbs": copy_gbs,
         "kernel_sources": kernel_sources_sha(),
     }
