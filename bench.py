@@ -505,6 +505,7 @@ def main():
     print(json.dumps(out), flush=True)
 
 
+SWEEP_ROUTERS = ("f32", "mxfp4")
 SWEEP_GEOMETRIES = [(2, 12), (4, 6), (4, 8), (8, 4), (16, 3), (16, 4), (64, 2), (256, 1),
                     (1024, 1)]
 SWEEP_P = [0.8, 0.9, 0.95, 0.99]
@@ -550,8 +551,11 @@ def sweep(args):
         if N % (b ** L) or N // b > (1 << 21):
             continue
         tree = Z.build_tree(K, R, b, L)
+        Z.quantize_router(tree)  # the FP4 router's copy; the float32 router is tried first
         ws = torch.empty(Z.workspace_bytes(tree, T, Hq), dtype=torch.uint8, device=dev)
-        for p in SWEEP_P:
+        for router, p in [(r, p) for r in SWEEP_ROUTERS for p in SWEEP_P]:
+            Z.set_router(tree, router)
+
             def run():
                 Z.attend(Q, K, V, tree, p, anchor, out=O, sel_idx=sel, sel_count=cnt,
                          workspace=ws)
@@ -575,7 +579,7 @@ def sweep(args):
             sel_h, cnt_h = sel.cpu().numpy(), cnt.cpu().numpy()
             hits = sum(int(pos in set(sel_h[bb, t, h, :cnt_h[bb, t, h]].tolist()))
                        for bb, pos, t, h in plan)
-            rows.append({"b": b, "L": L, "p": p, "top_node_tokens": b ** L,
+            rows.append({"b": b, "L": L, "p": p, "router": router, "top_node_tokens": b ** L,
                          "keys_read_pct": round(100 * float(kr.mean()), 2),
                          "keys_read_pct_min": round(100 * float(kr.min()), 2),
                          "keys_read_pct_max": round(100 * float(kr.max()), 2),
@@ -584,7 +588,7 @@ def sweep(args):
                          "attention_mass_kept_min": round(float(kept_mass.min()), 4),
                          "needle_recall": round(hits / len(plan), 4) if plan else None,
                          "attend_ms": round(ms, 4)})
-            print(f"# b={b} L={L} p={p}: {rows[-1]}", file=sys.stderr, flush=True)
+            print(f"# b={b} L={L} p={p} {router}: {rows[-1]}", file=sys.stderr, flush=True)
         del tree, ws
         torch.cuda.empty_cache()
     print(json.dumps({"sweep": args.workload, "query_heads": QH, "N": N, "rows": rows}),
