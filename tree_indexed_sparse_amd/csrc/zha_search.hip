@@ -1741,9 +1741,10 @@ __device__ __forceinline__ uint32_t wave_prefix_total(const uint32_t* cnt, int n
   return acc;
 }
 
-// write: per (chunk, unit). The chunk's masks and node ids are staged in LDS; each wave
-// compacts a quarter of the chunk with ballots, then writes the token lists of members
-// wave, wave + 4, ... (level 1 only).
+// write: per (chunk, unit, member group). The chunk's masks and node ids are staged in
+// LDS; in group 0 each wave compacts a quarter of the chunk with ballots into the union
+// list; at level 1 group z's wave w writes the token lists of members
+// w + 4 z, w + 4 (z + groups), ... (the groups share the members' list writing).
 __global__ __launch_bounds__(kUnionThreads) void wide_write_kernel(
     Geom geo, int level, LevelBufs parent, int has_parent, int n_top, LevelBufs cur,
     int anchor, int32_t* __restrict__ sel_idx, int64_t cap, WideSel w) {
@@ -1798,24 +1799,27 @@ __global__ __launch_bounds__(kUnionThreads) void wide_write_kernel(
   for (int v = 0; v < wave; ++v) pos += wtot[v];
   uint32_t* onodes = cur.nodes + u * cur.stride;
   uint32_t* omasks = cur.masks + u * cur.stride;
-  for (int r = 0; r < kPerWave / 64; ++r) {
-    const int e = e0 + 64 * r + lane;
-    const uint32_t msk = s_um[e];
-    const uint64_t bal = __ballot(msk != 0u);
-    if (msk) {
-      const uint32_t at = pos + (uint32_t)__popcll(bal & ((1ull << lane) - 1ull));
-      onodes[at] = s_node[e];
-      omasks[at] = msk;
+  const int zg = blockIdx.z, ng = gridDim.z;
+  if (zg == 0) {
+    for (int r = 0; r < kPerWave / 64; ++r) {
+      const int e = e0 + 64 * r + lane;
+      const uint32_t msk = s_um[e];
+      const uint64_t bal = __ballot(msk != 0u);
+      if (msk) {
+        const uint32_t at = pos + (uint32_t)__popcll(bal & ((1ull << lane) - 1ull));
+        onodes[at] = s_node[e];
+        omasks[at] = msk;
+      }
+      pos += (uint32_t)__popcll(bal);
     }
-    pos += (uint32_t)__popcll(bal);
-  }
-  if (chunk == nchunks - 1 && tid == kUnionThreads - 1) {
-    uint32_t tot = before;
-    for (int v = 0; v < NW; ++v) tot += wtot[v];
-    cur.count[u] = tot;
+    if (chunk == nchunks - 1 && tid == kUnionThreads - 1) {
+      uint32_t tot = before;
+      for (int v = 0; v < NW; ++v) tot += wtot[v];
+      cur.count[u] = tot;
+    }
   }
   if (level != 1 || !sel_idx) return;
-  for (int mm = wave; mm < Mu; mm += NW) {
+  for (int mm = wave + NW * zg; mm < Mu; mm += NW * ng) {
     const int qh = qh_of(geo, u, mm);
     const int anc = min(anchor, head_vis(geo, qh));  // the member's anchor tokens
     const int tok_base = (int)w.cut[4 * (int64_t)qh + 2];
@@ -2164,7 +2168,9 @@ hipError_t launch_union(const Geom& geo, int level, const float* S, int64_t S_st
                      hp, n_top, wide);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(wide_write_kernel, grid, dim3(kUnionThreads), 0, s, geo, level, par, hp,
+  // at level 1 the members' token lists are shared out over two workgroups per chunk
+  const dim3 wgrid(grid.x, grid.y, (level == 1 && sel_idx) ? 2 : 1);
+  hipLaunchKernelGGL(wide_write_kernel, wgrid, dim3(kUnionThreads), 0, s, geo, level, par, hp,
                      n_top, cur, anchor, sel_idx, cap, wide);
   return hipGetLastError();
 }
