@@ -77,9 +77,9 @@ def main():
     if args.sweep and args.gpus == 1:
         return sweep(args)
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
-              f"(asked for --gpus {args.gpus}). The (sequence, KV head) units shard with no "
-              f"communication; see DESIGN.md.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the library has "
+              f"no multi-GPU path. Its (sequence, KV head) units would shard across GPUs with "
+              f"no communication.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

@@ -20,7 +20,7 @@ which states the whole mechanism:
 Paragraph 2 of the same page fixes p = 0.95 and the two geometries (blocks of
 4 with 6 levels; blocks of 256 with 1 level).
 
-Readings where the page is silent (each is listed in the design doc):
+Readings where the page is silent:
 
 * pooling (not stated beyond "from 16 reference queries"): each reference query
   attends over a node's b children with a softmax at scale tau = 1/sqrt(d); the
