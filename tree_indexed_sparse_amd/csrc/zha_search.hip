@@ -956,10 +956,12 @@ __global__ __launch_bounds__(kTopThreads) void head_top_kernel(
   constexpr int RPW = 64 / LPR;           // rows per wave-wide load
   constexpr int STEP = RPW * kTopWaves * kTopUnroll;  // rows per batch
   __shared__ HeadTopShared sh;
-  const int qh = blockIdx.x;
+  // workgroup b takes member b / U of unit b % U: workgroups go to the XCDs round-robin,
+  // so (with U a multiple of 8) a unit's heads share one XCD's L2 for the rows they all read
+  const int u = (int)blockIdx.x % geo.U, m = (int)blockIdx.x / geo.U;
+  if (m >= members_of(geo, u)) return;
+  const int qh = qh_of(geo, u, m);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int u, m;
-  unit_member_of(geo, qh, &u, &m);
   const int b = geo.b;
   const bool keep_all = !(p < 1.0f);
   const int sub = lane % LPR, row_in = wave * RPW + lane / LPR;
@@ -2125,7 +2127,8 @@ hipError_t launch_top_levels(const Geom& geo, const float* pyramid, const LevelB
   const int QH = geo.B * geo.T * geo.Hq;
   const RouterView rv = router ? *router : RouterView{};
 #define ZHA_TOP(DD, TQ, F4)                                                                   \
-  hipLaunchKernelGGL((head_top_kernel<DD, TQ, F4>), dim3(QH), dim3(kTopThreads), 0, s, geo,    \
+  hipLaunchKernelGGL((head_top_kernel<DD, TQ, F4>), dim3(geo.U * geo.Tb * geo.G),             \
+                     dim3(kTopThreads), 0, s, geo,                                              \
                      pyramid, tl, geo.L, l_lo, (const TQ*)Q, p, sigma, lvl_kept, bitmaps, rv)
 #define ZHA_TOP_D(DD, TQ)          \
   if (router) ZHA_TOP(DD, TQ, true); \
