@@ -78,8 +78,14 @@ def _check(spec, name, p, anchor, positions, **kw):
          d=64, fixed=(255, 256, 257)),
     dict(name="64k deep, chunked level 1", wl="32k_deep", p=0.95, N=65536, B=1, T=2,
          fixed=(65535, 40000)),
+    # a head with no complete top node shares units with heads that have some: it has no
+    # entry at any chunked level (level 1 and 2 here), or none at a chunked top level
+    dict(name="64k deep, chunked levels, empty member", wl="32k_deep", p=0.95, N=65536, B=1,
+         T=2, fixed=(65535, 3000)),
     dict(name="64k one level, chunked top", wl="32k_deep", p=0.95, N=65536, B=1, L=1, T=2,
          fixed=(65535, 33000)),
+    dict(name="64k one level, chunked top, empty member", wl="32k_deep", p=0.9, N=65536, B=1,
+         L=1, T=2, fixed=(40000, 2)),
     dict(name="b=3", wl="tiny", p=0.9, N=3 ** 7, b=3, L=4, fixed=(80, 81, 2186)),
     dict(name="wide tree b=256", wl="256k_wide", p=0.95, N=16384, B=1, T=2, fixed=(300, 16383)),
 ])
@@ -160,3 +166,18 @@ def test_dense_causal_comparator(wl, kw):
                     err = max(err, float(np.max(np.abs(O_[bb, t, h] - want))))
     print(f"[dense causal {wl}] max err {err:.2e}", flush=True)
     assert err <= O_TOL[spec["dtype"]]
+
+
+def test_256k_deep_causal_sampled_units():
+    """The benchmark cache at full size with four positioned queries per sequence (the
+    last token, the middle, inside a top node, before the first complete top node); every
+    head of two (sequence, KV head) units is checked."""
+    spec = W.spec("256k_deep", T=4)
+    pos = np.tile(np.array([262143, 131071, 100001, 4000], np.int32), (spec["B"], 1))
+    res = H.run_gpu(spec, 0.95, positions=pos)
+    reps, _ = H.check_units(spec, res, 0.95, units=[(0, 0), (3, 3)], positions=pos,
+                            check_pyramid=False)
+    summ = C.summarize(reps)
+    print(f"[256k deep causal sampled] {summ}", flush=True)
+    assert summ["mismatches"] == 0, summ["first_mismatch"]
+    assert summ["max_o_err"] <= O_TOL[spec["dtype"]], summ["max_o_err"]

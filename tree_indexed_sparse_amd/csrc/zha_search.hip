@@ -1330,7 +1330,9 @@ __global__ __launch_bounds__(kCutThreads) void wide_cut_kernel(
   const int vis = head_vis(geo, qh);
   const int Fm = has_parent ? F : min(F, vis / geo.top_span);
   anchor = min(anchor, vis);
-  if (Fm == 0) {  // nothing to select: no entry scores above an infinite cut
+  // a member with no entry at this level (it kept nothing above: no complete top node)
+  // selects nothing; no entry scores above an infinite cut. Called block-uniformly.
+  auto empty_result = [&]() {
     if (tid == 0) {
       uint32_t* rec = w.cut + 4 * (int64_t)qh;
       rec[0] = __float_as_uint(INFINITY);
@@ -1342,6 +1344,9 @@ __global__ __launch_bounds__(kCutThreads) void wide_cut_kernel(
     }
     if (level == 1 && sel_idx)
       for (int i = tid; i < anchor; i += kCutThreads) sel_idx[(int64_t)qh * cap + i] = i;
+  };
+  if (Fm == 0) {
+    empty_result();
     return;
   }
 
@@ -1386,6 +1391,10 @@ __global__ __launch_bounds__(kCutThreads) void wide_cut_kernel(
 
   uint64_t Z;
   const uint64_t incl = cut_block_scan(hsum, sh.wsum, &Z);
+  if (Z == 0) {  // no member entry (the top entry alone carries mass 2^42)
+    empty_result();
+    return;
+  }
   const uint64_t T = keep_all ? Z : ceil_mul_p(p, Z);
   const uint64_t excl = incl - hsum;
   if (!keep_all && excl < T && incl >= T) {
