@@ -48,10 +48,10 @@ def _positions(spec, seed, fixed=()):
     return pos.astype(np.int32)
 
 
-def _check(spec, name, p, anchor, positions, **kw):
-    res = H.run_gpu(spec, p, anchor=anchor, positions=positions, **kw)
+def _check(spec, name, p, anchor, positions, n_tokens=None, **kw):
+    res = H.run_gpu(spec, p, anchor=anchor, positions=positions, N=n_tokens, **kw)
     reps, pyr = H.check_units(spec, res, p, anchor=anchor, positions=positions,
-                              check_pyramid=False)
+                              check_pyramid=False, n_tokens=n_tokens)
     summ = C.summarize(reps)
     print(f"[{name}] {summ}", flush=True)
     assert summ["mismatches"] == 0, summ["first_mismatch"]
@@ -88,15 +88,22 @@ def _check(spec, name, p, anchor, positions, **kw):
          L=1, T=2, fixed=(40000, 2)),
     dict(name="b=3", wl="tiny", p=0.9, N=3 ** 7, b=3, L=4, fixed=(80, 81, 2186)),
     dict(name="wide tree b=256", wl="256k_wide", p=0.95, N=16384, B=1, T=2, fixed=(300, 16383)),
+    dict(name="wide tree, head before the first node", wl="256k_wide", p=0.9, N=16384, B=1,
+         T=2, fixed=(9000, 100)),
+    dict(name="ragged cache of 3000 tokens", wl="tiny", p=0.9, n_tokens=3000,
+         fixed=(2999, 1500, 2047, 2048, 63, 64, 0, 2990)),
 ])
 def test_causal_matches_oracle(case):
     case = dict(case)
     name, wl, p = case.pop("name"), case.pop("wl"), case.pop("p")
     anchor = case.pop("anchor", 1)
     fixed = case.pop("fixed", ())
+    n_tokens = case.pop("n_tokens", None)
     spec = W.spec(wl, **case)
     pos = _positions(spec, seed=zlib.crc32(name.encode()) % 1000, fixed=fixed)
-    _check(spec, name, p, anchor, pos)
+    if n_tokens is not None:
+        pos = np.minimum(pos, n_tokens - 1)
+    _check(spec, name, p, anchor, pos, n_tokens=n_tokens)
 
 
 def test_causal_fp4_router():
