@@ -41,14 +41,25 @@ def sources() -> list:
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source for gfx950 and link libzha.so; returns its path."""
-    os.makedirs(OBJDIR, exist_ok=True)
+# Host-side AddressSanitizer + UndefinedBehaviorSanitizer (the device code is built as
+# usual): each sanitizer flag applies to the host compilation only.
+HOST_SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-omit-frame-pointer", "-g"]
+
+
+def build(verbose: bool = False, sanitize: bool = False) -> str:
+    """Compile every HIP source for gfx950 and link libzha.so; returns its path.
+    sanitize=True builds libzha_asan.so instead, with the host code under ASan and UBSan
+    (load it from a program built with clang's -fsanitize=address)."""
+    objdir = OBJDIR + ("_asan" if sanitize else "")
+    lib = LIB.replace("libzha.so", "libzha_asan.so") if sanitize else LIB
+    os.makedirs(objdir, exist_ok=True)
     cc = hipcc()
+    extra = HOST_SANITIZE if sanitize else []
 
     def compile_one(src: str) -> str:
-        obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
-        cmd = [cc, *FLAGS, "-c", src, "-o", obj]
+        obj = os.path.join(objdir, os.path.basename(src) + ".o")
+        cmd = [cc, *FLAGS, *extra, "-c", src, "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         r = subprocess.run(cmd, capture_output=True, text=True)
@@ -58,14 +69,18 @@ def build(verbose: bool = False) -> str:
 
     with ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
         objs = list(ex.map(compile_one, sources()))
-    tmp = LIB + ".tmp"
-    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    tmp = lib + ".tmp"
+    link_extra = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                  "-shared-libsan"] if sanitize else []
+    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *link_extra, *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    import sys
+
+    print(build(verbose=True, sanitize="--sanitize" in sys.argv))
