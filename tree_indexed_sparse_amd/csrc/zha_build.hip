@@ -394,7 +394,7 @@ __device__ __forceinline__ void wave_encode_row(const float* acc, int mem, bool 
 }
 
 template <int D, bool MASKED, bool ENC>
-__global__ __launch_bounds__(kPoolThreads) void pool_wave_b4_kernel(
+__global__ __launch_bounds__(kPoolThreads, ENC ? 2 : 3) void pool_wave_b4_kernel(
     const bf16_t* __restrict__ child, int64_t in_unit_stride, const bf16_t* __restrict__ Rall,
     PoolOut out, int nlev, int Hkv, int tile_begin, int tile_end, int row_limit, float tau) {
   constexpr int KC = D / 32;
@@ -402,9 +402,11 @@ __global__ __launch_bounds__(kPoolThreads) void pool_wave_b4_kernel(
   constexpr int RWb = D / 2 + 4;  // bf16 raw-row stride in dwords
   constexpr int RWf = D + 4;      // float row stride
   constexpr int DL = D / 16;      // output dims per lane in the weighted sums
+  // the level-2 rows (levels 2 -> 3) reuse the raw-row tile, free once level 1 is done:
+  // 51 KB per workgroup at d = 128, so three workgroups fit in a CU's LDS
+  static_assert(4 * RWf <= 16 * RWb, "level-2 rows must fit in the raw-row tile");
   __shared__ uint32_t sRaw[4][16 * RWb];
   __shared__ float sL1[4][16 * RWf];
-  __shared__ float sL2[4][4 * RWf];
 
   const int unit = blockIdx.y;
   const int g_kv = unit % Hkv;
@@ -424,7 +426,7 @@ __global__ __launch_bounds__(kPoolThreads) void pool_wave_b4_kernel(
 
   uint32_t* raw = sRaw[wave];
   float* l1 = sL1[wave];
-  float* l2 = sL2[wave];
+  float* l2 = reinterpret_cast<float*>(sRaw[wave]);
 
   // child weights of node `grp` from this lane's four scores z[r] (rows 4 grp + r):
   // softmax over the children, then the mean over the 16 references of the lane group
