@@ -134,7 +134,9 @@ def test_causal_fp4_router():
 
 
 def test_last_positions_equal_the_decode_entry_point():
-    """Every query at N - 1: zha_attend_causal gives zha_attend's outputs bit for bit."""
+    """Every query at N - 1: zha_attend_causal gives zha_attend's selections and counts bit
+    for bit, and its outputs up to the order of the split combine (the causal path cuts
+    the decode into finer pieces, since its units' work differs)."""
     Z = _Z()
     spec = W.spec("32k_deep", N=16384, B=2, T=2)
     inp = W.gen_all(spec, device="cuda")
@@ -148,7 +150,10 @@ def test_last_positions_equal_the_decode_entry_point():
     sa, sc = a[1].cpu().numpy(), c[1].cpu().numpy()
     for idx in np.ndindex(n.shape):
         assert np.array_equal(sa[idx][: n[idx]], sc[idx][: n[idx]])
-    assert torch.equal(a[0], c[0])
+    oa, oc = a[0].cpu().numpy(), c[0].cpu().numpy()
+    err = float(np.max(np.abs(oa - oc)))
+    print(f"[last positions] max |O_decode - O_causal| {err:.2e}", flush=True)
+    assert np.allclose(oa, oc, rtol=1e-5, atol=1e-6), err
 
 
 @pytest.mark.parametrize("wl,kw", [("tiny", {}), ("32k_deep", dict(N=8192, B=2, T=3))])

@@ -140,9 +140,7 @@ WsLayout layout_of(const Geom& g) {
   WsLayout w{};
   w.U = g.U;
   w.QH = g.B * g.T * g.Hq;
-  w.splits = (2048 + g.U - 1) / g.U;
-  if (w.splits > kMaxSplits) w.splits = kMaxSplits;
-  if (w.splits < 1) w.splits = 1;
+  w.splits = decode_splits(g.U, g.pos != nullptr);
   int64_t nl = g.N;
   for (int l = 1; l <= g.L; ++l) {
     nl /= g.b;
@@ -167,7 +165,7 @@ WsLayout layout_of(const Geom& g) {
   w.off_bits = off;
   off = align256(off + 4 * (int64_t)w.QH * w.bit_words);
   w.off_part = off;
-  off = align256(off + 4 * (int64_t)g.U * w.splits * kMaxMembers * (g.D + 2));
+  off = align256(off + 4 * (int64_t)g.U * decode_splits(g.U, true) * kMaxMembers * (g.D + 2));
   w.off_chunks = off;
   off = align256(off + 4 * compact_counter_words(g.U, w.n[1]));
   // chunked-selection scratch, sized for the largest frontier (level 1)
@@ -456,10 +454,9 @@ int dense_geom(int B, int Hkv, int N, int N_cap, int d, int T, int Hq, Geom* g) 
 }
 DenseLayout dense_layout(const Geom& g) {
   DenseLayout w{};
-  w.splits = (2048 + g.U - 1) / g.U;
-  if (w.splits > kMaxSplits) w.splits = kMaxSplits;
+  w.splits = decode_splits(g.U, g.pos != nullptr);
   w.off_part = 0;
-  w.total = align256(4 * (int64_t)g.U * w.splits * kMaxMembers * (g.D + 2));
+  w.total = align256(4 * (int64_t)g.U * decode_splits(g.U, true) * kMaxMembers * (g.D + 2));
   return w;
 }
 }  // namespace

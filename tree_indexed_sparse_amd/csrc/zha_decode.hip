@@ -165,12 +165,13 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(Geom geo, int spl
   }
 }
 
+// Split sp of `splits` over ntok work items: boundaries on multiples of `align`, the
+// pieces as equal as that allows (no short or empty last piece).
 __device__ __forceinline__ void split_range(int ntok, int splits, int sp, int align, int* t0,
                                             int* t1) {
-  int per = (ntok + splits - 1) / splits;
-  per = (per + align - 1) / align * align;
-  *t0 = min(sp * per, ntok);
-  *t1 = min(*t0 + per, ntok);
+  const int64_t pieces = (ntok + align - 1) / align;
+  *t0 = min((int)(sp * pieces / splits) * align, ntok);
+  *t1 = min((int)((sp + 1) * pieces / splits) * align, ntok);
 }
 
 // float32 inputs: lanes across head dims, one token at a time per wave.

@@ -13,6 +13,23 @@ constexpr int kMaxMembers = 16;    // query heads (x queries) sharing one union 
 constexpr int kMaxLog2Nodes = 21;  // frontier bound that keeps 2^42-scaled masses in u64
 constexpr int kMaxSplits = 128;    // decode splits per unit (partials merged in one workgroup)
 
+// Decode workgroups per launch: three per compute unit of the 256-CU MI355X. Two are
+// resident per CU at a time, and the launch takes as long as its busiest CU's share of the
+// K/V bytes, so the count is a multiple of the CU count and the splits are equal.
+constexpr int kDecodeWorkgroups = 3 * 256;
+
+// Decode splits per unit for U units: every unit gets the same number and the total stays
+// at or below kDecodeWorkgroups (no CU takes a fourth workgroup). With query positions the
+// units' work differs (each sees its own prefix of the cache): there the pieces are finer
+// (about 2048 workgroups), so that the dispatch of workgroups to free CUs evens it out.
+// The positioned count is never the smaller one; the workspace is sized for it.
+inline int decode_splits(int U, bool positioned) {
+  const int u = U > 0 ? U : 1;
+  int s = kDecodeWorkgroups / u;
+  if (positioned && 2048 / u > s) s = 2048 / u;
+  return s < 1 ? 1 : (s > kMaxSplits ? kMaxSplits : s);
+}
+
 typedef uint16_t bf16_t;
 
 __device__ __forceinline__ float to_f32(float v) { return v; }
