@@ -840,14 +840,20 @@ struct TopLevels {
   int64_t xstride[ZHA_MAX_LEVELS + 1];  // floats per (sequence, KV head) at level l
 };
 
+constexpr int kTopBuckets = 1024;                // score buckets of the selection
+constexpr int kTopCand = 64;                     // boundary buckets up to this size are sorted
+
 struct HeadTopShared {
   float S[kTopMax];
   uint32_t kn[2][kTopMax];              // kept node lists (previous level / this level)
-  unsigned long long hist[256];
+  unsigned long long hist[kTopBuckets]; // bucket masses; radix digit masses in the fallback
+  uint32_t hcnt[kTopBuckets];
+  unsigned long long cand[2][kTopCand]; // boundary-bucket rank keys, gathered and sorted
   unsigned long long wsum[kTopWaves];
   uint32_t wcnt[kTopWaves];
   uint32_t bits[kTopWords];
   float red[kTopWaves];
+  float red_mn[kTopWaves];
   unsigned long long scal64[2];
   uint32_t scal32[2];
 };
@@ -1021,22 +1027,38 @@ __global__ __launch_bounds__(kTopThreads) void head_top_kernel(
       sv[2] = v.z;
       sv[3] = v.w;
     }
-    uint32_t ord[kTopEPT];
     bool in[kTopEPT];
-    float mx = -INFINITY;
+    float mx = -INFINITY, mn = INFINITY;
 #pragma unroll
     for (int i = 0; i < kTopEPT; ++i) {
       in[i] = k0 + i < F;
-      ord[i] = ord_of(sv[i]);
-      if (in[i]) mx = fmaxf(mx, sv[i]);
+      if (in[i]) {
+        mx = fmaxf(mx, sv[i]);
+        mn = fminf(mn, sv[i]);
+      }
     }
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
-    if (lane == 0) sh.red[wave] = mx;
+    for (int off = 32; off >= 1; off >>= 1) {
+      mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+      mn = fminf(mn, __shfl_xor(mn, off, 64));
+    }
+    if (lane == 0) {
+      sh.red[wave] = mx;
+      sh.red_mn[wave] = mn;
+    }
+    if (tid == 0) sh.scal32[1] = 0u;  // gathered candidates
+    for (int i = tid; i < kTopBuckets; i += kTopThreads) {
+      sh.hist[i] = 0ull;
+      sh.hcnt[i] = 0u;
+    }
     __syncthreads();
     mx = sh.red[0];
+    mn = sh.red_mn[0];
 #pragma unroll
-    for (int w = 1; w < kTopWaves; ++w) mx = fmaxf(mx, sh.red[w]);
+    for (int w = 1; w < kTopWaves; ++w) {
+      mx = fmaxf(mx, sh.red[w]);
+      mn = fminf(mn, sh.red_mn[w]);
+    }
     uint64_t ms[kTopEPT];
     uint64_t msum = 0;
 #pragma unroll
@@ -1049,9 +1071,81 @@ __global__ __launch_bounds__(kTopThreads) void head_top_kernel(
     for (int i = 0; i < kTopEPT; ++i) keep[i] = in[i];
     if (!keep_all) {
       const uint64_t Z = top_block_sum(msum, sh.wsum);
-      uint64_t need = ceil_mul_p(p, Z);
+      const uint64_t T = ceil_mul_p(p, Z);
+      // Mass histogram over score buckets below the max (bucket 0 = highest scores); the
+      // boundary bucket, where the cumulative mass reaches T, is gathered and sorted by
+      // rank key (score desc, index asc) when it is small, and its masses are scanned in
+      // that order to the exact cut: the kept set is every entry ranked at or above it.
+      const float spread = fminf(mx - mn, kMaxSpread);
+      const float scale = spread > 0.f ? (float)kTopBuckets / spread : 0.f;
+#pragma unroll
+      for (int i = 0; i < kTopEPT; ++i) {
+        if (in[i]) {
+          const int bk = bucket_of<kTopBuckets>(sv[i], mx, scale, spread);
+          atomicAdd(&sh.hist[bk], (unsigned long long)ms[i]);
+          atomicAdd(&sh.hcnt[bk], 1u);
+        }
+      }
+      __syncthreads();
+      if (wave == 0) {
+        constexpr int per = kTopBuckets / 64;
+        uint64_t loc = 0;
+#pragma unroll
+        for (int i = 0; i < per; ++i) loc += sh.hist[lane * per + i];
+        const uint64_t incl = wave_incl_scan_u64(loc, lane);
+        const uint64_t excl = incl - loc;
+        if (excl < T && incl >= T) {
+          uint64_t run = excl;
+          for (int i = 0; i < per; ++i) {
+            const uint64_t nxt = run + sh.hist[lane * per + i];
+            if (nxt >= T) {
+              sh.scal32[0] = lane * per + i;  // boundary bucket
+              sh.scal64[0] = run;             // mass strictly before it
+              break;
+            }
+            run = nxt;
+          }
+        }
+      }
+      __syncthreads();
+      const int bstar = (int)sh.scal32[0];
+      const uint64_t before = sh.scal64[0];
+      const uint32_t nb = sh.hcnt[bstar];
+      if (nb <= (uint32_t)kTopCand) {
+#pragma unroll
+        for (int i = 0; i < kTopEPT; ++i)
+          if (in[i] && bucket_of<kTopBuckets>(sv[i], mx, scale, spread) == bstar)
+            sh.cand[0][atomicAdd(&sh.scal32[1], 1u)] = rank_key(sv[i], (uint32_t)(k0 + i));
+        __syncthreads();
+        if (wave == 0) {
+          // lane l < nb: candidate l goes to its rank among the (distinct) keys
+          const uint64_t key = lane < (int)nb ? sh.cand[0][lane] : 0ull;
+          int at = 0;
+          for (int j = 0; j < (int)nb; ++j) at += sh.cand[0][j] > key;
+          if (lane < (int)nb) sh.cand[1][at] = key;
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+          const uint64_t sk = lane < (int)nb ? sh.cand[1][lane] : 0ull;
+          const uint64_t mk = lane < (int)nb ? mass_fixed(float_of_ord((uint32_t)(sk >> 32)), mx)
+                                             : 0ull;
+          const uint64_t incl = wave_incl_scan_u64(mk, lane) + before;
+          if (lane < (int)nb && incl >= T && incl - mk < T) sh.scal64[1] = sk;
+        }
+        __syncthreads();
+        const uint64_t cut = sh.scal64[1];
+#pragma unroll
+        for (int i = 0; i < kTopEPT; ++i)
+          keep[i] = in[i] && rank_key(sv[i], (uint32_t)(k0 + i)) >= cut;
+      } else {
+      // boundary bucket too large to sort: mass-weighted radix select on the score ordinal
+      uint32_t ord[kTopEPT];
+#pragma unroll
+      for (int i = 0; i < kTopEPT; ++i) ord[i] = ord_of(sv[i]);
+      uint64_t need = T;
       uint32_t prefix = 0u, pbits = 0u;
       for (int shift = 24; shift >= 0; shift -= 8) {
+        __syncthreads();
         if (tid < 256) sh.hist[tid] = 0ull;
         __syncthreads();
 #pragma unroll
@@ -1100,6 +1194,7 @@ __global__ __launch_bounds__(kTopThreads) void head_top_kernel(
         const bool tie = in[i] && ord[i] == prefix;
         keep[i] = in[i] && (ord[i] > prefix || (tie && (uint64_t)rank < ties));
         rank += tie;
+      }
       }
     }
     // ---- kept list (ascending) and bitmap of kept node ids
