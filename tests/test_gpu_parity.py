@@ -190,6 +190,39 @@ def test_exact_ties_broken_by_lowest_index(N):
     Z.attend.last_workspace = None
 
 
+@pytest.mark.parametrize("case", [
+    dict(N=16384, L=5, groups=1, p=0.95),     # every score ties at every level
+    dict(N=16384, L=5, groups=8, p=0.9),      # 8 distinct keys in runs of 2048 tokens
+    dict(N=4096, L=4, groups=64, p=0.8),      # runs of 64 tokens: ties inside each top node
+])
+def test_exact_ties_in_fused_top_levels(case):
+    """Tied scores in the fused top levels (frontiers of at most 1024 entries walked per
+    head in one workgroup): boundary buckets both small enough to be sorted in one wave
+    and too large for it (the radix fallback); the kept sets take the lowest node ids
+    among tied entries, as in the oracle."""
+    import tree_indexed_sparse_amd as Z
+    import oracle as O
+
+    N, L, groups, p = case["N"], case["L"], case["groups"], case["p"]
+    spec = W.spec("tiny", N=N, b=4, L=L, T=2, needles="none")
+    inp = W.gen_all(spec, device="cuda")
+    K = inp["K"]
+    run = N // groups
+    K[0, 0] = K[0, 0, ::run].clone().repeat_interleave(run, dim=0)
+    res = H.run_gpu(spec, p, inputs=inp)
+    K_u = K[0, 0].cpu().numpy()
+    V_u = inp["V"][0, 0].cpu().numpy()
+    levels = O.build_tree_unit(K_u, inp["R"][0].cpu().numpy(), 4, L)
+    for t in range(2):
+        r = O.attend_head(inp["Q"][0, t, 0].cpu().numpy(), levels, K_u, V_u, 4, L, p, 1)
+        n = int(res["cnt"][0, t, 0])
+        print(f"[ties in top levels {case}] t={t} kept {n} tokens, oracle {len(r.S)}", flush=True)
+        assert n == len(r.S), (t, n, len(r.S))
+        assert np.array_equal(res["sel"][0, t, 0, :n], r.S)
+        assert np.max(np.abs(res["O"][0, t, 0] - r.O)) < 1e-4
+    Z.attend.last_workspace = None
+
+
 def test_tied_groups_in_chunked_selection():
     """Keys repeat in groups of 512 nodes (2048 tokens), so the 16384-node top frontier
     (chunked selection) has 32 distinct scores, each shared by 512 nodes: the cut falls
