@@ -394,6 +394,62 @@ __device__ __forceinline__ uint64_t wave_incl_scan_u64(uint64_t v, int lane) {
   return v;
 }
 
+// The same cut for n <= 64 candidates within one wave (no block barrier): called by one
+// whole wave; tmp: 64 words; writes out[0] = the cut key, out[1] = the kept candidates.
+// The caller's block barrier after it publishes out.
+__device__ void wave_cut(const unsigned long long* cand, unsigned long long* tmp, int n,
+                         uint64_t before, uint64_t T, float mx, unsigned long long* out) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t kk = lane < n ? cand[lane] : 0ull;
+  int at = 0;
+  for (int j = 0; j < n; ++j) at += cand[j] > kk;
+  if (lane < n) tmp[at] = kk;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const uint64_t sk = lane < n ? tmp[lane] : 0ull;
+  const uint64_t mk = lane < n ? mass_fixed(float_of_ord((uint32_t)(sk >> 32)), mx) : 0ull;
+  const uint64_t incl = wave_incl_scan_u64(mk, lane) + before;
+  if (lane < n && incl >= T && incl - mk < T) {
+    out[0] = sk;
+    out[1] = (uint64_t)(lane + 1);
+  }
+}
+
+// The exact cut among the n (1 <= n <= NT) candidates of a boundary bucket: distinct rank
+// keys in cand[0 .. n), in any order. Each is put at its rank (key descending: score
+// descending, index ascending), their masses are scanned in that order starting from
+// `before` (the mass of every entry ranked above the bucket), and the first candidate at
+// which the cumulative mass reaches T is the cut. Returns its key; *kept = the bucket's
+// candidates ranked at or above it. Called by every thread of the block; reorders cand;
+// wsum: NT / 64 words, out: two words of shared memory.
+template <int NT>
+__device__ uint64_t small_cut(unsigned long long* cand, int n, uint64_t before, uint64_t T,
+                              float mx, unsigned long long* wsum, unsigned long long* out,
+                              uint32_t* kept) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint64_t kk = tid < n ? cand[tid] : 0ull;
+  int at = 0;
+  for (int j = 0; j < n; ++j) at += cand[j] > kk;
+  __syncthreads();
+  if (tid < n) cand[at] = kk;
+  __syncthreads();
+  const uint64_t sk = tid < n ? cand[tid] : 0ull;
+  const uint64_t mk = tid < n ? mass_fixed(float_of_ord((uint32_t)(sk >> 32)), mx) : 0ull;
+  uint64_t incl = wave_incl_scan_u64(mk, lane);
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  for (int w = 0; w < wave; ++w) incl += wsum[w];
+  incl += before;
+  if (tid < n && incl >= T && incl - mk < T) {
+    out[0] = sk;
+    out[1] = (uint64_t)(tid + 1);
+  }
+  __syncthreads();
+  *kept = (uint32_t)out[1];
+  return out[0];
+}
+
 constexpr int kVec = 4;                         // frontier entries per thread per tile
 constexpr int kTileE = kSelThreads * kVec;      // 2048 entries per tile
 constexpr int kCache = 16384;                   // frontier entries cached in LDS (64 KB)
@@ -408,6 +464,7 @@ struct SelShared {
   uint32_t tile_bits[kTileE / 32];
   float red_f[2][kSelWaves];
   uint32_t wave_sum[kSelWaves];
+  unsigned long long wsum64[kSelWaves];
   unsigned long long scalar_u64[4];
   uint32_t scalar_u32[8];
 };
@@ -633,6 +690,14 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
         }
       }
       __syncthreads();
+      if (nb <= 64u) {
+        if (wave == 0) wave_cut(sh.cand, sh.hm, (int)nb, before, T, mx, &sh.scalar_u64[2]);
+        __syncthreads();
+      } else if (nb <= (uint32_t)kSelThreads) {
+        uint32_t kept_b;
+        small_cut<kSelThreads>(sh.cand, (int)nb, before, T, mx, sh.wsum64, &sh.scalar_u64[2],
+                               &kept_b);
+      } else {
       int P2 = 1;
       while (P2 < (int)nb) P2 <<= 1;
       for (int i = nb + tid; i < P2; i += kSelThreads) sh.cand[i] = 0ull;
@@ -677,6 +742,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
         }
       }
       __syncthreads();
+      }
     } else {
       // boundary bucket too large to sort: exact MSD radix select on the 64-bit rank
       // key, restricted to the boundary bucket, 8 bits per pass
@@ -841,14 +907,14 @@ struct TopLevels {
 };
 
 constexpr int kTopBuckets = 1024;                // score buckets of the selection
-constexpr int kTopCand = 64;                     // boundary buckets up to this size are sorted
+static_assert(kTopMax * sizeof(float) >= 64 * sizeof(unsigned long long),
+              "the score array holds the boundary bucket's candidate keys");
 
 struct HeadTopShared {
   float S[kTopMax];
   uint32_t kn[2][kTopMax];              // kept node lists (previous level / this level)
   unsigned long long hist[kTopBuckets]; // bucket masses; radix digit masses in the fallback
   uint32_t hcnt[kTopBuckets];
-  unsigned long long cand[2][kTopCand]; // boundary-bucket rank keys, gathered and sorted
   unsigned long long wsum[kTopWaves];
   uint32_t wcnt[kTopWaves];
   uint32_t bits[kTopWords];
@@ -1111,29 +1177,18 @@ __global__ __launch_bounds__(kTopThreads) void head_top_kernel(
       const int bstar = (int)sh.scal32[0];
       const uint64_t before = sh.scal64[0];
       const uint32_t nb = sh.hcnt[bstar];
-      if (nb <= (uint32_t)kTopCand) {
+      if (nb <= 64u) {
+        // the scores were read into registers above, so the score array holds the
+        // candidates now
+        unsigned long long* cand = reinterpret_cast<unsigned long long*>(sh.S);
 #pragma unroll
         for (int i = 0; i < kTopEPT; ++i)
           if (in[i] && bucket_of<kTopBuckets>(sv[i], mx, scale, spread) == bstar)
-            sh.cand[0][atomicAdd(&sh.scal32[1], 1u)] = rank_key(sv[i], (uint32_t)(k0 + i));
+            cand[atomicAdd(&sh.scal32[1], 1u)] = rank_key(sv[i], (uint32_t)(k0 + i));
         __syncthreads();
-        if (wave == 0) {
-          // lane l < nb: candidate l goes to its rank among the (distinct) keys
-          const uint64_t key = lane < (int)nb ? sh.cand[0][lane] : 0ull;
-          int at = 0;
-          for (int j = 0; j < (int)nb; ++j) at += sh.cand[0][j] > key;
-          if (lane < (int)nb) sh.cand[1][at] = key;
-          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-          __builtin_amdgcn_wave_barrier();
-          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-          const uint64_t sk = lane < (int)nb ? sh.cand[1][lane] : 0ull;
-          const uint64_t mk = lane < (int)nb ? mass_fixed(float_of_ord((uint32_t)(sk >> 32)), mx)
-                                             : 0ull;
-          const uint64_t incl = wave_incl_scan_u64(mk, lane) + before;
-          if (lane < (int)nb && incl >= T && incl - mk < T) sh.scal64[1] = sk;
-        }
+        if (wave == 0) wave_cut(cand, sh.hist, (int)nb, before, T, mx, sh.scal64);
         __syncthreads();
-        const uint64_t cut = sh.scal64[1];
+        const uint64_t cut = sh.scal64[0];
 #pragma unroll
         for (int i = 0; i < kTopEPT; ++i)
           keep[i] = in[i] && rank_key(sv[i], (uint32_t)(k0 + i)) >= cut;
@@ -1523,6 +1578,19 @@ __global__ __launch_bounds__(kCutThreads) void wide_cut_kernel(
         }
       }
       __syncthreads();
+      if (nb <= 64u) {
+        if (wave == 0) wave_cut(sh.cand, sh.radix, (int)nb, before, T, mx, &sh.scalar_u64[2]);
+        __syncthreads();
+        key = sh.scalar_u64[2];
+        if (tid == 0) sh.scalar_u32[3] = (uint32_t)sh.scalar_u64[3];  // kept of the bucket
+        __syncthreads();
+      } else if (nb <= (uint32_t)kCutThreads) {
+        uint32_t kept_b;
+        key = small_cut<kCutThreads>(sh.cand, (int)nb, before, T, mx, sh.wsum, &sh.scalar_u64[2],
+                                     &kept_b);
+        if (tid == 0) sh.scalar_u32[3] = kept_b;  // kept entries of the boundary bucket
+        __syncthreads();
+      } else {
       // the exact cut among the gathered candidates: a mass-weighted radix select on the
       // score ordinal (4 passes of 8 bits) finds the cut score; the candidates tied at it
       // share one mass, and the first ceil(rest / mass) of them by index are kept
@@ -1663,6 +1731,7 @@ __global__ __launch_bounds__(kCutThreads) void wide_cut_kernel(
       if (tid == 0) sh.scalar_u32[3] = nabove + (uint32_t)ties;
       __syncthreads();
       key = ((uint64_t)prefix << 32) | (uint64_t)(0xffffffffu - kc);
+      }
     } else {
       // boundary bucket too large to sort: exact MSD radix select on the rank key,
       // restricted to the boundary bucket, 8 bits per pass
