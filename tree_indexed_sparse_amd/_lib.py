@@ -87,8 +87,7 @@ def load() -> ctypes.CDLL:
         return _lib
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is not built; run `python __graft_entry__.py` or "
-            "`python tree_indexed_sparse_amd/build.py` first")
+            f"{LIB_PATH} is not built; run `python tree_indexed_sparse_amd/build.py` first")
     lib = ctypes.CDLL(LIB_PATH)
     vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
     P = ctypes.POINTER

@@ -7,7 +7,7 @@ with each other.
 """
 
 from .synth import (  # noqa: F401
-    CONFIGS,
+    WORKLOADS,
     spec,
     gen_R,
     gen_Q,

@@ -36,7 +36,7 @@ CLUSTER = 64
 N_REF = 16
 
 # name -> shapes. "dtype" is the storage dtype of K, V, Q and R.
-CONFIGS = {
+WORKLOADS = {
     # tiny fp32 case the oracle finishes in well under a second
     "tiny": dict(dtype="f32", B=1, T=8, Hq=1, Hkv=1, d=64, N=4096, b=4, L=3,
                  p=(0.95,), seed=1, needles="tiny"),
@@ -61,7 +61,7 @@ def spec(name: str, **overrides) -> dict:
     ``r_std`` (default 1/sqrt(d)) and ``needles`` may also be overridden, e.g.
     ``r_std=1.0`` for sharp pooling softmaxes in tests.
     """
-    s = dict(CONFIGS[name])
+    s = dict(WORKLOADS[name])
     s["name"] = name
     s.update(overrides)
     s.setdefault("r_std", 1.0 / math.sqrt(s["d"]))
