@@ -887,11 +887,14 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
 // Per level and head:
 //   score:  sigma * q . X for every frontier row; a row is split over D / 4 lanes that
 //           each take four dims, and the partial sums are added across those lanes;
-//   select: a mass-weighted radix select over the 32-bit score ordinal finds the cut
-//           score (the lowest score whose cumulative mass, in descending order, reaches
-//           ceil(p Z)); the entries tied at the cut share one mass, so the first
-//           ceil(rest / mass) of them by index are kept. This is the same
-//           (score desc, index asc) prefix the other selection paths keep.
+//   select: a fixed-point mass histogram over score buckets below the max finds the
+//           bucket where the cumulative mass (scores descending) reaches ceil(p Z); one
+//           wave ranks that bucket's entries (at most 64) by (score desc, index asc) and
+//           scans their masses to the exact cut. A larger boundary bucket (many equal
+//           scores) takes a mass-weighted radix select over the 32-bit score ordinal:
+//           the entries tied at the cut share one mass, so the first ceil(rest / mass)
+//           of them by index are kept. Both keep the same (score desc, index asc)
+//           prefix as the other selection paths.
 constexpr int kTopThreads = 1024;
 constexpr int kTopWaves = kTopThreads / 64;
 constexpr int kTopMax = 4096;                    // frontier entries the kernel holds
