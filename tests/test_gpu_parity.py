@@ -135,6 +135,19 @@ def test_edge_cases(case):
     _assert_ok(spec, summ, pyr)
 
 
+@pytest.mark.parametrize("B,Hkv", [(16, 48), (5, 60)])
+def test_many_units_few_decode_splits(B, Hkv):
+    """768 (sequence, KV head) units, which get one decode split each, and 300 units, which
+    get two: three sampled units against the oracle."""
+    spec = W.spec("tiny", B=B, Hkv=Hkv, Hq=Hkv, T=1, N=1024, needles="none")
+    res = H.run_gpu(spec, 0.9)
+    units = [(0, 0), (B - 1, Hkv - 1), (B // 2, Hkv // 3)]
+    reps, pyr = H.check_units(spec, res, 0.9, units=units)
+    summ = C.summarize(reps)
+    _report(f"{B * Hkv} units", summ, pyr)
+    _assert_ok(spec, summ, pyr)
+
+
 def test_bf16_d64_and_multi_sequence():
     spec = W.spec("32k_deep", d=64, N=8192, B=3, Hq=8, Hkv=2, L=4, r_std=0.125)
     res = H.run_gpu(spec, 0.95)
