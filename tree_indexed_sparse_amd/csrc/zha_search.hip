@@ -846,26 +846,12 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     if (level == 1 && sel) {
       const int ntok = (int)tile_total * b;
       int32_t* dst0 = sel + anchor - dup + (int64_t)running * b;
-      if ((b & 3) == 0) {
-        // four tokens of one node per 16-byte store where the run is aligned and past the
-        // anchor
-        for (int i = 4 * tid; i < ntok; i += 4 * kSelThreads) {
-          const int rr = (int)geo.bdiv.div((uint32_t)i), c = i - rr * b;
-          const int tok = (int)sh.tile_nodes[rr] * b + c;
-          int32_t* dst = dst0 + (int64_t)rr * b + c;
-          if (tok >= anchor && ((uintptr_t)dst & 15u) == 0) {
-            *reinterpret_cast<int4*>(dst) = make_int4(tok, tok + 1, tok + 2, tok + 3);
-          } else {
-            for (int j = 0; j < 4; ++j)
-              if (tok + j >= anchor) dst[j] = tok + j;
-          }
-        }
-      } else {
-        for (int i = tid; i < ntok; i += kSelThreads) {
-          const int rr = (int)geo.bdiv.div((uint32_t)i), c = i - rr * b;
-          const int tok = (int)sh.tile_nodes[rr] * b + c;
-          if (tok >= anchor) dst0[(int64_t)rr * b + c] = tok;
-        }
+      // one token per thread: each wave's store covers 256 contiguous bytes, however the
+      // list is aligned
+      for (int i = tid; i < ntok; i += kSelThreads) {
+        const int rr = (int)geo.bdiv.div((uint32_t)i), c = i - rr * b;
+        const int tok = (int)sh.tile_nodes[rr] * b + c;
+        if (tok >= anchor) dst0[(int64_t)rr * b + c] = tok;
       }
     }
     __syncthreads();
@@ -1931,6 +1917,7 @@ __global__ __launch_bounds__(kUnionThreads) void wide_write_kernel(
   __shared__ uint32_t s_um[kUnionChunk];
   __shared__ uint32_t s_node[kUnionChunk];
   __shared__ uint32_t wtot[NW];
+  __shared__ uint32_t s_stage[NW][64];  // a wave's kept nodes of 64 entries
   const int u = blockIdx.y, chunk = blockIdx.x;
   const int b = geo.b;
   const int F = has_parent ? b * (int)parent.count[u] : n_top;
@@ -2003,26 +1990,26 @@ __global__ __launch_bounds__(kUnionThreads) void wide_write_kernel(
     const int tok_base = (int)w.cut[4 * (int64_t)qh + 2];
     int32_t* sel = sel_idx + (int64_t)qh * cap;
     uint32_t mpos = wave_prefix_total(w.mcnt + (int64_t)qh * w.nuc, chunk, lane);
+    uint32_t* stage = s_stage[wave];
     for (int r = 0; r < kUnionChunk / 64; ++r) {
+      // the member's kept nodes of these 64 entries, in order, then their tokens with one
+      // 4-byte store per lane: each store instruction covers 256 contiguous bytes, however
+      // the list is aligned
       const int e = 64 * r + lane;
       const bool kept = (s_um[e] >> mm) & 1u;
       const uint64_t bal = __ballot(kept);
-      if (kept) {
-        const uint32_t at = mpos + (uint32_t)__popcll(bal & ((1ull << lane) - 1ull));
-        const int node = (int)s_node[e];
-        int32_t* dst = sel + tok_base + (int64_t)at * b;
-        if ((b & 3) == 0 && node * b >= anc && ((uintptr_t)dst & 15u) == 0) {
-          for (int c = 0; c < b; c += 4) {
-            const int tok = node * b + c;
-            *reinterpret_cast<int4*>(dst + c) = make_int4(tok, tok + 1, tok + 2, tok + 3);
-          }
-        } else {
-          for (int c = 0; c < b; ++c) {
-            const int tok = node * b + c;
-            if (tok >= anc) dst[c] = tok;
-          }
-        }
+      if (kept) stage[__popcll(bal & ((1ull << lane) - 1ull))] = s_node[e];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const int ntok = __popcll(bal) * b;
+      int32_t* dst = sel + tok_base + (int64_t)mpos * b;
+      for (int j = lane; j < ntok; j += 64) {
+        const int q = (int)geo.bdiv.div((uint32_t)j);
+        const int tok = (int)stage[q] * b + (j - q * b);
+        if (tok >= anc) dst[j] = tok;
       }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       mpos += (uint32_t)__popcll(bal);
     }
   }
