@@ -47,6 +47,43 @@ __device__ __forceinline__ uint32_t frontier_node(const uint32_t* pnodes, int k,
   return pnodes[q] * bd.d + ((uint32_t)k - q * bd.d);
 }
 
+// Token list run: dst[j] = nodes[j / b] * b + j % b for j < ntok, skipping tokens below
+// `anc` (the anchor tokens, written separately). Threads t = 0, nt, 2 nt, ... of the nt
+// taking part write the 16-byte aligned groups of four with one store each and the few
+// entries before the first aligned group and after the last with 4-byte stores, so every
+// store instruction covers contiguous, aligned memory however the run starts.
+__device__ __forceinline__ void write_token_run(int32_t* dst, int ntok, const uint32_t* nodes,
+                                                const FastDiv& bd, int anc, int t, int nt) {
+  const int b = (int)bd.d;
+  auto tok_of = [&](int j) {
+    const int q = (int)bd.div((uint32_t)j);
+    return (int)nodes[q] * b + (j - q * b);
+  };
+  const int head = min((int)((4u - (uint32_t)(((uintptr_t)dst >> 2) & 3u)) & 3u), ntok);
+  const int groups = (ntok - head) >> 2;
+  const int tail0 = head + 4 * groups;
+  for (int j = t; j < head; j += nt) {
+    const int tok = tok_of(j);
+    if (tok >= anc) dst[j] = tok;
+  }
+  for (int g = t; g < groups; g += nt) {
+    const int j = head + 4 * g;
+    const int t0 = tok_of(j), t1 = tok_of(j + 1), t2 = tok_of(j + 2), t3 = tok_of(j + 3);
+    if (t0 >= anc && t1 >= anc && t2 >= anc && t3 >= anc) {
+      *reinterpret_cast<int4*>(dst + j) = make_int4(t0, t1, t2, t3);
+    } else {
+      if (t0 >= anc) dst[j] = t0;
+      if (t1 >= anc) dst[j + 1] = t1;
+      if (t2 >= anc) dst[j + 2] = t2;
+      if (t3 >= anc) dst[j + 3] = t3;
+    }
+  }
+  for (int j = tail0 + t; j < ntok; j += nt) {
+    const int tok = tok_of(j);
+    if (tok >= anc) dst[j] = tok;
+  }
+}
+
 // ------------------------------------------------------------------------------ score
 // S^T[row][member] = X[row] . Q[member] on v_mfma_f32_16x16x4_f32, 16 frontier rows per
 // MFMA block: lane (member = l % 16, group = l / 16) feeds row `member`'s dims
@@ -844,15 +881,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const int words = min(kTileE, F - t0 + 31) / 32;
     if (tid < words) kbits[t0 / 32 + tid] = sh.tile_bits[tid];
     if (level == 1 && sel) {
-      const int ntok = (int)tile_total * b;
-      int32_t* dst0 = sel + anchor - dup + (int64_t)running * b;
-      // one token per thread: each wave's store covers 256 contiguous bytes, however the
-      // list is aligned
-      for (int i = tid; i < ntok; i += kSelThreads) {
-        const int rr = (int)geo.bdiv.div((uint32_t)i), c = i - rr * b;
-        const int tok = (int)sh.tile_nodes[rr] * b + c;
-        if (tok >= anchor) dst0[(int64_t)rr * b + c] = tok;
-      }
+      write_token_run(sel + anchor - dup + (int64_t)running * b, (int)tile_total * b,
+                      sh.tile_nodes, geo.bdiv, anchor, tid, kSelThreads);
     }
     __syncthreads();
     running += tile_total;
@@ -1992,15 +2022,15 @@ __global__ __launch_bounds__(kUnionThreads) void wide_write_kernel(
     uint32_t mpos = wave_prefix_total(w.mcnt + (int64_t)qh * w.nuc, chunk, lane);
     uint32_t* stage = s_stage[wave];
     for (int r = 0; r < kUnionChunk / 64; ++r) {
-      // the member's kept nodes of these 64 entries, in order, then their tokens with one
-      // 4-byte store per lane: each store instruction covers 256 contiguous bytes, however
-      // the list is aligned
+      // the member's kept nodes of these 64 entries, in order, then their tokens
       const int e = 64 * r + lane;
       const bool kept = (s_um[e] >> mm) & 1u;
       const uint64_t bal = __ballot(kept);
       if (kept) stage[__popcll(bal & ((1ull << lane) - 1ull))] = s_node[e];
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      // one token per lane: each store covers up to 256 contiguous bytes (a short run: the
+      // aligned 16-byte form costs more than it saves here)
       const int ntok = __popcll(bal) * b;
       int32_t* dst = sel + tok_base + (int64_t)mpos * b;
       for (int j = lane; j < ntok; j += 64) {
