@@ -562,6 +562,155 @@ __global__ __launch_bounds__(kPoolThreads, ENC ? 2 : 3) void pool_wave_b4_kernel
 }
 
 // ------------------------------------------------------------------------------------
+// Upper levels of deep trees (b = 4): the same wave-centric pooling of three levels over
+// float32 child rows (a stored pyramid level). Each wave owns 64 consecutive child rows;
+// a 16-row block at a time is loaded into A-operand registers, scored on
+// v_mfma_f32_16x16x4_f32 (the C layout again gives each lane all four children of one
+// node for one reference), staged in the wave's LDS tile for the weighted sums, and the
+// two levels above repeat this on the rows kept in LDS. No workgroup barrier; a node's
+// arithmetic never depends on its position.
+template <typename Tr, int D, bool MASKED>
+__global__ __launch_bounds__(kPoolThreads) void pool_wave_f32_kernel(
+    const float* __restrict__ child, int64_t in_unit_stride, const Tr* __restrict__ Rall,
+    PoolOut out, int nlev, int Hkv, int tile_begin, int tile_end, int row_limit, float tau) {
+  constexpr int NQ = D / 16;
+  constexpr int RWf = D + 4;  // float row stride (padding spreads banks)
+  constexpr int DL = D / 16;  // output dims per lane in the weighted sums
+  __shared__ float sRaw[4][16 * RWf];  // a block's child rows; later the middle level's rows
+  __shared__ float sL1[4][16 * RWf];   // the first pooled level's 16 rows
+
+  const int unit = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int mem = lane & 15, grp = lane >> 4;
+  const int t = tile_begin + blockIdx.x * (kPoolThreads / 64) + wave;
+  if (t >= tile_end) return;
+
+  const Tr* R = Rall + (int64_t)(unit % Hkv) * kNRef * D;
+  float rf[NQ][4];
+#pragma unroll
+  for (int q = 0; q < NQ; ++q)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) rf[q][e] = to_f32(R[mem * D + 16 * q + 4 * grp + e]);
+  float* raw = sRaw[wave];
+  float* l1 = sL1[wave];
+
+  auto weights = [&](const f32x4_t& zc, float w[4]) {
+    float z[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) z[r] = tau * zc[r];
+    const float mx = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+    float e[4], sum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      e[r] = expf(z[r] - mx);
+      sum += e[r];
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float a = e[r] / sum;
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) a += __shfl_xor(a, off, 64);
+      w[r] = a * (1.f / kNRef);
+    }
+  };
+  auto score = [&](const f32x4_t (&x)[NQ]) {
+    f32x4_t zc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      zc = __builtin_amdgcn_mfma_f32_16x16x4f32(x[q][0], rf[q][0], zc, 0, 0, 0);
+      zc = __builtin_amdgcn_mfma_f32_16x16x4f32(x[q][1], rf[q][1], zc, 0, 0, 0);
+      zc = __builtin_amdgcn_mfma_f32_16x16x4f32(x[q][2], rf[q][2], zc, 0, 0, 0);
+      zc = __builtin_amdgcn_mfma_f32_16x16x4f32(x[q][3], rf[q][3], zc, 0, 0, 0);
+    }
+    return zc;
+  };
+  // lane (mem, grp): node grp's weighted sum over dims DL mem .. + DL from rows `in`
+  auto pooled = [&](const float* in, const float w[4], float (&acc)[DL]) {
+#pragma unroll
+    for (int i = 0; i < DL; ++i) acc[i] = 0.f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const float* rp = &in[(4 * grp + c) * RWf + DL * mem];
+#pragma unroll
+      for (int i = 0; i < DL; ++i) acc[i] = fmaf(w[c], rp[i], acc[i]);
+    }
+  };
+
+  const float* src = child + unit * in_unit_stride + (int64_t)t * kWaveRows * D;
+  // child rows at or past row_limit are not cached yet: only complete nodes are stored
+  const int vrows = MASKED ? min(kWaveRows, row_limit - t * kWaveRows) : kWaveRows;
+  float* dst1 = out.ptr[0] + unit * out.unit_stride[0] + (int64_t)t * 16 * D;
+  f32x4_t x[NQ], xn[NQ];
+#pragma unroll
+  for (int q = 0; q < NQ; ++q)
+    x[q] = *reinterpret_cast<const f32x4_t*>(src + (int64_t)mem * D + 16 * q + 4 * grp);
+#pragma unroll
+  for (int blk = 0; blk < 4; ++blk) {
+    if (blk + 1 < 4) {  // the next block's rows are in flight while this one is pooled
+#pragma unroll
+      for (int q = 0; q < NQ; ++q)
+        xn[q] = *reinterpret_cast<const f32x4_t*>(src + (int64_t)(16 * (blk + 1) + mem) * D +
+                                                  16 * q + 4 * grp);
+    }
+    float w[4];
+    weights(score(x), w);
+#pragma unroll
+    for (int q = 0; q < NQ; ++q)
+      *reinterpret_cast<f32x4_t*>(&raw[mem * RWf + 16 * q + 4 * grp]) = x[q];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    float acc[DL];
+    pooled(raw, w, acc);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int node = 4 * blk + grp;
+    const bool st1 = 4 * (node + 1) <= vrows;
+#pragma unroll
+    for (int i = 0; i < DL; i += 4) {
+      const float4 o = make_float4(acc[i], acc[i + 1], acc[i + 2], acc[i + 3]);
+      if (st1) *reinterpret_cast<float4*>(dst1 + (int64_t)node * D + DL * mem + i) = o;
+      *reinterpret_cast<float4*>(&l1[node * RWf + DL * mem + i]) = o;
+    }
+    if (blk + 1 < 4) {
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) x[q] = xn[q];
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+  // the two levels above, from the rows in LDS (16 rows, then 4 kept in the raw tile)
+  for (int j = 1; j < nlev; ++j) {
+    const float* in = (j == 1) ? l1 : raw;
+    const int rows = (j == 1) ? 16 : 4;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q)
+      x[q] = mem < rows ? *reinterpret_cast<const f32x4_t*>(&in[mem * RWf + 16 * q + 4 * grp])
+                        : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float w[4];
+    weights(score(x), w);
+    const int nodes = rows / 4;
+    if (grp < nodes) {
+      float acc[DL];
+      pooled(in, w, acc);
+      float* dst = out.ptr[j] + unit * out.unit_stride[j] + ((int64_t)t * nodes + grp) * D;
+      const int span = j == 1 ? 16 : 64;  // child rows under one node of this level
+      const bool stj = span * (grp + 1) <= vrows;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int i = 0; i < DL; i += 4) {
+        const float4 o = make_float4(acc[i], acc[i + 1], acc[i + 2], acc[i + 3]);
+        if (stj) *reinterpret_cast<float4*>(dst + DL * mem + i) = o;
+        if (j == 1) *reinterpret_cast<float4*>(&raw[grp * RWf + DL * mem + i]) = o;
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+}
+
+// ------------------------------------------------------------------------------------
 // Wide nodes (64 < b <= 256) over bf16 keys: one workgroup per node, wave w owns children
 // 64 w .. 64 w + 63, loaded straight into the A operand of v_mfma_f32_16x16x32_bf16
 // (z = tau R x^T, 16 children x 16 references per block). Each reference's softmax max
@@ -728,6 +877,26 @@ hipError_t launch_wave_b4(const void* child, int64_t in_unit_stride, const void*
   return hipGetLastError();
 }
 
+template <typename Tr, int D>
+hipError_t launch_wave_f32(const void* child, int64_t in_unit_stride, const void* R,
+                           const PoolOut& out, int nlev, int units, int Hkv, int row_begin,
+                           int row_end, int row_limit, hipStream_t s) {
+  const int t0 = row_begin / kWaveRows, t1 = row_end / kWaveRows;
+  if (t1 <= t0) return hipSuccess;
+  const int per_wg = kPoolThreads / 64;  // one tile per wave
+  dim3 grid((t1 - t0 + per_wg - 1) / per_wg, units);
+  const float tau = 1.0f / sqrtf((float)D);
+  if (row_limit < row_end)
+    hipLaunchKernelGGL((pool_wave_f32_kernel<Tr, D, true>), grid, dim3(kPoolThreads), 0, s,
+                       (const float*)child, in_unit_stride, (const Tr*)R, out, nlev, Hkv, t0, t1,
+                       row_limit, tau);
+  else
+    hipLaunchKernelGGL((pool_wave_f32_kernel<Tr, D, false>), grid, dim3(kPoolThreads), 0, s,
+                       (const float*)child, in_unit_stride, (const Tr*)R, out, nlev, Hkv, t0, t1,
+                       row_limit, tau);
+  return hipGetLastError();
+}
+
 template <typename Tin, typename Tr, int D>
 hipError_t launch_pool_t(const void* child, int64_t in_unit_stride, const void* R, float* out,
                          int64_t out_unit_stride, int units, int Hkv, int node_begin,
@@ -827,6 +996,19 @@ hipError_t launch_pool_fused(int dtype_in, const void* child, int64_t in_unit_st
     out.unit_stride[j] = out_unit_strides[j];
     out.codes[j] = rcodes ? rcodes[j] : nullptr;
     out.scales[j] = rscales ? rscales[j] : nullptr;
+  }
+  if (dtype_in == ZHA_F32 && b == 4 && nlev == 3 && !out.codes[0]) {
+    // three upper levels of a deep tree over a stored float32 level: 64-row tiles (every
+    // launch of these levels is whole tiles, so each node always takes this kernel)
+    if (dtype_r == ZHA_BF16)
+      return D == 64 ? launch_wave_f32<bf16_t, 64>(child, in_unit_stride, R, out, nlev, units,
+                                                   Hkv, row_begin, row_end, row_limit, s)
+                     : launch_wave_f32<bf16_t, 128>(child, in_unit_stride, R, out, nlev, units,
+                                                    Hkv, row_begin, row_end, row_limit, s);
+    return D == 64 ? launch_wave_f32<float, 64>(child, in_unit_stride, R, out, nlev, units, Hkv,
+                                                row_begin, row_end, row_limit, s)
+                   : launch_wave_f32<float, 128>(child, in_unit_stride, R, out, nlev, units, Hkv,
+                                                 row_begin, row_end, row_limit, s);
   }
   if (dtype_r == ZHA_BF16) {
     // bf16 keys, b = 4, rows in whole 64-row wave tiles: the wave-centric kernel (the
