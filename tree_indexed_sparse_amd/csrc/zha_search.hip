@@ -915,7 +915,8 @@ constexpr int kTopThreads = 1024;
 constexpr int kTopWaves = kTopThreads / 64;
 constexpr int kTopMax = 4096;                    // frontier entries the kernel holds
 constexpr int kTopFuse = 1024;                   // levels of at most this many nodes are fused
-constexpr int kTopEPT = kTopMax / kTopThreads;   // entries per thread (4 consecutive)
+constexpr int kTopEPT = kTopMax / kTopThreads;   // entries per thread (consecutive)
+static_assert(kTopEPT % 4 == 0, "threads read their scores as float4");
 constexpr int kTopUnroll = 8;                    // row loads per lane per batch
 constexpr int kTopWords = kTopMax / 32;          // bitmap words per (head, level)
 
@@ -1102,15 +1103,16 @@ __global__ __launch_bounds__(kTopThreads) void head_top_kernel(
     }
     __syncthreads();
 
-    // ---- select: thread tid takes entries k0 .. k0 + 3 (k0 = 4 tid)
+    // ---- select: thread tid takes entries k0 .. k0 + kTopEPT - 1 (k0 = kTopEPT tid)
     const int k0 = kTopEPT * tid;
     float sv[kTopEPT];
-    {
-      const float4 v = *reinterpret_cast<const float4*>(&sh.S[k0]);
-      sv[0] = v.x;
-      sv[1] = v.y;
-      sv[2] = v.z;
-      sv[3] = v.w;
+#pragma unroll
+    for (int i = 0; i < kTopEPT; i += 4) {
+      const float4 v = *reinterpret_cast<const float4*>(&sh.S[k0 + i]);
+      sv[i] = v.x;
+      sv[i + 1] = v.y;
+      sv[i + 2] = v.z;
+      sv[i + 3] = v.w;
     }
     bool in[kTopEPT];
     float mx = -INFINITY, mn = INFINITY;
@@ -1300,7 +1302,7 @@ __global__ __launch_bounds__(kTopThreads) void head_top_kernel(
   }
 }
 
-// Union lists of the fused levels: workgroup (unit, level); thread t takes nodes 4t .. 4t+3.
+// Union lists of the fused levels: workgroup (unit, level); thread t takes kTopEPT nodes from kTopEPT t.
 __global__ __launch_bounds__(kTopThreads) void union_top_kernel(Geom geo, TopLevels tl, int l_lo,
                                                                  const uint32_t* __restrict__ bitmaps) {
   __shared__ uint32_t wcnt[kTopWaves];
@@ -1310,7 +1312,9 @@ __global__ __launch_bounds__(kTopThreads) void union_top_kernel(Geom geo, TopLev
   const LevelBufs& cur = tl.lv[l];
   const int n = (int)cur.stride;
   const int j0 = kTopEPT * tid;
-  uint32_t msk[kTopEPT] = {0u, 0u, 0u, 0u};
+  uint32_t msk[kTopEPT];
+#pragma unroll
+  for (int i = 0; i < kTopEPT; ++i) msk[i] = 0u;
   if (j0 < n) {
     for (int mm = 0; mm < Mu; ++mm) {
       const uint32_t w =
