@@ -148,6 +148,27 @@ def test_many_units_few_decode_splits(B, Hkv):
     _assert_ok(spec, summ, pyr)
 
 
+@pytest.mark.parametrize("case", [
+    dict(name="f32 d=64 L=6", wl="tiny", N=16384, L=6, T=2),
+    dict(name="f32 d=64 L=6, ragged", wl="tiny", N=16384, L=6, T=2, n_tokens=16384 - 1000),
+    dict(name="bf16 d=64 L=6", wl="32k_deep", d=64, N=16384, B=1, Hq=8, Hkv=2),
+    dict(name="bf16 d=128 L=7", wl="32k_deep", N=32768, B=1, L=7),
+])
+def test_upper_pyramid_levels(case):
+    """Deep trees whose levels above the third are pooled by the float32 wave kernel (three
+    fused levels at b = 4): float32 and bf16 reference queries, d = 64 and 128, a cache
+    that ends inside a tile, and a seventh level above them."""
+    case = dict(case)
+    name, wl = case.pop("name"), case.pop("wl")
+    n_tokens = case.pop("n_tokens", None)
+    spec = W.spec(wl, needles="none", **case)
+    res = H.run_gpu(spec, 0.9, N=n_tokens)
+    reps, pyr = H.check_units(spec, res, 0.9, n_tokens=n_tokens)
+    summ = C.summarize(reps)
+    _report(name, summ, pyr)
+    _assert_ok(spec, summ, pyr)
+
+
 def test_bf16_d64_and_multi_sequence():
     spec = W.spec("32k_deep", d=64, N=8192, B=3, Hq=8, Hkv=2, L=4, r_std=0.125)
     res = H.run_gpu(spec, 0.95)
