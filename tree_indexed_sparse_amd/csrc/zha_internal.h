@@ -21,12 +21,12 @@ constexpr int kDecodeWorkgroups = 3 * 256;
 // Decode splits per unit for U units: every unit gets the same number and the total stays
 // at or below kDecodeWorkgroups (no CU takes a fourth workgroup). With query positions the
 // units' work differs (each sees its own prefix of the cache): there the pieces are finer
-// (about 2048 workgroups), so that the dispatch of workgroups to free CUs evens it out.
+// (about 4096 workgroups), so that the dispatch of workgroups to free CUs evens it out.
 // The positioned count is never the smaller one; the workspace is sized for it.
 inline int decode_splits(int U, bool positioned) {
   const int u = U > 0 ? U : 1;
   int s = kDecodeWorkgroups / u;
-  if (positioned && 2048 / u > s) s = 2048 / u;
+  if (positioned && 4096 / u > s) s = 4096 / u;
   return s < 1 ? 1 : (s > kMaxSplits ? kMaxSplits : s);
 }
 
