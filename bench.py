@@ -430,6 +430,22 @@ def main():
         else:
             ms_c, _ = timed(capture(attend_c).replay, args.steps)
             ms_dc, _ = timed(capture(dense_c).replay, args.steps)
+        # per-kernel durations of the causal attend (eager launches with HIP events)
+        lib.zha_timing_enable(1)
+        timed(attend_c, max(1, args.steps // 4))
+        lib.zha_timing_enable(0)
+        kernels_c = {}
+        for name, kind, levels in (("score", LB.ZHA_K_SCORE, range(1, L + 1)),
+                                   ("select", LB.ZHA_K_SELECT, range(0, L + 1)),
+                                   ("compact", LB.ZHA_K_COMPACT, range(1, L + 1)),
+                                   ("descent_top", LB.ZHA_K_DESCENT, range(1, L + 1)),
+                                   ("decode", LB.ZHA_K_DECODE, [0]),
+                                   ("combine", LB.ZHA_K_COMBINE, [0])):
+            for lv in levels:
+                tot, n = ktime(kind, lv)
+                if n:
+                    key = f"{name}_l{lv}" if (lv or name == "select") else name
+                    kernels_c[key.replace("select_l0", "tail")] = round(tot / n, 4)
         attend_c()
         torch.cuda.synchronize()
         cc = cntc.cpu().numpy().astype(np.float64)
@@ -438,6 +454,7 @@ def main():
                   "attend_ms": round(ms_c, 4),
                   "query_heads_per_s": round(QHc / (ms_c * 1e-3), 1),
                   "dense_causal_ms": round(ms_dc, 4),
+                  "kernels_ms": kernels_c,
                   "speedup_of_attend": round(ms_dc / ms_c, 3),
                   "keys_read_pct_of_seen": round(100 * float(np.mean(cc / vis)), 3),
                   "keys_read_pct_of_cache": round(100 * float(np.mean(cc / N)), 3)}
