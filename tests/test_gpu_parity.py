@@ -169,6 +169,24 @@ def test_upper_pyramid_levels(case):
     _assert_ok(spec, summ, pyr)
 
 
+@pytest.mark.parametrize("case", [
+    dict(name="bf16 b=1024", wl="32k_deep", N=16384, B=1, b=1024, L=1),
+    dict(name="bf16 b=300, ragged top", wl="32k_deep", N=300 * 20, B=1, b=300, L=1),
+    dict(name="f32 d=64 b=512", wl="tiny", N=8192, b=512, L=1, T=2),
+])
+def test_very_wide_nodes(case):
+    """Nodes of more than 256 children (the pooling's large-node kernel): one-level trees
+    of 300, 512 and 1024 keys per node."""
+    case = dict(case)
+    name, wl = case.pop("name"), case.pop("wl")
+    spec = W.spec(wl, needles="none", **case)
+    res = H.run_gpu(spec, 0.9)
+    reps, pyr = H.check_units(spec, res, 0.9)
+    summ = C.summarize(reps)
+    _report(name, summ, pyr)
+    _assert_ok(spec, summ, pyr)
+
+
 def test_bf16_d64_and_multi_sequence():
     spec = W.spec("32k_deep", d=64, N=8192, B=3, Hq=8, Hkv=2, L=4, r_std=0.125)
     res = H.run_gpu(spec, 0.95)
