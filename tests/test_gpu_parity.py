@@ -173,10 +173,13 @@ def test_upper_pyramid_levels(case):
     dict(name="bf16 b=1024", wl="32k_deep", N=16384, B=1, b=1024, L=1),
     dict(name="bf16 b=300, ragged top", wl="32k_deep", N=300 * 20, B=1, b=300, L=1),
     dict(name="f32 d=64 b=512", wl="tiny", N=8192, b=512, L=1, T=2),
+    dict(name="bf16 b=128 L=2", wl="32k_deep", N=32768, B=1, b=128, L=2),
+    dict(name="f32 d=64 b=100 L=2", wl="tiny", N=20000, b=100, L=2, T=2),
 ])
 def test_very_wide_nodes(case):
-    """Nodes of more than 256 children (the pooling's large-node kernel): one-level trees
-    of 300, 512 and 1024 keys per node."""
+    """Nodes of more than 64 children: one-level trees of 300, 512 and 1024 keys per node
+    (the large-node pooling kernel), and two-level trees of 128 and 100 whose second level
+    pools float32 rows."""
     case = dict(case)
     name, wl = case.pop("name"), case.pop("wl")
     spec = W.spec(wl, needles="none", **case)
