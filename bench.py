@@ -263,7 +263,9 @@ def main():
         else:
             rows = int(lists[lv + 1][2].sum()) * b
         frontier_rows += rows
-        score_bytes[lv] = rows * d * 4
+        # each union-frontier row read once (float32), one score written per member
+        members = min(T, max(1, 16 // (Hq // Hkv))) * (Hq // Hkv)
+        score_bytes[lv] = rows * (d * 4 + 4 * members)
     # a pooling launch that starts at level lv reads level lv - 1 once and writes every
     # level it fuses (b^k <= 64 rows per tile, as the library groups them)
     build_bytes = {}
@@ -295,6 +297,17 @@ def main():
                         unit="GB/s", frac=round(ach / HBM_PEAK_GBS, 4),
                         traffic=pmc_traffic(dom, args.workload), alg_bytes_per_launch=dom_bytes,
                         avg_launch_ms=round(kernels[dom]["avg_ms"], 4))
+
+    # every kernel with algorithmic bytes, against the same peak (the roofline object above
+    # is the longest of them): the decode's K/V gather, the scoring and the pooling
+    kernel_rooflines = {}
+    for name, nbytes in alg_bytes.items():
+        if name in kernels and nbytes:
+            ach = nbytes / (kernels[name]["avg_ms"] * 1e-3) / 1e9
+            kernel_rooflines[name] = dict(achieved_gbs=round(ach, 1),
+                                          frac=round(ach / HBM_PEAK_GBS, 4),
+                                          traffic=pmc_traffic(name, args.workload),
+                                          alg_bytes_per_launch=nbytes)
 
     kr = counts / N
     keys = dict(mean=round(100 * kr.mean(), 3), min=round(100 * kr.min(), 3),
@@ -485,6 +498,7 @@ def main():
                    "step": "zha_build_tree + zha_attend", "accumulate": "fp32",
                    "parallelism": "single GPU"},
         "roofline": roofline,
+        "kernel_rooflines": kernel_rooflines,
         "cpu_baseline": cpu,
         "needles": needles,
         "near_ties": near_ties,
