@@ -217,3 +217,31 @@ def test_causal_entry_points_reject_bad_positions(lib):
     # the other checks are zha_attend's
     assert lib.zha_attend_causal(ctypes.byref(t), FAKE, 1, 7, FAKE, FAKE, FAKE, 0.9, 1, FAKE,
                                  FAKE, 4096, FAKE, FAKE, 1 << 40, None) == -2
+
+
+def test_missing_library_fails_loudly():
+    """Without the built HIP library every entry point raises: there is no CPU fallback."""
+    import subprocess
+    import sys
+
+    code = (
+        "import torch\n"
+        "import tree_indexed_sparse_amd._lib as L\n"
+        "L.LIB_PATH = '/nonexistent/libzha.so'\n"
+        "import tree_indexed_sparse_amd as Z\n"
+        "K = torch.zeros(1, 1, 64, 64)\n"
+        "R = torch.zeros(1, 16, 64)\n"
+        "for call in (Z.load, lambda: Z.build_tree(K, R, 4, 1), lambda: Z.tree_bytes(1, 1, 64, 64, 4, 1)):\n"
+        "    try:\n"
+        "        call()\n"
+        "    except ImportError as e:\n"
+        "        assert 'not built' in str(e)\n"
+        "    else:\n"
+        "        raise SystemExit('no error')\n"
+        "print('raised')\n"
+    )
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True,
+                       timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]
+    assert "raised" in r.stdout
