@@ -90,6 +90,9 @@ def _check(spec, name, p, anchor, positions, n_tokens=None, **kw):
     dict(name="wide tree b=256", wl="256k_wide", p=0.95, N=16384, B=1, T=2, fixed=(300, 16383)),
     dict(name="wide tree, head before the first node", wl="256k_wide", p=0.9, N=16384, B=1,
          T=2, fixed=(9000, 100)),
+    # 4 x 16 x 8 = 512 query heads: the fused top levels in two workgroups per CU
+    dict(name="tiny, 16 queries x 8 heads x 4 sequences", wl="tiny", p=0.9, B=4, T=16, Hq=8,
+         Hkv=2, fixed=(4095, 2047, 2048, 63, 64, 0)),
     dict(name="ragged cache of 3000 tokens", wl="tiny", p=0.9, n_tokens=3000,
          fixed=(2999, 1500, 2047, 2048, 63, 64, 0, 2990)),
 ])

@@ -200,6 +200,23 @@ def test_bf16_d64_and_multi_sequence():
 
 
 @pytest.mark.parametrize("case", [
+    dict(name="512 heads, G=16", d=128, N=8192, B=4, Hq=128, Hkv=8, p=0.95),
+    dict(name="272 heads (68 units), f32 d=64", wl="tiny", B=17, Hq=16, Hkv=4, T=1, p=0.9),
+])
+def test_more_heads_than_compute_units(case):
+    """More query heads than the GPU has compute units: the fused top levels run two
+    half-size workgroups per CU, which must keep exactly the same sets; every head checked."""
+    case = dict(case)
+    name, p = case.pop("name"), case.pop("p")
+    spec = W.spec(case.pop("wl", "32k_deep"), **case)
+    res = H.run_gpu(spec, p)
+    reps, pyr = H.check_units(spec, res, p)
+    summ = C.summarize(reps)
+    _report(name, summ, pyr)
+    _assert_ok(spec, summ, pyr)
+
+
+@pytest.mark.parametrize("case", [
     dict(name="64k deep p=0.95", N=65536, p=0.95),
     dict(name="64k deep p=0.5", N=65536, p=0.5),
     dict(name="64k deep p=1", N=65536, p=1.0),

@@ -13,10 +13,12 @@ constexpr int kMaxMembers = 16;    // query heads (x queries) sharing one union 
 constexpr int kMaxLog2Nodes = 21;  // frontier bound that keeps 2^42-scaled masses in u64
 constexpr int kMaxSplits = 128;    // decode splits per unit (partials merged in one workgroup)
 
-// Decode workgroups per launch: three per compute unit of the 256-CU MI355X. Two are
-// resident per CU at a time, and the launch takes as long as its busiest CU's share of the
-// K/V bytes, so the count is a multiple of the CU count and the splits are equal.
-constexpr int kDecodeWorkgroups = 3 * 256;
+constexpr int kComputeUnits = 256;  // MI355X: 8 XCDs of 32 CUs
+
+// Decode workgroups per launch: three per compute unit. Two are resident per CU at a
+// time, and the launch takes as long as its busiest CU's share of the K/V bytes, so the
+// count is a multiple of the CU count and the splits are equal.
+constexpr int kDecodeWorkgroups = 3 * kComputeUnits;
 
 // Decode splits per unit for U units: every unit gets the same number and the total stays
 // at or below kDecodeWorkgroups (no CU takes a fourth workgroup). With query positions the

@@ -917,7 +917,14 @@ constexpr int kTopMax = 4096;                    // frontier entries the kernel 
 constexpr int kTopFuse = 1024;                   // levels of at most this many nodes are fused
 constexpr int kTopEPT = kTopMax / kTopThreads;   // entries per thread (consecutive)
 static_assert(kTopEPT % 4 == 0, "threads read their scores as float4");
-constexpr int kTopUnroll = 8;                    // row loads per lane per batch
+// row loads per lane per batch: 8 at kTopThreads, so a CU has the same rows in flight
+// with one workgroup of kTopThreads or two of half that size
+template <int NT>
+constexpr int top_unroll() { return 8 * NT / kTopThreads; }
+// The kernel fits in 128 VGPRs, four waves per SIMD: one workgroup of kTopThreads per
+// CU, or two of kTopThreads / 2. The smaller one runs when there are more query heads than
+// CUs, so that two heads share a CU and each hides the other's barriers and load latency.
+constexpr int kTopMinWaves = 4;
 constexpr int kTopWords = kTopMax / 32;          // bitmap words per (head, level)
 
 struct TopLevels {
@@ -945,6 +952,7 @@ struct HeadTopShared {
 };
 
 // sum over the block of one u64 per thread (every thread gets it)
+template <int NT>
 __device__ __forceinline__ uint64_t top_block_sum(uint64_t v, unsigned long long* wsum) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
@@ -958,17 +966,17 @@ __device__ __forceinline__ uint64_t top_block_sum(uint64_t v, unsigned long long
   __syncthreads();
   uint64_t t = 0;
 #pragma unroll
-  for (int w = 0; w < kTopWaves; ++w) t += wsum[w];
+  for (int w = 0; w < (NT / 64); ++w) t += wsum[w];
   return t;
 }
 
-template <int D>
-__device__ __forceinline__ void top_rows_load(f32x4_t (&x)[kTopUnroll], const float* Xu,
+template <int D, int NT>
+__device__ __forceinline__ void top_rows_load(f32x4_t (&x)[top_unroll<NT>()], const float* Xu,
                                               const uint32_t* kn, bool top, const FastDiv& bd,
                                               int r0, int F, int sub, int row_in) {
-  constexpr int RPB = (64 / (D / 4)) * kTopWaves;  // rows per block-wide load
+  constexpr int RPB = (64 / (D / 4)) * (NT / 64);  // rows per block-wide load
 #pragma unroll
-  for (int i = 0; i < kTopUnroll; ++i) {
+  for (int i = 0; i < top_unroll<NT>(); ++i) {
     const uint32_t r = (uint32_t)min(r0 + i * RPB + row_in, F - 1);
     uint32_t node = r;
     if (!top) {
@@ -980,14 +988,14 @@ __device__ __forceinline__ void top_rows_load(f32x4_t (&x)[kTopUnroll], const fl
   }
 }
 
-template <int D>
-__device__ __forceinline__ void top_rows_score(const f32x4_t (&x)[kTopUnroll], const float (&qv)[4],
+template <int D, int NT>
+__device__ __forceinline__ void top_rows_score(const f32x4_t (&x)[top_unroll<NT>()], const float (&qv)[4],
                                                float* S, float sigma, int r0, int F, int sub,
                                                int row_in) {
   constexpr int LPR = D / 4;
-  constexpr int RPB = (64 / LPR) * kTopWaves;
+  constexpr int RPB = (64 / LPR) * (NT / 64);
 #pragma unroll
-  for (int i = 0; i < kTopUnroll; ++i) {
+  for (int i = 0; i < top_unroll<NT>(); ++i) {
     float v = x[i].x * qv[0];
     v = fmaf(x[i].y, qv[1], v);
     v = fmaf(x[i].z, qv[2], v);
@@ -1003,7 +1011,7 @@ __device__ __forceinline__ void top_rows_score(const f32x4_t (&x)[kTopUnroll], c
 // so the lanes of column 0 hold the block's 16 dot products (rows 4 (l / 16) + r).
 constexpr int kTopFp4Batch = 4;  // row blocks per wave in flight
 
-template <int D>
+template <int D, int NT>
 __device__ __forceinline__ void top_fp4_score(const uint8_t* RCu, const uint8_t* RSu,
                                               const uint32_t* kn, bool top, const FastDiv& bd,
                                               int F, uint4 qc, uint32_t qs, float* S,
@@ -1011,11 +1019,11 @@ __device__ __forceinline__ void top_fp4_score(const uint8_t* RCu, const uint8_t*
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int mem = lane & 15, grp = lane >> 4;
   const int nblk = (F + 15) / 16;
-  for (int b0 = wave; b0 < nblk; b0 += kTopWaves * kTopFp4Batch) {
+  for (int b0 = wave; b0 < nblk; b0 += (NT / 64) * kTopFp4Batch) {
     Fp4Rows R[kTopFp4Batch];
 #pragma unroll
     for (int j = 0; j < kTopFp4Batch; ++j) {
-      const int blk = b0 + j * kTopWaves;
+      const int blk = b0 + j * (NT / 64);
       const uint32_t r = (uint32_t)min(16 * blk + mem, F - 1);
       uint32_t node = r;
       if (!top) {
@@ -1026,7 +1034,7 @@ __device__ __forceinline__ void top_fp4_score(const uint8_t* RCu, const uint8_t*
     }
 #pragma unroll
     for (int j = 0; j < kTopFp4Batch; ++j) {
-      const int blk = b0 + j * kTopWaves;
+      const int blk = b0 + j * (NT / 64);
       const f32x4_t c = fp4_mfma(R[j], qc, qs, f32x4_t{0.f, 0.f, 0.f, 0.f});
       if (mem == 0 && blk < nblk) {
 #pragma unroll
@@ -1039,14 +1047,16 @@ __device__ __forceinline__ void top_fp4_score(const uint8_t* RCu, const uint8_t*
   }
 }
 
-template <int D, typename Tq, bool FP4>
-__global__ __launch_bounds__(kTopThreads) void head_top_kernel(
+template <int D, typename Tq, bool FP4, int NT>
+__global__ __launch_bounds__(NT, kTopMinWaves) void head_top_kernel(
     Geom geo, const float* __restrict__ pyramid, TopLevels tl, int l_hi, int l_lo,
     const Tq* __restrict__ Q, float p, float sigma, int32_t* __restrict__ lvl_kept,
     uint32_t* __restrict__ bitmaps, RouterView rv) {
+  constexpr int EPT = kTopMax / NT;       // entries per thread (consecutive)
+  static_assert(EPT % 4 == 0, "threads read their scores as float4");
   constexpr int LPR = D / 4;              // lanes per row
   constexpr int RPW = 64 / LPR;           // rows per wave-wide load
-  constexpr int STEP = RPW * kTopWaves * kTopUnroll;  // rows per batch
+  constexpr int STEP = RPW * (NT / 64) * top_unroll<NT>();  // rows per batch
   __shared__ HeadTopShared sh;
   // workgroup b takes member b / U of unit b % U: workgroups go to the XCDs round-robin,
   // so (with U a multiple of 8) a unit's heads share one XCD's L2 for the rows they all read
@@ -1086,38 +1096,38 @@ __global__ __launch_bounds__(kTopThreads) void head_top_kernel(
     // ---- score, two batches of rows in flight
     if constexpr (FP4) {
       const int64_t rows = tl.xstride[l] / D;
-      top_fp4_score<D>(rv.codes[l] + (int64_t)bg_of(geo, u) * rows * (D / 2),
+      top_fp4_score<D, NT>(rv.codes[l] + (int64_t)bg_of(geo, u) * rows * (D / 2),
                        rv.scales[l] + (int64_t)bg_of(geo, u) * rows * (D / kMxBlock), kn, top,
                        geo.bdiv, F, qc, qs, sh.S, sigma);
     } else {
-      f32x4_t xa[kTopUnroll], xb[kTopUnroll];
-      top_rows_load<D>(xa, Xu, kn, top, geo.bdiv, 0, F, sub, row_in);
+      f32x4_t xa[top_unroll<NT>()], xb[top_unroll<NT>()];
+      top_rows_load<D, NT>(xa, Xu, kn, top, geo.bdiv, 0, F, sub, row_in);
       for (int r0 = 0; r0 < F; r0 += 2 * STEP) {
-        if (r0 + STEP < F) top_rows_load<D>(xb, Xu, kn, top, geo.bdiv, r0 + STEP, F, sub, row_in);
-        top_rows_score<D>(xa, qv, sh.S, sigma, r0, F, sub, row_in);
+        if (r0 + STEP < F) top_rows_load<D, NT>(xb, Xu, kn, top, geo.bdiv, r0 + STEP, F, sub, row_in);
+        top_rows_score<D, NT>(xa, qv, sh.S, sigma, r0, F, sub, row_in);
         if (r0 + STEP >= F) break;
         if (r0 + 2 * STEP < F)
-          top_rows_load<D>(xa, Xu, kn, top, geo.bdiv, r0 + 2 * STEP, F, sub, row_in);
-        top_rows_score<D>(xb, qv, sh.S, sigma, r0 + STEP, F, sub, row_in);
+          top_rows_load<D, NT>(xa, Xu, kn, top, geo.bdiv, r0 + 2 * STEP, F, sub, row_in);
+        top_rows_score<D, NT>(xb, qv, sh.S, sigma, r0 + STEP, F, sub, row_in);
       }
     }
     __syncthreads();
 
-    // ---- select: thread tid takes entries k0 .. k0 + kTopEPT - 1 (k0 = kTopEPT tid)
-    const int k0 = kTopEPT * tid;
-    float sv[kTopEPT];
+    // ---- select: thread tid takes entries k0 .. k0 + EPT - 1 (k0 = EPT tid)
+    const int k0 = EPT * tid;
+    float sv[EPT];
 #pragma unroll
-    for (int i = 0; i < kTopEPT; i += 4) {
+    for (int i = 0; i < EPT; i += 4) {
       const float4 v = *reinterpret_cast<const float4*>(&sh.S[k0 + i]);
       sv[i] = v.x;
       sv[i + 1] = v.y;
       sv[i + 2] = v.z;
       sv[i + 3] = v.w;
     }
-    bool in[kTopEPT];
+    bool in[EPT];
     float mx = -INFINITY, mn = INFINITY;
 #pragma unroll
-    for (int i = 0; i < kTopEPT; ++i) {
+    for (int i = 0; i < EPT; ++i) {
       in[i] = k0 + i < F;
       if (in[i]) {
         mx = fmaxf(mx, sv[i]);
@@ -1134,7 +1144,7 @@ __global__ __launch_bounds__(kTopThreads) void head_top_kernel(
       sh.red_mn[wave] = mn;
     }
     if (tid == 0) sh.scal32[1] = 0u;  // gathered candidates
-    for (int i = tid; i < kTopBuckets; i += kTopThreads) {
+    for (int i = tid; i < kTopBuckets; i += NT) {
       sh.hist[i] = 0ull;
       sh.hcnt[i] = 0u;
     }
@@ -1142,22 +1152,22 @@ __global__ __launch_bounds__(kTopThreads) void head_top_kernel(
     mx = sh.red[0];
     mn = sh.red_mn[0];
 #pragma unroll
-    for (int w = 1; w < kTopWaves; ++w) {
+    for (int w = 1; w < (NT / 64); ++w) {
       mx = fmaxf(mx, sh.red[w]);
       mn = fminf(mn, sh.red_mn[w]);
     }
-    uint64_t ms[kTopEPT];
+    uint64_t ms[EPT];
     uint64_t msum = 0;
 #pragma unroll
-    for (int i = 0; i < kTopEPT; ++i) {
+    for (int i = 0; i < EPT; ++i) {
       ms[i] = in[i] ? mass_fixed(sv[i], mx) : 0ull;
       msum += ms[i];
     }
-    bool keep[kTopEPT];
+    bool keep[EPT];
 #pragma unroll
-    for (int i = 0; i < kTopEPT; ++i) keep[i] = in[i];
+    for (int i = 0; i < EPT; ++i) keep[i] = in[i];
     if (!keep_all) {
-      const uint64_t Z = top_block_sum(msum, sh.wsum);
+      const uint64_t Z = top_block_sum<NT>(msum, sh.wsum);
       const uint64_t T = ceil_mul_p(p, Z);
       // Mass histogram over score buckets below the max (bucket 0 = highest scores); the
       // boundary bucket, where the cumulative mass reaches T, is gathered and sorted by
@@ -1166,7 +1176,7 @@ __global__ __launch_bounds__(kTopThreads) void head_top_kernel(
       const float spread = fminf(mx - mn, kMaxSpread);
       const float scale = spread > 0.f ? (float)kTopBuckets / spread : 0.f;
 #pragma unroll
-      for (int i = 0; i < kTopEPT; ++i) {
+      for (int i = 0; i < EPT; ++i) {
         if (in[i]) {
           const int bk = bucket_of<kTopBuckets>(sv[i], mx, scale, spread);
           atomicAdd(&sh.hist[bk], (unsigned long long)ms[i]);
@@ -1203,7 +1213,7 @@ __global__ __launch_bounds__(kTopThreads) void head_top_kernel(
         // candidates now
         unsigned long long* cand = reinterpret_cast<unsigned long long*>(sh.S);
 #pragma unroll
-        for (int i = 0; i < kTopEPT; ++i)
+        for (int i = 0; i < EPT; ++i)
           if (in[i] && bucket_of<kTopBuckets>(sv[i], mx, scale, spread) == bstar)
             cand[atomicAdd(&sh.scal32[1], 1u)] = rank_key(sv[i], (uint32_t)(k0 + i));
         __syncthreads();
@@ -1211,13 +1221,13 @@ __global__ __launch_bounds__(kTopThreads) void head_top_kernel(
         __syncthreads();
         const uint64_t cut = sh.scal64[0];
 #pragma unroll
-        for (int i = 0; i < kTopEPT; ++i)
+        for (int i = 0; i < EPT; ++i)
           keep[i] = in[i] && rank_key(sv[i], (uint32_t)(k0 + i)) >= cut;
       } else {
       // boundary bucket too large to sort: mass-weighted radix select on the score ordinal
-      uint32_t ord[kTopEPT];
+      uint32_t ord[EPT];
 #pragma unroll
-      for (int i = 0; i < kTopEPT; ++i) ord[i] = ord_of(sv[i]);
+      for (int i = 0; i < EPT; ++i) ord[i] = ord_of(sv[i]);
       uint64_t need = T;
       uint32_t prefix = 0u, pbits = 0u;
       for (int shift = 24; shift >= 0; shift -= 8) {
@@ -1225,7 +1235,7 @@ __global__ __launch_bounds__(kTopThreads) void head_top_kernel(
         if (tid < 256) sh.hist[tid] = 0ull;
         __syncthreads();
 #pragma unroll
-        for (int i = 0; i < kTopEPT; ++i)
+        for (int i = 0; i < EPT; ++i)
           if (in[i] && (ord[i] & pbits) == prefix)
             atomicAdd(&sh.hist[(ord[i] >> shift) & 255u], (unsigned long long)ms[i]);
         __syncthreads();
@@ -1262,11 +1272,11 @@ __global__ __launch_bounds__(kTopThreads) void head_top_kernel(
       const uint64_t ties = (need + mcut - 1) / mcut;
       uint32_t ntie = 0;
 #pragma unroll
-      for (int i = 0; i < kTopEPT; ++i) ntie += (in[i] && ord[i] == prefix);
+      for (int i = 0; i < EPT; ++i) ntie += (in[i] && ord[i] == prefix);
       uint32_t tot;
-      uint32_t rank = block_excl_scan<kTopThreads>(ntie, sh.wcnt, &tot);
+      uint32_t rank = block_excl_scan<NT>(ntie, sh.wcnt, &tot);
 #pragma unroll
-      for (int i = 0; i < kTopEPT; ++i) {
+      for (int i = 0; i < EPT; ++i) {
         const bool tie = in[i] && ord[i] == prefix;
         keep[i] = in[i] && (ord[i] > prefix || (tie && (uint64_t)rank < ties));
         rank += tie;
@@ -1276,13 +1286,13 @@ __global__ __launch_bounds__(kTopThreads) void head_top_kernel(
     // ---- kept list (ascending) and bitmap of kept node ids
     uint32_t nk = 0;
 #pragma unroll
-    for (int i = 0; i < kTopEPT; ++i) nk += keep[i];
+    for (int i = 0; i < EPT; ++i) nk += keep[i];
     uint32_t kept;
-    uint32_t pos = block_excl_scan<kTopThreads>(nk, sh.wcnt, &kept);
+    uint32_t pos = block_excl_scan<NT>(nk, sh.wcnt, &kept);
     if (tid < kTopWords) sh.bits[tid] = 0u;
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < kTopEPT; ++i) {
+    for (int i = 0; i < EPT; ++i) {
       if (keep[i]) {
         uint32_t node = (uint32_t)(k0 + i);
         if (!top) {
@@ -2323,10 +2333,14 @@ hipError_t launch_top_levels(const Geom& geo, const float* pyramid, const LevelB
   const float sigma = 1.0f / sqrtf((float)geo.D);
   const int QH = geo.B * geo.T * geo.Hq;
   const RouterView rv = router ? *router : RouterView{};
-#define ZHA_TOP(DD, TQ, F4)                                                                   \
-  hipLaunchKernelGGL((head_top_kernel<DD, TQ, F4>), dim3(geo.U * geo.Tb * geo.G),             \
-                     dim3(kTopThreads), 0, s, geo,                                              \
+  const int n_wg = geo.U * geo.Tb * geo.G;
+  const bool half = n_wg > kComputeUnits;
+#define ZHA_TOP_NT(DD, TQ, F4, NT)                                                            \
+  hipLaunchKernelGGL((head_top_kernel<DD, TQ, F4, NT>), dim3(n_wg), dim3(NT), 0, s, geo,     \
                      pyramid, tl, geo.L, l_lo, (const TQ*)Q, p, sigma, lvl_kept, bitmaps, rv)
+#define ZHA_TOP(DD, TQ, F4)                          \
+  if (half) ZHA_TOP_NT(DD, TQ, F4, kTopThreads / 2); \
+  else ZHA_TOP_NT(DD, TQ, F4, kTopThreads)
 #define ZHA_TOP_D(DD, TQ)          \
   if (router) ZHA_TOP(DD, TQ, true); \
   else ZHA_TOP(DD, TQ, false)
@@ -2339,6 +2353,7 @@ hipError_t launch_top_levels(const Geom& geo, const float* pyramid, const LevelB
   }
 #undef ZHA_TOP_D
 #undef ZHA_TOP
+#undef ZHA_TOP_NT
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(union_top_kernel, dim3(geo.U, geo.L - l_lo + 1), dim3(kTopThreads), 0, s,
