@@ -166,6 +166,8 @@ def test_encoder_special_values(d):
     dict(name="64k deep, chunked level 1", wl="32k_deep", N=65536, B=1, p=0.95),
     dict(name="b=3", wl="tiny", N=3 ** 7, b=3, L=4, p=0.9),
     dict(name="wide tree b=256", wl="256k_wide", N=16384, B=1, p=0.95),
+    # more query heads than CUs: the fused top levels in two half-size workgroups per CU
+    dict(name="512 heads, G=16", wl="32k_deep", N=8192, B=4, Hq=128, Hkv=8, p=0.95),
 ])
 def test_fp4_search_on_the_oracle_router(case):
     """The tree's router copy holds the oracle's MXFP4 codes of the oracle's pyramid, so
