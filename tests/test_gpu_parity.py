@@ -239,14 +239,31 @@ def test_chunked_selection(case):
     _assert_ok(spec, summ, pyr)
 
 
-@pytest.mark.parametrize("N", [16384, 65536])
-def test_exact_ties_broken_by_lowest_index(N):
+@pytest.mark.parametrize("case", [
+    dict(name="64k deep, 384 heads", N=65536, B=3, Hq=128, Hkv=8, p=0.95),
+    dict(name="64k one level, chunked top, 384 heads", N=65536, B=3, Hq=128, Hkv=8, L=1, p=0.9),
+])
+def test_chunked_selection_more_heads_than_compute_units(case):
+    """The chunked selection's cut in half-size workgroups (two buckets per thread), which
+    run when the query heads outnumber the CUs; three sampled units (48 heads) checked."""
+    case = dict(case)
+    name, p = case.pop("name"), case.pop("p")
+    spec = W.spec("32k_deep", **case)
+    res = H.run_gpu(spec, p)
+    reps, pyr = H.check_units(spec, res, p, units=[(0, 0), (2, 7), (1, 3)])
+    summ = C.summarize(reps)
+    _report(name, summ, pyr)
+    _assert_ok(spec, summ, pyr)
+
+
+@pytest.mark.parametrize("N,T", [(16384, 2), (65536, 2), (65536, 300)])
+def test_exact_ties_broken_by_lowest_index(N, T):
     """Identical keys everywhere: every score at every level ties. The cut must keep the
     lowest node ids; the boundary bucket holds N / 4 entries, past the sort capacity
     (at N = 65536 in the chunked selection)."""
     import tree_indexed_sparse_amd as Z
 
-    spec = W.spec("tiny", N=N, b=4, L=1, T=2, needles="none")
+    spec = W.spec("tiny", N=N, b=4, L=1, T=T, needles="none")
     inp = W.gen_all(spec, device="cuda")
     inp["K"][:] = inp["K"][0, 0, 0]
     res = H.run_gpu(spec, 0.95, inputs=inp)
@@ -254,7 +271,7 @@ def test_exact_ties_broken_by_lowest_index(N):
     K_u = inp["K"][0, 0].cpu().numpy()
     V_u = inp["V"][0, 0].cpu().numpy()
     levels = O.build_tree_unit(K_u, inp["R"][0].cpu().numpy(), 4, 1)
-    for t in range(2):
+    for t in sorted({0, 1, T - 1}):
         r = O.attend_head(inp["Q"][0, t, 0].cpu().numpy(), levels, K_u, V_u, 4, 1, 0.95, 1)
         n = int(res["cnt"][0, t, 0])
         assert np.array_equal(res["sel"][0, t, 0, :n], r.S)
@@ -295,24 +312,28 @@ def test_exact_ties_in_fused_top_levels(case):
     Z.attend.last_workspace = None
 
 
-def test_tied_groups_in_chunked_selection():
-    """Keys repeat in groups of 512 nodes (2048 tokens), so the 16384-node top frontier
-    (chunked selection) has 32 distinct scores, each shared by 512 nodes: the cut falls
-    inside a tied group and must keep its lowest node ids, a count taken from the mass."""
+@pytest.mark.parametrize("run,T", [(2048, 2), (2048, 300), (4096, 300), (16384, 300)])
+def test_tied_groups_in_chunked_selection(run, T):
+    """Keys repeat in runs of `run` tokens (run / 4 nodes), so the 16384-node top frontier
+    (chunked selection) has 65536 / run distinct scores, each shared by run / 4 nodes: the
+    cut falls inside a tied group and must keep its lowest node ids, a count taken from the
+    mass. Groups of 512, 1024 and 4096 nodes put the boundary bucket in each of the exact
+    cut's paths; 300 queries (more than the CUs) run the half-size cut workgroups, and a
+    sample of them is checked."""
     import tree_indexed_sparse_amd as Z
     import oracle as O
 
-    spec = W.spec("tiny", N=65536, b=4, L=1, T=2, needles="none")
+    spec = W.spec("tiny", N=65536, b=4, L=1, T=T, needles="none")
     inp = W.gen_all(spec, device="cuda")
     K = inp["K"]
-    groups = K[0, 0, ::2048].clone()                      # 32 distinct key vectors
-    K[0, 0] = groups.repeat_interleave(2048, dim=0)
+    groups = K[0, 0, ::run].clone()
+    K[0, 0] = groups.repeat_interleave(run, dim=0)
     for p in (0.5, 0.9):
         res = H.run_gpu(spec, p, inputs=inp)
         K_u = K[0, 0].cpu().numpy()
         V_u = inp["V"][0, 0].cpu().numpy()
         levels = O.build_tree_unit(K_u, inp["R"][0].cpu().numpy(), 4, 1)
-        for t in range(2):
+        for t in sorted({0, 1, T // 2, T - 1}):
             r = O.attend_head(inp["Q"][0, t, 0].cpu().numpy(), levels, K_u, V_u, 4, 1, p, 1)
             n = int(res["cnt"][0, t, 0])
             assert n == len(r.S), (p, t, n, len(r.S))

@@ -1376,6 +1376,9 @@ constexpr int kWideTiles = kWideChunk / kTileE;
 constexpr int kWB = 1024;                           // buckets of the chunked histogram
 constexpr int kCutThreads = 1024;                   // one bucket per thread
 constexpr int kCutWaves = kCutThreads / 64;
+// Four waves per SIMD (up to 128 VGPRs): one workgroup of kCutThreads per CU, or two of
+// half that size, which run when the heads outnumber the CUs.
+constexpr int kCutMinWaves = 4;
 constexpr int kUnionThreads = 256;
 constexpr int kUnionChunk = 2048;                   // union/write chunk: 8 entries per thread
 constexpr int64_t kWideMin = 16384;                 // frontiers of this size or more
@@ -1476,6 +1479,7 @@ struct CutShared {
 };
 
 // block-wide inclusive scan of one u64 per thread; *total = the sum over the block
+template <int NT>
 __device__ __forceinline__ uint64_t cut_block_scan(uint64_t v, unsigned long long* wsum,
                                                    uint64_t* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -1485,7 +1489,7 @@ __device__ __forceinline__ uint64_t cut_block_scan(uint64_t v, unsigned long lon
   __syncthreads();
   uint64_t before = 0, tot = 0;
 #pragma unroll
-  for (int v2 = 0; v2 < kCutWaves; ++v2) {
+  for (int v2 = 0; v2 < NT / 64; ++v2) {
     const uint64_t c = wsum[v2];
     before += (v2 < wave) ? c : 0ull;
     tot += c;
@@ -1494,12 +1498,15 @@ __device__ __forceinline__ uint64_t cut_block_scan(uint64_t v, unsigned long lon
   return before + incl;
 }
 
-__global__ __launch_bounds__(kCutThreads) void wide_cut_kernel(
+template <int NT>
+__global__ __launch_bounds__(NT, kCutMinWaves) void wide_cut_kernel(
     Geom geo, int level, const float* __restrict__ S, int64_t S_stride, LevelBufs parent,
     int has_parent, int n_top, float p, int anchor, int32_t* __restrict__ sel_idx, int64_t cap,
     int32_t* __restrict__ sel_count, int32_t* __restrict__ lvl_kept, WideSel w) {
   __shared__ CutShared sh;
   const int qh = blockIdx.x;
+  constexpr int BPT = kWB / NT;  // buckets per thread: thread t owns BPT t .. BPT t + BPT - 1
+  static_assert(BPT * NT == kWB, "whole buckets per thread");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int u, m;
   unit_member_of(geo, qh, &u, &m);
@@ -1526,38 +1533,53 @@ __global__ __launch_bounds__(kCutThreads) void wide_cut_kernel(
       if (level == 1) sel_count[qh] = anchor;
     }
     if (level == 1 && sel_idx)
-      for (int i = tid; i < anchor; i += kCutThreads) sel_idx[(int64_t)qh * cap + i] = i;
+      for (int i = tid; i < anchor; i += NT) sel_idx[(int64_t)qh * cap + i] = i;
   };
   if (Fm == 0) {
     empty_result();
     return;
   }
 
-  // bucket totals over the chunks (thread `tid` owns bucket `tid`); loads issued first
-  uint64_t hsum = 0;
-  uint32_t csum = 0;
-  const int64_t hbase = (int64_t)qh * w.nch * kWB + tid;
+  // bucket totals over the chunks (thread `tid` owns buckets BPT tid .. BPT tid + BPT - 1);
+  // loads issued first
+  uint64_t hb[BPT];
+  uint32_t cb[BPT];
+#pragma unroll
+  for (int j = 0; j < BPT; ++j) {
+    hb[j] = 0ull;
+    cb[j] = 0u;
+  }
+  const int64_t hbase = (int64_t)qh * w.nch * kWB + BPT * tid;
   {
     int c = 0;
     for (; c + 4 <= nch; c += 4) {
-      uint64_t h[4];
-      uint32_t n[4];
+      uint64_t h[4][BPT];
+      uint32_t n[4][BPT];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        h[j] = w.hm[hbase + (int64_t)(c + j) * kWB];
-        n[j] = w.hc[hbase + (int64_t)(c + j) * kWB];
-      }
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        hsum += h[j];
-        csum += n[j];
+        for (int j = 0; j < BPT; ++j) {
+          h[i][j] = w.hm[hbase + (int64_t)(c + i) * kWB + j];
+          n[i][j] = w.hc[hbase + (int64_t)(c + i) * kWB + j];
+        }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < BPT; ++j) {
+          hb[j] += h[i][j];
+          cb[j] += n[i][j];
+        }
+    }
+    for (; c < nch; ++c)
+#pragma unroll
+      for (int j = 0; j < BPT; ++j) {
+        hb[j] += w.hm[hbase + (int64_t)c * kWB + j];
+        cb[j] += w.hc[hbase + (int64_t)c * kWB + j];
       }
-    }
-    for (; c < nch; ++c) {
-      hsum += w.hm[hbase + (int64_t)c * kWB];
-      csum += w.hc[hbase + (int64_t)c * kWB];
-    }
   }
+  uint64_t hsum = 0;
+#pragma unroll
+  for (int j = 0; j < BPT; ++j) hsum += hb[j];
   if (tid == 0) {
     sh.scalar_u32[0] = 0u;  // boundary bucket
     sh.scalar_u32[1] = 0u;  // its entry count
@@ -1567,13 +1589,13 @@ __global__ __launch_bounds__(kCutThreads) void wide_cut_kernel(
     sh.scalar_u64[2] = ~0ull;
   }
   float mx, mn;
-  partial_minmax<kCutThreads>(w, qh, F, sh.red, &mx, &mn);
+  partial_minmax<NT>(w, qh, F, sh.red, &mx, &mn);
   const float spread = fminf(mx - mn, kMaxSpread);
   const float scale = spread > 0.f ? (float)kWB / spread : 0.f;
   const bool keep_all = !(p < 1.0f);
 
   uint64_t Z;
-  const uint64_t incl = cut_block_scan(hsum, sh.wsum, &Z);
+  const uint64_t incl = cut_block_scan<NT>(hsum, sh.wsum, &Z);
   if (Z == 0) {  // no member entry (the top entry alone carries mass 2^42)
     empty_result();
     return;
@@ -1581,9 +1603,17 @@ __global__ __launch_bounds__(kCutThreads) void wide_cut_kernel(
   const uint64_t T = keep_all ? Z : ceil_mul_p(p, Z);
   const uint64_t excl = incl - hsum;
   if (!keep_all && excl < T && incl >= T) {
-    sh.scalar_u32[0] = (uint32_t)tid;
-    sh.scalar_u32[1] = csum;
-    sh.scalar_u64[0] = excl;
+    // exactly one of this thread's buckets has run < T <= run + its mass
+    uint64_t run = excl;
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) {
+      if (run < T && run + hb[j] >= T) {
+        sh.scalar_u32[0] = (uint32_t)(BPT * tid + j);
+        sh.scalar_u32[1] = cb[j];
+        sh.scalar_u64[0] = run;
+      }
+      run += hb[j];
+    }
   }
   __syncthreads();
   const int bstar = keep_all ? kWB : (int)sh.scalar_u32[0];
@@ -1593,11 +1623,11 @@ __global__ __launch_bounds__(kCutThreads) void wide_cut_kernel(
   uint64_t key = ~0ull;  // keep_all: every member entry ranks at or above the cut
   if (!keep_all) {
     if (nb <= (uint32_t)kCand) {
-      for (int base = kVec * tid; base < F; base += kVec * kCutThreads * kUnroll) {
+      for (int base = kVec * tid; base < F; base += kVec * NT * kUnroll) {
         Quad q[kUnroll];
 #pragma unroll
         for (int j = 0; j < kUnroll; ++j)
-          q[j] = load_quad(Sq, pmask, m, geo.bdiv, base + j * kVec * kCutThreads, Fm);
+          q[j] = load_quad(Sq, pmask, m, geo.bdiv, base + j * kVec * NT, Fm);
 #pragma unroll
         for (int j = 0; j < kUnroll; ++j) {
 #pragma unroll
@@ -1605,7 +1635,7 @@ __global__ __launch_bounds__(kCutThreads) void wide_cut_kernel(
             if (q[j].in[i] && bucket_of<kWB>(q[j].s[i], mx, scale, spread) == bstar) {
               const uint32_t slot = atomicAdd(&sh.scalar_u32[2], 1u);
               if (slot < (uint32_t)kCand)
-                sh.cand[slot] = rank_key(q[j].s[i], (uint32_t)(base + j * kVec * kCutThreads + i));
+                sh.cand[slot] = rank_key(q[j].s[i], (uint32_t)(base + j * kVec * NT + i));
             }
           }
         }
@@ -1617,9 +1647,9 @@ __global__ __launch_bounds__(kCutThreads) void wide_cut_kernel(
         key = sh.scalar_u64[2];
         if (tid == 0) sh.scalar_u32[3] = (uint32_t)sh.scalar_u64[3];  // kept of the bucket
         __syncthreads();
-      } else if (nb <= (uint32_t)kCutThreads) {
+      } else if (nb <= (uint32_t)NT) {
         uint32_t kept_b;
-        key = small_cut<kCutThreads>(sh.cand, (int)nb, before, T, mx, sh.wsum, &sh.scalar_u64[2],
+        key = small_cut<NT>(sh.cand, (int)nb, before, T, mx, sh.wsum, &sh.scalar_u64[2],
                                      &kept_b);
         if (tid == 0) sh.scalar_u32[3] = kept_b;  // kept entries of the boundary bucket
         __syncthreads();
@@ -1627,7 +1657,7 @@ __global__ __launch_bounds__(kCutThreads) void wide_cut_kernel(
       // the exact cut among the gathered candidates: a mass-weighted radix select on the
       // score ordinal (4 passes of 8 bits) finds the cut score; the candidates tied at it
       // share one mass, and the first ceil(rest / mass) of them by index are kept
-      constexpr int per = kCand / kCutThreads;
+      constexpr int per = kCand / NT;
       uint32_t cord[per], cidx[per];
       uint64_t cm[per];
       bool cv[per];
@@ -1708,7 +1738,7 @@ __global__ __launch_bounds__(kCutThreads) void wide_cut_kernel(
       nabove = ntie = imax = 0u;
       imin = 0xffffffffu;
 #pragma unroll
-      for (int v = 0; v < kCutWaves; ++v) {
+      for (int v = 0; v < (NT / 64); ++v) {
         nabove += sh.redu[0][v];
         ntie += sh.redu[1][v];
         imin = min(imin, sh.redu[2][v]);
@@ -1770,9 +1800,9 @@ __global__ __launch_bounds__(kCutThreads) void wide_cut_kernel(
       // restricted to the boundary bucket, 8 bits per pass
       uint64_t prefix = 0, pbits = 0, need = T - before;
       for (int shift = 56; shift >= 0; shift -= 8) {
-        for (int i = tid; i < 256; i += kCutThreads) sh.radix[i] = 0ull;
+        for (int i = tid; i < 256; i += NT) sh.radix[i] = 0ull;
         __syncthreads();
-        for (int k0 = kVec * tid; k0 < F; k0 += kVec * kCutThreads) {
+        for (int k0 = kVec * tid; k0 < F; k0 += kVec * NT) {
           const Quad q = load_quad(Sq, pmask, m, geo.bdiv, k0, Fm);
 #pragma unroll
           for (int i = 0; i < kVec; ++i) {
@@ -1804,7 +1834,7 @@ __global__ __launch_bounds__(kCutThreads) void wide_cut_kernel(
       }
       key = prefix;
       uint32_t nk = 0;
-      for (int k0 = kVec * tid; k0 < F; k0 += kVec * kCutThreads) {
+      for (int k0 = kVec * tid; k0 < F; k0 += kVec * NT) {
         const Quad q = load_quad(Sq, pmask, m, geo.bdiv, k0, Fm);
 #pragma unroll
         for (int i = 0; i < kVec; ++i)
@@ -1818,7 +1848,10 @@ __global__ __launch_bounds__(kCutThreads) void wide_cut_kernel(
   const uint32_t k_cut = keep_all ? 0xffffffffu : 0xffffffffu - (uint32_t)key;
   // kept total: the buckets above the boundary plus the boundary's kept entries
   uint64_t kept64;
-  cut_block_scan(tid < bstar ? (uint64_t)csum : 0ull, sh.wsum, &kept64);
+  uint64_t above = 0;
+#pragma unroll
+  for (int j = 0; j < BPT; ++j) above += (BPT * tid + j < bstar) ? (uint64_t)cb[j] : 0ull;
+  cut_block_scan<NT>(above, sh.wsum, &kept64);
   __syncthreads();
   const uint32_t kept = (uint32_t)kept64 + sh.scalar_u32[3];
   if (tid == 0) {
@@ -1844,7 +1877,7 @@ __global__ __launch_bounds__(kCutThreads) void wide_cut_kernel(
     if (level == 1) sel_count[qh] = anchor + (int32_t)kept * b - dup;
   }
   if (level == 1 && sel_idx)
-    for (int i = tid; i < anchor; i += kCutThreads) sel_idx[(int64_t)qh * cap + i] = i;
+    for (int i = tid; i < anchor; i += NT) sel_idx[(int64_t)qh * cap + i] = i;
 }
 
 // union: per (chunk of kUnionChunk entries, unit). Thread t takes entries 4t..4t+3 and
@@ -2283,9 +2316,14 @@ hipError_t launch_select(const Geom& geo, int level, const float* S, int64_t S_s
                        hp, n_top, *wide);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(wide_cut_kernel, dim3(QH), dim3(kCutThreads), 0, s, geo, level, S,
-                       S_stride, par, hp, n_top, p, anchor, sel_idx, cap, sel_count, lvl_kept,
-                       *wide);
+    if (QH > kComputeUnits)
+      hipLaunchKernelGGL(wide_cut_kernel<kCutThreads / 2>, dim3(QH), dim3(kCutThreads / 2), 0, s,
+                         geo, level, S, S_stride, par, hp, n_top, p, anchor, sel_idx, cap,
+                         sel_count, lvl_kept, *wide);
+    else
+      hipLaunchKernelGGL(wide_cut_kernel<kCutThreads>, dim3(QH), dim3(kCutThreads), 0, s, geo,
+                         level, S, S_stride, par, hp, n_top, p, anchor, sel_idx, cap, sel_count,
+                         lvl_kept, *wide);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(select_kernel, dim3(QH), dim3(kSelThreads), 0, s, geo, level, S, S_stride,
