@@ -564,19 +564,11 @@ def sweep(args):
     inp = W.gen_all(spec, device=dev)
     K, V, Q, R = inp["K"], inp["V"], inp["Q"], inp["R"]
     QH = B * T * Hq
-    # dense attention weights of every head over all N keys (measurement only)
-    wts = torch.empty((B, T, Hq, N), dtype=torch.float32, device=dev)
-    for bb in range(B):
-        for g in range(Hkv):
-            q = Q[bb, :, g * G:(g + 1) * G, :].float().reshape(T * G, d)
-            sc = (q @ K[bb, g].float().T) / np.sqrt(d)
-            wts[bb, :, g * G:(g + 1) * G, :] = torch.softmax(sc, dim=-1).reshape(T, G, N)
-    wts = wts.reshape(QH, N)
+    wts = dense_weights(Q, K)
     O = torch.empty((B, T, Hq, d), dtype=torch.float32, device=dev)
     sel = torch.empty((B, T, Hq, N), dtype=torch.int32, device=dev)
     cnt = torch.empty((B, T, Hq), dtype=torch.int32, device=dev)
     plan = [(bb, pos, t, h) for bb in range(B) for pos, t, h in W.needle_plan(spec, bb)]
-    ar = torch.arange(N, device=dev).view(1, N)
     rows = []
     for (b, L) in SWEEP_GEOMETRIES:
         if N % (b ** L) or N // b > (1 << 21):
@@ -599,13 +591,8 @@ def sweep(args):
             e1.record()
             torch.cuda.synchronize()
             ms = e0.elapsed_time(e1) / 5
-            c = cnt.view(QH, 1).long()
-            idx = sel.view(QH, N).long()
-            valid = ar < c
-            mask = torch.zeros((QH, N), dtype=torch.float32, device=dev)
-            mask.scatter_add_(1, torch.where(valid, idx, torch.zeros_like(idx)), valid.float())
-            kept_mass = (wts * (mask > 0)).sum(-1).cpu().numpy()
-            kr = (c.view(-1).float() / N).cpu().numpy()
+            kept_mass = selected_mass(wts, sel, cnt).cpu().numpy()
+            kr = (cnt.view(-1).float() / N).cpu().numpy()
             c1 = Z.level_view(tree, T, Hq, 1, ws)[2]
             sel_h, cnt_h = sel.cpu().numpy(), cnt.cpu().numpy()
             hits = sum(int(pos in set(sel_h[bb, t, h, :cnt_h[bb, t, h]].tolist()))
@@ -624,6 +611,38 @@ def sweep(args):
         torch.cuda.empty_cache()
     print(json.dumps({"sweep": args.workload, "query_heads": QH, "N": N, "rows": rows}),
           flush=True)
+
+
+def dense_weights(Q, K):
+    """Dense softmax attention weights (scale 1/sqrt(d), float32) of every query head over
+    every key of its KV head: [B * T * Hq, N]. Measurement only (the sweep's retained-mass
+    column)."""
+    import torch
+
+    B, T, Hq, d = Q.shape
+    Hkv, N = K.shape[1], K.shape[2]
+    G = Hq // Hkv
+    wts = torch.empty((B, T, Hq, N), dtype=torch.float32, device=Q.device)
+    for bb in range(B):
+        for g in range(Hkv):
+            q = Q[bb, :, g * G:(g + 1) * G, :].float().reshape(T * G, d)
+            sc = (q @ K[bb, g].float().T) / (d ** 0.5)
+            wts[bb, :, g * G:(g + 1) * G, :] = torch.softmax(sc, dim=-1).reshape(T, G, N)
+    return wts.reshape(B * T * Hq, N)
+
+
+def selected_mass(wts, sel, cnt):
+    """Share of each query head's dense attention weight that falls on its selected keys
+    (the first cnt entries of its list): [B * T * Hq]."""
+    import torch
+
+    QH, N = wts.shape
+    c = cnt.reshape(QH, 1).long()
+    idx = sel.reshape(QH, -1)[:, :N].long()
+    valid = torch.arange(idx.shape[1], device=wts.device).view(1, -1) < c
+    mask = torch.zeros((QH, N), dtype=torch.float32, device=wts.device)
+    mask.scatter_add_(1, torch.where(valid, idx, torch.zeros_like(idx)), valid.float())
+    return (wts * (mask > 0)).sum(-1)
 
 
 def tree_bytes_written(B, Hkv, N, d, b, L):

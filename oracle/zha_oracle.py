@@ -123,19 +123,6 @@ def tail_tokens(N: int, n_top: int, b: int, L: int) -> np.ndarray:
     return np.arange(n_top * b ** L, N, dtype=np.int64)
 
 
-def build_tree(K: np.ndarray, R: np.ndarray, b: int, L: int) -> list:
-    """Pyramid for K [B, Hkv, N, d] and R [Hkv, 16, d]: levels[l] is
-    [B, Hkv, N / b^l, d] float32 for l = 1..L; levels[0] is None."""
-    B, H, N, d = K.shape
-    out = [None] + [np.empty((B, H, N // b ** l, d), np.float32) for l in range(1, L + 1)]
-    for bi in range(B):
-        for g in range(H):
-            lv = build_tree_unit(K[bi, g], R[g], b, L)
-            for l in range(1, L + 1):
-                out[l][bi, g] = lv[l]
-    return out
-
-
 # ---------------------------------------------------------------------------
 # Search: score, top-p, expand (page 3, paragraph 1).
 # ---------------------------------------------------------------------------
@@ -361,23 +348,3 @@ def attend_head_causal(q, levels, K_u, V_u, b, L, p, anchor, pos) -> HeadResult:
     """Search and exact attention of the query at position `pos` over what it sees."""
     lv, Kc, Vc = causal_view(levels, K_u, V_u, b, L, pos)
     return attend_head(q, lv, Kc, Vc, b, L, p, anchor)
-
-
-def attend(Q, K, V, tree, b, L, p, anchor=1):
-    """Every query head: Q [B, T, Hq, d]; K, V [B, Hkv, N, d]; tree from
-    build_tree. Returns a nested list res[b][t][h] of HeadResult."""
-    B, T, Hq, _ = Q.shape
-    Hkv = K.shape[1]
-    G = Hq // Hkv
-    out = []
-    for bi in range(B):
-        rows = []
-        for t in range(T):
-            row = []
-            for h in range(Hq):
-                g = h // G
-                levels = [K[bi, g]] + [tree[l][bi, g] for l in range(1, L + 1)]
-                row.append(attend_head(Q[bi, t, h], levels, K[bi, g], V[bi, g], b, L, p, anchor))
-            rows.append(row)
-        out.append(rows)
-    return out

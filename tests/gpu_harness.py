@@ -18,6 +18,34 @@ import tree_indexed_sparse_amd as Z  # noqa: E402
 import workloads as W  # noqa: E402
 
 
+# Output bounds: max-abs 1e-4 for float32 inputs and 2e-2 for bf16 inputs on unit-scale
+# values, and in every case max |O - O_oracle| <= O_REL_TOL * max |O_oracle| per head (the
+# outputs at 256K are ~1e-2 in magnitude, where the absolute bf16 bound alone would accept
+# zeros); pyramid within 1e-5 relative to each level's largest magnitude.
+O_TOL = {"f32": 1e-4, "bf16": 2e-2}
+PYR_TOL = 1e-5
+
+
+def assert_parity(spec, summ, pyr=0.0):
+    """The parity bars on a compare.summarize() result."""
+    assert summ["heads"] > 0
+    assert summ["mismatches"] == 0, summ["first_mismatch"]
+    assert summ["max_o_err"] <= O_TOL[spec["dtype"]], summ["max_o_err"]
+    assert summ["max_o_rel"] <= C.O_REL_TOL, (summ["max_o_rel"], summ["min_o_scale"])
+    assert pyr <= PYR_TOL, pyr
+
+
+def output_errors(got, want):
+    """(max |got - want|, that over max |want|) for one head's output; a non-finite
+    output counts as an infinite error."""
+    got = np.asarray(got, np.float64)
+    want = np.asarray(want, np.float64)
+    if not np.all(np.isfinite(got)):
+        return float("inf"), float("inf")
+    e = float(np.max(np.abs(got - want)))
+    return e, e / max(float(np.max(np.abs(want))), 1e-30)
+
+
 def run_gpu(spec, p, anchor=1, inputs=None, want_lists=True, tree=None, device="cuda", N=None,
             positions=None):
     """N: tokens in use (default: the whole generated cache, its capacity). The tree's

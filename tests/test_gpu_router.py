@@ -24,7 +24,7 @@ from oracle import compare as C
 
 pytestmark = pytest.mark.gpu
 
-O_TOL = {"f32": 1e-4, "bf16": 2e-2}
+O_TOL = H.O_TOL
 PYR_TOL = 1e-5
 
 
@@ -87,8 +87,7 @@ def _load_oracle_router(tree, units_levels):
 def _summ_ok(spec, name, reps):
     summ = C.summarize(reps)
     print(f"[{name}] {summ}", flush=True)
-    assert summ["mismatches"] == 0, summ["first_mismatch"]
-    assert summ["max_o_err"] <= O_TOL[spec["dtype"]], summ["max_o_err"]
+    H.assert_parity(spec, summ)
     return summ
 
 
