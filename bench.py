@@ -39,7 +39,8 @@ def parse():
     ap.add_argument("--workload", default="256k_deep")
     ap.add_argument("--p", type=float, default=None)
     ap.add_argument("--cpu-units", type=int, default=16,
-                    help="(sequence, KV head) units the CPU oracle baseline runs on")
+                    help="(sequence, KV head) units the CPU oracle baseline runs on "
+                         "(0: every unit of the batch)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", action="store_true",
                     help="geometry sweep on the workload's tensors instead of the benchmark: "
@@ -153,6 +154,26 @@ def main():
                 "median": round(float(np.median(t)), 4),
                 "p90": round(float(np.percentile(t, 90)), 4), "reps": steps}
 
+    # Cache flush between timed repetitions: writing 1 GiB evicts the 4 MB L2 of every XCD
+    # and the 256 MB Infinity Cache, so a repetition finds none of the previous one's data
+    # on chip (the flush itself sits outside the event pair).
+    flush_buf = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+
+    def flushed(fn, steps):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        torch.cuda.synchronize()
+        for a, z in ev:
+            flush_buf.zero_()
+            a.record()
+            fn()
+            z.record()
+        torch.cuda.synchronize()
+        t = np.array([a.elapsed_time(z) for a, z in ev])
+        return {"median": round(float(np.median(t)), 4), "mean": round(float(t.mean()), 4),
+                "p10": round(float(np.percentile(t, 10)), 4),
+                "p90": round(float(np.percentile(t, 90)), 4), "reps": steps}
+
     for _ in range(args.warmup):
         full_step()
     torch.cuda.synchronize()
@@ -165,6 +186,7 @@ def main():
     # launch-bound small kernels of the search then run without per-launch host overhead.
     ms_step, ms_attend, graph = ms_eager, ms_attend_eager, False
     dist = None
+    fl_step = fl_attend = None
     def capture(fn):
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
@@ -186,6 +208,8 @@ def main():
         ms_step, wall_step = timed(g_step.replay, args.steps)
         ms_attend, _ = timed(g_attend.replay, args.steps)
         dist = per_step(g_step.replay, args.steps)
+        fl_step = flushed(g_step.replay, args.steps)
+        fl_attend = flushed(g_attend.replay, args.steps)
         graph = True
         print(f"# graph step {ms_step:.3f} ms (wall {wall_step:.3f} ms)", file=sys.stderr,
               flush=True)
@@ -217,6 +241,38 @@ def main():
         ms_appends, _ = timed(appends, max(1, args.steps // 4))
     ms_build, _ = timed(build_into, args.steps)
     torch.cuda.synchronize()
+
+    # one token at a time: the last 4096 tokens of the cache appended one by one to a tree
+    # over the tokens before them (each append pools exactly the nodes its token
+    # completes; most complete none and launch nothing), eager launches from Python
+    one_tok = None
+    if not args.no_extras:
+        n_one = min(4096, N)
+
+        def one_token_appends():
+            c_tree.N = N - n_one
+            for _ in range(n_one):
+                LB.check(lib.zha_tree_append(ctypes.byref(c_tree), K.data_ptr(), R.data_ptr(),
+                                             1, torch.cuda.current_stream().cuda_stream))
+
+        one_token_appends()
+        ms_one, wall_one = timed(one_token_appends, 3)
+        lib.zha_timing_enable(1)
+        one_token_appends()
+        lib.zha_timing_enable(0)
+        tot, nl = ctypes.c_double(), ctypes.c_int64()
+        LB.check(lib.zha_timing_read(LB.ZHA_K_POOL, -1, ctypes.byref(tot), ctypes.byref(nl)))
+        one_tok = {"tokens": n_one, "b": b,
+                   "gpu_us_per_token": round(1e3 * ms_one / n_one, 3),
+                   "host_us_per_token": round(1e3 * wall_one / n_one, 3),
+                   "pool_launches": nl.value,
+                   "pool_kernel_us_per_token": round(1e3 * tot.value / n_one, 3),
+                   "pool_kernel_us_per_launch": round(1e3 * tot.value / max(nl.value, 1), 3),
+                   "note": "gpu: HIP events around the 4096 appends (the GPU idles between "
+                           "launches the host issues slower than it runs them); host: wall "
+                           "time of the Python loop; kernel: the pooling launches' own time"}
+        build_into()
+        torch.cuda.synchronize()
 
     # per-kernel durations: HIP events the library records around each of its launches
     lib.zha_timing_enable(1)
@@ -502,6 +558,18 @@ def main():
         "cpu_baseline": cpu,
         "needles": needles,
         "near_ties": near_ties,
+        "attend_roofline": {"what": "zha_attend (tree prebuilt): search + decode + combine",
+                            "bound": "hbm", "achieved": round(attend_alg / (ms_attend * 1e-3) / 1e9, 1),
+                            "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                            "frac": round(attend_alg / (ms_attend * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                            "alg_bytes": attend_alg, "ms": round(ms_attend, 4),
+                            "flushed_ms": fl_attend["median"] if fl_attend else None,
+                            "flushed_frac": round(attend_alg / (fl_attend["median"] * 1e-3) / 1e9
+                                                  / HBM_PEAK_GBS, 4) if fl_attend else None},
+        "flushed": {"what": "1 GiB written between repetitions, outside the timed region",
+                    "step_ms": fl_step, "attend_ms": fl_attend,
+                    "query_heads_per_s": round(QH / (fl_step["median"] * 1e-3), 1)
+                    if fl_step else None},
         "decode_only": {"ms": round(ms_attend, 4), "eager_ms": round(ms_attend_eager, 4),
                         "query_heads_per_s": round(QH / (ms_attend * 1e-3), 1),
                         "alg_bytes": attend_alg,
@@ -514,6 +582,7 @@ def main():
             "speedup_of_attend": round(ms_dense / ms_attend, 3)},
         "build": {"oneshot_ms": round(ms_build, 4), "appends": n_app,
                   "appends_ms": None if args.no_extras else round(ms_appends, 4),
+                  "one_token_appends": one_tok,
                   "oneshot_in_dense_decodes":
                       None if args.no_extras else round(ms_build / ms_dense, 3)},
         "step_alg_gbs": round(step_alg / (ms_step * 1e-3) / 1e9, 1),
@@ -683,45 +752,95 @@ def pmc_traffic(kernel, workload):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(spec, p, anchor, n_units):
-    """The CPU oracle, as it stands, on a bounded sample: n_units (sequence, KV head) units
-    of the same workload, each running the whole path (pyramid build, descent and exact
-    attention for the unit's query heads). Rate = query heads / oracle seconds."""
-    import numpy as np
+CPU_WORKERS = 16   # host cores a one-GPU machine gives a run
+
+
+def _oracle_worker(args):
+    """One worker of the CPU baseline: regenerate its units' inputs, wait for every other
+    worker, then run the oracle (one BLAS thread) on them, repeating the whole pass until a
+    second has gone by (the small workloads take milliseconds). Returns (start, end, the
+    fragility records of one pass, passes)."""
+    spec, p, anchor, units, barrier = args
     import threadpoolctl
 
     import oracle as O
     import workloads as W
 
     G = spec["Hq"] // spec["Hkv"]
-    units = [(i % spec["B"], i % spec["Hkv"]) for i in range(n_units)]
     Q = W.gen_Q(spec)
     R = W.gen_R(spec)
-    data = {u: W.gen_KV_unit(spec, u[0], u[1], Q) for u in units}
-    info = threadpoolctl.threadpool_info()
-    threads = max([i.get("num_threads", 1) for i in info] or [1])
-    t0 = time.perf_counter()
-    heads = 0
-    results = []
-    for (bb, g) in units:
-        K_u, V_u = data[(bb, g)]
-        levels = O.build_tree_unit(K_u, R[g], spec["b"], spec["L"])
-        for t in range(spec["T"]):
-            for h in range(g * G, (g + 1) * G):
-                results.append(O.attend_head(Q[bb, t, h], levels, K_u, V_u, spec["b"],
-                                             spec["L"], p, anchor))
-                heads += 1
-    sec = time.perf_counter() - t0
-    decisions = sum(len(r.levels) for r in results)
-    fragile = sum(1 for r in results for lv in r.levels if lv.fragile)
+    data = [(u, W.gen_KV_unit(spec, u[0], u[1], Q)) for u in units]
+
+    def one_pass():
+        out = []
+        for (bb, g), (K_u, V_u) in data:
+            levels = O.build_tree_unit(K_u, R[g], spec["b"], spec["L"])
+            for t in range(spec["T"]):
+                for h in range(g * G, (g + 1) * G):
+                    r = O.attend_head(Q[bb, t, h], levels, K_u, V_u, spec["b"], spec["L"], p,
+                                      anchor)
+                    out.append((len(r.levels), sum(1 for lv in r.levels if lv.fragile),
+                                [(bb, t, h, lv.level, kind, float(f"{gap:.3g}"))
+                                 for lv in r.levels for kind, gap in lv.fragile]))
+        return out
+
+    barrier.wait()
+    with threadpoolctl.threadpool_limits(1):
+        t0 = time.perf_counter()
+        first = one_pass()
+        passes = 1
+        while time.perf_counter() - t0 < 1.0:
+            one_pass()
+            passes += 1
+        t1 = time.perf_counter()
+    return t0, t1, first, passes
+
+
+def cpu_baseline(spec, p, anchor, n_units, workers=CPU_WORKERS):
+    """The CPU oracle, as it stands, on a bounded sample: n_units (sequence, KV head) units
+    of the same workload, each running the whole path (pyramid build, descent and exact
+    attention for the unit's query heads). The units are spread over `workers` processes
+    (one BLAS thread each; the oracle itself is unchanged); the rate is query heads over
+    the wall time from the first worker's start to the last worker's end, after every
+    worker has generated its inputs."""
+    import multiprocessing as mp
+
+    all_units = [(bb, g) for bb in range(spec["B"]) for g in range(spec["Hkv"])]
+    units = all_units[:n_units] if n_units > 0 else all_units
+    workers = max(1, min(workers, len(units)))
+    ctx = mp.get_context("spawn")
+    with ctx.Manager() as mgr:
+        barrier = mgr.Barrier(workers)
+        jobs = [(spec, p, anchor, units[i::workers], barrier) for i in range(workers)]
+        with ctx.Pool(workers) as pool:
+            res = pool.map(_oracle_worker, jobs)
+    t0 = min(r[0] for r in res)
+    t1 = max(r[1] for r in res)
+    sec = t1 - t0
+    heads = sum(len(r[2]) * r[3] for r in res)     # query heads attended, every pass
+    passes = min(r[3] for r in res)
+    decisions = sum(x[0] for r in res for x in r[2])
+    fragile = sum(x[1] for r in res for x in r[2])
+    log = [x[2] for r in res for x in r[2]]
+    kinds = {}
+    for head in log:
+        for entry in head:
+            kinds[entry[4]] = kinds.get(entry[4], 0) + 1
     ties = {"decisions": decisions, "fragile_decisions": fragile,
-            "heads_with_any": sum(1 for r in results if r.fragile),
-            "heads": heads, "sample": "the oracle's own decisions on the cpu_baseline units"}
-    return {"value": round(heads / sec, 3), "unit": "query-heads/s", "cores": threads,
+            "heads_with_any": sum(1 for head in log if head), "heads": len(log),
+            "by_kind": kinds,
+            "sample": "the oracle's own decisions on the cpu_baseline units",
+            "log_fields": ["sequence", "t", "h", "level", "kind", "gap"],
+            "log": sorted(e for head in log for e in head)}
+    full = len(units) == len(all_units)
+    return {"value": round(heads / sec, 3), "unit": "query-heads/s", "cores": workers,
             "kind": "oracle",
-            "sample": f"{n_units} (sequence, KV head) units = {heads} query heads of "
+            "sample": f"{len(units)} of {len(all_units)} (sequence, KV head) units"
+                      f"{' (the whole batch)' if full else ''}"
+                      f"{f', {passes}+ passes' if passes > 1 else ''} = {heads} query heads of "
                       f"{spec['name']}, full path per unit (pyramid build + descent + "
-                      f"attention), {sec:.1f}s",
+                      f"attention), {workers} processes with one BLAS thread each, "
+                      f"{sec:.1f}s wall",
             "cpu": cpu_model()}, ties
 
 
