@@ -196,6 +196,25 @@ int zha_attend_causal(const zha_tree* t, const void* Q, int T, int Hq, const int
                       size_t ws_bytes, void* stream);
 
 /*
+ * zha_attend without a workspace argument, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * The workspace is a fixed device array of ZHA_NOALLOC_SCRATCH_BYTES that the library
+ * holds on every GPU it runs on until the process ends; the current device's copy
+ * (hipGetDevice; `stream` must belong to that device) is used. The call allocates nothing.
+ * Every argument, output and rule is that of zha_attend. Errors: ZHA_ERR_CAPACITY when
+ * zha_attend_workspace_bytes(t, T, Hq) exceeds ZHA_NOALLOC_SCRATCH_BYTES (checked on the
+ * host before anything is enqueued; e.g. 256K tokens, 4 sequences, 32/4 heads, d = 128,
+ * b = 4, L = 6 need about 77 MiB and fit, a 1M-token batch of 8 does not). All calls on
+ * one GPU share its scratch: calls that overlap on one GPU (other streams, other host
+ * threads) race and must be serialised by the caller. The scratch needs no clearing; each
+ * call overwrites what it reads.
+ */
+#define ZHA_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+int zha_attend_noalloc(const zha_tree* t, const void* Q, int T, int Hq, const void* K,
+                       const void* V, float p, int anchor, float* O, int32_t* sel_idx,
+                       int64_t cap, int32_t* sel_count, void* stream);
+
+/*
  * Dense comparator: exact softmax attention of every query head over all N cached keys of
  * its KV head, with the same decode and combine kernels zha_attend uses (every member
  * reads every token; there is no tree and no search). It is what the tree-indexed path is

@@ -245,3 +245,19 @@ def test_missing_library_fails_loudly():
                        timeout=300)
     assert r.returncode == 0, r.stderr[-2000:]
     assert "raised" in r.stdout
+
+
+def test_noalloc_rejects_a_workspace_beyond_its_scratch(lib):
+    """zha_attend_noalloc: a shape whose workspace exceeds the fixed device scratch (a 1M-token
+    batch of 8) is rejected on the host with ZHA_ERR_CAPACITY before anything is enqueued."""
+    t = L.ZhaTree()
+    t.B, t.Hkv, t.N, t.N_cap, t.d, t.b, t.L, t.dtype = 8, 4, 1 << 20, 1 << 20, 128, 4, 7, 1
+    t.pyramid = FAKE.value
+    assert lib.zha_attend_workspace_bytes(ctypes.byref(t), 1, 32) > L.ZHA_NOALLOC_SCRATCH_BYTES
+    code = lib.zha_attend_noalloc(ctypes.byref(t), FAKE, 1, 32, FAKE, FAKE, 0.95, 1, FAKE, None,
+                                  1 << 20, FAKE, None)
+    assert code == -4
+    assert b"scratch" in lib.zha_last_error()
+    t.B = 0
+    assert lib.zha_attend_noalloc(ctypes.byref(t), FAKE, 1, 32, FAKE, FAKE, 0.95, 1, FAKE, None,
+                                  1 << 20, FAKE, None) == -2

@@ -21,6 +21,7 @@ from ._lib import (  # noqa: F401
     ZHA_BF16,
     ZHA_F32,
     ZHA_N_REF,
+    ZHA_NOALLOC_SCRATCH_BYTES,
     ZHA_ROUTER_F32,
     ZHA_ROUTER_MXFP4,
     ZhaError,
@@ -29,7 +30,8 @@ from ._lib import (  # noqa: F401
     load,
 )
 
-__all__ = ["Tree", "build_tree", "tree_append", "attend", "workspace_bytes", "level_view",
+__all__ = ["Tree", "build_tree", "tree_append", "attend", "attend_noalloc", "workspace_bytes",
+           "level_view",
            "tree_bytes", "pyramid_level", "router_bytes", "quantize_router", "set_router",
            "router_level", "ZhaError", "load"]
 
@@ -206,6 +208,23 @@ def attend(Q, K, V, tree: Tree, p: float, anchor: int = 1, *, want_lists: bool =
                                     _dev(sel_count, "sel_count"), _dev(workspace, "workspace"),
                                     workspace.numel(), _stream(dev)))
     attend.last_workspace = workspace
+    return out, sel_idx, sel_count
+
+
+def attend_noalloc(Q, K, V, tree: Tree, p: float, anchor: int = 1, *, out, sel_idx,
+                   sel_count):
+    """zha_attend_noalloc: zha_attend with the library's fixed device scratch as its
+    workspace; the caller passes the outputs (O [B,T,Hq,d] float32, sel_idx [B,T,Hq,cap]
+    int32 or None, sel_count [B,T,Hq] int32), so nothing is allocated."""
+    lib = load()
+    B, T, Hq, d = Q.shape
+    if Q.dtype != K.dtype or V.dtype != K.dtype:
+        raise ZhaError(-3, "Q, K and V must share a dtype")
+    cap = sel_idx.shape[-1] if sel_idx is not None else tree.N
+    sel_ptr = _dev(sel_idx, "sel_idx") if sel_idx is not None else None
+    check(lib.zha_attend_noalloc(ctypes.byref(tree.c), _dev(Q, "Q"), T, Hq, _dev(K, "K"),
+                                 _dev(V, "V"), float(p), int(anchor), _dev(out, "O"), sel_ptr,
+                                 cap, _dev(sel_count, "sel_count"), _stream(Q.device)))
     return out, sel_idx, sel_count
 
 

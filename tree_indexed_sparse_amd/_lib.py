@@ -18,6 +18,7 @@ ZHA_MAX_LEVELS = 12
 ZHA_N_REF = 16
 ZHA_F32, ZHA_BF16 = 0, 1
 ZHA_ROUTER_F32, ZHA_ROUTER_MXFP4 = 0, 1
+ZHA_NOALLOC_SCRATCH_BYTES = 128 << 20
 
 STATUS = {
     0: "ZHA_OK",
@@ -38,6 +39,7 @@ EXPORTS = (
     "zha_attend_workspace_bytes",
     "zha_attend",
     "zha_attend_causal",
+    "zha_attend_noalloc",
     "zha_attend_level_view",
     "zha_dense_workspace_bytes",
     "zha_dense_attend",
@@ -110,6 +112,9 @@ def load() -> ctypes.CDLL:
     lib.zha_attend_causal.argtypes = [P(ZhaTree), vp, i32, i32, vp, vp, vp, f32, i32, vp, vp, i64,
                                       vp, vp, sz, vp]
     lib.zha_attend_causal.restype = i32
+    lib.zha_attend_noalloc.argtypes = [P(ZhaTree), vp, i32, i32, vp, vp, f32, i32, vp, vp, i64,
+                                       vp, vp]
+    lib.zha_attend_noalloc.restype = i32
     lib.zha_attend_level_view.argtypes = [P(ZhaTree), i32, i32, i32, P(i64), P(i64), P(i64),
                                           P(i64), P(i64)]
     lib.zha_attend_level_view.restype = i32

@@ -691,6 +691,66 @@ int zha_attend_causal(const zha_tree* t, const void* Q, int T, int Hq, const int
                      workspace, ws_bytes, stream);
 }
 
+}  // extern "C"
+
+// ------------------------------------------------------------- allocation-free attend
+// The workspace of zha_attend_noalloc: a file-scope device array that each GPU holds for
+// the life of the process. Host code never uses the array's name as an address (on the
+// host it is only a stand-in for the symbol); the per-device address comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+namespace {
+static __device__ __align__(256) unsigned char scratch[ZHA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's copy of `scratch`.
+int scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(ZHA_ERR_UNSUPPORTED, "device %d outside the %d devices the scratch serves", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(ZHA_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return ZHA_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int zha_attend_noalloc(const zha_tree* t, const void* Q, int T, int Hq, const void* K,
+                       const void* V, float p, int anchor, float* O, int32_t* sel_idx,
+                       int64_t cap, int32_t* sel_count, void* stream) {
+  int st = check_tree(t);
+  if (st != ZHA_OK) return st;
+  Geom g;
+  st = make_geom(t, T, Hq, &g);
+  if (st != ZHA_OK) return st;
+  if (t->N >= 1) {
+    const int64_t need = layout_of(g).total;
+    if (need > (int64_t)ZHA_NOALLOC_SCRATCH_BYTES)
+      return fail(ZHA_ERR_CAPACITY,
+                  "zha_attend_noalloc: this tree and query shape need %lld bytes of workspace, "
+                  "more than the %lld-byte device scratch; use zha_attend with a workspace",
+                  (long long)need, (long long)ZHA_NOALLOC_SCRATCH_BYTES);
+  }
+  void* ws = nullptr;
+  st = scratch_of_current_device(&ws);
+  if (st != ZHA_OK) return st;
+  return attend_impl(t, Q, T, Hq, nullptr, K, V, p, anchor, O, sel_idx, cap, sel_count, ws,
+                     (size_t)ZHA_NOALLOC_SCRATCH_BYTES, stream);
+}
+
 int zha_timing_enable(int on) {
   std::lock_guard<std::mutex> lk(g_tmu);
   if (on) {
