@@ -16,8 +16,6 @@
 // One level = three launches (score, select, compact). Kernel boundaries order them; no
 // kernel here uses a device-scope fence.
 
-#include <type_traits>
-
 #include "zha_internal.h"
 #include "zha_mxfp4.h"
 
@@ -85,57 +83,10 @@ __device__ __forceinline__ void write_token_run(int32_t* dst, int ntok, const ui
 }
 
 // ------------------------------------------------------------------------------ score
-// S^T[row][member] = X[row] . Q[member] on v_mfma_f32_16x16x4_f32, 16 frontier rows per
-// MFMA block: lane (member = l % 16, group = l / 16) feeds row `member`'s dims
-// 16q + 4 group + e as A and member `member`'s query at the same dims as B, so each
-// lane's 16-byte row loads are contiguous within the row. The C block leaves four
-// consecutive rows of one member per lane, stored as one 16-byte write.
-// Each wave walks its row blocks with the next block's loads in flight while the current
-// one is multiplied; summary rows are read once per call, with non-temporal loads.
-template <int D>
-struct ScoreRows {
-  f32x4_t a[D / 16];
-};
-
-template <int D>
-__device__ __forceinline__ void score_load(ScoreRows<D>& R, const float* __restrict__ Xu,
-                                           const uint32_t* sPn, int p0, int has_parent,
-                                           const FastDiv& bd, int k, int F, int grp) {
-  const bool ok = k < F;
-  const uint32_t kq = bd.div((uint32_t)k);
-  const uint32_t node =
-      ok ? (has_parent ? sPn[kq - p0] * bd.d + ((uint32_t)k - kq * bd.d) : (uint32_t)k) : 0u;
-  const f32x4_t* xr = reinterpret_cast<const f32x4_t*>(Xu + (int64_t)node * D + 4 * grp);
-#pragma unroll
-  for (int q = 0; q < D / 16; ++q)
-    R.a[q] = ok ? __builtin_nontemporal_load(xr + 4 * q) : f32x4_t{0.f, 0.f, 0.f, 0.f};
-}
-
-// qf[q][e] = query dim 16q + e of the row at `qr` (already offset by 4 * group)
-template <int D>
-__device__ __forceinline__ void load_query_fragment(const float* qr, float (&qf)[D / 16][4]) {
-  f32x4_t v[D / 16];
-#pragma unroll
-  for (int q = 0; q < D / 16; ++q) v[q] = *reinterpret_cast<const f32x4_t*>(qr + 16 * q);
-#pragma unroll
-  for (int q = 0; q < D / 16; ++q)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) qf[q][e] = v[q][e];
-}
-template <int D>
-__device__ __forceinline__ void load_query_fragment(const bf16_t* qr, float (&qf)[D / 16][4]) {
-  typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
-  u32x2_t v[D / 16];
-#pragma unroll
-  for (int q = 0; q < D / 16; ++q) v[q] = *reinterpret_cast<const u32x2_t*>(qr + 16 * q);
-#pragma unroll
-  for (int q = 0; q < D / 16; ++q) {
-    qf[q][0] = __uint_as_float(v[q].x << 16);
-    qf[q][1] = __uint_as_float(v[q].x & 0xffff0000u);
-    qf[q][2] = __uint_as_float(v[q].y << 16);
-    qf[q][3] = __uint_as_float(v[q].y & 0xffff0000u);
-  }
-}
+// Scores of a level's union frontier for every member of a unit: sigma * q . X per row,
+// each row read once per call. The float32 router's rows are scored on the vector units
+// (score_rows_kernel, below); the FP4 router's MXFP4 rows on the scaled FP4 MFMA
+// (score_fp4_kernel).
 
 // ---- FP4 router: the query and the summary rows as MXFP4 operands of
 // v_mfma_scale_f32_16x16x128_f8f6f4 (both in E2M1). Lane l (row or query column l % 16,
@@ -210,13 +161,17 @@ __device__ __forceinline__ f32x4_t fp4_mfma(const Fp4Rows& R, uint4 qc, uint32_t
   return d;
 }
 
-template <int D, typename Tq, bool FP4>
-__global__ __launch_bounds__(kScoreThreads) void score_kernel(
-    Geom geo, const float* __restrict__ X, int64_t X_unit_stride, const Tq* __restrict__ Q,
+// S^T[row][member] on v_mfma_scale_f32_16x16x128_f8f6f4, 16 frontier rows per MFMA block:
+// lane (row or member l % 16, 32-element block l / 16) holds that block's codes and scale;
+// the C block leaves four consecutive rows of one member per lane, stored as one 16-byte
+// write. Each wave walks its row blocks with the next block's loads in flight while the
+// current one is multiplied.
+template <int D, typename Tq>
+__global__ __launch_bounds__(kScoreThreads) void score_fp4_kernel(
+    Geom geo, const Tq* __restrict__ Q,
     LevelBufs parent, int has_parent, int n_top, float* __restrict__ S, int64_t S_stride,
     float sigma, int ent, float* __restrict__ pmax, float* __restrict__ pmin, int64_t pstride,
     const uint8_t* __restrict__ RC, const uint8_t* __restrict__ RS, int64_t rows_cap) {
-  constexpr int NQ = D / 16;
   constexpr int kMaxParents = kScoreEntries / 2 + 2;
   const int kPerWave = ent / (kScoreThreads / 64);
   __shared__ uint32_t sPn[kMaxParents];
@@ -242,26 +197,14 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
       sPm[i] = mk;
     }
   }
-  // query fragment: unconditional vector loads from a valid row, zeroed past the members
-  float qf[NQ][4];
+  // query operand: this lane's MXFP4 block of its member's query (zero past the members)
   uint4 qc = make_uint4(0u, 0u, 0u, 0u);
   uint32_t qs = 127u;
-  if constexpr (FP4) {
-    fp4_query_operand<D, Tq>(Q + (int64_t)qh_of(geo, u, mem < Mu ? mem : 0) * D, grp, mem < Mu,
-                             &qc, &qs);
-  } else {
-    load_query_fragment<D>(Q + (int64_t)qh_of(geo, u, mem < Mu ? mem : 0) * D + 4 * grp, qf);
-    if (mem >= Mu) {
-#pragma unroll
-      for (int q = 0; q < NQ; ++q)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) qf[q][e] = 0.f;
-    }
-  }
+  fp4_query_operand<D, Tq>(Q + (int64_t)qh_of(geo, u, mem < Mu ? mem : 0) * D, grp, mem < Mu,
+                           &qc, &qs);
   __syncthreads();
-  const float* Xu = X + (int64_t)bg_of(geo, u) * X_unit_stride;
-  const uint8_t* RCu = FP4 ? RC + (int64_t)bg_of(geo, u) * rows_cap * (D / 2) : nullptr;
-  const uint8_t* RSu = FP4 ? RS + (int64_t)bg_of(geo, u) * rows_cap * (D / kMxBlock) : nullptr;
+  const uint8_t* RCu = RC + (int64_t)bg_of(geo, u) * rows_cap * (D / 2);
+  const uint8_t* RSu = RS + (int64_t)bg_of(geo, u) * rows_cap * (D / kMxBlock);
   float* Srow = S + (int64_t)qh_of(geo, u, mem < Mu ? mem : 0) * S_stride;
   const int k_wave = k_wg + wave * kPerWave;
   const int nrb = k_wave < F ? min(kPerWave / 16, (F - k_wave + 15) / 16) : 0;
@@ -269,34 +212,18 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
   // at the top level a member's frontier is the top nodes complete for it
   const int f_mem = has_parent ? F : (mem < Mu ? min(F, head_ntop(geo, qh_of(geo, u, mem))) : 0);
 
-  using Rows = typename std::conditional<FP4, Fp4Rows, ScoreRows<D>>::type;
-  auto load_rows = [&](Rows& R, int k) {
-    if constexpr (FP4) {
-      const bool ok = k < F;
-      const uint32_t kq = geo.bdiv.div((uint32_t)k);
-      const uint32_t node =
-          ok ? (has_parent ? sPn[kq - p0] * geo.bdiv.d + ((uint32_t)k - kq * geo.bdiv.d)
-                           : (uint32_t)k)
-             : 0u;
-      fp4_row_operand<D>(RCu, RSu, node, grp, R);
-    } else {
-      score_load<D>(R, Xu, sPn, p0, has_parent, geo.bdiv, k, F, grp);
-    }
+  auto load_rows = [&](Fp4Rows& R, int k) {
+    const bool ok = k < F;
+    const uint32_t kq = geo.bdiv.div((uint32_t)k);
+    const uint32_t node =
+        ok ? (has_parent ? sPn[kq - p0] * geo.bdiv.d + ((uint32_t)k - kq * geo.bdiv.d)
+                         : (uint32_t)k)
+           : 0u;
+    fp4_row_operand<D>(RCu, RSu, node, grp, R);
   };
 
-  auto compute = [&](const Rows& R, int rb) {
-    f32x4_t c = {0.f, 0.f, 0.f, 0.f};
-    if constexpr (FP4) {
-      c = fp4_mfma(R, qc, qs, c);
-    } else {
-#pragma unroll
-      for (int q = 0; q < NQ; ++q) {
-        c = __builtin_amdgcn_mfma_f32_16x16x4f32(R.a[q].x, qf[q][0], c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x4f32(R.a[q].y, qf[q][1], c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x4f32(R.a[q].z, qf[q][2], c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x4f32(R.a[q].w, qf[q][3], c, 0, 0, 0);
-      }
-    }
+  auto compute = [&](const Fp4Rows& R, int rb) {
+    const f32x4_t c = fp4_mfma(R, qc, qs, f32x4_t{0.f, 0.f, 0.f, 0.f});
     // rows kb..kb+3 of member `mem`; + 0.0f turns a -0 score into +0 so float and bit
     // orders agree
     const int kb = k_wave + 16 * rb + 4 * grp;
@@ -326,7 +253,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
     }
   };
 
-  Rows A, Bv;
+  Fp4Rows A, Bv;
   if (nrb > 0) load_rows(A, k_wave + mem);
   for (int rb = 0; rb < nrb; rb += 2) {
     if (rb + 1 < nrb) load_rows(Bv, k_wave + 16 * (rb + 1) + mem);
@@ -357,6 +284,235 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
       const int64_t at = (int64_t)qh_of(geo, u, threadIdx.x) * pstride + blockIdx.x;
       pmax[at] = mx;
       pmin[at] = mn;
+    }
+  }
+}
+
+// ---- float32 rows, coalesced: the scoring of the float32 router. A row of D floats is
+// split over LPR lanes, each taking DPL = D / LPR dims as DPL / 4 16-byte loads placed
+// 16 LPR bytes apart, so every load instruction reads RPI = 64 / LPR rows, each over
+// 16 LPR contiguous bytes (whole cache lines). Each lane forms its dims' partial dot
+// product with every member's query; a butterfly over the row's lanes then halves the
+// member set at each exchange (the lane whose exchange bit is set keeps the upper half,
+// its partner the lower, each adding the other's copy of the half it keeps), so after
+// log2(M) exchanges a lane holds one member's sum over its lane group and the remaining
+// exchanges complete it: lane sub = l % LPR ends with member sub / (LPR / M). Exchanges
+// within 16 lanes are DPP moves (partners by quad permutation or by mirroring within 8 or
+// 16 lanes: any pairing across the split works, since each step sums disjoint pairs).
+// The four waves of a workgroup take its rows in turn, 16 at a time, so the workgroup
+// reads one contiguous stream. Scores stay in LDS until the last row is loaded and then
+// leave as 16-byte stores per member: a store issued while row loads are in flight would
+// make the compiler wait for every outstanding load before the next use of one (it cannot
+// order loads and stores on the one counter). Two groups of row loads are in flight per
+// wave; rows are read once per call (non-temporal loads).
+constexpr int kRowEntries = 1024;            // most frontier entries per workgroup
+constexpr int kRowGroup = 16;                // rows per load group
+
+__device__ __forceinline__ void load_q4(const float* q, float* o) {
+  const float4 v = *reinterpret_cast<const float4*>(q);
+  o[0] = v.x;
+  o[1] = v.y;
+  o[2] = v.z;
+  o[3] = v.w;
+}
+__device__ __forceinline__ void load_q4(const bf16_t* q, float* o) {
+  const uint2 v = *reinterpret_cast<const uint2*>(q);
+  o[0] = __uint_as_float(v.x << 16);
+  o[1] = __uint_as_float(v.x & 0xffff0000u);
+  o[2] = __uint_as_float(v.y << 16);
+  o[3] = __uint_as_float(v.y & 0xffff0000u);
+}
+
+// the value of this lane's partner across lane bit log2(DIST)
+template <int DIST>
+__device__ __forceinline__ float lane_xchg(float v) {
+  const int x = __float_as_int(v);
+  if constexpr (DIST == 1) return __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false));
+  else if constexpr (DIST == 2) return __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false));
+  else if constexpr (DIST == 4) return __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0x141, 0xF, 0xF, false));
+  else if constexpr (DIST == 8) return __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0x140, 0xF, 0xF, false));
+  else return __shfl_xor(v, DIST, 64);
+}
+
+// halving exchanges over lane bits log2(DIST), log2(DIST / 2), ... while C values remain
+template <int C, int DIST>
+struct MemberHalve {
+  static __device__ __forceinline__ void run(float* v, int lane) {
+    if constexpr (C > 1) {
+      const bool hi = (lane & DIST) != 0;
+#pragma unroll
+      for (int t = 0; t < C / 2; ++t) {
+        const float send = hi ? v[t] : v[t + C / 2];
+        const float keep = hi ? v[t + C / 2] : v[t];
+        v[t] = keep + lane_xchg<DIST>(send);
+      }
+      MemberHalve<C / 2, DIST / 2>::run(v, lane);
+    } else if constexpr (DIST >= 1) {
+      v[0] += lane_xchg<DIST>(v[0]);
+      MemberHalve<1, DIST / 2>::run(v, lane);
+    }
+  }
+};
+
+template <int D, typename Tq, int M, int LPR>
+__global__ __launch_bounds__(kScoreThreads) void score_rows_kernel(
+    Geom geo, const float* __restrict__ X, int64_t X_unit_stride, const Tq* __restrict__ Q,
+    LevelBufs parent, int has_parent, int n_top, float* __restrict__ S, int64_t S_stride,
+    float sigma, int ent, float* __restrict__ pmax, float* __restrict__ pmin, int64_t pstride) {
+  constexpr int DPL = D / LPR;                // dims per lane
+  constexpr int NLD = DPL / 4;                // 16-byte loads per lane per row
+  constexpr int RPI = 64 / LPR;               // rows per load instruction
+  constexpr int RL = LPR / M;                 // lanes per member once reduced
+  static_assert(M <= LPR && (M & (M - 1)) == 0, "M: a power of two up to the lanes of a row");
+  static_assert(NLD >= 1 && NLD * 4 * LPR == D, "whole 16-byte loads per lane");
+  constexpr int NW = kScoreThreads / 64;
+  constexpr int IPG = kRowGroup / RPI;        // row slots per lane per load group
+  constexpr int kMaxParents = kRowEntries / 2 + 2;
+  static_assert(M % NW == 0, "members spread evenly over the waves for the stores");
+  __shared__ uint32_t sPn[kMaxParents];
+  __shared__ uint32_t sPm[kMaxParents];
+  __shared__ float sS[M][kRowEntries];
+
+  const int u = blockIdx.y;
+  const int F = has_parent ? geo.b * (int)parent.count[u] : n_top;
+  const int k_wg = blockIdx.x * ent;
+  if (k_wg >= F) return;
+  const int k_end = min(k_wg + ent, F);
+  const int Mu = members_of(geo, u);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int sub = lane % LPR, rin = lane / LPR;
+  const int p0 = (int)geo.bdiv.div((uint32_t)k_wg);
+  if (has_parent) {
+    const int np = (int)geo.bdiv.div((uint32_t)(k_end - 1)) - p0 + 1;
+    for (int i = threadIdx.x; i < np; i += kScoreThreads) {
+      sPn[i] = parent.nodes[u * parent.stride + p0 + i];
+      sPm[i] = parent.masks[u * parent.stride + p0 + i];
+    }
+  }
+  // this lane's dims of every member's query, zero past the unit's members
+  float qv[M][DPL];
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    const Tq* qr = Q + (int64_t)qh_of(geo, u, m < Mu ? m : 0) * D + 4 * sub;
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) load_q4(qr + 4 * LPR * j, &qv[m][4 * j]);
+  }
+#pragma unroll
+  for (int m = 0; m < M; ++m)
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) qv[m][e] = m < Mu ? qv[m][e] : 0.f;
+  __syncthreads();
+  const float* Xu = X + (int64_t)bg_of(geo, u) * X_unit_stride + 4 * sub;
+  // the workgroup's rows in groups of kRowGroup, taken by the waves in turn, so the four
+  // waves read one contiguous stream
+  const int groups_wg = (k_end - k_wg + kRowGroup - 1) / kRowGroup;
+  const int n_groups = groups_wg > wave ? (groups_wg - wave + NW - 1) / NW : 0;
+
+  // Every group's loads are issued unconditionally (rows past the range read its last row
+  // again, a line already in cache): a branch around a load would make the compiler wait
+  // for all outstanding loads where the paths join.
+  typedef f32x4_t Group[IPG][NLD];
+  auto load_group = [&](Group& x, int g) {
+    uint32_t node[IPG];
+#pragma unroll
+    for (int i = 0; i < IPG; ++i) {
+      const uint32_t kc =
+          (uint32_t)min(k_wg + (g * NW + wave) * kRowGroup + i * RPI + rin, k_end - 1);
+      const uint32_t q = geo.bdiv.div(kc);
+      const uint32_t pn = sPn[has_parent ? q - p0 : 0];
+      node[i] = has_parent ? pn * geo.bdiv.d + (kc - q * geo.bdiv.d) : kc;
+    }
+#pragma unroll
+    for (int i = 0; i < IPG; ++i)
+#pragma unroll
+      for (int j = 0; j < NLD; ++j)
+        x[i][j] = __builtin_nontemporal_load(
+            reinterpret_cast<const f32x4_t*>(Xu + (int64_t)node[i] * D + 4 * LPR * j));
+  };
+
+  auto compute_group = [&](const Group& x, int g) {
+    const int r0 = (g * NW + wave) * kRowGroup;  // row of the workgroup's range
+#pragma unroll
+    for (int i = 0; i < IPG; ++i) {
+      float v[M];
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        float a = x[i][0].x * qv[m][0];
+        a = fmaf(x[i][0].y, qv[m][1], a);
+        a = fmaf(x[i][0].z, qv[m][2], a);
+        a = fmaf(x[i][0].w, qv[m][3], a);
+#pragma unroll
+        for (int j = 1; j < NLD; ++j) {
+          a = fmaf(x[i][j].x, qv[m][4 * j], a);
+          a = fmaf(x[i][j].y, qv[m][4 * j + 1], a);
+          a = fmaf(x[i][j].z, qv[m][4 * j + 2], a);
+          a = fmaf(x[i][j].w, qv[m][4 * j + 3], a);
+        }
+        v[m] = a;
+      }
+      MemberHalve<M, LPR / 2>::run(v, lane);
+      // + 0.0f turns a -0 score into +0 so float and bit orders agree
+      if (sub % RL == 0) sS[sub / RL][r0 + i * RPI + rin] = sigma * v[0] + 0.0f;
+    }
+  };
+
+  if (n_groups > 0) {
+    Group xa, xb;
+    load_group(xa, 0);
+    for (int g = 0; g < n_groups; g += 2) {
+      load_group(xb, g + 1);
+      compute_group(xa, g);
+      load_group(xa, g + 2);
+      if (g + 1 < n_groups) compute_group(xb, g + 1);
+    }
+  }
+  __syncthreads();
+
+  // scores out, after the last row load: wave w stores members w, w + NW, ..., each as one
+  // contiguous run of 16-byte stores, and reduces its max and min over the member's
+  // frontier entries for the chunked selection
+  const int n = k_end - k_wg;
+#pragma unroll
+  for (int mi = 0; mi < M / NW; ++mi) {
+    const int mm = wave + NW * mi;
+    if (mm >= Mu) break;
+    float* dst = S + (int64_t)qh_of(geo, u, mm) * S_stride + k_wg;
+    const int f_mem = has_parent ? F : min(F, head_ntop(geo, qh_of(geo, u, mm)));
+    float mx = -INFINITY, mn = INFINITY;
+    for (int c = 4 * lane; c < n; c += 256) {
+      const float4 o = *reinterpret_cast<const float4*>(&sS[mm][c]);
+      if (c + 3 < n) {
+        *reinterpret_cast<float4*>(dst + c) = o;
+      } else {
+        dst[c] = o.x;
+        if (c + 1 < n) dst[c + 1] = o.y;
+        if (c + 2 < n) dst[c + 2] = o.z;
+      }
+      if (pmax) {
+        const float ov[4] = {o.x, o.y, o.z, o.w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int kk = k_wg + c + r;
+          const bool in = c + r < n && kk < f_mem &&
+                          (!has_parent || ((sPm[geo.bdiv.div((uint32_t)kk) - p0] >> mm) & 1u));
+          if (in) {
+            mx = fmaxf(mx, ov[r]);
+            mn = fminf(mn, ov[r]);
+          }
+        }
+      }
+    }
+    if (pmax) {
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+        mn = fminf(mn, __shfl_xor(mn, off, 64));
+      }
+      if (lane == 0) {
+        const int64_t at = (int64_t)qh_of(geo, u, mm) * pstride + blockIdx.x;
+        pmax[at] = mx;
+        pmin[at] = mn;
+      }
     }
   }
 }
@@ -2263,6 +2419,7 @@ hipError_t launch_score(const Geom& geo, const float* X, int64_t X_unit_stride, 
                         const uint8_t* rscales, int64_t rows_cap, hipStream_t s) {
   const int cap_entries = parent ? (int)(geo.b * parent->stride) : n_top;
   const int ent = score_entries(cap_entries, geo.U);
+  if (!rcodes && ent > kRowEntries) return hipErrorInvalidValue;
   dim3 grid((cap_entries + ent - 1) / ent, geo.U);
   const float sigma = 1.0f / sqrtf((float)geo.D);
   LevelBufs par = parent ? *parent : LevelBufs{};
@@ -2270,13 +2427,21 @@ hipError_t launch_score(const Geom& geo, const float* X, int64_t X_unit_stride, 
   float* pmax = wide ? wide->pmax : nullptr;
   float* pmin = wide ? wide->pmin : nullptr;
   const int64_t pstride = wide ? wide->pstride : 0;
-#define ZHA_SCORE(DD, TQ, F4)                                                                 \
-  hipLaunchKernelGGL((score_kernel<DD, TQ, F4>), grid, dim3(kScoreThreads), 0, s, geo, X,      \
-                     X_unit_stride, (const TQ*)Q, par, hp, n_top, S, S_stride, sigma, ent,     \
-                     pmax, pmin, pstride, rcodes, rscales, rows_cap)
-#define ZHA_SCORE_D(DD, TQ)          \
-  if (rcodes) ZHA_SCORE(DD, TQ, true); \
-  else ZHA_SCORE(DD, TQ, false)
+#define ZHA_SCORE_FP4(DD, TQ)                                                           \
+  hipLaunchKernelGGL((score_fp4_kernel<DD, TQ>), grid, dim3(kScoreThreads), 0, s, geo,       \
+                     (const TQ*)Q, par, hp, n_top, S, S_stride, sigma, ent, pmax, pmin,        \
+                     pstride, rcodes, rscales, rows_cap)
+#define ZHA_ROWS(DD, TQ, MM, LL)                                                        \
+  hipLaunchKernelGGL((score_rows_kernel<DD, TQ, MM, LL>), grid, dim3(kScoreThreads), 0, s, geo, \
+                     X, X_unit_stride, (const TQ*)Q, par, hp, n_top, S, S_stride, sigma, ent,  \
+                     pmax, pmin, pstride)
+  // the float32 router scores with coalesced whole-row loads; the member count rounds up
+  // to 8 or 16, and a lane holds 8 dims of every member's query when that fits (64 values)
+  const bool m16 = geo.Tb * geo.G > 8;
+#define ZHA_SCORE_D(DD, TQ)                                       \
+  if (rcodes) ZHA_SCORE_FP4(DD, TQ);                              \
+  else if (m16) ZHA_ROWS(DD, TQ, 16, (DD) / 4);                   \
+  else ZHA_ROWS(DD, TQ, 8, (DD) / 8)
   if (geo.D == 64) {
     if (dtype == ZHA_BF16) { ZHA_SCORE_D(64, bf16_t); }
     else { ZHA_SCORE_D(64, float); }
@@ -2285,7 +2450,8 @@ hipError_t launch_score(const Geom& geo, const float* X, int64_t X_unit_stride, 
     else { ZHA_SCORE_D(128, float); }
   }
 #undef ZHA_SCORE_D
-#undef ZHA_SCORE
+#undef ZHA_ROWS
+#undef ZHA_SCORE_FP4
   return hipGetLastError();
 }
 
