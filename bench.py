@@ -48,6 +48,9 @@ def parse():
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the dense comparator and the append-build timings (profiling "
                          "runs: every decode dispatch is then the tree-indexed attend's)")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="only copy a 2 GiB device buffer 5 times (the known-size kernel that "
+                         "rocprofv3 HBM counters are scaled by) and print its bandwidth")
     ap.add_argument("--no-graph", action="store_true",
                     help="time eager launches only (by default the step is also captured as a "
                          "HIP graph and its replays are the headline timing)")
@@ -75,6 +78,13 @@ def kernel_sources_sha(kernel=None) -> str:
 
 def main():
     args = parse()
+    if args.calibrate and args.gpus == 1:
+        import torch
+        dev = torch.device("cuda:0")
+        print(json.dumps({"copy_bytes_read": 1 << 31, "copy_bytes_written": 1 << 31,
+                          "copies": 5, "copy_gbs": copy_probe(torch, dev, reps=5, warm=0)}),
+              flush=True)
+        return
     if args.sweep and args.gpus == 1:
         return sweep(args)
     if args.gpus != 1:
@@ -718,18 +728,17 @@ def tree_bytes_written(B, Hkv, N, d, b, L):
     return sum(B * Hkv * (N // b ** lv) * d * 4 for lv in range(1, L + 1))
 
 
-def copy_probe(torch, dev):
+def copy_probe(torch, dev, reps=5, warm=2):
     """Device-to-device copy bandwidth (read + write bytes / time) of a 2 GiB buffer."""
     n = 1 << 29
     a = torch.empty(n, dtype=torch.float32, device=dev)
     c = torch.empty_like(a)
     a.fill_(1.0)
-    for _ in range(2):
+    for _ in range(warm):
         c.copy_(a)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
-    reps = 5
     for _ in range(reps):
         c.copy_(a)
     e1.record()

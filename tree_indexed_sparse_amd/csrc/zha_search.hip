@@ -2405,12 +2405,12 @@ __global__ __launch_bounds__(kCompactThreads) void compact_kernel(
 
 }  // namespace
 
-// Frontier entries per score workgroup (a multiple of 64: 16-row blocks over four waves).
-// Measured at 256K: 1024 / 512 / 256 by frontier size streams as fast as any other
-// choice tried (one-round sizing from the CU count was slower).
+// Frontier entries per score workgroup (a multiple of 64: 16-row groups over four waves).
+// Measured at 256K deep: 1024 for the level-1 frontiers (64K entries per unit; 512 and
+// 2048 were slower), 256 below (the 16K-entry level: 30 us against 35 us with 512).
 int score_entries(int64_t cap_entries, int units) {
   (void)units;
-  return cap_entries >= 65536 ? 1024 : (cap_entries >= 8192 ? 512 : 256);
+  return cap_entries >= 65536 ? 1024 : 256;
 }
 
 hipError_t launch_score(const Geom& geo, const float* X, int64_t X_unit_stride, const void* Q,
@@ -2436,11 +2436,14 @@ hipError_t launch_score(const Geom& geo, const float* X, int64_t X_unit_stride, 
                      X, X_unit_stride, (const TQ*)Q, par, hp, n_top, S, S_stride, sigma, ent,  \
                      pmax, pmin, pstride)
   // the float32 router scores with coalesced whole-row loads; the member count rounds up
-  // to 8 or 16, and a lane holds 8 dims of every member's query when that fits (64 values)
+  // to 8 or 16. Rows are split over 16 lanes (8 at d = 64 with 8 members), so every
+  // exchange of the member butterfly is a DPP move within 16 lanes (with 32 lanes per row
+  // the first exchange crosses rows through LDS: 0.84 against 0.59 ms for 16 members at
+  // 256K)
   const bool m16 = geo.Tb * geo.G > 8;
 #define ZHA_SCORE_D(DD, TQ)                                       \
   if (rcodes) ZHA_SCORE_FP4(DD, TQ);                              \
-  else if (m16) ZHA_ROWS(DD, TQ, 16, (DD) / 4);                   \
+  else if (m16) ZHA_ROWS(DD, TQ, 16, 16);                         \
   else ZHA_ROWS(DD, TQ, 8, (DD) / 8)
   if (geo.D == 64) {
     if (dtype == ZHA_BF16) { ZHA_SCORE_D(64, bf16_t); }
