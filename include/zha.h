@@ -238,17 +238,30 @@ int zha_dense_attend_causal(const void* Q, int T, int Hq, const int32_t* positio
 /*
  * Diagnostics of the last zha_attend that used `workspace` (valid once it completed).
  * The G = Hq / Hkv heads of one KV head (and up to 16 / G queries of one sequence) form a
- * "unit" that shares one union list per level: unit u = ((b * Hkv + g) * nTB + tb), with
- * Tb = min(T, 16 / G) queries per unit, nTB = ceil(T / Tb); member m = (t % Tb) * G + h % G.
- * For level l in 1..L this reports byte offsets into the workspace of:
- *   nodes  uint32 [U][stride]: ascending ids of the level-l nodes kept by any member
+ * "unit" that shares one union frontier per level: unit u = ((b * Hkv + g) * nTB + tb),
+ * with Tb = min(T, 16 / G) queries per unit, nTB = ceil(T / Tb); member
+ * m = (t % Tb) * G + h % G. Level 1 (the list the decode reads) is kept as a union list;
+ * this reports byte offsets into the workspace of:
+ *   nodes  uint32 [U][stride]: ascending ids of the level-1 nodes kept by any member
  *   masks  uint32 [U][stride]: bit m set when member m kept that node
  *   count  uint32 [U]:         number of valid entries per unit
- * and the number of units U and members per unit bound Tb * G through *units / *stride.
+ * and the number of units U through *units. level must be 1 (ZHA_ERR_INVALID_ARG
+ * otherwise).
  */
 int zha_attend_level_view(const zha_tree* t, int T, int Hq, int level, int64_t* off_nodes,
                           int64_t* off_masks, int64_t* off_count, int64_t* stride,
                           int64_t* units);
+
+/*
+ * The nodes each query head kept at level `level` in 2..L, as bits by node id: row qh
+ * (qh = (b * T + t) * Hq + h) is *words uint32 words starting at byte offset
+ * *off_bits + 4 * qh * *words of the workspace; bit j of the row (word j / 32, bit j % 32)
+ * is set when head qh kept node j. Nodes 0 .. *nodes - 1 (those under the complete top
+ * nodes; none when the cache holds no complete top node) are valid. Same validity as
+ * zha_attend_level_view.
+ */
+int zha_attend_level_bits(const zha_tree* t, int T, int Hq, int level, int64_t* off_bits,
+                          int64_t* words, int64_t* nodes);
 
 /*
  * Per-launch timing (for benchmarks and profiling). While enabled, every kernel this

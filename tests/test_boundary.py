@@ -129,15 +129,35 @@ def test_level_view_offsets_are_inside_the_workspace(lib):
     t = _tree()
     need = lib.zha_attend_workspace_bytes(ctypes.byref(t), 3, 8)
     vals = [ctypes.c_int64() for _ in range(5)]
-    for level in (1, 2, 3):
+    assert lib.zha_attend_level_view(ctypes.byref(t), 3, 8, 1,
+                                     *[ctypes.byref(v) for v in vals]) == 0
+    o_n, o_m, o_c, stride, units = (v.value for v in vals)
+    assert stride == 4096 // 4
+    assert units == 1 * 2 * 1           # Tb = min(3, 16 / 4) = 3 queries per unit
+    assert max(o_n, o_m) + 4 * units * stride <= need and o_c + 4 * units <= need
+    for level in (2, 3, 4):               # only level 1 keeps a union list
         assert lib.zha_attend_level_view(ctypes.byref(t), 3, 8, level,
+                                         *[ctypes.byref(v) for v in vals]) == -1
+
+
+def test_level_bits_offsets_are_inside_the_workspace(lib):
+    """Levels 2..L: every head's row of kept bits lies inside the workspace (the tree is
+    b = 4, L = 3 over 4096 tokens: 64 top nodes, so 256 level-2 nodes)."""
+    t = _tree()
+    QH = 1 * 3 * 8
+    need = lib.zha_attend_workspace_bytes(ctypes.byref(t), 3, 8)
+    vals = [ctypes.c_int64() for _ in range(3)]
+    for level in (2, 3):
+        assert lib.zha_attend_level_bits(ctypes.byref(t), 3, 8, level,
                                          *[ctypes.byref(v) for v in vals]) == 0
-        o_n, o_m, o_c, stride, units = (v.value for v in vals)
-        assert stride == 4096 // 4 ** level
-        assert units == 1 * 2 * 1           # Tb = min(3, 16 / 4) = 3 queries per unit
-        assert max(o_n, o_m) + 4 * units * stride <= need and o_c + 4 * units <= need
-    assert lib.zha_attend_level_view(ctypes.byref(t), 3, 8, 4,
-                                     *[ctypes.byref(v) for v in vals]) == -1
+        off, words, nodes = (v.value for v in vals)
+        assert nodes == 4096 // 4 ** level
+        assert 32 * words >= nodes
+        last = off + 4 * ((QH - 1) * words + (nodes + 31) // 32)  # end of the last row's bits
+        assert off % 4 == 0 and last <= need
+    for level in (0, 1, 4):
+        assert lib.zha_attend_level_bits(ctypes.byref(t), 3, 8, level,
+                                         *[ctypes.byref(v) for v in vals]) == -1
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -261,3 +281,39 @@ def test_noalloc_rejects_a_workspace_beyond_its_scratch(lib):
     t.B = 0
     assert lib.zha_attend_noalloc(ctypes.byref(t), FAKE, 1, 32, FAKE, FAKE, 0.95, 1, FAKE, None,
                                   1 << 20, FAKE, None) == -2
+
+
+def test_level_view_assembles_unit_masks_from_head_bits(lib):
+    """The diagnostic reader of levels >= 2 (tree_indexed_sparse_amd.level_view) on a host
+    workspace whose rows of kept bits are filled by hand: the fused levels' rows end at the
+    workspace's last byte, and the unit masks must be the members' bits, member m at bit m."""
+    import numpy as np
+    import torch
+    import tree_indexed_sparse_amd as Z
+
+    t = _tree(Hkv=1)
+    T, Hq = 8, 1                          # one unit of 8 queries
+    need = lib.zha_attend_workspace_bytes(ctypes.byref(t), T, Hq)
+    ws = torch.zeros(need, dtype=torch.uint8)
+    words = ws.view(torch.int32)
+    vals = [ctypes.c_int64() for _ in range(3)]
+    rng = np.random.default_rng(5)
+
+    class _T:
+        c = t
+
+    for level in (2, 3):
+        assert lib.zha_attend_level_bits(ctypes.byref(t), T, Hq, level,
+                                         *[ctypes.byref(v) for v in vals]) == 0
+        off, W, n = (v.value for v in vals)
+        truth = rng.random((T, n)) < 0.05
+        for qh in range(T):
+            for j in np.nonzero(truth[qh])[0]:
+                bit = 1 << (int(j) % 32)
+                words[off // 4 + qh * W + int(j) // 32] |= bit if bit < 2 ** 31 else -2 ** 31
+        nodes, masks, count = Z.level_view(_T(), T, Hq, level, ws)
+        union = np.nonzero(truth.any(0))[0]
+        assert count[0] == union.size
+        assert (nodes[0, :union.size] == union).all()
+        want = [sum(int(truth[m, j]) << m for m in range(T)) for j in union]
+        assert list(masks[0, :union.size]) == want

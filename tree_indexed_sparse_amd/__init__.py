@@ -267,20 +267,54 @@ def dense_attend(Q, K, V, N: int | None = None, *, out=None, workspace=None, pos
 
 
 def level_view(tree: Tree, T: int, Hq: int, level: int, workspace: torch.Tensor):
-    """Per-level union lists a finished zha_attend left in `workspace`:
-    (nodes [U, stride] int64, masks [U, stride] int64, count [U] int64) on the host."""
+    """Per-level union lists a finished zha_attend left in `workspace`, on the host:
+    (nodes [U, stride] int64, masks [U, stride] int64, count [U] int64) with bit m of a
+    mask set when member m of the unit kept the node. Level 1 is read as the library keeps
+    it (zha_attend_level_view); the levels above are assembled here from the heads' kept
+    bits (zha_attend_level_bits), a diagnostic view of what the search kept."""
+    import numpy as np
+
     lib = load()
-    o_n, o_m, o_c, st, units = (ctypes.c_int64() for _ in range(5))
-    check(lib.zha_attend_level_view(ctypes.byref(tree.c), T, Hq, level, ctypes.byref(o_n),
-                                    ctypes.byref(o_m), ctypes.byref(o_c), ctypes.byref(st),
-                                    ctypes.byref(units)))
-    U, S = units.value, st.value
     w = workspace.view(torch.uint8)
 
     def u32(off, n):
         return w[off:off + 4 * n].view(torch.int32).cpu().numpy().astype("int64") & 0xFFFFFFFF
 
-    nodes = u32(o_n.value, U * S).reshape(U, S)
-    masks = u32(o_m.value, U * S).reshape(U, S)
-    count = u32(o_c.value, U)
-    return nodes, masks, count
+    if level == 1:
+        o_n, o_m, o_c, st, units = (ctypes.c_int64() for _ in range(5))
+        check(lib.zha_attend_level_view(ctypes.byref(tree.c), T, Hq, level, ctypes.byref(o_n),
+                                        ctypes.byref(o_m), ctypes.byref(o_c), ctypes.byref(st),
+                                        ctypes.byref(units)))
+        U, S = units.value, st.value
+        return (u32(o_n.value, U * S).reshape(U, S), u32(o_m.value, U * S).reshape(U, S),
+                u32(o_c.value, U))
+    o_b, words, nodes = (ctypes.c_int64() for _ in range(3))
+    check(lib.zha_attend_level_bits(ctypes.byref(tree.c), T, Hq, level, ctypes.byref(o_b),
+                                    ctypes.byref(words), ctypes.byref(nodes)))
+    B, Hkv = int(tree.c.B), int(tree.c.Hkv)
+    QH, n, W = B * T * Hq, nodes.value, words.value
+    nw = (n + 31) // 32  # the words that hold nodes 0 .. n - 1 in each head's row
+    span = 4 * ((QH - 1) * W + nw)  # rows are W words apart; the last ends inside the workspace
+    raw = w[o_b.value:o_b.value + span].cpu().numpy()
+    rows = np.stack([raw[4 * W * qh:4 * W * qh + 4 * nw] for qh in range(QH)])
+    kept = np.unpackbits(rows, axis=1, bitorder="little")[:, :n]  # [QH, n]
+    # units: the G heads of a KV head and Tb queries of a sequence
+    G = Hq // Hkv
+    Tb = min(T, 16 // G)
+    nTB = -(-T // Tb)
+    U = B * Hkv * nTB
+    masks = np.zeros((U, n), np.int64)
+    for u in range(U):
+        tb, kv, bb = u % nTB, (u // nTB) % Hkv, u // (nTB * Hkv)
+        for m in range(min(Tb, T - tb * Tb) * G):
+            t, h = tb * Tb + m // G, kv * G + m % G
+            masks[u] |= kept[(bb * T + t) * Hq + h].astype(np.int64) << m
+    out_nodes = np.zeros((U, n), np.int64)
+    out_masks = np.zeros((U, n), np.int64)
+    count = np.zeros(U, np.int64)
+    for u in range(U):
+        nz = np.nonzero(masks[u])[0]
+        count[u] = nz.size
+        out_nodes[u, :nz.size] = nz
+        out_masks[u, :nz.size] = masks[u, nz]
+    return out_nodes, out_masks, count

@@ -41,6 +41,7 @@ EXPORTS = (
     "zha_attend_causal",
     "zha_attend_noalloc",
     "zha_attend_level_view",
+    "zha_attend_level_bits",
     "zha_dense_workspace_bytes",
     "zha_dense_attend",
     "zha_dense_attend_causal",
@@ -118,6 +119,8 @@ def load() -> ctypes.CDLL:
     lib.zha_attend_level_view.argtypes = [P(ZhaTree), i32, i32, i32, P(i64), P(i64), P(i64),
                                           P(i64), P(i64)]
     lib.zha_attend_level_view.restype = i32
+    lib.zha_attend_level_bits.argtypes = [P(ZhaTree), i32, i32, i32, P(i64), P(i64), P(i64)]
+    lib.zha_attend_level_bits.restype = i32
     lib.zha_dense_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32]
     lib.zha_dense_workspace_bytes.restype = sz
     lib.zha_dense_attend.argtypes = [vp, i32, i32, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp,

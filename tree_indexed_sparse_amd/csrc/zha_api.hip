@@ -99,14 +99,19 @@ int check_geometry(int B, int Hkv, int N, int N_cap, int d, int b, int L) {
 }
 
 // Workspace of zha_attend: every offset is in bytes and 256-byte aligned.
+// Workspace of one attend call. Level 1 keeps a compacted union list (nodes, masks,
+// count); every level l >= 2 keeps its member masks uncompacted, by node id (masks[l],
+// written by the score launch one level down), and the members' kept bits (bits[l], or the
+// fused descent's bitmaps for the levels it walks).
 struct WsLayout {
   int U, QH, splits;
   int64_t n[ZHA_MAX_LEVELS + 1];  // nodes per unit at each level (current N)
-  int64_t off_count, off_lvl, off_S, off_bits, off_part, off_chunks;
+  int64_t off_count, off_lvl, off_S, off_part, off_chunks;
   int64_t off_pmax, off_pmin, off_hm, off_hc, off_cut, off_umask, off_ucnt, off_mcnt, off_tbits;
   int64_t pstride, nch, ustride, nuc;
-  int64_t off_nodes[ZHA_MAX_LEVELS + 1], off_masks[ZHA_MAX_LEVELS + 1];
-  int64_t S_stride, bit_words;
+  int64_t off_nodes1, off_masks[ZHA_MAX_LEVELS + 1];
+  int64_t off_bits[ZHA_MAX_LEVELS + 1], bit_words[ZHA_MAX_LEVELS + 1];
+  int64_t S_stride;
   int64_t total;
 };
 
@@ -153,17 +158,19 @@ WsLayout layout_of(const Geom& g) {
   off = align256(off + 4 * (int64_t)w.QH * (g.L + 1));
   for (int l = 1; l <= g.L; ++l) {
     const int64_t bytes = 4 * (int64_t)g.U * w.n[l];
-    w.off_nodes[l] = off;
-    off = align256(off + bytes);
+    if (l == 1) {
+      w.off_nodes1 = off;
+      off = align256(off + bytes);
+    }
     w.off_masks[l] = off;
     off = align256(off + bytes);
+    w.bit_words[l] = (w.n[l] + 31) / 32;
+    w.off_bits[l] = off;
+    off = align256(off + 4 * (int64_t)w.QH * w.bit_words[l]);
   }
   w.S_stride = (w.n[1] + 3) / 4 * 4;  // score rows start 16-byte aligned
   w.off_S = off;
   off = align256(off + 4 * (int64_t)w.QH * w.S_stride);
-  w.bit_words = (w.n[1] + 31) / 32;
-  w.off_bits = off;
-  off = align256(off + 4 * (int64_t)w.QH * w.bit_words);
   w.off_part = off;
   off = align256(off + 4 * (int64_t)g.U * decode_splits(g.U, true) * kMaxMembers * (g.D + 2));
   w.off_chunks = off;
@@ -195,13 +202,32 @@ WsLayout layout_of(const Geom& g) {
   return w;
 }
 
-LevelBufs level_bufs(char* ws, const WsLayout& w, int l) {
+// level 1's union list
+LevelBufs level1_bufs(char* ws, const WsLayout& w) {
   LevelBufs lb;
-  lb.nodes = (uint32_t*)(ws + w.off_nodes[l]);
-  lb.masks = (uint32_t*)(ws + w.off_masks[l]);
-  lb.count = (uint32_t*)(ws + w.off_count) + (int64_t)l * w.U;
-  lb.stride = w.n[l];
+  lb.nodes = (uint32_t*)(ws + w.off_nodes1);
+  lb.masks = (uint32_t*)(ws + w.off_masks[1]);
+  lb.count = (uint32_t*)(ws + w.off_count) + w.U;
+  lb.stride = w.n[1];
   return lb;
+}
+
+// The kept bits of level l: the fused descent's bitmaps for l >= l_top > 0. Byte offset
+// into the workspace and words per query head.
+void level_bits_at(const WsLayout& w, int L, int l_top, int l, int64_t* off, int64_t* words) {
+  if (l_top && l >= l_top) {
+    int64_t word_off;
+    top_level_layout(L, l, &word_off, words);
+    *off = w.off_tbits + 4 * word_off;
+    return;
+  }
+  *off = w.off_bits[l];
+  *words = w.bit_words[l];
+}
+KeepBits level_bits(char* ws, const WsLayout& w, int L, int l_top, int l) {
+  int64_t off, words;
+  level_bits_at(w, L, l_top, l, &off, &words);
+  return KeepBits{(uint32_t*)(ws + off), words};
 }
 
 int check_tree(const zha_tree* t) {
@@ -528,16 +554,37 @@ int zha_attend_level_view(const zha_tree* t, int T, int Hq, int level, int64_t* 
   Geom g;
   st = make_geom(t, T, Hq, &g);
   if (st != ZHA_OK) return st;
-  if (level < 1 || level > t->L)
-    return fail(ZHA_ERR_INVALID_ARG, "level %d outside [1, %d]", level, t->L);
+  if (level != 1)
+    return fail(ZHA_ERR_INVALID_ARG,
+                "level %d: only level 1 keeps a union list (zha_attend_level_bits has the "
+                "levels above)", level);
   if (!off_nodes || !off_masks || !off_count || !stride || !units)
     return fail(ZHA_ERR_INVALID_ARG, "output pointers must not be NULL");
   const WsLayout w = layout_of(g);
-  *off_nodes = w.off_nodes[level];
-  *off_masks = w.off_masks[level];
-  *off_count = w.off_count + 4 * (int64_t)level * w.U;
-  *stride = w.n[level];
+  *off_nodes = w.off_nodes1;
+  *off_masks = w.off_masks[1];
+  *off_count = w.off_count + 4 * (int64_t)w.U;
+  *stride = w.n[1];
   *units = w.U;
+  return ZHA_OK;
+}
+
+int zha_attend_level_bits(const zha_tree* t, int T, int Hq, int level, int64_t* off_bits,
+                          int64_t* words, int64_t* nodes) {
+  int st = check_tree(t);
+  if (st != ZHA_OK) return st;
+  Geom g;
+  st = make_geom(t, T, Hq, &g);
+  if (st != ZHA_OK) return st;
+  if (level < 2 || level > t->L)
+    return fail(ZHA_ERR_INVALID_ARG, "level %d outside [2, %d]", level, t->L);
+  if (!off_bits || !words || !nodes)
+    return fail(ZHA_ERR_INVALID_ARG, "output pointers must not be NULL");
+  const WsLayout w = layout_of(g);
+  const int64_t n_top = w.n[t->L];
+  const int l_top = n_top > 0 ? top_levels_lowest(g, w.n) : 0;
+  level_bits_at(w, t->L, l_top, level, off_bits, words);
+  *nodes = n_top * ipow(t->b, t->L - level);
   return ZHA_OK;
 }
 
@@ -574,11 +621,9 @@ int attend_impl(const zha_tree* t, const void* Q, int T, int Hq, const int32_t* 
 
   hipStream_t s = (hipStream_t)stream;
   char* ws = (char*)workspace;
-  LevelBufs lv[ZHA_MAX_LEVELS + 2];
-  for (int l = 1; l <= t->L; ++l) lv[l] = level_bufs(ws, w, l);
+  const LevelBufs lv1 = level1_bufs(ws, w);
   float* S = (float*)(ws + w.off_S);
   int32_t* lvl = (int32_t*)(ws + w.off_lvl);
-  const KeepBits kb{(uint32_t*)(ws + w.off_bits), w.bit_words};
   WideSel wsel;
   wsel.pmax = (float*)(ws + w.off_pmax);
   wsel.pmin = (float*)(ws + w.off_pmin);
@@ -622,39 +667,52 @@ int attend_impl(const zha_tree* t, const void* Q, int T, int Hq, const int32_t* 
   const int l_top = searched ? top_levels_lowest(g, w.n) : 0;
   if (l_top) {
     e = timed(ZHA_K_DESCENT, l_top, s, [&] {
-      return launch_top_levels(g, t->pyramid, lv, t->level_off, unit_stride, l_top, Q, t->dtype,
-                               p, lvl, (uint32_t*)(ws + w.off_tbits), fp4 ? &rv : nullptr, s);
+      return launch_top_levels(g, t->pyramid, t->level_off, unit_stride, l_top, Q, t->dtype, p,
+                               lvl, (uint32_t*)(ws + w.off_tbits), fp4 ? &rv : nullptr, s);
     });
     if (e != hipSuccess) return hip_fail(e, "top-level descent launch");
   }
   int64_t cap_l = t->N_cap;
   for (int l = 1; l <= t->L; ++l) cap_l /= t->b;  // capacity nodes at the top level
   for (int l = l_top ? l_top - 1 : t->L; l < t->L; ++l) cap_l *= t->b;
+  int64_t F = n_top_nodes;  // frontier entries at level l: its nodes under the top nodes
+  for (int l = l_top ? l_top - 1 : t->L; l < t->L; ++l) F *= t->b;
   for (int l = l_top ? l_top - 1 : t->L; searched && l >= 1; --l) {
-    const LevelBufs* parent = (l < t->L) ? &lv[l + 1] : nullptr;
-    const int n_top = (l == t->L) ? (int)w.n[t->L] : 0;
+    Frontier fr{};
+    fr.F = (int)F;
+    if (l < t->L) {
+      const KeepBits pb = level_bits(ws, w, t->L, l_top, l + 1);
+      fr.pbits = pb.bits;
+      fr.pwords = pb.words;
+      fr.pmask = (uint32_t*)(ws + w.off_masks[l + 1]);
+      fr.pstride = w.n[l + 1];
+    }
     const float* X = t->pyramid + t->level_off[l];
-    const int64_t frontier_cap = parent ? t->b * parent->stride : n_top;
-    wsel.pent = score_entries(frontier_cap, g.U);
-    const WideSel* wide = select_is_wide(frontier_cap) ? &wsel : nullptr;
+    wsel.pent = score_entries(F, g.U);
+    const WideSel* wide = select_is_wide(F) ? &wsel : nullptr;
+    // the kept bits the level below reads (level 1: the narrow selection's, for its
+    // compaction; the chunked one compacts from the scores and cuts)
+    const KeepBits kb = (l > 1 || !wide) ? level_bits(ws, w, t->L, l_top, l) : KeepBits{};
     e = timed(ZHA_K_SCORE, l, s, [&] {
-      return launch_score(g, X, cap_l * t->d, Q, t->dtype, parent, n_top, S, w.S_stride, wide,
+      return launch_score(g, X, cap_l * t->d, Q, t->dtype, fr, S, w.S_stride, wide,
                           fp4 ? rv.codes[l] : nullptr, fp4 ? rv.scales[l] : nullptr, cap_l, s);
     });
     if (e != hipSuccess) return hip_fail(e, "score launch");
     e = timed(ZHA_K_SELECT, l, s, [&] {
-      return launch_select(g, l, S, w.S_stride, parent, n_top, kb, p, anchor,
-                           l == 1 ? sel_idx : nullptr, cap, sel_count, lvl, wide, s);
+      return launch_select(g, l, S, w.S_stride, fr, kb, p, anchor, l == 1 ? sel_idx : nullptr,
+                           cap, sel_count, lvl, wide, s);
     });
     if (e != hipSuccess) return hip_fail(e, "select launch");
-    e = timed(ZHA_K_COMPACT, l, s, [&] {
-      if (wide)
-        return launch_union(g, l, S, w.S_stride, parent, n_top, lv[l], anchor,
-                            l == 1 ? sel_idx : nullptr, cap, *wide, s);
-      return launch_compact(g, parent, n_top, kb, lv[l], (uint32_t*)(ws + w.off_chunks), s);
-    });
-    if (e != hipSuccess) return hip_fail(e, "compact launch");
+    if (l == 1) {
+      e = timed(ZHA_K_COMPACT, l, s, [&] {
+        if (wide)
+          return launch_union(g, S, w.S_stride, fr, lv1, anchor, sel_idx, cap, *wide, s);
+        return launch_compact(g, fr, kb, lv1, (uint32_t*)(ws + w.off_chunks), s);
+      });
+      if (e != hipSuccess) return hip_fail(e, "compact launch");
+    }
     cap_l *= t->b;
+    F *= t->b;
   }
   if (!searched || n_tail > 0 || positions) {
     e = timed(ZHA_K_SELECT, 0, s, [&] {
@@ -665,7 +723,7 @@ int attend_impl(const zha_tree* t, const void* Q, int T, int Hq, const int32_t* 
   }
   float* part = (float*)(ws + w.off_part);
   e = timed(ZHA_K_DECODE, 0, s, [&] {
-    return launch_decode(g, t->dtype, K, V, Q, lv[1], searched ? 1 : 0, searched ? anchor : 0,
+    return launch_decode(g, t->dtype, K, V, Q, lv1, searched ? 1 : 0, searched ? anchor : 0,
                          w.splits, part, s);
   });
   if (e != hipSuccess) return hip_fail(e, "decode launch");

@@ -116,12 +116,29 @@ struct LevelBufs {
   int64_t stride;    // = nodes at this level
 };
 
-// Per-query-head kept flags over the current frontier (bit k of row qh), rewritten at
-// every level by the selector and read by the compaction.
+// Per-query-head kept flags of one level, by node id (bit j of row qh: head qh kept node j).
 struct KeepBits {
   uint32_t* bits;    // [QH][words]
   int64_t words;
 };
+
+// The frontier a level is searched over, indexed by node id: entry k is node k of the
+// level. Below the top it holds the children of every node of the level above; entry k
+// belongs to member m's frontier when m kept its parent k / b (entries whose parent no
+// member kept are skipped, not compacted away). At the top level (pbits null) it is the
+// complete top nodes, each member's own the first head_ntop of them.
+struct Frontier {
+  const uint32_t* pbits;  // [QH][pwords]: the level above's kept bits; null at the top
+  int64_t pwords;
+  uint32_t* pmask;        // [U][pstride]: member mask per parent node (bit m: member m kept
+  int64_t pstride;        //   it), written by the level's score launch, read after it
+  int F;                  // entries: the level's nodes under the complete top nodes
+};
+
+// unit u's member masks per parent node (null at the top)
+__host__ __device__ __forceinline__ const uint32_t* parent_masks(const Frontier& fr, int u) {
+  return fr.pbits ? fr.pmask + (int64_t)u * fr.pstride : nullptr;
+}
 
 // Scratch of the chunked selection and compaction that large frontiers take (workgroups
 // over frontier chunks instead of one per query head or unit).
@@ -189,9 +206,9 @@ bool pool_fused_encodes(int dtype_in, int dtype_r, int b, int nlev, int row_begi
 // rcodes != nullptr: score the level's MXFP4 copy (rcodes / rscales, rows_cap rows per
 // unit) with the query quantised to MXFP4, instead of the float32 rows X.
 hipError_t launch_score(const Geom& geo, const float* X, int64_t X_unit_stride, const void* Q,
-                        int dtype, const LevelBufs* parent, int n_top, float* S,
-                        int64_t S_stride, const WideSel* wide, const uint8_t* rcodes,
-                        const uint8_t* rscales, int64_t rows_cap, hipStream_t s);
+                        int dtype, const Frontier& fr, float* S, int64_t S_stride,
+                        const WideSel* wide, const uint8_t* rcodes, const uint8_t* rscales,
+                        int64_t rows_cap, hipStream_t s);
 
 // Whether a frontier of up to `cap_entries` entries takes the chunked selection, and the
 // sizes of its scratch for frontiers up to `cap_entries`.
@@ -203,34 +220,37 @@ int64_t wide_union_chunks(int64_t cap_entries);  // compaction chunks
 int64_t wide_union_stride(int64_t cap_entries);  // umask row length
 int wide_buckets();
 
-// Per-member top-p: kept flags into `kb`; at level 1 also the token lists and counts.
+// Per-member top-p: the kept flags into `kb` (by node id; the chunked selection writes
+// them only when kb.bits is set); at level 1 also the token lists and counts.
 hipError_t launch_select(const Geom& geo, int level, const float* S, int64_t S_stride,
-                         const LevelBufs* parent, int n_top, KeepBits kb, float p, int anchor,
+                         const Frontier& fr, KeepBits kb, float p, int anchor,
                          int32_t* sel_idx, int64_t cap, int32_t* sel_count, int32_t* lvl_kept,
                          const WideSel* wide, hipStream_t s);
 
 // Union of the members' kept flags -> ascending kept-node list with member masks.
 // chunk_cnt: scratch of compact_counter_words(U, frontier capacity) words.
-hipError_t launch_compact(const Geom& geo, const LevelBufs* parent, int n_top, KeepBits kb,
-                          const LevelBufs& cur, uint32_t* chunk_cnt, hipStream_t s);
+hipError_t launch_compact(const Geom& geo, const Frontier& fr, KeepBits kb, const LevelBufs& cur,
+                          uint32_t* chunk_cnt, hipStream_t s);
 
 // Fused descent through the top levels (frontiers of at most 1024 entries): the lowest
-// such level >= 2 (0 if none; the top level must qualify), and the launches that walk
-// levels L .. l_lo per query head and write each level's union list. bitmaps: scratch of
-// top_bitmap_words(QH, L) words.
+// such level >= 2 (0 if none; the top level must qualify), and the launch that walks
+// levels L .. l_lo per query head and writes each level's kept bits into `bitmaps`
+// (top_bitmap_words(QH, L) words; top_level_bits gives a level's rows).
 int top_levels_lowest(const Geom& geo, const int64_t* nodes_per_level);
 // router != nullptr: the levels are scored from the MXFP4 copy.
-hipError_t launch_top_levels(const Geom& geo, const float* pyramid, const LevelBufs* lv,
-                             const int64_t* level_off, const int64_t* unit_stride, int l_lo,
-                             const void* Q, int dtype, float p, int32_t* lvl_kept,
-                             uint32_t* bitmaps, const RouterView* router, hipStream_t s);
+hipError_t launch_top_levels(const Geom& geo, const float* pyramid, const int64_t* level_off,
+                             const int64_t* unit_stride, int l_lo, const void* Q, int dtype,
+                             float p, int32_t* lvl_kept, uint32_t* bitmaps,
+                             const RouterView* router, hipStream_t s);
 int64_t top_bitmap_words(int QH, int L);
+// level `level`'s bitmaps: row qh starts at word word_off + qh * row_words
+void top_level_layout(int L, int level, int64_t* word_off, int64_t* row_words);
 
-// Compaction after the chunked selection: the members' keep flags straight from their
-// scores and cuts, the union list, and at level 1 the token lists.
-hipError_t launch_union(const Geom& geo, int level, const float* S, int64_t S_stride,
-                        const LevelBufs* parent, int n_top, const LevelBufs& cur, int anchor,
-                        int32_t* sel_idx, int64_t cap, const WideSel& wide, hipStream_t s);
+// Compaction after the chunked selection at level 1: the members' keep flags straight
+// from their scores and cuts, the union list and the token lists.
+hipError_t launch_union(const Geom& geo, const float* S, int64_t S_stride, const Frontier& fr,
+                        const LevelBufs& cur, int anchor, int32_t* sel_idx, int64_t cap,
+                        const WideSel& wide, hipStream_t s);
 int64_t compact_counter_words(int U, int64_t n);
 
 // Sparse GQA decode: the tokens of the level-1 union list (has_list), the anchor tokens

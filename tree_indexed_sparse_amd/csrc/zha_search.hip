@@ -10,11 +10,14 @@
 //
 // GQA: the members of a unit (the query heads, and queries, that read one KV head) share
 // one union frontier per level, so each summary row is read once and scored for every
-// member. Each member then selects over its own sub-frontier, and a per-unit compaction
-// turns the members' kept flags into the next level's union list.
+// member. Each member then selects over its own sub-frontier and records the nodes it
+// keeps as bits by node id. A level's frontier is indexed by node id: entry k is node k,
+// and its score launch ORs the members' bits of the parent k / b into the entry's member
+// mask, skipping the rows of entries no member reaches. Only level 1 is compacted, into
+// the kept-node list the decode reads and the members' token lists.
 //
-// One level = three launches (score, select, compact). Kernel boundaries order them; no
-// kernel here uses a device-scope fence.
+// A level = a score and a select launch (plus the compaction at level 1). Kernel
+// boundaries order them; no kernel here uses a device-scope fence.
 
 #include "zha_internal.h"
 #include "zha_mxfp4.h"
@@ -37,12 +40,30 @@ constexpr float kMaxSpread = 32.0f;             // exp(-32) * 2^42 < 1: lower ma
 constexpr int kCompactThreads = 1024;
 constexpr int kCompactChunk = 16384;            // frontier entries per compaction step
 
-// node id of frontier entry k: the top level's frontier is every node; below, entry k
-// is child k % b of the (k / b)-th node the level above kept (pnodes: that unit's list)
-__device__ __forceinline__ uint32_t frontier_node(const uint32_t* pnodes, int k, const FastDiv& bd) {
-  if (!pnodes) return (uint32_t)k;
-  const uint32_t q = bd.div((uint32_t)k);
-  return pnodes[q] * bd.d + ((uint32_t)k - q * bd.d);
+// The unit's member masks of parents p0 .. p0 + np - 1 (bit m: member m kept the parent),
+// ORed from the members' kept bits one level up: into sPm and into the frontier's parent
+// masks, which the level's selection and compaction read. sPw: kMaxMembers * wcap words of
+// staging. Every thread calls this; it ends with a barrier.
+template <int NT>
+__device__ __forceinline__ void stage_parent_masks(const Geom& geo, const Frontier& fr, int u,
+                                                   int Mu, int p0, int np, uint32_t* sPw,
+                                                   int wcap, uint32_t* sPm) {
+  const int w0 = p0 >> 5;
+  const int nw = ((p0 + np - 1) >> 5) - w0 + 1;  // <= wcap
+  for (int i = threadIdx.x; i < Mu * nw; i += NT) {
+    const int mm = i / nw, wd = i - mm * nw;
+    sPw[mm * wcap + wd] = fr.pbits[(int64_t)qh_of(geo, u, mm) * fr.pwords + w0 + wd];
+  }
+  __syncthreads();
+  uint32_t* gm = fr.pmask + (int64_t)u * fr.pstride;
+  for (int i = threadIdx.x; i < np; i += NT) {
+    const int j = p0 + i, wd = (j >> 5) - w0, bt = j & 31;
+    uint32_t mk = 0u;
+    for (int mm = 0; mm < Mu; ++mm) mk |= ((sPw[mm * wcap + wd] >> bt) & 1u) << mm;
+    sPm[i] = mk;
+    gm[j] = mk;
+  }
+  __syncthreads();
 }
 
 // Token list run: dst[j] = nodes[j / b] * b + j % b for j < ntok, skipping tokens below
@@ -168,19 +189,19 @@ __device__ __forceinline__ f32x4_t fp4_mfma(const Fp4Rows& R, uint4 qc, uint32_t
 // current one is multiplied.
 template <int D, typename Tq>
 __global__ __launch_bounds__(kScoreThreads) void score_fp4_kernel(
-    Geom geo, const Tq* __restrict__ Q,
-    LevelBufs parent, int has_parent, int n_top, float* __restrict__ S, int64_t S_stride,
+    Geom geo, const Tq* __restrict__ Q, Frontier fr, float* __restrict__ S, int64_t S_stride,
     float sigma, int ent, float* __restrict__ pmax, float* __restrict__ pmin, int64_t pstride,
     const uint8_t* __restrict__ RC, const uint8_t* __restrict__ RS, int64_t rows_cap) {
   constexpr int kMaxParents = kScoreEntries / 2 + 2;
+  constexpr int kPw = (kMaxParents + 31) / 32 + 1;
   const int kPerWave = ent / (kScoreThreads / 64);
-  __shared__ uint32_t sPn[kMaxParents];
+  __shared__ uint32_t sPw[kMaxMembers * kPw];
   __shared__ uint32_t sPm[kMaxParents];
   __shared__ float sRed[2][kScoreThreads / 64][16];
 
   const int u = blockIdx.y;
-  const int b = geo.b;
-  const int F = has_parent ? b * (int)parent.count[u] : n_top;
+  const bool has_parent = fr.pbits != nullptr;
+  const int F = fr.F;
   const int k_wg = blockIdx.x * ent;
   if (k_wg >= F) return;
   const int Mu = members_of(geo, u);
@@ -188,20 +209,15 @@ __global__ __launch_bounds__(kScoreThreads) void score_fp4_kernel(
   const int mem = lane & 15, grp = lane >> 4;
 
   const int p0 = (int)geo.bdiv.div((uint32_t)k_wg);
-  if (has_parent) {
-    const int np = (int)geo.bdiv.div((uint32_t)(min(k_wg + ent, F) - 1)) - p0 + 1;
-    for (int i = threadIdx.x; i < np; i += kScoreThreads) {
-      const uint32_t nd = parent.nodes[u * parent.stride + p0 + i];
-      const uint32_t mk = parent.masks[u * parent.stride + p0 + i];
-      sPn[i] = nd;
-      sPm[i] = mk;
-    }
-  }
   // query operand: this lane's MXFP4 block of its member's query (zero past the members)
   uint4 qc = make_uint4(0u, 0u, 0u, 0u);
   uint32_t qs = 127u;
   fp4_query_operand<D, Tq>(Q + (int64_t)qh_of(geo, u, mem < Mu ? mem : 0) * D, grp, mem < Mu,
                            &qc, &qs);
+  if (has_parent) {
+    const int np = (int)geo.bdiv.div((uint32_t)(min(k_wg + ent, F) - 1)) - p0 + 1;
+    stage_parent_masks<kScoreThreads>(geo, fr, u, Mu, p0, np, sPw, kPw, sPm);
+  }
   __syncthreads();
   const uint8_t* RCu = RC + (int64_t)bg_of(geo, u) * rows_cap * (D / 2);
   const uint8_t* RSu = RS + (int64_t)bg_of(geo, u) * rows_cap * (D / kMxBlock);
@@ -212,14 +228,11 @@ __global__ __launch_bounds__(kScoreThreads) void score_fp4_kernel(
   // at the top level a member's frontier is the top nodes complete for it
   const int f_mem = has_parent ? F : (mem < Mu ? min(F, head_ntop(geo, qh_of(geo, u, mem))) : 0);
 
+  // entries whose parent no member kept read row 0 (a cached line) and are not stored
+  // for any member's selection (none has them in its frontier)
   auto load_rows = [&](Fp4Rows& R, int k) {
-    const bool ok = k < F;
-    const uint32_t kq = geo.bdiv.div((uint32_t)k);
-    const uint32_t node =
-        ok ? (has_parent ? sPn[kq - p0] * geo.bdiv.d + ((uint32_t)k - kq * geo.bdiv.d)
-                         : (uint32_t)k)
-           : 0u;
-    fp4_row_operand<D>(RCu, RSu, node, grp, R);
+    const bool ok = k < F && (!has_parent || sPm[geo.bdiv.div((uint32_t)k) - p0] != 0u);
+    fp4_row_operand<D>(RCu, RSu, ok ? (uint32_t)k : 0u, grp, R);
   };
 
   auto compute = [&](const Fp4Rows& R, int rb) {
@@ -357,8 +370,8 @@ struct MemberHalve {
 template <int D, typename Tq, int M, int LPR>
 __global__ __launch_bounds__(kScoreThreads) void score_rows_kernel(
     Geom geo, const float* __restrict__ X, int64_t X_unit_stride, const Tq* __restrict__ Q,
-    LevelBufs parent, int has_parent, int n_top, float* __restrict__ S, int64_t S_stride,
-    float sigma, int ent, float* __restrict__ pmax, float* __restrict__ pmin, int64_t pstride) {
+    Frontier fr, float* __restrict__ S, int64_t S_stride, float sigma, int ent,
+    float* __restrict__ pmax, float* __restrict__ pmin, int64_t pstride) {
   constexpr int DPL = D / LPR;                // dims per lane
   constexpr int NLD = DPL / 4;                // 16-byte loads per lane per row
   constexpr int RPI = 64 / LPR;               // rows per load instruction
@@ -368,13 +381,15 @@ __global__ __launch_bounds__(kScoreThreads) void score_rows_kernel(
   constexpr int NW = kScoreThreads / 64;
   constexpr int IPG = kRowGroup / RPI;        // row slots per lane per load group
   constexpr int kMaxParents = kRowEntries / 2 + 2;
+  constexpr int kPw = (kMaxParents + 31) / 32 + 1;
   static_assert(M % NW == 0, "members spread evenly over the waves for the stores");
-  __shared__ uint32_t sPn[kMaxParents];
+  __shared__ uint32_t sPw[kMaxMembers * kPw];
   __shared__ uint32_t sPm[kMaxParents];
   __shared__ float sS[M][kRowEntries];
 
   const int u = blockIdx.y;
-  const int F = has_parent ? geo.b * (int)parent.count[u] : n_top;
+  const bool has_parent = fr.pbits != nullptr;
+  const int F = fr.F;
   const int k_wg = blockIdx.x * ent;
   if (k_wg >= F) return;
   const int k_end = min(k_wg + ent, F);
@@ -382,13 +397,6 @@ __global__ __launch_bounds__(kScoreThreads) void score_rows_kernel(
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int sub = lane % LPR, rin = lane / LPR;
   const int p0 = (int)geo.bdiv.div((uint32_t)k_wg);
-  if (has_parent) {
-    const int np = (int)geo.bdiv.div((uint32_t)(k_end - 1)) - p0 + 1;
-    for (int i = threadIdx.x; i < np; i += kScoreThreads) {
-      sPn[i] = parent.nodes[u * parent.stride + p0 + i];
-      sPm[i] = parent.masks[u * parent.stride + p0 + i];
-    }
-  }
   // this lane's dims of every member's query, zero past the unit's members
   float qv[M][DPL];
 #pragma unroll
@@ -396,6 +404,10 @@ __global__ __launch_bounds__(kScoreThreads) void score_rows_kernel(
     const Tq* qr = Q + (int64_t)qh_of(geo, u, m < Mu ? m : 0) * D + 4 * sub;
 #pragma unroll
     for (int j = 0; j < NLD; ++j) load_q4(qr + 4 * LPR * j, &qv[m][4 * j]);
+  }
+  if (has_parent) {
+    const int np = (int)geo.bdiv.div((uint32_t)(k_end - 1)) - p0 + 1;
+    stage_parent_masks<kScoreThreads>(geo, fr, u, Mu, p0, np, sPw, kPw, sPm);
   }
 #pragma unroll
   for (int m = 0; m < M; ++m)
@@ -409,8 +421,9 @@ __global__ __launch_bounds__(kScoreThreads) void score_rows_kernel(
   const int n_groups = groups_wg > wave ? (groups_wg - wave + NW - 1) / NW : 0;
 
   // Every group's loads are issued unconditionally (rows past the range read its last row
-  // again, a line already in cache): a branch around a load would make the compiler wait
-  // for all outstanding loads where the paths join.
+  // again, a line already in cache; rows whose parent no member kept read row 0, and no
+  // member's selection reads their scores): a branch around a load would make the compiler
+  // wait for all outstanding loads where the paths join.
   typedef f32x4_t Group[IPG][NLD];
   auto load_group = [&](Group& x, int g) {
     uint32_t node[IPG];
@@ -418,9 +431,8 @@ __global__ __launch_bounds__(kScoreThreads) void score_rows_kernel(
     for (int i = 0; i < IPG; ++i) {
       const uint32_t kc =
           (uint32_t)min(k_wg + (g * NW + wave) * kRowGroup + i * RPI + rin, k_end - 1);
-      const uint32_t q = geo.bdiv.div(kc);
-      const uint32_t pn = sPn[has_parent ? q - p0 : 0];
-      node[i] = has_parent ? pn * geo.bdiv.d + (kc - q * geo.bdiv.d) : kc;
+      const uint32_t pm = sPm[has_parent ? geo.bdiv.div(kc) - p0 : 0];
+      node[i] = (!has_parent || pm != 0u) ? kc : 0u;
     }
 #pragma unroll
     for (int i = 0; i < IPG; ++i)
@@ -718,8 +730,8 @@ __device__ __forceinline__ Quad load_quad(const float* Sq, const uint32_t* pmask
 }
 
 __global__ __launch_bounds__(kSelThreads) void select_kernel(
-    Geom geo, int level, const float* __restrict__ S, int64_t S_stride, LevelBufs parent,
-    int has_parent, int n_top, KeepBits kb, float p, int anchor, int32_t* __restrict__ sel_idx,
+    Geom geo, int level, const float* __restrict__ S, int64_t S_stride, Frontier fr,
+    KeepBits kb, float p, int anchor, int32_t* __restrict__ sel_idx,
     int64_t cap, int32_t* __restrict__ sel_count, int32_t* __restrict__ lvl_kept) {
   __shared__ SelShared sh;
   const int qh = blockIdx.x;
@@ -727,14 +739,13 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   int u, m;
   unit_member_of(geo, qh, &u, &m);
   const int b = geo.b;
-  const int F = has_parent ? b * (int)parent.count[u] : n_top;
+  const int F = fr.F;
   // the member's own frontier: at the top level, the top nodes complete for it
   const int vis = head_vis(geo, qh);
-  const int Fm = has_parent ? F : min(F, vis / geo.top_span);
+  const int Fm = fr.pbits ? F : min(F, vis / geo.top_span);
   anchor = min(anchor, vis);
   const float* Sq = S + (int64_t)qh * S_stride;
-  const uint32_t* pmask = has_parent ? parent.masks + u * parent.stride : nullptr;
-  const uint32_t* pnodes = has_parent ? parent.nodes + u * parent.stride : nullptr;
+  const uint32_t* pmask = parent_masks(fr, u);
   uint32_t* kbits = kb.bits + (int64_t)qh * kb.words;
   const bool cached = F <= kCache;
   if (tid == 0) {
@@ -987,17 +998,14 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     return s > s_cut || (s == s_cut && (uint32_t)k <= k_cut);
   };
 
-  // anchor overlap: kept level-1 tokens below `anchor` (they can only sit in the first
-  // ceil(anchor / b) frontier entries, since node ids are distinct and ascending)
+  // anchor overlap: kept level-1 tokens below `anchor` (they sit in the first
+  // ceil(anchor / b) frontier entries: entry k is node k)
   if (level == 1 && tid == 0) {
     int dup = 0;
     const int lim = min(F, (anchor + b - 1) / b);
     for (int k = 0; k < lim; ++k) {
       const bool in = pmask ? ((pmask[geo.bdiv.div((uint32_t)k)] >> m) & 1u) : k < Fm;
-      if (keep_of(Sq[k], in, k)) {
-        const int node = (int)frontier_node(pnodes, k, geo.bdiv);
-        if (node * b < anchor) dup += min(b, anchor - node * b);
-      }
+      if (keep_of(Sq[k], in, k) && k * b < anchor) dup += min(b, anchor - k * b);
     }
     sh.scalar_u32[2] = (uint32_t)dup;
   }
@@ -1031,7 +1039,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
       uint32_t r = r0;
 #pragma unroll
       for (int i = 0; i < kVec; ++i)
-        if ((kept_bits >> i) & 1u) sh.tile_nodes[r++] = frontier_node(pnodes, k0 + i, geo.bdiv);
+        if ((kept_bits >> i) & 1u) sh.tile_nodes[r++] = (uint32_t)(k0 + i);
     }
     __syncthreads();
     const int words = min(kTileE, F - t0 + 31) / 32;
@@ -1051,11 +1059,11 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
 
 // -------------------------------------------------------------- fused upper levels
 // The levels whose frontier holds at most kTopFuse entries (the top levels of a deep tree)
-// run in two launches instead of three per level. Each query head walks them top-down in
+// run in one launch instead of three per level. Each query head walks them top-down in
 // its own workgroup, with its own frontier (the children of the nodes it kept one level
 // up), scores and kept list in LDS; it records the nodes it keeps at each level as a
-// bitmap. A second launch ORs the members' bitmaps of each unit into the level's union
-// list, which the lower levels (and diagnostics) read.
+// bitmap by node id, which the next level's score launch ORs per unit into its parent
+// masks.
 // Per level and head:
 //   score:  sigma * q . X for every frontier row; a row is split over D / 4 lanes that
 //           each take four dims, and the partial sums are added across those lanes;
@@ -1084,7 +1092,6 @@ constexpr int kTopMinWaves = 4;
 constexpr int kTopWords = kTopMax / 32;          // bitmap words per (head, level)
 
 struct TopLevels {
-  LevelBufs lv[ZHA_MAX_LEVELS + 1];
   int64_t xoff[ZHA_MAX_LEVELS + 1];     // float offset of level l in the pyramid
   int64_t xstride[ZHA_MAX_LEVELS + 1];  // floats per (sequence, KV head) at level l
 };
@@ -1235,7 +1242,7 @@ __global__ __launch_bounds__(NT, kTopMinWaves) void head_top_kernel(
   }
   int cur = 0;
   // top level: every node complete for this head
-  int F = min((int)tl.lv[l_hi].stride, head_ntop(geo, qh));
+  int F = head_ntop(geo, qh);
   if (F == 0) {
     // no complete top node: the head keeps nothing at any of these levels. (A non-empty
     // frontier always keeps at least one node, so below the top no frontier is empty.)
@@ -1468,46 +1475,6 @@ __global__ __launch_bounds__(NT, kTopMinWaves) void head_top_kernel(
   }
 }
 
-// Union lists of the fused levels: workgroup (unit, level); thread t takes kTopEPT nodes from kTopEPT t.
-__global__ __launch_bounds__(kTopThreads) void union_top_kernel(Geom geo, TopLevels tl, int l_lo,
-                                                                 const uint32_t* __restrict__ bitmaps) {
-  __shared__ uint32_t wcnt[kTopWaves];
-  const int u = blockIdx.x, l = l_lo + blockIdx.y;
-  const int tid = threadIdx.x;
-  const int Mu = members_of(geo, u);
-  const LevelBufs& cur = tl.lv[l];
-  const int n = (int)cur.stride;
-  const int j0 = kTopEPT * tid;
-  uint32_t msk[kTopEPT];
-#pragma unroll
-  for (int i = 0; i < kTopEPT; ++i) msk[i] = 0u;
-  if (j0 < n) {
-    for (int mm = 0; mm < Mu; ++mm) {
-      const uint32_t w =
-          bitmaps[((int64_t)qh_of(geo, u, mm) * (geo.L + 1) + l) * kTopWords + (j0 >> 5)];
-#pragma unroll
-      for (int i = 0; i < kTopEPT; ++i) msk[i] |= ((w >> ((j0 + i) & 31)) & 1u) << mm;
-    }
-  }
-  uint32_t nz = 0;
-#pragma unroll
-  for (int i = 0; i < kTopEPT; ++i) {
-    if (j0 + i >= n) msk[i] = 0u;
-    nz += msk[i] != 0u;
-  }
-  uint32_t total;
-  uint32_t pos = block_excl_scan<kTopThreads>(nz, wcnt, &total);
-#pragma unroll
-  for (int i = 0; i < kTopEPT; ++i) {
-    if (msk[i]) {
-      cur.nodes[u * cur.stride + pos] = (uint32_t)(j0 + i);
-      cur.masks[u * cur.stride + pos] = msk[i];
-      ++pos;
-    }
-  }
-  if (tid == 0) cur.count[u] = total;
-}
-
 // ------------------------------------------------------------------ chunked selection
 // A large frontier runs its top-p and compaction in four launches whose workgroups each
 // take one chunk of the frontier:
@@ -1577,21 +1544,20 @@ __device__ __forceinline__ void partial_minmax(const WideSel& w, int qh, int F, 
 }
 
 __global__ __launch_bounds__(kWideThreads) void wide_hist_kernel(
-    Geom geo, const float* __restrict__ S, int64_t S_stride, LevelBufs parent, int has_parent,
-    int n_top, WideSel w) {
+    Geom geo, const float* __restrict__ S, int64_t S_stride, Frontier fr, WideSel w) {
   __shared__ unsigned long long hm[kWB];
   __shared__ uint32_t hc[kWB];
   __shared__ float red[2 * (kWideThreads / 64)];
   const int qh = blockIdx.y, chunk = blockIdx.x;
   int u, m;
   unit_member_of(geo, qh, &u, &m);
-  const int F = has_parent ? geo.b * (int)parent.count[u] : n_top;
+  const int F = fr.F;
   const int c0 = chunk * kWideChunk;
   if (c0 >= F) return;
   const int tid = threadIdx.x;
   const float* Sq = S + (int64_t)qh * S_stride;
-  const uint32_t* pmask = has_parent ? parent.masks + u * parent.stride : nullptr;
-  const int Fm = has_parent ? F : min(F, head_ntop(geo, qh));  // the member's frontier
+  const uint32_t* pmask = parent_masks(fr, u);
+  const int Fm = fr.pbits ? F : min(F, head_ntop(geo, qh));  // the member's frontier
   const int end = min(Fm, c0 + kWideChunk);
   Quad q[kWideTiles];
 #pragma unroll
@@ -1656,8 +1622,8 @@ __device__ __forceinline__ uint64_t cut_block_scan(uint64_t v, unsigned long lon
 
 template <int NT>
 __global__ __launch_bounds__(NT, kCutMinWaves) void wide_cut_kernel(
-    Geom geo, int level, const float* __restrict__ S, int64_t S_stride, LevelBufs parent,
-    int has_parent, int n_top, float p, int anchor, int32_t* __restrict__ sel_idx, int64_t cap,
+    Geom geo, int level, const float* __restrict__ S, int64_t S_stride, Frontier fr,
+    KeepBits kb, float p, int anchor, int32_t* __restrict__ sel_idx, int64_t cap,
     int32_t* __restrict__ sel_count, int32_t* __restrict__ lvl_kept, WideSel w) {
   __shared__ CutShared sh;
   const int qh = blockIdx.x;
@@ -1667,18 +1633,21 @@ __global__ __launch_bounds__(NT, kCutMinWaves) void wide_cut_kernel(
   int u, m;
   unit_member_of(geo, qh, &u, &m);
   const int b = geo.b;
-  const int F = has_parent ? b * (int)parent.count[u] : n_top;
+  const int F = fr.F;
   const int nch = (F + kWideChunk - 1) / kWideChunk;
   const float* Sq = S + (int64_t)qh * S_stride;
-  const uint32_t* pmask = has_parent ? parent.masks + u * parent.stride : nullptr;
-  const uint32_t* pnodes = has_parent ? parent.nodes + u * parent.stride : nullptr;
+  const uint32_t* pmask = parent_masks(fr, u);
   // the member's own frontier: at the top level, the top nodes complete for it
   const int vis = head_vis(geo, qh);
-  const int Fm = has_parent ? F : min(F, vis / geo.top_span);
+  const int Fm = fr.pbits ? F : min(F, vis / geo.top_span);
   anchor = min(anchor, vis);
+  uint32_t* krow = kb.bits ? kb.bits + (int64_t)qh * kb.words : nullptr;
+  const int kwords = (F + 31) / 32;
   // a member with no entry at this level (it kept nothing above: no complete top node)
   // selects nothing; no entry scores above an infinite cut. Called block-uniformly.
   auto empty_result = [&]() {
+    if (krow)
+      for (int i = tid; i < kwords; i += NT) krow[i] = 0u;
     if (tid == 0) {
       uint32_t* rec = w.cut + 4 * (int64_t)qh;
       rec[0] = __float_as_uint(INFINITY);
@@ -2010,18 +1979,42 @@ __global__ __launch_bounds__(NT, kCutMinWaves) void wide_cut_kernel(
   cut_block_scan<NT>(above, sh.wsum, &kept64);
   __syncthreads();
   const uint32_t kept = (uint32_t)kept64 + sh.scalar_u32[3];
+  // the member's kept flags by node id, for the score launch of the level below: one entry
+  // per lane, a wave's 64 flags by ballot, four entries per thread in flight (loads from
+  // indices clamped below Fm; entries at or past Fm are not in)
+  if (krow) {
+    const int ntot = kwords * 32;
+    for (int base = 0; base < ntot; base += 4 * NT) {
+      float sv[4];
+      uint32_t pw[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int kc = min(base + j * NT + tid, Fm - 1);
+        sv[j] = Sq[kc];
+        pw[j] = pmask ? pmask[geo.bdiv.div((uint32_t)kc)] : 0xffffffffu;
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int k = base + j * NT + tid;
+        const bool keep = k < Fm && ((pw[j] >> m) & 1u) &&
+                          (sv[j] > s_cut || (sv[j] == s_cut && (uint32_t)k <= k_cut));
+        const uint64_t bal = __ballot(keep);
+        const int w0 = (base + j * NT + 64 * wave) >> 5;
+        if (lane < 2 && w0 + lane < kwords) krow[w0 + lane] = (uint32_t)(bal >> (32 * lane));
+      }
+    }
+  }
   if (tid == 0) {
-    // anchor overlap at level 1: kept tokens below `anchor` (first ceil(anchor / b) entries)
+    // anchor overlap at level 1: kept tokens below `anchor` (in the first ceil(anchor / b)
+    // entries: entry k is node k)
     int dup = 0;
     if (level == 1) {
       const int lim = min(F, (anchor + b - 1) / b);
       for (int k = 0; k < lim; ++k) {
         const bool in = pmask ? ((pmask[geo.bdiv.div((uint32_t)k)] >> m) & 1u) : k < Fm;
         const float sk = Sq[k];
-        if (in && (sk > s_cut || (sk == s_cut && (uint32_t)k <= k_cut))) {
-          const int node = (int)frontier_node(pnodes, k, geo.bdiv);
-          if (node * b < anchor) dup += min(b, anchor - node * b);
-        }
+        if (in && (sk > s_cut || (sk == s_cut && (uint32_t)k <= k_cut)) && k * b < anchor)
+          dup += min(b, anchor - k * b);
       }
     }
     uint32_t* rec = w.cut + 4 * (int64_t)qh;
@@ -2039,15 +2032,13 @@ __global__ __launch_bounds__(NT, kCutMinWaves) void wide_cut_kernel(
 // union: per (chunk of kUnionChunk entries, unit). Thread t takes entries 4t..4t+3 and
 // 1024+4t..1024+4t+3 of the chunk, so each member's row is read as two coalesced float4.
 __global__ __launch_bounds__(kUnionThreads) void wide_union_kernel(
-    Geom geo, const float* __restrict__ S, int64_t S_stride, LevelBufs parent, int has_parent,
-    int n_top, WideSel w) {
+    Geom geo, const float* __restrict__ S, int64_t S_stride, Frontier fr, WideSel w) {
   __shared__ float s_cut[kMaxMembers];
   __shared__ uint32_t k_cut[kMaxMembers];
   __shared__ int s_lim[kMaxMembers];
   __shared__ uint32_t cnt[kUnionThreads / 64][kMaxMembers + 1];
   const int u = blockIdx.y, chunk = blockIdx.x;
-  const int b = geo.b;
-  const int F = has_parent ? b * (int)parent.count[u] : n_top;
+  const int F = fr.F;
   const int c0 = chunk * kUnionChunk;
   if (c0 >= F) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -2057,11 +2048,11 @@ __global__ __launch_bounds__(kUnionThreads) void wide_union_kernel(
     const uint32_t* rec = w.cut + 4 * (int64_t)qh;
     s_cut[tid] = __uint_as_float(rec[0]);
     k_cut[tid] = rec[1];
-    s_lim[tid] = has_parent ? F : min(F, head_ntop(geo, qh));  // member's top frontier
+    s_lim[tid] = fr.pbits ? F : min(F, head_ntop(geo, qh));  // member's top frontier
   }
   int kk[8];
   uint32_t pm[8];
-  const uint32_t* pmask = has_parent ? parent.masks + u * parent.stride : nullptr;
+  const uint32_t* pmask = parent_masks(fr, u);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     kk[i] = c0 + (i >> 2) * (kUnionChunk / 2) + 4 * tid + (i & 3);
@@ -2138,51 +2129,32 @@ __device__ __forceinline__ uint32_t wave_prefix_total(const uint32_t* cnt, int n
   return acc;
 }
 
-// write: per (chunk, unit, member group). The chunk's masks and node ids are staged in
-// LDS; in group 0 each wave compacts a quarter of the chunk with ballots into the union
-// list; at level 1 group z's wave w writes the token lists of members
-// w + 4 z, w + 4 (z + groups), ... (the groups share the members' list writing).
+// write (level 1): per (chunk, unit, member group). The chunk's masks are staged in LDS;
+// in group 0 each wave compacts a quarter of the chunk with ballots into the union list;
+// group z's wave w writes the token lists of members w + 4 z, w + 4 (z + groups), ...
+// (the groups share the members' list writing).
 __global__ __launch_bounds__(kUnionThreads) void wide_write_kernel(
-    Geom geo, int level, LevelBufs parent, int has_parent, int n_top, LevelBufs cur,
-    int anchor, int32_t* __restrict__ sel_idx, int64_t cap, WideSel w) {
+    Geom geo, Frontier fr, LevelBufs cur, int anchor, int32_t* __restrict__ sel_idx,
+    int64_t cap, WideSel w) {
   constexpr int NW = kUnionThreads / 64;
   constexpr int kPerWave = kUnionChunk / NW;
   __shared__ uint32_t s_um[kUnionChunk];
-  __shared__ uint32_t s_node[kUnionChunk];
   __shared__ uint32_t wtot[NW];
   __shared__ uint32_t s_stage[NW][64];  // a wave's kept nodes of 64 entries
   const int u = blockIdx.y, chunk = blockIdx.x;
   const int b = geo.b;
-  const int F = has_parent ? b * (int)parent.count[u] : n_top;
-  const int c0 = chunk * kUnionChunk;
+  const int F = fr.F;
+  const int c0 = chunk * kUnionChunk;  // entry c0 + e is node c0 + e
   if (c0 >= F) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int Mu = members_of(geo, u);
   const int nchunks = (F + kUnionChunk - 1) / kUnionChunk;
-  const uint32_t* pnodes = has_parent ? parent.nodes + u * parent.stride : nullptr;
-  const uint32_t* umg = w.umask + (int64_t)u * w.ustride + c0;
   {
+    const uint32_t* umg = w.umask + (int64_t)u * w.ustride + c0;
     const uint4 a = *reinterpret_cast<const uint4*>(umg + 4 * tid);
     const uint4 c = *reinterpret_cast<const uint4*>(umg + kUnionChunk / 2 + 4 * tid);
-    // node ids: parent loads from indices clamped below F (entries past F are never used)
-    uint32_t nd[8], kq[8], pn[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int e = (i >> 2) * (kUnionChunk / 2) + 4 * tid + (i & 3);
-      nd[i] = (uint32_t)min(c0 + e, F - 1);
-      kq[i] = geo.bdiv.div(nd[i]);
-    }
-    if (pnodes) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) pn[i] = pnodes[kq[i]];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) nd[i] = pn[i] * (uint32_t)b + (nd[i] - kq[i] * (uint32_t)b);
-    }
     *reinterpret_cast<uint4*>(&s_um[4 * tid]) = a;
     *reinterpret_cast<uint4*>(&s_um[kUnionChunk / 2 + 4 * tid]) = c;
-    *reinterpret_cast<uint4*>(&s_node[4 * tid]) = make_uint4(nd[0], nd[1], nd[2], nd[3]);
-    *reinterpret_cast<uint4*>(&s_node[kUnionChunk / 2 + 4 * tid]) =
-        make_uint4(nd[4], nd[5], nd[6], nd[7]);
   }
   const uint32_t before = wave_prefix_total(w.ucnt + (int64_t)u * w.nuc, chunk, lane);
   __syncthreads();
@@ -2205,7 +2177,7 @@ __global__ __launch_bounds__(kUnionThreads) void wide_write_kernel(
       const uint64_t bal = __ballot(msk != 0u);
       if (msk) {
         const uint32_t at = pos + (uint32_t)__popcll(bal & ((1ull << lane) - 1ull));
-        onodes[at] = s_node[e];
+        onodes[at] = (uint32_t)(c0 + e);
         omasks[at] = msk;
       }
       pos += (uint32_t)__popcll(bal);
@@ -2216,7 +2188,7 @@ __global__ __launch_bounds__(kUnionThreads) void wide_write_kernel(
       cur.count[u] = tot;
     }
   }
-  if (level != 1 || !sel_idx) return;
+  if (!sel_idx) return;
   for (int mm = wave + NW * zg; mm < Mu; mm += NW * ng) {
     const int qh = qh_of(geo, u, mm);
     const int anc = min(anchor, head_vis(geo, qh));  // the member's anchor tokens
@@ -2229,7 +2201,7 @@ __global__ __launch_bounds__(kUnionThreads) void wide_write_kernel(
       const int e = 64 * r + lane;
       const bool kept = (s_um[e] >> mm) & 1u;
       const uint64_t bal = __ballot(kept);
-      if (kept) stage[__popcll(bal & ((1ull << lane) - 1ull))] = s_node[e];
+      if (kept) stage[__popcll(bal & ((1ull << lane) - 1ull))] = (uint32_t)(c0 + e);
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       // one token per lane: each store covers up to 256 contiguous bytes (a short run: the
@@ -2328,27 +2300,13 @@ __device__ __forceinline__ uint32_t chunk_masks(const Geom& geo, int u, int Mu, 
 // Writes this thread's kept entries from position r on. Node ids come from parent loads
 // at indices clamped below F, issued together before any store.
 template <int EPT>
-__device__ __forceinline__ void chunk_write(const uint32_t* pnodes, const FastDiv& bd, int F,
-                                            int c0, uint32_t r, const uint32_t (&msk)[EPT],
+__device__ __forceinline__ void chunk_write(int c0, uint32_t r, const uint32_t (&msk)[EPT],
                                             const LevelBufs& cur, int u) {
-  const int e0 = EPT * threadIdx.x;
-  uint32_t nd[EPT];
-#pragma unroll
-  for (int i = 0; i < EPT; ++i) nd[i] = (uint32_t)min(c0 + e0 + i, F - 1);
-  if (pnodes) {
-    uint32_t kq[EPT], pn[EPT];
-#pragma unroll
-    for (int i = 0; i < EPT; ++i) {
-      kq[i] = bd.div(nd[i]);
-      pn[i] = pnodes[kq[i]];
-    }
-#pragma unroll
-    for (int i = 0; i < EPT; ++i) nd[i] = pn[i] * bd.d + (nd[i] - kq[i] * bd.d);
-  }
+  const int e0 = EPT * threadIdx.x;  // entry c0 + e0 + i is node c0 + e0 + i
 #pragma unroll
   for (int i = 0; i < EPT; ++i) {
     if (msk[i]) {
-      cur.nodes[u * cur.stride + r] = nd[i];
+      cur.nodes[u * cur.stride + r] = (uint32_t)(c0 + e0 + i);
       cur.masks[u * cur.stride + r] = msk[i];
       ++r;
     }
@@ -2360,15 +2318,12 @@ constexpr int kEPT = kCompactChunk / kCompactThreads;  // entries per thread (16
 // mode 0: one workgroup walks every chunk of the unit. mode 1: count chunk blockIdx.x into
 // chunk_cnt. mode 2: write chunk blockIdx.x after the counts of the chunks before it.
 __global__ __launch_bounds__(kCompactThreads) void compact_kernel(
-    Geom geo, LevelBufs parent, int has_parent, int n_top, KeepBits kb, LevelBufs cur,
-    int mode, uint32_t* __restrict__ chunk_cnt, int max_chunks) {
+    Geom geo, int F, KeepBits kb, LevelBufs cur, int mode, uint32_t* __restrict__ chunk_cnt,
+    int max_chunks) {
   __shared__ uint32_t sbits[kMaxMembers][kCompactChunk / 32];
   __shared__ uint32_t wave_sum[kCompactThreads / 64];
   const int u = blockIdx.y;
-  const int b = geo.b;
-  const int F = has_parent ? b * (int)parent.count[u] : n_top;
   const int Mu = members_of(geo, u);
-  const uint32_t* pnodes = has_parent ? parent.nodes + u * parent.stride : nullptr;
   uint32_t msk[kEPT];
   if (mode == 0) {
     uint32_t out = 0;
@@ -2377,7 +2332,7 @@ __global__ __launch_bounds__(kCompactThreads) void compact_kernel(
       const uint32_t cnt = chunk_masks<kEPT>(geo, u, Mu, F, c0, kb, sbits, msk);
       uint32_t total;
       const uint32_t r = out + block_excl_scan<kCompactThreads>(cnt, wave_sum, &total);
-      chunk_write<kEPT>(pnodes, geo.bdiv, F, c0, r, msk, cur, u);
+      chunk_write<kEPT>(c0, r, msk, cur, u);
       out += total;
     }
     if (threadIdx.x == 0) cur.count[u] = out;
@@ -2399,7 +2354,7 @@ __global__ __launch_bounds__(kCompactThreads) void compact_kernel(
   }
   uint32_t before = 0;
   for (int c = 0; c < chunk; ++c) before += chunk_cnt[u * max_chunks + c];
-  chunk_write<kEPT>(pnodes, geo.bdiv, F, c0, before + r, msk, cur, u);
+  chunk_write<kEPT>(c0, before + r, msk, cur, u);
   if (chunk == nchunks - 1 && threadIdx.x == 0) cur.count[u] = before + total;
 }
 
@@ -2414,27 +2369,25 @@ int score_entries(int64_t cap_entries, int units) {
 }
 
 hipError_t launch_score(const Geom& geo, const float* X, int64_t X_unit_stride, const void* Q,
-                        int dtype, const LevelBufs* parent, int n_top, float* S,
-                        int64_t S_stride, const WideSel* wide, const uint8_t* rcodes,
-                        const uint8_t* rscales, int64_t rows_cap, hipStream_t s) {
-  const int cap_entries = parent ? (int)(geo.b * parent->stride) : n_top;
-  const int ent = score_entries(cap_entries, geo.U);
+                        int dtype, const Frontier& fr, float* S, int64_t S_stride,
+                        const WideSel* wide, const uint8_t* rcodes, const uint8_t* rscales,
+                        int64_t rows_cap, hipStream_t s) {
+  if (fr.F < 1) return hipErrorInvalidValue;
+  const int ent = score_entries(fr.F, geo.U);
   if (!rcodes && ent > kRowEntries) return hipErrorInvalidValue;
-  dim3 grid((cap_entries + ent - 1) / ent, geo.U);
+  dim3 grid((fr.F + ent - 1) / ent, geo.U);
   const float sigma = 1.0f / sqrtf((float)geo.D);
-  LevelBufs par = parent ? *parent : LevelBufs{};
-  const int hp = parent ? 1 : 0;
   float* pmax = wide ? wide->pmax : nullptr;
   float* pmin = wide ? wide->pmin : nullptr;
   const int64_t pstride = wide ? wide->pstride : 0;
 #define ZHA_SCORE_FP4(DD, TQ)                                                           \
   hipLaunchKernelGGL((score_fp4_kernel<DD, TQ>), grid, dim3(kScoreThreads), 0, s, geo,       \
-                     (const TQ*)Q, par, hp, n_top, S, S_stride, sigma, ent, pmax, pmin,        \
-                     pstride, rcodes, rscales, rows_cap)
+                     (const TQ*)Q, fr, S, S_stride, sigma, ent, pmax, pmin, pstride, rcodes,   \
+                     rscales, rows_cap)
 #define ZHA_ROWS(DD, TQ, MM, LL)                                                        \
   hipLaunchKernelGGL((score_rows_kernel<DD, TQ, MM, LL>), grid, dim3(kScoreThreads), 0, s, geo, \
-                     X, X_unit_stride, (const TQ*)Q, par, hp, n_top, S, S_stride, sigma, ent,  \
-                     pmax, pmin, pstride)
+                     X, X_unit_stride, (const TQ*)Q, fr, S, S_stride, sigma, ent, pmax, pmin,  \
+                     pstride)
   // the float32 router scores with coalesced whole-row loads; the member count rounds up
   // to 8 or 16. Rows are split over 16 lanes (8 at d = 64 with 8 members), so every
   // exchange of the member butterfly is a DPP move within 16 lanes (with 32 lanes per row
@@ -2472,52 +2425,48 @@ int64_t wide_union_stride(int64_t cap_entries) {
 int wide_buckets() { return kWB; }
 
 hipError_t launch_select(const Geom& geo, int level, const float* S, int64_t S_stride,
-                         const LevelBufs* parent, int n_top, KeepBits kb, float p, int anchor,
+                         const Frontier& fr, KeepBits kb, float p, int anchor,
                          int32_t* sel_idx, int64_t cap, int32_t* sel_count, int32_t* lvl_kept,
                          const WideSel* wide, hipStream_t s) {
-  LevelBufs par = parent ? *parent : LevelBufs{};
   const int QH = geo.B * geo.T * geo.Hq;
+  if (fr.F < 1) return hipErrorInvalidValue;
   if (wide) {
-    const int hp = parent ? 1 : 0;
-    const int64_t cap_entries = parent ? geo.b * parent->stride : n_top;
-    const dim3 grid((unsigned)((cap_entries + kWideChunk - 1) / kWideChunk), QH);
-    hipLaunchKernelGGL(wide_hist_kernel, grid, dim3(kWideThreads), 0, s, geo, S, S_stride, par,
-                       hp, n_top, *wide);
+    const dim3 grid((unsigned)((fr.F + kWideChunk - 1) / kWideChunk), QH);
+    hipLaunchKernelGGL(wide_hist_kernel, grid, dim3(kWideThreads), 0, s, geo, S, S_stride, fr,
+                       *wide);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (QH > kComputeUnits)
       hipLaunchKernelGGL(wide_cut_kernel<kCutThreads / 2>, dim3(QH), dim3(kCutThreads / 2), 0, s,
-                         geo, level, S, S_stride, par, hp, n_top, p, anchor, sel_idx, cap,
-                         sel_count, lvl_kept, *wide);
+                         geo, level, S, S_stride, fr, kb, p, anchor, sel_idx, cap, sel_count,
+                         lvl_kept, *wide);
     else
       hipLaunchKernelGGL(wide_cut_kernel<kCutThreads>, dim3(QH), dim3(kCutThreads), 0, s, geo,
-                         level, S, S_stride, par, hp, n_top, p, anchor, sel_idx, cap, sel_count,
+                         level, S, S_stride, fr, kb, p, anchor, sel_idx, cap, sel_count,
                          lvl_kept, *wide);
     return hipGetLastError();
   }
+  if (!kb.bits) return hipErrorInvalidValue;
   hipLaunchKernelGGL(select_kernel, dim3(QH), dim3(kSelThreads), 0, s, geo, level, S, S_stride,
-                     par, parent ? 1 : 0, n_top, kb, p, anchor, sel_idx, cap, sel_count,
-                     lvl_kept);
+                     fr, kb, p, anchor, sel_idx, cap, sel_count, lvl_kept);
   return hipGetLastError();
 }
 
-hipError_t launch_compact(const Geom& geo, const LevelBufs* parent, int n_top, KeepBits kb,
-                          const LevelBufs& cur, uint32_t* chunk_cnt, hipStream_t s) {
-  LevelBufs par = parent ? *parent : LevelBufs{};
-  const int hp = parent ? 1 : 0;
-  const int cap = parent ? (int)(geo.b * parent->stride) : n_top;  // frontier capacity
-  const int max_chunks = (cap + kCompactChunk - 1) / kCompactChunk;
+hipError_t launch_compact(const Geom& geo, const Frontier& fr, KeepBits kb, const LevelBufs& cur,
+                          uint32_t* chunk_cnt, hipStream_t s) {
+  const int F = fr.F;
+  const int max_chunks = (F + kCompactChunk - 1) / kCompactChunk;
   if (max_chunks <= 1) {
-    hipLaunchKernelGGL(compact_kernel, dim3(1, geo.U), dim3(kCompactThreads), 0, s, geo, par, hp,
-                       n_top, kb, cur, 0, chunk_cnt, 1);
+    hipLaunchKernelGGL(compact_kernel, dim3(1, geo.U), dim3(kCompactThreads), 0, s, geo, F, kb,
+                       cur, 0, chunk_cnt, 1);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(compact_kernel, dim3(max_chunks, geo.U), dim3(kCompactThreads), 0, s, geo,
-                     par, hp, n_top, kb, cur, 1, chunk_cnt, max_chunks);
+                     F, kb, cur, 1, chunk_cnt, max_chunks);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(compact_kernel, dim3(max_chunks, geo.U), dim3(kCompactThreads), 0, s, geo,
-                     par, hp, n_top, kb, cur, 2, chunk_cnt, max_chunks);
+                     F, kb, cur, 2, chunk_cnt, max_chunks);
   return hipGetLastError();
 }
 
@@ -2527,13 +2476,12 @@ int top_levels_lowest(const Geom& geo, const int64_t* nodes_per_level) {
   return lo;  // 0: no level qualifies
 }
 
-hipError_t launch_top_levels(const Geom& geo, const float* pyramid, const LevelBufs* lv,
-                             const int64_t* level_off, const int64_t* unit_stride, int l_lo,
-                             const void* Q, int dtype, float p, int32_t* lvl_kept,
-                             uint32_t* bitmaps, const RouterView* router, hipStream_t s) {
+hipError_t launch_top_levels(const Geom& geo, const float* pyramid, const int64_t* level_off,
+                             const int64_t* unit_stride, int l_lo, const void* Q, int dtype,
+                             float p, int32_t* lvl_kept, uint32_t* bitmaps,
+                             const RouterView* router, hipStream_t s) {
   TopLevels tl{};
   for (int l = l_lo; l <= geo.L; ++l) {
-    tl.lv[l] = lv[l];
     tl.xoff[l] = level_off[l];
     tl.xstride[l] = unit_stride[l];
   }
@@ -2561,14 +2509,14 @@ hipError_t launch_top_levels(const Geom& geo, const float* pyramid, const LevelB
 #undef ZHA_TOP_D
 #undef ZHA_TOP
 #undef ZHA_TOP_NT
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(union_top_kernel, dim3(geo.U, geo.L - l_lo + 1), dim3(kTopThreads), 0, s,
-                     geo, tl, l_lo, bitmaps);
   return hipGetLastError();
 }
 
 int64_t top_bitmap_words(int QH, int L) { return (int64_t)QH * (L + 1) * kTopWords; }
+void top_level_layout(int L, int level, int64_t* word_off, int64_t* row_words) {
+  *word_off = (int64_t)level * kTopWords;
+  *row_words = (int64_t)(L + 1) * kTopWords;
+}
 
 hipError_t launch_tail(const Geom& geo, int searched, int anchor, int32_t* sel_idx,
                        int64_t cap, int32_t* sel_count, uint32_t* counts, int count_words,
@@ -2579,21 +2527,19 @@ hipError_t launch_tail(const Geom& geo, int searched, int anchor, int32_t* sel_i
   return hipGetLastError();
 }
 
-hipError_t launch_union(const Geom& geo, int level, const float* S, int64_t S_stride,
-                        const LevelBufs* parent, int n_top, const LevelBufs& cur, int anchor,
-                        int32_t* sel_idx, int64_t cap, const WideSel& wide, hipStream_t s) {
-  LevelBufs par = parent ? *parent : LevelBufs{};
-  const int hp = parent ? 1 : 0;
-  const int64_t cap_entries = parent ? geo.b * parent->stride : n_top;
-  const dim3 grid((unsigned)wide_union_chunks(cap_entries), geo.U);
-  hipLaunchKernelGGL(wide_union_kernel, grid, dim3(kUnionThreads), 0, s, geo, S, S_stride, par,
-                     hp, n_top, wide);
+hipError_t launch_union(const Geom& geo, const float* S, int64_t S_stride, const Frontier& fr,
+                        const LevelBufs& cur, int anchor, int32_t* sel_idx, int64_t cap,
+                        const WideSel& wide, hipStream_t s) {
+  if (fr.F < 1) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)wide_union_chunks(fr.F), geo.U);
+  hipLaunchKernelGGL(wide_union_kernel, grid, dim3(kUnionThreads), 0, s, geo, S, S_stride, fr,
+                     wide);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // at level 1 the members' token lists are shared out over two workgroups per chunk
-  const dim3 wgrid(grid.x, grid.y, (level == 1 && sel_idx) ? 2 : 1);
-  hipLaunchKernelGGL(wide_write_kernel, wgrid, dim3(kUnionThreads), 0, s, geo, level, par, hp,
-                     n_top, cur, anchor, sel_idx, cap, wide);
+  // the members' token lists are shared out over two workgroups per chunk
+  const dim3 wgrid(grid.x, grid.y, sel_idx ? 2 : 1);
+  hipLaunchKernelGGL(wide_write_kernel, wgrid, dim3(kUnionThreads), 0, s, geo, fr, cur, anchor,
+                     sel_idx, cap, wide);
   return hipGetLastError();
 }
 
