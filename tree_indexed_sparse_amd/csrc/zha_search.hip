@@ -228,6 +228,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_fp4_kernel(
   // at the top level a member's frontier is the top nodes complete for it
   const int f_mem = has_parent ? F : (mem < Mu ? min(F, head_ntop(geo, qh_of(geo, u, mem))) : 0);
 
+  const bool quad_parent = has_parent && geo.b % 4 == 0;
   // entries whose parent no member kept read row 0 (a cached line) and are not stored
   // for any member's selection (none has them in its frontier)
   auto load_rows = [&](Fp4Rows& R, int k) {
@@ -240,7 +241,10 @@ __global__ __launch_bounds__(kScoreThreads) void score_fp4_kernel(
     // rows kb..kb+3 of member `mem`; + 0.0f turns a -0 score into +0 so float and bit
     // orders agree
     const int kb = k_wave + 16 * rb + 4 * grp;
-    if (mem < Mu && kb < F) {
+    // with b a multiple of 4 the four rows share one parent: not stored for a member whose
+    // frontier does not hold them (it never reads them)
+    const bool mine = !quad_parent || ((sPm[geo.bdiv.div((uint32_t)kb) - p0] >> mem) & 1u);
+    if (mem < Mu && kb < F && mine) {
       const float4 o = make_float4(sigma * c[0] + 0.0f, sigma * c[1] + 0.0f,
                                    sigma * c[2] + 0.0f, sigma * c[3] + 0.0f);
       if (kb + 3 < F) {
@@ -484,6 +488,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_rows_kernel(
   // contiguous run of 16-byte stores, and reduces its max and min over the member's
   // frontier entries for the chunked selection
   const int n = k_end - k_wg;
+  const bool quad_parent = has_parent && geo.b % 4 == 0;
 #pragma unroll
   for (int mi = 0; mi < M / NW; ++mi) {
     const int mm = wave + NW * mi;
@@ -493,6 +498,9 @@ __global__ __launch_bounds__(kScoreThreads) void score_rows_kernel(
     float mx = -INFINITY, mn = INFINITY;
     for (int c = 4 * lane; c < n; c += 256) {
       const float4 o = *reinterpret_cast<const float4*>(&sS[mm][c]);
+      // with b a multiple of 4 the four entries share one parent: a member whose frontier
+      // does not hold them never reads their scores, so they are not stored
+      if (quad_parent && !((sPm[geo.bdiv.div((uint32_t)(k_wg + c)) - p0] >> mm) & 1u)) continue;
       if (c + 3 < n) {
         *reinterpret_cast<float4*>(dst + c) = o;
       } else {
@@ -726,6 +734,24 @@ __device__ __forceinline__ Quad load_quad(const float* Sq, const uint32_t* pmask
     pw[i] = pmask ? pmask[bd.div((uint32_t)max(min(k0 + i, end - 1), 0))] : 0xffffffffu;
 #pragma unroll
   for (int i = 0; i < kVec; ++i) q.in[i] = k0 + i < end && ((pw[i] >> m) & 1u);
+  return q;
+}
+
+// load_quad when b is a multiple of 4 (the quad's entries share the parent k0 / b): the
+// parent mask is loaded first and a member outside the quad's parent reads the row's first
+// float4 (a cached line) instead of its scores, which the score launch did not store.
+__device__ __forceinline__ Quad load_quad_b4(const float* Sq, const uint32_t* pmask, int m,
+                                             const FastDiv& bd, int k0, int end) {
+  Quad q;
+  const int kc = k0 < end ? k0 : max((end - 1) & ~3, 0);
+  const bool in = (pmask[bd.div((uint32_t)kc)] >> m) & 1u;
+  const float4 v = *reinterpret_cast<const float4*>(Sq + (in ? kc : 0));
+  q.s[0] = v.x;
+  q.s[1] = v.y;
+  q.s[2] = v.z;
+  q.s[3] = v.w;
+#pragma unroll
+  for (int i = 0; i < kVec; ++i) q.in[i] = in && k0 + i < end;
   return q;
 }
 
@@ -1560,9 +1586,15 @@ __global__ __launch_bounds__(kWideThreads) void wide_hist_kernel(
   const int Fm = fr.pbits ? F : min(F, head_ntop(geo, qh));  // the member's frontier
   const int end = min(Fm, c0 + kWideChunk);
   Quad q[kWideTiles];
+  if (pmask && geo.b % 4 == 0) {
 #pragma unroll
-  for (int j = 0; j < kWideTiles; ++j)
-    q[j] = load_quad(Sq, pmask, m, geo.bdiv, c0 + j * kTileE + kVec * tid, end);
+    for (int j = 0; j < kWideTiles; ++j)
+      q[j] = load_quad_b4(Sq, pmask, m, geo.bdiv, c0 + j * kTileE + kVec * tid, end);
+  } else {
+#pragma unroll
+    for (int j = 0; j < kWideTiles; ++j)
+      q[j] = load_quad(Sq, pmask, m, geo.bdiv, c0 + j * kTileE + kVec * tid, end);
+  }
   for (int i = tid; i < kWB; i += kWideThreads) {
     hm[i] = 0ull;
     hc[i] = 0u;
@@ -2073,13 +2105,19 @@ __global__ __launch_bounds__(kUnionThreads) void wide_union_kernel(
   // below F stays inside the row (past F the row's first float4 is read and ignored)
   const int off_a = kk[0] < F ? c0 + 4 * tid : 0;
   const int off_c = kk[4] < F ? c0 + kUnionChunk / 2 + 4 * tid : 0;
+  // with b a multiple of 4 each float4 is one parent's entries: a member outside it reads
+  // the row's first float4 (a cached line) instead of scores the score launch did not store
+  const bool quad_parent = pmask && geo.b % 4 == 0;
   for (int g0 = 0; g0 < Mu; g0 += 4) {
     float4 a[4], c[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const float* Sq = S + (int64_t)qh_of(geo, u, min(g0 + j, Mu - 1)) * S_stride;
-      a[j] = *reinterpret_cast<const float4*>(Sq + off_a);
-      c[j] = *reinterpret_cast<const float4*>(Sq + off_c);
+      const int mm = min(g0 + j, Mu - 1);
+      const float* Sq = S + (int64_t)qh_of(geo, u, mm) * S_stride;
+      const bool ia = !quad_parent || ((pm[0] >> mm) & 1u);
+      const bool ic = !quad_parent || ((pm[4] >> mm) & 1u);
+      a[j] = *reinterpret_cast<const float4*>(Sq + (ia ? off_a : 0));
+      c[j] = *reinterpret_cast<const float4*>(Sq + (ic ? off_c : 0));
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
