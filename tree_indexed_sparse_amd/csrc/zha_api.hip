@@ -680,6 +680,7 @@ int attend_impl(const zha_tree* t, const void* Q, int T, int Hq, const int32_t* 
   for (int l = l_top ? l_top - 1 : t->L; searched && l >= 1; --l) {
     Frontier fr{};
     fr.F = (int)F;
+    fr.span = (int)ipow(t->b, t->L - l);
     if (l < t->L) {
       const KeepBits pb = level_bits(ws, w, t->L, l_top, l + 1);
       fr.pbits = pb.bits;

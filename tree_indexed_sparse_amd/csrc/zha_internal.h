@@ -133,11 +133,31 @@ struct Frontier {
   uint32_t* pmask;        // [U][pstride]: member mask per parent node (bit m: member m kept
   int64_t pstride;        //   it), written by the level's score launch, read after it
   int F;                  // entries: the level's nodes under the complete top nodes
+  int span;               // nodes of this level under one top node (b^(L - l))
 };
 
 // unit u's member masks per parent node (null at the top)
 __host__ __device__ __forceinline__ const uint32_t* parent_masks(const Frontier& fr, int u) {
   return fr.pbits ? fr.pmask + (int64_t)u * fr.pstride : nullptr;
+}
+
+// Entries of member qh's frontier lie below this: the nodes under the top nodes complete
+// for it (with query positions a member sees a prefix of the cache).
+__device__ __forceinline__ int member_entries(const Geom& g, const Frontier& fr, int qh) {
+  return min(fr.F, head_ntop(g, qh) * fr.span);
+}
+// Entries of unit u's frontier lie below this: the largest of its members' bounds, which
+// depend only on the positions of the unit's queries (tb Tb .. of sequence bb).
+__device__ __forceinline__ int unit_entries(const Geom& g, const Frontier& fr, int u) {
+  if (!g.pos) return fr.F;
+  const int tb = u % g.nTB, bb = u / (g.nTB * g.Hkv);
+  const int t0 = tb * g.Tb, t1 = min(g.T, t0 + g.Tb);
+  int vis = 0;
+  for (int t = t0; t < t1; ++t) {
+    const int p = g.pos[bb * g.T + t];
+    vis = max(vis, (p < 0 ? 0 : (p >= g.N ? g.N - 1 : p)) + 1);
+  }
+  return min(fr.F, (vis / g.top_span) * fr.span);
 }
 
 // Scratch of the chunked selection and compaction that large frontiers take (workgroups

@@ -201,7 +201,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_fp4_kernel(
 
   const int u = blockIdx.y;
   const bool has_parent = fr.pbits != nullptr;
-  const int F = fr.F;
+  const int F = unit_entries(geo, fr, u);
   const int k_wg = blockIdx.x * ent;
   if (k_wg >= F) return;
   const int Mu = members_of(geo, u);
@@ -225,8 +225,8 @@ __global__ __launch_bounds__(kScoreThreads) void score_fp4_kernel(
   const int k_wave = k_wg + wave * kPerWave;
   const int nrb = k_wave < F ? min(kPerWave / 16, (F - k_wave + 15) / 16) : 0;
   float lmx = -INFINITY, lmn = INFINITY;  // over this lane's member rows
-  // at the top level a member's frontier is the top nodes complete for it
-  const int f_mem = has_parent ? F : (mem < Mu ? min(F, head_ntop(geo, qh_of(geo, u, mem))) : 0);
+  // the entries a member's frontier can hold: below the top nodes complete for it
+  const int f_mem = mem < Mu ? member_entries(geo, fr, qh_of(geo, u, mem)) : 0;
 
   const bool quad_parent = has_parent && geo.b % 4 == 0;
   // entries whose parent no member kept read row 0 (a cached line) and are not stored
@@ -393,7 +393,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_rows_kernel(
 
   const int u = blockIdx.y;
   const bool has_parent = fr.pbits != nullptr;
-  const int F = fr.F;
+  const int F = unit_entries(geo, fr, u);
   const int k_wg = blockIdx.x * ent;
   if (k_wg >= F) return;
   const int k_end = min(k_wg + ent, F);
@@ -494,7 +494,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_rows_kernel(
     const int mm = wave + NW * mi;
     if (mm >= Mu) break;
     float* dst = S + (int64_t)qh_of(geo, u, mm) * S_stride + k_wg;
-    const int f_mem = has_parent ? F : min(F, head_ntop(geo, qh_of(geo, u, mm)));
+    const int f_mem = member_entries(geo, fr, qh_of(geo, u, mm));
     float mx = -INFINITY, mn = INFINITY;
     for (int c = 4 * lane; c < n; c += 256) {
       const float4 o = *reinterpret_cast<const float4*>(&sS[mm][c]);
@@ -765,15 +765,16 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   int u, m;
   unit_member_of(geo, qh, &u, &m);
   const int b = geo.b;
+  // the member's frontier lies below Fm (the nodes under the top nodes complete for it);
+  // its kept bits are written for all F entries of the level
   const int F = fr.F;
-  // the member's own frontier: at the top level, the top nodes complete for it
   const int vis = head_vis(geo, qh);
-  const int Fm = fr.pbits ? F : min(F, vis / geo.top_span);
+  const int Fm = member_entries(geo, fr, qh);
   anchor = min(anchor, vis);
   const float* Sq = S + (int64_t)qh * S_stride;
   const uint32_t* pmask = parent_masks(fr, u);
   uint32_t* kbits = kb.bits + (int64_t)qh * kb.words;
-  const bool cached = F <= kCache;
+  const bool cached = Fm <= kCache;
   if (tid == 0) {
     sh.scalar_u32[0] = 0u;
     sh.scalar_u32[1] = 0u;
@@ -786,7 +787,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   auto get = [&](int k0) -> Quad {
     if (!cached) return load_global(k0);
     Quad q;
-    if (k0 >= F) {
+    if (k0 >= Fm) {
 #pragma unroll
       for (int i = 0; i < kVec; ++i) {
         q.s[i] = 0.f;
@@ -807,7 +808,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   // pass 0: max, min over the member's frontier; fill the LDS cache when it fits.
   // Every pass loads kUnroll tiles before using them, to keep several loads in flight.
   float mx = -INFINITY, mn = INFINITY;
-  for (int base = kVec * tid; base < F; base += kTileE * kUnroll) {
+  for (int base = kVec * tid; base < Fm; base += kTileE * kUnroll) {
     Quad q[kUnroll];
 #pragma unroll
     for (int j = 0; j < kUnroll; ++j) q[j] = load_global(base + j * kTileE);
@@ -821,7 +822,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
           mn = fminf(mn, q[j].s[i]);
         }
       }
-      if (cached && k0 < F)
+      if (cached && k0 < Fm)
         *reinterpret_cast<float4*>(&sh.cache[k0]) =
             make_float4(q[j].in[0] ? q[j].s[0] : NAN, q[j].in[1] ? q[j].s[1] : NAN,
                         q[j].in[2] ? q[j].s[2] : NAN, q[j].in[3] ? q[j].s[3] : NAN);
@@ -857,7 +858,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     }
     __syncthreads();
     // pass 1: fixed-point mass histogram over score buckets (bucket 0 = highest scores)
-    for (int base = kVec * tid; base < F; base += kTileE * kUnroll) {
+    for (int base = kVec * tid; base < Fm; base += kTileE * kUnroll) {
       Quad q[kUnroll];
 #pragma unroll
       for (int j = 0; j < kUnroll; ++j) q[j] = get(base + j * kTileE);
@@ -904,7 +905,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const uint32_t nb = sh.hc[bstar];
     if (nb <= (uint32_t)kCand) {
       // gather the boundary bucket, sort it by rank key, scan its masses
-      for (int base = kVec * tid; base < F; base += kTileE * kUnroll) {
+      for (int base = kVec * tid; base < Fm; base += kTileE * kUnroll) {
         Quad q[kUnroll];
 #pragma unroll
         for (int j = 0; j < kUnroll; ++j) q[j] = get(base + j * kTileE);
@@ -980,7 +981,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
       for (int shift = 56; shift >= 0; shift -= 8) {
         for (int i = tid; i < 256; i += kSelThreads) sh.hm[i] = 0ull;
         __syncthreads();
-        for (int k0 = kVec * tid; k0 < F; k0 += kTileE) {
+        for (int k0 = kVec * tid; k0 < Fm; k0 += kTileE) {
           const Quad q = get(k0);
 #pragma unroll
           for (int i = 0; i < kVec; ++i) {
@@ -1028,9 +1029,9 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   // ceil(anchor / b) frontier entries: entry k is node k)
   if (level == 1 && tid == 0) {
     int dup = 0;
-    const int lim = min(F, (anchor + b - 1) / b);
+    const int lim = min(Fm, (anchor + b - 1) / b);
     for (int k = 0; k < lim; ++k) {
-      const bool in = pmask ? ((pmask[geo.bdiv.div((uint32_t)k)] >> m) & 1u) : k < Fm;
+      const bool in = !pmask || ((pmask[geo.bdiv.div((uint32_t)k)] >> m) & 1u);
       if (keep_of(Sq[k], in, k) && k * b < anchor) dup += min(b, anchor - k * b);
     }
     sh.scalar_u32[2] = (uint32_t)dup;
@@ -1577,13 +1578,13 @@ __global__ __launch_bounds__(kWideThreads) void wide_hist_kernel(
   const int qh = blockIdx.y, chunk = blockIdx.x;
   int u, m;
   unit_member_of(geo, qh, &u, &m);
-  const int F = fr.F;
+  const int F = unit_entries(geo, fr, u);
   const int c0 = chunk * kWideChunk;
   if (c0 >= F) return;
   const int tid = threadIdx.x;
   const float* Sq = S + (int64_t)qh * S_stride;
   const uint32_t* pmask = parent_masks(fr, u);
-  const int Fm = fr.pbits ? F : min(F, head_ntop(geo, qh));  // the member's frontier
+  const int Fm = member_entries(geo, fr, qh);  // the member's frontier lies below Fm
   const int end = min(Fm, c0 + kWideChunk);
   Quad q[kWideTiles];
   if (pmask && geo.b % 4 == 0) {
@@ -1665,16 +1666,17 @@ __global__ __launch_bounds__(NT, kCutMinWaves) void wide_cut_kernel(
   int u, m;
   unit_member_of(geo, qh, &u, &m);
   const int b = geo.b;
-  const int F = fr.F;
+  // the unit's frontier lies below F, the member's below Fm; its kept bits are written for
+  // all fr.F entries of the level
+  const int F = unit_entries(geo, fr, u);
   const int nch = (F + kWideChunk - 1) / kWideChunk;
   const float* Sq = S + (int64_t)qh * S_stride;
   const uint32_t* pmask = parent_masks(fr, u);
-  // the member's own frontier: at the top level, the top nodes complete for it
   const int vis = head_vis(geo, qh);
-  const int Fm = fr.pbits ? F : min(F, vis / geo.top_span);
+  const int Fm = member_entries(geo, fr, qh);
   anchor = min(anchor, vis);
   uint32_t* krow = kb.bits ? kb.bits + (int64_t)qh * kb.words : nullptr;
-  const int kwords = (F + 31) / 32;
+  const int kwords = (fr.F + 31) / 32;
   // a member with no entry at this level (it kept nothing above: no complete top node)
   // selects nothing; no entry scores above an infinite cut. Called block-uniformly.
   auto empty_result = [&]() {
@@ -2041,9 +2043,9 @@ __global__ __launch_bounds__(NT, kCutMinWaves) void wide_cut_kernel(
     // entries: entry k is node k)
     int dup = 0;
     if (level == 1) {
-      const int lim = min(F, (anchor + b - 1) / b);
+      const int lim = min(Fm, (anchor + b - 1) / b);
       for (int k = 0; k < lim; ++k) {
-        const bool in = pmask ? ((pmask[geo.bdiv.div((uint32_t)k)] >> m) & 1u) : k < Fm;
+        const bool in = !pmask || ((pmask[geo.bdiv.div((uint32_t)k)] >> m) & 1u);
         const float sk = Sq[k];
         if (in && (sk > s_cut || (sk == s_cut && (uint32_t)k <= k_cut)) && k * b < anchor)
           dup += min(b, anchor - k * b);
@@ -2070,7 +2072,7 @@ __global__ __launch_bounds__(kUnionThreads) void wide_union_kernel(
   __shared__ int s_lim[kMaxMembers];
   __shared__ uint32_t cnt[kUnionThreads / 64][kMaxMembers + 1];
   const int u = blockIdx.y, chunk = blockIdx.x;
-  const int F = fr.F;
+  const int F = unit_entries(geo, fr, u);
   const int c0 = chunk * kUnionChunk;
   if (c0 >= F) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -2080,7 +2082,7 @@ __global__ __launch_bounds__(kUnionThreads) void wide_union_kernel(
     const uint32_t* rec = w.cut + 4 * (int64_t)qh;
     s_cut[tid] = __uint_as_float(rec[0]);
     k_cut[tid] = rec[1];
-    s_lim[tid] = fr.pbits ? F : min(F, head_ntop(geo, qh));  // member's top frontier
+    s_lim[tid] = member_entries(geo, fr, qh);  // the member's frontier lies below this
   }
   int kk[8];
   uint32_t pm[8];
@@ -2181,7 +2183,7 @@ __global__ __launch_bounds__(kUnionThreads) void wide_write_kernel(
   __shared__ uint32_t s_stage[NW][64];  // a wave's kept nodes of 64 entries
   const int u = blockIdx.y, chunk = blockIdx.x;
   const int b = geo.b;
-  const int F = fr.F;
+  const int F = unit_entries(geo, fr, u);
   const int c0 = chunk * kUnionChunk;  // entry c0 + e is node c0 + e
   if (c0 >= F) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -2356,11 +2358,12 @@ constexpr int kEPT = kCompactChunk / kCompactThreads;  // entries per thread (16
 // mode 0: one workgroup walks every chunk of the unit. mode 1: count chunk blockIdx.x into
 // chunk_cnt. mode 2: write chunk blockIdx.x after the counts of the chunks before it.
 __global__ __launch_bounds__(kCompactThreads) void compact_kernel(
-    Geom geo, int F, KeepBits kb, LevelBufs cur, int mode, uint32_t* __restrict__ chunk_cnt,
+    Geom geo, Frontier fr, KeepBits kb, LevelBufs cur, int mode, uint32_t* __restrict__ chunk_cnt,
     int max_chunks) {
   __shared__ uint32_t sbits[kMaxMembers][kCompactChunk / 32];
   __shared__ uint32_t wave_sum[kCompactThreads / 64];
   const int u = blockIdx.y;
+  const int F = unit_entries(geo, fr, u);
   const int Mu = members_of(geo, u);
   uint32_t msk[kEPT];
   if (mode == 0) {
@@ -2495,16 +2498,16 @@ hipError_t launch_compact(const Geom& geo, const Frontier& fr, KeepBits kb, cons
   const int F = fr.F;
   const int max_chunks = (F + kCompactChunk - 1) / kCompactChunk;
   if (max_chunks <= 1) {
-    hipLaunchKernelGGL(compact_kernel, dim3(1, geo.U), dim3(kCompactThreads), 0, s, geo, F, kb,
+    hipLaunchKernelGGL(compact_kernel, dim3(1, geo.U), dim3(kCompactThreads), 0, s, geo, fr, kb,
                        cur, 0, chunk_cnt, 1);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(compact_kernel, dim3(max_chunks, geo.U), dim3(kCompactThreads), 0, s, geo,
-                     F, kb, cur, 1, chunk_cnt, max_chunks);
+                     fr, kb, cur, 1, chunk_cnt, max_chunks);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(compact_kernel, dim3(max_chunks, geo.U), dim3(kCompactThreads), 0, s, geo,
-                     F, kb, cur, 2, chunk_cnt, max_chunks);
+                     fr, kb, cur, 2, chunk_cnt, max_chunks);
   return hipGetLastError();
 }
 
