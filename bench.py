@@ -323,15 +323,25 @@ def main():
     decode_bytes = kv_bytes + int(c1.sum()) * 8 + QH * d * elem + QH * d * 4
     frontier_rows = 0
     score_bytes = {}
+    members = min(T, max(1, 16 // (Hq // Hkv))) * (Hq // Hkv)
     for lv in range(1, L + 1):
         if lv == L:
             rows = (N // b ** L) * U
+            scores = rows * members
         else:
-            rows = int(lists[lv + 1][2].sum()) * b
+            _, pmasks, pcount = lists[lv + 1]
+            rows = int(pcount.sum()) * b
+            # with b a multiple of 4 a member's scores are stored only over its own frontier
+            # (the children of the nodes it kept one level up); otherwise for every member
+            if b % 4 == 0:
+                kept = sum(int(np.unpackbits(pmasks[u, :pcount[u]].astype("<u4").view(np.uint8)).sum())
+                           for u in range(pmasks.shape[0]))
+                scores = kept * b
+            else:
+                scores = rows * members
         frontier_rows += rows
-        # each union-frontier row read once (float32), one score written per member
-        members = min(T, max(1, 16 // (Hq // Hkv))) * (Hq // Hkv)
-        score_bytes[lv] = rows * (d * 4 + 4 * members)
+        # each union-frontier row read once (float32), the members' scores written
+        score_bytes[lv] = rows * d * 4 + 4 * scores
     # a pooling launch that starts at level lv reads level lv - 1 once and writes every
     # level it fuses (b^k <= 64 rows per tile, as the library groups them)
     build_bytes = {}

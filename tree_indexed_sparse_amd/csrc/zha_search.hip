@@ -1046,6 +1046,32 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   // stores); at level 1 also the token list
   uint32_t running = 0;
   Quad qn = get(kVec * tid);  // the next tile's entries are loaded one tile ahead
+  if (level != 1) {
+    // kept flags only: the 8 threads of a word OR their 4-bit groups across lanes and one
+    // stores it; the kept count is summed once at the end
+    uint32_t mine = 0;
+    for (int t0 = 0; t0 < F; t0 += kTileE) {
+      const int k0 = t0 + kVec * tid;
+      const Quad q = qn;
+      qn = get(k0 + kTileE);
+      uint32_t kept_bits = 0;
+#pragma unroll
+      for (int i = 0; i < kVec; ++i) {
+        if (keep_of(q.s[i], q.in[i], k0 + i)) {
+          kept_bits |= 1u << i;
+          ++mine;
+        }
+      }
+      uint32_t wd = kept_bits << (4 * (tid % 8));
+      wd |= __shfl_xor(wd, 1, 64);
+      wd |= __shfl_xor(wd, 2, 64);
+      wd |= __shfl_xor(wd, 4, 64);
+      if (tid % 8 == 0 && k0 < F) kbits[k0 / 32] = wd;
+    }
+    block_excl_scan<kSelThreads>(mine, sh.wave_sum, &running);
+    if (tid == 0) lvl_kept[(int64_t)qh * (geo.L + 1) + level] = (int32_t)running;
+    return;
+  }
   for (int t0 = 0; t0 < F; t0 += kTileE) {
     const int k0 = t0 + kVec * tid;
     const Quad q = qn;
@@ -1132,7 +1158,6 @@ struct HeadTopShared {
   uint32_t kn[2][kTopMax];              // kept node lists (previous level / this level)
   unsigned long long hist[kTopBuckets]; // bucket masses; radix digit masses in the fallback
   uint32_t hcnt[kTopBuckets];
-  unsigned long long wsum[kTopWaves];
   uint32_t wcnt[kTopWaves];
   uint32_t bits[kTopWords];
   float red[kTopWaves];
@@ -1140,25 +1165,6 @@ struct HeadTopShared {
   unsigned long long scal64[2];
   uint32_t scal32[2];
 };
-
-// sum over the block of one u64 per thread (every thread gets it)
-template <int NT>
-__device__ __forceinline__ uint64_t top_block_sum(uint64_t v, unsigned long long* wsum) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const uint32_t lo = __shfl_xor((uint32_t)v, off, 64);
-    const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), off, 64);
-    v += ((uint64_t)hi << 32) | lo;
-  }
-  __syncthreads();
-  if (lane == 0) wsum[wave] = v;
-  __syncthreads();
-  uint64_t t = 0;
-#pragma unroll
-  for (int w = 0; w < (NT / 64); ++w) t += wsum[w];
-  return t;
-}
 
 template <int D, int NT>
 __device__ __forceinline__ void top_rows_load(f32x4_t (&x)[top_unroll<NT>()], const float* Xu,
@@ -1347,22 +1353,17 @@ __global__ __launch_bounds__(NT, kTopMinWaves) void head_top_kernel(
       mn = fminf(mn, sh.red_mn[w]);
     }
     uint64_t ms[EPT];
-    uint64_t msum = 0;
 #pragma unroll
-    for (int i = 0; i < EPT; ++i) {
-      ms[i] = in[i] ? mass_fixed(sv[i], mx) : 0ull;
-      msum += ms[i];
-    }
+    for (int i = 0; i < EPT; ++i) ms[i] = in[i] ? mass_fixed(sv[i], mx) : 0ull;
     bool keep[EPT];
 #pragma unroll
     for (int i = 0; i < EPT; ++i) keep[i] = in[i];
     if (!keep_all) {
-      const uint64_t Z = top_block_sum<NT>(msum, sh.wsum);
-      const uint64_t T = ceil_mul_p(p, Z);
-      // Mass histogram over score buckets below the max (bucket 0 = highest scores); the
-      // boundary bucket, where the cumulative mass reaches T, is gathered and sorted by
-      // rank key (score desc, index asc) when it is small, and its masses are scanned in
-      // that order to the exact cut: the kept set is every entry ranked at or above it.
+      // Mass histogram over score buckets below the max (bucket 0 = highest scores); its
+      // total is the frontier's mass Z, and the boundary bucket, where the cumulative mass
+      // reaches T = ceil(p Z), is gathered and sorted by rank key (score desc, index asc)
+      // when it is small, and its masses are scanned in that order to the exact cut: the
+      // kept set is every entry ranked at or above it.
       const float spread = fminf(mx - mn, kMaxSpread);
       const float scale = spread > 0.f ? (float)kTopBuckets / spread : 0.f;
 #pragma unroll
@@ -1380,6 +1381,8 @@ __global__ __launch_bounds__(NT, kTopMinWaves) void head_top_kernel(
 #pragma unroll
         for (int i = 0; i < per; ++i) loc += sh.hist[lane * per + i];
         const uint64_t incl = wave_incl_scan_u64(loc, lane);
+        const uint64_t T = ceil_mul_p(p, __shfl(incl, 63, 64));
+        if (lane == 0) sh.scal64[1] = T;
         const uint64_t excl = incl - loc;
         if (excl < T && incl >= T) {
           uint64_t run = excl;
@@ -1397,6 +1400,7 @@ __global__ __launch_bounds__(NT, kTopMinWaves) void head_top_kernel(
       __syncthreads();
       const int bstar = (int)sh.scal32[0];
       const uint64_t before = sh.scal64[0];
+      const uint64_t T = sh.scal64[1];
       const uint32_t nb = sh.hcnt[bstar];
       if (nb <= 64u) {
         // the scores were read into registers above, so the score array holds the
