@@ -33,7 +33,7 @@ constexpr int kScoreEntries = 2048;  // most frontier entries per workgroup (512
 
 constexpr int kSelThreads = 512;
 constexpr int kSelWaves = kSelThreads / 64;
-constexpr int kBuckets = 2048;
+constexpr int kBuckets = 512;
 constexpr int kCand = 2048;
 constexpr float kMaxSpread = 32.0f;             // exp(-32) * 2^42 < 1: lower masses are 0
 
@@ -1149,14 +1149,14 @@ struct TopLevels {
   int64_t xstride[ZHA_MAX_LEVELS + 1];  // floats per (sequence, KV head) at level l
 };
 
-constexpr int kTopBuckets = 1024;                // score buckets of the selection
+constexpr int kTopBuckets = 256;                 // score buckets of the selection
 static_assert(kTopMax * sizeof(float) >= 64 * sizeof(unsigned long long),
               "the score array holds the boundary bucket's candidate keys");
 
 struct HeadTopShared {
   float S[kTopMax];
   uint32_t kn[2][kTopMax];              // kept node lists (previous level / this level)
-  unsigned long long hist[kTopBuckets]; // bucket masses; radix digit masses in the fallback
+  unsigned long long hist[kTopBuckets > 256 ? kTopBuckets : 256];  // bucket / radix digit masses
   uint32_t hcnt[kTopBuckets];
   uint32_t wcnt[kTopWaves];
   uint32_t bits[kTopWords];
@@ -1536,7 +1536,8 @@ constexpr int kCutMinWaves = 4;
 constexpr int kUnionThreads = 256;
 constexpr int kUnionChunk = 2048;                   // union/write chunk: 8 entries per thread
 constexpr int64_t kWideMin = 16384;                 // frontiers of this size or more
-static_assert(kWB == kCutThreads, "the cut kernel gives each thread one bucket");
+static_assert(kWB <= kCutThreads || kWB % kCutThreads == 0,
+              "the cut kernel gives each thread one bucket, or a whole number of them");
 static_assert(kWideChunk % kTileE == 0, "histogram chunks hold whole tiles");
 static_assert(kUnionChunk == 8 * kUnionThreads, "union threads take two float4 per row");
 
@@ -1664,9 +1665,12 @@ __global__ __launch_bounds__(NT, kCutMinWaves) void wide_cut_kernel(
     int32_t* __restrict__ sel_count, int32_t* __restrict__ lvl_kept, WideSel w) {
   __shared__ CutShared sh;
   const int qh = blockIdx.x;
-  constexpr int BPT = kWB / NT;  // buckets per thread: thread t owns BPT t .. BPT t + BPT - 1
-  static_assert(BPT * NT == kWB, "whole buckets per thread");
+  // buckets per thread: thread t owns BPT t .. BPT t + BPT - 1 (threads past kWB / BPT own
+  // none)
+  constexpr int BPT = kWB >= NT ? kWB / NT : 1;
+  static_assert(BPT * NT >= kWB && kWB % BPT == 0, "whole buckets per thread");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const bool owner = BPT * tid < kWB;
   int u, m;
   unit_member_of(geo, qh, &u, &m);
   const int b = geo.b;
@@ -1712,7 +1716,7 @@ __global__ __launch_bounds__(NT, kCutMinWaves) void wide_cut_kernel(
     hb[j] = 0ull;
     cb[j] = 0u;
   }
-  const int64_t hbase = (int64_t)qh * w.nch * kWB + BPT * tid;
+  const int64_t hbase = (int64_t)qh * w.nch * kWB + BPT * (owner ? tid : 0);
   {
     int c = 0;
     for (; c + 4 <= nch; c += 4) {
@@ -1739,6 +1743,11 @@ __global__ __launch_bounds__(NT, kCutMinWaves) void wide_cut_kernel(
         hb[j] += w.hm[hbase + (int64_t)c * kWB + j];
         cb[j] += w.hc[hbase + (int64_t)c * kWB + j];
       }
+  }
+#pragma unroll
+  for (int j = 0; j < BPT; ++j) {
+    hb[j] = owner ? hb[j] : 0ull;
+    cb[j] = owner ? cb[j] : 0u;
   }
   uint64_t hsum = 0;
 #pragma unroll
