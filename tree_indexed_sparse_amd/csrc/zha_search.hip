@@ -1134,10 +1134,12 @@ constexpr int kTopMax = 4096;                    // frontier entries the kernel 
 constexpr int kTopFuse = 1024;                   // levels of at most this many nodes are fused
 constexpr int kTopEPT = kTopMax / kTopThreads;   // entries per thread (consecutive)
 static_assert(kTopEPT % 4 == 0, "threads read their scores as float4");
-// row loads per lane per batch: 8 at kTopThreads, so a CU has the same rows in flight
-// with one workgroup of kTopThreads or two of half that size
+// row loads per lane per batch: 4 at kTopThreads, so a CU has the same rows in flight
+// with one workgroup of kTopThreads or two of half that size (8 spilled registers and
+// measured slower: 38.7 against 33.5 us for the top levels at 256K deep; 2 and 3 measured
+// the same as 4)
 template <int NT>
-constexpr int top_unroll() { return 8 * NT / kTopThreads; }
+constexpr int top_unroll() { return 4 * NT / kTopThreads; }
 // The kernel fits in 128 VGPRs, four waves per SIMD: one workgroup of kTopThreads per
 // CU, or two of kTopThreads / 2. The smaller one runs when there are more query heads than
 // CUs, so that two heads share a CU and each hides the other's barriers and load latency.
