@@ -2195,7 +2195,7 @@ __global__ __launch_bounds__(kUnionThreads) void wide_write_kernel(
   constexpr int kPerWave = kUnionChunk / NW;
   __shared__ uint32_t s_um[kUnionChunk];
   __shared__ uint32_t wtot[NW];
-  __shared__ uint32_t s_stage[NW][64];  // a wave's kept nodes of 64 entries
+  __shared__ uint32_t s_stage[NW][8 * 64];  // a wave's kept nodes of 8 x 64 entries
   const int u = blockIdx.y, chunk = blockIdx.x;
   const int b = geo.b;
   const int F = unit_entries(geo, fr, u);
@@ -2251,26 +2251,27 @@ __global__ __launch_bounds__(kUnionThreads) void wide_write_kernel(
     int32_t* sel = sel_idx + (int64_t)qh * cap;
     uint32_t mpos = wave_prefix_total(w.mcnt + (int64_t)qh * w.nuc, chunk, lane);
     uint32_t* stage = s_stage[wave];
-    for (int r = 0; r < kUnionChunk / 64; ++r) {
-      // the member's kept nodes of these 64 entries, in order, then their tokens
-      const int e = 64 * r + lane;
-      const bool kept = (s_um[e] >> mm) & 1u;
-      const uint64_t bal = __ballot(kept);
-      if (kept) stage[__popcll(bal & ((1ull << lane) - 1ull))] = (uint32_t)(c0 + e);
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      // one token per lane: each store covers up to 256 contiguous bytes (a short run: the
-      // aligned 16-byte form costs more than it saves here)
-      const int ntok = __popcll(bal) * b;
-      int32_t* dst = sel + tok_base + (int64_t)mpos * b;
-      for (int j = lane; j < ntok; j += 64) {
-        const int q = (int)geo.bdiv.div((uint32_t)j);
-        const int tok = (int)stage[q] * b + (j - q * b);
-        if (tok >= anc) dst[j] = tok;
+    // the member's kept nodes of 8 x 64 entries, in order (ballots), then their tokens as
+    // one run of 16-byte aligned stores (4-byte stores at its ends): 4 to 32 times fewer
+    // store instructions than one token per lane per 64 entries (union and write 34.9 ->
+    // 31.6 us at 256K deep; runs of 4 x 64 and 32 x 64 entries measured slower)
+    for (int r0 = 0; r0 < kUnionChunk / 64; r0 += 8) {
+      uint32_t n = 0;
+#pragma unroll
+      for (int r = r0; r < r0 + 8; ++r) {
+        const int e = 64 * r + lane;
+        const bool kept = (s_um[e] >> mm) & 1u;
+        const uint64_t bal = __ballot(kept);
+        if (kept) stage[n + __popcll(bal & ((1ull << lane) - 1ull))] = (uint32_t)(c0 + e);
+        n += (uint32_t)__popcll(bal);
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      mpos += (uint32_t)__popcll(bal);
+      write_token_run(sel + tok_base + (int64_t)mpos * b, (int)n * b, stage, geo.bdiv, anc, lane,
+                      64);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      mpos += n;
     }
   }
 }
