@@ -1130,10 +1130,9 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
 //           prefix as the other selection paths.
 constexpr int kTopThreads = 1024;
 constexpr int kTopWaves = kTopThreads / 64;
-constexpr int kTopMax = 4096;                    // frontier entries the kernel holds
 constexpr int kTopFuse = 1024;                   // levels of at most this many nodes are fused
-constexpr int kTopEPT = kTopMax / kTopThreads;   // entries per thread (consecutive)
-static_assert(kTopEPT % 4 == 0, "threads read their scores as float4");
+// frontier entries the kernel holds: a fused level's frontier holds at most its nodes
+constexpr int kTopMax = kTopFuse;
 // row loads per lane per batch: 4 at kTopThreads, so a CU has the same rows in flight
 // with one workgroup of kTopThreads or two of half that size (8 spilled registers and
 // measured slower: 38.7 against 33.5 us for the top levels at 256K deep; 2 and 3 measured
@@ -1251,7 +1250,7 @@ __global__ __launch_bounds__(NT, kTopMinWaves) void head_top_kernel(
     const Tq* __restrict__ Q, float p, float sigma, int32_t* __restrict__ lvl_kept,
     uint32_t* __restrict__ bitmaps, RouterView rv) {
   constexpr int EPT = kTopMax / NT;       // entries per thread (consecutive)
-  static_assert(EPT % 4 == 0, "threads read their scores as float4");
+  static_assert(EPT >= 1 && EPT * NT == kTopMax, "whole entries per thread");
   constexpr int LPR = D / 4;              // lanes per row
   constexpr int RPW = 64 / LPR;           // rows per wave-wide load
   constexpr int STEP = RPW * (NT / 64) * top_unroll<NT>();  // rows per batch
@@ -1315,13 +1314,7 @@ __global__ __launch_bounds__(NT, kTopMinWaves) void head_top_kernel(
     const int k0 = EPT * tid;
     float sv[EPT];
 #pragma unroll
-    for (int i = 0; i < EPT; i += 4) {
-      const float4 v = *reinterpret_cast<const float4*>(&sh.S[k0 + i]);
-      sv[i] = v.x;
-      sv[i + 1] = v.y;
-      sv[i + 2] = v.z;
-      sv[i + 3] = v.w;
-    }
+    for (int i = 0; i < EPT; ++i) sv[i] = sh.S[k0 + i];
     bool in[EPT];
     float mx = -INFINITY, mn = INFINITY;
 #pragma unroll
