@@ -108,6 +108,34 @@ def test_causal_matches_oracle(case):
     _check(spec, name, p, anchor, pos, n_tokens=n_tokens)
 
 
+def test_unit_whose_queries_see_no_complete_top_node():
+    """The chunked level-1 path with a unit that searches nothing: sequence 1's two queries
+    sit before the first complete top node (4,096 tokens) while sequence 0's reach the
+    chunked frontiers, so sequence 1's units keep no node at any level and each of their
+    queries attends its whole prefix. The workspace starts filled with a small nonzero
+    pattern (every word 5), so a union count or list that the call failed to write would
+    show up as extra keys attended."""
+    Z = _Z()
+    spec = W.spec("32k_deep", N=65536, B=2, T=2)
+    pos = np.array([[65535, 40000], [3000, 100]], np.int32)
+    inp = W.gen_all(spec, device="cuda")
+    tree = Z.build_tree(inp["K"], inp["R"], spec["b"], spec["L"])
+    need = Z.workspace_bytes(tree, spec["T"], spec["Hq"])
+    ws = torch.full(((need + 3) // 4,), 5, dtype=torch.int32, device="cuda").view(torch.uint8)
+    O_, sel, cnt = Z.attend(inp["Q"], inp["K"], inp["V"], tree, 0.95, 1, workspace=ws,
+                            positions=torch.from_numpy(pos).cuda())
+    torch.cuda.synchronize()
+    res = dict(tree=tree, O=O_.cpu().numpy(), sel=sel.cpu().numpy(), cnt=cnt.cpu().numpy(),
+               lists={l: Z.level_view(tree, spec["T"], spec["Hq"], l, ws)
+                      for l in range(1, spec["L"] + 1)}, inputs=inp)
+    for t in range(spec["T"]):  # dense over the prefix: every token up to the position
+        assert (res["cnt"][1, t] == pos[1, t] + 1).all()
+    reps, pyr = H.check_units(spec, res, 0.95, anchor=1, positions=pos)
+    summ = C.summarize(reps)
+    print(f"[empty unit] pyramid {pyr:.2e}; {summ}", flush=True)
+    H.assert_parity(spec, summ, pyr)
+
+
 def test_causal_fp4_router():
     Z = _Z()
     spec = W.spec("32k_deep", N=8192, B=1, Hq=8, Hkv=2, T=4)

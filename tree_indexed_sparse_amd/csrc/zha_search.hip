@@ -2193,7 +2193,11 @@ __global__ __launch_bounds__(kUnionThreads) void wide_write_kernel(
   const int b = geo.b;
   const int F = unit_entries(geo, fr, u);
   const int c0 = chunk * kUnionChunk;  // entry c0 + e is node c0 + e
-  if (c0 >= F) return;
+  if (c0 >= F) {
+    // a unit whose queries see no complete top node has an empty list
+    if (F == 0 && chunk == 0 && blockIdx.z == 0 && threadIdx.x == 0) cur.count[u] = 0u;
+    return;
+  }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int Mu = members_of(geo, u);
   const int nchunks = (F + kUnionChunk - 1) / kUnionChunk;
