@@ -27,8 +27,9 @@
  *     workspace 256-byte aligned (hipMalloc returns 256-byte aligned memory); other
  *     pointers are rejected with ZHA_ERR_INVALID_ARG.
  *   - Supported: d in {64, 128}; dtype ZHA_F32 or ZHA_BF16 (K, V, Q and the reference
- *     queries share one dtype); b >= 2; 1 <= L <= ZHA_MAX_LEVELS; N_cap % b^L == 0 (any
- *     N <= N_cap); Hq % Hkv == 0 and Hq / Hkv <= 16; N_cap / b <= 2^21.
+ *     queries share one dtype); b >= 2; 1 <= L <= ZHA_MAX_LEVELS; b^L <= 2^31;
+ *     N_cap % b^L == 0 (any N <= N_cap); Hq % Hkv == 0 and Hq / Hkv <= 16;
+ *     N_cap / b <= 2^21.
  */
 #ifndef ZHA_H_
 #define ZHA_H_
@@ -44,7 +45,8 @@ typedef enum {
   ZHA_OK = 0,
   ZHA_ERR_INVALID_ARG = -1, /* null or misaligned pointer, p not in (0, 1], anchor out of
                                range, b < 2, L < 1, unknown router or no router copy */
-  ZHA_ERR_SHAPE = -2,       /* N_cap % b^L != 0, Hq % Hkv != 0, N > N_cap, buffer too small */
+  ZHA_ERR_SHAPE = -2,       /* b^L > 2^31, N_cap % b^L != 0, Hq % Hkv != 0, N > N_cap,
+                               buffer too small */
   ZHA_ERR_DTYPE = -3,       /* unknown dtype */
   ZHA_ERR_CAPACITY = -4,    /* selected-list capacity smaller than N */
   ZHA_ERR_UNSUPPORTED = -5, /* d not in {64, 128}, Hq / Hkv > 16, L > ZHA_MAX_LEVELS, N / b > 2^21 */

@@ -48,6 +48,25 @@ def test_tree_bytes_closed_form(lib):
     assert lib.zha_tree_bytes(1, 1, 4096, 64, 1, 3) == 0      # b < 2
 
 
+@pytest.mark.parametrize("b,Ll,n_cap", [(65536, 4, 65536), (1024, 12, 1 << 20),
+                                        (2 ** 31 - 1, 2, 4096), (46341, 2, 4096),
+                                        (7, 12, 7 ** 11)])
+def test_geometry_with_b_pow_L_past_2_pow_31_is_an_error(lib, b, Ll, n_cap):
+    # b^L wraps 64 bits for the first two (65536^4 = 2^64): the check must stop the power
+    # at 2^31 instead of dividing by a wrapped zero
+    assert lib.zha_tree_bytes(1, 1, n_cap, 64, b, Ll) == 0
+    assert lib.zha_router_bytes(1, 1, n_cap, 64, b, Ll) == 0
+    assert _build(lib, N=0, N_cap=n_cap, b=b, L=Ll) == -2
+    assert "exceeds 2^31" in lib.zha_last_error().decode()
+    assert _attend(lib, t=_tree(N=0, N_cap=n_cap, b=b, L=Ll)) == -2
+
+
+def test_geometry_with_b_pow_L_just_inside_passes_the_power_check(lib):
+    # b^L = 2^30 tokens per top node is accepted; 2^32 is not
+    assert lib.zha_tree_bytes(1, 1, 2 ** 30, 64, 2 ** 15, 2) > 0
+    assert lib.zha_tree_bytes(1, 1, 2 ** 30, 64, 2 ** 16, 2) == 0
+
+
 def _build(lib, **kw):
     a = dict(K=FAKE, R=FAKE, dtype=1, B=1, Hkv=1, N=4096, N_cap=4096, d=64, b=4, L=3,
              pyr=FAKE, nbytes=1 << 30)
@@ -180,6 +199,9 @@ def test_dense_workspace_bytes(lib):
     assert n >= 16 * 16 * 130 * 4          # one (d + 2)-float partial per member and split
     assert lib.zha_dense_workspace_bytes(1, 1, 0, 4096, 64, 1, 1) == 0
     assert lib.zha_dense_workspace_bytes(1, 1, 4096, 4096, 96, 1, 1) == 0
+    # the documented bound N <= 2^21
+    assert lib.zha_dense_workspace_bytes(1, 1, 2 ** 21, 2 ** 21, 64, 1, 1) > 0
+    assert lib.zha_dense_workspace_bytes(1, 1, 2 ** 21 + 1, 2 ** 22, 64, 1, 1) == 0
 
 
 def test_router_bytes_closed_form(lib):

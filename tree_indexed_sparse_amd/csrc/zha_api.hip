@@ -87,8 +87,14 @@ int check_geometry(int B, int Hkv, int N, int N_cap, int d, int b, int L) {
   if (L > ZHA_MAX_LEVELS)
     return fail(ZHA_ERR_UNSUPPORTED, "levels L must be <= %d (got %d)", ZHA_MAX_LEVELS, L);
   if (d != 64 && d != 128) return fail(ZHA_ERR_UNSUPPORTED, "head dim must be 64 or 128 (got %d)", d);
-  const int64_t top = ipow(b, L);
-  if (top > (int64_t)1 << 31) return fail(ZHA_ERR_SHAPE, "b^L overflows");
+  // b^L, stopping as soon as it passes 2^31 (each factor is below 2^31, so no product
+  // overflows 64 bits)
+  int64_t top = 1;
+  for (int i = 0; i < L; ++i) {
+    top *= b;
+    if (top > (int64_t)1 << 31)
+      return fail(ZHA_ERR_SHAPE, "b^L = %d^%d exceeds 2^31 tokens per top node", b, L);
+  }
   if (N_cap < 1 || N_cap % top != 0)
     return fail(ZHA_ERR_SHAPE, "cache capacity N_cap=%d must be a positive multiple of b^L=%lld",
                 N_cap, (long long)top);
@@ -468,6 +474,8 @@ int dense_geom(int B, int Hkv, int N, int N_cap, int d, int T, int Hq, Geom* g) 
   if (B < 1 || Hkv < 1) return fail(ZHA_ERR_SHAPE, "B and Hkv must be >= 1 (got %d, %d)", B, Hkv);
   if (d != 64 && d != 128) return fail(ZHA_ERR_UNSUPPORTED, "head dim must be 64 or 128 (got %d)", d);
   if (N < 1 || N > N_cap) return fail(ZHA_ERR_SHAPE, "N=%d must lie in [1, N_cap=%d]", N, N_cap);
+  if (N > (1 << kMaxLog2Nodes))
+    return fail(ZHA_ERR_UNSUPPORTED, "N=%d must be <= 2^%d", N, kMaxLog2Nodes);
   zha_tree t{};
   t.B = B;
   t.Hkv = Hkv;
