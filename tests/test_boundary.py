@@ -123,6 +123,16 @@ def test_attend_rejects_bad_arguments(lib, kw, code):
     assert len(lib.zha_last_error()) > 0
 
 
+def test_attend_rejects_query_head_counts_past_int32(lib):
+    # B * T * Hq = 2 * 2^26 * 16 = 2^31 query heads: numbered in int32, so rejected on the
+    # host (before, the product wrapped negative and the workspace check passed)
+    t = _tree(B=2, Hkv=2)
+    assert _attend(lib, t=t, T=2 ** 26, Hq=16) == -5
+    assert "exceeds 2^31 - 1" in lib.zha_last_error().decode()
+    assert lib.zha_attend_workspace_bytes(ctypes.byref(t), 2 ** 26, 16) == 0
+    assert lib.zha_attend_workspace_bytes(ctypes.byref(t), 2 ** 20, 16) > 0
+
+
 def test_attend_rejects_bad_trees(lib):
     assert _attend(lib, t=_tree(d=80)) == -5
     assert _attend(lib, t=_tree(N=4100)) == -2       # N > N_cap

@@ -128,6 +128,10 @@ int make_geom(const zha_tree* t, int T, int Hq, Geom* g) {
   const int G = Hq / t->Hkv;
   if (G > kMaxMembers)
     return fail(ZHA_ERR_UNSUPPORTED, "Hq / Hkv = %d exceeds %d", G, kMaxMembers);
+  // query heads are numbered in int32 (kernel indices, workspace rows)
+  if ((int64_t)t->B * T * Hq > INT32_MAX)
+    return fail(ZHA_ERR_UNSUPPORTED, "B * T * Hq = %lld query heads exceeds 2^31 - 1",
+                (long long)t->B * T * Hq);
   g->B = t->B;
   g->T = T;
   g->Hq = Hq;
