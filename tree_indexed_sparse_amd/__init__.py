@@ -56,6 +56,39 @@ def _stream(device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
+def _shape(t: torch.Tensor, name: str, want: tuple, dtype=None) -> None:
+    """Raise unless t has shape `want` (None entries match any size) and, if given, dtype.
+    The library takes bare pointers, so a tensor smaller than the call implies would be
+    read or written out of bounds on the GPU: the checks run on the host, before the call."""
+    got = tuple(t.shape)
+    if len(got) != len(want) or any(w is not None and g != w for g, w in zip(got, want)):
+        shown = ", ".join("*" if w is None else str(w) for w in want)
+        raise ZhaError(-2, f"{name} has shape {list(got)}, expected [{shown}]")
+    if dtype is not None and t.dtype != dtype:
+        raise ZhaError(-3, f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
+def _same_device(device, **tensors) -> None:
+    for name, t in tensors.items():
+        if t is not None and t.device != device:
+            raise ZhaError(-1, f"{name} is on {t.device}, expected {device}")
+
+
+def _nbytes(t: torch.Tensor) -> int:
+    return t.numel() * t.element_size()
+
+
+def _check_kv(tree: "Tree", K: torch.Tensor, V: torch.Tensor | None = None) -> None:
+    """K (and V) must be the cache the tree indexes: [B, Hkv, N_cap, d] in its dtype."""
+    c = tree.c
+    want = (int(c.B), int(c.Hkv), int(c.N_cap), int(c.d))
+    _shape(K, "K", want)
+    if _DTYPES.get(K.dtype) != int(c.dtype):
+        raise ZhaError(-3, f"K has dtype {K.dtype}; the tree was built from another dtype")
+    if V is not None:
+        _shape(V, "V", want, K.dtype)
+
+
 def tree_bytes(B: int, Hkv: int, N_cap: int, d: int, b: int, L: int) -> int:
     return int(load().zha_tree_bytes(B, Hkv, N_cap, d, b, L))
 
@@ -98,10 +131,13 @@ def build_tree(K: torch.Tensor, R: torch.Tensor, b: int, L: int, N: int | None =
     empty, given its copy (zha_router_quantize), and extended by N tokens
     (zha_tree_append), so the pooling launches encode the rows they write."""
     lib = load()
+    _shape(K, "K", (None, None, None, None))
     B, Hkv, N_cap, d = K.shape
     N = N_cap if N is None else N
     if R.dtype != K.dtype:
         raise ZhaError(-3, "K and R must share a dtype")
+    _shape(R, "R", (Hkv, ZHA_N_REF, d))
+    _same_device(K.device, R=R)
     nbytes = tree_bytes(B, Hkv, N_cap, d, b, L)
     storage = torch.empty(max(nbytes, 4), dtype=torch.uint8, device=K.device)
     c = ZhaTree()
@@ -117,6 +153,9 @@ def build_tree(K: torch.Tensor, R: torch.Tensor, b: int, L: int, N: int | None =
 
 def tree_append(tree: Tree, K: torch.Tensor, R: torch.Tensor, n_new: int) -> None:
     """zha_tree_append: pool tokens [N, N + n_new) and extend the tree."""
+    _check_kv(tree, K)
+    _shape(R, "R", (int(tree.c.Hkv), ZHA_N_REF, int(tree.c.d)), K.dtype)
+    _same_device(tree.storage.device, K=K, R=R)
     check(load().zha_tree_append(ctypes.byref(tree.c), _dev(K, "K"), _dev(R, "R"), n_new,
                                  _stream(K.device)))
 
@@ -173,16 +212,34 @@ def workspace_bytes(tree: Tree, T: int, Hq: int) -> int:
     return int(load().zha_attend_workspace_bytes(ctypes.byref(tree.c), T, Hq))
 
 
+def _check_outputs(B, T, Hq, d, out, sel_idx, sel_count, required=False) -> None:
+    """Caller-supplied outputs: O [B, T, Hq, d] float32, sel_idx [B, T, Hq, cap] int32 (the
+    library checks cap against N), sel_count [B, T, Hq] int32."""
+    if required and (out is None or sel_count is None):
+        raise ZhaError(-1, "out and sel_count must be given")
+    if out is not None:
+        _shape(out, "out", (B, T, Hq, d), torch.float32)
+    if sel_idx is not None:
+        _shape(sel_idx, "sel_idx", (B, T, Hq, None), torch.int32)
+    if sel_count is not None:
+        _shape(sel_count, "sel_count", (B, T, Hq), torch.int32)
+
+
 def attend(Q, K, V, tree: Tree, p: float, anchor: int = 1, *, want_lists: bool = True,
            out=None, sel_idx=None, sel_count=None, workspace=None, positions=None):
     """zha_attend (or zha_attend_causal when `positions`, an int32 device tensor [B, T] of
     query positions, is given). Returns (O [B,T,Hq,d] float32, sel_idx [B,T,Hq,N] int32 or
     None, sel_count [B,T,Hq] int32). Buffers may be passed in to avoid allocation."""
     lib = load()
+    _check_kv(tree, K, V)
+    _shape(Q, "Q", (int(tree.c.B), None, None, int(tree.c.d)))
     B, T, Hq, d = Q.shape
     dev = Q.device
     if Q.dtype != K.dtype or V.dtype != K.dtype:
         raise ZhaError(-3, "Q, K and V must share a dtype")
+    _check_outputs(B, T, Hq, d, out, sel_idx, sel_count)
+    _same_device(dev, K=K, V=V, out=out, sel_idx=sel_idx, sel_count=sel_count,
+                 workspace=workspace, positions=positions, pyramid=tree.storage)
     if out is None:
         out = torch.empty((B, T, Hq, d), dtype=torch.float32, device=dev)
     cap = tree.N
@@ -200,13 +257,13 @@ def attend(Q, K, V, tree: Tree, p: float, anchor: int = 1, *, want_lists: bool =
         check(lib.zha_attend(ctypes.byref(tree.c), _dev(Q, "Q"), T, Hq, _dev(K, "K"),
                              _dev(V, "V"), float(p), int(anchor), _dev(out, "O"), sel_ptr, cap,
                              _dev(sel_count, "sel_count"), _dev(workspace, "workspace"),
-                             workspace.numel(), _stream(dev)))
+                             _nbytes(workspace), _stream(dev)))
     else:
         check(lib.zha_attend_causal(ctypes.byref(tree.c), _dev(Q, "Q"), T, Hq,
                                     _positions(positions, B, T), _dev(K, "K"), _dev(V, "V"),
                                     float(p), int(anchor), _dev(out, "O"), sel_ptr, cap,
                                     _dev(sel_count, "sel_count"), _dev(workspace, "workspace"),
-                                    workspace.numel(), _stream(dev)))
+                                    _nbytes(workspace), _stream(dev)))
     attend.last_workspace = workspace
     return out, sel_idx, sel_count
 
@@ -217,9 +274,14 @@ def attend_noalloc(Q, K, V, tree: Tree, p: float, anchor: int = 1, *, out, sel_i
     workspace; the caller passes the outputs (O [B,T,Hq,d] float32, sel_idx [B,T,Hq,cap]
     int32 or None, sel_count [B,T,Hq] int32), so nothing is allocated."""
     lib = load()
+    _check_kv(tree, K, V)
+    _shape(Q, "Q", (int(tree.c.B), None, None, int(tree.c.d)))
     B, T, Hq, d = Q.shape
     if Q.dtype != K.dtype or V.dtype != K.dtype:
         raise ZhaError(-3, "Q, K and V must share a dtype")
+    _check_outputs(B, T, Hq, d, out, sel_idx, sel_count, required=True)
+    _same_device(Q.device, K=K, V=V, out=out, sel_idx=sel_idx, sel_count=sel_count,
+                 pyramid=tree.storage)
     cap = sel_idx.shape[-1] if sel_idx is not None else tree.N
     sel_ptr = _dev(sel_idx, "sel_idx") if sel_idx is not None else None
     check(lib.zha_attend_noalloc(ctypes.byref(tree.c), _dev(Q, "Q"), T, Hq, _dev(K, "K"),
@@ -243,12 +305,18 @@ def dense_attend(Q, K, V, N: int | None = None, *, out=None, workspace=None, pos
     zha_dense_attend_causal over keys [0, position] when `positions` [B, T] is given.
     K, V [B,Hkv,N_cap,d]; returns O [B,T,Hq,d] float32."""
     lib = load()
+    _shape(Q, "Q", (None, None, None, None))
+    _shape(K, "K", (Q.shape[0], None, None, Q.shape[3]))
+    _shape(V, "V", tuple(K.shape))
     B, T, Hq, d = Q.shape
     _, Hkv, N_cap, _ = K.shape
     N = N_cap if N is None else N
     dev = Q.device
     if Q.dtype != K.dtype or V.dtype != K.dtype:
         raise ZhaError(-3, "Q, K and V must share a dtype")
+    if out is not None:
+        _shape(out, "out", (B, T, Hq, d), torch.float32)
+    _same_device(dev, K=K, V=V, out=out, workspace=workspace, positions=positions)
     if out is None:
         out = torch.empty((B, T, Hq, d), dtype=torch.float32, device=dev)
     need = dense_workspace_bytes(B, Hkv, N, N_cap, d, T, Hq)
@@ -257,12 +325,12 @@ def dense_attend(Q, K, V, N: int | None = None, *, out=None, workspace=None, pos
     if positions is None:
         check(lib.zha_dense_attend(_dev(Q, "Q"), T, Hq, _dev(K, "K"), _dev(V, "V"), _dt(K), B,
                                    Hkv, N, N_cap, d, _dev(out, "O"), _dev(workspace, "workspace"),
-                                   workspace.numel(), _stream(dev)))
+                                   _nbytes(workspace), _stream(dev)))
     else:
         check(lib.zha_dense_attend_causal(_dev(Q, "Q"), T, Hq, _positions(positions, B, T),
                                           _dev(K, "K"), _dev(V, "V"), _dt(K), B, Hkv, N, N_cap, d,
                                           _dev(out, "O"), _dev(workspace, "workspace"),
-                                          workspace.numel(), _stream(dev)))
+                                          _nbytes(workspace), _stream(dev)))
     return out
 
 
