@@ -35,6 +35,15 @@ def assert_parity(spec, summ, pyr=0.0):
     assert pyr <= PYR_TOL, pyr
 
 
+def assert_exact_selection(summ):
+    """Every head's selected tokens equal the oracle's own unguided selection, and no
+    near-tie was resolved differently. The near-tie rule would allow such differences;
+    on the workloads that assert this none occurs, and since every kernel reduces in a
+    fixed order the outcome is the same on every run."""
+    assert summ["exact_unguided"] == summ["heads"], summ
+    assert summ["diverged_decisions"] == 0, summ
+
+
 def output_errors(got, want):
     """(max |got - want|, that over max |want|) for one head's output; a non-finite
     output counts as an infinite error."""

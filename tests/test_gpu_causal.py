@@ -224,3 +224,4 @@ def test_256k_deep_causal_sampled_units():
     summ = C.summarize(reps)
     print(f"[256k deep causal sampled] {summ}", flush=True)
     H.assert_parity(spec, summ)
+    H.assert_exact_selection(summ)

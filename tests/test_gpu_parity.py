@@ -69,6 +69,7 @@ def test_32k_deep_all_heads():
     summ = C.summarize(reps)
     _report("32k deep", summ, pyr)
     _assert_ok(spec, summ, pyr)
+    H.assert_exact_selection(summ)
     kr = np.array([r.keys for r in reps]) / spec["N"]
     print(f"[32k deep] keys read mean {100 * kr.mean():.1f}%", flush=True)
 
@@ -378,6 +379,8 @@ def test_256k_deep_every_unit():
     _report("256k deep, every unit", summ, pyr)
     assert summ["heads"] == spec["B"] * spec["Hq"]
     _assert_ok(spec, summ, pyr)
+    # every head has a decision inside the near-tie windows here; none resolves differently
+    H.assert_exact_selection(summ)
 
 
 @pytest.mark.parametrize("b,L,N", [(2, 12, 65536), (4, 8, 131072), (16, 4, 131072)])
@@ -499,6 +502,7 @@ def test_256k_wide_sampled_units(p):
     summ = C.summarize(reps)
     _report(f"256k wide sampled p={p}", summ, pyr)
     _assert_ok(spec, summ, pyr)
+    H.assert_exact_selection(summ)
 
 
 def test_1m_deep_sampled_units():

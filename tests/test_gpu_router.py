@@ -318,4 +318,4 @@ def test_256k_deep_fp4_sampled_units():
     res = H.run_gpu(spec, 0.95, inputs=inp, tree=tree)
     reps, _ = H.check_units(spec, res, 0.95, units=[(0, 0), (3, 3)], oracle_levels=lv,
                             check_pyramid=False, fp4=True)
-    _summ_ok(spec, "256k deep fp4 sampled", reps)
+    H.assert_exact_selection(_summ_ok(spec, "256k deep fp4 sampled", reps))
