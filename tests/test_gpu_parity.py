@@ -383,6 +383,20 @@ def test_256k_deep_every_unit():
     H.assert_exact_selection(summ)
 
 
+def test_256k_deep_agreeing_heads_sampled_units():
+    """The 256K deep workload's keys with queries whose heads agree and whose scores are
+    sharp (about 1.1% of the keys read per head, 5% per KV head): small frontiers at every
+    level, a short union list for the decode; every head of three units."""
+    spec = W.spec("256k_deep_agree")
+    res = H.run_gpu(spec, 0.95)
+    reps, pyr = H.check_units(spec, res, 0.95, units=[(0, 0), (1, 2), (3, 3)])
+    summ = C.summarize(reps)
+    _report("256k deep agreeing heads, sampled", summ, pyr)
+    _assert_ok(spec, summ, pyr)
+    kr = np.array([r.keys for r in reps]) / spec["N"]
+    print(f"[256k deep agreeing heads] keys read mean {100 * kr.mean():.2f}%", flush=True)
+
+
 @pytest.mark.parametrize("b,L,N", [(2, 12, 65536), (4, 8, 131072), (16, 4, 131072)])
 def test_sweep_geometries(b, L, N):
     """Tree geometries of the geometry sweep beyond the two the benchmark runs: binary

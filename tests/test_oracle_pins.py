@@ -350,6 +350,33 @@ def test_workload_recipe_shapes_and_needles():
     assert torch.equal(torch.from_numpy(K2).to(torch.bfloat16).float(), torch.from_numpy(K2))
 
 
+def test_agreeing_query_recipe():
+    """The agreeing-heads variant of the query recipe: the default draws are untouched;
+    q = scale (sqrt(1 - rho^2) eps + rho u) with u shared by the G heads of a KV head, so
+    heads of one group correlate at about rho^2, heads of different groups not at all, and
+    every coordinate has variance scale^2."""
+    import workloads as W
+
+    base = W.spec("256k_deep", N=4096, B=3, T=2)
+    Q0 = W.gen_Q(base)
+    assert np.array_equal(Q0, W.gen_Q(dict(base, q_shared=0.0, q_scale=1.0)))
+    s = dict(base, q_shared=0.9, q_scale=3.0, dtype="f32")
+    Q = W.gen_Q(s).astype(np.float64)
+    G = s["Hq"] // s["Hkv"]
+    same, other = [], []
+    for b in range(s["B"]):
+        for t in range(s["T"]):
+            for h in range(s["Hq"]):
+                for h2 in range(h + 1, s["Hq"]):
+                    c = np.corrcoef(Q[b, t, h], Q[b, t, h2])[0, 1]
+                    (same if h // G == h2 // G else other).append(c)
+    assert abs(np.mean(same) - 0.81) < 0.03 and abs(np.mean(other)) < 0.03
+    assert abs(Q.std() - 3.0) < 0.05
+    # the named workload carries the recipe and the 256K deep keys and values
+    a = W.spec("256k_deep_agree")
+    assert (a["q_shared"], a["q_scale"], a["seed"], a["N"]) == (0.9, 3.0, 3, 262144)
+
+
 # ------------------------------------------------------------- ragged caches (tail)
 
 @pytest.mark.parametrize("b,L", [(4, 3), (2, 5), (8, 2)])

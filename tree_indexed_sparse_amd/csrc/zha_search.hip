@@ -13,11 +13,15 @@
 // member. Each member then selects over its own sub-frontier and records the nodes it
 // keeps as bits by node id. A level's frontier is indexed by node id: entry k is node k,
 // and its score launch ORs the members' bits of the parent k / b into the entry's member
-// mask, skipping the rows of entries no member reaches. Only level 1 is compacted, into
-// the kept-node list the decode reads and the members' token lists.
+// mask and scores only the rows of parents some member kept (with b a multiple of 4 each
+// workgroup lists its kept parents in LDS and walks their rows, so a sparse level costs
+// its kept rows, not the whole tree). Only level 1 is compacted in memory, into the
+// kept-node list the decode reads and the members' token lists.
 //
 // A level = a score and a select launch (plus the compaction at level 1). Kernel
 // boundaries order them; no kernel here uses a device-scope fence.
+
+#include <type_traits>
 
 #include "zha_internal.h"
 #include "zha_mxfp4.h"
@@ -387,8 +391,11 @@ __global__ __launch_bounds__(kScoreThreads) void score_rows_kernel(
   constexpr int kMaxParents = kRowEntries / 2 + 2;
   constexpr int kPw = (kMaxParents + 31) / 32 + 1;
   static_assert(M % NW == 0, "members spread evenly over the waves for the stores");
+  static_assert(kRowEntries / 4 <= kScoreThreads,
+                "with b a multiple of 4 a workgroup's whole parents fit one per thread");
   __shared__ uint32_t sPw[kMaxMembers * kPw];
   __shared__ uint32_t sPm[kMaxParents];
+  __shared__ uint16_t sKept[kMaxParents];  // the kept parents, ascending (compact mode)
   __shared__ float sS[M][kRowEntries];
 
   const int u = blockIdx.y;
@@ -409,9 +416,41 @@ __global__ __launch_bounds__(kScoreThreads) void score_rows_kernel(
 #pragma unroll
     for (int j = 0; j < NLD; ++j) load_q4(qr + 4 * LPR * j, &qv[m][4 * j]);
   }
+  // With b a multiple of 4 a member's scores are stored only over its own frontier (the
+  // children of the parents it kept), so the rows of parents no member kept are never
+  // needed: when the workgroup's range holds whole parents and at least an eighth of them
+  // were kept by no member, only the kept parents' rows are scored (compact mode), in
+  // ascending order. Otherwise every row of the range is (rows of unkept parents read row
+  // 0, a cached line, and their scores are not stored). The stored scores are the same
+  // either way.
+  const bool quad_parent = has_parent && geo.b % 4 == 0;
+  bool compact = false;
+  int n_rows = k_end - k_wg;  // rows scored by the workgroup
   if (has_parent) {
     const int np = (int)geo.bdiv.div((uint32_t)(k_end - 1)) - p0 + 1;
     stage_parent_masks<kScoreThreads>(geo, fr, u, Mu, p0, np, sPw, kPw, sPm);
+    if (quad_parent && k_wg % geo.b == 0 && k_end % geo.b == 0) {
+      // whole parents: np = (k_end - k_wg) / b <= kRowEntries / 4 = kScoreThreads
+      const int nk = __syncthreads_count((int)threadIdx.x < np && sPm[threadIdx.x] != 0u);
+      // compact mode's row addressing (a division and an LDS read per row slot ahead of
+      // the loads) costs about a tenth of a dense row's time: it pays once an eighth of
+      // the parents or more are unkept
+      if (8 * nk <= 7 * np) {
+        if (wave == 0) {
+          int at = 0;
+          for (int base = 0; base < np; base += 64) {
+            const int i = base + lane;
+            const bool kept = i < np && sPm[i] != 0u;
+            const uint64_t bal = __ballot(kept);
+            if (kept) sKept[at + __popcll(bal & ((1ull << lane) - 1ull))] = (uint16_t)i;
+            at += __popcll(bal);
+          }
+        }
+        __syncthreads();
+        compact = true;
+        n_rows = nk * geo.b;
+      }
+    }
   }
 #pragma unroll
   for (int m = 0; m < M; ++m)
@@ -421,74 +460,100 @@ __global__ __launch_bounds__(kScoreThreads) void score_rows_kernel(
   const float* Xu = X + (int64_t)bg_of(geo, u) * X_unit_stride + 4 * sub;
   // the workgroup's rows in groups of kRowGroup, taken by the waves in turn, so the four
   // waves read one contiguous stream
-  const int groups_wg = (k_end - k_wg + kRowGroup - 1) / kRowGroup;
+  const int groups_wg = (n_rows + kRowGroup - 1) / kRowGroup;
   const int n_groups = groups_wg > wave ? (groups_wg - wave + NW - 1) / NW : 0;
 
-  // Every group's loads are issued unconditionally (rows past the range read its last row
-  // again, a line already in cache; rows whose parent no member kept read row 0, and no
-  // member's selection reads their scores): a branch around a load would make the compiler
-  // wait for all outstanding loads where the paths join.
+  // Every group's loads are issued unconditionally (rows past the workgroup's rows read its
+  // last row again, a line already in cache; in dense mode, rows whose parent no member
+  // kept read row 0, and no member's selection reads their scores): a branch around a load
+  // would make the compiler wait for all outstanding loads where the paths join.
   typedef f32x4_t Group[IPG][NLD];
-  auto load_group = [&](Group& x, int g) {
-    uint32_t node[IPG];
+  // One instantiation per mode (compact is uniform over the workgroup), so the dense mode
+  // keeps its own address arithmetic and neither pays for the other's.
+  auto score_groups = [&](auto compact_tag) {
+    constexpr bool kCompact = decltype(compact_tag)::value;
+    // dst[i]: the entry (relative to k_wg) whose score row slot i of the group holds, or -1
+    // for a slot past the workgroup's rows (its load repeats the last row)
+    auto load_group = [&](Group& x, int (&dst)[IPG], int g) {
+      uint32_t node[IPG];
 #pragma unroll
-    for (int i = 0; i < IPG; ++i) {
-      const uint32_t kc =
-          (uint32_t)min(k_wg + (g * NW + wave) * kRowGroup + i * RPI + rin, k_end - 1);
-      const uint32_t pm = sPm[has_parent ? geo.bdiv.div(kc) - p0 : 0];
-      node[i] = (!has_parent || pm != 0u) ? kc : 0u;
-    }
-#pragma unroll
-    for (int i = 0; i < IPG; ++i)
-#pragma unroll
-      for (int j = 0; j < NLD; ++j)
-        x[i][j] = __builtin_nontemporal_load(
-            reinterpret_cast<const f32x4_t*>(Xu + (int64_t)node[i] * D + 4 * LPR * j));
-  };
-
-  auto compute_group = [&](const Group& x, int g) {
-    const int r0 = (g * NW + wave) * kRowGroup;  // row of the workgroup's range
-#pragma unroll
-    for (int i = 0; i < IPG; ++i) {
-      float v[M];
-#pragma unroll
-      for (int m = 0; m < M; ++m) {
-        float a = x[i][0].x * qv[m][0];
-        a = fmaf(x[i][0].y, qv[m][1], a);
-        a = fmaf(x[i][0].z, qv[m][2], a);
-        a = fmaf(x[i][0].w, qv[m][3], a);
-#pragma unroll
-        for (int j = 1; j < NLD; ++j) {
-          a = fmaf(x[i][j].x, qv[m][4 * j], a);
-          a = fmaf(x[i][j].y, qv[m][4 * j + 1], a);
-          a = fmaf(x[i][j].z, qv[m][4 * j + 2], a);
-          a = fmaf(x[i][j].w, qv[m][4 * j + 3], a);
+      for (int i = 0; i < IPG; ++i) {
+        const int r = (g * NW + wave) * kRowGroup + i * RPI + rin;
+        const int rc = min(r, n_rows - 1);
+        if constexpr (kCompact) {
+          // row rc of the kept parents' rows: child rc % b of the (rc / b)-th kept parent
+          const uint32_t j = geo.bdiv.div((uint32_t)rc);
+          const uint32_t kc = ((uint32_t)p0 + sKept[j]) * (uint32_t)geo.b + (uint32_t)rc -
+                              j * (uint32_t)geo.b;
+          node[i] = kc;
+          dst[i] = r < n_rows ? (int)kc - k_wg : -1;
+        } else {
+          const uint32_t kc = (uint32_t)(k_wg + rc);
+          const uint32_t pm = sPm[has_parent ? geo.bdiv.div(kc) - p0 : 0];
+          node[i] = (!has_parent || pm != 0u) ? kc : 0u;
         }
-        v[m] = a;
       }
-      MemberHalve<M, LPR / 2>::run(v, lane);
-      // + 0.0f turns a -0 score into +0 so float and bit orders agree
-      if (sub % RL == 0) sS[sub / RL][r0 + i * RPI + rin] = sigma * v[0] + 0.0f;
+#pragma unroll
+      for (int i = 0; i < IPG; ++i)
+#pragma unroll
+        for (int j = 0; j < NLD; ++j)
+          x[i][j] = __builtin_nontemporal_load(
+              reinterpret_cast<const f32x4_t*>(Xu + (int64_t)node[i] * D + 4 * LPR * j));
+    };
+
+    auto compute_group = [&](const Group& x, const int (&dst)[IPG], int g) {
+      const int r0 = (g * NW + wave) * kRowGroup;  // dense mode: row of the workgroup's range
+#pragma unroll
+      for (int i = 0; i < IPG; ++i) {
+        float v[M];
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+          float a = x[i][0].x * qv[m][0];
+          a = fmaf(x[i][0].y, qv[m][1], a);
+          a = fmaf(x[i][0].z, qv[m][2], a);
+          a = fmaf(x[i][0].w, qv[m][3], a);
+#pragma unroll
+          for (int j = 1; j < NLD; ++j) {
+            a = fmaf(x[i][j].x, qv[m][4 * j], a);
+            a = fmaf(x[i][j].y, qv[m][4 * j + 1], a);
+            a = fmaf(x[i][j].z, qv[m][4 * j + 2], a);
+            a = fmaf(x[i][j].w, qv[m][4 * j + 3], a);
+          }
+          v[m] = a;
+        }
+        MemberHalve<M, LPR / 2>::run(v, lane);
+        // + 0.0f turns a -0 score into +0 so float and bit orders agree (dense mode: slots
+        // past the range store into entries past it, which nothing reads)
+        if constexpr (kCompact) {
+          if (sub % RL == 0 && dst[i] >= 0) sS[sub / RL][dst[i]] = sigma * v[0] + 0.0f;
+        } else {
+          if (sub % RL == 0) sS[sub / RL][r0 + i * RPI + rin] = sigma * v[0] + 0.0f;
+        }
+      }
+    };
+
+    if (n_groups > 0) {
+      Group xa, xb;
+      int da[IPG], db[IPG];
+      load_group(xa, da, 0);
+      for (int g = 0; g < n_groups; g += 2) {
+        load_group(xb, db, g + 1);
+        compute_group(xa, da, g);
+        load_group(xa, da, g + 2);
+        if (g + 1 < n_groups) compute_group(xb, db, g + 1);
+      }
     }
   };
-
-  if (n_groups > 0) {
-    Group xa, xb;
-    load_group(xa, 0);
-    for (int g = 0; g < n_groups; g += 2) {
-      load_group(xb, g + 1);
-      compute_group(xa, g);
-      load_group(xa, g + 2);
-      if (g + 1 < n_groups) compute_group(xb, g + 1);
-    }
-  }
+  if (compact)
+    score_groups(std::true_type{});
+  else
+    score_groups(std::false_type{});
   __syncthreads();
 
   // scores out, after the last row load: wave w stores members w, w + NW, ..., each as one
   // contiguous run of 16-byte stores, and reduces its max and min over the member's
   // frontier entries for the chunked selection
   const int n = k_end - k_wg;
-  const bool quad_parent = has_parent && geo.b % 4 == 0;
 #pragma unroll
   for (int mi = 0; mi < M / NW; ++mi) {
     const int mm = wave + NW * mi;

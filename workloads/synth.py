@@ -15,7 +15,8 @@ slice can be regenerated alone):
 * keys      K[b,g,i] = mu[b,g,i // 64] + 0.3 * eps[b,g,i],  mu, eps ~ N(0, I_d)
 * values    V[b,g,i] ~ N(0, I_d)
 * reference queries R[g] ~ N(0, I_d / d) (16 per KV head; variance 1/d)
-* queries   Q[b,t,h] ~ N(0, I_d)
+* queries   Q[b,t,h] ~ N(0, I_d); in the "agree" variant the G heads of a KV head share
+            most of one direction and every score is scaled up (gen_Q)
 * needle    K[b, h // G, pos] = 4 * q / |q| for the aimed query q; never at token 0
 
 then every tensor is rounded once to the storage dtype (bf16 round-to-nearest-
@@ -23,7 +24,7 @@ even through torch, or kept as float32). The rounded values are the canonical
 inputs for every consumer.
 
 Streams: 0 centroids, 1 key noise, 2 values, 3 queries, 4 reference queries,
-5 needle placement.
+5 needle placement, 6 shared query directions.
 """
 
 from __future__ import annotations
@@ -46,6 +47,14 @@ WORKLOADS = {
     # single layer, 256K context, deep tree b=4 L=6 (64 top nodes of 4096 tokens)
     "256k_deep": dict(dtype="bf16", B=4, T=1, Hq=32, Hkv=4, d=128, N=262144, b=4, L=6,
                       p=(0.95,), seed=3, needles="stratified16"),
+    # the same keys and values as 256k_deep, with queries whose 8 heads per KV head share
+    # most of one direction (correlation 0.81) and scores three times as sharp: each head
+    # reads about 1.1% of the keys (the share the pages report on real attention) and the
+    # union of a KV head's heads about 5%, where the independent queries above read 41%
+    # per head and 98.5% in union
+    "256k_deep_agree": dict(dtype="bf16", B=4, T=1, Hq=32, Hkv=4, d=128, N=262144, b=4, L=6,
+                            p=(0.95,), seed=3, needles="stratified16", q_shared=0.9,
+                            q_scale=3.0),
     # the same tensors as 256k_deep (same seed), wide tree b=256 L=1
     "256k_wide": dict(dtype="bf16", B=4, T=1, Hq=32, Hkv=4, d=128, N=262144, b=256, L=1,
                       p=(0.8, 0.95, 0.99), seed=3, needles="stratified16"),
@@ -95,10 +104,25 @@ def gen_R(s: dict) -> np.ndarray:
 
 
 def gen_Q(s: dict) -> np.ndarray:
-    """Decode queries, [B, T, Hq, d], rounded to the storage dtype."""
+    """Decode queries, [B, T, Hq, d], rounded to the storage dtype.
+
+    By default every query is an independent N(0, I_d) draw. With ``q_shared`` = rho > 0
+    the G query heads of a KV head lean on one shared direction per (sequence, query,
+    KV head), u ~ N(0, I_d) from stream 6: q = q_scale * (sqrt(1 - rho^2) eps + rho u),
+    which keeps each query N(0, q_scale^2 I_d) while the heads of a group agree; a
+    ``q_scale`` above 1 sharpens every softmax over the keys."""
     out = np.empty((s["B"], s["T"], s["Hq"], s["d"]), np.float32)
     for b in range(s["B"]):
         out[b] = _rng(s["seed"], b, 0, 3).standard_normal((s["T"], s["Hq"], s["d"]), dtype=np.float32)
+    rho, scale = float(s.get("q_shared", 0.0)), float(s.get("q_scale", 1.0))
+    if rho != 0.0 or scale != 1.0:
+        G = s["Hq"] // s["Hkv"]
+        for b in range(s["B"]):
+            u = _rng(s["seed"], b, 0, 6).standard_normal((s["T"], s["Hkv"], s["d"]),
+                                                        dtype=np.float32)
+            shared = np.repeat(u, G, axis=1)                       # [T, Hq, d]
+            out[b] = np.float32(scale) * (np.float32(math.sqrt(1.0 - rho * rho)) * out[b]
+                                          + np.float32(rho) * shared)
     return to_storage(out, s["dtype"])
 
 
