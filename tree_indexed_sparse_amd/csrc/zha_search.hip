@@ -21,8 +21,6 @@
 // A level = a score and a select launch (plus the compaction at level 1). Kernel
 // boundaries order them; no kernel here uses a device-scope fence.
 
-#include <type_traits>
-
 #include "zha_internal.h"
 #include "zha_mxfp4.h"
 
@@ -468,30 +466,40 @@ __global__ __launch_bounds__(kScoreThreads) void score_rows_kernel(
   // kept read row 0, and no member's selection reads their scores): a branch around a load
   // would make the compiler wait for all outstanding loads where the paths join.
   typedef f32x4_t Group[IPG][NLD];
-  // One instantiation per mode (compact is uniform over the workgroup), so the dense mode
-  // keeps its own address arithmetic and neither pays for the other's.
-  auto score_groups = [&](auto compact_tag) {
-    constexpr bool kCompact = decltype(compact_tag)::value;
-    // dst[i]: the entry (relative to k_wg) whose score row slot i of the group holds, or -1
-    // for a slot past the workgroup's rows (its load repeats the last row)
-    auto load_group = [&](Group& x, int (&dst)[IPG], int g) {
+  // sigma * q . x for every member over one row slot, left by the butterfly in the lanes
+  // sub % RL == 0 (member sub / RL)
+  auto row_score = [&](const f32x4_t (&xr)[NLD]) {
+    float v[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      float a = xr[0].x * qv[m][0];
+      a = fmaf(xr[0].y, qv[m][1], a);
+      a = fmaf(xr[0].z, qv[m][2], a);
+      a = fmaf(xr[0].w, qv[m][3], a);
+#pragma unroll
+      for (int j = 1; j < NLD; ++j) {
+        a = fmaf(xr[j].x, qv[m][4 * j], a);
+        a = fmaf(xr[j].y, qv[m][4 * j + 1], a);
+        a = fmaf(xr[j].z, qv[m][4 * j + 2], a);
+        a = fmaf(xr[j].w, qv[m][4 * j + 3], a);
+      }
+      v[m] = a;
+    }
+    MemberHalve<M, LPR / 2>::run(v, lane);
+    // + 0.0f turns a -0 score into +0 so float and bit orders agree
+    return sigma * v[0] + 0.0f;
+  };
+
+  if (!compact) {
+    // dense: every row of the range; rows whose parent no member kept read row 0
+    auto load_group = [&](Group& x, int g) {
       uint32_t node[IPG];
 #pragma unroll
       for (int i = 0; i < IPG; ++i) {
-        const int r = (g * NW + wave) * kRowGroup + i * RPI + rin;
-        const int rc = min(r, n_rows - 1);
-        if constexpr (kCompact) {
-          // row rc of the kept parents' rows: child rc % b of the (rc / b)-th kept parent
-          const uint32_t j = geo.bdiv.div((uint32_t)rc);
-          const uint32_t kc = ((uint32_t)p0 + sKept[j]) * (uint32_t)geo.b + (uint32_t)rc -
-                              j * (uint32_t)geo.b;
-          node[i] = kc;
-          dst[i] = r < n_rows ? (int)kc - k_wg : -1;
-        } else {
-          const uint32_t kc = (uint32_t)(k_wg + rc);
-          const uint32_t pm = sPm[has_parent ? geo.bdiv.div(kc) - p0 : 0];
-          node[i] = (!has_parent || pm != 0u) ? kc : 0u;
-        }
+        const uint32_t kc =
+            (uint32_t)min(k_wg + (g * NW + wave) * kRowGroup + i * RPI + rin, k_end - 1);
+        const uint32_t pm = sPm[has_parent ? geo.bdiv.div(kc) - p0 : 0];
+        node[i] = (!has_parent || pm != 0u) ? kc : 0u;
       }
 #pragma unroll
       for (int i = 0; i < IPG; ++i)
@@ -500,54 +508,68 @@ __global__ __launch_bounds__(kScoreThreads) void score_rows_kernel(
           x[i][j] = __builtin_nontemporal_load(
               reinterpret_cast<const f32x4_t*>(Xu + (int64_t)node[i] * D + 4 * LPR * j));
     };
-
-    auto compute_group = [&](const Group& x, const int (&dst)[IPG], int g) {
-      const int r0 = (g * NW + wave) * kRowGroup;  // dense mode: row of the workgroup's range
+    auto compute_group = [&](const Group& x, int g) {
+      const int r0 = (g * NW + wave) * kRowGroup;  // row of the workgroup's range
 #pragma unroll
       for (int i = 0; i < IPG; ++i) {
-        float v[M];
-#pragma unroll
-        for (int m = 0; m < M; ++m) {
-          float a = x[i][0].x * qv[m][0];
-          a = fmaf(x[i][0].y, qv[m][1], a);
-          a = fmaf(x[i][0].z, qv[m][2], a);
-          a = fmaf(x[i][0].w, qv[m][3], a);
-#pragma unroll
-          for (int j = 1; j < NLD; ++j) {
-            a = fmaf(x[i][j].x, qv[m][4 * j], a);
-            a = fmaf(x[i][j].y, qv[m][4 * j + 1], a);
-            a = fmaf(x[i][j].z, qv[m][4 * j + 2], a);
-            a = fmaf(x[i][j].w, qv[m][4 * j + 3], a);
-          }
-          v[m] = a;
-        }
-        MemberHalve<M, LPR / 2>::run(v, lane);
-        // + 0.0f turns a -0 score into +0 so float and bit orders agree (dense mode: slots
-        // past the range store into entries past it, which nothing reads)
-        if constexpr (kCompact) {
-          if (sub % RL == 0 && dst[i] >= 0) sS[sub / RL][dst[i]] = sigma * v[0] + 0.0f;
-        } else {
-          if (sub % RL == 0) sS[sub / RL][r0 + i * RPI + rin] = sigma * v[0] + 0.0f;
-        }
+        const float sc = row_score(x[i]);
+        // slots past the range store into entries past it, which nothing reads
+        if (sub % RL == 0) sS[sub / RL][r0 + i * RPI + rin] = sc;
       }
     };
-
+    if (n_groups > 0) {
+      Group xa, xb;
+      load_group(xa, 0);
+      for (int g = 0; g < n_groups; g += 2) {
+        load_group(xb, g + 1);
+        compute_group(xa, g);
+        load_group(xa, g + 2);
+        if (g + 1 < n_groups) compute_group(xb, g + 1);
+      }
+    }
+  } else {
+    // compact: the kept parents' rows only. dst[i]: the entry (relative to k_wg) whose
+    // score slot i of the group holds, or -1 for a slot past them (its load repeats the
+    // last row)
+    auto load_group = [&](Group& x, int (&dst)[IPG], int g) {
+      uint32_t node[IPG];
+#pragma unroll
+      for (int i = 0; i < IPG; ++i) {
+        const int r = (g * NW + wave) * kRowGroup + i * RPI + rin;
+        const int rc = min(r, n_rows - 1);
+        // row rc of the kept parents' rows: child rc % b of the (rc / b)-th kept parent
+        const uint32_t j = geo.bdiv.div((uint32_t)rc);
+        const uint32_t kc = ((uint32_t)p0 + sKept[j]) * (uint32_t)geo.b + (uint32_t)rc -
+                            j * (uint32_t)geo.b;
+        node[i] = kc;
+        dst[i] = r < n_rows ? (int)kc - k_wg : -1;
+      }
+#pragma unroll
+      for (int i = 0; i < IPG; ++i)
+#pragma unroll
+        for (int j = 0; j < NLD; ++j)
+          x[i][j] = __builtin_nontemporal_load(
+              reinterpret_cast<const f32x4_t*>(Xu + (int64_t)node[i] * D + 4 * LPR * j));
+    };
+    auto compute_group = [&](const Group& x, const int (&dst)[IPG]) {
+#pragma unroll
+      for (int i = 0; i < IPG; ++i) {
+        const float sc = row_score(x[i]);
+        if (sub % RL == 0 && dst[i] >= 0) sS[sub / RL][dst[i]] = sc;
+      }
+    };
     if (n_groups > 0) {
       Group xa, xb;
       int da[IPG], db[IPG];
       load_group(xa, da, 0);
       for (int g = 0; g < n_groups; g += 2) {
         load_group(xb, db, g + 1);
-        compute_group(xa, da, g);
+        compute_group(xa, da);
         load_group(xa, da, g + 2);
-        if (g + 1 < n_groups) compute_group(xb, db, g + 1);
+        if (g + 1 < n_groups) compute_group(xb, db);
       }
     }
-  };
-  if (compact)
-    score_groups(std::true_type{});
-  else
-    score_groups(std::false_type{});
+  }
   __syncthreads();
 
   // scores out, after the last row load: wave w stores members w, w + NW, ..., each as one
