@@ -81,6 +81,13 @@ typedef enum { ZHA_ROUTER_F32 = 0, ZHA_ROUTER_MXFP4 = 1 } zha_router;
  * router_data + router_scale_off[l] + (u * (N_cap / b^l) + j) * d / 32 (E8M0: the block of
  * elements 32k .. 32k + 31 is scaled by 2^(byte - 127)). zha_build_tree sets router to
  * ZHA_ROUTER_F32 and router_data to NULL.
+ *
+ * The view is the library's: zha_build_tree writes the level offsets and
+ * zha_router_quantize the router copy's; a caller may change N only through
+ * zha_tree_append and router between the two copies. Every entry point that takes a tree
+ * checks its fields, its geometry and that every offset is where the library puts it,
+ * and returns ZHA_ERR_INVALID_ARG otherwise (a view filled by hand can be laid out by
+ * zha_build_tree over zero tokens, which enqueues nothing).
  */
 typedef struct {
   int32_t B, Hkv, N, N_cap, d, b, L;

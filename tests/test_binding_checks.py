@@ -10,6 +10,7 @@ import pytest
 import torch
 
 import tree_indexed_sparse_amd as Z
+from abi_views import lay_out
 from tree_indexed_sparse_amd import _lib as LB
 
 pytestmark = pytest.mark.skipif(not os.path.exists(LB.LIB_PATH), reason="libzha.so not built")
@@ -23,7 +24,7 @@ def _tree(dtype=LB.ZHA_BF16):
     for k, v in dict(B=B, Hkv=HKV, N=NCAP, N_cap=NCAP, d=D, b=BR, L=LV, dtype=dtype).items():
         setattr(c, k, v)
     c.pyramid = 0x2000  # never dereferenced: every call below stops on the host
-    return Z.Tree(c, torch.empty(4, dtype=torch.uint8))
+    return Z.Tree(lay_out(LB.load(), c), torch.empty(4, dtype=torch.uint8))
 
 
 def _inputs(dt=torch.bfloat16):

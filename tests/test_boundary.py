@@ -8,6 +8,7 @@ import re
 
 import pytest
 
+from abi_views import lay_out
 from tree_indexed_sparse_amd import _lib as L
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -95,7 +96,7 @@ def _tree(**kw):
     for k, v in a.items():
         setattr(t, k, v)
     t.pyramid = 0x2000
-    return t
+    return lay_out(L.load(), t)
 
 
 def _attend(lib, t=None, **kw):
@@ -121,6 +122,34 @@ def _attend(lib, t=None, **kw):
 def test_attend_rejects_bad_arguments(lib, kw, code):
     assert _attend(lib, **kw) == code
     assert len(lib.zha_last_error()) > 0
+
+
+def test_tree_view_offsets_must_be_the_librarys(lib):
+    """A view whose level offsets (or attached router copy's offsets) differ from where the
+    library lays them out is rejected before anything is enqueued: a kernel would otherwise
+    read a level at an arbitrary place."""
+    t = _tree()
+    assert lib.zha_attend_workspace_bytes(ctypes.byref(t), 1, 8) > 0
+    for level, delta in ((1, 64), (2, -4), (3, 1 << 20)):
+        bad = _tree()
+        bad.level_off[level] += delta
+        assert _attend(lib, t=bad) == -1
+        assert b"level_off" in lib.zha_last_error()
+        assert lib.zha_attend_workspace_bytes(ctypes.byref(bad), 1, 8) == 0
+        assert lib.zha_tree_append(ctypes.byref(bad), FAKE, FAKE, 0, None) == -1
+    # an attached router copy must sit where zha_router_quantize puts it
+    r = _tree()
+    r.router_data = 0x4000
+    assert _attend(lib, t=r) == -1
+    assert b"router offsets" in lib.zha_last_error()
+    # zha_router_quantize lays the copy out itself: over zero tokens it enqueues nothing
+    q = _tree(N=0)
+    assert lib.zha_router_quantize(ctypes.byref(q), 0, FAKE, 1 << 40, None) == 0
+    assert q.router == L.ZHA_ROUTER_MXFP4 and q.router_data == FAKE.value
+    assert q.router_code_off[2] > 0 and q.router_scale_off[1] > q.router_code_off[1]
+    assert lib.zha_tree_append(ctypes.byref(q), FAKE, FAKE, 0, None) == 0
+    q.router_scale_off[3] += 16
+    assert lib.zha_tree_append(ctypes.byref(q), FAKE, FAKE, 0, None) == -1
 
 
 def test_attend_rejects_query_head_counts_past_int32(lib):
@@ -305,6 +334,7 @@ def test_noalloc_rejects_a_workspace_beyond_its_scratch(lib):
     t = L.ZhaTree()
     t.B, t.Hkv, t.N, t.N_cap, t.d, t.b, t.L, t.dtype = 8, 4, 1 << 20, 1 << 20, 128, 4, 7, 1
     t.pyramid = FAKE.value
+    lay_out(lib, t)
     assert lib.zha_attend_workspace_bytes(ctypes.byref(t), 1, 32) > L.ZHA_NOALLOC_SCRATCH_BYTES
     code = lib.zha_attend_noalloc(ctypes.byref(t), FAKE, 1, 32, FAKE, FAKE, 0.95, 1, FAKE, None,
                                   1 << 20, FAKE, None)

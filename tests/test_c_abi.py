@@ -29,14 +29,20 @@ int main(void) {
   EXPECT(zha_router_bytes(1, 2, 4096, 96, 4, 3) == 0);
   EXPECT(zha_router_bytes(1, 2, 4096, 64, 4, 3) > 0);
 
+  void* fake = (void*)0x1000;
+  /* the library lays the view out: over zero tokens the build enqueues nothing */
   zha_tree t;
   memset(&t, 0, sizeof t);
-  t.B = 1; t.Hkv = 2; t.N = 4096; t.N_cap = 4096; t.d = 64; t.b = 4; t.L = 3;
-  t.dtype = ZHA_BF16; t.pyramid = (float*)0x2000; t.router = ZHA_ROUTER_F32;
+  EXPECT(zha_build_tree(fake, fake, ZHA_BF16, 1, 2, 0, 4096, 64, 4, 3, fake, 1 << 30, &t,
+                        NULL) == ZHA_OK);
+  EXPECT(t.N == 0 && t.level_off[1] == 0 && t.level_off[2] == 2 * 1024 * 64);
+  t.N = 4096;
   EXPECT(zha_attend_workspace_bytes(&t, 1, 8) > 0);
   EXPECT(zha_attend_workspace_bytes(&t, 1, 7) == 0);  /* Hq % Hkv != 0 */
+  t.level_off[3] += 1;                                  /* not the library's layout */
+  EXPECT(zha_attend_workspace_bytes(&t, 1, 8) == 0);
+  t.level_off[3] -= 1;
 
-  void* fake = (void*)0x1000;
   EXPECT(zha_attend(NULL, fake, 1, 8, fake, fake, 0.9f, 1, (float*)fake, NULL, 4096,
                     (int32_t*)fake, fake, 1 << 30, NULL) == ZHA_ERR_INVALID_ARG);
   EXPECT(strlen(zha_last_error()) > 0);

@@ -240,16 +240,16 @@ KeepBits level_bits(char* ws, const WsLayout& w, int L, int l_top, int l) {
   return KeepBits{(uint32_t*)(ws + off), words};
 }
 
-int check_tree(const zha_tree* t) {
-  if (!t) return fail(ZHA_ERR_INVALID_ARG, "tree is NULL");
-  if (!t->pyramid) return fail(ZHA_ERR_INVALID_ARG, "tree has no pyramid");
-  if (t->dtype != ZHA_F32 && t->dtype != ZHA_BF16)
-    return fail(ZHA_ERR_DTYPE, "unknown dtype %d", t->dtype);
-  if (t->router != ZHA_ROUTER_F32 && t->router != ZHA_ROUTER_MXFP4)
-    return fail(ZHA_ERR_INVALID_ARG, "unknown router %d", t->router);
-  if (t->router == ZHA_ROUTER_MXFP4 && !t->router_data)
-    return fail(ZHA_ERR_INVALID_ARG, "router is MXFP4 but the tree has no router copy");
-  return check_geometry(t->B, t->Hkv, t->N, t->N_cap, t->d, t->b, t->L);
+// Float offsets of the pyramid levels (level l at level_off[l], each level 256-byte
+// aligned) for a valid geometry. Returns the total bytes.
+int64_t pyramid_layout(int B, int Hkv, int N_cap, int d, int b, int L, int64_t* level_off) {
+  int64_t off = 0, nl = N_cap;
+  for (int l = 1; l <= L; ++l) {
+    nl /= b;
+    if (level_off) level_off[l] = off / 4;
+    off = align256(off + 4 * (int64_t)B * Hkv * nl * d);
+  }
+  return off;
 }
 
 // Byte offsets of the MXFP4 router copy: per level the codes, then the scales, each
@@ -266,6 +266,42 @@ int64_t router_layout(int B, int Hkv, int N_cap, int d, int b, int L, int64_t* c
     off = align256(off + rows * (d / 32));
   }
   return off;
+}
+
+// A tree view as zha_build_tree (and zha_router_quantize) lay it out: valid fields and
+// geometry, and every level's offset (and the router copy's, if attached) where the
+// library puts it, so that no kernel is handed a pointer outside the caller's buffers.
+int check_tree(const zha_tree* t) {
+  if (!t) return fail(ZHA_ERR_INVALID_ARG, "tree is NULL");
+  if (!t->pyramid) return fail(ZHA_ERR_INVALID_ARG, "tree has no pyramid");
+  if (t->dtype != ZHA_F32 && t->dtype != ZHA_BF16)
+    return fail(ZHA_ERR_DTYPE, "unknown dtype %d", t->dtype);
+  if (t->router != ZHA_ROUTER_F32 && t->router != ZHA_ROUTER_MXFP4)
+    return fail(ZHA_ERR_INVALID_ARG, "unknown router %d", t->router);
+  if (t->router == ZHA_ROUTER_MXFP4 && !t->router_data)
+    return fail(ZHA_ERR_INVALID_ARG, "router is MXFP4 but the tree has no router copy");
+  const int st = check_geometry(t->B, t->Hkv, t->N, t->N_cap, t->d, t->b, t->L);
+  if (st != ZHA_OK) return st;
+  int64_t lo[ZHA_MAX_LEVELS + 1] = {0};
+  pyramid_layout(t->B, t->Hkv, t->N_cap, t->d, t->b, t->L, lo);
+  for (int l = 1; l <= t->L; ++l)
+    if (t->level_off[l] != lo[l])
+      return fail(ZHA_ERR_INVALID_ARG,
+                  "tree level_off[%d] = %lld where zha_build_tree puts the level at %lld: "
+                  "the view was not made (or was changed) outside the library",
+                  l, (long long)t->level_off[l], (long long)lo[l]);
+  if (t->router_data) {
+    int64_t co[ZHA_MAX_LEVELS + 1] = {0}, so[ZHA_MAX_LEVELS + 1] = {0};
+    router_layout(t->B, t->Hkv, t->N_cap, t->d, t->b, t->L, co, so);
+    for (int l = 1; l <= t->L; ++l)
+      if (t->router_code_off[l] != co[l] || t->router_scale_off[l] != so[l])
+        return fail(ZHA_ERR_INVALID_ARG,
+                    "tree router offsets of level %d (%lld, %lld) are not where "
+                    "zha_router_quantize puts them (%lld, %lld)",
+                    l, (long long)t->router_code_off[l], (long long)t->router_scale_off[l],
+                    (long long)co[l], (long long)so[l]);
+  }
+  return ZHA_OK;
 }
 
 // Encode, at every level not marked in `skip`, rows [n_lo / b^l, n_hi / b^l) of each unit
@@ -308,12 +344,7 @@ size_t zha_tree_bytes(int B, int Hkv, int N_cap, int d, int b, int L) {
   const int st = check_geometry(B, Hkv, 0, N_cap, d, b, L);
   g_err = saved;
   if (st != ZHA_OK) return 0;
-  int64_t total = 0, nl = N_cap;
-  for (int l = 1; l <= L; ++l) {
-    nl /= b;
-    total = align256(total + 4 * (int64_t)B * Hkv * nl * d);
-  }
-  return (size_t)total;
+  return (size_t)pyramid_layout(B, Hkv, N_cap, d, b, L, nullptr);
 }
 
 size_t zha_router_bytes(int B, int Hkv, int N_cap, int d, int b, int L) {
@@ -333,12 +364,16 @@ int zha_router_quantize(zha_tree* t, int n_from, void* router_data, size_t route
   zha_tree v = *t;  // checked as it will be once the copy is attached
   v.router = ZHA_ROUTER_MXFP4;
   v.router_data = (uint8_t*)router_data;
-  int st = check_tree(&v);
+  // the geometry first (the router layout divides by b), then the copy's offsets as the
+  // library lays them, then the whole view
+  int st = check_geometry(v.B, v.Hkv, v.N, v.N_cap, v.d, v.b, v.L);
+  if (st != ZHA_OK) return st;
+  const int64_t need = router_layout(v.B, v.Hkv, v.N_cap, v.d, v.b, v.L, v.router_code_off,
+                                     v.router_scale_off);
+  st = check_tree(&v);
   if (st != ZHA_OK) return st;
   if (n_from < 0 || n_from > t->N)
     return fail(ZHA_ERR_SHAPE, "n_from=%d must lie in [0, N=%d]", n_from, t->N);
-  const int64_t need = router_layout(t->B, t->Hkv, t->N_cap, t->d, t->b, t->L,
-                                     v.router_code_off, v.router_scale_off);
   if ((int64_t)router_bytes < need)
     return fail(ZHA_ERR_SHAPE, "router buffer has %zu bytes, needs %lld", router_bytes,
                 (long long)need);
@@ -446,12 +481,7 @@ int zha_build_tree(const void* K, const void* R, int dtype, int B, int Hkv, int 
   t.L = L;
   t.dtype = dtype;
   t.pyramid = (float*)pyramid;
-  int64_t off = 0, nl = N_cap;
-  for (int l = 1; l <= L; ++l) {
-    nl /= b;
-    t.level_off[l] = off / 4;
-    off = align256(off + 4 * (int64_t)B * Hkv * nl * d);
-  }
+  pyramid_layout(B, Hkv, N_cap, d, b, L, t.level_off);
   st = zha_tree_append(&t, K, R, N, stream);
   if (st != ZHA_OK) return st;
   *out = t;
