@@ -83,11 +83,12 @@ typedef enum { ZHA_ROUTER_F32 = 0, ZHA_ROUTER_MXFP4 = 1 } zha_router;
  * ZHA_ROUTER_F32 and router_data to NULL.
  *
  * The view is the library's: zha_build_tree writes the level offsets and
- * zha_router_quantize the router copy's; a caller may change N only through
- * zha_tree_append and router between the two copies. Every entry point that takes a tree
- * checks its fields, its geometry and that every offset is where the library puts it,
- * and returns ZHA_ERR_INVALID_ARG otherwise (a view filled by hand can be laid out by
- * zha_build_tree over zero tokens, which enqueues nothing).
+ * zha_router_quantize the router copy's. A caller may lower N to append tokens again (each
+ * append re-pools the nodes it completes) and may switch router between the two copies;
+ * N grows only through zha_tree_append. Every entry point that takes a tree checks its
+ * fields, its geometry and that every offset is where the library puts it, and returns
+ * ZHA_ERR_INVALID_ARG otherwise (a view filled by hand can be laid out by zha_build_tree
+ * over zero tokens, which enqueues nothing).
  */
 typedef struct {
   int32_t B, Hkv, N, N_cap, d, b, L;
