@@ -101,6 +101,10 @@ def test_attend_rejects_tensors_on_another_device():
     meta = torch.zeros(B, T, HQ, D, device="meta")
     code, msg = _code(lambda: Z.attend(a["Q"], a["K"], a["V"], _tree(), 0.95, out=meta))
     assert code == -1 and "meta" in msg
+    import numpy as np
+    pos = np.zeros((B, T), np.int32)  # positions must be a tensor, not an array
+    code, msg = _code(lambda: Z.attend(a["Q"], a["K"], a["V"], _tree(), 0.95, positions=pos))
+    assert code == -1 and "torch tensor" in msg
 
 
 def test_build_and_append_reject_mis_shaped_reference_queries():

@@ -70,7 +70,11 @@ def _shape(t: torch.Tensor, name: str, want: tuple, dtype=None) -> None:
 
 def _same_device(device, **tensors) -> None:
     for name, t in tensors.items():
-        if t is not None and t.device != device:
+        if t is None:
+            continue
+        if not isinstance(t, torch.Tensor):
+            raise ZhaError(-1, f"{name} must be a torch tensor (got {type(t).__name__})")
+        if t.device != device:
             raise ZhaError(-1, f"{name} is on {t.device}, expected {device}")
 
 
