@@ -385,7 +385,7 @@ def test_256k_deep_every_unit():
 
 def test_256k_deep_agreeing_heads_sampled_units():
     """The 256K deep workload's keys with queries whose heads agree and whose scores are
-    sharp (about 1.1% of the keys read per head, 5% per KV head): small frontiers at every
+    sharp (about 2% of the keys read per head, 7% per KV head): small frontiers at every
     level, a short union list for the decode; every head of three units."""
     spec = W.spec("256k_deep_agree")
     res = H.run_gpu(spec, 0.95)

@@ -49,9 +49,9 @@ WORKLOADS = {
                       p=(0.95,), seed=3, needles="stratified16"),
     # the same keys and values as 256k_deep, with queries whose 8 heads per KV head share
     # most of one direction (correlation 0.81) and scores three times as sharp: each head
-    # reads about 1.1% of the keys (the share the pages report on real attention) and the
-    # union of a KV head's heads about 5%, where the independent queries above read 41%
-    # per head and 98.5% in union
+    # reads about 2% of the keys (near the ~1.1% read on real attention with the deep tree
+    # at p = 0.95 in the Le Fil IA page's paragraph 2) and the union of a KV head's heads
+    # about 7%, where the independent queries above read 41% per head and 98.5% in union
     "256k_deep_agree": dict(dtype="bf16", B=4, T=1, Hq=32, Hkv=4, d=128, N=262144, b=4, L=6,
                             p=(0.95,), seed=3, needles="stratified16", q_shared=0.9,
                             q_scale=3.0),
