@@ -377,6 +377,28 @@ def test_agreeing_query_recipe():
     assert (a["q_shared"], a["q_scale"], a["seed"], a["N"]) == (0.9, 3.0, 3, 262144)
 
 
+def test_agreeing_heads_select_few_keys_and_a_small_union():
+    """What the agreeing-heads workload is for, on one (sequence, KV head) unit of 64K
+    tokens through the oracle: its heads each read a few percent of the keys and their
+    union stays small, where the independent heads of the same cache read ~40% each and
+    almost all of it together (the 256K workloads measure 2.0% / 7.0% and 41% / 98.5%)."""
+    import workloads as W
+
+    def shares(name):
+        s = W.spec(name, N=65536, B=1)
+        Q, R = W.gen_Q(s), W.gen_R(s)
+        K, V = W.gen_KV_unit(s, 0, 1, Q)
+        lv = O.build_tree_unit(K, R[1], s["b"], s["L"])
+        sets = [O.search(Q[0, 0, h], lv, s["b"], s["L"], 0.95, 1)[0] for h in range(8, 16)]
+        per_head = np.array([x.size for x in sets]) / s["N"]
+        return per_head, np.unique(np.concatenate(sets)).size / s["N"]
+
+    agree, agree_union = shares("256k_deep_agree")
+    indep, indep_union = shares("256k_deep")
+    assert agree.max() < 0.06 and agree_union < 0.15
+    assert indep.min() > 0.30 and indep_union > 0.90
+
+
 # ------------------------------------------------------------- ragged caches (tail)
 
 @pytest.mark.parametrize("b,L", [(4, 3), (2, 5), (8, 2)])
