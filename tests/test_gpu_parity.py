@@ -393,6 +393,7 @@ def test_256k_deep_agreeing_heads_sampled_units():
     summ = C.summarize(reps)
     _report("256k deep agreeing heads, sampled", summ, pyr)
     _assert_ok(spec, summ, pyr)
+    H.assert_exact_selection(summ)
     kr = np.array([r.keys for r in reps]) / spec["N"]
     print(f"[256k deep agreeing heads] keys read mean {100 * kr.mean():.2f}%", flush=True)
 
